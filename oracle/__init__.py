@@ -1,0 +1,15 @@
+"""CPU oracle for the ARK-ASR-3B int8 decoder step.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+link anything under this package: only tests, the smoke check and the
+benchmark's CPU-baseline leg use it.  It shares no code with the HIP path.
+
+Parity status per function (see each docstring for the passage it follows):
+  every function here is pinned by tests under tests/ that check it against
+  closed forms, brute force on tiny inputs, invariants fixed by the pages, or
+  the pages' printed numbers.  The behaviour of the trained model (its
+  transcripts, the verification table missing from the model card) is parity
+  unpinned: no trained weights exist in this environment.
+"""
+from .ark import *  # noqa: F401,F403
+from .ark import __all__  # noqa: F401
