@@ -1,0 +1,346 @@
+"""ctypes binding of libark.so (include/ark.h).
+
+Argument marshalling only: every step of the decoder runs in the library's
+HIP kernels.  PyTorch supplies device memory and the current HIP stream.
+The functions mirror the C entry points by name and raise ArkError on a
+non-zero status.  Loading fails loudly when libark.so has not been built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libark.so")
+
+ARK_OK, ARK_E_NULL, ARK_E_SHAPE, ARK_E_RANGE, ARK_E_WORKSPACE, ARK_E_HIP, ARK_E_ALIGN = \
+    0, -1, -2, -3, -4, -5, -6
+
+
+class ArkError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn}: {text} (status {status})")
+        self.status = status
+
+
+class ArkDims(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("hidden", C.c_int32), ("n_heads", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("intermediate", C.c_int32),
+                ("vocab", C.c_int32), ("max_total_len", C.c_int32), ("rms_eps", C.c_double),
+                ("rope_theta", C.c_double)]
+
+
+class ArkQLinear(C.Structure):
+    _fields_ = [("w", C.c_void_p), ("scale", C.c_void_p), ("colsum", C.c_void_p),
+                ("bias", C.c_void_p), ("n", C.c_int32), ("k", C.c_int32)]
+
+
+class ArkLayer(C.Structure):
+    _fields_ = [("ln1", C.c_void_p), ("ln2", C.c_void_p), ("q", ArkQLinear), ("k", ArkQLinear),
+                ("v", ArkQLinear), ("o", ArkQLinear), ("gate", ArkQLinear), ("up", ArkQLinear),
+                ("down", ArkQLinear)]
+
+
+class ArkModel(C.Structure):
+    _fields_ = [("d", ArkDims), ("layers", C.POINTER(ArkLayer)), ("final_norm", C.c_void_p),
+                ("lm_head", ArkQLinear), ("embed_f16", C.c_void_p), ("rope_cos", C.c_void_p),
+                ("rope_sin", C.c_void_p)]
+
+
+P = C.c_void_p
+I32 = C.c_int32
+PP = C.POINTER(C.c_void_p)
+PI32 = C.POINTER(C.c_int32)
+
+_SIGS = {
+    "ark_workspace_bytes": (C.c_size_t, [C.POINTER(ArkDims), I32, I32]),
+    "ark_status_string": (C.c_char_p, [C.c_int]),
+    "ark_prep_weight": (C.c_int, [P, I32, I32, P, P, P, P]),
+    "ark_rope_table": (C.c_int, [I32, I32, C.c_double, P, P, P]),
+    "ark_embed_splice": (C.c_int, [C.POINTER(ArkDims), I32, I32, P, P, P, I32, I32, P, P]),
+    "ark_prefill": (C.c_int, [C.POINTER(ArkModel), I32, I32, P, PI32, PP, PP, P, P, P, P, P,
+                              C.c_size_t, P]),
+    "ark_decode_step": (C.c_int, [C.POINTER(ArkModel), I32, P, PI32, PP, PP, P, P, P, P, P,
+                                  C.c_size_t, P]),
+    "ark_masked_argmax": (C.c_int, [I32, I32, P, P, P, P]),
+    "ark_cache_write": (C.c_int, [C.POINTER(ArkDims), I32, I32, PI32, PP, PP, P, P, P]),
+    "ark_greedy_decode": (C.c_int, [C.POINTER(ArkModel), I32, P, PI32, PP, PP, P, P, P, P, I32,
+                                    I32, I32, P, P, C.c_size_t, P]),
+    "ark_test_dynquant": (C.c_int, [I32, I32, I32, P, P, P, P, P, C.c_size_t, P]),
+    "ark_test_qlinear": (C.c_int, [I32, I32, P, P, P, C.POINTER(ArkQLinear), P, P, I32, P,
+                                   C.c_size_t, P]),
+}
+
+_LIB = None
+
+
+def lib() -> C.CDLL:
+    """Load libark.so (built in-tree); raises if it is missing."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m speech_decoder_int8_amd.build`")
+        lb = C.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(lb, name)
+            f.restype = res
+            f.argtypes = args
+        _LIB = lb
+    return _LIB
+
+
+def status_string(status: int) -> str:
+    return lib().ark_status_string(status).decode()
+
+
+def _check(fn: str, status: int) -> int:
+    if status < 0:
+        raise ArkError(fn, status, status_string(status))
+    return status
+
+
+# ------------------------------------------------------------- marshalling --
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def _ptr_array(ts) -> C.Array:
+    arr = (C.c_void_p * len(ts))()
+    for i, t in enumerate(ts):
+        arr[i] = t.data_ptr()
+    return arr
+
+
+def _pos_array(pos) -> C.Array:
+    p = np.ascontiguousarray(np.asarray(pos, dtype=np.int32).reshape(-1))
+    arr = (C.c_int32 * len(p))(*p.tolist())
+    return arr
+
+
+def dims_of(cfg) -> ArkDims:
+    return ArkDims(cfg.n_layers, cfg.hidden, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim,
+                   cfg.intermediate, cfg.vocab, cfg.max_total_len, cfg.rms_eps, cfg.rope_theta)
+
+
+def workspace_bytes(dims: ArkDims, B: int, S: int) -> int:
+    return lib().ark_workspace_bytes(C.byref(dims), B, S)
+
+
+# ------------------------------------------------------------------- prep --
+def prep_weight(w, stream=None):
+    """fp32 [n][k] device tensor -> (codes int8 [n][k], scale fp32 [n], colsum int32 [n])."""
+    import torch
+    n, k = w.shape
+    codes = torch.empty((n, k), dtype=torch.int8, device=w.device)
+    scale = torch.empty(n, dtype=torch.float32, device=w.device)
+    colsum = torch.empty(n, dtype=torch.int32, device=w.device)
+    _check("ark_prep_weight", lib().ark_prep_weight(_ptr(w), n, k, _ptr(codes), _ptr(scale),
+                                                     _ptr(colsum), _stream(stream)))
+    return codes, scale, colsum
+
+
+def rope_table(T: int, head_dim: int, theta: float, device="cuda", stream=None):
+    import torch
+    c = torch.empty((T, head_dim // 2), dtype=torch.float64, device=device)
+    s = torch.empty((T, head_dim // 2), dtype=torch.float64, device=device)
+    _check("ark_rope_table", lib().ark_rope_table(T, head_dim, theta, _ptr(c), _ptr(s), _stream(stream)))
+    return c, s
+
+
+class QLinear:
+    """Device tensors of one prepared projection and its ctypes view."""
+
+    def __init__(self, codes, scale, colsum, bias=None):
+        self.codes, self.scale, self.colsum, self.bias = codes, scale, colsum, bias
+
+    @classmethod
+    def from_f32(cls, w_f32, bias=None, stream=None):
+        return cls(*prep_weight(w_f32, stream), bias)
+
+    def c(self) -> ArkQLinear:
+        n, k = self.codes.shape
+        return ArkQLinear(_ptr(self.codes), _ptr(self.scale), _ptr(self.colsum), _ptr(self.bias), n, k)
+
+
+class DeviceModel:
+    """A prepared decoder on the GPU: int8 weights, gains, rope tables,
+    embedding table, plus the ark_model struct that points at them."""
+
+    def __init__(self, cfg, layers, final_norm, lm_head, embed_f16, rope_cos, rope_sin):
+        self.cfg = cfg
+        self.layers = layers              # list of dicts of QLinear / tensors
+        self.final_norm = final_norm
+        self.lm_head = lm_head            # QLinear or None
+        self.embed_f16 = embed_f16        # int16 tensor (fp16 bits) or None
+        self.rope_cos, self.rope_sin = rope_cos, rope_sin
+        self.dims = dims_of(cfg)
+        self._layer_arr = (ArkLayer * cfg.n_layers)()
+        for i, L in enumerate(layers):
+            self._layer_arr[i] = ArkLayer(_ptr(L["ln1"]), _ptr(L["ln2"]), L["q"].c(), L["k"].c(),
+                                          L["v"].c(), L["o"].c(), L["gate"].c(), L["up"].c(),
+                                          L["down"].c())
+        self.c = ArkModel(self.dims, self._layer_arr, _ptr(final_norm),
+                          lm_head.c() if lm_head is not None else ArkQLinear(),
+                          _ptr(embed_f16), _ptr(rope_cos), _ptr(rope_sin))
+
+    def view(self, layers=None) -> "DeviceModel":
+        """The same weights restricted to some layers (no LM head)."""
+        idx = list(range(self.cfg.n_layers)) if layers is None else list(layers)
+        sub = DeviceModel.__new__(DeviceModel)
+        sub.__dict__.update(self.__dict__)
+        sub.cfg = self.cfg.with_(n_layers=len(idx))
+        sub.layers = [self.layers[i] for i in idx]
+        sub.dims = dims_of(sub.cfg)
+        sub._layer_arr = (ArkLayer * len(idx))(*[self._layer_arr[i] for i in idx])
+        sub.c = ArkModel(sub.dims, sub._layer_arr, None, ArkQLinear(), _ptr(self.embed_f16),
+                         _ptr(self.rope_cos), _ptr(self.rope_sin))
+        sub.lm_head = None
+        return sub
+
+
+def load_model(cfg, synth, device="cuda", stream=None, layers=None) -> DeviceModel:
+    """Upload the seeded fp32 weights of `cfg` layer by layer and prepare them
+    on the GPU (ark_prep_weight); the fp32 copies are released as it goes."""
+    import torch
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+    out = []
+    for l in (range(cfg.n_layers) if layers is None else layers):
+        w = synth.layer_weights(cfg, l)
+        L = {"ln1": up(w["ln1"]), "ln2": up(w["ln2"])}
+        for name, key, bias in (("q", "wq", "bq"), ("k", "wk", "bk"), ("v", "wv", "bv"),
+                                ("o", "wo", None), ("gate", "wg", None), ("up", "wu", None),
+                                ("down", "wd", None)):
+            wt = up(w[key])
+            L[name] = QLinear.from_f32(wt, up(w[bias]) if bias else None, stream)
+            del wt
+        out.append(L)
+        del w
+    final_norm, lm = None, None
+    if cfg.lm_head:
+        final_norm = up(synth.final_norm(cfg))
+        codes = torch.empty((cfg.vocab, cfg.hidden), dtype=torch.int8, device=device)
+        scale = torch.empty(cfg.vocab, dtype=torch.float32, device=device)
+        colsum = torch.empty(cfg.vocab, dtype=torch.int32, device=device)
+        step = 16 * synth.ROW_CHUNK
+        for r0 in range(0, cfg.vocab, step):
+            r1 = min(cfg.vocab, r0 + step)
+            wt = up(synth.lm_head_rows(cfg, r0, r1))
+            c, s, cs = prep_weight(wt, stream)
+            codes[r0:r1].copy_(c)
+            scale[r0:r1].copy_(s)
+            colsum[r0:r1].copy_(cs)
+            del wt, c, s, cs
+        lm = QLinear(codes, scale, colsum)
+    emb = up(synth.embed_table_f16(cfg).view(np.int16))
+    rc, rs = rope_table(cfg.max_total_len, cfg.head_dim, cfg.rope_theta, device, stream)
+    torch.cuda.current_stream().synchronize()
+    return DeviceModel(cfg, out, final_norm, lm, emb, rc, rs)
+
+
+# ------------------------------------------------------------- the path --
+def workspace(model: DeviceModel, B: int, S: int):
+    import torch
+    n = workspace_bytes(model.dims, B, S)
+    if n == 0:
+        raise ArkError("ark_workspace_bytes", ARK_E_SHAPE, "invalid dims")
+    return torch.empty(n, dtype=torch.uint8, device="cuda")
+
+
+def embed_splice(dims: ArkDims, ids, table_f16, audio, a0: int, out, stream=None):
+    B, S = ids.shape
+    N = 0 if audio is None else audio.shape[1]
+    _check("ark_embed_splice", lib().ark_embed_splice(C.byref(dims), B, S, _ptr(ids), _ptr(table_f16),
+                                                       _ptr(audio), a0, N, _ptr(out), _stream(stream)))
+    return out
+
+
+def prefill(model: DeviceModel, embeds, cache_position, k_cache, v_cache, k_delta, v_delta,
+            logits=None, hidden_out=None, ws=None, stream=None):
+    B, S = embeds.shape[0], embeds.shape[1]
+    if ws is None:
+        ws = workspace(model, B, S)
+    _check("ark_prefill", lib().ark_prefill(
+        C.byref(model.c), B, S, _ptr(embeds), _pos_array(cache_position), _ptr_array(k_cache),
+        _ptr_array(v_cache), _ptr(k_delta), _ptr(v_delta), _ptr(logits), _ptr(hidden_out),
+        _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def decode_step(model: DeviceModel, token_ids, cache_position, k_cache, v_cache, k_delta, v_delta,
+                logits=None, hidden_out=None, ws=None, stream=None):
+    B = token_ids.shape[0]
+    if ws is None:
+        ws = workspace(model, B, 1)
+    _check("ark_decode_step", lib().ark_decode_step(
+        C.byref(model.c), B, _ptr(token_ids), _pos_array(cache_position), _ptr_array(k_cache),
+        _ptr_array(v_cache), _ptr(k_delta), _ptr(v_delta), _ptr(logits), _ptr(hidden_out),
+        _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def masked_argmax(logits, mask, out_ids, stream=None):
+    B, V = logits.shape
+    _check("ark_masked_argmax", lib().ark_masked_argmax(B, V, _ptr(logits), _ptr(mask), _ptr(out_ids),
+                                                         _stream(stream)))
+    return out_ids
+
+
+def cache_write(dims: ArkDims, cache_position, k_cache, v_cache, k_delta, v_delta, stream=None):
+    B, S = k_delta.shape[1], k_delta.shape[2]
+    _check("ark_cache_write", lib().ark_cache_write(
+        C.byref(dims), B, S, _pos_array(cache_position), _ptr_array(k_cache), _ptr_array(v_cache),
+        _ptr(k_delta), _ptr(v_delta), _stream(stream)))
+
+
+def greedy_decode(model: DeviceModel, token_ids, cache_position, k_cache, v_cache, k_delta,
+                  v_delta, logits, mask, end_id: int, max_steps: int, out_tokens, ws=None,
+                  check_every: int = 1, stream=None):
+    """Runs the native greedy loop; returns (steps, new cache positions)."""
+    B = token_ids.shape[0]
+    if ws is None:
+        ws = workspace(model, B, 1)
+    pos = _pos_array(cache_position)
+    n = _check("ark_greedy_decode", lib().ark_greedy_decode(
+        C.byref(model.c), B, _ptr(token_ids), pos, _ptr_array(k_cache), _ptr_array(v_cache),
+        _ptr(k_delta), _ptr(v_delta), _ptr(logits), _ptr(mask), end_id, max_steps, check_every,
+        _ptr(out_tokens), _ptr(ws), ws.numel(), _stream(stream)))
+    return n, np.array(pos[:], dtype=np.int32)
+
+
+def test_dynquant(x, stream=None):
+    """x [B][R][K] fp32 -> (codes uint8, scale [B], zp [B]) via the prefill kernels."""
+    import torch
+    B, R, K = x.shape
+    codes = torch.empty((B, R, K), dtype=torch.uint8, device=x.device)
+    scale = torch.empty(B, dtype=torch.float32, device=x.device)
+    zp = torch.empty(B, dtype=torch.int32, device=x.device)
+    ws = torch.empty(16 * B * (R + 1), dtype=torch.uint8, device=x.device)
+    _check("ark_test_dynquant", lib().ark_test_dynquant(B, R, K, _ptr(x), _ptr(codes), _ptr(scale),
+                                                         _ptr(zp), _ptr(ws), ws.numel(), _stream(stream)))
+    return codes, scale, zp
+
+
+def test_qlinear(codes, scale, zp, W: QLinear, use_gemm: bool, stream=None):
+    """codes [B][R][k] uint8, scale [B], zp [B] uint8 -> (acc int32, y fp32) [B*R][n]."""
+    import torch
+    B, R, k = codes.shape
+    n = W.codes.shape[0]
+    acc = torch.empty((B * R, n), dtype=torch.int32, device=codes.device)
+    y = torch.empty((B * R, n), dtype=torch.float32, device=codes.device)
+    ws = torch.empty(B * R * (k + 8) + 256, dtype=torch.uint8, device=codes.device)
+    wc = W.c()
+    _check("ark_test_qlinear", lib().ark_test_qlinear(B, R, _ptr(codes), _ptr(scale), _ptr(zp), C.byref(wc),
+                                                       _ptr(acc), _ptr(y), int(use_gemm), _ptr(ws),
+                                                       ws.numel(), _stream(stream)))
+    return acc, y

@@ -1,0 +1,430 @@
+// C ABI of the decoder step: host-side validation, workspace planning and
+// kernel sequencing.  Validation touches no HIP API, so every error path can
+// be exercised without a GPU; a call that fails validation enqueues nothing.
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "../../include/ark.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+using namespace ark;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+struct Plan {
+  size_t x, h, codes, qkv, q, attn, a, rmin, rmax, qs, qz, part, done, total;
+};
+
+Plan plan(const ark_dims& d, int B, int S) {
+  const size_t R = (size_t)B * S;
+  const size_t H = d.hidden, Q = (size_t)d.n_heads * d.head_dim;
+  const size_t KV = (size_t)d.n_kv_heads * d.head_dim, I = d.intermediate;
+  const size_t Kmax = std::max(std::max(H, Q), I);
+  Plan p;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align_up(bytes);
+    return at;
+  };
+  p.x = take(R * H * 4);
+  p.h = take(R * H * 4);
+  p.codes = take(R * Kmax);
+  p.qkv = take(R * (Q + 2 * KV) * 4);
+  p.q = take(R * Q * 4);
+  p.attn = take(R * Q * 4);
+  p.a = take(R * I * 4);
+  p.rmin = take(R * 4);
+  p.rmax = take(R * 4);
+  p.qs = take((size_t)std::max(B, 64) * 4);
+  p.qz = take((size_t)std::max(B, 64) * 4);
+  p.part = take(attention_ws_bytes(B, S, d.n_heads, d.max_total_len));
+  p.done = take((size_t)kMaxBatch * 4);
+  p.total = o;
+  return p;
+}
+
+bool dims_ok(const ark_dims& d) {
+  if (d.n_layers < 1 || d.n_layers > kMaxLayers) return false;
+  if (d.head_dim != kHeadDim) return false;
+  if (d.n_heads < 1 || d.n_kv_heads < 1 || d.n_heads % d.n_kv_heads) return false;
+  if (d.n_heads / d.n_kv_heads > 8) return false;
+  if (d.hidden < 256 || d.hidden % 256) return false;
+  if (d.intermediate < 64 || d.intermediate % 64) return false;
+  if (d.max_total_len < 32 || d.max_total_len % 32 || d.max_total_len > 8192) return false;
+  if (d.vocab < 1) return false;
+  if (!(d.rms_eps >= 0.0) || !(d.rope_theta > 0.0)) return false;
+  return true;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_qlinear(const ark_qlinear& q, int n, int k, bool bias_allowed) {
+  if (!q.w || !q.scale || !q.colsum) return ARK_E_NULL;
+  if (q.n != n || q.k != k) return ARK_E_SHAPE;
+  if (q.bias && !bias_allowed) return ARK_E_SHAPE;
+  if (!aligned(q.w, 16)) return ARK_E_ALIGN;
+  return ARK_OK;
+}
+
+int check_model(const ark_model* m, bool need_embed) {
+  if (!m) return ARK_E_NULL;
+  const ark_dims& d = m->d;
+  if (!dims_ok(d)) return ARK_E_SHAPE;
+  if (!m->layers || !m->rope_cos || !m->rope_sin) return ARK_E_NULL;
+  if (need_embed && !m->embed_f16) return ARK_E_NULL;
+  const int H = d.hidden, Q = d.n_heads * d.head_dim, KV = d.n_kv_heads * d.head_dim;
+  const int I = d.intermediate;
+  for (int l = 0; l < d.n_layers; ++l) {
+    const ark_layer& L = m->layers[l];
+    if (!L.ln1 || !L.ln2) return ARK_E_NULL;
+    int e;
+    if ((e = check_qlinear(L.q, Q, H, true))) return e;
+    if ((e = check_qlinear(L.k, KV, H, true))) return e;
+    if ((e = check_qlinear(L.v, KV, H, true))) return e;
+    if ((e = check_qlinear(L.o, H, Q, false))) return e;
+    if ((e = check_qlinear(L.gate, I, H, false))) return e;
+    if ((e = check_qlinear(L.up, I, H, false))) return e;
+    if ((e = check_qlinear(L.down, H, I, false))) return e;
+  }
+  if (m->lm_head.w) {
+    if (!m->final_norm) return ARK_E_NULL;
+    int e;
+    if ((e = check_qlinear(m->lm_head, d.vocab, H, false))) return e;
+  }
+  return ARK_OK;
+}
+
+int check_step(const ark_model* m, int B, int S, const int32_t* pos, const float* const* kc,
+               const float* const* vc, const float* kd, const float* vd, const float* logits,
+               const void* ws, size_t ws_bytes) {
+  if (B < 1 || B > kMaxBatch || S < 1) return ARK_E_SHAPE;
+  if (!pos || !kc || !vc || !kd || !vd || !ws) return ARK_E_NULL;
+  const ark_dims& d = m->d;
+  for (int l = 0; l < d.n_layers; ++l)
+    if (!kc[l] || !vc[l]) return ARK_E_NULL;
+  if (logits && !m->lm_head.w) return ARK_E_SHAPE;
+  for (int b = 0; b < B; ++b)
+    if (pos[b] < 0 || (int64_t)pos[b] + S > d.max_total_len) return ARK_E_RANGE;
+  if (!aligned(ws, kAlign) || !aligned(kd, 16) || !aligned(vd, 16)) return ARK_E_ALIGN;
+  for (int l = 0; l < d.n_layers; ++l)
+    if (!aligned(kc[l], 16) || !aligned(vc[l], 16)) return ARK_E_ALIGN;
+  if (ws_bytes < plan(d, B, S).total) return ARK_E_WORKSPACE;
+  return ARK_OK;
+}
+
+inline Seg seg_of(const ark_qlinear& q, float* out, int ldo) {
+  Seg s;
+  s.w = q.w;
+  s.sw = q.scale;
+  s.cs = q.colsum;
+  s.bias = q.bias;
+  s.n = q.n;
+  s.out = out;
+  s.ldo = ldo;
+  return s;
+}
+
+#define HIP_TRY(expr)                       \
+  do {                                      \
+    if ((expr) != hipSuccess) return ARK_E_HIP; \
+  } while (0)
+
+// All layers and the LM head over the rows already in x ([B*S][H]).
+int run_forward(const ark_model* m, int B, int S, float* x, const int32_t* pos_host,
+                const float* const* kc, const float* const* vc, float* kd, float* vd,
+                float* logits, char* ws, hipStream_t st) {
+  const ark_dims& d = m->d;
+  const Plan p = plan(d, B, S);
+  const int R = B * S, H = d.hidden, NH = d.n_heads, NKV = d.n_kv_heads;
+  const int Q = NH * kHeadDim, KV = NKV * kHeadDim, I = d.intermediate, T = d.max_total_len;
+  const bool gemv = (S == 1 && B <= 4);
+  float* h = (float*)(ws + p.h);
+  int8_t* codes = (int8_t*)(ws + p.codes);
+  float* qkv = (float*)(ws + p.qkv);
+  float* q = (float*)(ws + p.q);
+  float* attn = (float*)(ws + p.attn);
+  float* a = (float*)(ws + p.a);
+  float* rmin = (float*)(ws + p.rmin);
+  float* rmax = (float*)(ws + p.rmax);
+  float* qs = (float*)(ws + p.qs);
+  int* qz = (int*)(ws + p.qz);
+  void* part = ws + p.part;
+  PosArgs pos;
+  memset(&pos, 0, sizeof(pos));
+  for (int b = 0; b < B; ++b) pos.p[b] = pos_host[b];
+  const int ldqkv = Q + 2 * KV;
+
+  for (int l = 0; l < d.n_layers; ++l) {
+    const ark_layer& L = m->layers[l];
+    float* kdl = kd + (size_t)l * R * KV;
+    float* vdl = vd + (size_t)l * R * KV;
+    Seg qkvs[3] = {seg_of(L.q, qkv, ldqkv), seg_of(L.k, qkv + Q, ldqkv),
+                   seg_of(L.v, qkv + Q + KV, ldqkv)};
+    Seg os[1] = {seg_of(L.o, x, H)};
+    Seg gus[2] = {seg_of(L.gate, a, I), seg_of(L.up, a, I)};
+    Seg ds[1] = {seg_of(L.down, x, H)};
+    if (gemv) {
+      HIP_TRY(launch_gemv(st, B, H, x, H, L.ln1, d.rms_eps, qkvs, 3, EPI_STORE));
+    } else {
+      HIP_TRY(launch_rmsnorm_rows(st, R, H, x, H, L.ln1, d.rms_eps, h, rmin, rmax));
+      HIP_TRY(launch_quant_rows(st, B, S, H, h, rmin, rmax, codes, nullptr, qs, qz));
+      HIP_TRY(launch_gemm(st, R, H, codes, qs, qz, S, qkvs, 3, EPI_STORE, nullptr));
+    }
+    HIP_TRY(launch_rope(st, B, S, NH, NKV, qkv, m->rope_cos, m->rope_sin, pos, q, kdl, vdl));
+    HIP_TRY(launch_attention(st, B, S, NH, NKV, T, q, kc[l], vc[l], kdl, vdl, pos, attn, part));
+    if (gemv) {
+      HIP_TRY(launch_gemv(st, B, Q, attn, Q, nullptr, 0.0, os, 1, EPI_RESID));
+      HIP_TRY(launch_gemv(st, B, H, x, H, L.ln2, d.rms_eps, gus, 2, EPI_SWIGLU));
+      HIP_TRY(launch_gemv(st, B, I, a, I, nullptr, 0.0, ds, 1, EPI_RESID));
+    } else {
+      HIP_TRY(launch_rowminmax(st, R, Q, attn, rmin, rmax));
+      HIP_TRY(launch_quant_rows(st, B, S, Q, attn, rmin, rmax, codes, nullptr, qs, qz));
+      HIP_TRY(launch_gemm(st, R, Q, codes, qs, qz, S, os, 1, EPI_RESID, nullptr));
+      HIP_TRY(launch_rmsnorm_rows(st, R, H, x, H, L.ln2, d.rms_eps, h, rmin, rmax));
+      HIP_TRY(launch_quant_rows(st, B, S, H, h, rmin, rmax, codes, nullptr, qs, qz));
+      HIP_TRY(launch_gemm(st, R, H, codes, qs, qz, S, gus, 2, EPI_SWIGLU, nullptr));
+      HIP_TRY(launch_rowminmax(st, R, I, a, rmin, rmax));
+      HIP_TRY(launch_quant_rows(st, B, S, I, a, rmin, rmax, codes, nullptr, qs, qz));
+      HIP_TRY(launch_gemm(st, R, I, codes, qs, qz, S, ds, 1, EPI_RESID, nullptr));
+    }
+  }
+
+  if (logits) {
+    Seg lm[1] = {seg_of(m->lm_head, logits, d.vocab)};
+    const float* last = x + (size_t)(S - 1) * H;  // row S-1 of each sequence, stride S*H
+    if (B <= 4) {
+      HIP_TRY(launch_gemv(st, B, H, last, S * H, m->final_norm, d.rms_eps, lm, 1, EPI_STORE));
+    } else {
+      HIP_TRY(launch_rmsnorm_rows(st, B, H, last, S * H, m->final_norm, d.rms_eps, h, rmin, rmax));
+      HIP_TRY(launch_quant_rows(st, B, 1, H, h, rmin, rmax, codes, nullptr, qs, qz));
+      HIP_TRY(launch_gemm(st, B, H, codes, qs, qz, 1, lm, 1, EPI_STORE, nullptr));
+    }
+  }
+  return ARK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ark_status_string(int status) {
+  switch (status) {
+    case ARK_OK: return "ok";
+    case ARK_E_NULL: return "a required pointer is NULL";
+    case ARK_E_SHAPE: return "a size is invalid, inconsistent or unsupported";
+    case ARK_E_RANGE: return "cache_position out of range for the static cache";
+    case ARK_E_WORKSPACE: return "workspace too small";
+    case ARK_E_HIP: return "HIP launch failed";
+    case ARK_E_ALIGN: return "pointer misaligned";
+    default: return "unknown status";
+  }
+}
+
+size_t ark_workspace_bytes(const ark_dims* d, int32_t B, int32_t S) {
+  if (!d || !dims_ok(*d) || B < 1 || B > kMaxBatch || S < 1) return 0;
+  return plan(*d, B, S).total;
+}
+
+int ark_prep_weight(const float* w, int32_t n, int32_t k, int8_t* codes, float* scale,
+                    int32_t* colsum, void* stream) {
+  if (!w || !codes || !scale || !colsum) return ARK_E_NULL;
+  if (n < 1 || k < 16 || k % 16) return ARK_E_SHAPE;
+  return launch_prep_weight((hipStream_t)stream, w, n, k, codes, scale, colsum) == hipSuccess
+             ? ARK_OK
+             : ARK_E_HIP;
+}
+
+int ark_rope_table(int32_t T, int32_t head_dim, double theta, double* cos_out, double* sin_out,
+                   void* stream) {
+  if (!cos_out || !sin_out) return ARK_E_NULL;
+  if (T < 1 || head_dim < 2 || head_dim % 2 || !(theta > 0.0)) return ARK_E_SHAPE;
+  return launch_rope_table((hipStream_t)stream, T, head_dim, theta, cos_out, sin_out) == hipSuccess
+             ? ARK_OK
+             : ARK_E_HIP;
+}
+
+int ark_embed_splice(const ark_dims* d, int32_t B, int32_t S, const int32_t* ids,
+                     const uint16_t* embed_f16, const float* audio, int32_t a0, int32_t N,
+                     float* out, void* stream) {
+  if (!d || !ids || !embed_f16 || !out) return ARK_E_NULL;
+  if (B < 1 || S < 1 || d->hidden < 1 || d->vocab < 1) return ARK_E_SHAPE;
+  if (N < 0 || a0 < 0 || (int64_t)a0 + N > S) return ARK_E_SHAPE;
+  if ((N > 0) != (audio != nullptr)) return N > 0 ? ARK_E_NULL : ARK_E_SHAPE;
+  return launch_embed((hipStream_t)stream, B, S, d->hidden, d->vocab, ids, embed_f16, audio, a0,
+                      N, out) == hipSuccess
+             ? ARK_OK
+             : ARK_E_HIP;
+}
+
+int ark_prefill(const ark_model* m, int32_t B, int32_t S, const float* embeds,
+                const int32_t* cache_position, const float* const* k_cache,
+                const float* const* v_cache, float* k_delta, float* v_delta, float* logits,
+                float* hidden_out, void* workspace, size_t workspace_bytes, void* stream) {
+  int e = check_model(m, false);
+  if (e) return e;
+  if (!embeds) return ARK_E_NULL;
+  e = check_step(m, B, S, cache_position, k_cache, v_cache, k_delta, v_delta, logits, workspace,
+                 workspace_bytes);
+  if (e) return e;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const Plan p = plan(m->d, B, S);
+  float* x = hidden_out ? hidden_out : (float*)(ws + p.x);
+  const size_t xb = (size_t)B * S * m->d.hidden * 4;
+  if (hipMemcpyAsync(x, embeds, xb, hipMemcpyDeviceToDevice, st) != hipSuccess) return ARK_E_HIP;
+  return run_forward(m, B, S, x, cache_position, k_cache, v_cache, k_delta, v_delta, logits, ws,
+                     st);
+}
+
+int ark_decode_step(const ark_model* m, int32_t B, const int32_t* token_ids,
+                    const int32_t* cache_position, const float* const* k_cache,
+                    const float* const* v_cache, float* k_delta, float* v_delta, float* logits,
+                    float* hidden_out, void* workspace, size_t workspace_bytes, void* stream) {
+  int e = check_model(m, true);
+  if (e) return e;
+  if (!token_ids) return ARK_E_NULL;
+  e = check_step(m, B, 1, cache_position, k_cache, v_cache, k_delta, v_delta, logits, workspace,
+                 workspace_bytes);
+  if (e) return e;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const Plan p = plan(m->d, B, 1);
+  float* x = hidden_out ? hidden_out : (float*)(ws + p.x);
+  if (launch_embed(st, B, 1, m->d.hidden, m->d.vocab, token_ids, m->embed_f16, nullptr, 0, 0, x) !=
+      hipSuccess)
+    return ARK_E_HIP;
+  return run_forward(m, B, 1, x, cache_position, k_cache, v_cache, k_delta, v_delta, logits, ws,
+                     st);
+}
+
+int ark_masked_argmax(int32_t B, int32_t V, const float* logits, const uint8_t* mask,
+                      int32_t* out_ids, void* stream) {
+  if (!logits || !mask || !out_ids) return ARK_E_NULL;
+  if (B < 1 || V < 1) return ARK_E_SHAPE;
+  return launch_masked_argmax((hipStream_t)stream, B, V, logits, mask, out_ids) == hipSuccess
+             ? ARK_OK
+             : ARK_E_HIP;
+}
+
+int ark_cache_write(const ark_dims* d, int32_t B, int32_t S, const int32_t* cache_position,
+                    float* const* k_cache, float* const* v_cache, const float* k_delta,
+                    const float* v_delta, void* stream) {
+  if (!d || !cache_position || !k_cache || !v_cache || !k_delta || !v_delta) return ARK_E_NULL;
+  if (!dims_ok(*d) || B < 1 || B > kMaxBatch || S < 1) return ARK_E_SHAPE;
+  for (int l = 0; l < d->n_layers; ++l) {
+    if (!k_cache[l] || !v_cache[l]) return ARK_E_NULL;
+    if (!aligned(k_cache[l], 16) || !aligned(v_cache[l], 16)) return ARK_E_ALIGN;
+  }
+  if (!aligned(k_delta, 16) || !aligned(v_delta, 16)) return ARK_E_ALIGN;
+  for (int b = 0; b < B; ++b)
+    if (cache_position[b] < 0 || (int64_t)cache_position[b] + S > d->max_total_len)
+      return ARK_E_RANGE;
+  return launch_cache_write((hipStream_t)stream, d->n_layers, B, S, d->max_total_len,
+                            d->n_kv_heads * d->head_dim, cache_position, k_cache, v_cache,
+                            k_delta, v_delta) == hipSuccess
+             ? ARK_OK
+             : ARK_E_HIP;
+}
+
+int ark_greedy_decode(const ark_model* m, int32_t B, int32_t* token_ids, int32_t* cache_position,
+                      float* const* k_cache, float* const* v_cache, float* k_delta, float* v_delta,
+                      float* logits, const uint8_t* mask, int32_t end_id, int32_t max_steps,
+                      int32_t check_every, int32_t* out_tokens, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int e = check_model(m, true);
+  if (e) return e;
+  if (!token_ids || !logits || !mask || !out_tokens) return ARK_E_NULL;
+  if (!m->lm_head.w) return ARK_E_SHAPE;
+  if (max_steps < 0 || check_every < 1) return ARK_E_SHAPE;
+  e = check_step(m, B, 1, cache_position, (const float* const*)k_cache,
+                 (const float* const*)v_cache, k_delta, v_delta, logits, workspace,
+                 workspace_bytes);
+  if (e) return e;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const Plan p = plan(m->d, B, 1);
+  int32_t* done = (int32_t*)(ws + p.done);
+  if (hipMemsetAsync(done, 0, (size_t)kMaxBatch * 4, st) != hipSuccess) return ARK_E_HIP;
+  std::vector<int32_t> pos(cache_position, cache_position + B);
+  std::vector<int32_t> flags(B);
+  const int T = m->d.max_total_len;
+  int steps = 0;
+  for (int t = 0; t < max_steps; ++t) {
+    bool room = true;
+    for (int b = 0; b < B; ++b) room = room && pos[b] + 1 <= T;
+    if (!room) break;
+    e = ark_decode_step(m, B, token_ids, pos.data(), (const float* const*)k_cache,
+                        (const float* const*)v_cache, k_delta, v_delta, logits, nullptr, workspace,
+                        workspace_bytes, stream);
+    if (e) return e;
+    if (launch_masked_argmax(st, B, m->d.vocab, logits, mask, token_ids) != hipSuccess)
+      return ARK_E_HIP;
+    if (launch_greedy_post(st, B, token_ids, out_tokens + (size_t)t * B, end_id, done) !=
+        hipSuccess)
+      return ARK_E_HIP;
+    if (launch_cache_write(st, m->d.n_layers, B, 1, T, m->d.n_kv_heads * m->d.head_dim,
+                           pos.data(), k_cache, v_cache, k_delta, v_delta) != hipSuccess)
+      return ARK_E_HIP;
+    for (int b = 0; b < B; ++b) pos[b] += 1;
+    ++steps;
+    if ((t + 1) % check_every == 0 || t + 1 == max_steps) {
+      if (hipMemcpyAsync(flags.data(), done, (size_t)B * 4, hipMemcpyDeviceToHost, st) !=
+              hipSuccess ||
+          hipStreamSynchronize(st) != hipSuccess)
+        return ARK_E_HIP;
+      bool all = true;
+      for (int b = 0; b < B; ++b) all = all && flags[b];
+      if (all) break;
+    }
+  }
+  for (int b = 0; b < B; ++b) cache_position[b] = pos[b];
+  return steps;
+}
+
+int ark_test_dynquant(int32_t B, int32_t R, int32_t K, const float* x, uint8_t* codes,
+                      float* scale, int32_t* zp, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (!x || !codes || !scale || !zp || !workspace) return ARK_E_NULL;
+  if (B < 1 || R < 1 || K < 1) return ARK_E_SHAPE;
+  if (workspace_bytes < 16 * (size_t)B * (R + 1)) return ARK_E_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  float* rmin = (float*)workspace;
+  float* rmax = rmin + (size_t)B * R;
+  if (launch_rowminmax(st, B * R, K, x, rmin, rmax) != hipSuccess) return ARK_E_HIP;
+  if (launch_quant_rows(st, B, R, K, x, rmin, rmax, nullptr, codes, scale, zp) != hipSuccess)
+    return ARK_E_HIP;
+  return ARK_OK;
+}
+
+int ark_test_qlinear(int32_t B, int32_t R, const uint8_t* codes, const float* scale,
+                     const uint8_t* zp, const ark_qlinear* W, int32_t* acc, float* y,
+                     int32_t use_gemm, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!codes || !scale || !zp || !W || !y || !workspace) return ARK_E_NULL;
+  if (!W->w || !W->scale || !W->colsum) return ARK_E_NULL;
+  if (B < 1 || R < 1 || W->n < 1 || W->k < 64 || W->k % 64) return ARK_E_SHAPE;
+  const int rows = B * R;
+  if (!use_gemm && rows > 4) return ARK_E_SHAPE;
+  const size_t need = (size_t)rows * (W->k + 8) + 256;
+  if (workspace_bytes < need) return ARK_E_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  int8_t* sc = (int8_t*)ws;
+  float* srow = (float*)(ws + align_up((size_t)rows * W->k));
+  int* zrow = (int*)(srow + rows);
+  if (launch_test_codes(st, rows, W->k, R, codes, sc, scale, zp, srow, zrow) != hipSuccess)
+    return ARK_E_HIP;
+  Seg s = seg_of(*W, y, W->n);
+  hipError_t err = use_gemm ? launch_gemm(st, rows, W->k, sc, srow, zrow, 1, &s, 1, EPI_STORE, acc)
+                            : launch_gemv_codes(st, rows, W->k, sc, srow, zrow, &s, 1, EPI_STORE,
+                                                acc);
+  return err == hipSuccess ? ARK_OK : ARK_E_HIP;
+}
+
+}  // extern "C"

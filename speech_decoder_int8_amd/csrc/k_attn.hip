@@ -1,0 +1,266 @@
+// Rotary embedding and grouped-query attention over the static cache.
+//
+// Model card "ark-asr-3b-onnx", section "Shapes": 16 query heads share 2 KV
+// heads of dimension 128; the cache is [T, 2, 128] per sequence and layer and
+// every query attends over ALL T positions, masked beyond its own position.
+// Rows [p, p + S) come from this call's deltas, all other rows from the
+// cache; masked rows are removed by selection (their contents, even NaN,
+// never reach a result).  Scores, softmax and the weighted sum run in fp64.
+//
+// One workgroup serves the 8 query heads of one KV head, so each K/V chunk is
+// staged in LDS once for all of them.  Decode (S = 1) splits T across
+// workgroups and merges the partial softmax states in a second kernel.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ark {
+
+// ------------------------------------------------------------------ rope --
+__global__ __launch_bounds__(256) void k_rope(int S, int NH, int NKV, const float* __restrict__ qkv,
+                                              const double* __restrict__ cosT,
+                                              const double* __restrict__ sinT, PosArgs P,
+                                              float* __restrict__ q, float* __restrict__ kd,
+                                              float* __restrict__ vd) {
+  const int r = blockIdx.x;
+  const int b = r / S, i = r % S;
+  const int pos = P.p[b] + i;
+  const int ld = (NH + 2 * NKV) * kHeadDim;
+  const float* src = qkv + (size_t)r * ld;
+  for (int t = threadIdx.x; t < (NH + NKV) * 64; t += 256) {
+    const int head = t >> 6, j = t & 63;
+    const float* x = src + head * kHeadDim;
+    const double c = cosT[pos * 64 + j], s = sinT[pos * 64 + j];
+    const double x1 = x[j], x2 = x[j + 64];
+    const float o1 = (float)(x1 * c - x2 * s);
+    const float o2 = (float)(x2 * c + x1 * s);
+    float* dst = head < NH ? q + (size_t)r * NH * kHeadDim + head * kHeadDim
+                           : kd + (size_t)r * NKV * kHeadDim + (head - NH) * kHeadDim;
+    dst[j] = o1;
+    dst[j + 64] = o2;
+  }
+  const float* vs = src + (NH + NKV) * kHeadDim;
+  for (int e = threadIdx.x; e < NKV * kHeadDim; e += 256) vd[(size_t)r * NKV * kHeadDim + e] = vs[e];
+}
+
+hipError_t launch_rope(hipStream_t st, int B, int S, int NH, int NKV, const float* qkv,
+                       const double* cosT, const double* sinT, const PosArgs& pos, float* q,
+                       float* k_delta, float* v_delta) {
+  hipLaunchKernelGGL(k_rope, dim3(B * S), dim3(256), 0, st, S, NH, NKV, qkv, cosT, sinT, pos, q,
+                     k_delta, v_delta);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------- attention --
+struct AttnParams {
+  int B, S, NH, NKV, G, T;
+  const float* q;
+  const float* kc;
+  const float* vc;
+  const float* kd;
+  const float* vd;
+  PosArgs pos;
+  float* out;
+  int nsplit, tsplit;
+  double* part;  // [B][NH][S][nsplit][2 + 128]
+};
+
+constexpr int kPart = 2 + kHeadDim;
+
+template <int QT, int KC>
+__global__ __launch_bounds__(256) void k_attn(AttnParams P) {
+  constexpr int NQ = QT * 8;        // query vectors per workgroup (8 heads x QT rows)
+  constexpr int TPQ = 256 / NQ;     // threads per query vector
+  constexpr int KPT = KC / TPQ;     // scores per thread per chunk
+  constexpr int DPT = kHeadDim / TPQ;  // output dims per thread
+  static_assert(KPT >= 1 && DPT >= 1, "tile shape");
+  __shared__ __align__(16) float Qs[NQ][kHeadDim];
+  __shared__ __align__(16) float Ks[KC][kHeadDim];
+  __shared__ __align__(16) float Vs[KC][kHeadDim];
+  __shared__ double Ps[NQ][KC];
+
+  const int tid = threadIdx.x;
+  const int b = blockIdx.y / P.NKV, g = blockIdx.y % P.NKV;
+  const int qtile = blockIdx.x / P.nsplit, split = blockIdx.x % P.nsplit;
+  const int i0 = qtile * QT;
+  const int p = P.pos.p[b];
+  const int S = P.S, T = P.T, NH = P.NH, NKV = P.NKV;
+  const int qv = tid / TPQ, sub = tid % TPQ;
+  const int qi = qv >> 3, hh = qv & 7;
+  const bool active = hh < P.G && i0 + qi < S;
+  const int h = g * P.G + hh;
+  const int qpos = p + i0 + qi;  // absolute position of this query row
+
+  // stage the queries of this workgroup
+  for (int e = tid; e < NQ * kHeadDim; e += 256) {
+    const int v = e / kHeadDim, d = e % kHeadDim;
+    const int vqi = v >> 3, vhh = v & 7;
+    float val = 0.0f;
+    if (vhh < P.G && i0 + vqi < S)
+      val = P.q[((size_t)(b * S + i0 + vqi) * NH + g * P.G + vhh) * kHeadDim + d];
+    Qs[v][d] = val;
+  }
+
+  const double scale = 1.0 / sqrt((double)kHeadDim);
+  double m = -INFINITY, l = 0.0;
+  double o[DPT];
+#pragma unroll
+  for (int e = 0; e < DPT; ++e) o[e] = 0.0;
+
+  const int jbeg = split * P.tsplit, jend = min(T, jbeg + P.tsplit);
+  for (int j0 = jbeg; j0 < jend; j0 += KC) {
+    __syncthreads();
+    // K/V rows j0 .. j0 + KC - 1 (cache or this call's deltas)
+    for (int e = tid; e < KC * (kHeadDim / 4); e += 256) {
+      const int jj = e / (kHeadDim / 4), d4 = e % (kHeadDim / 4);
+      const int j = j0 + jj;
+      float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
+      if (j < jend) {
+        size_t off;
+        const float *ks, *vs;
+        if (j >= p && j < p + S) {
+          off = ((size_t)(b * S + (j - p)) * NKV + g) * kHeadDim;
+          ks = P.kd;
+          vs = P.vd;
+        } else {
+          off = ((size_t)(b * T + j) * NKV + g) * kHeadDim;
+          ks = P.kc;
+          vs = P.vc;
+        }
+        kv = ((const float4*)(ks + off))[d4];
+        vv = ((const float4*)(vs + off))[d4];
+      }
+      ((float4*)Ks[jj])[d4] = kv;
+      ((float4*)Vs[jj])[d4] = vv;
+    }
+    __syncthreads();
+
+    // scores of this thread's keys
+    double sc[KPT];
+    double cmax = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < KPT; ++t) {
+      const int jj = sub + t * TPQ;
+      const int j = j0 + jj;
+      double s = -INFINITY;
+      if (active && j < jend && j <= qpos) {
+        double dot = 0.0;
+#pragma unroll 8
+        for (int d = 0; d < kHeadDim; ++d) dot = fma((double)Qs[qv][d], (double)Ks[jj][d], dot);
+        s = dot * scale;
+      }
+      sc[t] = s;
+      cmax = fmax(cmax, s);
+    }
+#pragma unroll
+    for (int off = TPQ / 2; off > 0; off >>= 1) cmax = fmax(cmax, __shfl_xor(cmax, off, kWave));
+    const double mnew = fmax(m, cmax);
+    double alpha = 1.0, lsum = 0.0;
+    if (mnew != -INFINITY) {
+      alpha = (m == -INFINITY) ? 0.0 : exp(m - mnew);
+#pragma unroll
+      for (int t = 0; t < KPT; ++t) {
+        const double e = (sc[t] == -INFINITY) ? 0.0 : exp(sc[t] - mnew);
+        Ps[qv][sub + t * TPQ] = e;
+        lsum += e;
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < KPT; ++t) Ps[qv][sub + t * TPQ] = 0.0;
+    }
+#pragma unroll
+    for (int off = TPQ / 2; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off, kWave);
+    l = l * alpha + lsum;
+    m = mnew;
+    __syncthreads();
+
+    // weighted values (masked rows selected out, never multiplied)
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) o[e] *= alpha;
+    for (int jj = 0; jj < KC; ++jj) {
+      const double w = Ps[qv][jj];
+#pragma unroll
+      for (int e = 0; e < DPT; ++e) {
+        const double v = (double)Vs[jj][sub + e * TPQ];
+        o[e] = (w != 0.0) ? fma(w, v, o[e]) : o[e];
+      }
+    }
+  }
+
+  if (!active) return;
+  const int row = b * S + i0 + qi;
+  if (P.nsplit == 1) {
+    float* dst = P.out + ((size_t)row * NH + h) * kHeadDim;
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) dst[sub + e * TPQ] = (float)(o[e] / l);
+  } else {
+    double* dst = P.part + ((((size_t)b * NH + h) * S + i0 + qi) * P.nsplit + split) * kPart;
+    if (sub == 0) {
+      dst[0] = m;
+      dst[1] = l;
+    }
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) dst[2 + sub + e * TPQ] = o[e];
+  }
+}
+
+// Merge the split partial softmax states of one (sequence, head, row).
+__global__ __launch_bounds__(128) void k_attn_combine(int S, int NH, int nsplit,
+                                                      const double* __restrict__ part,
+                                                      float* __restrict__ out) {
+  const int idx = blockIdx.x;  // (b * NH + h) * S + i
+  const int i = idx % S, h = (idx / S) % NH, b = idx / (S * NH);
+  const double* src = part + (size_t)idx * nsplit * kPart;
+  double M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmax(M, src[s * kPart]);
+  double L = 0.0, O = 0.0;
+  const int d = threadIdx.x;
+  for (int s = 0; s < nsplit; ++s) {
+    const double ms = src[s * kPart];
+    if (ms == -INFINITY) continue;
+    const double w = exp(ms - M);
+    L += src[s * kPart + 1] * w;
+    O += src[s * kPart + 2 + d] * w;
+  }
+  out[((size_t)(b * S + i) * NH + h) * kHeadDim + d] = (float)(O / L);
+}
+
+static int decode_split(int T) { return T / 32; }
+
+size_t attention_ws_bytes(int B, int S, int NH, int T) {
+  if (S != 1) return 0;
+  return (size_t)B * NH * decode_split(T) * kPart * sizeof(double);
+}
+
+hipError_t launch_attention(hipStream_t st, int B, int S, int NH, int NKV, int T, const float* q,
+                            const float* k_cache, const float* v_cache, const float* k_delta,
+                            const float* v_delta, const PosArgs& pos, float* out, void* ws) {
+  AttnParams P;
+  P.B = B;
+  P.S = S;
+  P.NH = NH;
+  P.NKV = NKV;
+  P.G = NH / NKV;
+  P.T = T;
+  P.q = q;
+  P.kc = k_cache;
+  P.vc = v_cache;
+  P.kd = k_delta;
+  P.vd = v_delta;
+  P.pos = pos;
+  P.out = out;
+  P.part = (double*)ws;
+  if (S == 1) {
+    P.nsplit = decode_split(T);
+    P.tsplit = 32;
+    hipLaunchKernelGGL((k_attn<1, 32>), dim3(P.nsplit, B * NKV), dim3(256), 0, st, P);
+    hipLaunchKernelGGL(k_attn_combine, dim3(B * NH), dim3(128), 0, st, 1, NH, P.nsplit, P.part,
+                       out);
+  } else {
+    P.nsplit = 1;
+    P.tsplit = T;
+    hipLaunchKernelGGL((k_attn<8, 16>), dim3((S + 7) / 8, B * NKV), dim3(256), 0, st, P);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ark

@@ -1,0 +1,87 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ark {
+
+// One int8 projection with its output: rows of the projection go to
+// out[r * ldo + n] (n < m.n).
+struct Seg {
+  const int8_t* w;
+  const float* sw;
+  const int32_t* cs;
+  const float* bias;
+  int n;
+  float* out;
+  int ldo;
+};
+
+enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+
+// ---- prep / misc (k_misc.hip)
+hipError_t launch_prep_weight(hipStream_t st, const float* w, int n, int k, int8_t* codes,
+                              float* scale, int32_t* colsum);
+hipError_t launch_rope_table(hipStream_t st, int T, int D, double theta, double* c, double* s);
+hipError_t launch_embed(hipStream_t st, int B, int S, int H, int V, const int32_t* ids,
+                        const uint16_t* table, const float* audio, int a0, int N, float* out);
+hipError_t launch_masked_argmax(hipStream_t st, int B, int V, const float* logits,
+                                const uint8_t* mask, int32_t* out_ids);
+hipError_t launch_test_codes(hipStream_t st, int rows, int K, int R, const uint8_t* in,
+                             int8_t* out, const float* s_in, const uint8_t* z_in, float* s_row,
+                             int* z_row);
+constexpr int kMaxLayers = 64;
+constexpr int kMaxBatch = 64;
+hipError_t launch_cache_write(hipStream_t st, int L, int B, int S, int T, int row_floats,
+                              const int32_t* pos_host, float* const* k_cache,
+                              float* const* v_cache, const float* k_delta, const float* v_delta);
+// Greedy-loop bookkeeping: tokens of finished sequences become end_id, the
+// step's ids are copied to out_row, and done flags are updated.
+hipError_t launch_greedy_post(hipStream_t st, int B, int32_t* tokens, int32_t* out_row,
+                              int32_t end_id, int32_t* done);
+
+// ---- quantisation (k_quant.hip)
+// h[r] = rmsnorm(x[r]) (fp64 inside), plus per-row min/max of h.
+hipError_t launch_rmsnorm_rows(hipStream_t st, int R, int H, const float* x, int ldx,
+                               const float* gain, double eps, float* h, float* rmin, float* rmax);
+hipError_t launch_rowminmax(hipStream_t st, int R, int K, const float* x, float* rmin, float* rmax);
+// Rows r of sequence b = r / S share one (s, z) from the min/max of all their
+// rows; writes shifted codes (code - 128) and, if non-null, plain uint8 codes.
+hipError_t launch_quant_rows(hipStream_t st, int B, int S, int K, const float* x,
+                             const float* rmin, const float* rmax, int8_t* codes,
+                             uint8_t* codes_u8, float* s_out, int* z_out);
+
+// ---- int8 projections
+// Decode GEMV (k_gemv.hip): B <= 4 rows of input x (row stride ldx), fused
+// prologue (RMSNorm when gain != nullptr, then per-row quantisation), segments
+// concatenated along the output dimension (EPI_SWIGLU: seg[0] gate, seg[1] up,
+// result to seg[0].out).  acc_out (optional) receives raw int32 accumulators.
+hipError_t launch_gemv(hipStream_t st, int B, int K, const float* x, int ldx, const float* gain,
+                       double eps, const Seg* segs, int nseg, Epi epi);
+// Same GEMV on precomputed shifted codes [B][K] with per-row (s, z).
+hipError_t launch_gemv_codes(hipStream_t st, int B, int K, const int8_t* codes, const float* s,
+                             const int* z, const Seg* segs, int nseg, Epi epi, int32_t* acc_out);
+// MFMA GEMM (k_gemm.hip): shifted codes [M][K]; row r uses (s[r / rows_per_seq],
+// z[r / rows_per_seq]).
+hipError_t launch_gemm(hipStream_t st, int M, int K, const int8_t* codes, const float* s,
+                       const int* z, int rows_per_seq, const Seg* segs, int nseg, Epi epi,
+                       int32_t* acc_out);
+
+// ---- rotary + attention (k_attn.hip)
+// qkv_raw [R][q_dim + 2*kv_dim] (bias added) -> q_rot [R][q_dim], k_delta /
+// v_delta [R][kv_dim]; row r of sequence r / S sits at pos[r / S] + r % S.
+struct PosArgs {
+  int32_t p[64];
+};
+hipError_t launch_rope(hipStream_t st, int B, int S, int NH, int NKV, const float* qkv,
+                       const double* cosT, const double* sinT, const PosArgs& pos, float* q,
+                       float* k_delta, float* v_delta);
+// Full-cache GQA attention.  out [B*S][NH*128] fp32.  ws: scratch for split
+// partials (decode); attention_ws_bytes gives its size.
+size_t attention_ws_bytes(int B, int S, int NH, int T);
+hipError_t launch_attention(hipStream_t st, int B, int S, int NH, int NKV, int T, const float* q,
+                            const float* k_cache, const float* v_cache, const float* k_delta,
+                            const float* v_delta, const PosArgs& pos, float* out, void* ws);
+
+}  // namespace ark

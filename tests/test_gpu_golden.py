@@ -1,0 +1,92 @@
+"""Full-size parity of the 36-layer decoder against stored oracle outputs.
+
+tests/golden/<config>.npz is written by tests/golden/make_golden.py, which
+calls only the CPU oracle.  The GPU runs the same seeded workload through the
+C ABI, fed with the oracle's tokens (teacher forcing), and is compared at
+every step on sampled logits, the last row's hidden state and sampled delta
+rows (1e-3 relative), and on the greedy id (exact, or a documented near tie).
+"""
+import os
+
+import numpy as np
+import pytest
+
+import synth
+
+torch = pytest.importorskip("torch")
+from speech_decoder_int8_amd import ark  # noqa: E402
+
+from gpu_util import TOL, GpuState, host, rel, t  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _golden(name):
+    path = os.path.join(HERE, "golden", f"{name}.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated")
+    return dict(np.load(path))
+
+
+def _check(g, step, gs, kd, vd, hid, mask, near_ties):
+    k = step - int(g.get("top_vals_from", 0))
+    lg = host(gs.logits)
+    scale = float(np.max(np.abs(g["top_vals"][k])))
+    samp = lg[:, g["samp_idx"]]
+    err = np.max(np.abs(samp - g["samp_vals"][k])) / scale
+    top = np.take_along_axis(lg, g["top_ids"][k].astype(np.int64), axis=1)
+    err = max(err, np.max(np.abs(top - g["top_vals"][k])) / scale)
+    assert err <= TOL, f"step {step}: logits relative error {err:.3g}"
+    r = rel(host(hid)[:, -1, :], g["hid_last"][k])
+    assert r <= TOL, f"step {step}: hidden relative error {r:.3g}"
+    rows = g[f"rows_s{step}"]
+    for l in g["layers"]:
+        for nm, d in (("kd", kd), ("vd", vd)):
+            r = rel(host(d[int(l)])[:, rows], g[f"{nm}_s{step}_l{int(l)}"])
+            assert r <= TOL, f"step {step}: {nm} layer {l} relative error {r:.3g}"
+    tok = np.where(mask[None, :] == 1, -np.inf, lg).argmax(axis=1)
+    want = g["tokens"][step]
+    for b in np.nonzero(tok != want)[0]:
+        gap = float(g["gap"][k][b])
+        assert gap <= 2 * err * scale, f"step {step} seq {b}: token {tok[b]} != {want[b]}, gap {gap:.3g}"
+        near_ties.append((step, int(b), gap))
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c4_t1024"])
+def test_full_size_against_golden(name):
+    g = _golden(name)
+    cfg = synth.CONFIGS[name]
+    gm = ark.load_model(cfg, synth)
+    B, L = cfg.batch, cfg.n_layers
+    mask = cfg.mask()
+    gs = GpuState(gm, B, max(1, cfg.prefill_len))
+    near = []
+    if cfg.prefill_len:
+        if cfg.prefill_from_embeds:
+            x = t(synth.prefill_embeds(cfg))
+        else:
+            x = torch.empty((B, cfg.prefill_len, cfg.hidden), dtype=torch.float32, device="cuda")
+            ark.embed_splice(gm.dims, t(synth.prompt_ids(cfg)), gm.embed_f16,
+                             t(synth.audio_rows(cfg)), cfg.audio_offset, x)
+        p = np.zeros(B, np.int64)
+        kd, vd, hid = gs.prefill(x, p)
+        _check(g, 0, gs, kd, vd, hid, mask, near)
+        gs.write_back(p, kd, vd)
+        p = p + cfg.prefill_len
+        del x
+    else:
+        lengths = synth.cache_lengths(cfg)
+        for l in range(L):
+            gs.kc[l].copy_(t(synth.prefilled_cache(cfg, l, "k", lengths)))
+            gs.vc[l].copy_(t(synth.prefilled_cache(cfg, l, "v", lengths)))
+        p = lengths.astype(np.int64)
+    for step in range(1, cfg.n_decode + 1):
+        ids = t(g["tokens"][step - 1].astype(np.int32))
+        kd, vd, hid = gs.decode(ids, p)
+        _check(g, step, gs, kd, vd, hid, mask, near)
+        gs.write_back(p, kd, vd)
+        p = p + 1
+    print(f"{name}: {cfg.n_decode + (1 if cfg.prefill_len else 0)} steps, near ties: {near}")
+    del gs, gm
+    torch.cuda.empty_cache()

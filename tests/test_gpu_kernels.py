@@ -1,0 +1,138 @@
+"""Kernel-level parity of the HIP path against the CPU oracle (GPU only).
+
+Integer, byte and index work is compared bit for bit; fp64 tables within a
+few ulps.  Every call goes through the C ABI (libark.so) via the binding.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+from speech_decoder_int8_amd import ark  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def t(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(x):
+    torch.cuda.synchronize()
+    return x.cpu().numpy()
+
+
+@pytest.mark.parametrize("n,k", [(37, 64), (300, 2048), (129, 11008)])
+def test_prep_weight_bit_exact(n, k):
+    rng = np.random.default_rng(n * 31 + k)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    w[3] = 0.0                                   # a zero row
+    w[5, 7] = 0.5                                # a dominant element
+    codes, scale, colsum = ark.prep_weight(t(w))
+    qo, so = oracle.prep_weight(w)
+    assert np.array_equal(host(codes), qo)
+    assert np.array_equal(host(scale), so)
+    assert np.array_equal(host(colsum), qo.astype(np.int64).sum(1).astype(np.int32))
+
+
+def test_rope_table_matches_oracle():
+    for T, theta in ((512, 1e6), (1024, 1e6), (64, 1e4)):
+        c, s = ark.rope_table(T, 128, theta)
+        co, so = oracle.rope_tables(T, 128, theta)
+        assert np.allclose(host(c), co, rtol=0, atol=4e-16 * np.maximum(1, np.arange(T))[:, None])
+        assert np.allclose(host(s), so, rtol=0, atol=4e-16 * np.maximum(1, np.arange(T))[:, None])
+
+
+@pytest.mark.parametrize("B,R,K", [(1, 1, 2048), (3, 7, 2048), (2, 49, 11008), (1, 5, 300)])
+def test_dynquant_bit_exact(B, R, K):
+    rng = np.random.default_rng(B * 100 + R)
+    x = (rng.standard_normal((B, R, K)) * rng.uniform(0.1, 5, (B, 1, 1))).astype(np.float32)
+    if B > 1:
+        x[1] = np.abs(x[1])                      # a tensor with no negative value
+    x[0, 0, :3] = 0.0
+    codes, scale, zp = ark.test_dynquant(t(x))
+    codes, scale, zp = host(codes), host(scale), host(zp)
+    for b in range(B):
+        qo, so, zo = oracle.dynquant(x[b])
+        assert np.array_equal(codes[b], qo) and scale[b] == so and zp[b] == int(zo)
+
+
+def test_dynquant_all_zero_tensor():
+    x = np.zeros((1, 2, 256), np.float32)
+    codes, scale, zp = ark.test_dynquant(t(x))
+    assert not host(codes).any() and host(scale)[0] == 0 and host(zp)[0] == 0
+
+
+@pytest.mark.parametrize("use_gemm", [False, True])
+@pytest.mark.parametrize("B,R,n,k", [(1, 1, 300, 2048), (2, 2, 2560, 2048), (1, 3, 96, 11008),
+                                     (3, 67, 333, 2048), (2, 16, 130, 1024)])
+def test_qlinear_bit_exact(use_gemm, B, R, n, k):
+    if not use_gemm and B * R > 4:
+        pytest.skip("the decode GEMV takes at most 4 rows")
+    rng = np.random.default_rng(n + k + B * R)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    bias = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    codes = rng.integers(0, 256, (B, R, k)).astype(np.uint8)
+    codes[0, 0, :] = 255                           # extreme accumulators
+    scale = rng.uniform(0.001, 0.05, B).astype(np.float32)
+    zp = rng.integers(0, 256, B).astype(np.uint8)
+    zp[0] = 0
+    W = ark.QLinear.from_f32(t(w), t(bias))
+    acc, y = ark.test_qlinear(t(codes), t(scale), t(zp), W, use_gemm)
+    qw, sw = oracle.prep_weight(w)
+    for b in range(B):
+        acc_o = oracle.matmul_integer(codes[b], zp[b], qw)
+        y_o = oracle.dequant(acc_o, scale[b], sw, bias)
+        assert np.array_equal(host(acc)[b * R:(b + 1) * R], acc_o.astype(np.int32))
+        assert np.array_equal(host(y)[b * R:(b + 1) * R], y_o)
+
+
+def test_masked_argmax_bit_exact_and_forced_cases():
+    V = 151936
+    mask = synth.CONFIGS["c1"].mask()
+    rng = np.random.default_rng(5)
+    lg = rng.standard_normal((6, V)).astype(np.float32)
+    lg[0, V - 1] = 50.0                              # masked raw maximum
+    lg[1, synth.CONFIGS["c1"].end_id] = 50.0         # the end id may win
+    lg[2, 100] = lg[2, 7] = 60.0                     # tie -> lowest id
+    lg[3, :] = np.nan
+    lg[3, 12345] = -1.0                              # NaN never chosen
+    lg[4, :V - 64] = np.nan                          # only masked/end ids left
+    lg[5, :] = -np.inf
+    out = torch.empty(6, dtype=torch.int32, device=DEV)
+    ark.masked_argmax(t(lg), t(mask), out)
+    assert host(out).tolist() == oracle.masked_argmax(lg, mask).tolist()
+    assert host(out).tolist()[:5] == [int(np.argmax(np.where(mask == 1, -np.inf, lg[0]))),
+                                      synth.CONFIGS["c1"].end_id, 7, 12345,
+                                      synth.CONFIGS["c1"].end_id]
+
+
+def test_cache_write_bit_exact():
+    cfg = synth.SMALL.with_(batch=3)
+    rng = np.random.default_rng(6)
+    L, B, T, S = cfg.n_layers, 3, cfg.max_total_len, 5
+    kc = [rng.standard_normal((B, T, 2, 128)).astype(np.float32) for _ in range(L)]
+    vc = [rng.standard_normal((B, T, 2, 128)).astype(np.float32) for _ in range(L)]
+    kd = rng.standard_normal((L, B, S, 2, 128)).astype(np.float32)
+    vd = rng.standard_normal((L, B, S, 2, 128)).astype(np.float32)
+    pos = [0, 17, T - S]
+    gk, gv = [t(c) for c in kc], [t(c) for c in vc]
+    ark.cache_write(ark.dims_of(cfg), pos, gk, gv, t(kd), t(vd))
+    for l in range(L):
+        assert np.array_equal(host(gk[l]), oracle.cache_write(kc[l], kd[l], pos))
+        assert np.array_equal(host(gv[l]), oracle.cache_write(vc[l], vd[l], pos))
+
+
+def test_embed_splice_bit_exact():
+    cfg = synth.SMALL.with_(batch=2)
+    table = synth.embed_table_f16(cfg)
+    ids = synth.prompt_ids(cfg)
+    audio = synth.audio_rows(cfg)
+    out = torch.empty((2, cfg.prefill_len, cfg.hidden), dtype=torch.float32, device=DEV)
+    ark.embed_splice(ark.dims_of(cfg), t(ids), t(table.view(np.int16)), t(audio),
+                     cfg.audio_offset, out)
+    assert np.array_equal(host(out), oracle.embed_splice(table, ids, audio, cfg.audio_offset))
