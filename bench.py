@@ -1,0 +1,337 @@
+#!/usr/bin/env python3
+"""Throughput of the ARK-ASR-3B int8 decoder step on one MI355X.
+
+Headline (`value`): greedy decode tokens/s at batch 1 on the 3 s-clip
+workload: the full 36-layer decoder (hidden 2048, 16/2 heads x 128, FFN
+11008, int8 LM head over 151936 ids, static cache T = 512) after the
+49-row prompt prefill.  One step is one greedy token: embedding gather,
+36 layers, LM head, masked argmax and the cache write-back, run by the
+library's native loop.  Inputs and weights are seeded synthetic data
+(random-init weights of that architecture), resident in HBM before timing.
+
+Extra figures on the same JSON line: prompt prefill tokens/s, batch-32
+decode, the coalesced 16 x 387 prefill at T = 512 and 1024, and the
+T = 512 vs 1024 decode cost.  `roofline` is the dominant decode kernel,
+timed live with HIP events around each of its launches inside the timed
+region; `cpu_baseline` is the CPU oracle on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM = 8.0e12        # MI355X HBM3E, bytes/s
+PEAK_INT8 = 5.0e15       # MI355X dense int8 MFMA, ops/s
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------- work per unit --
+def decode_bytes(cfg, B: int) -> int:
+    """Algorithmic HBM bytes of one decode step of B sequences: every int8
+    weight and fp32 scale/bias/gain once, the full static cache of every
+    sequence (keys and values, all T rows), the new K/V rows, the fp16
+    embedding rows and the fp32 logits."""
+    L, H, I, V, T = cfg.n_layers, cfg.hidden, cfg.intermediate, cfg.vocab, cfg.max_total_len
+    Q, KV = cfg.q_dim, cfg.kv_dim
+    w8 = L * (Q * H + 2 * KV * H + H * Q + 3 * I * H) + V * H
+    scales = (L * (Q + 2 * KV + H + 2 * I + H) + V) * 4
+    bias = L * (Q + 2 * KV) * 4
+    gains = (L * 2 * H + H) * 4
+    kv = B * L * 2 * T * KV * 4
+    deltas = B * L * 2 * KV * 4
+    return w8 + scales + bias + gains + kv + deltas + B * H * 2 + B * V * 4
+
+
+def gateup_bytes(cfg, B: int) -> int:
+    """Algorithmic bytes of one gate/up launch at batch B: both int8
+    matrices and their scales, the input rows and gain, the SwiGLU output."""
+    H, I = cfg.hidden, cfg.intermediate
+    return 2 * I * H + 2 * I * 4 + B * H * 4 + H * 4 + B * I * 4
+
+
+def prefill_int8_ops(cfg, R: int, B: int) -> int:
+    """int8 multiply-add ops (2 per MAC) of a prefill of R rows in B sequences."""
+    L, H, I, V = cfg.n_layers, cfg.hidden, cfg.intermediate, cfg.vocab
+    Q, KV = cfg.q_dim, cfg.kv_dim
+    return 2 * R * L * (Q * H + 2 * KV * H + H * Q + 3 * I * H) + 2 * B * V * H
+
+
+# ------------------------------------------------------------ GPU driver --
+class Run:
+    def __init__(self, torch, ark, model, B, S_max):
+        cfg = model.cfg
+        self.torch, self.ark, self.model, self.B = torch, ark, model, B
+        shape = (B, cfg.max_total_len, cfg.n_kv_heads, cfg.head_dim)
+        self.kc = [torch.zeros(shape, dtype=torch.float32, device="cuda") for _ in range(cfg.n_layers)]
+        self.vc = [torch.zeros(shape, dtype=torch.float32, device="cuda") for _ in range(cfg.n_layers)]
+        self.kd = torch.empty((cfg.n_layers, B, S_max, cfg.n_kv_heads, cfg.head_dim), device="cuda")
+        self.vd = torch.empty_like(self.kd)
+        self.kd1 = torch.empty((cfg.n_layers, B, 1, cfg.n_kv_heads, cfg.head_dim), device="cuda")
+        self.vd1 = torch.empty_like(self.kd1)
+        self.logits = torch.empty((B, cfg.vocab), device="cuda")
+        self.ws = ark.workspace(model, B, S_max)
+        self.ws1 = ark.workspace(model, B, 1)
+        self.mask = torch.from_numpy(cfg.mask()).cuda()
+        self.tok = torch.zeros(B, dtype=torch.int32, device="cuda")
+
+    def prefill(self, x, pos):
+        self.ark.prefill(self.model, x, pos, self.kc, self.vc, self.kd, self.vd, self.logits, None,
+                         self.ws)
+
+    def greedy(self, pos0: int, steps: int, out):
+        """`steps` greedy tokens from position pos0 (wrapping back to pos0
+        whenever the static cache would overflow; the cost of a step does
+        not depend on its position because every step attends all T rows)."""
+        T = self.model.cfg.max_total_len
+        done = 0
+        while done < steps:
+            n = min(steps - done, T - pos0)
+            got, _ = self.ark.greedy_decode(self.model, self.tok, [pos0] * self.B, self.kc, self.vc,
+                                            self.kd1, self.vd1, self.logits, self.mask, -1, n, out,
+                                            ws=self.ws1, check_every=n)
+            assert got == n, (got, n)
+            done += n
+
+
+def timed(torch, fn, reps=1):
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / reps
+
+
+def gpu_bench(args):
+    import numpy as np
+    import torch
+
+    import synth
+    from speech_decoder_int8_amd import ark
+
+    ark.lib()                                   # fails loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+    cfg = synth.CONFIGS["c1"]
+    log("loading the 36-layer model (seeded weights, quantised on the GPU)")
+    t0 = time.perf_counter()
+    gm = ark.load_model(cfg, synth)
+    log(f"model ready in {time.perf_counter() - t0:.1f}s")
+    S = cfg.prefill_len
+    run = Run(torch, ark, gm, 1, S)
+    x = torch.empty((1, S, cfg.hidden), dtype=torch.float32, device="cuda")
+    ark.embed_splice(gm.dims, torch.from_numpy(synth.prompt_ids(cfg)).cuda(), gm.embed_f16,
+                     torch.from_numpy(synth.audio_rows(cfg)).cuda(), cfg.audio_offset, x)
+    run.prefill(x, [0])
+    ark.cache_write(gm.dims, [0], run.kc, run.vc, run.kd, run.vd)
+    ark.masked_argmax(run.logits, run.mask, run.tok)
+    torch.cuda.synchronize()
+
+    K, W = args.steps, args.warmup
+    out = torch.empty((max(K, W, 1), 1), dtype=torch.int32, device="cuda")
+    pos0 = S + W if S + W + K <= cfg.max_total_len else S
+    if W:
+        run.greedy(S, W, out)
+    log(f"timing {K} decode steps")
+    launches_per_step = cfg.n_layers
+    ev = ark.HipEvents(K * launches_per_step)
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev.arm()
+    t0 = time.perf_counter()
+    e0.record(st)
+    run.greedy(pos0, K, out)
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev.disarm()
+    durs = ev.durations_ms()
+    ev.close()
+    gpu_ms = e0.elapsed_time(e1)
+    ms_step = wall * 1e3 / K
+    tok_s = K / wall
+    kern_ms = float(np.mean(durs)) if durs else float("nan")
+    gb = gateup_bytes(cfg, 1)
+    achieved = gb / (kern_ms * 1e-3) if durs else float("nan")
+    result = {
+        "metric": "decode tokens/s (bs1, bs32) + prefill tokens/s; % HBM / int8-MFMA roofline",
+        "value": round(tok_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": "c1: 36-layer ARK-ASR-3B int8 decoder, batch 1 greedy decode after a "
+                        "49-row prompt prefill (3 s clip), static cache T=512, int8 LM head 151936",
+            "batch": 1, "prefill_len": S, "max_total_len": cfg.max_total_len,
+            "hidden": cfg.hidden, "layers": cfg.n_layers, "heads": f"{cfg.n_heads}q/{cfg.n_kv_heads}kv x {cfg.head_dim}",
+            "intermediate": cfg.intermediate, "vocab": cfg.vocab,
+        },
+        "step_hbm": {
+            "algorithmic_bytes_per_step": decode_bytes(cfg, 1),
+            "gpu_event_ms_per_step": round(gpu_ms / K, 4),
+            "achieved_GBps": round(decode_bytes(cfg, 1) / (wall / K) / 1e9, 1),
+            "frac_of_8TBps": round(decode_bytes(cfg, 1) / (wall / K) / PEAK_HBM, 4),
+        },
+        "roofline": {
+            "kernel": ark.dominant_kernel(),
+            "bound": "hbm",
+            "achieved": round(achieved / 1e9, 1),
+            "peak": PEAK_HBM / 1e9,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM, 4),
+            "traffic": None,
+            "bytes_per_launch": gb,
+            "avg_launch_us": round(kern_ms * 1e3, 3),
+            "launches_timed": len(durs),
+        },
+    }
+    log(f"decode bs1: {tok_s:.1f} tok/s, {ms_step:.3f} ms/step; dominant kernel {kern_ms * 1e3:.2f} us")
+
+    if args.extras:
+        ex = {}
+        # prompt prefill of the 3 s clip
+        t = timed(torch, lambda: run.prefill(x, [0]), reps=5)
+        ex["prefill_c1_tok_s"] = round(S / t, 1)
+        ex["prefill_c1_ms"] = round(t * 1e3, 3)
+        del run
+        torch.cuda.empty_cache()
+        # batch-32 decode from pre-filled caches of valid length U[50, 400]
+        c3 = synth.CONFIGS["c3"]
+        r32 = Run(torch, ark, gm, c3.batch, 1)
+        lengths = synth.cache_lengths(c3)
+        for l in range(cfg.n_layers):
+            r32.kc[l].normal_()
+            r32.vc[l].normal_()
+        r32.tok.copy_(torch.from_numpy(synth.start_ids(c3)).cuda())
+        steps32 = 16
+        out32 = torch.empty((steps32, c3.batch), dtype=torch.int32, device="cuda")
+        p0 = int(lengths.max())
+
+        def dec32():
+            r32.greedy(p0, steps32, out32)
+        dec32()
+        t = timed(torch, dec32)
+        ex["decode_bs32_tok_s"] = round(c3.batch * steps32 / t, 1)
+        ex["decode_bs32_ms_per_step"] = round(t * 1e3 / steps32, 3)
+        ex["decode_bs32_frac_of_8TBps"] = round(decode_bytes(cfg, c3.batch) / (t / steps32) / PEAK_HBM, 4)
+        del r32
+        torch.cuda.empty_cache()
+        # coalesced prefill 16 x 387 and batch-16 decode at T = 512 and 1024
+        c4 = synth.CONFIGS["c4"]
+        xe = torch.randn((c4.batch, c4.prefill_len, cfg.hidden), device="cuda")
+        for T in (512, 1024):
+            m = gm if T == cfg.max_total_len else gm.with_max_total_len(T)
+            r16 = Run(torch, ark, m, c4.batch, c4.prefill_len)
+            r16.prefill(xe, [0] * c4.batch)
+            t = timed(torch, lambda: r16.prefill(xe, [0] * c4.batch), reps=2)
+            R = c4.batch * c4.prefill_len
+            ex[f"prefill_16x387_T{T}_tok_s"] = round(R / t, 1)
+            ex[f"prefill_16x387_T{T}_ms"] = round(t * 1e3, 2)
+            ex[f"prefill_16x387_T{T}_int8_frac_of_5POPS"] = round(
+                prefill_int8_ops(cfg, R, c4.batch) / t / PEAK_INT8, 4)
+            ark.cache_write(m.dims, [0] * c4.batch, r16.kc, r16.vc, r16.kd, r16.vd)
+            out16 = torch.empty((8, c4.batch), dtype=torch.int32, device="cuda")
+            r16.greedy(c4.prefill_len, 8, out16)
+            t = timed(torch, lambda: r16.greedy(c4.prefill_len, 8, out16))
+            ex[f"decode_bs16_T{T}_ms_per_step"] = round(t * 1e3 / 8, 3)
+            del r16, m
+            torch.cuda.empty_cache()
+        ex["decode_bs16_T1024_over_T512"] = round(ex["decode_bs16_T1024_ms_per_step"] /
+                                                  ex["decode_bs16_T512_ms_per_step"], 3)
+        ex["prefill_T1024_over_T512"] = round(ex["prefill_16x387_T1024_ms"] / ex["prefill_16x387_T512_ms"], 3)
+        ex["note"] = ("batch-32 and 16x387 figures reuse the c1 weights; their timing does not "
+                      "depend on weight values")
+        result["extras"] = ex
+        log(f"extras: {ex}")
+    return result
+
+
+# -------------------------------------------------------- CPU baseline ---
+def cpu_baseline(n_layers: int):
+    """The oracle, untuned, on a bounded sample of the same workload: one
+    decode token through `n_layers` of the 36 layers plus the LM head; the
+    per-token time is 36/n_layers x the layer time + the LM-head time."""
+    import numpy as np
+
+    import oracle
+    import synth
+    cfg = synth.CONFIGS["c1"]
+    log(f"cpu baseline: building {n_layers} oracle layers + LM head")
+    om = oracle.build_model(cfg, synth, layers=range(n_layers))
+    head = om.lm_head
+    om.lm_head = None
+    x = oracle.embed_ids(om.embed, np.array([[7]]))
+    shape = (1, cfg.max_total_len, cfg.n_kv_heads, cfg.head_dim)
+    kc = [np.zeros(shape, np.float32) for _ in range(n_layers)]
+    vc = [np.zeros(shape, np.float32) for _ in range(n_layers)]
+    p = np.array([cfg.prefill_len])
+    t0 = time.perf_counter()
+    _, _, _, hid = oracle.forward(om, x, p, kc, vc)
+    t_layers = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    hn = oracle.rmsnorm(hid[:, -1, :], om.final_norm, cfg.rms_eps)
+    c, s, z = oracle.dynquant(hn)
+    oracle.dequant(oracle.matmul_integer(c, z, head[0]), s, head[1])
+    t_head = time.perf_counter() - t0
+    per_token = t_layers * cfg.n_layers / n_layers + t_head
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in blas] or [1])
+    except Exception:  # pragma: no cover
+        threads = cores
+    return {
+        "value": round(1.0 / per_token, 4),
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"one c1 decode token (batch 1, T=512) through {n_layers} of 36 layers "
+                   f"({t_layers:.2f}s) plus the LM head ({t_head:.2f}s), scaled to 36 layers; "
+                   f"{cores} host cores visible, numpy BLAS threads {threads}"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=32)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--no-extras", dest="extras", action="store_false")
+    ap.add_argument("--no-cpu", dest="cpu", action="store_false")
+    ap.add_argument("--cpu-layers", type=int, default=6)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs the decoder step on a single GPU; multi-GPU runs "
+              f"(--gpus {args.gpus}, WORLD_SIZE {world}) are not supported", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
+    result = gpu_bench(args)
+    result["cpu_baseline"] = cpu_baseline(args.cpu_layers) if args.cpu else None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -246,6 +246,22 @@ int ark_test_qlinear(int32_t B, int32_t R, const uint8_t* codes, const float* sc
                      int32_t use_gemm, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/* ------------------------------------------------- instrumentation ---- */
+
+/* Benchmark instrumentation of the decode step's dominant kernel (the
+ * kernel that moves most of a bs1 decode token's bytes; its name is
+ * returned by ark_dominant_kernel()).  While armed, the library records
+ * events[2i] / events[2i+1] (caller-created hipEvent_t, passed as void*)
+ * on the launch stream immediately before / after the i-th launch of that
+ * kernel, for i < n_pairs; ark_profile_arm(NULL, 0) disarms (the count of
+ * recorded launches is kept until the next arming).  Process-wide state, not
+ * thread-safe: for benchmarks only.  Errors: ARK_E_SHAPE. */
+int ark_profile_arm(void* const* events, int32_t n_pairs);
+/* Launches recorded since the last arming. */
+int32_t ark_profile_count(void);
+/* Name of the instrumented kernel (static storage). */
+const char* ark_dominant_kernel(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -71,6 +71,9 @@ _SIGS = {
     "ark_test_dynquant": (C.c_int, [I32, I32, I32, P, P, P, P, P, C.c_size_t, P]),
     "ark_test_qlinear": (C.c_int, [I32, I32, P, P, P, C.POINTER(ArkQLinear), P, P, I32, P,
                                    C.c_size_t, P]),
+    "ark_profile_arm": (C.c_int, [PP, I32]),
+    "ark_profile_count": (C.c_int32, []),
+    "ark_dominant_kernel": (C.c_char_p, []),
 }
 
 _LIB = None
@@ -192,6 +195,12 @@ class DeviceModel:
         self.c = ArkModel(self.dims, self._layer_arr, _ptr(final_norm),
                           lm_head.c() if lm_head is not None else ArkQLinear(),
                           _ptr(embed_f16), _ptr(rope_cos), _ptr(rope_sin))
+
+    def with_max_total_len(self, T: int) -> "DeviceModel":
+        """The same weights with a static cache of T rows (new rotary tables)."""
+        cfg = self.cfg.with_(max_total_len=T)
+        rc, rs = rope_table(T, cfg.head_dim, cfg.rope_theta, self.rope_cos.device)
+        return DeviceModel(cfg, self.layers, self.final_norm, self.lm_head, self.embed_f16, rc, rs)
 
     def view(self, layers=None) -> "DeviceModel":
         """The same weights restricted to some layers (no LM head)."""
@@ -344,3 +353,48 @@ def test_qlinear(codes, scale, zp, W: QLinear, use_gemm: bool, stream=None):
                                                        _ptr(acc), _ptr(y), int(use_gemm), _ptr(ws),
                                                        ws.numel(), _stream(stream)))
     return acc, y
+
+
+# ------------------------------------------------------- instrumentation --
+class HipEvents:
+    """n pairs of timing hipEvents (created through the HIP runtime) armed
+    around the library's dominant decode kernel (ark_profile_arm)."""
+
+    def __init__(self, n_pairs: int):
+        self.hip = C.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [C.c_void_p]
+        self.n = n_pairs
+        self.arr = (C.c_void_p * (2 * n_pairs))()
+        for i in range(2 * n_pairs):
+            ev = C.c_void_p()
+            if self.hip.hipEventCreate(C.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.arr[i] = ev.value
+
+    def arm(self):
+        _check("ark_profile_arm", lib().ark_profile_arm(self.arr, self.n))
+
+    @staticmethod
+    def disarm():
+        lib().ark_profile_arm(None, 0)
+
+    def durations_ms(self):
+        """Elapsed ms of every recorded pair (call after synchronising)."""
+        k = lib().ark_profile_count()
+        out = []
+        for i in range(k):
+            ms = C.c_float()
+            if self.hip.hipEventElapsedTime(C.byref(ms), self.arr[2 * i], self.arr[2 * i + 1]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out.append(ms.value)
+        return out
+
+    def close(self):
+        for i in range(2 * self.n):
+            self.hip.hipEventDestroy(self.arr[i])
+
+
+def dominant_kernel() -> str:
+    return lib().ark_dominant_kernel().decode()

@@ -131,6 +131,24 @@ inline Seg seg_of(const ark_qlinear& q, float* out, int ldo) {
   return s;
 }
 
+// Benchmark instrumentation (see ark_profile_arm).
+struct Profiler {
+  hipEvent_t* ev = nullptr;
+  int n = 0;
+  int count = 0;
+};
+Profiler g_prof;
+
+inline void prof_begin(hipStream_t st, bool dominant) {
+  if (dominant && g_prof.ev && g_prof.count < g_prof.n) hipEventRecord(g_prof.ev[2 * g_prof.count], st);
+}
+inline void prof_end(hipStream_t st, bool dominant) {
+  if (dominant && g_prof.ev && g_prof.count < g_prof.n) {
+    hipEventRecord(g_prof.ev[2 * g_prof.count + 1], st);
+    ++g_prof.count;
+  }
+}
+
 #define HIP_TRY(expr)                       \
   do {                                      \
     if ((expr) != hipSuccess) return ARK_E_HIP; \
@@ -181,7 +199,9 @@ int run_forward(const ark_model* m, int B, int S, float* x, const int32_t* pos_h
     HIP_TRY(launch_attention(st, B, S, NH, NKV, T, q, kc[l], vc[l], kdl, vdl, pos, attn, part));
     if (gemv) {
       HIP_TRY(launch_gemv(st, B, Q, attn, Q, nullptr, 0.0, os, 1, EPI_RESID));
+      prof_begin(st, B == 1);
       HIP_TRY(launch_gemv(st, B, H, x, H, L.ln2, d.rms_eps, gus, 2, EPI_SWIGLU));
+      prof_end(st, B == 1);
       HIP_TRY(launch_gemv(st, B, I, a, I, nullptr, 0.0, ds, 1, EPI_RESID));
     } else {
       HIP_TRY(launch_rowminmax(st, R, Q, attn, rmin, rmax));
@@ -387,6 +407,18 @@ int ark_greedy_decode(const ark_model* m, int32_t B, int32_t* token_ids, int32_t
   for (int b = 0; b < B; ++b) cache_position[b] = pos[b];
   return steps;
 }
+
+int ark_profile_arm(void* const* events, int32_t n_pairs) {
+  if (events && n_pairs < 1) return ARK_E_SHAPE;
+  g_prof.ev = events ? (hipEvent_t*)events : nullptr;
+  g_prof.n = events ? n_pairs : 0;
+  if (events) g_prof.count = 0;  // disarming keeps the count of the last armed run
+  return ARK_OK;
+}
+
+int32_t ark_profile_count(void) { return g_prof.count; }
+
+const char* ark_dominant_kernel(void) { return "ark::k_gemv<1, 2, 2>"; }
 
 int ark_test_dynquant(int32_t B, int32_t R, int32_t K, const float* x, uint8_t* codes,
                       float* scale, int32_t* zp, void* workspace, size_t workspace_bytes,

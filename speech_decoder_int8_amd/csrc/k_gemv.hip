@@ -39,7 +39,7 @@ __device__ __forceinline__ int dot16(const i32x4 w, const i32x4 a, int acc) {
   return acc;
 }
 
-template <int BMAX, int NR>
+template <int BMAX, int NR, int EPI>
 __global__ __launch_bounds__(256) void k_gemv(GemvParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ float qs_l[BMAX];
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams P) {
   __syncthreads();
 
   // ---- weight rows of this wave
-  const bool swiglu = P.epi == EPI_SWIGLU;
+  constexpr bool swiglu = EPI == EPI_SWIGLU;
   constexpr int NW = 2 * NR;
   const int row0 = (blockIdx.x * 4 + wave) * NR;
   const int8_t* wp[NW];
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams P) {
         float y = dequant(at, s, S.sw[n]);
         if (S.bias) y = y + S.bias[n];
         float* o = S.out + (size_t)b * S.ldo + n;
-        if (P.epi == EPI_RESID)
+        if (EPI == EPI_RESID)
           *o = *o + y;
         else
           *o = y;
@@ -189,6 +189,28 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams P) {
       }
     }
   }
+}
+
+template <int BMAX, int NR>
+static void launch_epi(hipStream_t st, Epi epi, int grid, size_t lds, const GemvParams& P) {
+  if (epi == EPI_STORE)
+    hipLaunchKernelGGL((k_gemv<BMAX, NR, EPI_STORE>), dim3(grid), dim3(256), lds, st, P);
+  else if (epi == EPI_RESID)
+    hipLaunchKernelGGL((k_gemv<BMAX, NR, EPI_RESID>), dim3(grid), dim3(256), lds, st, P);
+  else
+    hipLaunchKernelGGL((k_gemv<BMAX, NR, EPI_SWIGLU>), dim3(grid), dim3(256), lds, st, P);
+}
+
+template <int NR>
+static hipError_t launch_bmax(hipStream_t st, int bmax, Epi epi, int grid, size_t lds,
+                              const GemvParams& P) {
+  if (bmax == 1)
+    launch_epi<1, NR>(st, epi, grid, lds, P);
+  else if (bmax == 2)
+    launch_epi<2, NR>(st, epi, grid, lds, P);
+  else
+    launch_epi<4, NR>(st, epi, grid, lds, P);
+  return hipGetLastError();
 }
 
 static hipError_t gemv_dispatch(hipStream_t st, GemvParams& P, const Seg* segs, int nseg, Epi epi) {
@@ -204,13 +226,7 @@ static hipError_t gemv_dispatch(hipStream_t st, GemvParams& P, const Seg* segs, 
   const int grid = (P.rows_total + 4 * NR - 1) / (4 * NR);
   const int bmax = P.B <= 1 ? 1 : (P.B <= 2 ? 2 : 4);
   const size_t lds = (size_t)bmax * P.K + ((P.x && P.gain) ? (size_t)bmax * P.K * 4 : 0);
-  if (bmax == 1)
-    hipLaunchKernelGGL((k_gemv<1, NR>), dim3(grid), dim3(256), lds, st, P);
-  else if (bmax == 2)
-    hipLaunchKernelGGL((k_gemv<2, NR>), dim3(grid), dim3(256), lds, st, P);
-  else
-    hipLaunchKernelGGL((k_gemv<4, NR>), dim3(grid), dim3(256), lds, st, P);
-  return hipGetLastError();
+  return launch_bmax<NR>(st, bmax, epi, grid, lds, P);
 }
 
 hipError_t launch_gemv(hipStream_t st, int B, int K, const float* x, int ldx, const float* gain,
