@@ -262,6 +262,13 @@ int32_t ark_profile_count(void);
 /* Name of the instrumented kernel (static storage). */
 const char* ark_dominant_kernel(void);
 
+/* Diagnostics of the persistent batch-1 decode kernel: when the environment
+ * variable ARK_MEGA_TRACE is "1", each decode step records 100 MHz
+ * real-time-counter stamps at its phase boundaries (workgroups 0, 1 and 255;
+ * uint64 [3][n_layers + 1][16]) at this byte offset of the workspace.
+ * 0 if the dims are invalid. */
+size_t ark_decode_trace_offset(const ark_dims* d);
+
 #ifdef __cplusplus
 }
 #endif

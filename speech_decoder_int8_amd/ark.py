@@ -74,6 +74,7 @@ _SIGS = {
     "ark_profile_arm": (C.c_int, [PP, I32]),
     "ark_profile_count": (C.c_int32, []),
     "ark_dominant_kernel": (C.c_char_p, []),
+    "ark_decode_trace_offset": (C.c_size_t, [C.POINTER(ArkDims)]),
 }
 
 _LIB = None
@@ -398,3 +399,16 @@ class HipEvents:
 
 def dominant_kernel() -> str:
     return lib().ark_dominant_kernel().decode()
+
+
+def decode_trace(model: DeviceModel, ws):
+    """Phase timestamps of the last traced decode step (ARK_MEGA_TRACE=1):
+    numpy uint64 [3][n_layers + 1][32] (workgroups 0, 1 and 255, every
+    layer) and [256][16] (every workgroup, one layer) read from the workspace."""
+    import torch
+    off = lib().ark_decode_trace_offset(C.byref(model.dims))
+    n1 = 3 * (model.cfg.n_layers + 1) * 32
+    n = n1 + 256 * 16
+    torch.cuda.synchronize()
+    raw = ws[off:off + n * 8].cpu().numpy().view(np.uint64)
+    return raw[:n1].reshape(3, model.cfg.n_layers + 1, 32), raw[n1:].reshape(256, 16)

@@ -1,6 +1,7 @@
 // C ABI of the decoder step: host-side validation, workspace planning and
 // kernel sequencing.  Validation touches no HIP API, so every error path can
 // be exercised without a GPU; a call that fails validation enqueues nothing.
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -18,8 +19,17 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
 struct Plan {
-  size_t x, h, codes, qkv, q, attn, a, rmin, rmax, qs, qz, part, done, total;
+  size_t x, h, codes, qkv, q, attn, a, rmin, rmax, qs, qz, part, done, mega, total;
 };
+
+bool use_mega(const ark_dims& d, int B, int S) {
+  if (B != 1 || S != 1) return false;
+  if (!decode_mega_supported(d.hidden, d.n_heads, d.n_kv_heads, d.head_dim, d.intermediate,
+                             d.max_total_len, d.n_layers))
+    return false;
+  const char* e = getenv("ARK_DECODE_PATH");
+  return !(e && strcmp(e, "multi") == 0);
+}
 
 Plan plan(const ark_dims& d, int B, int S) {
   const size_t R = (size_t)B * S;
@@ -44,8 +54,11 @@ Plan plan(const ark_dims& d, int B, int S) {
   p.rmax = take(R * 4);
   p.qs = take((size_t)std::max(B, 64) * 4);
   p.qz = take((size_t)std::max(B, 64) * 4);
-  p.part = take(attention_ws_bytes(B, S, d.n_heads, d.max_total_len));
+  // decode-only regions are always reserved, so a workspace sized for a
+  // prefill of B sequences also serves their decode steps
+  p.part = take(attention_ws_bytes(B, 1, d.n_heads, d.max_total_len));
   p.done = take((size_t)kMaxBatch * 4);
+  p.mega = take(B == 1 ? decode_mega_ws_bytes(d.n_layers, d.max_total_len) : 0);
   p.total = o;
   return p;
 }
@@ -230,6 +243,67 @@ int run_forward(const ark_model* m, int B, int S, float* x, const int32_t* pos_h
   return ARK_OK;
 }
 
+int mega_upload(const ark_model* m, const float* const* kc, const float* const* vc, char* ws,
+                hipStream_t st) {
+  const ark_dims& d = m->d;
+  MegaLayer tab[kMaxLayers];
+  for (int l = 0; l < d.n_layers; ++l) {
+    const ark_layer& L = m->layers[l];
+    const ark_qlinear* q[7] = {&L.q, &L.k, &L.v, &L.o, &L.gate, &L.up, &L.down};
+    for (int i = 0; i < 7; ++i) {
+      tab[l].w[i] = q[i]->w;
+      tab[l].sw[i] = q[i]->scale;
+      tab[l].cs[i] = q[i]->colsum;
+    }
+    tab[l].bias[0] = L.q.bias;
+    tab[l].bias[1] = L.k.bias;
+    tab[l].bias[2] = L.v.bias;
+    tab[l].ln1 = L.ln1;
+    tab[l].ln2 = L.ln2;
+    tab[l].kc = kc[l];
+    tab[l].vc = vc[l];
+  }
+  const Plan p = plan(d, 1, 1);
+  return decode_mega_upload(st, ws + p.mega, d.n_layers, d.max_total_len, tab) == hipSuccess
+             ? ARK_OK
+             : ARK_E_HIP;
+}
+
+int mega_step(const ark_model* m, const int32_t* token, int pos, float* kd, float* vd,
+              float* logits, float* hidden_out, const uint8_t* mask, int32_t* out_token, char* ws,
+              hipStream_t st) {
+  const ark_dims& d = m->d;
+  const Plan p = plan(d, 1, 1);
+  MegaStep S;
+  S.L = d.n_layers;
+  S.T = d.max_total_len;
+  S.V = d.vocab;
+  S.pos = pos;
+  S.eps = d.rms_eps;
+  S.token = token;
+  S.table = m->embed_f16;
+  S.final_norm = logits ? m->final_norm : nullptr;
+  S.lm_w = logits ? m->lm_head.w : nullptr;
+  S.lm_sw = m->lm_head.scale;
+  S.lm_cs = m->lm_head.colsum;
+  S.rcos = m->rope_cos;
+  S.rsin = m->rope_sin;
+  S.kdelta = kd;
+  S.vdelta = vd;
+  S.logits = logits;
+  S.hidden_out = hidden_out;
+  S.mask = logits ? mask : nullptr;
+  S.out_token = out_token;
+  prof_begin(st, true);
+  const hipError_t e = decode_mega_launch(st, ws + p.mega, S);
+  prof_end(st, true);
+  return e == hipSuccess ? ARK_OK : ARK_E_HIP;
+}
+
+bool mega_ready(const ark_model* m, int B) {
+  return use_mega(m->d, B, 1) && decode_mega_init() == hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -315,6 +389,11 @@ int ark_decode_step(const ark_model* m, int32_t B, const int32_t* token_ids,
   if (e) return e;
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
+  if (mega_ready(m, B)) {
+    if ((e = mega_upload(m, k_cache, v_cache, ws, st))) return e;
+    return mega_step(m, token_ids, cache_position[0], k_delta, v_delta, logits, hidden_out, nullptr,
+                     nullptr, ws, st);
+  }
   const Plan p = plan(m->d, B, 1);
   float* x = hidden_out ? hidden_out : (float*)(ws + p.x);
   if (launch_embed(st, B, 1, m->d.hidden, m->d.vocab, token_ids, m->embed_f16, nullptr, 0, 0, x) !=
@@ -375,17 +454,27 @@ int ark_greedy_decode(const ark_model* m, int32_t B, int32_t* token_ids, int32_t
   std::vector<int32_t> pos(cache_position, cache_position + B);
   std::vector<int32_t> flags(B);
   const int T = m->d.max_total_len;
+  const bool mega = mega_ready(m, B);
+  if (mega && (e = mega_upload(m, (const float* const*)k_cache, (const float* const*)v_cache, ws, st)))
+    return e;
   int steps = 0;
   for (int t = 0; t < max_steps; ++t) {
     bool room = true;
     for (int b = 0; b < B; ++b) room = room && pos[b] + 1 <= T;
     if (!room) break;
-    e = ark_decode_step(m, B, token_ids, pos.data(), (const float* const*)k_cache,
-                        (const float* const*)v_cache, k_delta, v_delta, logits, nullptr, workspace,
-                        workspace_bytes, stream);
-    if (e) return e;
-    if (launch_masked_argmax(st, B, m->d.vocab, logits, mask, token_ids) != hipSuccess)
-      return ARK_E_HIP;
+    if (mega) {
+      // one persistent kernel computes the logits and the masked greedy id
+      e = mega_step(m, token_ids, pos[0], k_delta, v_delta, logits, nullptr, mask, token_ids, ws,
+                    st);
+      if (e) return e;
+    } else {
+      e = ark_decode_step(m, B, token_ids, pos.data(), (const float* const*)k_cache,
+                          (const float* const*)v_cache, k_delta, v_delta, logits, nullptr,
+                          workspace, workspace_bytes, stream);
+      if (e) return e;
+      if (launch_masked_argmax(st, B, m->d.vocab, logits, mask, token_ids) != hipSuccess)
+        return ARK_E_HIP;
+    }
     if (launch_greedy_post(st, B, token_ids, out_tokens + (size_t)t * B, end_id, done) !=
         hipSuccess)
       return ARK_E_HIP;
@@ -418,7 +507,16 @@ int ark_profile_arm(void* const* events, int32_t n_pairs) {
 
 int32_t ark_profile_count(void) { return g_prof.count; }
 
-const char* ark_dominant_kernel(void) { return "ark::k_gemv<1, 2, 2>"; }
+size_t ark_decode_trace_offset(const ark_dims* d) {
+  if (!d || !dims_ok(*d)) return 0;
+  return plan(*d, 1, 1).mega + decode_mega_trace_offset(d->n_layers, d->max_total_len);
+}
+
+const char* ark_dominant_kernel(void) {
+  const char* e = getenv("ARK_DECODE_PATH");
+  if (e && strcmp(e, "multi") == 0) return "ark::k_gemv<1, 2, 2>";
+  return "ark::mk::k_decode";
+}
 
 int ark_test_dynquant(int32_t B, int32_t R, int32_t K, const float* x, uint8_t* codes,
                       float* scale, int32_t* zp, void* workspace, size_t workspace_bytes,

@@ -1,0 +1,1143 @@
+// Persistent decode step for the ARK-ASR-3B geometry at batch 1.
+//
+// One cooperative launch runs all 36 layers and the LM head of a decode
+// token (model card "ark-asr-3b-onnx", sections Shapes and Files: hidden
+// 2048, 16 query / 2 KV heads of 128, int8 per-channel MatMuls with dynamic
+// activation quantisation, full static-cache attention, int8 LM head).
+//
+// Why one kernel: a batch-1 token streams 3.09 GB of int8 weights but has
+// five all-to-all dependencies per layer (each MatMul needs the whole
+// quantised input vector).  Separate kernels pay launch gaps and short,
+// latency-bound streams; here the weight stream runs ahead of the
+// dependency chain instead.
+//
+// Work split: 256 workgroups x 16 waves.  Wave 0 ("poller") waits for the
+// inputs of each phase and never has weight loads in flight, so its waits
+// are not serialised behind the weight stream (vector loads complete in
+// order).  Waves 1..15 ("streamers") own fixed output rows of every phase and
+// issue the loads of a phase's weights into registers one phase ahead (at
+// most 14 KiB per wave, which fits the 128 VGPRs a 16-wave workgroup allows).
+//
+// Data exchange between workgroups (which sit on different XCDs with
+// separate L2s) uses 64-bit words (fp32 value | tag << 32) written with
+// device-scope stores and read with device-scope loads, so no cache
+// write-back/invalidate fence is needed; every buffer is written once per
+// launch (the preparation kernel zeroes them), so tag 1 means "written".
+// Every wait is bounded: on time-out the kernel records an error and runs
+// to completion.
+#include <float.h>
+#include <limits.h>
+#include <stdlib.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ark {
+namespace mk {
+
+constexpr int H = 2048, NH = 16, NKV = 2, D = kHeadDim, Q = NH * D, KVD = NKV * D, I = 11008;
+constexpr int G = NH / NKV;               // query heads per KV head
+constexpr int NQKV = Q + 2 * KVD;         // 2560 q|k|v rows
+constexpr int NWG = 256, NT = 1024, NW = 16, NS = NW - 1;
+constexpr int KEYS = 64;                  // cache rows per attention item
+constexpr int PART = 2 + D;               // fp64 words of one partial softmax state
+constexpr uint32_t SPIN_LIMIT = 1u << 15;  // ~30-60 ms per wait: a failure ends in seconds
+constexpr int NREP = 8;                   // replicas of each broadcast vector (one per XCD)
+constexpr unsigned long long MAGIC = 0x41524b5f58434831ull;
+
+// per-layer exchange words: q|k|v once (read by the attention workgroups),
+// every vector that all workgroups read in NREP replicas, so each replica is
+// read by the 32 workgroups of one XCD instead of all 256 reading one copy
+constexpr int OFF_QKV = 0, OFF_X0 = NQKV, OFF_ATT = OFF_X0 + NREP * H,
+              OFF_X1 = OFF_ATT + NREP * Q, OFF_A = OFF_X1 + NREP * H,
+              XCH_LAYER = OFF_A + NREP * I;
+
+// rows per workgroup in each phase, and the rotation that spreads them over
+// the 15 streamers (o rows go to streamers 0..7, down rows to 7..14)
+constexpr int R_QKV = NQKV / NWG, R_O = H / NWG, R_GU = I / NWG, R_D = H / NWG;
+static_assert(R_QKV * NWG == NQKV && R_O * NWG == H && R_GU * NWG == I, "row split");
+constexpr int ROT_QKV = 0, ROT_O = 0, ROT_GU = 0, ROT_D = 8;
+static_assert(R_QKV <= 15 && R_O <= 15 && R_D <= 15 && R_GU <= 45, "rows per streamer");
+
+typedef unsigned long long u64;
+typedef __attribute__((address_space(1))) const i32x4 gi32x4;
+
+// 16-byte streaming load through a global (not flat) pointer: flat loads
+// would also count against the LDS wait counter.
+__device__ __forceinline__ i32x4 ldg_nt(const void* p) {
+  return __builtin_nontemporal_load((gi32x4*)p);
+}
+template <typename T>
+__device__ __forceinline__ T ldg(const T* p) {
+  return *(const __attribute__((address_space(1))) T*)p;
+}
+
+__device__ __forceinline__ void xput(u64* p, float v, uint32_t tag) {
+  __hip_atomic_store(p, ((u64)tag << 32) | (u64)__float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+// element i of a replicated vector of length n
+__device__ __forceinline__ void xput_rep(u64* base, int n, int i, float v, uint32_t tag) {
+#pragma unroll
+  for (int r = 0; r < NREP; ++r) xput(base + (size_t)r * n + i, v, tag);
+}
+__device__ __forceinline__ unsigned xcc_id() {
+  unsigned x;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+  return x & (NREP - 1);
+}
+__device__ __forceinline__ u64 xget(const u64* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void put_f64(double* p, double v) {
+  __hip_atomic_store((u64*)p, (u64)__double_as_longlong(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// DMA of `bytes` (multiple of 1024) from global to LDS by one wave, 1 KiB per
+// instruction; device-scope loads when `coherent`.
+template <bool coherent>
+__device__ __forceinline__ void dma_wave(const void* src, void* lds, int bytes, int lane16) {
+  const char* s = (const char*)src + lane16;
+  char* d = (char*)lds;
+  for (int off = 0; off < bytes; off += 1024) {
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(s + off),
+                                     (void __attribute__((address_space(3)))*)(d + off), 16, 0,
+                                     coherent ? 16 : 0);
+  }
+}
+
+struct LayerW {
+  const int8_t* w[7];  // q, k, v, o, gate, up, down
+  const float* sw[7];
+  const int32_t* cs[7];
+  const float* bias[3];
+  const float* ln1;
+  const float* ln2;
+  const float* kc;  // [T][NKV][D]
+  const float* vc;
+};
+
+struct MegaArgs {
+  const LayerW* layers;
+  int L, T, V, pos;
+  double eps;
+  const float* final_norm;
+  const int8_t* lm_w;
+  const float* lm_sw;
+  const int32_t* lm_cs;
+  const double* rcos;
+  const double* rsin;
+  float* kdelta;
+  float* vdelta;
+  float* logits;
+  float* hidden_out;
+  const uint8_t* mask;
+  int32_t* out_token;
+  u64* xch;
+  u64* part;
+  uint32_t* ctr;
+  float* amax_v;
+  int* amax_i;
+  uint32_t* err;
+  u64* trace;  // optional phase timestamps [3 workgroups][L + 1][16]
+  u64* marker;
+  u64 marker_value;
+  uint32_t* epoch;  // [0] last launch's tag, [1] this launch's tag
+};
+
+// Phase timestamps (100 MHz real-time counter) of workgroups 0, 1 and the
+// last one for every layer, and of every workgroup for one layer, when a
+// trace buffer is given: [3][L + 1][32] then [NWG][16].
+constexpr int TRACE_WIDE_LAYER = 2;
+__device__ __forceinline__ void trace_at(const MegaArgs& A, int w, int l, int ev) {
+  if (A.trace && threadIdx.x == 0) {
+    const u64 t = __builtin_amdgcn_s_memrealtime();
+    const int slot = w == 0 ? 0 : (w == 1 ? 1 : (w == NWG - 1 ? 2 : -1));
+    if (slot >= 0) A.trace[((size_t)slot * (A.L + 1) + l) * 32 + ev] = t;
+    if (l == (A.L > TRACE_WIDE_LAYER ? TRACE_WIDE_LAYER : 0))
+      A.trace[(size_t)3 * (A.L + 1) * 32 + (size_t)w * 16 + ev] = t;
+  }
+}
+
+// The latest of the streaming waves' timestamps for a phase's end (each
+// wave's lane 0 calls this once).
+__device__ __forceinline__ void trace_done(const MegaArgs& A, int w, int l, int ev, int lane) {
+  if (A.trace && lane == 0) {
+    const u64 t = __builtin_amdgcn_s_memrealtime();
+    const int slot = w == 0 ? 0 : (w == 1 ? 1 : (w == NWG - 1 ? 2 : -1));
+    if (slot >= 0)
+      __hip_atomic_fetch_max(A.trace + ((size_t)slot * (A.L + 1) + l) * 32 + ev, t,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (l == (A.L > TRACE_WIDE_LAYER ? TRACE_WIDE_LAYER : 0))
+      __hip_atomic_fetch_max(A.trace + (size_t)3 * (A.L + 1) * 32 + (size_t)w * 16 + ev, t,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+__device__ __forceinline__ void trace_val(const MegaArgs& A, int w, int l, int ev, uint32_t v) {
+  if (A.trace && threadIdx.x == 0 && l == (A.L > TRACE_WIDE_LAYER ? TRACE_WIDE_LAYER : 0))
+    A.trace[(size_t)3 * (A.L + 1) * 32 + (size_t)w * 16 + ev] = v;
+}
+// Slot of a sub-phase timestamp (events 16..31) of workgroups 0, 1 and the
+// last one, or null.
+__device__ __forceinline__ u64* trace_sub(const MegaArgs& A, int w, int l, int ev) {
+  const int slot = w == 0 ? 0 : (w == 1 ? 1 : (w == NWG - 1 ? 2 : -1));
+  return (A.trace && slot >= 0) ? A.trace + ((size_t)slot * (A.L + 1) + l) * 32 + ev : nullptr;
+}
+__device__ __forceinline__ void stamp(u64* t, int i, int lane) {
+  if (t && lane == 0) t[i] = __builtin_amdgcn_s_memrealtime();
+}
+
+struct Shared {
+  float xs[H];         // layer input (kept for the o residual)
+  float x1s[H];        // input of the MLP half (kept for the down residual)
+  float gain[H];
+  int8_t codes[11264];
+  alignas(16) unsigned char stage[104 * 1024];
+  double redd[NW];
+  float redf[2 * NW];
+  float bestv[NW];
+  int besti[NW];
+  int flag;
+};
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// ------------------------------------------------------------- waiting --
+// One wave: wait until words [c0, c1) of v carry the tag and copy them to
+// dst (word c0 first).  Producers write v in blocks of blk words (block b =
+// words [b*blk, b*blk + blk)); the wave first polls the first word of each
+// block that meets the range, then reads the range with device-scope loads
+// straight into LDS and checks every tag, again until all match.  The copy
+// is whole KiB: dst needs room up to the next KiB boundary.  Bounded: after
+// SPIN_LIMIT rounds the error word is set and the wave goes on.  Returns
+// the number of sparse polls plus 65536 x the number of copies.
+__device__ uint32_t poll_range(const u64* v, int c0, int c1, int blk, unsigned char* dst,
+                               uint32_t* err, int lane, uint32_t tag, u64* tr = nullptr) {
+  uint32_t spins = 0;
+  const int b0 = c0 / blk, b1 = (c1 - 1) / blk;
+  for (;;) {
+    bool ok = true;
+    for (int b = b0 + lane; b <= b1; b += 64)
+      ok &= (uint32_t)(xget(v + max(c0, b * blk)) >> 32) == tag;
+    if (__all(ok)) break;
+    if (++spins > SPIN_LIMIT) {
+      if (lane == 0) atomicOr(err, 1u);
+      break;
+    }
+  }
+  const uint32_t pre = spins;
+  stamp(tr, 1, lane);
+  const int bytes = ((c1 - c0) * 8 + 1023) & ~1023;
+  for (;;) {
+    dma_wave<true>(v + c0, dst, bytes, lane * 16);
+    __builtin_amdgcn_s_waitcnt(0);
+    const u64* s = (const u64*)dst;
+    bool ok = true;
+#pragma unroll 4
+    for (int i = lane; i < c1 - c0; i += 64) ok &= (uint32_t)(s[i] >> 32) == tag;
+    if (__all(ok)) break;
+    if (++spins > SPIN_LIMIT) {
+      if (lane == 0) atomicOr(err, 2u);
+      break;
+    }
+  }
+  return pre + ((spins - pre + 1) << 16);
+}
+
+// All waves: poll_range over words [0, n) of v, split into one chunk of
+// whole KiB per wave, staged at stage + 8 i.  Also waits for every load the
+// wave has in flight.  Returns wave 0's poll_range count.
+__device__ uint32_t poll_all(const u64* v, int n, int blk, unsigned char* stage, uint32_t* err,
+                             int lane, int wave, uint32_t tag, u64* tr = nullptr) {
+  if (wave == 0) stamp(tr, 0, lane);
+  const int chunk = ((n + NW - 1) / NW + 127) & ~127;
+  const int c0 = wave * chunk, c1 = min(n, c0 + chunk);
+  uint32_t r = 0;
+  if (c0 < c1)
+    r = poll_range(v, c0, c1, blk, stage + (size_t)c0 * 8, err, lane, tag, wave == 0 ? tr : nullptr);
+  __builtin_amdgcn_s_waitcnt(0);
+  if (wave == 0) stamp(tr, 2, lane);
+  return r;
+}
+
+// Waves 0..7: start copying an H-float gain vector into LDS (completes by the
+// next poll_all).
+__device__ __forceinline__ void load_gain(const float* g, float* dst, int wave, int lane16) {
+  if (wave < H / 256) dma_wave<false>(g + wave * 256, dst + wave * 256, 1024, lane16);
+}
+
+// All threads: staged words -> fp32 values.
+__device__ __forceinline__ void unstage(const unsigned char* stage, float* dst, int n, int tid) {
+  const u64* s = (const u64*)stage;
+#pragma unroll 2
+  for (int i = tid; i < n; i += NT) dst[i] = __uint_as_float((uint32_t)s[i]);
+}
+
+// ----------------------------------------------------------- prologues --
+// RMSNorm (fp64 inside) of x with gain g, then the dynamic uint8 quantiser;
+// shifted codes to sh.codes.  All 512 threads.
+__device__ QParam prologue_norm(const float* x, const float* g, double eps, Shared& sh, int tid) {
+  double ss = 0.0;
+  for (int i = tid; i < H; i += NT) {
+    const double v = x[i];
+    ss += v * v;
+  }
+  ss = block_sum<NT>(ss, sh.redd);
+  const double rs = 1.0 / sqrt(ss / (double)H + eps);
+  float hv[H / NT];
+  float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < H / NT; ++j) {
+    const int i = tid + j * NT;
+    hv[j] = (float)(((double)x[i] * rs) * (double)g[i]);
+    lo = fminf(lo, hv[j]);
+    hi = fmaxf(hi, hv[j]);
+  }
+  block_minmax<NT>(lo, hi, sh.redf);
+  const QParam p = quant_param(lo, hi);
+#pragma unroll
+  for (int j = 0; j < H / NT; ++j) sh.codes[tid + j * NT] = shift_code(quant_code(hv[j], p));
+  __syncthreads();
+  return p;
+}
+
+// Dynamic uint8 quantiser straight from the staged exchange words.
+__device__ QParam prologue_plain(const unsigned char* stage, int n, Shared& sh, int tid) {
+  const u64* x = (const u64*)stage;
+  float lo = INFINITY, hi = -INFINITY;
+#pragma unroll 2
+  for (int i = tid; i < n; i += NT) {
+    const float v = __uint_as_float((uint32_t)x[i]);
+    lo = fminf(lo, v);
+    hi = fmaxf(hi, v);
+  }
+  block_minmax<NT>(lo, hi, sh.redf);
+  const QParam p = quant_param(lo, hi);
+#pragma unroll 2
+  for (int i = tid; i < n; i += NT)
+    sh.codes[i] = shift_code(quant_code(__uint_as_float((uint32_t)x[i]), p));
+  __syncthreads();
+  return p;
+}
+
+// ------------------------------------------------------ weight streams --
+// Rows of a phase: workgroup w owns rows [w*R, (w+1)*R); streamer s (0..14)
+// owns local rows i = (s + rot) % 15 + 15k.
+__device__ __forceinline__ int row_local(int s, int rot, int k) { return (s + rot) % NS + NS * k; }
+
+// Load NR rows x U units (1 KiB per unit: 16 bytes per lane) of a K-byte
+// row-major int8 matrix into registers, plus per-row metadata.
+template <int NR, int U>
+__device__ __forceinline__ void load_rows(i32x4 (&r)[NR][U], float (&msw)[NR], int (&mcs)[NR],
+                                          const int8_t* W, const float* sw, const int32_t* cs,
+                                          int K, int row0, int R, int s, int rot, int lane16) {
+  // metadata first: a later wait on it must not also wait for the weights
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    const int i = row_local(s, rot, k);
+    const bool valid = i < R;
+    msw[k] = valid ? ldg(sw + row0 + i) : 0.0f;
+    mcs[k] = valid ? ldg(cs + row0 + i) : 0;
+  }
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    const int i = row_local(s, rot, k);
+    const bool valid = i < R;
+    const int8_t* p = W + (size_t)(row0 + (valid ? i : 0)) * K;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int off = u * 1024 + lane16;
+      r[k][u] = (valid && off < K) ? ldg_nt(p + off)
+                                   : i32x4{0, 0, 0, 0};
+    }
+  }
+}
+
+__device__ __forceinline__ int dot16(const i32x4 w, const i32x4 a, int acc) {
+  acc = __builtin_amdgcn_sdot4(w[0], a[0], acc, false);
+  acc = __builtin_amdgcn_sdot4(w[1], a[1], acc, false);
+  acc = __builtin_amdgcn_sdot4(w[2], a[2], acc, false);
+  acc = __builtin_amdgcn_sdot4(w[3], a[3], acc, false);
+  return acc;
+}
+
+// Dot products of NR register-resident rows with the LDS codes: each 16-byte
+// code chunk is read once and used for every row; returns wave totals.
+template <int NR, int U>
+__device__ __forceinline__ void dot_rows(const i32x4 (&r)[NR][U], const int8_t* codes,
+                                         int (&out)[NR], int lane16) {
+#pragma unroll
+  for (int k = 0; k < NR; ++k) out[k] = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const i32x4 a = *(const i32x4*)(codes + u * 1024 + lane16);
+#pragma unroll
+    for (int k = 0; k < NR; ++k) out[k] = dot16(r[k][u], a, out[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < NR; ++k) out[k] = wave_sum(out[k]);
+}
+
+// Rolling window over a streamer's units (16 bytes per lane each): the first
+// W are issued by prime(), run() consumes unit i and refills its slot with
+// unit i + W.  Fully unrolled, so every slot is a fixed register.
+template <int N, int W, typename Addr>
+__device__ __forceinline__ void prime_units(i32x4 (&buf)[W], Addr addr) {
+#pragma unroll
+  for (int j = 0; j < W; ++j) {
+    if (j < N) {
+      const int8_t* a = addr(j);
+      buf[j] = a ? ldg_nt(a) : i32x4{0, 0, 0, 0};
+    }
+  }
+}
+template <int N, int W, typename Addr, typename Use>
+__device__ __forceinline__ void run_units(i32x4 (&buf)[W], Addr addr, Use use) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int j = i % W;
+    use(i, buf[j]);
+    if (i + W < N) {
+      const int8_t* a = addr(i + W);
+      buf[j] = a ? ldg_nt(a) : i32x4{0, 0, 0, 0};
+    }
+  }
+}
+
+// ---------------------------------------------------------- attention --
+// Work item (KV head g, split sp): keys [sp*64, sp*64+64) for the 8 query
+// heads of g.  Only splits holding a key at or before the position run (the
+// rest would be masked whole).  With one live split the item finishes the
+// softmax itself.  Otherwise splits 1.. publish their partial softmax state
+// per head (running max, sum and weighted values, fp64 as two tagged 32-bit
+// halves) and split 0 waits for them, merges and publishes the output.
+//
+// LDS, after the 16 KiB that stage the layer input: keys and values of the
+// split as pairs of rows 1040 bytes apart (key k at float offset kv_row(k)),
+// so a score thread's 16-byte reads of its key row, 8 consecutive pairs at a
+// time, cover all 32 banks; then the q|k|v words, rotated q and k, v, the
+// softmax weights and per-head max/sum.
+constexpr int ATT_KV = 16 * 1024;                      // byte offset in stage
+constexpr int ATT_QKV = ATT_KV + 2 * (KEYS / 2) * 260 * 4;
+constexpr int ATT_Q = ATT_QKV + 10 * 1024;
+constexpr int ATT_END = ATT_Q + (G + 2) * D * 4 + G * KEYS * 8 + 2 * G * 8;
+constexpr int PSTATE = 2 * PART;                       // words per (split, head)
+constexpr int MERGE_BATCH = 4;                         // splits merged per pass
+static_assert(ATT_END <= 104 * 1024, "attention staging exceeds LDS stage");
+static_assert(ATT_KV + MERGE_BATCH * G * PSTATE * 8 + 1024 <= ATT_Q, "merge batch too large");
+
+__device__ __forceinline__ int kv_row(int k) { return (k >> 1) * 260 + (k & 1) * D; }
+
+// All waves: start copying the live cache rows of item (g, sp) into LDS (two
+// keys per 1 KiB instruction, pairs spread over the waves).  Completes by the
+// next poll of the wave.
+__device__ __forceinline__ void load_kv(const MegaArgs& A, int l, int item, Shared& sh, int wave,
+                                        int lane) {
+  const int nsplit = A.T / KEYS;
+  const int g = item / nsplit, j0 = (item % nsplit) * KEYS;
+  const int npair = (min(KEYS, A.pos + 1 - j0) + 1) / 2;
+  const LayerW& Lw = A.layers[l];
+  float* Ks = (float*)(sh.stage + ATT_KV);
+  float* Vs = Ks + (KEYS / 2) * 260;
+  for (int pr = wave; pr < npair; pr += NW) {
+    const int j = j0 + 2 * pr + (lane >> 5);
+    const size_t off = ((size_t)j * NKV + g) * D + (lane & 31) * 4;
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(Lw.kc + off),
+                                     (void __attribute__((address_space(3)))*)(Ks + pr * 260), 16,
+                                     0, 0);
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(Lw.vc + off),
+                                     (void __attribute__((address_space(3)))*)(Vs + pr * 260), 16,
+                                     0, 0);
+  }
+}
+
+__device__ __forceinline__ void put_half(u64* p, uint32_t v, uint32_t tag) {
+  __hip_atomic_store(p, ((u64)tag << 32) | (u64)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void put_tagged_f64(u64* p, double v, uint32_t tag) {
+  const u64 b = (u64)__double_as_longlong(v);
+  put_half(p, (uint32_t)b, tag);
+  put_half(p + 1, (uint32_t)(b >> 32), tag);
+}
+__device__ __forceinline__ double get_tagged_f64(const u64* p) {
+  return __longlong_as_double((long long)((p[0] & 0xffffffffull) | (p[1] << 32)));
+}
+
+__device__ void attention_item(const MegaArgs& A, uint32_t epoch, int l, int item, int nlive,
+                               Shared& sh, u64* xl, int tid, int lane, int wave) {
+  const int nsplit = A.T / KEYS;
+  const int g = item / nsplit, sp = item % nsplit;
+  const int j0 = sp * KEYS;
+  const int p = A.pos;
+  float* Ks = (float*)(sh.stage + ATT_KV);
+  float* Vs = Ks + (KEYS / 2) * 260;
+  unsigned char* qst = sh.stage + ATT_QKV;           // q|k|v words (10 KiB)
+  float* qr = (float*)(sh.stage + ATT_Q);            // rotated q [8][128]
+  float* kr = qr + G * D;                            // rotated k [128]
+  float* vv = kr + D;                                // v [128]
+  double* ps = (double*)(vv + D);                    // weights [8][64]
+  double* hm = ps + G * KEYS;                        // per-head max and sum [8][2]
+  u64* tr = trace_sub(A, item, l, 22);
+
+  // q of heads 8g..8g+7 (waves 0..7), k and v of head g (waves 8, 9)
+  if (wave < G + 2) {
+    const int n0 = wave < G ? (g * G + wave) * D : (wave == G ? Q + g * D : Q + KVD + g * D);
+    poll_range(xl + OFF_QKV, n0, n0 + D, R_QKV, qst + wave * D * 8, A.err, lane, epoch);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's cache rows
+  if (wave == 0) stamp(tr, 0, lane);
+  __syncthreads();
+  // rotary embedding (fp64) of q and k at position p; v as is
+  {
+    const u64* s = (const u64*)qst;
+    const double* cs = A.rcos + (size_t)p * (D / 2);
+    const double* sn = A.rsin + (size_t)p * (D / 2);
+    for (int t = tid; t < (G + 1) * (D / 2); t += NT) {
+      const int head = t / (D / 2), j = t % (D / 2);
+      const double x1 = __uint_as_float((uint32_t)s[head * D + j]);
+      const double x2 = __uint_as_float((uint32_t)s[head * D + j + D / 2]);
+      const double c = cs[j], sv = sn[j];
+      float* dst = head < G ? qr + head * D : kr;
+      dst[j] = (float)(x1 * c - x2 * sv);
+      dst[j + D / 2] = (float)(x2 * c + x1 * sv);
+    }
+    for (int t = tid; t < D; t += NT) vv[t] = __uint_as_float((uint32_t)s[(G + 1) * D + t]);
+  }
+  __syncthreads();
+  // this call's row replaces cache row p; split 0 publishes the deltas
+  if (p >= j0 && p < j0 + KEYS) {
+    for (int t = tid; t < D; t += NT) {
+      Ks[kv_row(p - j0) + t] = kr[t];
+      Vs[kv_row(p - j0) + t] = vv[t];
+    }
+  }
+  if (sp == 0) {
+    for (int t = tid; t < D; t += NT) {
+      A.kdelta[(size_t)l * KVD + g * D + t] = kr[t];
+      A.vdelta[(size_t)l * KVD + g * D + t] = vv[t];
+    }
+  }
+  __syncthreads();
+  if (tid == 0) stamp(tr, 1, lane);
+  // scores on waves 0..7: thread -> (head = wave, key jj); keys after the
+  // position are selected away (weight exactly 0, row never read)
+  if (wave < G) {
+    const int hh = wave, jj = 2 * (lane & 31) + (lane >> 5), j = j0 + jj;
+    double sc = -INFINITY;
+    if (j <= p) {
+      const float4* qh = (const float4*)(qr + hh * D);
+      const float4* kj = (const float4*)(Ks + kv_row(jj));
+      double d0 = 0.0, d1 = 0.0;
+#pragma unroll 4
+      for (int d = 0; d < D / 4; ++d) {
+        const float4 qv = qh[d], kv = kj[d];
+        d0 = fma((double)qv.x, (double)kv.x, d0);
+        d1 = fma((double)qv.y, (double)kv.y, d1);
+        d0 = fma((double)qv.z, (double)kv.z, d0);
+        d1 = fma((double)qv.w, (double)kv.w, d1);
+      }
+      sc = (d0 + d1) / sqrt((double)D);
+    }
+    const double m = wave_max(sc);
+    const double e = (sc == -INFINITY) ? 0.0 : exp(sc - m);
+    const double lsum = wave_sum(e);
+    ps[hh * KEYS + jj] = e;
+    if (lane == 0) {
+      hm[2 * hh] = m;
+      hm[2 * hh + 1] = lsum;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) stamp(tr, 2, lane);
+  // weighted values: thread -> (head = wave / 2, dim = (wave % 2) * 64 + lane)
+  const int hv = wave >> 1, dv = (wave & 1) * 64 + lane;
+  const int nk = min(KEYS, p + 1 - j0);
+  double o = 0.0;
+  for (int k = 0; k < nk; ++k) o = fma(ps[hv * KEYS + k], (double)Vs[kv_row(k) + dv], o);
+  if (nlive == 1) {
+    xput_rep(xl + OFF_ATT, Q, (g * G + hv) * D + dv, (float)(o / hm[2 * hv + 1]), epoch);
+    return;
+  }
+  u64* part = A.part + ((size_t)l * NKV + g) * nsplit * G * PSTATE;  // split 0 unused
+  if (sp > 0) {
+    u64* pst = part + ((size_t)sp * G + hv) * PSTATE;
+    if (dv == 0) {
+      put_tagged_f64(pst, hm[2 * hv], epoch);
+      put_tagged_f64(pst + 2, hm[2 * hv + 1], epoch);
+    }
+    put_tagged_f64(pst + 4 + 2 * dv, o, epoch);
+    return;
+  }
+  if (tid == 0) stamp(tr, 3, lane);
+  // split 0: merge the other live splits' states, MERGE_BATCH per pass
+  double M = hm[2 * hv], Lsum = hm[2 * hv + 1], O = o;
+  const u64* pb = (const u64*)(sh.stage + ATT_KV);
+  for (int s0 = 1; s0 < nlive; s0 += MERGE_BATCH) {
+    const int ns = min(MERGE_BATCH, nlive - s0);
+    const int n = ns * G * PSTATE;
+    const int chunk = ((n + NW - 1) / NW + 127) & ~127;
+    const int c0 = wave * chunk, c1 = min(n, c0 + chunk);
+    __syncthreads();  // the previous batch is merged (or the values read)
+    if (c0 < c1)
+      poll_range(part + (size_t)s0 * G * PSTATE, c0, c1, G * PSTATE, sh.stage + ATT_KV + c0 * 8,
+                 A.err, lane, epoch);
+    __syncthreads();
+    for (int s = 0; s < ns; ++s) {
+      const u64* q = pb + ((size_t)s * G + hv) * PSTATE;
+      const double ms = get_tagged_f64(q);
+      const double Mn = fmax(M, ms);
+      const double a = exp(M - Mn);
+      const double b = exp(ms - Mn);
+      Lsum = Lsum * a + get_tagged_f64(q + 2) * b;
+      O = O * a + get_tagged_f64(q + 4 + 2 * dv) * b;
+      M = Mn;
+    }
+  }
+  if (tid == 0) stamp(tr, 4, lane);
+  xput_rep(xl + OFF_ATT, Q, (g * G + hv) * D + dv, (float)(O / Lsum), epoch);
+}
+
+// ------------------------------------------------------------ the kernel --
+__global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  Shared& sh = *(Shared*)smem_raw;
+  int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(wave_id());
+  const bool streamer = wave > 0;
+  int w = blockIdx.x;
+  // Per-lane byte offset, redefined opaquely in every layer so the compiler
+  // recomputes addresses in the loop instead of keeping dozens of hoisted
+  // 64-bit addresses live next to the prefetched weights.
+  int lane16 = lane * 16;
+  int s = wave - 1;  // streamer index 0..14
+
+  // weight registers (streamers)
+  constexpr int W = 8;                 // units in flight per streamer (big phases)
+  constexpr int NGU = 3 * 2 * 2;       // gate/up units: 3 pairs x {gate, up} x 2
+  constexpr int ND = 11;               // down units: one 11008-byte row
+  i32x4 wq[1][2], wo[1][2], win[W];
+  float sq[1], so[1], sg[3], su[3], sd[1];
+  int cq[1], co[1], cg[3], cu[3], cd[1];
+  float bq[1] = {0.f};
+
+  auto issue_qkv = [&](int l) {
+    const LayerW& Lw = A.layers[l];
+    // rows of the concatenated q|k|v space: [w*10, w*10+10)
+#pragma unroll
+    for (int k = 0; k < 1; ++k) {
+      const int i = row_local(s, ROT_QKV, k);
+      const bool valid = i < R_QKV;
+      const int n = w * R_QKV + (valid ? i : 0);
+      const int seg = n < Q ? 0 : (n < Q + KVD ? 1 : 2);
+      const int nl = n - (seg == 0 ? 0 : (seg == 1 ? Q : Q + KVD));
+      const int8_t* p = Lw.w[seg] + (size_t)nl * H;
+      sq[k] = valid ? ldg(Lw.sw[seg] + nl) : 0.f;
+      cq[k] = valid ? ldg(Lw.cs[seg] + nl) : 0;
+      bq[k] = valid ? ldg(Lw.bias[seg] + nl) : 0.f;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        wq[k][u] = valid ? ldg_nt(p + u * 1024 + lane16)
+                         : i32x4{0, 0, 0, 0};
+    }
+  };
+  auto issue_o_gu = [&](int l) {
+    const LayerW& Lw = A.layers[l];
+    load_rows<1, 2>(wo, so, co, Lw.w[3], Lw.sw[3], Lw.cs[3], Q, w * R_O, R_O, s, ROT_O, lane16);
+  };
+  // unit i of the gate/up phase: pair i / 4, matrix (i / 2) % 2, unit i % 2
+  auto gu_addr = [&](const LayerW& Lw, int i) -> const int8_t* {
+    const int k = i / 4, m = (i / 2) % 2, u = i % 2;
+    const int r = row_local(s, ROT_GU, k);
+    if (r >= R_GU) return nullptr;
+    return Lw.w[4 + m] + (size_t)(w * R_GU + r) * H + u * 1024 + lane16;
+  };
+  auto down_addr = [&](const LayerW& Lw, int u) -> const int8_t* {
+    const int r = row_local(s, ROT_D, 0);
+    const int off = u * 1024 + lane16;
+    if (r >= R_D || off >= I) return nullptr;
+    return Lw.w[6] + (size_t)(w * R_D + r) * I + off;
+  };
+  auto issue_gate_up = [&](int l) {
+    const LayerW& Lw = A.layers[l];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int r = row_local(s, ROT_GU, k);
+      const bool valid = r < R_GU;
+      sg[k] = valid ? ldg(Lw.sw[4] + w * R_GU + r) : 0.f;
+      cg[k] = valid ? ldg(Lw.cs[4] + w * R_GU + r) : 0;
+      su[k] = valid ? ldg(Lw.sw[5] + w * R_GU + r) : 0.f;
+      cu[k] = valid ? ldg(Lw.cs[5] + w * R_GU + r) : 0;
+    }
+    prime_units<NGU, W>(win, [&](int i) { return gu_addr(Lw, i); });
+  };
+  auto issue_down = [&](int l) {
+    const LayerW& Lw = A.layers[l];
+    const int r = row_local(s, ROT_D, 0);
+    sd[0] = r < R_D ? ldg(Lw.sw[6] + w * R_D + r) : 0.f;
+    cd[0] = r < R_D ? ldg(Lw.cs[6] + w * R_D + r) : 0;
+    prime_units<ND, W>(win, [&](int u) { return down_addr(Lw, u); });
+  };
+
+  const size_t rep = xcc_id();
+  const uint32_t epoch = __builtin_amdgcn_readfirstlane(A.epoch[1]);
+  if (w == 0 && tid == 0) {
+    A.epoch[0] = epoch;           // the next launch counts on from here
+    *A.marker = A.marker_value;   // the exchange area is initialised
+  }
+  if (streamer) issue_qkv(0);
+
+  // attention items: (KV head, 64-key split) pairs whose split holds a key
+  // at or before the position, on workgroups g * nsplit + split
+  const int nsplit = A.T / KEYS;
+  const int nlive = min(nsplit, A.pos / KEYS + 1);
+  const bool att = w < NKV * nsplit && (w % nsplit) < nlive;
+  for (int l = 0; l < A.L; ++l) {
+    asm volatile("" : "+v"(lane16), "+v"(tid), "+v"(lane), "+s"(w), "+s"(s));
+    const LayerW& Lw = A.layers[l];
+    u64* xl = A.xch + (size_t)l * XCH_LAYER;
+    u64* xn = A.xch + (size_t)(l + 1) * XCH_LAYER;   // next layer's input lives at its OFF_X0
+
+    // ---- q, k, v
+    trace_at(A, w, l, 0);
+    if (att) load_kv(A, l, w, sh, wave, lane);
+    load_gain(Lw.ln1, sh.gain, wave, lane16);
+    trace_val(A, w, l, 11, poll_all(xl + OFF_X0 + rep * H, H, R_D, sh.stage, A.err, lane, wave, epoch, trace_sub(A, w, l, 27)));
+    __syncthreads();
+    trace_at(A, w, l, 1);
+    unstage(sh.stage, sh.xs, H, tid);
+    __syncthreads();
+    QParam qp = prologue_norm(sh.xs, sh.gain, A.eps, sh, tid);
+    trace_at(A, w, l, 2);
+    if (streamer) {
+      const int zc = 128 - qp.z;
+      int accs[1];
+      dot_rows<1, 2>(wq, sh.codes, accs, lane16);
+#pragma unroll
+      for (int k = 0; k < 1; ++k) {
+        const int i = row_local(s, ROT_QKV, k);
+        const int acc = accs[k];
+        if (lane == 0 && i < R_QKV) {
+          float y = dequant(acc + zc * cq[k], qp.s, sq[k]);
+          y = y + bq[k];
+          xput(xl + OFF_QKV + w * R_QKV + i, y, epoch);
+        }
+      }
+      trace_done(A, w, l, 3, lane);
+      // workgroups without attention work stream the o rows and the first
+      // gate/up units while the attention runs elsewhere
+      if (!att) {
+        issue_o_gu(l);
+        issue_gate_up(l);
+      }
+    }
+
+    // ---- attention
+    if (att) {
+      __syncthreads();
+      attention_item(A, epoch, l, w, nlive, sh, xl, tid, lane, wave);
+      __syncthreads();
+      if (streamer) issue_o_gu(l);
+    }
+
+    // ---- o projection + residual
+    asm volatile("" : "+v"(lane16), "+v"(tid), "+v"(lane));
+    trace_at(A, w, l, 4);
+    trace_val(A, w, l, 12, poll_all(xl + OFF_ATT + rep * Q, Q, G * D, sh.stage, A.err, lane, wave, epoch));
+    __syncthreads();
+    trace_at(A, w, l, 5);
+    qp = prologue_plain(sh.stage, Q, sh, tid);
+    if (streamer) {
+      const int zc = 128 - qp.z;
+      int accs[1];
+      dot_rows<1, 2>(wo, sh.codes, accs, lane16);
+#pragma unroll
+      for (int k = 0; k < 1; ++k) {
+        const int i = row_local(s, ROT_O, k);
+        const int acc = accs[k];
+        if (lane == 0 && i < R_O) {
+          const int n = w * R_O + i;
+          const float y = dequant(acc + zc * co[k], qp.s, so[k]);
+          xput_rep(xl + OFF_X1, H, n, sh.xs[n] + y, epoch);
+        }
+      }
+      trace_done(A, w, l, 6, lane);
+      if (att) issue_gate_up(l);
+    }
+
+    // ---- gate/up + SwiGLU
+    asm volatile("" : "+v"(lane16), "+v"(tid), "+v"(lane));
+    load_gain(Lw.ln2, sh.gain, wave, lane16);
+    trace_val(A, w, l, 13, poll_all(xl + OFF_X1 + rep * H, H, R_O, sh.stage, A.err, lane, wave, epoch, trace_sub(A, w, l, 16)));
+    __syncthreads();
+    trace_at(A, w, l, 7);
+    unstage(sh.stage, sh.x1s, H, tid);
+    __syncthreads();
+    qp = prologue_norm(sh.x1s, sh.gain, A.eps, sh, tid);
+    if (streamer) {
+      const int zc = 128 - qp.z;
+      int aggs[3] = {0, 0, 0}, aus[3] = {0, 0, 0};
+      const i32x4 c0 = *(const i32x4*)(sh.codes + lane16);
+      const i32x4 c1 = *(const i32x4*)(sh.codes + 1024 + lane16);
+      run_units<NGU, W>(win, [&](int i) { return gu_addr(Lw, i); }, [&](int i, const i32x4 v) {
+        const int k = i / 4, m = (i / 2) % 2, u = i % 2;
+        int& acc = m ? aus[k] : aggs[k];
+        acc = dot16(v, u ? c1 : c0, acc);
+      });
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        aggs[k] = wave_sum(aggs[k]);
+        aus[k] = wave_sum(aus[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const int i = row_local(s, ROT_GU, k);
+        const int ag = aggs[k];
+        const int au = aus[k];
+        if (lane == 0 && i < R_GU) {
+          const float gv = dequant(ag + zc * cg[k], qp.s, sg[k]);
+          const float uv = dequant(au + zc * cu[k], qp.s, su[k]);
+          const double gd = gv;
+          xput_rep(xl + OFF_A, I, w * R_GU + i, (float)(gd / (1.0 + exp(-gd)) * (double)uv), epoch);
+        }
+      }
+      trace_done(A, w, l, 8, lane);
+      issue_down(l);
+    }
+
+    // ---- down + residual
+    asm volatile("" : "+v"(lane16), "+v"(tid), "+v"(lane));
+    trace_val(A, w, l, 14, poll_all(xl + OFF_A + rep * I, I, R_GU, sh.stage, A.err, lane, wave, epoch, trace_sub(A, w, l, 19)));
+    __syncthreads();
+    trace_at(A, w, l, 9);
+    qp = prologue_plain(sh.stage, I, sh, tid);
+    if (streamer) {
+      const int zc = 128 - qp.z;
+      int accs[1] = {0};
+      run_units<ND, W>(win, [&](int u) { return down_addr(Lw, u); }, [&](int u, const i32x4 v) {
+        accs[0] = dot16(v, *(const i32x4*)(sh.codes + u * 1024 + lane16), accs[0]);
+      });
+      accs[0] = wave_sum(accs[0]);
+#pragma unroll
+      for (int k = 0; k < 1; ++k) {
+        const int i = row_local(s, ROT_D, k);
+        const int acc = accs[k];
+        if (lane == 0 && i < R_D) {
+          const int n = w * R_D + i;
+          const float y = dequant(acc + zc * cd[k], qp.s, sd[k]);
+          xput_rep(xn + OFF_X0, H, n, sh.x1s[n] + y, epoch);
+        }
+      }
+      trace_done(A, w, l, 10, lane);
+      if (l + 1 < A.L) issue_qkv(l + 1);
+    }
+  }
+
+  // ---- final norm + LM head + masked argmax
+  u64* xf = A.xch + (size_t)A.L * XCH_LAYER;
+  if (A.final_norm) load_gain(A.final_norm, sh.gain, wave, lane16);
+  poll_all(xf + OFF_X0 + rep * H, H, R_D, sh.stage, A.err, lane, wave, epoch);
+  __syncthreads();
+  unstage(sh.stage, sh.xs, H, tid);
+  __syncthreads();
+  trace_at(A, w, A.L, 0);
+  if (w == 0 && A.hidden_out)
+    for (int i = tid; i < H; i += NT) A.hidden_out[i] = sh.xs[i];
+  if (!A.lm_w) return;
+  const QParam qp = prologue_norm(sh.xs, sh.gain, A.eps, sh, tid);
+  const int r0 = (int)(((long long)w * A.V) / NWG), r1 = (int)(((long long)(w + 1) * A.V) / NWG);
+  float bv = -INFINITY;
+  int bi = INT_MAX;
+  if (streamer) {
+    const int zc = 128 - qp.z;
+    constexpr int GR = 4;  // rows per group of one streamer; two groups in flight
+    i32x4 b0[GR][2], b1[GR][2];
+    float w0[GR], w1[GR];
+    int c0[GR], c1[GR], m0[GR], m1[GR];
+    const int nmine = (r1 - r0 - s + NS - 1) / NS;  // rows of this streamer
+    const int ngroups = (nmine + GR - 1) / GR;
+    // the metadata is loaded with the weights so no later load has to wait
+    // behind the prefetched group
+    auto load_group = [&](int gidx, i32x4 (&b)[GR][2], float (&sw)[GR], int (&cs)[GR],
+                          int (&mk)[GR]) {
+#pragma unroll
+      for (int k = 0; k < GR; ++k) {
+        const int n = r0 + s + NS * (gidx * GR + k);
+        const bool valid = n < r1;
+        const int8_t* p = A.lm_w + (size_t)(valid ? n : r0) * H;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          b[k][u] = valid ? ldg_nt(p + u * 1024 + lane16)
+                          : i32x4{0, 0, 0, 0};
+        sw[k] = valid ? ldg(A.lm_sw + n) : 0.f;
+        cs[k] = valid ? ldg(A.lm_cs + n) : 0;
+        mk[k] = (valid && A.mask) ? (int)ldg(A.mask + n) : 1;
+      }
+    };
+    auto use_group = [&](int gidx, const i32x4 (&b)[GR][2], const float (&sw)[GR],
+                         const int (&cs)[GR], const int (&mk)[GR]) {
+      int accs[GR];
+      dot_rows<GR, 2>(b, sh.codes, accs, lane16);
+#pragma unroll
+      for (int k = 0; k < GR; ++k) {
+        const int n = r0 + s + NS * (gidx * GR + k);
+        const int acc = accs[k];
+        if (lane == 0 && n < r1) {
+          const float y = dequant(acc + zc * cs[k], qp.s, sw[k]);
+          A.logits[n] = y;
+          if (mk[k] == 0 && !isnan(y) && (y > bv || (y == bv && n < bi))) {
+            bv = y;
+            bi = n;
+          }
+        }
+      }
+    };
+    if (ngroups > 0) load_group(0, b0, w0, c0, m0);
+    for (int gg = 0; gg < ngroups; gg += 2) {
+      if (gg + 1 < ngroups) load_group(gg + 1, b1, w1, c1, m1);
+      use_group(gg, b0, w0, c0, m0);
+      if (gg + 1 < ngroups) {
+        if (gg + 2 < ngroups) load_group(gg + 2, b0, w0, c0, m0);
+        use_group(gg + 1, b1, w1, c1, m1);
+      }
+    }
+  }
+  trace_at(A, w, A.L, 1);
+  if (!A.mask) return;
+  // workgroup best -> partial; the last workgroup reduces all partials
+  if (lane == 0) {
+    sh.bestv[wave] = bv;
+    sh.besti[wave] = bi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int k = 1; k < NW; ++k)
+      if (sh.besti[k] != INT_MAX && (sh.bestv[k] > bv || (sh.bestv[k] == bv && sh.besti[k] < bi))) {
+        bv = sh.bestv[k];
+        bi = sh.besti[k];
+      }
+    __hip_atomic_store((uint32_t*)A.amax_v + w, __float_as_uint(bv), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store((uint32_t*)A.amax_i + w, (uint32_t)bi, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
+    const uint32_t old = __hip_atomic_fetch_add(A.ctr + 2 * A.L, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    sh.flag = (old == NWG - 1);
+  }
+  __syncthreads();
+  if (!sh.flag || wave != 0) return;
+  bv = -INFINITY;
+  bi = INT_MAX;
+  for (int k = lane; k < NWG; k += 64) {
+    const float v = __uint_as_float(__hip_atomic_load((uint32_t*)A.amax_v + k, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT));
+    const int i = (int)__hip_atomic_load((uint32_t*)A.amax_i + k, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    if (i != INT_MAX && (v > bv || (v == bv && i < bi))) {
+      bv = v;
+      bi = i;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float v = __shfl_xor(bv, o, 64);
+    const int i = __shfl_xor(bi, o, 64);
+    if (i != INT_MAX && (v > bv || (v == bv && i < bi))) {
+      bv = v;
+      bi = i;
+    }
+  }
+  if (lane == 0) *A.out_token = (bi == INT_MAX) ? -1 : bi;
+}
+
+// Zero the counters (and, on the first use of a workspace, the exchange
+// words and partial states), pick this launch's tag, then publish the embedding of the token as
+// the first layer's input in every replica, carrying that tag.  The tag
+// counter lives in the workspace, so exchange words left by any earlier
+// launch on it carry a different tag; a workspace whose marker does not hold
+// this layout's value is cleared and counts from 1.
+__global__ __launch_bounds__(256) void k_decode_prep(u64* xch, size_t nwords, uint32_t* ctr,
+                                                     int nctr, uint32_t* err, const u64* marker,
+                                                     u64 marker_value, uint32_t* epoch,
+                                                     const int32_t* token, const uint16_t* table,
+                                                     int V) {
+  const bool fresh = *marker != marker_value;
+  uint32_t e = fresh ? 1u : epoch[0] + 1u;
+  if (e == 0) e = 1;
+  if (fresh) {
+    // the first layer's input block is written below, not cleared
+    const size_t stride = (size_t)gridDim.x * 256;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < nwords; i += stride)
+      if (i < OFF_X0 || i >= OFF_X0 + (size_t)NREP * H) xch[i] = 0;
+  }
+  if (blockIdx.x == 0) {
+    for (int i = threadIdx.x; i < nctr; i += 256) ctr[i] = 0;
+    if (threadIdx.x == 0) {
+      *err = 0;
+      epoch[1] = e;
+    }
+  }
+  if (blockIdx.x == 1) {
+    const int id = *token;
+    for (int i = threadIdx.x; i < H; i += 256) {
+      const float v = (id >= 0 && id < V) ? half_bits_to_float(table[(size_t)id * H + i])
+                                          : __int_as_float(0x7fc00000);
+      for (int r = 0; r < NREP; ++r)
+        xch[OFF_X0 + (size_t)r * H + i] = ((u64)e << 32) | (u64)__float_as_uint(v);
+    }
+  }
+}
+
+}  // namespace mk
+
+// ------------------------------------------------------------------ host --
+// exchange words: L layers plus the final hidden state (the next layer's
+// input block of the last layer)
+static size_t mega_xch_words(int L) {
+  return (size_t)L * mk::XCH_LAYER + mk::OFF_X0 + (size_t)mk::NREP * mk::H;
+}
+
+size_t decode_mega_ws_bytes(int L, int T) {
+  const size_t xch = mega_xch_words(L) * 8;
+  const size_t part = (size_t)L * mk::NKV * (T / mk::KEYS) * mk::G * mk::PSTATE * 8;
+  const size_t ctr = (size_t)(2 * L + 64) * 4;
+  const size_t amax = (size_t)mk::NWG * 8;
+  const size_t table = (size_t)L * sizeof(mk::LayerW);
+  const size_t trace = ((size_t)3 * (L + 1) * 32 + mk::NWG * 16) * 8;
+  auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  return al(xch) + al(part) + al(ctr) + al(amax) + al(table) + al(trace) + 256;
+}
+
+bool decode_mega_supported(int H, int NH, int NKV, int D, int I, int T, int L) {
+  // the partial-state merge moves whole 1 KiB blocks of 8 splits: T % 512 == 0
+  return H == mk::H && NH == mk::NH && NKV == mk::NKV && D == mk::D && I == mk::I &&
+         T % 512 == 0 && T >= 512 && T <= 4096 && L >= 1 && L <= kMaxLayers;
+}
+
+struct MegaLayout {
+  mk::u64* xch;
+  mk::u64* part;
+  uint32_t* ctr;
+  float* amax_v;
+  int* amax_i;
+  mk::LayerW* table;
+  uint32_t* err;
+  mk::u64* trace;
+  mk::u64* marker;
+  uint32_t* epoch;
+};
+
+static MegaLayout mega_layout(void* ws, int L, int T) {
+  auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  char* p = (char*)ws;
+  MegaLayout m;
+  m.xch = (mk::u64*)p;
+  p += al(mega_xch_words(L) * 8);
+  m.part = (mk::u64*)p;
+  p += al((size_t)L * mk::NKV * (T / mk::KEYS) * mk::G * mk::PSTATE * 8);
+  m.ctr = (uint32_t*)p;
+  m.err = m.ctr + 2 * L + 32;
+  m.marker = (mk::u64*)(m.ctr + 2 * L + 48);
+  m.epoch = m.ctr + 2 * L + 52;
+  p += al((size_t)(2 * L + 64) * 4);
+  m.amax_v = (float*)p;
+  m.amax_i = (int*)(p + mk::NWG * 4);
+  p += al((size_t)mk::NWG * 8);
+  m.table = (mk::LayerW*)p;
+  p += al((size_t)L * sizeof(mk::LayerW));
+  m.trace = (mk::u64*)p;
+  return m;
+}
+
+hipError_t decode_mega_upload(hipStream_t st, void* ws, int L, int T, const MegaLayer* layers) {
+  MegaLayout lay = mega_layout(ws, L, T);
+  mk::LayerW tab[kMaxLayers];
+  for (int l = 0; l < L; ++l) {
+    for (int i = 0; i < 7; ++i) {
+      tab[l].w[i] = layers[l].w[i];
+      tab[l].sw[i] = layers[l].sw[i];
+      tab[l].cs[i] = layers[l].cs[i];
+    }
+    for (int i = 0; i < 3; ++i) tab[l].bias[i] = layers[l].bias[i];
+    tab[l].ln1 = layers[l].ln1;
+    tab[l].ln2 = layers[l].ln2;
+    tab[l].kc = layers[l].kc;
+    tab[l].vc = layers[l].vc;
+  }
+  return hipMemcpyAsync(lay.table, tab, sizeof(mk::LayerW) * L, hipMemcpyHostToDevice, st);
+}
+
+hipError_t decode_mega_launch(hipStream_t st, void* ws, const MegaStep& S) {
+  MegaLayout lay = mega_layout(ws, S.L, S.T);
+  // the exchange words and the partial attention states that follow them
+  const size_t part_words = (size_t)S.L * mk::NKV * (S.T / mk::KEYS) * mk::G * mk::PSTATE;
+  const size_t nwords = (size_t)(lay.part - lay.xch) + part_words;
+  const mk::u64 marker = mk::MAGIC ^ (mk::u64)nwords ^ ((mk::u64)S.T << 40);
+  hipLaunchKernelGGL(mk::k_decode_prep, dim3(mk::NWG), dim3(256), 0, st, lay.xch, nwords, lay.ctr,
+                     2 * S.L + 32, lay.err, lay.marker, marker, lay.epoch, S.token, S.table, S.V);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  mk::MegaArgs A;
+  A.layers = lay.table;
+  A.L = S.L;
+  A.T = S.T;
+  A.V = S.V;
+  A.pos = S.pos;
+  A.eps = S.eps;
+  A.final_norm = S.final_norm;
+  A.lm_w = S.lm_w;
+  A.lm_sw = S.lm_sw;
+  A.lm_cs = S.lm_cs;
+  A.rcos = S.rcos;
+  A.rsin = S.rsin;
+  A.kdelta = S.kdelta;
+  A.vdelta = S.vdelta;
+  A.logits = S.logits;
+  A.hidden_out = S.hidden_out;
+  A.mask = S.mask;
+  A.out_token = S.out_token;
+  A.xch = lay.xch;
+  A.part = lay.part;
+  A.ctr = lay.ctr;
+  A.amax_v = lay.amax_v;
+  A.amax_i = lay.amax_i;
+  A.err = lay.err;
+  const char* tr = getenv("ARK_MEGA_TRACE");
+  A.trace = (tr && tr[0] == '1') ? lay.trace : nullptr;
+  A.marker = lay.marker;
+  A.marker_value = marker;
+  A.epoch = lay.epoch;
+  void* args[] = {&A};
+  return hipLaunchCooperativeKernel((const void*)mk::k_decode, dim3(mk::NWG), dim3(mk::NT), args,
+                                    sizeof(mk::Shared), st);
+}
+
+size_t decode_mega_trace_offset(int L, int T) {
+  MegaLayout lay = mega_layout(nullptr, L, T);
+  return (size_t)((char*)lay.trace - (char*)nullptr);
+}
+
+hipError_t decode_mega_init() {
+  static bool done = false;
+  static hipError_t status = hipSuccess;
+  if (!done) {
+    done = true;
+    status = hipFuncSetAttribute((const void*)mk::k_decode,
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, sizeof(mk::Shared));
+    if (status == hipSuccess) {
+      int dev = 0, ncu = 0, coop = 0, nblk = 0;
+      hipGetDevice(&dev);
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+      hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&nblk, (const void*)mk::k_decode, mk::NT,
+                                                   sizeof(mk::Shared));
+      if (!coop || (long)ncu * nblk < mk::NWG) status = hipErrorCooperativeLaunchTooLarge;
+    }
+  }
+  return status;
+}
+
+}  // namespace ark

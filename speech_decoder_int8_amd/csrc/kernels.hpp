@@ -84,4 +84,40 @@ hipError_t launch_attention(hipStream_t st, int B, int S, int NH, int NKV, int T
                             const float* k_cache, const float* v_cache, const float* k_delta,
                             const float* v_delta, const PosArgs& pos, float* out, void* ws);
 
+// ---- persistent batch-1 decode step for the ARK geometry (k_decode.hip)
+struct MegaLayer {
+  const int8_t* w[7];  // q, k, v, o, gate, up, down
+  const float* sw[7];
+  const int32_t* cs[7];
+  const float* bias[3];
+  const float* ln1;
+  const float* ln2;
+  const float* kc;
+  const float* vc;
+};
+struct MegaStep {
+  int L, T, V, pos;
+  double eps;
+  const int32_t* token;
+  const uint16_t* table;
+  const float* final_norm;
+  const int8_t* lm_w;
+  const float* lm_sw;
+  const int32_t* lm_cs;
+  const double* rcos;
+  const double* rsin;
+  float* kdelta;
+  float* vdelta;
+  float* logits;
+  float* hidden_out;
+  const uint8_t* mask;
+  int32_t* out_token;
+};
+bool decode_mega_supported(int H, int NH, int NKV, int D, int I, int T, int L);
+size_t decode_mega_ws_bytes(int L, int T);
+size_t decode_mega_trace_offset(int L, int T);
+hipError_t decode_mega_init();
+hipError_t decode_mega_upload(hipStream_t st, void* ws, int L, int T, const MegaLayer* layers);
+hipError_t decode_mega_launch(hipStream_t st, void* ws, const MegaStep& S);
+
 }  // namespace ark

@@ -9,8 +9,12 @@ oracle's own tokens):
   gap    [n_steps + 1, B]  top-2 gap of the unmasked logits at each step
   top_ids / top_vals       [n_steps + 1, B, 16] largest unmasked logits
   samp_idx [512]; samp_vals [n_steps + 1, B, 512]  logits at fixed indices
-  hid_last [n_steps + 1, B, H]  residual stream of each sequence's last row
+  hid_last [n_steps + 1, B', H]  residual stream of each sequence's last row
   kd_* / vd_*              deltas of layers (0, L/2, L-1) at sampled rows
+  seqs [B']                the sequences hid_last and the deltas keep (all of
+                           them up to 4, else first, middle and last)
+`python tests/golden/make_golden.py --trim c3` applies that subsetting to a
+file written before it existed.
 """
 from __future__ import annotations
 
@@ -117,11 +121,33 @@ def run(name: str) -> None:
         out[k] = np.stack(v)
     out.update(deltas)
     path = os.path.join(HERE, f"{name}.npz")
-    np.savez_compressed(path, **out)
+    np.savez_compressed(path, **trim(out, B))
     print(f"[{name}] wrote {path} ({os.path.getsize(path) / 1e3:.0f} kB) in {time.time() - t0:.0f}s",
           flush=True)
 
 
+def trim(out: dict, B: int) -> dict:
+    """Keep the per-sequence hidden states and deltas of a few sequences."""
+    if "seqs" in out:
+        return out
+    seqs = np.arange(B) if B <= 4 else np.array(sorted({0, B // 2, B - 1}))
+    res = {}
+    for k, v in out.items():
+        if k == "hid_last" or k.startswith(("kd_", "vd_")):
+            v = v[:, seqs] if k == "hid_last" else v[seqs]
+        res[k] = v
+    res["seqs"] = seqs.astype(np.int32)
+    return res
+
+
 if __name__ == "__main__":
-    for n in sys.argv[1:]:
-        run(n)
+    args = sys.argv[1:]
+    if args and args[0] == "--trim":
+        for n in args[1:]:
+            path = os.path.join(HERE, f"{n}.npz")
+            g = dict(np.load(path))
+            np.savez_compressed(path, **trim(g, g["tokens"].shape[1]))
+            print(f"[{n}] trimmed to {os.path.getsize(path) / 1e3:.0f} kB")
+    else:
+        for n in args:
+            run(n)

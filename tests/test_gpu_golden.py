@@ -38,12 +38,13 @@ def _check(g, step, gs, kd, vd, hid, mask, near_ties):
     top = np.take_along_axis(lg, g["top_ids"][k].astype(np.int64), axis=1)
     err = max(err, np.max(np.abs(top - g["top_vals"][k])) / scale)
     assert err <= TOL, f"step {step}: logits relative error {err:.3g}"
-    r = rel(host(hid)[:, -1, :], g["hid_last"][k])
+    seqs = g["seqs"] if "seqs" in g else np.arange(lg.shape[0])
+    r = rel(host(hid)[seqs, -1, :], g["hid_last"][k])
     assert r <= TOL, f"step {step}: hidden relative error {r:.3g}"
     rows = g[f"rows_s{step}"]
     for l in g["layers"]:
         for nm, d in (("kd", kd), ("vd", vd)):
-            r = rel(host(d[int(l)])[:, rows], g[f"{nm}_s{step}_l{int(l)}"])
+            r = rel(host(d[int(l)])[seqs][:, rows], g[f"{nm}_s{step}_l{int(l)}"])
             assert r <= TOL, f"step {step}: {nm} layer {l} relative error {r:.3g}"
     tok = np.where(mask[None, :] == 1, -np.inf, lg).argmax(axis=1)
     want = g["tokens"][step]
