@@ -20,30 +20,64 @@ typedef long i64x2 __attribute__((ext_vector_type(2)));
 constexpr int kWave = 64;
 constexpr int kHeadDim = 128;
 
+// Wave-wide reductions, result in every lane (all 64 lanes must be active).
+// Within each row of 16 lanes: DPP exchanges with lane^1, lane^2 (quad
+// permutes), the mirror lane of the 8-lane half and of the 16-lane row, so
+// every lane holds its row's result; the four rows are then combined in the
+// fixed order 0, 16, 32, 48 from lane reads.  Integer sums and min/max are
+// exact; a double sum is rounded in that fixed order.
+namespace dpp {
+constexpr int kXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kHalfMirror = 0x141; // row_half_mirror
+constexpr int kMirror = 0x140;     // row_mirror
+template <int C>
+__device__ __forceinline__ int mov(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, C, 0xF, 0xF, false);
+}
+template <int C>
+__device__ __forceinline__ float mov(float v) {
+  return __int_as_float(mov<C>(__float_as_int(v)));
+}
+template <int C>
+__device__ __forceinline__ double mov(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = mov<C>((int)b), hi = mov<C>((int)(b >> 32));
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+__device__ __forceinline__ int lane_read(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ float lane_read(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ double lane_read(double v, int l) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)b, l), hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+template <typename T, typename Op>
+__device__ __forceinline__ T all_reduce(T v, Op op) {
+  v = op(v, mov<kXor1>(v));
+  v = op(v, mov<kXor2>(v));
+  v = op(v, mov<kHalfMirror>(v));
+  v = op(v, mov<kMirror>(v));
+  return op(op(op(lane_read(v, 0), lane_read(v, 16)), lane_read(v, 32)), lane_read(v, 48));
+}
+}  // namespace dpp
+
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return dpp::all_reduce(v, [](double a, double b) { return a + b; });
 }
 __device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return dpp::all_reduce(v, [](int a, int b) { return a + b; });
 }
 __device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
-  return v;
+  return dpp::all_reduce(v, [](float a, float b) { return fminf(a, b); });
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  return dpp::all_reduce(v, [](float a, float b) { return fmaxf(a, b); });
 }
 __device__ __forceinline__ double wave_max(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, kWave));
-  return v;
+  return dpp::all_reduce(v, [](double a, double b) { return fmax(a, b); });
 }
 
 // Block-wide reductions for blockDim.x == NT (multiple of 64).  `red` must

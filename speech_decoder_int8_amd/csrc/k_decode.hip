@@ -11,20 +11,19 @@
 // latency-bound streams; here the weight stream runs ahead of the
 // dependency chain instead.
 //
-// Work split: 256 workgroups x 16 waves.  Wave 0 ("poller") waits for the
-// inputs of each phase and never has weight loads in flight, so its waits
-// are not serialised behind the weight stream (vector loads complete in
-// order).  Waves 1..15 ("streamers") own fixed output rows of every phase and
-// issue the loads of a phase's weights into registers one phase ahead (at
-// most 14 KiB per wave, which fits the 128 VGPRs a 16-wave workgroup allows).
+// Work split: 256 workgroups x 16 waves.  In the layers every wave streams
+// weights: it owns fixed output rows (or, for the down projection, half a
+// row) of each phase and issues the loads of a phase's weights into
+// registers ahead of the phase's input.  The attention of a token runs on
+// 2 x (live 64-key items, at most 8) workgroups; the gate/up rows are spread
+// over the other workgroups only, which stream them while the attention runs.
 //
 // Data exchange between workgroups (which sit on different XCDs with
 // separate L2s) uses 64-bit words (fp32 value | tag << 32) written with
 // device-scope stores and read with device-scope loads, so no cache
-// write-back/invalidate fence is needed; every buffer is written once per
-// launch (the preparation kernel zeroes them), so tag 1 means "written".
-// Every wait is bounded: on time-out the kernel records an error and runs
-// to completion.
+// write-back/invalidate fence is needed.  The tag is a per-launch epoch kept
+// in the workspace, so words of earlier launches never match.  Every wait is
+// bounded: on time-out the kernel records an error and runs to completion.
 #include <float.h>
 #include <limits.h>
 #include <stdlib.h>
@@ -39,7 +38,8 @@ constexpr int H = 2048, NH = 16, NKV = 2, D = kHeadDim, Q = NH * D, KVD = NKV * 
 constexpr int G = NH / NKV;               // query heads per KV head
 constexpr int NQKV = Q + 2 * KVD;         // 2560 q|k|v rows
 constexpr int NWG = 256, NT = 1024, NW = 16, NS = NW - 1;
-constexpr int KEYS = 64;                  // cache rows per attention item
+constexpr int KEYS = 64;                  // cache rows per attention chunk
+constexpr int NI = 8;                     // attention items per KV head (chunk stride)
 constexpr int PART = 2 + D;               // fp64 words of one partial softmax state
 constexpr uint32_t SPIN_LIMIT = 1u << 15;  // ~30-60 ms per wait: a failure ends in seconds
 constexpr int NREP = 8;                   // replicas of each broadcast vector (one per XCD)
@@ -52,12 +52,17 @@ constexpr int OFF_QKV = 0, OFF_X0 = NQKV, OFF_ATT = OFF_X0 + NREP * H,
               OFF_X1 = OFF_ATT + NREP * Q, OFF_A = OFF_X1 + NREP * H,
               XCH_LAYER = OFF_A + NREP * I;
 
-// rows per workgroup in each phase, and the rotation that spreads them over
-// the 15 streamers (o rows go to streamers 0..7, down rows to 7..14)
-constexpr int R_QKV = NQKV / NWG, R_O = H / NWG, R_GU = I / NWG, R_D = H / NWG;
-static_assert(R_QKV * NWG == NQKV && R_O * NWG == H && R_GU * NWG == I, "row split");
-constexpr int ROT_QKV = 0, ROT_O = 0, ROT_GU = 0, ROT_D = 8;
-static_assert(R_QKV <= 15 && R_O <= 15 && R_D <= 15 && R_GU <= 45, "rows per streamer");
+// rows per workgroup of the q|k|v, o and down phases (wave s owns row s of
+// q|k|v and o; waves 2r and 2r+1 split down row r); the gate/up rows are
+// spread at run time over the workgroups without attention work, at most
+// GU_ROWS per wave
+constexpr int R_QKV = NQKV / NWG, R_O = H / NWG, R_D = H / NWG;
+static_assert(R_QKV * NWG == NQKV && R_O * NWG == H && R_D * NWG == H, "row split");
+static_assert(R_QKV <= NW && R_O <= NW && 2 * R_D == NW, "rows per wave");
+constexpr int GU_ROWS = 3;
+static_assert((I + (NWG - NKV * NI) - 1) / (NWG - NKV * NI) <= GU_ROWS * NW, "gate/up rows");
+constexpr int D_UNITS = (I / 1024 + 2) / 2;   // 1 KiB units of half a down row (6)
+constexpr int GU_LDS = 16 * 1024;             // stage offset of the gate/up units in LDS
 
 typedef unsigned long long u64;
 typedef __attribute__((address_space(1))) const i32x4 gi32x4;
@@ -189,6 +194,32 @@ __device__ __forceinline__ void stamp(u64* t, int i, int lane) {
   if (t && lane == 0) t[i] = __builtin_amdgcn_s_memrealtime();
 }
 
+// exp(x) in fp64, written out so its constants come from LDS at the point
+// of use (kept in registers across the kernel they would be spilled):
+// x = k ln2 + r with |r| <= ln2 / 2 (two-part ln2, k ln2_hi exact for
+// |k| < 2^11), e^r by its Taylor series to degree 13 (the first dropped term
+// is below 5e-18), times 2^k.  A few fp64 ulp from the correctly rounded
+// value; every caller rounds its result to fp32 afterwards.
+// Table: 1/k! for k = 0..13 (each correctly rounded), ln2_hi (ln2 with the
+// low 21 mantissa bits cleared), ln2_lo = ln2 - ln2_hi, 1/ln2.
+__constant__ double kExpTab[17] = {
+    0x1.0p+0, 0x1.0p+0, 0x1.0p-1, 0x1.5555555555555p-3, 0x1.5555555555555p-5,
+    0x1.1111111111111p-7, 0x1.6c16c16c16c17p-10, 0x1.a01a01a01a01ap-13,
+    0x1.a01a01a01a01ap-16, 0x1.71de3a556c734p-19, 0x1.27e4fb7789f5cp-22,
+    0x1.ae64567f544e4p-26, 0x1.1eed8eff8d898p-29, 0x1.6124613a86d09p-33,
+    0x1.62e42fee00000p-1, 0x1.a39ef35793c76p-33, 0x1.71547652b82fep+0};
+
+__device__ __forceinline__ double exp_t(double x, const double* t) {
+  if (!(x > -746.0)) return (x != x) ? x : 0.0;  // NaN stays NaN; underflow to 0
+  if (x > 709.8) return INFINITY;
+  const double k = rint(x * t[16]);
+  const double r = fma(-k, t[15], fma(-k, t[14], x));
+  double p = t[13];
+#pragma unroll
+  for (int i = 12; i >= 0; --i) p = fma(p, r, t[i]);
+  return ldexp(p, (int)k);
+}
+
 struct Shared {
   float xs[H];         // layer input (kept for the o residual)
   float x1s[H];        // input of the MLP half (kept for the down residual)
@@ -199,6 +230,10 @@ struct Shared {
   float redf[2 * NW];
   float bestv[NW];
   int besti[NW];
+  int redi[NW];
+  double expc[17];     // exp_t table
+  double rcos[D / 2];  // rotary table row of the position (attention workgroups)
+  double rsin[D / 2];
   int flag;
 };
 
@@ -279,13 +314,16 @@ __device__ __forceinline__ void unstage(const unsigned char* stage, float* dst, 
 // ----------------------------------------------------------- prologues --
 // RMSNorm (fp64 inside) of x with gain g, then the dynamic uint8 quantiser;
 // shifted codes to sh.codes.  All 512 threads.
-__device__ QParam prologue_norm(const float* x, const float* g, double eps, Shared& sh, int tid) {
+__device__ QParam prologue_norm(const float* x, const float* g, double eps, Shared& sh, int tid,
+                                u64* tr = nullptr) {
+  if (tid == 0) stamp(tr, 0, 0);
   double ss = 0.0;
   for (int i = tid; i < H; i += NT) {
     const double v = x[i];
     ss += v * v;
   }
   ss = block_sum<NT>(ss, sh.redd);
+  if (tid == 0) stamp(tr, 1, 0);
   const double rs = 1.0 / sqrt(ss / (double)H + eps);
   float hv[H / NT];
   float lo = INFINITY, hi = -INFINITY;
@@ -297,10 +335,12 @@ __device__ QParam prologue_norm(const float* x, const float* g, double eps, Shar
     hi = fmaxf(hi, hv[j]);
   }
   block_minmax<NT>(lo, hi, sh.redf);
+  if (tid == 0) stamp(tr, 2, 0);
   const QParam p = quant_param(lo, hi);
 #pragma unroll
   for (int j = 0; j < H / NT; ++j) sh.codes[tid + j * NT] = shift_code(quant_code(hv[j], p));
   __syncthreads();
+  if (tid == 0) stamp(tr, 3, 0);
   return p;
 }
 
@@ -324,9 +364,9 @@ __device__ QParam prologue_plain(const unsigned char* stage, int n, Shared& sh, 
 }
 
 // ------------------------------------------------------ weight streams --
-// Rows of a phase: workgroup w owns rows [w*R, (w+1)*R); streamer s (0..14)
-// owns local rows i = (s + rot) % 15 + 15k.
-__device__ __forceinline__ int row_local(int s, int rot, int k) { return (s + rot) % NS + NS * k; }
+// Rows of a phase: workgroup w owns rows [w*R, (w+1)*R); wave s owns local
+// rows i = (s + rot) % 16 + 16k.
+__device__ __forceinline__ int row_local(int s, int rot, int k) { return (s + rot) % NW + NW * k; }
 
 // Load NR rows x U units (1 KiB per unit: 16 bytes per lane) of a K-byte
 // row-major int8 matrix into registers, plus per-row metadata.
@@ -408,15 +448,16 @@ __device__ __forceinline__ void run_units(i32x4 (&buf)[W], Addr addr, Use use) {
 }
 
 // ---------------------------------------------------------- attention --
-// Work item (KV head g, split sp): keys [sp*64, sp*64+64) for the 8 query
-// heads of g.  Only splits holding a key at or before the position run (the
-// rest would be masked whole).  With one live split the item finishes the
-// softmax itself.  Otherwise splits 1.. publish their partial softmax state
-// per head (running max, sum and weighted values, fp64 as two tagged 32-bit
-// halves) and split 0 waits for them, merges and publishes the output.
+// Work item (KV head g, item sp < 8): the live 64-key chunks sp, sp+8, ...
+// (chunks holding a key at or before the position) for the 8 query heads of
+// g, combined with the online-softmax update.  With one item per head the
+// item finishes the softmax itself.  Otherwise items 1.. publish their
+// partial softmax state per head (running max, sum and weighted values,
+// fp64 as two tagged 32-bit halves) and item 0 waits for them, merges and
+// publishes the output.
 //
 // LDS, after the 16 KiB that stage the layer input: keys and values of the
-// split as pairs of rows 1040 bytes apart (key k at float offset kv_row(k)),
+// chunk as pairs of rows 1040 bytes apart (key k at float offset kv_row(k)),
 // so a score thread's 16-byte reads of its key row, 8 consecutive pairs at a
 // time, cover all 32 banks; then the q|k|v words, rotated q and k, v, the
 // softmax weights and per-head max/sum.
@@ -424,20 +465,18 @@ constexpr int ATT_KV = 16 * 1024;                      // byte offset in stage
 constexpr int ATT_QKV = ATT_KV + 2 * (KEYS / 2) * 260 * 4;
 constexpr int ATT_Q = ATT_QKV + 10 * 1024;
 constexpr int ATT_END = ATT_Q + (G + 2) * D * 4 + G * KEYS * 8 + 2 * G * 8;
-constexpr int PSTATE = 2 * PART;                       // words per (split, head)
-constexpr int MERGE_BATCH = 4;                         // splits merged per pass
+constexpr int PSTATE = 2 * PART;                       // words per (item, head)
+constexpr int MERGE_BATCH = 4;                         // items merged per pass
 static_assert(ATT_END <= 104 * 1024, "attention staging exceeds LDS stage");
 static_assert(ATT_KV + MERGE_BATCH * G * PSTATE * 8 + 1024 <= ATT_Q, "merge batch too large");
 
 __device__ __forceinline__ int kv_row(int k) { return (k >> 1) * 260 + (k & 1) * D; }
 
-// All waves: start copying the live cache rows of item (g, sp) into LDS (two
-// keys per 1 KiB instruction, pairs spread over the waves).  Completes by the
-// next poll of the wave.
-__device__ __forceinline__ void load_kv(const MegaArgs& A, int l, int item, Shared& sh, int wave,
-                                        int lane) {
-  const int nsplit = A.T / KEYS;
-  const int g = item / nsplit, j0 = (item % nsplit) * KEYS;
+// All waves: start copying the live cache rows of KV head g in the chunk
+// starting at j0 into LDS (two keys per 1 KiB instruction, pairs spread over
+// the waves).  Completes by the wave's next full wait.
+__device__ __forceinline__ void load_kv(const MegaArgs& A, int l, int g, int j0, Shared& sh,
+                                        int wave, int lane) {
   const int npair = (min(KEYS, A.pos + 1 - j0) + 1) / 2;
   const LayerW& Lw = A.layers[l];
   float* Ks = (float*)(sh.stage + ATT_KV);
@@ -466,11 +505,20 @@ __device__ __forceinline__ double get_tagged_f64(const u64* p) {
   return __longlong_as_double((long long)((p[0] & 0xffffffffull) | (p[1] << 32)));
 }
 
-__device__ void attention_item(const MegaArgs& A, uint32_t epoch, int l, int item, int nlive,
-                               Shared& sh, u64* xl, int tid, int lane, int wave) {
-  const int nsplit = A.T / KEYS;
-  const int g = item / nsplit, sp = item % nsplit;
-  const int j0 = sp * KEYS;
+// Online-softmax merge of a state (m, l, o) into (M, L, O).
+__device__ __forceinline__ void softmax_merge(double& M, double& L, double& O, double m, double l,
+                                              double o, const double* et) {
+  const double Mn = fmax(M, m);
+  const double a = exp_t(M - Mn, et);   // 0 while M is still -inf
+  const double b = exp_t(m - Mn, et);
+  L = L * a + l * b;
+  O = O * a + o * b;
+  M = Mn;
+}
+
+__device__ void attention_item(const MegaArgs& A, uint32_t epoch, int l, int item, int nitem,
+                               int nchunk, Shared& sh, u64* xl, int tid, int lane, int wave) {
+  const int g = item / NI, sp = item % NI;
   const int p = A.pos;
   float* Ks = (float*)(sh.stage + ATT_KV);
   float* Vs = Ks + (KEYS / 2) * 260;
@@ -487,14 +535,14 @@ __device__ void attention_item(const MegaArgs& A, uint32_t epoch, int l, int ite
     const int n0 = wave < G ? (g * G + wave) * D : (wave == G ? Q + g * D : Q + KVD + g * D);
     poll_range(xl + OFF_QKV, n0, n0 + D, R_QKV, qst + wave * D * 8, A.err, lane, epoch);
   }
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's cache rows
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's cache rows of the first chunk
   if (wave == 0) stamp(tr, 0, lane);
   __syncthreads();
   // rotary embedding (fp64) of q and k at position p; v as is
   {
     const u64* s = (const u64*)qst;
-    const double* cs = A.rcos + (size_t)p * (D / 2);
-    const double* sn = A.rsin + (size_t)p * (D / 2);
+    const double* cs = sh.rcos;
+    const double* sn = sh.rsin;
     for (int t = tid; t < (G + 1) * (D / 2); t += NT) {
       const int head = t / (D / 2), j = t % (D / 2);
       const double x1 = __uint_as_float((uint32_t)s[head * D + j]);
@@ -507,93 +555,103 @@ __device__ void attention_item(const MegaArgs& A, uint32_t epoch, int l, int ite
     for (int t = tid; t < D; t += NT) vv[t] = __uint_as_float((uint32_t)s[(G + 1) * D + t]);
   }
   __syncthreads();
-  // this call's row replaces cache row p; split 0 publishes the deltas
-  if (p >= j0 && p < j0 + KEYS) {
-    for (int t = tid; t < D; t += NT) {
-      Ks[kv_row(p - j0) + t] = kr[t];
-      Vs[kv_row(p - j0) + t] = vv[t];
-    }
-  }
+  // item 0 publishes the deltas
   if (sp == 0) {
     for (int t = tid; t < D; t += NT) {
       A.kdelta[(size_t)l * KVD + g * D + t] = kr[t];
       A.vdelta[(size_t)l * KVD + g * D + t] = vv[t];
     }
   }
-  __syncthreads();
-  if (tid == 0) stamp(tr, 1, lane);
-  // scores on waves 0..7: thread -> (head = wave, key jj); keys after the
-  // position are selected away (weight exactly 0, row never read)
-  if (wave < G) {
-    const int hh = wave, jj = 2 * (lane & 31) + (lane >> 5), j = j0 + jj;
-    double sc = -INFINITY;
-    if (j <= p) {
-      const float4* qh = (const float4*)(qr + hh * D);
-      const float4* kj = (const float4*)(Ks + kv_row(jj));
-      double d0 = 0.0, d1 = 0.0;
-#pragma unroll 4
-      for (int d = 0; d < D / 4; ++d) {
-        const float4 qv = qh[d], kv = kj[d];
-        d0 = fma((double)qv.x, (double)kv.x, d0);
-        d1 = fma((double)qv.y, (double)kv.y, d1);
-        d0 = fma((double)qv.z, (double)kv.z, d0);
-        d1 = fma((double)qv.w, (double)kv.w, d1);
+  const int hv = wave >> 1, dv = (wave & 1) * 64 + lane;  // PV thread -> (head, dim)
+  double M = -INFINITY, Lsum = 0.0, O = 0.0;
+  for (int c = sp; c < nchunk; c += NI) {
+    const int j0 = c * KEYS;
+    if (c != sp) {
+      __syncthreads();  // the previous chunk's values and weights are used
+      load_kv(A, l, g, j0, sh, wave, lane);
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+    __syncthreads();
+    // this call's row replaces cache row p
+    if (p >= j0 && p < j0 + KEYS)
+      for (int t = tid; t < D; t += NT) {
+        Ks[kv_row(p - j0) + t] = kr[t];
+        Vs[kv_row(p - j0) + t] = vv[t];
       }
-      sc = (d0 + d1) / sqrt((double)D);
+    __syncthreads();
+    if (tid == 0) stamp(tr, 1, lane);
+    // scores on waves 0..7: thread -> (head = wave, key jj); keys after the
+    // position are selected away (weight exactly 0, row never read)
+    if (wave < G) {
+      const int hh = wave, jj = 2 * (lane & 31) + (lane >> 5), j = j0 + jj;
+      double sc = -INFINITY;
+      if (j <= p) {
+        const float4* qh = (const float4*)(qr + hh * D);
+        const float4* kj = (const float4*)(Ks + kv_row(jj));
+        double d0 = 0.0, d1 = 0.0;
+#pragma unroll 4
+        for (int d = 0; d < D / 4; ++d) {
+          const float4 qv = qh[d], kv = kj[d];
+          d0 = fma((double)qv.x, (double)kv.x, d0);
+          d1 = fma((double)qv.y, (double)kv.y, d1);
+          d0 = fma((double)qv.z, (double)kv.z, d0);
+          d1 = fma((double)qv.w, (double)kv.w, d1);
+        }
+        sc = (d0 + d1) / sqrt((double)D);
+      }
+      const double m = wave_max(sc);
+      const double e = (sc == -INFINITY) ? 0.0 : exp_t(sc - m, sh.expc);
+      const double lsum = wave_sum(e);
+      ps[hh * KEYS + jj] = e;
+      if (lane == 0) {
+        hm[2 * hh] = m;
+        hm[2 * hh + 1] = lsum;
+      }
     }
-    const double m = wave_max(sc);
-    const double e = (sc == -INFINITY) ? 0.0 : exp(sc - m);
-    const double lsum = wave_sum(e);
-    ps[hh * KEYS + jj] = e;
-    if (lane == 0) {
-      hm[2 * hh] = m;
-      hm[2 * hh + 1] = lsum;
+    __syncthreads();
+    if (tid == 0) stamp(tr, 2, lane);
+    // weighted values of the chunk, folded into the running state
+    const int nk = min(KEYS, p + 1 - j0);
+    double o0 = 0.0, o1 = 0.0;
+    int k = 0;
+    for (; k + 1 < nk; k += 2) {
+      o0 = fma(ps[hv * KEYS + k], (double)Vs[kv_row(k) + dv], o0);
+      o1 = fma(ps[hv * KEYS + k + 1], (double)Vs[kv_row(k + 1) + dv], o1);
     }
+    if (k < nk) o0 = fma(ps[hv * KEYS + k], (double)Vs[kv_row(k) + dv], o0);
+    softmax_merge(M, Lsum, O, hm[2 * hv], hm[2 * hv + 1], o0 + o1, sh.expc);
   }
-  __syncthreads();
-  if (tid == 0) stamp(tr, 2, lane);
-  // weighted values: thread -> (head = wave / 2, dim = (wave % 2) * 64 + lane)
-  const int hv = wave >> 1, dv = (wave & 1) * 64 + lane;
-  const int nk = min(KEYS, p + 1 - j0);
-  double o = 0.0;
-  for (int k = 0; k < nk; ++k) o = fma(ps[hv * KEYS + k], (double)Vs[kv_row(k) + dv], o);
-  if (nlive == 1) {
-    xput_rep(xl + OFF_ATT, Q, (g * G + hv) * D + dv, (float)(o / hm[2 * hv + 1]), epoch);
+  if (nitem == 1) {
+    xput_rep(xl + OFF_ATT, Q, (g * G + hv) * D + dv, (float)(O / Lsum), epoch);
     return;
   }
-  u64* part = A.part + ((size_t)l * NKV + g) * nsplit * G * PSTATE;  // split 0 unused
+  u64* part = A.part + ((size_t)l * NKV + g) * NI * G * PSTATE;  // item 0's slot unused
   if (sp > 0) {
     u64* pst = part + ((size_t)sp * G + hv) * PSTATE;
     if (dv == 0) {
-      put_tagged_f64(pst, hm[2 * hv], epoch);
-      put_tagged_f64(pst + 2, hm[2 * hv + 1], epoch);
+      put_tagged_f64(pst, M, epoch);
+      put_tagged_f64(pst + 2, Lsum, epoch);
     }
-    put_tagged_f64(pst + 4 + 2 * dv, o, epoch);
+    put_tagged_f64(pst + 4 + 2 * dv, O, epoch);
     return;
   }
   if (tid == 0) stamp(tr, 3, lane);
-  // split 0: merge the other live splits' states, MERGE_BATCH per pass
-  double M = hm[2 * hv], Lsum = hm[2 * hv + 1], O = o;
+  // item 0: merge the other items' states, MERGE_BATCH per pass
   const u64* pb = (const u64*)(sh.stage + ATT_KV);
-  for (int s0 = 1; s0 < nlive; s0 += MERGE_BATCH) {
-    const int ns = min(MERGE_BATCH, nlive - s0);
+  for (int s0 = 1; s0 < nitem; s0 += MERGE_BATCH) {
+    const int ns = min(MERGE_BATCH, nitem - s0);
     const int n = ns * G * PSTATE;
     const int chunk = ((n + NW - 1) / NW + 127) & ~127;
     const int c0 = wave * chunk, c1 = min(n, c0 + chunk);
-    __syncthreads();  // the previous batch is merged (or the values read)
+    __syncthreads();  // the chunk's values (or the previous batch) are used
     if (c0 < c1)
       poll_range(part + (size_t)s0 * G * PSTATE, c0, c1, G * PSTATE, sh.stage + ATT_KV + c0 * 8,
                  A.err, lane, epoch);
     __syncthreads();
     for (int s = 0; s < ns; ++s) {
       const u64* q = pb + ((size_t)s * G + hv) * PSTATE;
-      const double ms = get_tagged_f64(q);
-      const double Mn = fmax(M, ms);
-      const double a = exp(M - Mn);
-      const double b = exp(ms - Mn);
-      Lsum = Lsum * a + get_tagged_f64(q + 2) * b;
-      O = O * a + get_tagged_f64(q + 4 + 2 * dv) * b;
-      M = Mn;
+      softmax_merge(M, Lsum, O, get_tagged_f64(q), get_tagged_f64(q + 2),
+                    get_tagged_f64(q + 4 + 2 * dv), sh.expc);
     }
   }
   if (tid == 0) stamp(tr, 4, lane);
@@ -606,79 +664,93 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
   Shared& sh = *(Shared*)smem_raw;
   int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(wave_id());
-  const bool streamer = wave > 0;
   int w = blockIdx.x;
-  // Per-lane byte offset, redefined opaquely in every layer so the compiler
-  // recomputes addresses in the loop instead of keeping dozens of hoisted
-  // 64-bit addresses live next to the prefetched weights.
+  // Per-lane byte offset and wave index, redefined opaquely in every layer so
+  // the compiler recomputes addresses in the loop instead of keeping dozens
+  // of hoisted 64-bit addresses live next to the prefetched weights.
   int lane16 = lane * 16;
-  int s = wave - 1;  // streamer index 0..14
+  int s = wave;
 
-  // weight registers (streamers)
-  constexpr int W = 8;                 // units in flight per streamer (big phases)
-  constexpr int NGU = 3 * 2 * 2;       // gate/up units: 3 pairs x {gate, up} x 2
-  constexpr int ND = 11;               // down units: one 11008-byte row
+  // attention items: (KV head g, item sp < NI) on workgroup g * NI + sp when
+  // chunk sp holds a key at or before the position
+  const int nchunk = A.pos / KEYS + 1;
+  const int nitem = min(NI, nchunk);
+  const bool att = w < NKV * NI && (w % NI) < nitem;
+  // gate/up rows: rg per workgroup without attention work, by rank
+  const int natt = NKV * nitem;
+  const int rank = w - (w >= NKV * NI ? natt : (w / NI) * nitem + min(w % NI, nitem));
+  const int rg = (I + (NWG - natt) - 1) / (NWG - natt);
+  const int gu0 = att ? 0 : rank * rg;
+  const int ngu = att ? 0 : max(0, min(rg, I - gu0));
+
+  // weight registers
+  constexpr int W = 8;                      // units in flight per wave (big phases)
+  constexpr int NGU = GU_ROWS * 2 * 2;      // gate/up units: rows x {gate, up} x 2
+  static_assert(NGU == W + 4, "gate/up: 8 units in registers, 4 in LDS");
   i32x4 wq[1][2], wo[1][2], win[W];
-  float sq[1], so[1], sg[3], su[3], sd[1];
-  int cq[1], co[1], cg[3], cu[3], cd[1];
+  float sq[1], so[1], sg[GU_ROWS], su[GU_ROWS], sd;
+  int cq[1], co[1], cg[GU_ROWS], cu[GU_ROWS], cd;
   float bq[1] = {0.f};
 
   auto issue_qkv = [&](int l) {
     const LayerW& Lw = A.layers[l];
-    // rows of the concatenated q|k|v space: [w*10, w*10+10)
+    // rows of the concatenated q|k|v space: [w*10, w*10+10), row s
+    const bool valid = s < R_QKV;
+    const int n = w * R_QKV + (valid ? s : 0);
+    const int seg = n < Q ? 0 : (n < Q + KVD ? 1 : 2);
+    const int nl = n - (seg == 0 ? 0 : (seg == 1 ? Q : Q + KVD));
+    const int8_t* p = Lw.w[seg] + (size_t)nl * H;
+    sq[0] = valid ? ldg(Lw.sw[seg] + nl) : 0.f;
+    cq[0] = valid ? ldg(Lw.cs[seg] + nl) : 0;
+    bq[0] = valid ? ldg(Lw.bias[seg] + nl) : 0.f;
 #pragma unroll
-    for (int k = 0; k < 1; ++k) {
-      const int i = row_local(s, ROT_QKV, k);
-      const bool valid = i < R_QKV;
-      const int n = w * R_QKV + (valid ? i : 0);
-      const int seg = n < Q ? 0 : (n < Q + KVD ? 1 : 2);
-      const int nl = n - (seg == 0 ? 0 : (seg == 1 ? Q : Q + KVD));
-      const int8_t* p = Lw.w[seg] + (size_t)nl * H;
-      sq[k] = valid ? ldg(Lw.sw[seg] + nl) : 0.f;
-      cq[k] = valid ? ldg(Lw.cs[seg] + nl) : 0;
-      bq[k] = valid ? ldg(Lw.bias[seg] + nl) : 0.f;
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-        wq[k][u] = valid ? ldg_nt(p + u * 1024 + lane16)
-                         : i32x4{0, 0, 0, 0};
-    }
+    for (int u = 0; u < 2; ++u) wq[0][u] = valid ? ldg_nt(p + u * 1024 + lane16) : i32x4{0, 0, 0, 0};
   };
-  auto issue_o_gu = [&](int l) {
+  auto issue_o = [&](int l) {
     const LayerW& Lw = A.layers[l];
-    load_rows<1, 2>(wo, so, co, Lw.w[3], Lw.sw[3], Lw.cs[3], Q, w * R_O, R_O, s, ROT_O, lane16);
+    load_rows<1, 2>(wo, so, co, Lw.w[3], Lw.sw[3], Lw.cs[3], Q, w * R_O, R_O, s, 0, lane16);
   };
-  // unit i of the gate/up phase: pair i / 4, matrix (i / 2) % 2, unit i % 2
+  // unit i of the gate/up phase: row s + 16 (i / 4), matrix (i / 2) % 2, unit i % 2
   auto gu_addr = [&](const LayerW& Lw, int i) -> const int8_t* {
     const int k = i / 4, m = (i / 2) % 2, u = i % 2;
-    const int r = row_local(s, ROT_GU, k);
-    if (r >= R_GU) return nullptr;
-    return Lw.w[4 + m] + (size_t)(w * R_GU + r) * H + u * 1024 + lane16;
+    const int r = s + NW * k;
+    if (r >= ngu) return nullptr;
+    return Lw.w[4 + m] + (size_t)(gu0 + r) * H + u * 1024 + lane16;
   };
+  // unit u of the down phase: half (s & 1) of row s >> 1
   auto down_addr = [&](const LayerW& Lw, int u) -> const int8_t* {
-    const int r = row_local(s, ROT_D, 0);
-    const int off = u * 1024 + lane16;
-    if (r >= R_D || off >= I) return nullptr;
-    return Lw.w[6] + (size_t)(w * R_D + r) * I + off;
+    const int off = ((s & 1) * D_UNITS + u) * 1024 + lane16;
+    if (off >= I) return nullptr;
+    return Lw.w[6] + (size_t)(w * R_D + (s >> 1)) * I + off;
   };
   auto issue_gate_up = [&](int l) {
     const LayerW& Lw = A.layers[l];
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      const int r = row_local(s, ROT_GU, k);
-      const bool valid = r < R_GU;
-      sg[k] = valid ? ldg(Lw.sw[4] + w * R_GU + r) : 0.f;
-      cg[k] = valid ? ldg(Lw.cs[4] + w * R_GU + r) : 0;
-      su[k] = valid ? ldg(Lw.sw[5] + w * R_GU + r) : 0.f;
-      cu[k] = valid ? ldg(Lw.cs[5] + w * R_GU + r) : 0;
+    for (int k = 0; k < GU_ROWS; ++k) {
+      const int r = s + NW * k;
+      const bool valid = r < ngu;
+      sg[k] = valid ? ldg(Lw.sw[4] + gu0 + r) : 0.f;
+      cg[k] = valid ? ldg(Lw.cs[4] + gu0 + r) : 0;
+      su[k] = valid ? ldg(Lw.sw[5] + gu0 + r) : 0.f;
+      cu[k] = valid ? ldg(Lw.cs[5] + gu0 + r) : 0;
     }
-    prime_units<NGU, W>(win, [&](int i) { return gu_addr(Lw, i); });
+    // units 0..7 into registers, the last row's four units into this wave's
+    // 4 KiB of LDS (stage bytes [16K, 80K) are free until the gate/up phase)
+    prime_units<W, W>(win, [&](int i) { return gu_addr(Lw, i); });
+    if (s + NW * 2 < ngu) {
+#pragma unroll
+      for (int i = W; i < NGU; ++i)
+        __builtin_amdgcn_global_load_lds(
+            (const void __attribute__((address_space(1)))*)gu_addr(Lw, i),
+            (void __attribute__((address_space(3)))*)(sh.stage + GU_LDS + s * 4096 + (i - W) * 1024),
+            16, 0, 2);
+    }
   };
   auto issue_down = [&](int l) {
     const LayerW& Lw = A.layers[l];
-    const int r = row_local(s, ROT_D, 0);
-    sd[0] = r < R_D ? ldg(Lw.sw[6] + w * R_D + r) : 0.f;
-    cd[0] = r < R_D ? ldg(Lw.cs[6] + w * R_D + r) : 0;
-    prime_units<ND, W>(win, [&](int u) { return down_addr(Lw, u); });
+    sd = ldg(Lw.sw[6] + w * R_D + (s >> 1));
+    cd = ldg(Lw.cs[6] + w * R_D + (s >> 1));
+    prime_units<D_UNITS, W>(win, [&](int u) { return down_addr(Lw, u); });
   };
 
   const size_t rep = xcc_id();
@@ -687,13 +759,13 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
     A.epoch[0] = epoch;           // the next launch counts on from here
     *A.marker = A.marker_value;   // the exchange area is initialised
   }
-  if (streamer) issue_qkv(0);
+  issue_qkv(0);
+  if (tid < 17) sh.expc[tid] = kExpTab[tid];
+  if (att && tid < D / 2) {
+    sh.rcos[tid] = A.rcos[(size_t)A.pos * (D / 2) + tid];
+    sh.rsin[tid] = A.rsin[(size_t)A.pos * (D / 2) + tid];
+  }
 
-  // attention items: (KV head, 64-key split) pairs whose split holds a key
-  // at or before the position, on workgroups g * nsplit + split
-  const int nsplit = A.T / KEYS;
-  const int nlive = min(nsplit, A.pos / KEYS + 1);
-  const bool att = w < NKV * nsplit && (w % nsplit) < nlive;
   for (int l = 0; l < A.L; ++l) {
     asm volatile("" : "+v"(lane16), "+v"(tid), "+v"(lane), "+s"(w), "+s"(s));
     const LayerW& Lw = A.layers[l];
@@ -702,44 +774,36 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
 
     // ---- q, k, v
     trace_at(A, w, l, 0);
-    if (att) load_kv(A, l, w, sh, wave, lane);
+    if (att) load_kv(A, l, w / NI, (w % NI) * KEYS, sh, wave, lane);
     load_gain(Lw.ln1, sh.gain, wave, lane16);
     trace_val(A, w, l, 11, poll_all(xl + OFF_X0 + rep * H, H, R_D, sh.stage, A.err, lane, wave, epoch, trace_sub(A, w, l, 27)));
     __syncthreads();
     trace_at(A, w, l, 1);
     unstage(sh.stage, sh.xs, H, tid);
     __syncthreads();
-    QParam qp = prologue_norm(sh.xs, sh.gain, A.eps, sh, tid);
+    QParam qp = prologue_norm(sh.xs, sh.gain, A.eps, sh, tid, trace_sub(A, w, l, 11));
     trace_at(A, w, l, 2);
-    if (streamer) {
-      const int zc = 128 - qp.z;
+    {
       int accs[1];
       dot_rows<1, 2>(wq, sh.codes, accs, lane16);
-#pragma unroll
-      for (int k = 0; k < 1; ++k) {
-        const int i = row_local(s, ROT_QKV, k);
-        const int acc = accs[k];
-        if (lane == 0 && i < R_QKV) {
-          float y = dequant(acc + zc * cq[k], qp.s, sq[k]);
-          y = y + bq[k];
-          xput(xl + OFF_QKV + w * R_QKV + i, y, epoch);
-        }
-      }
-      trace_done(A, w, l, 3, lane);
-      // workgroups without attention work stream the o rows and the first
-      // gate/up units while the attention runs elsewhere
-      if (!att) {
-        issue_o_gu(l);
-        issue_gate_up(l);
+      if (lane == 0 && s < R_QKV) {
+        float y = dequant(accs[0] + (128 - qp.z) * cq[0], qp.s, sq[0]);
+        y = y + bq[0];
+        xput(xl + OFF_QKV + w * R_QKV + s, y, epoch);
       }
     }
+    trace_done(A, w, l, 3, lane);
 
-    // ---- attention
+    // ---- attention; the other workgroups stream the o rows and their
+    // gate/up rows meanwhile
     if (att) {
       __syncthreads();
-      attention_item(A, epoch, l, w, nlive, sh, xl, tid, lane, wave);
+      attention_item(A, epoch, l, w, nitem, nchunk, sh, xl, tid, lane, wave);
       __syncthreads();
-      if (streamer) issue_o_gu(l);
+      issue_o(l);
+    } else {
+      issue_o(l);
+      issue_gate_up(l);
     }
 
     // ---- o projection + residual
@@ -749,90 +813,89 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
     __syncthreads();
     trace_at(A, w, l, 5);
     qp = prologue_plain(sh.stage, Q, sh, tid);
-    if (streamer) {
-      const int zc = 128 - qp.z;
+    {
       int accs[1];
       dot_rows<1, 2>(wo, sh.codes, accs, lane16);
-#pragma unroll
-      for (int k = 0; k < 1; ++k) {
-        const int i = row_local(s, ROT_O, k);
-        const int acc = accs[k];
-        if (lane == 0 && i < R_O) {
-          const int n = w * R_O + i;
-          const float y = dequant(acc + zc * co[k], qp.s, so[k]);
-          xput_rep(xl + OFF_X1, H, n, sh.xs[n] + y, epoch);
-        }
+      if (lane == 0 && s < R_O) {
+        const int n = w * R_O + s;
+        const float y = dequant(accs[0] + (128 - qp.z) * co[0], qp.s, so[0]);
+        xput_rep(xl + OFF_X1, H, n, sh.xs[n] + y, epoch);
       }
-      trace_done(A, w, l, 6, lane);
-      if (att) issue_gate_up(l);
     }
+    trace_done(A, w, l, 6, lane);
+    // attention workgroups have no gate/up rows: their down rows next
+    if (att) issue_down(l);
 
     // ---- gate/up + SwiGLU
     asm volatile("" : "+v"(lane16), "+v"(tid), "+v"(lane));
-    load_gain(Lw.ln2, sh.gain, wave, lane16);
+    if (!att) load_gain(Lw.ln2, sh.gain, wave, lane16);
     trace_val(A, w, l, 13, poll_all(xl + OFF_X1 + rep * H, H, R_O, sh.stage, A.err, lane, wave, epoch, trace_sub(A, w, l, 16)));
     __syncthreads();
     trace_at(A, w, l, 7);
     unstage(sh.stage, sh.x1s, H, tid);
     __syncthreads();
-    qp = prologue_norm(sh.x1s, sh.gain, A.eps, sh, tid);
-    if (streamer) {
+    if (!att) {
+      qp = prologue_norm(sh.x1s, sh.gain, A.eps, sh, tid);
       const int zc = 128 - qp.z;
-      int aggs[3] = {0, 0, 0}, aus[3] = {0, 0, 0};
+      int aggs[GU_ROWS] = {}, aus[GU_ROWS] = {};
       const i32x4 c0 = *(const i32x4*)(sh.codes + lane16);
       const i32x4 c1 = *(const i32x4*)(sh.codes + 1024 + lane16);
-      run_units<NGU, W>(win, [&](int i) { return gu_addr(Lw, i); }, [&](int i, const i32x4 v) {
+      run_units<W, W>(win, [&](int i) { return gu_addr(Lw, i); }, [&](int i, const i32x4 v) {
         const int k = i / 4, m = (i / 2) % 2, u = i % 2;
         int& acc = m ? aus[k] : aggs[k];
         acc = dot16(v, u ? c1 : c0, acc);
       });
+      if (s + NW * 2 < ngu) {
 #pragma unroll
-      for (int k = 0; k < 3; ++k) {
+        for (int i = W; i < NGU; ++i) {
+          const i32x4 v = *(const i32x4*)(sh.stage + GU_LDS + s * 4096 + (i - W) * 1024 + lane16);
+          const int m = (i / 2) % 2, u = i % 2;
+          int& acc = m ? aus[2] : aggs[2];
+          acc = dot16(v, u ? c1 : c0, acc);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < GU_ROWS; ++k) {
         aggs[k] = wave_sum(aggs[k]);
         aus[k] = wave_sum(aus[k]);
       }
 #pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        const int i = row_local(s, ROT_GU, k);
-        const int ag = aggs[k];
-        const int au = aus[k];
-        if (lane == 0 && i < R_GU) {
-          const float gv = dequant(ag + zc * cg[k], qp.s, sg[k]);
-          const float uv = dequant(au + zc * cu[k], qp.s, su[k]);
+      for (int k = 0; k < GU_ROWS; ++k) {
+        const int i = s + NW * k;
+        if (lane == 0 && i < ngu) {
+          const float gv = dequant(aggs[k] + zc * cg[k], qp.s, sg[k]);
+          const float uv = dequant(aus[k] + zc * cu[k], qp.s, su[k]);
           const double gd = gv;
-          xput_rep(xl + OFF_A, I, w * R_GU + i, (float)(gd / (1.0 + exp(-gd)) * (double)uv), epoch);
+          xput_rep(xl + OFF_A, I, gu0 + i, (float)(gd / (1.0 + exp_t(-gd, sh.expc)) * (double)uv), epoch);
         }
       }
       trace_done(A, w, l, 8, lane);
       issue_down(l);
     }
 
-    // ---- down + residual
+    // ---- down + residual: waves 2r and 2r+1 each take half of row r
     asm volatile("" : "+v"(lane16), "+v"(tid), "+v"(lane));
-    trace_val(A, w, l, 14, poll_all(xl + OFF_A + rep * I, I, R_GU, sh.stage, A.err, lane, wave, epoch, trace_sub(A, w, l, 19)));
+    trace_val(A, w, l, 14, poll_all(xl + OFF_A + rep * I, I, rg, sh.stage, A.err, lane, wave, epoch, trace_sub(A, w, l, 19)));
     __syncthreads();
     trace_at(A, w, l, 9);
     qp = prologue_plain(sh.stage, I, sh, tid);
-    if (streamer) {
-      const int zc = 128 - qp.z;
-      int accs[1] = {0};
-      run_units<ND, W>(win, [&](int u) { return down_addr(Lw, u); }, [&](int u, const i32x4 v) {
-        accs[0] = dot16(v, *(const i32x4*)(sh.codes + u * 1024 + lane16), accs[0]);
+    {
+      int acc = 0;
+      const int8_t* cb = sh.codes + (s & 1) * D_UNITS * 1024 + lane16;
+      run_units<D_UNITS, W>(win, [&](int u) { return down_addr(Lw, u); }, [&](int u, const i32x4 v) {
+        acc = dot16(v, *(const i32x4*)(cb + u * 1024), acc);
       });
-      accs[0] = wave_sum(accs[0]);
-#pragma unroll
-      for (int k = 0; k < 1; ++k) {
-        const int i = row_local(s, ROT_D, k);
-        const int acc = accs[k];
-        if (lane == 0 && i < R_D) {
-          const int n = w * R_D + i;
-          const float y = dequant(acc + zc * cd[k], qp.s, sd[k]);
-          xput_rep(xn + OFF_X0, H, n, sh.x1s[n] + y, epoch);
-        }
+      acc = wave_sum(acc);
+      if (lane == 0) sh.redi[s] = acc;
+      __syncthreads();
+      if (lane == 0 && (s & 1) == 0) {
+        const int n = w * R_D + (s >> 1);
+        const float y = dequant(sh.redi[s] + sh.redi[s + 1] + (128 - qp.z) * cd, qp.s, sd);
+        xput_rep(xn + OFF_X0, H, n, sh.x1s[n] + y, epoch);
       }
-      trace_done(A, w, l, 10, lane);
-      if (l + 1 < A.L) issue_qkv(l + 1);
     }
+    trace_done(A, w, l, 10, lane);
+    if (l + 1 < A.L) issue_qkv(l + 1);
   }
 
   // ---- final norm + LM head + masked argmax
@@ -850,7 +913,8 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
   const int r0 = (int)(((long long)w * A.V) / NWG), r1 = (int)(((long long)(w + 1) * A.V) / NWG);
   float bv = -INFINITY;
   int bi = INT_MAX;
-  if (streamer) {
+  if (wave > 0) {
+    const int s = wave - 1;  // streamer 0..14
     const int zc = 128 - qp.z;
     constexpr int GR = 4;  // rows per group of one streamer; two groups in flight
     i32x4 b0[GR][2], b1[GR][2];
@@ -1002,7 +1066,7 @@ static size_t mega_xch_words(int L) {
 
 size_t decode_mega_ws_bytes(int L, int T) {
   const size_t xch = mega_xch_words(L) * 8;
-  const size_t part = (size_t)L * mk::NKV * (T / mk::KEYS) * mk::G * mk::PSTATE * 8;
+  const size_t part = (size_t)L * mk::NKV * mk::NI * mk::G * mk::PSTATE * 8;
   const size_t ctr = (size_t)(2 * L + 64) * 4;
   const size_t amax = (size_t)mk::NWG * 8;
   const size_t table = (size_t)L * sizeof(mk::LayerW);
@@ -1012,9 +1076,9 @@ size_t decode_mega_ws_bytes(int L, int T) {
 }
 
 bool decode_mega_supported(int H, int NH, int NKV, int D, int I, int T, int L) {
-  // the partial-state merge moves whole 1 KiB blocks of 8 splits: T % 512 == 0
+  // attention chunks are 64 whole cache rows
   return H == mk::H && NH == mk::NH && NKV == mk::NKV && D == mk::D && I == mk::I &&
-         T % 512 == 0 && T >= 512 && T <= 4096 && L >= 1 && L <= kMaxLayers;
+         T % mk::KEYS == 0 && T >= mk::KEYS && T <= 8192 && L >= 1 && L <= kMaxLayers;
 }
 
 struct MegaLayout {
@@ -1037,7 +1101,7 @@ static MegaLayout mega_layout(void* ws, int L, int T) {
   m.xch = (mk::u64*)p;
   p += al(mega_xch_words(L) * 8);
   m.part = (mk::u64*)p;
-  p += al((size_t)L * mk::NKV * (T / mk::KEYS) * mk::G * mk::PSTATE * 8);
+  p += al((size_t)L * mk::NKV * mk::NI * mk::G * mk::PSTATE * 8);
   m.ctr = (uint32_t*)p;
   m.err = m.ctr + 2 * L + 32;
   m.marker = (mk::u64*)(m.ctr + 2 * L + 48);
@@ -1073,7 +1137,7 @@ hipError_t decode_mega_upload(hipStream_t st, void* ws, int L, int T, const Mega
 hipError_t decode_mega_launch(hipStream_t st, void* ws, const MegaStep& S) {
   MegaLayout lay = mega_layout(ws, S.L, S.T);
   // the exchange words and the partial attention states that follow them
-  const size_t part_words = (size_t)S.L * mk::NKV * (S.T / mk::KEYS) * mk::G * mk::PSTATE;
+  const size_t part_words = (size_t)S.L * mk::NKV * mk::NI * mk::G * mk::PSTATE;
   const size_t nwords = (size_t)(lay.part - lay.xch) + part_words;
   const mk::u64 marker = mk::MAGIC ^ (mk::u64)nwords ^ ((mk::u64)S.T << 40);
   hipLaunchKernelGGL(mk::k_decode_prep, dim3(mk::NWG), dim3(256), 0, st, lay.xch, nwords, lay.ctr,

@@ -103,3 +103,41 @@ def test_greedy_loop_matches_oracle(models, path):
     assert np.array_equal(host(out), np.stack(want))
     for l in range(CFG.n_layers):
         assert_close(host(gs.kc[l])[0, :60 + steps], kc[l][0, :60 + steps], f"{path} k cache {l}")
+
+
+CFG_LONG = CFG.with_(name="real2_t1024", max_total_len=1024)
+
+
+@pytest.fixture(scope="module")
+def models_long():
+    return oracle.build_model(CFG_LONG, synth), ark.load_model(CFG_LONG, synth)
+
+
+@pytest.mark.parametrize("p0", [511, 700, 1022])
+def test_long_cache_decode_matches_oracle(models_long, path, p0):
+    # more than 8 live 64-key chunks per KV head: each attention item of the
+    # single-kernel step folds several chunks
+    om, gm = models_long
+    rng = np.random.default_rng(p0 + 7)
+    kc, vc = _caches(CFG_LONG, [p0], rng)
+    gs = GpuState(gm, 1, 1)
+    gs.load_caches(kc, vc)
+    mask = CFG_LONG.mask()
+    tok = np.array([int(rng.integers(0, CFG_LONG.vocab - 64))], np.int32)
+    p = np.array([p0])
+    for step in range(min(2, CFG_LONG.max_total_len - p0)):
+        kd, vd, hid = gs.decode(t(tok), p)
+        lo, kdo, vdo, hido = oracle.decode_step(om, tok, p, kc, vc)
+        for l in range(CFG_LONG.n_layers):
+            assert_close(host(kd[l]), kdo[l], f"{path} step {step} k_delta {l}")
+            assert_close(host(vd[l]), vdo[l], f"{path} step {step} v_delta {l}")
+        assert_close(host(hid), hido, f"{path} step {step} hidden")
+        lg = host(gs.logits)
+        err = assert_close(lg, lo, f"{path} step {step} logits") * np.max(np.abs(lo))
+        check_tokens(oracle.masked_argmax(lg, mask), oracle.masked_argmax(lo, mask), lo, mask, err,
+                     f"{path} step {step}")
+        gs.write_back(p, kd, vd)
+        kc = [oracle.cache_write(kc[l], kdo[l], p) for l in range(CFG_LONG.n_layers)]
+        vc = [oracle.cache_write(vc[l], vdo[l], p) for l in range(CFG_LONG.n_layers)]
+        tok = oracle.masked_argmax(lo, mask)
+        p = p + 1
