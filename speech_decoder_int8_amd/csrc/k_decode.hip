@@ -48,9 +48,12 @@ constexpr unsigned long long MAGIC = 0x41524b5f58434831ull;
 // per-layer exchange words: q|k|v once (read by the attention workgroups),
 // every vector that all workgroups read in NREP replicas, so each replica is
 // read by the 32 workgroups of one XCD instead of all 256 reading one copy
+// The SwiGLU vector also has one flag word per producer workgroup (per
+// replica), written once the producer's stores of it are complete, so its
+// readers poll 256 flags instead of re-reading 88 KiB.
 constexpr int OFF_QKV = 0, OFF_X0 = NQKV, OFF_ATT = OFF_X0 + NREP * H,
               OFF_X1 = OFF_ATT + NREP * Q, OFF_A = OFF_X1 + NREP * H,
-              XCH_LAYER = OFF_A + NREP * I;
+              OFF_AF = OFF_A + NREP * I, XCH_LAYER = OFF_AF + NREP * NWG;
 
 // rows per workgroup of the q|k|v, o and down phases (wave s owns row s of
 // q|k|v and o; waves 2r and 2r+1 split down row r); the gate/up rows are
@@ -231,6 +234,7 @@ struct Shared {
   float bestv[NW];
   int besti[NW];
   int redi[NW];
+  LayerW lt[2];        // weight table of layers l and l + 1 (slot l % 2)
   double expc[17];     // exp_t table
   double rcos[D / 2];  // rotary table row of the position (attention workgroups)
   double rsin[D / 2];
@@ -244,19 +248,21 @@ __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 // One wave: wait until words [c0, c1) of v carry the tag and copy them to
 // dst (word c0 first).  Producers write v in blocks of blk words (block b =
 // words [b*blk, b*blk + blk)); the wave first polls the first word of each
-// block that meets the range, then reads the range with device-scope loads
+// block that meets the range (or, given flags, the block's flag word), then
+// reads the range with device-scope loads
 // straight into LDS and checks every tag, again until all match.  The copy
 // is whole KiB: dst needs room up to the next KiB boundary.  Bounded: after
 // SPIN_LIMIT rounds the error word is set and the wave goes on.  Returns
 // the number of sparse polls plus 65536 x the number of copies.
 __device__ uint32_t poll_range(const u64* v, int c0, int c1, int blk, unsigned char* dst,
-                               uint32_t* err, int lane, uint32_t tag, u64* tr = nullptr) {
+                               uint32_t* err, int lane, uint32_t tag, u64* tr = nullptr,
+                               const u64* flags = nullptr) {
   uint32_t spins = 0;
   const int b0 = c0 / blk, b1 = (c1 - 1) / blk;
   for (;;) {
     bool ok = true;
     for (int b = b0 + lane; b <= b1; b += 64)
-      ok &= (uint32_t)(xget(v + max(c0, b * blk)) >> 32) == tag;
+      ok &= (uint32_t)(xget(flags ? flags + b : v + max(c0, b * blk)) >> 32) == tag;
     if (__all(ok)) break;
     if (++spins > SPIN_LIMIT) {
       if (lane == 0) atomicOr(err, 1u);
@@ -286,13 +292,15 @@ __device__ uint32_t poll_range(const u64* v, int c0, int c1, int blk, unsigned c
 // whole KiB per wave, staged at stage + 8 i.  Also waits for every load the
 // wave has in flight.  Returns wave 0's poll_range count.
 __device__ uint32_t poll_all(const u64* v, int n, int blk, unsigned char* stage, uint32_t* err,
-                             int lane, int wave, uint32_t tag, u64* tr = nullptr) {
+                             int lane, int wave, uint32_t tag, u64* tr = nullptr,
+                             const u64* flags = nullptr) {
   if (wave == 0) stamp(tr, 0, lane);
   const int chunk = ((n + NW - 1) / NW + 127) & ~127;
   const int c0 = wave * chunk, c1 = min(n, c0 + chunk);
   uint32_t r = 0;
   if (c0 < c1)
-    r = poll_range(v, c0, c1, blk, stage + (size_t)c0 * 8, err, lane, tag, wave == 0 ? tr : nullptr);
+    r = poll_range(v, c0, c1, blk, stage + (size_t)c0 * 8, err, lane, tag, wave == 0 ? tr : nullptr,
+                   flags);
   __builtin_amdgcn_s_waitcnt(0);
   if (wave == 0) stamp(tr, 2, lane);
   return r;
@@ -478,7 +486,7 @@ __device__ __forceinline__ int kv_row(int k) { return (k >> 1) * 260 + (k & 1) *
 __device__ __forceinline__ void load_kv(const MegaArgs& A, int l, int g, int j0, Shared& sh,
                                         int wave, int lane) {
   const int npair = (min(KEYS, A.pos + 1 - j0) + 1) / 2;
-  const LayerW& Lw = A.layers[l];
+  const LayerW& Lw = sh.lt[l & 1];
   float* Ks = (float*)(sh.stage + ATT_KV);
   float* Vs = Ks + (KEYS / 2) * 260;
   for (int pr = wave; pr < npair; pr += NW) {
@@ -687,13 +695,14 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
   constexpr int W = 8;                      // units in flight per wave (big phases)
   constexpr int NGU = GU_ROWS * 2 * 2;      // gate/up units: rows x {gate, up} x 2
   static_assert(NGU == W + 4, "gate/up: 8 units in registers, 4 in LDS");
+  static_assert(sizeof(LayerW) % 8 == 0 && sizeof(LayerW) / 8 <= 64, "layer table");
   i32x4 wq[1][2], wo[1][2], win[W];
   float sq[1], so[1], sg[GU_ROWS], su[GU_ROWS], sd;
   int cq[1], co[1], cg[GU_ROWS], cu[GU_ROWS], cd;
   float bq[1] = {0.f};
 
   auto issue_qkv = [&](int l) {
-    const LayerW& Lw = A.layers[l];
+    const LayerW& Lw = sh.lt[l & 1];
     // rows of the concatenated q|k|v space: [w*10, w*10+10), row s
     const bool valid = s < R_QKV;
     const int n = w * R_QKV + (valid ? s : 0);
@@ -707,7 +716,7 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
     for (int u = 0; u < 2; ++u) wq[0][u] = valid ? ldg_nt(p + u * 1024 + lane16) : i32x4{0, 0, 0, 0};
   };
   auto issue_o = [&](int l) {
-    const LayerW& Lw = A.layers[l];
+    const LayerW& Lw = sh.lt[l & 1];
     load_rows<1, 2>(wo, so, co, Lw.w[3], Lw.sw[3], Lw.cs[3], Q, w * R_O, R_O, s, 0, lane16);
   };
   // unit i of the gate/up phase: row s + 16 (i / 4), matrix (i / 2) % 2, unit i % 2
@@ -724,7 +733,7 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
     return Lw.w[6] + (size_t)(w * R_D + (s >> 1)) * I + off;
   };
   auto issue_gate_up = [&](int l) {
-    const LayerW& Lw = A.layers[l];
+    const LayerW& Lw = sh.lt[l & 1];
 #pragma unroll
     for (int k = 0; k < GU_ROWS; ++k) {
       const int r = s + NW * k;
@@ -747,7 +756,7 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
     }
   };
   auto issue_down = [&](int l) {
-    const LayerW& Lw = A.layers[l];
+    const LayerW& Lw = sh.lt[l & 1];
     sd = ldg(Lw.sw[6] + w * R_D + (s >> 1));
     cd = ldg(Lw.cs[6] + w * R_D + (s >> 1));
     prime_units<D_UNITS, W>(win, [&](int u) { return down_addr(Lw, u); });
@@ -759,8 +768,15 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
     A.epoch[0] = epoch;           // the next launch counts on from here
     *A.marker = A.marker_value;   // the exchange area is initialised
   }
-  issue_qkv(0);
+  // the weight table lives in LDS: pointers read from global memory with
+  // vector loads would make every address wait for all loads in flight
+  constexpr int LTW = sizeof(LayerW) / 8;
+  if (tid < LTW) ((u64*)&sh.lt[0])[tid] = ((const u64*)&A.layers[0])[tid];
+  if (A.L > 1 && tid >= 64 && tid < 64 + LTW)
+    ((u64*)&sh.lt[1])[tid - 64] = ((const u64*)&A.layers[1])[tid - 64];
   if (tid < 17) sh.expc[tid] = kExpTab[tid];
+  __syncthreads();
+  issue_qkv(0);
   if (att && tid < D / 2) {
     sh.rcos[tid] = A.rcos[(size_t)A.pos * (D / 2) + tid];
     sh.rsin[tid] = A.rsin[(size_t)A.pos * (D / 2) + tid];
@@ -768,9 +784,13 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
 
   for (int l = 0; l < A.L; ++l) {
     asm volatile("" : "+v"(lane16), "+v"(tid), "+v"(lane), "+s"(w), "+s"(s));
-    const LayerW& Lw = A.layers[l];
+    const LayerW& Lw = sh.lt[l & 1];
     u64* xl = A.xch + (size_t)l * XCH_LAYER;
     u64* xn = A.xch + (size_t)(l + 1) * XCH_LAYER;   // next layer's input lives at its OFF_X0
+    // table of layer l + 1 into the other slot (layer l - 1 is done with it;
+    // read after this layer's barriers)
+    if (l >= 1 && l + 1 < A.L && tid < LTW)
+      ((u64*)&sh.lt[(l + 1) & 1])[tid] = ((const u64*)&A.layers[l + 1])[tid];
 
     // ---- q, k, v
     trace_at(A, w, l, 0);
@@ -870,12 +890,16 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
         }
       }
       trace_done(A, w, l, 8, lane);
+      // this workgroup's block is complete once every wave's stores are
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid < NREP) xput(xl + OFF_AF + tid * NWG + rank, 0.f, epoch);
       issue_down(l);
     }
 
     // ---- down + residual: waves 2r and 2r+1 each take half of row r
     asm volatile("" : "+v"(lane16), "+v"(tid), "+v"(lane));
-    trace_val(A, w, l, 14, poll_all(xl + OFF_A + rep * I, I, rg, sh.stage, A.err, lane, wave, epoch, trace_sub(A, w, l, 19)));
+    trace_val(A, w, l, 14, poll_all(xl + OFF_A + rep * I, I, rg, sh.stage, A.err, lane, wave, epoch, trace_sub(A, w, l, 19), xl + OFF_AF + rep * NWG));
     __syncthreads();
     trace_at(A, w, l, 9);
     qp = prologue_plain(sh.stage, I, sh, tid);
