@@ -49,8 +49,8 @@ constexpr unsigned long long MAGIC = 0x41524b5f58434831ull;
 // every vector that all workgroups read in NREP replicas, so each replica is
 // read by the 32 workgroups of one XCD instead of all 256 reading one copy
 // The SwiGLU vector also has one flag word per producer workgroup (per
-// replica), written once the producer's stores of it are complete, so its
-// readers poll 256 flags instead of re-reading 88 KiB.
+// replica), written after the producer's stores of it, so its readers poll
+// 256 flags instead of re-reading 88 KiB while the vector fills.
 constexpr int OFF_QKV = 0, OFF_X0 = NQKV, OFF_ATT = OFF_X0 + NREP * H,
               OFF_X1 = OFF_ATT + NREP * Q, OFF_A = OFF_X1 + NREP * H,
               OFF_AF = OFF_A + NREP * I, XCH_LAYER = OFF_AF + NREP * NWG;
@@ -186,6 +186,11 @@ __device__ __forceinline__ void trace_done(const MegaArgs& A, int w, int l, int 
 __device__ __forceinline__ void trace_val(const MegaArgs& A, int w, int l, int ev, uint32_t v) {
   if (A.trace && threadIdx.x == 0 && l == (A.L > TRACE_WIDE_LAYER ? TRACE_WIDE_LAYER : 0))
     A.trace[(size_t)3 * (A.L + 1) * 32 + (size_t)w * 16 + ev] = v;
+}
+// Wide-trace slot of a poll count (workgroup w, layer TRACE_WIDE_LAYER), or null.
+__device__ __forceinline__ uint32_t* trace_stat(const MegaArgs& A, int w, int l, int ev) {
+  if (!A.trace || l != (A.L > TRACE_WIDE_LAYER ? TRACE_WIDE_LAYER : 0)) return nullptr;
+  return (uint32_t*)(A.trace + (size_t)3 * (A.L + 1) * 32 + (size_t)w * 16 + ev);
 }
 // Slot of a sub-phase timestamp (events 16..31) of workgroups 0, 1 and the
 // last one, or null.
@@ -367,6 +372,89 @@ __device__ QParam prologue_plain(const unsigned char* stage, int n, Shared& sh, 
 #pragma unroll 2
   for (int i = tid; i < n; i += NT)
     sh.codes[i] = shift_code(quant_code(__uint_as_float((uint32_t)x[i]), p));
+  __syncthreads();
+  return p;
+}
+
+// All waves: poll_all of an H-word vector whose wave chunks are 128 words,
+// then RMSNorm (fp64 inside) with gain sh.gain and the dynamic uint8
+// quantiser, each wave on its own chunk: the values go to x (fp32), the
+// shifted codes to sh.codes.  Three barriers in all.
+__device__ QParam poll_norm(const u64* v, int blk, float* x, Shared& sh, double eps, int lane,
+                            int wave, int tid, uint32_t tag, uint32_t* err, u64* tr = nullptr,
+                            uint32_t* stat = nullptr) {
+  static_assert(H == NW * 128, "one 128-word chunk per wave");
+  const uint32_t r = poll_all(v, H, blk, sh.stage, err, lane, wave, tag, tr);
+  if (stat && tid == 0) *stat = r;
+  const u64* st = (const u64*)sh.stage;
+  const int i0 = wave * 128 + lane, i1 = i0 + 64;
+  const float v0 = __uint_as_float((uint32_t)st[i0]), v1 = __uint_as_float((uint32_t)st[i1]);
+  x[i0] = v0;
+  x[i1] = v1;
+  double ss = (double)v0 * (double)v0 + (double)v1 * (double)v1;
+  ss = wave_sum(ss);
+  if (lane == 0) sh.redd[wave] = ss;
+  __syncthreads();
+  ss = 0.0;
+#pragma unroll
+  for (int k = 0; k < NW; ++k) ss += sh.redd[k];
+  const double rs = 1.0 / sqrt(ss / (double)H + eps);
+  const float h0 = (float)(((double)v0 * rs) * (double)sh.gain[i0]);
+  const float h1 = (float)(((double)v1 * rs) * (double)sh.gain[i1]);
+  float lo = wave_min(fminf(h0, h1)), hi = wave_max(fmaxf(h0, h1));
+  if (lane == 0) {
+    sh.redf[2 * wave] = lo;
+    sh.redf[2 * wave + 1] = hi;
+  }
+  __syncthreads();
+  lo = sh.redf[0];
+  hi = sh.redf[1];
+#pragma unroll
+  for (int k = 1; k < NW; ++k) {
+    lo = fminf(lo, sh.redf[2 * k]);
+    hi = fmaxf(hi, sh.redf[2 * k + 1]);
+  }
+  const QParam p = quant_param(lo, hi);
+  sh.codes[i0] = shift_code(quant_code(h0, p));
+  sh.codes[i1] = shift_code(quant_code(h1, p));
+  __syncthreads();
+  return p;
+}
+
+// All waves: poll_all of an n-word vector, then the dynamic uint8 quantiser
+// on it, each wave on its own chunk; shifted codes to sh.codes.  Two
+// barriers.
+__device__ QParam poll_quant(const u64* v, int n, int blk, Shared& sh, int lane, int wave,
+                             uint32_t tag, uint32_t* err, u64* tr = nullptr,
+                             const u64* flags = nullptr, uint32_t* stat = nullptr) {
+  const uint32_t r = poll_all(v, n, blk, sh.stage, err, lane, wave, tag, tr, flags);
+  if (stat && threadIdx.x == 0) *stat = r;
+  const int chunk = ((n + NW - 1) / NW + 127) & ~127;
+  const int c0 = wave * chunk, c1 = min(n, c0 + chunk);
+  const u64* st = (const u64*)sh.stage;
+  float lo = INFINITY, hi = -INFINITY;
+  for (int i = c0 + lane; i < c1; i += 64) {
+    const float x = __uint_as_float((uint32_t)st[i]);
+    lo = fminf(lo, x);
+    hi = fmaxf(hi, x);
+  }
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  if (lane == 0) {
+    sh.redf[2 * wave] = lo;
+    sh.redf[2 * wave + 1] = hi;
+  }
+  __syncthreads();
+  lo = sh.redf[0];
+  hi = sh.redf[1];
+#pragma unroll
+  for (int k = 1; k < NW; ++k) {
+    lo = fminf(lo, sh.redf[2 * k]);
+    hi = fmaxf(hi, sh.redf[2 * k + 1]);
+  }
+  const QParam p = quant_param(lo, hi);
+  for (int i = c0 + lane; i < c1; i += 64)
+    sh.codes[i] = shift_code(quant_code(__uint_as_float((uint32_t)st[i]), p));
   __syncthreads();
   return p;
 }
@@ -796,12 +884,8 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
     trace_at(A, w, l, 0);
     if (att) load_kv(A, l, w / NI, (w % NI) * KEYS, sh, wave, lane);
     load_gain(Lw.ln1, sh.gain, wave, lane16);
-    trace_val(A, w, l, 11, poll_all(xl + OFF_X0 + rep * H, H, R_D, sh.stage, A.err, lane, wave, epoch, trace_sub(A, w, l, 27)));
-    __syncthreads();
-    trace_at(A, w, l, 1);
-    unstage(sh.stage, sh.xs, H, tid);
-    __syncthreads();
-    QParam qp = prologue_norm(sh.xs, sh.gain, A.eps, sh, tid, trace_sub(A, w, l, 11));
+    QParam qp = poll_norm(xl + OFF_X0 + rep * H, R_D, sh.xs, sh, A.eps, lane, wave, tid, epoch,
+                          A.err, trace_sub(A, w, l, 27), trace_stat(A, w, l, 11));
     trace_at(A, w, l, 2);
     {
       int accs[1];
@@ -829,10 +913,9 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
     // ---- o projection + residual
     asm volatile("" : "+v"(lane16), "+v"(tid), "+v"(lane));
     trace_at(A, w, l, 4);
-    trace_val(A, w, l, 12, poll_all(xl + OFF_ATT + rep * Q, Q, G * D, sh.stage, A.err, lane, wave, epoch));
-    __syncthreads();
+    qp = poll_quant(xl + OFF_ATT + rep * Q, Q, G * D, sh, lane, wave, epoch, A.err, nullptr, nullptr,
+                    trace_stat(A, w, l, 12));
     trace_at(A, w, l, 5);
-    qp = prologue_plain(sh.stage, Q, sh, tid);
     {
       int accs[1];
       dot_rows<1, 2>(wo, sh.codes, accs, lane16);
@@ -848,14 +931,11 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
 
     // ---- gate/up + SwiGLU
     asm volatile("" : "+v"(lane16), "+v"(tid), "+v"(lane));
-    if (!att) load_gain(Lw.ln2, sh.gain, wave, lane16);
-    trace_val(A, w, l, 13, poll_all(xl + OFF_X1 + rep * H, H, R_O, sh.stage, A.err, lane, wave, epoch, trace_sub(A, w, l, 16)));
-    __syncthreads();
+    load_gain(Lw.ln2, sh.gain, wave, lane16);
+    qp = poll_norm(xl + OFF_X1 + rep * H, R_O, sh.x1s, sh, A.eps, lane, wave, tid, epoch, A.err,
+                   trace_sub(A, w, l, 16), trace_stat(A, w, l, 13));
     trace_at(A, w, l, 7);
-    unstage(sh.stage, sh.x1s, H, tid);
-    __syncthreads();
     if (!att) {
-      qp = prologue_norm(sh.x1s, sh.gain, A.eps, sh, tid);
       const int zc = 128 - qp.z;
       int aggs[GU_ROWS] = {}, aus[GU_ROWS] = {};
       const i32x4 c0 = *(const i32x4*)(sh.codes + lane16);
@@ -890,8 +970,9 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
         }
       }
       trace_done(A, w, l, 8, lane);
-      // this workgroup's block is complete once every wave's stores are
-      __builtin_amdgcn_s_waitcnt(0);
+      // every wave has issued its stores of this workgroup's block: raise the
+      // flag (a hint only; readers still check every word's tag, so a flag
+      // that overtakes a data word costs a re-read, not a wrong value)
       __syncthreads();
       if (tid < NREP) xput(xl + OFF_AF + tid * NWG + rank, 0.f, epoch);
       issue_down(l);
@@ -899,10 +980,9 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
 
     // ---- down + residual: waves 2r and 2r+1 each take half of row r
     asm volatile("" : "+v"(lane16), "+v"(tid), "+v"(lane));
-    trace_val(A, w, l, 14, poll_all(xl + OFF_A + rep * I, I, rg, sh.stage, A.err, lane, wave, epoch, trace_sub(A, w, l, 19), xl + OFF_AF + rep * NWG));
-    __syncthreads();
+    qp = poll_quant(xl + OFF_A + rep * I, I, rg, sh, lane, wave, epoch, A.err, trace_sub(A, w, l, 19),
+                    xl + OFF_AF + rep * NWG, trace_stat(A, w, l, 14));
     trace_at(A, w, l, 9);
-    qp = prologue_plain(sh.stage, I, sh, tid);
     {
       int acc = 0;
       const int8_t* cb = sh.codes + (s & 1) * D_UNITS * 1024 + lane16;
