@@ -48,12 +48,13 @@ constexpr unsigned long long MAGIC = 0x41524b5f58434831ull;
 // per-layer exchange words: q|k|v once (read by the attention workgroups),
 // every vector that all workgroups read in NREP replicas, so each replica is
 // read by the 32 workgroups of one XCD instead of all 256 reading one copy
-// The SwiGLU vector also has one flag word per producer workgroup (per
-// replica), written after the producer's stores of it, so its readers poll
-// 256 flags instead of re-reading 88 KiB while the vector fills.
+// The SwiGLU vector is exchanged already quantised, in two rounds: each
+// producer workgroup's min and max (OFF_AMM, 2 words per producer), then its
+// codes packed 4 per word (OFF_AC, word k = codes of rows 4k..4k+3).
 constexpr int OFF_QKV = 0, OFF_X0 = NQKV, OFF_ATT = OFF_X0 + NREP * H,
-              OFF_X1 = OFF_ATT + NREP * Q, OFF_A = OFF_X1 + NREP * H,
-              OFF_AF = OFF_A + NREP * I, XCH_LAYER = OFF_AF + NREP * NWG;
+              OFF_X1 = OFF_ATT + NREP * Q, OFF_AMM = OFF_X1 + NREP * H,
+              OFF_AC = OFF_AMM + NREP * 2 * NWG, XCH_LAYER = OFF_AC + NREP * (I / 4);
+static_assert(I % 4 == 0, "packed codes");
 
 // rows per workgroup of the q|k|v, o and down phases (wave s owns row s of
 // q|k|v and o; waves 2r and 2r+1 split down row r); the gate/up rows are
@@ -63,9 +64,19 @@ constexpr int R_QKV = NQKV / NWG, R_O = H / NWG, R_D = H / NWG;
 static_assert(R_QKV * NWG == NQKV && R_O * NWG == H && R_D * NWG == H, "row split");
 static_assert(R_QKV <= NW && R_O <= NW && 2 * R_D == NW, "rows per wave");
 constexpr int GU_ROWS = 3;
-static_assert((I + (NWG - NKV * NI) - 1) / (NWG - NKV * NI) <= GU_ROWS * NW, "gate/up rows");
-constexpr int D_UNITS = (I / 1024 + 2) / 2;   // 1 KiB units of half a down row (6)
+static_assert((((I + (NWG - NKV * NI) - 1) / (NWG - NKV * NI) + 3) & ~3) <= GU_ROWS * NW,
+              "gate/up rows");
+constexpr int STAGE = 112 * 1024;             // LDS staging bytes
 constexpr int GU_LDS = 16 * 1024;             // stage offset of the gate/up units in LDS
+// down projection: waves 8..15 ("loaders") each own one of the 8 rows (11
+// units of 1 KiB, the last one partial): units 0..7 in registers, 8..10 in
+// LDS at DN_LDS + 3 KiB x loader; waves 0..7 poll and quantise its input
+constexpr int D_UNITS = (I + 1023) / 1024;    // 11
+constexpr int D_LDS_UNITS = D_UNITS - 8;      // 3
+constexpr int NPOLL = NW - R_D;               // 8 polling waves
+constexpr int DN_LDS = 88 * 1024;
+static_assert(DN_LDS + R_D * D_LDS_UNITS * 1024 <= STAGE, "down units exceed LDS stage");
+static_assert(GU_LDS + NW * 4096 <= DN_LDS, "gate/up units overlap the down units");
 
 typedef unsigned long long u64;
 typedef __attribute__((address_space(1))) const i32x4 gi32x4;
@@ -78,6 +89,13 @@ __device__ __forceinline__ i32x4 ldg_nt(const void* p) {
 template <typename T>
 __device__ __forceinline__ T ldg(const T* p) {
   return *(const __attribute__((address_space(1))) T*)p;
+}
+// Wave-uniform read of data that no kernel writes (per-row scales, column
+// sums, biases) through the constant address space: a scalar load into an
+// SGPR, waited on with the LDS counter, never behind the weight stream.
+template <typename T>
+__device__ __forceinline__ T ldc(const T* p, int i) {
+  return ((const __attribute__((address_space(4))) T*)(uintptr_t)p)[__builtin_amdgcn_readfirstlane(i)];
 }
 
 __device__ __forceinline__ void xput(u64* p, float v, uint32_t tag) {
@@ -233,13 +251,13 @@ struct Shared {
   float x1s[H];        // input of the MLP half (kept for the down residual)
   float gain[H];
   int8_t codes[11264];
-  alignas(16) unsigned char stage[104 * 1024];
+  alignas(16) unsigned char stage[STAGE];
   double redd[NW];
   float redf[2 * NW];
   float bestv[NW];
   int besti[NW];
-  int redi[NW];
   LayerW lt[2];        // weight table of layers l and l + 1 (slot l % 2)
+  float aval[GU_ROWS * NW];  // this workgroup's SwiGLU values
   double expc[17];     // exp_t table
   double rcos[D / 2];  // rotary table row of the position (attention workgroups)
   double rsin[D / 2];
@@ -298,9 +316,10 @@ __device__ uint32_t poll_range(const u64* v, int c0, int c1, int blk, unsigned c
 // wave has in flight.  Returns wave 0's poll_range count.
 __device__ uint32_t poll_all(const u64* v, int n, int blk, unsigned char* stage, uint32_t* err,
                              int lane, int wave, uint32_t tag, u64* tr = nullptr,
-                             const u64* flags = nullptr) {
+                             const u64* flags = nullptr, int np = NW) {
+  if (wave >= np) return 0;  // not a polling wave: its loads in flight stay in flight
   if (wave == 0) stamp(tr, 0, lane);
-  const int chunk = ((n + NW - 1) / NW + 127) & ~127;
+  const int chunk = ((n + np - 1) / np + 127) & ~127;
   const int c0 = wave * chunk, c1 = min(n, c0 + chunk);
   uint32_t r = 0;
   if (c0 < c1)
@@ -421,22 +440,35 @@ __device__ QParam poll_norm(const u64* v, int blk, float* x, Shared& sh, double 
   return p;
 }
 
-// All waves: poll_all of an n-word vector, then the dynamic uint8 quantiser
-// on it, each wave on its own chunk; shifted codes to sh.codes.  Two
-// barriers.
+// All waves (barriers): poll_all of an n-word vector by waves below np,
+// then the dynamic uint8 quantiser on it (each wave on its own chunk when
+// all waves poll, else all waves on the whole vector after a barrier);
+// shifted codes to sh.codes.
 __device__ QParam poll_quant(const u64* v, int n, int blk, Shared& sh, int lane, int wave,
                              uint32_t tag, uint32_t* err, u64* tr = nullptr,
-                             const u64* flags = nullptr, uint32_t* stat = nullptr) {
-  const uint32_t r = poll_all(v, n, blk, sh.stage, err, lane, wave, tag, tr, flags);
+                             const u64* flags = nullptr, uint32_t* stat = nullptr, int np = NW,
+                             bool pairs = false) {
+  const uint32_t r = poll_all(v, n, blk, sh.stage, err, lane, wave, tag, tr, flags, np);
   if (stat && threadIdx.x == 0) *stat = r;
-  const int chunk = ((n + NW - 1) / NW + 127) & ~127;
-  const int c0 = wave * chunk, c1 = min(n, c0 + chunk);
   const u64* st = (const u64*)sh.stage;
   float lo = INFINITY, hi = -INFINITY;
-  for (int i = c0 + lane; i < c1; i += 64) {
+  int c0, c1, step;
+  if (np == NW) {  // every wave scans its own chunk
+    const int chunk = ((n + np - 1) / np + 127) & ~127;
+    c0 = wave * chunk + lane;
+    c1 = min(n, wave * chunk + chunk);
+    step = 64;
+  } else {  // the vector is complete once every poller is past the barrier
+    __syncthreads();
+    c0 = threadIdx.x;
+    c1 = n;
+    step = NT;
+  }
+  for (int i = c0; i < c1; i += step) {
     const float x = __uint_as_float((uint32_t)st[i]);
-    lo = fminf(lo, x);
-    hi = fmaxf(hi, x);
+    // pairs: the words are (min, max) pairs of the producers
+    if (!pairs || !(i & 1)) lo = fminf(lo, x);
+    if (!pairs || (i & 1)) hi = fmaxf(hi, x);
   }
   lo = wave_min(lo);
   hi = wave_max(hi);
@@ -453,10 +485,26 @@ __device__ QParam poll_quant(const u64* v, int n, int blk, Shared& sh, int lane,
     hi = fmaxf(hi, sh.redf[2 * k + 1]);
   }
   const QParam p = quant_param(lo, hi);
-  for (int i = c0 + lane; i < c1; i += 64)
+  if (pairs) return p;  // the quantisation parameters only
+  for (int i = c0; i < c1; i += step)
     sh.codes[i] = shift_code(quant_code(__uint_as_float((uint32_t)st[i]), p));
   __syncthreads();
   return p;
+}
+
+// Waves below NPOLL: poll n words of packed codes (4 per word, producer
+// blocks of blk words) and unpack them to sh.codes; all waves end at a
+// barrier.  The staging of each polling wave ends before DN_LDS.
+__device__ void poll_codes(const u64* v, int n, int blk, Shared& sh, int lane, int wave,
+                           uint32_t tag, uint32_t* err) {
+  poll_all(v, n, blk, sh.stage, err, lane, wave, tag, nullptr, nullptr, NPOLL);
+  if (wave < NPOLL) {
+    const int chunk = ((n + NPOLL - 1) / NPOLL + 127) & ~127;
+    const int c1 = min(n, wave * chunk + chunk);
+    const u64* st = (const u64*)sh.stage;
+    for (int i = wave * chunk + lane; i < c1; i += 64) ((uint32_t*)sh.codes)[i] = (uint32_t)st[i];
+  }
+  __syncthreads();
 }
 
 // ------------------------------------------------------ weight streams --
@@ -475,8 +523,8 @@ __device__ __forceinline__ void load_rows(i32x4 (&r)[NR][U], float (&msw)[NR], i
   for (int k = 0; k < NR; ++k) {
     const int i = row_local(s, rot, k);
     const bool valid = i < R;
-    msw[k] = valid ? ldg(sw + row0 + i) : 0.0f;
-    mcs[k] = valid ? ldg(cs + row0 + i) : 0;
+    msw[k] = valid ? ldc(sw, row0 + i) : 0.0f;
+    mcs[k] = valid ? ldc(cs, row0 + i) : 0;
   }
 #pragma unroll
   for (int k = 0; k < NR; ++k) {
@@ -563,7 +611,7 @@ constexpr int ATT_Q = ATT_QKV + 10 * 1024;
 constexpr int ATT_END = ATT_Q + (G + 2) * D * 4 + G * KEYS * 8 + 2 * G * 8;
 constexpr int PSTATE = 2 * PART;                       // words per (item, head)
 constexpr int MERGE_BATCH = 4;                         // items merged per pass
-static_assert(ATT_END <= 104 * 1024, "attention staging exceeds LDS stage");
+static_assert(ATT_END <= STAGE, "attention staging exceeds LDS stage");  // the down units are loaded after it
 static_assert(ATT_KV + MERGE_BATCH * G * PSTATE * 8 + 1024 <= ATT_Q, "merge batch too large");
 
 __device__ __forceinline__ int kv_row(int k) { return (k >> 1) * 260 + (k & 1) * D; }
@@ -775,7 +823,8 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
   // gate/up rows: rg per workgroup without attention work, by rank
   const int natt = NKV * nitem;
   const int rank = w - (w >= NKV * NI ? natt : (w / NI) * nitem + min(w % NI, nitem));
-  const int rg = (I + (NWG - natt) - 1) / (NWG - natt);
+  const int rg = ((I + (NWG - natt) - 1) / (NWG - natt) + 3) & ~3;  // whole code words
+  const int nprod = (I + rg - 1) / rg;                                  // ranks with rows
   const int gu0 = att ? 0 : rank * rg;
   const int ngu = att ? 0 : max(0, min(rg, I - gu0));
 
@@ -797,9 +846,9 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
     const int seg = n < Q ? 0 : (n < Q + KVD ? 1 : 2);
     const int nl = n - (seg == 0 ? 0 : (seg == 1 ? Q : Q + KVD));
     const int8_t* p = Lw.w[seg] + (size_t)nl * H;
-    sq[0] = valid ? ldg(Lw.sw[seg] + nl) : 0.f;
-    cq[0] = valid ? ldg(Lw.cs[seg] + nl) : 0;
-    bq[0] = valid ? ldg(Lw.bias[seg] + nl) : 0.f;
+    sq[0] = valid ? ldc(Lw.sw[seg], nl) : 0.f;
+    cq[0] = valid ? ldc(Lw.cs[seg], nl) : 0;
+    bq[0] = valid ? ldc(Lw.bias[seg], nl) : 0.f;
 #pragma unroll
     for (int u = 0; u < 2; ++u) wq[0][u] = valid ? ldg_nt(p + u * 1024 + lane16) : i32x4{0, 0, 0, 0};
   };
@@ -814,11 +863,11 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
     if (r >= ngu) return nullptr;
     return Lw.w[4 + m] + (size_t)(gu0 + r) * H + u * 1024 + lane16;
   };
-  // unit u of the down phase: half (s & 1) of row s >> 1
+  // unit u of the down phase: bytes [u KiB, u KiB + 1 KiB) of row s - NPOLL
+  // (a lane past the row's end reads the row start; its code is zero)
   auto down_addr = [&](const LayerW& Lw, int u) -> const int8_t* {
-    const int off = ((s & 1) * D_UNITS + u) * 1024 + lane16;
-    if (off >= I) return nullptr;
-    return Lw.w[6] + (size_t)(w * R_D + (s >> 1)) * I + off;
+    const int off = u * 1024 + lane16;
+    return Lw.w[6] + (size_t)(w * R_D + s - NPOLL) * I + (off < I ? off : 0);
   };
   auto issue_gate_up = [&](int l) {
     const LayerW& Lw = sh.lt[l & 1];
@@ -826,10 +875,10 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
     for (int k = 0; k < GU_ROWS; ++k) {
       const int r = s + NW * k;
       const bool valid = r < ngu;
-      sg[k] = valid ? ldg(Lw.sw[4] + gu0 + r) : 0.f;
-      cg[k] = valid ? ldg(Lw.cs[4] + gu0 + r) : 0;
-      su[k] = valid ? ldg(Lw.sw[5] + gu0 + r) : 0.f;
-      cu[k] = valid ? ldg(Lw.cs[5] + gu0 + r) : 0;
+      sg[k] = valid ? ldc(Lw.sw[4], gu0 + r) : 0.f;
+      cg[k] = valid ? ldc(Lw.cs[4], gu0 + r) : 0;
+      su[k] = valid ? ldc(Lw.sw[5], gu0 + r) : 0.f;
+      cu[k] = valid ? ldc(Lw.cs[5], gu0 + r) : 0;
     }
     // units 0..7 into registers, the last row's four units into this wave's
     // 4 KiB of LDS (stage bytes [16K, 80K) are free until the gate/up phase)
@@ -843,11 +892,25 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
             16, 0, 2);
     }
   };
-  auto issue_down = [&](int l) {
+  // loaders: the LDS part of their down row (any time the region is free)
+  auto issue_down_lds = [&](int l) {
+    if (s < NPOLL) return;
     const LayerW& Lw = sh.lt[l & 1];
-    sd = ldg(Lw.sw[6] + w * R_D + (s >> 1));
-    cd = ldg(Lw.cs[6] + w * R_D + (s >> 1));
-    prime_units<D_UNITS, W>(win, [&](int u) { return down_addr(Lw, u); });
+#pragma unroll
+    for (int u = W; u < D_UNITS; ++u)
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)down_addr(Lw, u),
+          (void __attribute__((address_space(3)))*)(sh.stage + DN_LDS +
+                                                    ((s - NPOLL) * D_LDS_UNITS + u - W) * 1024),
+          16, 0, 2);
+  };
+  // loaders: the register part (needs the weight registers free)
+  auto issue_down = [&](int l) {
+    if (s < NPOLL) return;
+    const LayerW& Lw = sh.lt[l & 1];
+    sd = ldc(Lw.sw[6], w * R_D + s - NPOLL);
+    cd = ldc(Lw.cs[6], w * R_D + s - NPOLL);
+    prime_units<W, W>(win, [&](int u) { return down_addr(Lw, u); });
   };
 
   const size_t rep = xcc_id();
@@ -863,6 +926,9 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
   if (A.L > 1 && tid >= 64 && tid < 64 + LTW)
     ((u64*)&sh.lt[1])[tid - 64] = ((const u64*)&A.layers[1])[tid - 64];
   if (tid < 17) sh.expc[tid] = kExpTab[tid];
+  // codes past the SwiGLU vector stay zero: the tail of the last down unit
+  // multiplies them
+  for (int i = I + tid; i < (int)sizeof(sh.codes); i += NT) sh.codes[i] = 0;
   __syncthreads();
   issue_qkv(0);
   if (att && tid < D / 2) {
@@ -905,9 +971,11 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
       attention_item(A, epoch, l, w, nitem, nchunk, sh, xl, tid, lane, wave);
       __syncthreads();
       issue_o(l);
+      issue_down_lds(l);
     } else {
       issue_o(l);
       issue_gate_up(l);
+      issue_down_lds(l);
     }
 
     // ---- o projection + residual
@@ -959,6 +1027,7 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
         aggs[k] = wave_sum(aggs[k]);
         aus[k] = wave_sum(aus[k]);
       }
+      float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
       for (int k = 0; k < GU_ROWS; ++k) {
         const int i = s + NW * k;
@@ -966,35 +1035,72 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
           const float gv = dequant(aggs[k] + zc * cg[k], qp.s, sg[k]);
           const float uv = dequant(aus[k] + zc * cu[k], qp.s, su[k]);
           const double gd = gv;
-          xput_rep(xl + OFF_A, I, gu0 + i, (float)(gd / (1.0 + exp_t(-gd, sh.expc)) * (double)uv), epoch);
+          const float a = (float)(gd / (1.0 + exp_t(-gd, sh.expc)) * (double)uv);
+          sh.aval[i] = a;
+          lo = fminf(lo, a);
+          hi = fmaxf(hi, a);
         }
       }
+      if (lane == 0) {
+        sh.redf[2 * s] = lo;
+        sh.redf[2 * s + 1] = hi;
+      }
       trace_done(A, w, l, 8, lane);
-      // every wave has issued its stores of this workgroup's block: raise the
-      // flag (a hint only; readers still check every word's tag, so a flag
-      // that overtakes a data word costs a re-read, not a wrong value)
       __syncthreads();
-      if (tid < NREP) xput(xl + OFF_AF + tid * NWG + rank, 0.f, epoch);
+      // round 1: this workgroup's min and max
+      if (tid < NREP && rank < nprod) {
+        lo = sh.redf[0];
+        hi = sh.redf[1];
+        for (int k = 1; k < NW; ++k) {
+          lo = fminf(lo, sh.redf[2 * k]);
+          hi = fmaxf(hi, sh.redf[2 * k + 1]);
+        }
+        u64* mm = xl + OFF_AMM + tid * 2 * NWG + 2 * rank;
+        xput(mm, lo, epoch);
+        xput(mm + 1, hi, epoch);
+      }
       issue_down(l);
     }
 
-    // ---- down + residual: waves 2r and 2r+1 each take half of row r
+    // ---- SwiGLU quantisation parameters from all producers' min/max
     asm volatile("" : "+v"(lane16), "+v"(tid), "+v"(lane));
-    qp = poll_quant(xl + OFF_A + rep * I, I, rg, sh, lane, wave, epoch, A.err, trace_sub(A, w, l, 19),
-                    xl + OFF_AF + rep * NWG, trace_stat(A, w, l, 14));
+    qp = poll_quant(xl + OFF_AMM + rep * 2 * NWG, 2 * nprod, 2, sh, lane, wave, epoch, A.err,
+                    trace_sub(A, w, l, 19), nullptr, trace_stat(A, w, l, 14), NPOLL, true);
+    // round 2: producers quantise their rows and publish the packed codes
+    if (!att && tid < ngu / 4) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        word |= (uint32_t)(uint8_t)shift_code(quant_code(sh.aval[4 * tid + j], qp)) << (8 * j);
+      const int k = gu0 / 4 + tid;
+#pragma unroll
+      for (int r = 0; r < NREP; ++r)
+        __hip_atomic_store(xl + OFF_AC + (size_t)r * (I / 4) + k, ((u64)epoch << 32) | word,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // ---- down + residual: waves 0..7 poll and quantise the SwiGLU vector
+    // while the loaders' down rows arrive; loader 8 + r computes row r
+    asm volatile("" : "+v"(lane16), "+v"(tid), "+v"(lane));
+    poll_codes(xl + OFF_AC + rep * (I / 4), I / 4, rg / 4, sh, lane, wave, epoch, A.err);
     trace_at(A, w, l, 9);
-    {
+    if (s >= NPOLL) {
       int acc = 0;
-      const int8_t* cb = sh.codes + (s & 1) * D_UNITS * 1024 + lane16;
-      run_units<D_UNITS, W>(win, [&](int u) { return down_addr(Lw, u); }, [&](int u, const i32x4 v) {
+      const int8_t* cb = sh.codes + lane16;
+      run_units<W, W>(win, [&](int u) { return down_addr(Lw, u); }, [&](int u, const i32x4 v) {
         acc = dot16(v, *(const i32x4*)(cb + u * 1024), acc);
       });
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS units
+#pragma unroll
+      for (int u = W; u < D_UNITS; ++u) {
+        const i32x4 v = *(const i32x4*)(sh.stage + DN_LDS +
+                                        ((s - NPOLL) * D_LDS_UNITS + u - W) * 1024 + lane16);
+        acc = dot16(v, *(const i32x4*)(cb + u * 1024), acc);
+      }
       acc = wave_sum(acc);
-      if (lane == 0) sh.redi[s] = acc;
-      __syncthreads();
-      if (lane == 0 && (s & 1) == 0) {
-        const int n = w * R_D + (s >> 1);
-        const float y = dequant(sh.redi[s] + sh.redi[s + 1] + (128 - qp.z) * cd, qp.s, sd);
+      if (lane == 0) {
+        const int n = w * R_D + s - NPOLL;
+        const float y = dequant(acc + (128 - qp.z) * cd, qp.s, sd);
         xput_rep(xn + OFF_X0, H, n, sh.x1s[n] + y, epoch);
       }
     }
