@@ -294,9 +294,13 @@ int mega_step(const ark_model* m, const int32_t* token, int pos, float* kd, floa
   S.hidden_out = hidden_out;
   S.mask = logits ? mask : nullptr;
   S.out_token = out_token;
-  prof_begin(st, true);
-  const hipError_t e = decode_mega_launch(st, ws + p.mega, S);
-  prof_end(st, true);
+  hipEvent_t eb = nullptr, ee = nullptr;
+  if (g_prof.ev && g_prof.count < g_prof.n) {
+    eb = g_prof.ev[2 * g_prof.count];
+    ee = g_prof.ev[2 * g_prof.count + 1];
+    ++g_prof.count;
+  }
+  const hipError_t e = decode_mega_launch(st, ws + p.mega, S, eb, ee);
   return e == hipSuccess ? ARK_OK : ARK_E_HIP;
 }
 

@@ -1344,7 +1344,8 @@ hipError_t decode_mega_upload(hipStream_t st, void* ws, int L, int T, const Mega
   return hipMemcpyAsync(lay.table, tab, sizeof(mk::LayerW) * L, hipMemcpyHostToDevice, st);
 }
 
-hipError_t decode_mega_launch(hipStream_t st, void* ws, const MegaStep& S) {
+hipError_t decode_mega_launch(hipStream_t st, void* ws, const MegaStep& S, hipEvent_t ev_begin,
+                              hipEvent_t ev_end) {
   MegaLayout lay = mega_layout(ws, S.L, S.T);
   // the exchange words and the partial attention states that follow them
   const size_t part_words = (size_t)S.L * mk::NKV * mk::NI * mk::G * mk::PSTATE;
@@ -1385,8 +1386,11 @@ hipError_t decode_mega_launch(hipStream_t st, void* ws, const MegaStep& S) {
   A.marker_value = marker;
   A.epoch = lay.epoch;
   void* args[] = {&A};
-  return hipLaunchCooperativeKernel((const void*)mk::k_decode, dim3(mk::NWG), dim3(mk::NT), args,
-                                    sizeof(mk::Shared), st);
+  if (ev_begin) hipEventRecord(ev_begin, st);
+  e = hipLaunchCooperativeKernel((const void*)mk::k_decode, dim3(mk::NWG), dim3(mk::NT), args,
+                                 sizeof(mk::Shared), st);
+  if (ev_end) hipEventRecord(ev_end, st);
+  return e;
 }
 
 size_t decode_mega_trace_offset(int L, int T) {

@@ -118,6 +118,9 @@ size_t decode_mega_ws_bytes(int L, int T);
 size_t decode_mega_trace_offset(int L, int T);
 hipError_t decode_mega_init();
 hipError_t decode_mega_upload(hipStream_t st, void* ws, int L, int T, const MegaLayer* layers);
-hipError_t decode_mega_launch(hipStream_t st, void* ws, const MegaStep& S);
+// ev_begin / ev_end (nullable) are recorded around the persistent kernel
+// alone (not its preparation kernel).
+hipError_t decode_mega_launch(hipStream_t st, void* ws, const MegaStep& S, hipEvent_t ev_begin,
+                              hipEvent_t ev_end);
 
 }  // namespace ark
