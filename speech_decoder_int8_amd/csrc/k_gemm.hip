@@ -12,6 +12,8 @@
 // the 64-wide K step.  Because A and B use the same lane->K assignment, the
 // product is sum_k A[i][k] * B[j][k] whatever order the instruction walks K.
 // The 16x16 result sits in lane (j + 16*(i/4)), register i % 4.
+#include <stdlib.h>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -203,6 +205,8 @@ hipError_t launch_gemm(hipStream_t st, int M, int K, const int8_t* codes, const 
     P.seg_start[i + 1] = P.seg_start[i] + segs[i].n;
   }
   P.ncols = (epi == EPI_SWIGLU) ? segs[0].n : P.seg_start[nseg];
+  if (gemm_big_supported(M, K) && !getenv("ARK_GEMM_SMALL"))
+    return launch_gemm_big(st, M, K, codes, s, z, rows_per_seq, segs, nseg, epi, acc_out);
   if (M <= 32) {
     constexpr int BM = 32, BN = 128;
     const int tn = epi == EPI_SWIGLU ? BN / 2 : BN;

@@ -1,0 +1,329 @@
+// Large int8 x int8 -> int32 GEMM for prefill on gfx950 matrix cores
+// (v_mfma_i32_32x32x32_i8), with the same dequantising epilogues as k_gemm
+// (store (+bias), residual add, SwiGLU over paired gate/up columns).
+//
+// Tiles of BM x 256 x 64 (BM = 128), 256 threads as 2 x 2 waves, each
+// wave (BM/2) x 128 of 32x32 accumulators.  Operand tiles go from global
+// memory straight into LDS with 16-byte LDS-DMA loads (no register staging),
+// NS stages deep, so the loads of step k+NS-1 overlap the matrix work of
+// step k; one barrier per 64-wide K step.
+//
+// LDS tile layout: 64-byte rows; the 16-byte chunk c of row r sits at chunk
+// position c ^ ((r >> 1) & 3), so the 8 lanes served together by a 16-byte
+// read (8 consecutive rows, same chunk) cover all 32 banks.  The DMA writes
+// 1 KiB per instruction at lane-contiguous positions; each lane picks the
+// global (row, chunk) that belongs at its position.
+//
+// Fragment layout: lane l supplies row (l % 32) of its A and of its B
+// fragment, both with K bytes [16*(l/32), +16) of the 32-wide K substep; the
+// 32x32 result sits in lane (j + 32*((i/4)%2)), register (i/8)*4 + i%4 for
+// row i, column j.  A and B share the lane -> K assignment, so each output
+// is the full sum over K whatever order the instruction walks it.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ark {
+
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+namespace g2 {
+constexpr int BN = 256, BK = 64, NT = 256;
+}  // namespace g2
+
+struct Gemm2Params {
+  int M, K, ncols, epi, rows_per_seq, nseg, tiles_m, tiles;
+  const int8_t* A;
+  const float* qs;
+  const int* qz;
+  Seg seg[3];
+  int seg_start[4];
+  int32_t* acc_out;
+};
+
+#ifndef ARK_G2_SWZ_SHIFT
+#define ARK_G2_SWZ_SHIFT 2
+#endif
+__device__ __forceinline__ int swz(int r, int c) {
+  return r * 64 + ((c ^ ((r >> ARK_G2_SWZ_SHIFT) & 3)) << 4);
+}
+__device__ __forceinline__ int swzc(int r, int p) { return p ^ ((r >> ARK_G2_SWZ_SHIFT) & 3); }
+
+__device__ __forceinline__ void dma16(const int8_t* src, int8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                   (void __attribute__((address_space(3)))*)lds_base, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) for a compile-time n, expcnt/lgkmcnt untouched
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+template <int BM, int NS>
+__global__ __launch_bounds__(256, 1) void k_gemm_big(Gemm2Params P) {
+  using namespace g2;
+  constexpr int FM = BM / 64;               // 32-row blocks per wave
+  constexpr int FN = 4;                     // 32-column blocks per wave
+  constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK, STAGE = A_BYTES + B_BYTES;
+  constexpr int A_INS = A_BYTES / 1024 / 4, B_INS = B_BYTES / 1024 / 4;  // per wave per stage
+  constexpr int INS = A_INS + B_INS;
+  extern __shared__ __align__(16) int8_t lds[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const bool swiglu = P.epi == EPI_SWIGLU;
+
+  // XCD-aware tile order: the workgroups of one XCD (bid % 8) take a
+  // contiguous run of tiles, n-tile major, so they share weight tiles in
+  // their L2.
+  const int per = (P.tiles + 7) / 8;
+  const int t = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (t >= P.tiles) return;
+  const int m0 = (t % P.tiles_m) * BM;
+  const int nb = (t / P.tiles_m) * (swiglu ? BN / 2 : BN);
+  const int K = P.K, nk = K / BK;
+
+  // per-lane DMA sources: A instructions wave*A_INS + i, B instructions
+  // wave*B_INS + i; instruction u covers rows 16u .. 16u+15
+  const int8_t* asrc[A_INS];
+  int achunk[A_INS];
+#pragma unroll
+  for (int i = 0; i < A_INS; ++i) {
+    const int r = 16 * (wave * A_INS + i) + (lane >> 2);
+    achunk[i] = swzc(r, lane & 3);
+    asrc[i] = P.A + (size_t)min(m0 + r, P.M - 1) * K + 16 * achunk[i];
+  }
+  const int8_t* bsrc[B_INS];
+#pragma unroll
+  for (int i = 0; i < B_INS; ++i) {
+    const int r = 16 * (wave * B_INS + i) + (lane >> 2);
+    const int c = swzc(r, lane & 3);
+    const int8_t* w;
+    if (swiglu) {
+      const int blk = r >> 5;
+      const int n = min(nb + (blk >> 1) * 32 + (r & 31), P.ncols - 1);
+      w = ((blk & 1) ? P.seg[1].w : P.seg[0].w) + (size_t)n * K;
+    } else {
+      const int col = min(nb + r, P.ncols - 1);
+      int s = 0;
+      while (s + 1 < P.nseg && col >= P.seg_start[s + 1]) ++s;
+      w = P.seg[s].w + (size_t)(col - P.seg_start[s]) * K;
+    }
+    bsrc[i] = w + 16 * c;
+  }
+
+  auto issue = [&](int ks, int buf) {
+    int8_t* base = lds + buf * STAGE;
+    const int k0 = ks * BK;
+#pragma unroll
+    for (int i = 0; i < A_INS; ++i) dma16(asrc[i] + k0, base + (wave * A_INS + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < B_INS; ++i)
+      dma16(bsrc[i] + k0, base + A_BYTES + (wave * B_INS + i) * 1024);
+  };
+
+  i32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
+
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) issue(s, s);
+
+  const int lr = lane & 31, lc = lane >> 5;
+  for (int ks = 0; ks < nk; ++ks) {
+    // this wave's loads of step ks are done once at most the later issued
+    // stages' loads are outstanding
+    if (NS == 3 && ks + 1 < nk)
+      wait_vm<INS>();
+    else
+      wait_vm<0>();
+    // every wave's step-ks loads are in LDS and every wave is done reading
+    // the buffer refilled next; a plain barrier (no wait for the loads that
+    // stay in flight)
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
+    __builtin_amdgcn_s_barrier();
+#ifndef ARK_G2_NO_DMA
+    if (ks + NS - 1 < nk) issue(ks + NS - 1, (ks + NS - 1) % NS);
+#endif
+    const int8_t* As = lds + (ks % NS) * STAGE;
+    const int8_t* Bs = As + A_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int c = 2 * kk + lc;
+      i32x4 fa[FM], fb[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        fa[i] = *(const i32x4*)(As + swz(wm * (BM / 2) + i * 32 + lr, c));
+#pragma unroll
+      for (int j = 0; j < FN; ++j) fb[j] = *(const i32x4*)(Bs + swz(wn * 128 + j * 32 + lr, c));
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#ifndef ARK_G2_NO_MFMA
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+#else
+          acc[i][j][0] ^= fa[i][0] ^ fb[j][1];
+#endif
+    }
+  }
+
+  // ---- epilogue: row i of a 32x32 block is in register (i/8)*4 + i%4 of
+  // lanes with (l/32) == (i/4)%2 (every index below is a compile-time
+  // constant, so the accumulators stay in registers).  All per-column and
+  // per-row parameters are loaded up front: the output stores may alias
+  // them as far as the compiler knows, which would otherwise chain every
+  // load behind the previous store.
+  float csw[FN], cbias[FN], usw[FN / 2];
+  bool hasb[FN];
+  int ccs[FN], ucs[FN / 2];
+  float* cout[FN];
+  int cldo[FN];
+  bool cok[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    if (swiglu) {
+      if (j % 2 == 0) {
+        const int n = nb + (wn * 2 + j / 2) * 32 + lr;
+        const int nn = min(n, P.ncols - 1);
+        cok[j] = n < P.ncols;
+        csw[j] = P.seg[0].sw[nn];
+        ccs[j] = P.seg[0].cs[nn];
+        usw[j / 2] = P.seg[1].sw[nn];
+        ucs[j / 2] = P.seg[1].cs[nn];
+        cout[j] = P.seg[0].out + nn;
+        cldo[j] = P.seg[0].ldo;
+      }
+    } else {
+      const int col = nb + wn * 128 + j * 32 + lr;
+      const int cc = min(col, P.ncols - 1);
+      int si = 0;
+      while (si + 1 < P.nseg && cc >= P.seg_start[si + 1]) ++si;
+      const Seg& S = P.seg[si];
+      const int n = cc - P.seg_start[si];
+      cok[j] = col < P.ncols;
+      csw[j] = S.sw[n];
+      ccs[j] = S.cs[n];
+      hasb[j] = S.bias != nullptr;
+      cbias[j] = hasb[j] ? S.bias[n] : 0.f;
+      cout[j] = S.out + n;
+      cldo[j] = S.ldo;
+    }
+  }
+  const int rbase = m0 + wm * (BM / 2) + lc * 4;
+  float rs[FM][4];
+  int rz[FM][4];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // rows rbase + i*32 + q*8 + (0..3) all lie in one sequence unless a
+      // sequence boundary falls inside; take the first row's and check below
+      const int b = min(rbase + i * 32 + q * 8, P.M - 1) / P.rows_per_seq;
+      rs[i][q] = P.qs[b];
+      rz[i][q] = 128 - P.qz[b];
+    }
+#pragma clang loop unroll(full)
+  for (int i = 0; i < FM; ++i) {
+#pragma clang loop unroll(full)
+    for (int v = 0; v < 16; ++v) {
+      const int row = rbase + i * 32 + (v >> 2) * 8 + (v & 3);
+      if (row >= P.M) continue;
+      float s = rs[i][v >> 2];
+      int zc = rz[i][v >> 2];
+      if ((row / P.rows_per_seq) != (min(rbase + i * 32 + (v >> 2) * 8, P.M - 1) / P.rows_per_seq)) {
+        const int b = row / P.rows_per_seq;  // a sequence starts inside this group of 4 rows
+        s = P.qs[b];
+        zc = 128 - P.qz[b];
+      }
+      if (swiglu) {
+#pragma clang loop unroll(full)
+        for (int j = 0; j < FN; j += 2) {
+          if (cok[j]) {
+            const int agc = acc[i][j][v] + zc * ccs[j];
+            const float g = dequant(agc, s, csw[j]);
+            const float u = dequant(acc[i][j + 1][v] + zc * ucs[j / 2], s, usw[j / 2]);
+            const double gd = g;
+            cout[j][(size_t)row * cldo[j]] = (float)(gd / (1.0 + exp(-gd)) * (double)u);
+            if (P.acc_out) P.acc_out[(size_t)row * P.ncols + nb + (wn * 2 + j / 2) * 32 + lr] = agc;
+          }
+        }
+      } else {
+        // residual: the old values of this row are read before any store
+        float old[FN];
+#pragma clang loop unroll(full)
+        for (int j = 0; j < FN; ++j)
+          old[j] = (P.epi == EPI_RESID && cok[j]) ? cout[j][(size_t)row * cldo[j]] : 0.f;
+#pragma clang loop unroll(full)
+        for (int j = 0; j < FN; ++j) {
+          if (cok[j]) {
+            const int at = acc[i][j][v] + zc * ccs[j];
+            float y = dequant(at, s, csw[j]);
+            if (hasb[j]) y = y + cbias[j];
+            float* o = cout[j] + (size_t)row * cldo[j];
+            if (P.epi == EPI_RESID)
+              *o = old[j] + y;
+            else
+              *o = y;
+            if (P.acc_out) P.acc_out[(size_t)row * P.ncols + nb + wn * 128 + j * 32 + lr] = at;
+          }
+        }
+      }
+    }
+  }
+}
+
+static constexpr int kStages = 3;
+
+template <int BM>
+static hipError_t launch_big(hipStream_t st, Gemm2Params P) {
+  constexpr int bytes = kStages * (BM + g2::BN) * g2::BK;
+  static bool attr = false;
+  if (!attr) {
+    const hipError_t e = hipFuncSetAttribute((const void*)k_gemm_big<BM, kStages>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const int tn = P.epi == EPI_SWIGLU ? g2::BN / 2 : g2::BN;
+  P.tiles_m = (P.M + BM - 1) / BM;
+  P.tiles = P.tiles_m * ((P.ncols + tn - 1) / tn);
+  const int grid = 8 * ((P.tiles + 7) / 8);
+  hipLaunchKernelGGL((k_gemm_big<BM, kStages>), dim3(grid), dim3(g2::NT), bytes, st, P);
+  return hipGetLastError();
+}
+
+bool gemm_big_supported(int M, int K) { return M >= 128 && K % g2::BK == 0; }
+
+hipError_t launch_gemm_big(hipStream_t st, int M, int K, const int8_t* codes, const float* s,
+                           const int* z, int rows_per_seq, const Seg* segs, int nseg, Epi epi,
+                           int32_t* acc_out) {
+  Gemm2Params P = {};
+  P.M = M;
+  P.K = K;
+  P.A = codes;
+  P.qs = s;
+  P.qz = z;
+  P.rows_per_seq = rows_per_seq;
+  P.nseg = nseg;
+  P.epi = epi;
+  P.acc_out = acc_out;
+  P.seg_start[0] = 0;
+  for (int i = 0; i < nseg; ++i) {
+    P.seg[i] = segs[i];
+    P.seg_start[i + 1] = P.seg_start[i] + segs[i].n;
+  }
+  P.ncols = (epi == EPI_SWIGLU) ? segs[0].n : P.seg_start[nseg];
+#ifndef ARK_G2_BM
+#define ARK_G2_BM 128
+#endif
+  return launch_big<ARK_G2_BM>(st, P);
+}
+
+}  // namespace ark

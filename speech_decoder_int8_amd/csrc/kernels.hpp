@@ -64,6 +64,12 @@ hipError_t launch_gemv_codes(hipStream_t st, int B, int K, const int8_t* codes, 
                              const int* z, const Seg* segs, int nseg, Epi epi, int32_t* acc_out);
 // MFMA GEMM (k_gemm.hip): shifted codes [M][K]; row r uses (s[r / rows_per_seq],
 // z[r / rows_per_seq]).
+// Large-M GEMM (prefill): same contract as launch_gemm; requires
+// gemm_big_supported(M, K).
+bool gemm_big_supported(int M, int K);
+hipError_t launch_gemm_big(hipStream_t st, int M, int K, const int8_t* codes, const float* s,
+                           const int* z, int rows_per_seq, const Seg* segs, int nseg, Epi epi,
+                           int32_t* acc_out);
 hipError_t launch_gemm(hipStream_t st, int M, int K, const int8_t* codes, const float* s,
                        const int* z, int rows_per_seq, const Seg* segs, int nseg, Epi epi,
                        int32_t* acc_out);
@@ -74,6 +80,13 @@ hipError_t launch_gemm(hipStream_t st, int M, int K, const int8_t* codes, const 
 struct PosArgs {
   int32_t p[64];
 };
+
+// Prefill attention (S > 1) on fp64 matrix cores; G = NH / NKV <= 8.
+bool attention_prefill_supported(int NH, int NKV);
+hipError_t launch_attention_prefill(hipStream_t st, int B, int S, int NH, int NKV, int T,
+                                    const float* q, const float* k_cache, const float* v_cache,
+                                    const float* k_delta, const float* v_delta,
+                                    const PosArgs& pos, float* out);
 hipError_t launch_rope(hipStream_t st, int B, int S, int NH, int NKV, const float* qkv,
                        const double* cosT, const double* sinT, const PosArgs& pos, float* q,
                        float* k_delta, float* v_delta);

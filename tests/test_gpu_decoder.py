@@ -131,6 +131,19 @@ def test_small_decode_from_prefilled_caches(small, B):
     run_parity(cfg, om, gm, None, lengths, kc, vc, 4, ids=ids)
 
 
+def test_small_long_prefill_large_tile_gemm(small):
+    # 2 x 150 rows: every projection of the prefill runs the large-tile GEMM
+    # (store + bias, residual and SwiGLU epilogues, ragged last tiles)
+    cfg, om, _ = small
+    cfg = cfg.with_(batch=2, prefill_len=150, max_total_len=192)
+    om = oracle.build_model(cfg, synth)
+    gm = ark.load_model(cfg, synth)
+    rng = np.random.default_rng(33)
+    x = rng.standard_normal((2, 150, cfg.hidden)).astype(np.float32)
+    kc, vc = _empty(cfg, 2)
+    run_parity(cfg, om, gm, x, [0, 20], kc, vc, 2)
+
+
 def test_small_native_greedy_loop_matches_oracle(small):
     cfg, om, gm = small
     B = cfg.batch

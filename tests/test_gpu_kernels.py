@@ -69,7 +69,9 @@ def test_dynquant_all_zero_tensor():
 
 @pytest.mark.parametrize("use_gemm", [False, True])
 @pytest.mark.parametrize("B,R,n,k", [(1, 1, 300, 2048), (2, 2, 2560, 2048), (1, 3, 96, 11008),
-                                     (3, 67, 333, 2048), (2, 16, 130, 1024)])
+                                     (3, 67, 333, 2048), (2, 16, 130, 1024),
+                                     # M >= 128: the large-tile prefill GEMM (ragged and whole tiles)
+                                     (2, 100, 2560, 2048), (1, 256, 512, 1024), (1, 130, 200, 11008)])
 def test_qlinear_bit_exact(use_gemm, B, R, n, k):
     if not use_gemm and B * R > 4:
         pytest.skip("the decode GEMV takes at most 4 rows")
