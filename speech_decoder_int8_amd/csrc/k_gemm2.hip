@@ -61,7 +61,7 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 template <int BM, int NS>
-__global__ __launch_bounds__(256, 1) void k_gemm_big(Gemm2Params P) {
+__global__ __launch_bounds__(256, 2) void k_gemm_big(Gemm2Params P) {
   using namespace g2;
   constexpr int FM = BM / 64;               // 32-row blocks per wave
   constexpr int FN = 4;                     // 32-column blocks per wave
@@ -75,13 +75,18 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(Gemm2Params P) {
   const bool swiglu = P.epi == EPI_SWIGLU;
 
   // XCD-aware tile order: the workgroups of one XCD (bid % 8) take a
-  // contiguous run of tiles, n-tile major, so they share weight tiles in
-  // their L2.
+  // contiguous run of tiles, and runs walk groups of 8 m-tiles x all
+  // n-tiles m-fastest, so the ~64 concurrent workgroups of an XCD share
+  // about 8 activation and 8 weight tiles in their L2.
   const int per = (P.tiles + 7) / 8;
   const int t = (blockIdx.x % 8) * per + blockIdx.x / 8;
   if (t >= P.tiles) return;
-  const int m0 = (t % P.tiles_m) * BM;
-  const int nb = (t / P.tiles_m) * (swiglu ? BN / 2 : BN);
+  const int tiles_n = P.tiles / P.tiles_m;
+  const int grp = t / (8 * tiles_n);
+  const int gm = min(8, P.tiles_m - grp * 8);
+  const int tg = t - grp * 8 * tiles_n;
+  const int m0 = (grp * 8 + tg % gm) * BM;
+  const int nb = (tg / gm) * (swiglu ? BN / 2 : BN);
   const int K = P.K, nk = K / BK;
 
   // per-lane DMA sources: A instructions wave*A_INS + i, B instructions
@@ -153,25 +158,38 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(Gemm2Params P) {
 #endif
     const int8_t* As = lds + (ks % NS) * STAGE;
     const int8_t* Bs = As + A_BYTES;
+    // both 32-wide K substeps' fragments are read up front into separate
+    // registers, so no read waits for a matrix instruction still using its
+    // source registers
+    i32x4 fa[2][FM], fb[2][FN];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int c = 2 * kk + lc;
-      i32x4 fa[FM], fb[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        fa[i] = *(const i32x4*)(As + swz(wm * (BM / 2) + i * 32 + lr, c));
+        fa[kk][i] = *(const i32x4*)(As + swz(wm * (BM / 2) + i * 32 + lr, c));
 #pragma unroll
-      for (int j = 0; j < FN; ++j) fb[j] = *(const i32x4*)(Bs + swz(wn * 128 + j * 32 + lr, c));
+      for (int j = 0; j < FN; ++j) fb[kk][j] = *(const i32x4*)(Bs + swz(wn * 128 + j * 32 + lr, c));
+    }
+    // pin all fragments live at once (keeps the reads ahead of the MFMAs)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(fa[kk][i]));
+#pragma unroll
+      for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(fb[kk][j]));
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #ifndef ARK_G2_NO_MFMA
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
 #else
-          acc[i][j][0] ^= fa[i][0] ^ fb[j][1];
+          acc[i][j][0] ^= fa[kk][i][0] ^ fb[kk][j][1];
 #endif
-    }
   }
 
   // ---- epilogue: row i of a 32x32 block is in register (i/8)*4 + i%4 of
