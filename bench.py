@@ -74,6 +74,35 @@ def step_kernel_bytes(cfg, live_rows: float) -> float:
     return w8 + scales + bias + gains + kv + deltas + H * 2 + V + V * 4
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_bs1_c1_persistent_hbm_counters.md")
+TRAFFIC_SOURCES = ("speech_decoder_int8_amd/csrc/k_decode.hip", "speech_decoder_int8_amd/csrc/common.hpp")
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of the persistent decode kernel as the
+    FETCH_SIZE/WRITE_SIZE counters measured them (scaled by a plain copy of
+    known size), read from the committed counter summary.  None when the
+    summary is missing or the kernel's sources changed since the counters
+    were taken (the summary records their sha256)."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if line.startswith("traffic_") and ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    if fields.get("traffic_kernel") != kernel or fields.get("traffic_sources_sha256") != h.hexdigest():
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def gateup_bytes(cfg, B: int) -> int:
     """Algorithmic bytes of one gate/up launch at batch B: both int8
     matrices and their scales, the input rows and gain, the SwiGLU output."""
@@ -185,9 +214,12 @@ def gpu_bench(args):
     ms_step = wall * 1e3 / K
     tok_s = K / wall
     kern_ms = float(np.mean(durs)) if durs else float("nan")
-    # positions pos0 .. pos0 + K - 1: pos0 + k valid rows at step k
-    gb = step_kernel_bytes(cfg, pos0 + (K - 1) / 2) if persistent else gateup_bytes(cfg, 1)
+    # the method's bytes per token (all T cache rows, as the full-cache
+    # formulation reads them); the kernel itself skips the masked rows
+    gb = decode_bytes(cfg, 1) if persistent else gateup_bytes(cfg, 1)
+    live_gb = step_kernel_bytes(cfg, pos0 + (K - 1) / 2)   # pos0 + k valid rows at step k
     achieved = gb / (kern_ms * 1e-3) if durs else float("nan")
+    traffic = measured_traffic(kernel) if persistent else None
     result = {
         "metric": "decode tokens/s (bs1, bs32) + prefill tokens/s; % HBM / int8-MFMA roofline",
         "value": round(tok_s, 2),
@@ -222,8 +254,9 @@ def gpu_bench(args):
             "peak": PEAK_HBM / 1e9,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM, 4),
-            "traffic": None,
+            "traffic": traffic,
             "bytes_per_launch": int(gb),
+            "live_rows_bytes_per_launch": int(live_gb),
             "avg_launch_us": round(kern_ms * 1e3, 3),
             "launches_timed": len(durs),
         },
@@ -289,6 +322,20 @@ def gpu_bench(args):
     return result
 
 
+def copy_probe(mib: int) -> None:
+    """A plain device-to-device copy of `mib` MiB, 8 times: under
+    `rocprofv3 --pmc FETCH_SIZE` (or WRITE_SIZE) each dispatch should read
+    (write) exactly mib MiB, which calibrates the counters' units."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(8):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n * 4, "copies": 8}), flush=True)
+
+
 # -------------------------------------------------------- CPU baseline ---
 def cpu_baseline(n_layers: int):
     """The oracle, untuned, on a bounded sample of the same workload: one
@@ -343,6 +390,9 @@ def main():
     ap.add_argument("--no-extras", dest="extras", action="store_false")
     ap.add_argument("--no-cpu", dest="cpu", action="store_false")
     ap.add_argument("--cpu-layers", type=int, default=6)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only copy a device buffer of MIB MiB 8 times and exit (a plain copy "
+                         "kernel of known size, to scale the HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -352,6 +402,9 @@ def main():
     if args.steps < 1 or args.warmup < 0:
         print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     result = gpu_bench(args)
     result["cpu_baseline"] = cpu_baseline(args.cpu_layers) if args.cpu else None
     print(json.dumps(result), flush=True)

@@ -9,10 +9,16 @@
 // step k; one barrier per 64-wide K step.
 //
 // LDS tile layout: 64-byte rows; the 16-byte chunk c of row r sits at chunk
-// position c ^ ((r >> 1) & 3), so the 8 lanes served together by a 16-byte
-// read (8 consecutive rows, same chunk) cover all 32 banks.  The DMA writes
-// 1 KiB per instruction at lane-contiguous positions; each lane picks the
-// global (row, chunk) that belongs at its position.
+// position c ^ ((r >> 2) & 3), so the 16 lanes served together by a 16-byte
+// read (16 consecutive rows, same chunk) cover all 64 banks of gfx950's LDS.
+// The DMA writes 1 KiB per instruction at lane-contiguous positions; each
+// lane picks the global (row, chunk) that belongs at its position.
+//
+// Two workgroups share a CU (launch bounds 256 x 2), so one's epilogue and
+// prologue overlap the other's main loop.  Workgroup ids are dealt
+// round-robin over the 8 XCDs, so the tile order gives each XCD a
+// contiguous run of tiles (groups of 8 M-tiles, M fastest) and its L2 sees
+// few distinct operand tiles at a time.
 //
 // Fragment layout: lane l supplies row (l % 32) of its A and of its B
 // fragment, both with K bytes [16*(l/32), +16) of the 32-wide K substep; the
@@ -40,13 +46,11 @@ struct Gemm2Params {
   int32_t* acc_out;
 };
 
-#ifndef ARK_G2_SWZ_SHIFT
-#define ARK_G2_SWZ_SHIFT 2
-#endif
-__device__ __forceinline__ int swz(int r, int c) {
-  return r * 64 + ((c ^ ((r >> ARK_G2_SWZ_SHIFT) & 3)) << 4);
-}
-__device__ __forceinline__ int swzc(int r, int p) { return p ^ ((r >> ARK_G2_SWZ_SHIFT) & 3); }
+// 16-byte chunk c of tile row r sits at chunk c ^ ((r >> 2) & 3): the 16
+// lanes of one fragment read (rows r..r+15 of one chunk column) then cover
+// all 64 LDS banks without a conflict
+__device__ __forceinline__ int swz(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+__device__ __forceinline__ int swzc(int r, int p) { return p ^ ((r >> 2) & 3); }
 
 __device__ __forceinline__ void dma16(const int8_t* src, int8_t* lds_base) {
   __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
@@ -153,9 +157,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(Gemm2Params P) {
     // stay in flight)
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
     __builtin_amdgcn_s_barrier();
-#ifndef ARK_G2_NO_DMA
     if (ks + NS - 1 < nk) issue(ks + NS - 1, (ks + NS - 1) % NS);
-#endif
     const int8_t* As = lds + (ks % NS) * STAGE;
     const int8_t* Bs = As + A_BYTES;
     // both 32-wide K substeps' fragments are read up front into separate
@@ -185,11 +187,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(Gemm2Params P) {
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-#ifndef ARK_G2_NO_MFMA
           acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
-#else
-          acc[i][j][0] ^= fa[kk][i][0] ^ fb[kk][j][1];
-#endif
   }
 
   // ---- epilogue: row i of a 32x32 block is in register (i/8)*4 + i%4 of
@@ -338,10 +336,7 @@ hipError_t launch_gemm_big(hipStream_t st, int M, int K, const int8_t* codes, co
     P.seg_start[i + 1] = P.seg_start[i] + segs[i].n;
   }
   P.ncols = (epi == EPI_SWIGLU) ? segs[0].n : P.seg_start[nseg];
-#ifndef ARK_G2_BM
-#define ARK_G2_BM 128
-#endif
-  return launch_big<ARK_G2_BM>(st, P);
+  return launch_big<128>(st, P);
 }
 
 }  // namespace ark
