@@ -39,7 +39,10 @@ constexpr int G = NH / NKV;               // query heads per KV head
 constexpr int NQKV = Q + 2 * KVD;         // 2560 q|k|v rows
 constexpr int NWG = 256, NT = 1024, NW = 16, NS = NW - 1;
 constexpr int KEYS = 64;                  // cache rows per attention chunk
-constexpr int NI = 8;                     // attention items per KV head (chunk stride)
+constexpr int HPI = 4;                    // query heads per attention item
+constexpr int HH = G / HPI;               // items side by side per KV head (head groups)
+constexpr int NIH = 4;                    // items per (KV head, head group) along the cache
+constexpr int NATT = NKV * HH * NIH;      // workgroups that may hold an attention item
 constexpr int PART = 2 + D;               // fp64 words of one partial softmax state
 constexpr uint32_t SPIN_LIMIT = 1u << 15;  // ~30-60 ms per wait: a failure ends in seconds
 constexpr int NREP = 8;                   // replicas of each broadcast vector (one per XCD)
@@ -64,8 +67,8 @@ constexpr int R_QKV = NQKV / NWG, R_O = H / NWG, R_D = H / NWG;
 static_assert(R_QKV * NWG == NQKV && R_O * NWG == H && R_D * NWG == H, "row split");
 static_assert(R_QKV <= NW && R_O <= NW && 2 * R_D == NW, "rows per wave");
 constexpr int GU_ROWS = 3;
-static_assert((((I + (NWG - NKV * NI) - 1) / (NWG - NKV * NI) + 3) & ~3) <= GU_ROWS * NW,
-              "gate/up rows");
+static_assert(GU_ROWS <= 4, "SwiGLU rows of a wave sit on lanes of one DPP quad");
+static_assert((((I + (NWG - NATT) - 1) / (NWG - NATT) + 3) & ~3) <= GU_ROWS * NW, "gate/up rows");
 constexpr int STAGE = 112 * 1024;             // LDS staging bytes
 constexpr int GU_LDS = 16 * 1024;             // stage offset of the gate/up units in LDS
 // down projection: waves 8..15 ("loaders") each own one of the 8 rows (11
@@ -236,14 +239,37 @@ __constant__ double kExpTab[17] = {
     0x1.62e42fee00000p-1, 0x1.a39ef35793c76p-33, 0x1.71547652b82fep+0};
 
 __device__ __forceinline__ double exp_t(double x, const double* t) {
-  if (!(x > -746.0)) return (x != x) ? x : 0.0;  // NaN stays NaN; underflow to 0
-  if (x > 709.8) return INFINITY;
-  const double k = rint(x * t[16]);
-  const double r = fma(-k, t[15], fma(-k, t[14], x));
-  double p = t[13];
-#pragma unroll
-  for (int i = 12; i >= 0; --i) p = fma(p, r, t[i]);
-  return ldexp(p, (int)k);
+  // the table in two groups, each requested before its first use: two LDS
+  // round trips instead of one per coefficient, few registers held at once
+  const double2* t2 = (const double2*)t;
+  const double2 c7 = t2[7], c6 = t2[6], c5 = t2[5], c4 = t2[4];
+  const double inv_ln2 = t[16];
+  asm volatile("" ::"v"(c7.x), "v"(c7.y), "v"(c6.x), "v"(c6.y), "v"(c5.x), "v"(c5.y), "v"(c4.x),
+               "v"(c4.y), "v"(inv_ln2));
+  const bool tiny = !(x > -746.0);  // also NaN
+  const bool huge = x > 709.8;
+  const double xs = (tiny || huge) ? 0.0 : x;
+  const double k = rint(xs * inv_ln2);
+  const double r = fma(-k, c7.y, fma(-k, c7.x, xs));
+  const double2 c3 = t2[3], c2 = t2[2], c1 = t2[1], c0 = t2[0];
+  double p = c6.y;  // 1/13!
+  p = fma(p, r, c6.x);
+  p = fma(p, r, c5.y);
+  p = fma(p, r, c5.x);
+  p = fma(p, r, c4.y);
+  p = fma(p, r, c4.x);
+  asm volatile("" ::"v"(c3.x), "v"(c3.y), "v"(c2.x), "v"(c2.y), "v"(c1.x), "v"(c1.y), "v"(c0.x),
+               "v"(c0.y));
+  p = fma(p, r, c3.y);
+  p = fma(p, r, c3.x);
+  p = fma(p, r, c2.y);
+  p = fma(p, r, c2.x);
+  p = fma(p, r, c1.y);
+  p = fma(p, r, c1.x);
+  p = fma(p, r, c0.y);
+  p = fma(p, r, c0.x);
+  const double e = ldexp(p, (int)k);
+  return tiny ? ((x != x) ? x : 0.0) : (huge ? (double)INFINITY : e);
 }
 
 struct Shared {
@@ -253,19 +279,50 @@ struct Shared {
   int8_t codes[11264];
   alignas(16) unsigned char stage[STAGE];
   double redd[NW];
-  float redf[2 * NW];
+  alignas(16) float redf[2 * NW];
   float bestv[NW];
   int besti[NW];
   LayerW lt[2];        // weight table of layers l and l + 1 (slot l % 2)
   float aval[GU_ROWS * NW];  // this workgroup's SwiGLU values
-  double expc[17];     // exp_t table
+  alignas(16) double expc[17];  // exp_t table
   double rcos[D / 2];  // rotary table row of the position (attention workgroups)
   double rsin[D / 2];
+  float qpf;           // quantisation parameters handed from the computing waves
+  int qpz;
   int flag;
 };
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// Workgroup barrier that orders LDS only: every wave's LDS reads and writes
+// are complete, while its global loads (prefetched weights) stay in flight.
+// Data a wave copied into LDS by DMA is covered only once that wave has
+// waited for its own loads (vmcnt) before the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), no vmcnt wait
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Reduce the 16 per-wave partials that lanes 0..15 of the calling wave hold
+// (one DPP row), result in every lane.  All 64 lanes must be active.
+template <typename T, typename Op>
+__device__ __forceinline__ T reduce16(T v, Op op) {
+  static_assert(NW == 16, "one partial per lane of a DPP row");
+  v = op(v, dpp::mov<dpp::kXor1>(v));
+  v = op(v, dpp::mov<dpp::kXor2>(v));
+  v = op(v, dpp::mov<dpp::kHalfMirror>(v));
+  v = op(v, dpp::mov<dpp::kMirror>(v));
+  return dpp::lane_read(v, 0);
+}
+// Min and max of the 16 per-wave (min, max) pairs in red.
+__device__ __forceinline__ void minmax16(const float* red, int lane, float& lo, float& hi) {
+  const float2 m = ((const float2*)red)[lane & 15];
+  lo = reduce16(m.x, [](float a, float b) { return fminf(a, b); });
+  hi = reduce16(m.y, [](float a, float b) { return fmaxf(a, b); });
+}
 
 // ------------------------------------------------------------- waiting --
 // One wave: wait until words [c0, c1) of v carry the tag and copy them to
@@ -397,46 +454,76 @@ __device__ QParam prologue_plain(const unsigned char* stage, int n, Shared& sh, 
 
 // All waves: poll_all of an H-word vector whose wave chunks are 128 words,
 // then RMSNorm (fp64 inside) with gain sh.gain and the dynamic uint8
-// quantiser, each wave on its own chunk: the values go to x (fp32), the
-// shifted codes to sh.codes.  Three barriers in all.
+// quantiser: the values go to x (fp32), the shifted codes to sh.codes.
+// Waves 0..3 (one per SIMD) do the arithmetic, 512 elements each: the
+// wave-uniform part (sum, square root, division, quantisation parameters)
+// then runs once per SIMD instead of once per wave.  Four barriers.
+constexpr int NORM_WAVES = 4;
+constexpr int NORM_PER_LANE = H / (NORM_WAVES * 64);
 __device__ QParam poll_norm(const u64* v, int blk, float* x, Shared& sh, double eps, int lane,
                             int wave, int tid, uint32_t tag, uint32_t* err, u64* tr = nullptr,
-                            uint32_t* stat = nullptr) {
+                            uint32_t* stat = nullptr, u64* tn0 = nullptr, u64* tn1 = nullptr,
+                            u64* tn2 = nullptr) {
   static_assert(H == NW * 128, "one 128-word chunk per wave");
   const uint32_t r = poll_all(v, H, blk, sh.stage, err, lane, wave, tag, tr);
   if (stat && tid == 0) *stat = r;
+  lds_barrier();
   const u64* st = (const u64*)sh.stage;
-  const int i0 = wave * 128 + lane, i1 = i0 + 64;
-  const float v0 = __uint_as_float((uint32_t)st[i0]), v1 = __uint_as_float((uint32_t)st[i1]);
-  x[i0] = v0;
-  x[i1] = v1;
-  double ss = (double)v0 * (double)v0 + (double)v1 * (double)v1;
-  ss = wave_sum(ss);
-  if (lane == 0) sh.redd[wave] = ss;
-  __syncthreads();
-  ss = 0.0;
+  const bool mine = wave < NORM_WAVES;
+  const int i0 = wave * (H / NORM_WAVES) + lane;  // element i0 + 64 k
+  float xv[NORM_PER_LANE];
+  if (mine) {
+    double ss = 0.0;
 #pragma unroll
-  for (int k = 0; k < NW; ++k) ss += sh.redd[k];
-  const double rs = 1.0 / sqrt(ss / (double)H + eps);
-  const float h0 = (float)(((double)v0 * rs) * (double)sh.gain[i0]);
-  const float h1 = (float)(((double)v1 * rs) * (double)sh.gain[i1]);
-  float lo = wave_min(fminf(h0, h1)), hi = wave_max(fmaxf(h0, h1));
-  if (lane == 0) {
-    sh.redf[2 * wave] = lo;
-    sh.redf[2 * wave + 1] = hi;
+    for (int k = 0; k < NORM_PER_LANE; ++k) {
+      xv[k] = __uint_as_float((uint32_t)st[i0 + 64 * k]);
+      x[i0 + 64 * k] = xv[k];
+      ss += (double)xv[k] * (double)xv[k];
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) sh.redd[wave] = ss;
   }
-  __syncthreads();
-  lo = sh.redf[0];
-  hi = sh.redf[1];
+  lds_barrier();
+  if (tid == 0) stamp(tn0, 0, 0);
+  float hv[NORM_PER_LANE];
+  if (mine) {
+    const double ss = ((sh.redd[0] + sh.redd[1]) + sh.redd[2]) + sh.redd[3];
+    const double rs = 1.0 / sqrt(ss / (double)H + eps);
+    float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
-  for (int k = 1; k < NW; ++k) {
-    lo = fminf(lo, sh.redf[2 * k]);
-    hi = fmaxf(hi, sh.redf[2 * k + 1]);
+    for (int k = 0; k < NORM_PER_LANE; ++k) {
+      hv[k] = (float)(((double)xv[k] * rs) * (double)sh.gain[i0 + 64 * k]);
+      lo = fminf(lo, hv[k]);
+      hi = fmaxf(hi, hv[k]);
+    }
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    if (lane == 0) {
+      sh.redf[2 * wave] = lo;
+      sh.redf[2 * wave + 1] = hi;
+    }
   }
-  const QParam p = quant_param(lo, hi);
-  sh.codes[i0] = shift_code(quant_code(h0, p));
-  sh.codes[i1] = shift_code(quant_code(h1, p));
-  __syncthreads();
+  lds_barrier();
+  if (tid == 0) stamp(tn1, 0, 0);
+  QParam p;
+  if (mine) {
+    const float4 m0 = *(const float4*)sh.redf, m1 = *(const float4*)(sh.redf + 4);
+    const float lo = fminf(fminf(m0.x, m0.z), fminf(m1.x, m1.z));
+    const float hi = fmaxf(fmaxf(m0.y, m0.w), fmaxf(m1.y, m1.w));
+    p = quant_param(lo, hi);
+#pragma unroll
+    for (int k = 0; k < NORM_PER_LANE; ++k) sh.codes[i0 + 64 * k] = shift_code(quant_code(hv[k], p));
+    if (wave == 0 && lane == 0) {
+      sh.qpf = p.s;
+      sh.qpz = p.z;
+    }
+  }
+  lds_barrier();
+  if (tid == 0) stamp(tn2, 0, 0);
+  if (!mine) {
+    p.s = sh.qpf;
+    p.z = sh.qpz;
+  }
   return p;
 }
 
@@ -448,8 +535,9 @@ __device__ QParam poll_quant(const u64* v, int n, int blk, Shared& sh, int lane,
                              uint32_t tag, uint32_t* err, u64* tr = nullptr,
                              const u64* flags = nullptr, uint32_t* stat = nullptr, int np = NW,
                              bool pairs = false) {
+  const int tid = wave * 64 + lane;
   const uint32_t r = poll_all(v, n, blk, sh.stage, err, lane, wave, tag, tr, flags, np);
-  if (stat && threadIdx.x == 0) *stat = r;
+  if (stat && tid == 0) *stat = r;
   const u64* st = (const u64*)sh.stage;
   float lo = INFINITY, hi = -INFINITY;
   int c0, c1, step;
@@ -459,8 +547,8 @@ __device__ QParam poll_quant(const u64* v, int n, int blk, Shared& sh, int lane,
     c1 = min(n, wave * chunk + chunk);
     step = 64;
   } else {  // the vector is complete once every poller is past the barrier
-    __syncthreads();
-    c0 = threadIdx.x;
+    lds_barrier();
+    c0 = tid;
     c1 = n;
     step = NT;
   }
@@ -476,19 +564,13 @@ __device__ QParam poll_quant(const u64* v, int n, int blk, Shared& sh, int lane,
     sh.redf[2 * wave] = lo;
     sh.redf[2 * wave + 1] = hi;
   }
-  __syncthreads();
-  lo = sh.redf[0];
-  hi = sh.redf[1];
-#pragma unroll
-  for (int k = 1; k < NW; ++k) {
-    lo = fminf(lo, sh.redf[2 * k]);
-    hi = fmaxf(hi, sh.redf[2 * k + 1]);
-  }
+  lds_barrier();
+  minmax16(sh.redf, lane, lo, hi);
   const QParam p = quant_param(lo, hi);
   if (pairs) return p;  // the quantisation parameters only
   for (int i = c0; i < c1; i += step)
     sh.codes[i] = shift_code(quant_code(__uint_as_float((uint32_t)st[i]), p));
-  __syncthreads();
+  lds_barrier();
   return p;
 }
 
@@ -504,7 +586,7 @@ __device__ void poll_codes(const u64* v, int n, int blk, Shared& sh, int lane, i
     const u64* st = (const u64*)sh.stage;
     for (int i = wave * chunk + lane; i < c1; i += 64) ((uint32_t*)sh.codes)[i] = (uint32_t)st[i];
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // ------------------------------------------------------ weight streams --
@@ -592,27 +674,28 @@ __device__ __forceinline__ void run_units(i32x4 (&buf)[W], Addr addr, Use use) {
 }
 
 // ---------------------------------------------------------- attention --
-// Work item (KV head g, item sp < 8): the live 64-key chunks sp, sp+8, ...
-// (chunks holding a key at or before the position) for the 8 query heads of
-// g, combined with the online-softmax update.  With one item per head the
-// item finishes the softmax itself.  Otherwise items 1.. publish their
-// partial softmax state per head (running max, sum and weighted values,
-// fp64 as two tagged 32-bit halves) and item 0 waits for them, merges and
-// publishes the output.
-//
-// LDS, after the 16 KiB that stage the layer input: keys and values of the
-// chunk as pairs of rows 1040 bytes apart (key k at float offset kv_row(k)),
-// so a score thread's 16-byte reads of its key row, 8 consecutive pairs at a
-// time, cover all 32 banks; then the q|k|v words, rotated q and k, v, the
-// softmax weights and per-head max/sum.
+// Work items: (KV head g, head group hh of 4 query heads, item sp < 4) on
+// workgroup 8 g + 4 hh + sp.  With nchunk live 64-key chunks (those holding
+// a key at or before the position) each (g, hh) uses nitem = min(4,
+// ceil(nchunk / 2)) items, item sp taking chunks sp, sp + nitem, ...; so up
+// to 127 rows are attended without a merge between workgroups.
+constexpr int ATT_RED = 0;                             // fp64 partial sums, 16 KiB
 constexpr int ATT_KV = 16 * 1024;                      // byte offset in stage
 constexpr int ATT_QKV = ATT_KV + 2 * (KEYS / 2) * 260 * 4;
-constexpr int ATT_Q = ATT_QKV + 10 * 1024;
-constexpr int ATT_END = ATT_Q + (G + 2) * D * 4 + G * KEYS * 8 + 2 * G * 8;
+constexpr int ATT_Q = ATT_QKV + 10 * 1024;             // rotated q, fp64 [HPI][D]
+constexpr int ATT_KR = ATT_Q + HPI * D * 8;            // rotated k and v, fp32 [D] each
+constexpr int ATT_P = ATT_KR + 2 * D * 4;              // softmax weights, fp64 [KEYS][HPI]
+constexpr int ATT_HM = ATT_P + HPI * KEYS * 8;         // per-head max and sum, fp64
+constexpr int ATT_END = ATT_HM + HPI * 2 * 8;
+constexpr int SC_SLICES = 8;                           // score waves: 16 dims each
+constexpr int PV_SLICES = 4;                           // P V key slices: 16 keys each
 constexpr int PSTATE = 2 * PART;                       // words per (item, head)
 constexpr int MERGE_BATCH = 4;                         // items merged per pass
 static_assert(ATT_END <= STAGE, "attention staging exceeds LDS stage");  // the down units are loaded after it
-static_assert(ATT_KV + MERGE_BATCH * G * PSTATE * 8 + 1024 <= ATT_Q, "merge batch too large");
+static_assert(SC_SLICES * HPI * KEYS * 8 <= ATT_KV && PV_SLICES * HPI * D * 8 <= ATT_KV,
+              "partial sums exceed their region");
+static_assert(MERGE_BATCH * HPI * PSTATE * 8 + 1024 <= ATT_QKV - ATT_KV, "merge batch too large");
+static_assert(SC_SLICES * 16 == D && PV_SLICES * 16 == KEYS && HPI * D <= NT, "attention split");
 
 __device__ __forceinline__ int kv_row(int k) { return (k >> 1) * 260 + (k & 1) * D; }
 
@@ -660,123 +743,209 @@ __device__ __forceinline__ void softmax_merge(double& M, double& L, double& O, d
   M = Mn;
 }
 
-__device__ void attention_item(const MegaArgs& A, uint32_t epoch, int l, int item, int nitem,
-                               int nchunk, Shared& sh, u64* xl, int tid, int lane, int wave) {
-  const int g = item / NI, sp = item % NI;
+// One attention item: query heads h0 .. h0 + 3 of KV head g (h0 = 8 g + 4 hh)
+// over the chunks c = sp, sp + nitem, ... of the cache, folded with the
+// online-softmax update; fp64 inside (the products of two fp32 values are
+// exact in fp64).  Every step spreads over the waves so that no SIMD
+// repeats wave-uniform work: scores as 8 slices of 16 dims (lane = key, all
+// four heads per lane, so each key value is widened once), partial sums
+// through LDS, the softmax of head h on wave h, the weighted values as 4
+// slices of 16 keys x 2 halves of the dims (lane = dim), partial sums
+// through LDS, and thread (h, d) < 512 keeps the running state of output
+// (h, d).  With more than one item, items sp > 0 publish their states (fp64
+// as two tagged 32-bit halves) and item 0 waits for them, merges and
+// publishes the output.
+//
+// LDS (stage offsets): partial sums [0, 16K); keys and values of the chunk
+// as pairs of rows 1040 bytes apart (key k at float offset kv_row(k)); the
+// q|k|v words; rotated q (fp64), k and v; the softmax weights; per-head
+// max and sum.
+__device__ void attention_item(const MegaArgs& A, uint32_t epoch, int l, int g, int hh, int sp,
+                               int nitem, int nchunk, Shared& sh, u64* xl, u64* tr, int tid,
+                               int lane, int wave) {
   const int p = A.pos;
   float* Ks = (float*)(sh.stage + ATT_KV);
   float* Vs = Ks + (KEYS / 2) * 260;
-  unsigned char* qst = sh.stage + ATT_QKV;           // q|k|v words (10 KiB)
-  float* qr = (float*)(sh.stage + ATT_Q);            // rotated q [8][128]
-  float* kr = qr + G * D;                            // rotated k [128]
-  float* vv = kr + D;                                // v [128]
-  double* ps = (double*)(vv + D);                    // weights [8][64]
-  double* hm = ps + G * KEYS;                        // per-head max and sum [8][2]
-  u64* tr = trace_sub(A, item, l, 22);
+  unsigned char* qst = sh.stage + ATT_QKV;
+  double* qd = (double*)(sh.stage + ATT_Q);
+  float* kr = (float*)(sh.stage + ATT_KR);
+  float* vv = kr + D;
+  double* pw = (double*)(sh.stage + ATT_P);
+  double* hm = (double*)(sh.stage + ATT_HM);
+  double* red = (double*)(sh.stage + ATT_RED);
+  const int h0 = g * G + hh * HPI;
 
-  // q of heads 8g..8g+7 (waves 0..7), k and v of head g (waves 8, 9)
-  if (wave < G + 2) {
-    const int n0 = wave < G ? (g * G + wave) * D : (wave == G ? Q + g * D : Q + KVD + g * D);
+  // q of heads h0..h0+3 (waves 0..3), k and v of KV head g (waves 4, 5)
+  if (wave < HPI + 2) {
+    const int n0 = wave < HPI ? (h0 + wave) * D : (wave == HPI ? Q + g * D : Q + KVD + g * D);
     poll_range(xl + OFF_QKV, n0, n0 + D, R_QKV, qst + wave * D * 8, A.err, lane, epoch);
   }
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's cache rows of the first chunk
-  if (wave == 0) stamp(tr, 0, lane);
-  __syncthreads();
-  // rotary embedding (fp64) of q and k at position p; v as is
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the first chunk's rows
+  lds_barrier();
+  if (tid == 0) stamp(tr, 0, lane);
+  // rotary embedding (fp64) at position p, rounded to fp32; q kept widened
   {
     const u64* s = (const u64*)qst;
     const double* cs = sh.rcos;
     const double* sn = sh.rsin;
-    for (int t = tid; t < (G + 1) * (D / 2); t += NT) {
+    for (int t = tid; t < (HPI + 1) * (D / 2); t += NT) {
       const int head = t / (D / 2), j = t % (D / 2);
       const double x1 = __uint_as_float((uint32_t)s[head * D + j]);
       const double x2 = __uint_as_float((uint32_t)s[head * D + j + D / 2]);
       const double c = cs[j], sv = sn[j];
-      float* dst = head < G ? qr + head * D : kr;
-      dst[j] = (float)(x1 * c - x2 * sv);
-      dst[j + D / 2] = (float)(x2 * c + x1 * sv);
+      const float r1 = (float)(x1 * c - x2 * sv);
+      const float r2 = (float)(x2 * c + x1 * sv);
+      if (head < HPI) {
+        qd[head * D + j] = r1;
+        qd[head * D + j + D / 2] = r2;
+      } else {
+        kr[j] = r1;
+        kr[j + D / 2] = r2;
+      }
     }
-    for (int t = tid; t < D; t += NT) vv[t] = __uint_as_float((uint32_t)s[(G + 1) * D + t]);
+    for (int t = tid; t < D; t += NT) vv[t] = __uint_as_float((uint32_t)s[(HPI + 1) * D + t]);
   }
-  __syncthreads();
-  // item 0 publishes the deltas
-  if (sp == 0) {
+  lds_barrier();
+  // the first item of head group 0 publishes the deltas (stores left in flight)
+  if (hh == 0 && sp == 0)
     for (int t = tid; t < D; t += NT) {
       A.kdelta[(size_t)l * KVD + g * D + t] = kr[t];
       A.vdelta[(size_t)l * KVD + g * D + t] = vv[t];
     }
-  }
-  const int hv = wave >> 1, dv = (wave & 1) * 64 + lane;  // PV thread -> (head, dim)
+  const bool mine = tid < HPI * D;
+  const int oh = tid >> 7, od = tid & (D - 1);  // output (head, dim) of a state thread
   double M = -INFINITY, Lsum = 0.0, O = 0.0;
-  for (int c = sp; c < nchunk; c += NI) {
+  for (int c = sp; c < nchunk; c += nitem) {
     const int j0 = c * KEYS;
+    const int nk = min(KEYS, p + 1 - j0);  // keys at or before the position
     if (c != sp) {
-      __syncthreads();  // the previous chunk's values and weights are used
+      lds_barrier();  // the previous chunk's values and partial sums are used
       load_kv(A, l, g, j0, sh, wave, lane);
       __builtin_amdgcn_s_waitcnt(0);
+      lds_barrier();
     }
-    __syncthreads();
     // this call's row replaces cache row p
     if (p >= j0 && p < j0 + KEYS)
       for (int t = tid; t < D; t += NT) {
         Ks[kv_row(p - j0) + t] = kr[t];
         Vs[kv_row(p - j0) + t] = vv[t];
       }
-    __syncthreads();
+    lds_barrier();
     if (tid == 0) stamp(tr, 1, lane);
-    // scores on waves 0..7: thread -> (head = wave, key jj); keys after the
-    // position are selected away (weight exactly 0, row never read)
-    if (wave < G) {
-      const int hh = wave, jj = 2 * (lane & 31) + (lane >> 5), j = j0 + jj;
-      double sc = -INFINITY;
-      if (j <= p) {
-        const float4* qh = (const float4*)(qr + hh * D);
-        const float4* kj = (const float4*)(Ks + kv_row(jj));
-        double d0 = 0.0, d1 = 0.0;
-#pragma unroll 4
-        for (int d = 0; d < D / 4; ++d) {
-          const float4 qv = qh[d], kv = kj[d];
-          d0 = fma((double)qv.x, (double)kv.x, d0);
-          d1 = fma((double)qv.y, (double)kv.y, d1);
-          d0 = fma((double)qv.z, (double)kv.z, d0);
-          d1 = fma((double)qv.w, (double)kv.w, d1);
+    // scores, partial over dims [16 w, 16 w + 16) on waves 0..7, lane = key;
+    // keys past the position are selected away below (their rows are stale)
+    if (wave < SC_SLICES) {
+      const float4* kp = (const float4*)(Ks + kv_row(lane) + 16 * wave);
+      double acc[HPI];
+#pragma unroll
+      for (int h = 0; h < HPI; ++h) acc[h] = 0.0;
+#pragma unroll
+      for (int d4 = 0; d4 < 4; ++d4) {
+        // the group's key and q values are all requested before the first use
+        const float4 kv = kp[d4];
+        double2 qa[HPI], qb[HPI];
+#pragma unroll
+        for (int h = 0; h < HPI; ++h) {
+          const double2* qh = (const double2*)(qd + h * D + 16 * wave + 4 * d4);
+          qa[h] = qh[0];
+          qb[h] = qh[1];
         }
-        sc = (d0 + d1) / sqrt((double)D);
+        asm volatile("" ::"v"(kv.x), "v"(qa[0].x), "v"(qa[1].x), "v"(qa[2].x), "v"(qa[3].x),
+                     "v"(qb[0].x), "v"(qb[1].x), "v"(qb[2].x), "v"(qb[3].x));
+        const double k0 = kv.x, k1 = kv.y, k2 = kv.z, k3 = kv.w;
+#pragma unroll
+        for (int h = 0; h < HPI; ++h) {
+          acc[h] = fma(qa[h].x, k0, acc[h]);
+          acc[h] = fma(qa[h].y, k1, acc[h]);
+          acc[h] = fma(qb[h].x, k2, acc[h]);
+          acc[h] = fma(qb[h].y, k3, acc[h]);
+        }
       }
+#pragma unroll
+      for (int h = 0; h < HPI; ++h) red[(wave * HPI + h) * KEYS + lane] = acc[h];
+    }
+    lds_barrier();
+    // softmax of head h on wave h, lane = key
+    if (wave < HPI) {
+      double sc = 0.0;
+#pragma unroll
+      for (int s = 0; s < SC_SLICES; ++s) sc += red[(s * HPI + wave) * KEYS + lane];
+      sc = lane < nk ? sc / sqrt((double)D) : -INFINITY;
       const double m = wave_max(sc);
-      const double e = (sc == -INFINITY) ? 0.0 : exp_t(sc - m, sh.expc);
-      const double lsum = wave_sum(e);
-      ps[hh * KEYS + jj] = e;
+      const double e = lane < nk ? exp_t(sc - m, sh.expc) : 0.0;
+      const double ls = wave_sum(e);
+      pw[lane * HPI + wave] = e;
       if (lane == 0) {
-        hm[2 * hh] = m;
-        hm[2 * hh + 1] = lsum;
+        hm[2 * wave] = m;
+        hm[2 * wave + 1] = ls;
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (tid == 0) stamp(tr, 2, lane);
-    // weighted values of the chunk, folded into the running state
-    const int nk = min(KEYS, p + 1 - j0);
-    double o0 = 0.0, o1 = 0.0;
-    int k = 0;
-    for (; k + 1 < nk; k += 2) {
-      o0 = fma(ps[hv * KEYS + k], (double)Vs[kv_row(k) + dv], o0);
-      o1 = fma(ps[hv * KEYS + k + 1], (double)Vs[kv_row(k + 1) + dv], o1);
+    // weighted values, partial over keys [16 ks, 16 ks + 16) on waves 0..7:
+    // lane = dim within half (w & 1), all four heads per lane
+    if (wave < 2 * PV_SLICES) {
+      const int d = 64 * (wave & 1) + lane, ks = wave >> 1;
+      double acc[HPI];
+#pragma unroll
+      for (int h = 0; h < HPI; ++h) acc[h] = 0.0;
+      // keys past the position have weight 0 but stale rows: skipped, in
+      // groups of 4 whose loads are all requested before the first use
+      for (int k4 = 16 * ks; k4 < min(nk, 16 * ks + 16); k4 += 4) {
+        float vf[4];
+        double2 pa[4], pb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int k = min(k4 + i, nk - 1);  // a key past the end repeats one with weight use below
+          vf[i] = Vs[kv_row(k) + d];
+          pa[i] = *(const double2*)(pw + k * HPI);
+          pb[i] = *(const double2*)(pw + k * HPI + 2);
+        }
+        asm volatile("" ::"v"(vf[0]), "v"(vf[1]), "v"(vf[2]), "v"(vf[3]), "v"(pa[0].x), "v"(pa[1].x),
+                     "v"(pa[2].x), "v"(pa[3].x), "v"(pb[0].x), "v"(pb[1].x), "v"(pb[2].x), "v"(pb[3].x));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (k4 + i < nk) {
+            const double v = vf[i];
+            acc[0] = fma(pa[i].x, v, acc[0]);
+            acc[1] = fma(pa[i].y, v, acc[1]);
+            acc[2] = fma(pb[i].x, v, acc[2]);
+            acc[3] = fma(pb[i].y, v, acc[3]);
+          }
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < HPI; ++h) red[(ks * HPI + h) * D + d] = acc[h];
     }
-    if (k < nk) o0 = fma(ps[hv * KEYS + k], (double)Vs[kv_row(k) + dv], o0);
-    softmax_merge(M, Lsum, O, hm[2 * hv], hm[2 * hv + 1], o0 + o1, sh.expc);
+    lds_barrier();
+    // fold the chunk into the running state of output (h, d)
+    if (mine) {
+      double o = 0.0;
+#pragma unroll
+      for (int s = 0; s < PV_SLICES; ++s) o += red[(s * HPI + oh) * D + od];
+      if (c == sp) {  // the merge into the empty state, written out
+        M = hm[2 * oh];
+        Lsum = hm[2 * oh + 1];
+        O = o;
+      } else {
+        softmax_merge(M, Lsum, O, hm[2 * oh], hm[2 * oh + 1], o, sh.expc);
+      }
+    }
   }
   if (nitem == 1) {
-    xput_rep(xl + OFF_ATT, Q, (g * G + hv) * D + dv, (float)(O / Lsum), epoch);
+    if (mine) xput_rep(xl + OFF_ATT, Q, (h0 + oh) * D + od, (float)(O / Lsum), epoch);
     return;
   }
-  u64* part = A.part + ((size_t)l * NKV + g) * NI * G * PSTATE;  // item 0's slot unused
+  u64* part = A.part + (((size_t)l * NKV + g) * HH + hh) * NIH * HPI * PSTATE;  // item 0's slot unused
   if (sp > 0) {
-    u64* pst = part + ((size_t)sp * G + hv) * PSTATE;
-    if (dv == 0) {
-      put_tagged_f64(pst, M, epoch);
-      put_tagged_f64(pst + 2, Lsum, epoch);
+    if (mine) {
+      u64* pst = part + ((size_t)sp * HPI + oh) * PSTATE;
+      if (od == 0) {
+        put_tagged_f64(pst, M, epoch);
+        put_tagged_f64(pst + 2, Lsum, epoch);
+      }
+      put_tagged_f64(pst + 4 + 2 * od, O, epoch);
     }
-    put_tagged_f64(pst + 4 + 2 * dv, O, epoch);
     return;
   }
   if (tid == 0) stamp(tr, 3, lane);
@@ -784,22 +953,24 @@ __device__ void attention_item(const MegaArgs& A, uint32_t epoch, int l, int ite
   const u64* pb = (const u64*)(sh.stage + ATT_KV);
   for (int s0 = 1; s0 < nitem; s0 += MERGE_BATCH) {
     const int ns = min(MERGE_BATCH, nitem - s0);
-    const int n = ns * G * PSTATE;
+    const int n = ns * HPI * PSTATE;
     const int chunk = ((n + NW - 1) / NW + 127) & ~127;
     const int c0 = wave * chunk, c1 = min(n, c0 + chunk);
-    __syncthreads();  // the chunk's values (or the previous batch) are used
+    lds_barrier();  // the chunk's values (or the previous batch) are used
     if (c0 < c1)
-      poll_range(part + (size_t)s0 * G * PSTATE, c0, c1, G * PSTATE, sh.stage + ATT_KV + c0 * 8,
-                 A.err, lane, epoch);
-    __syncthreads();
-    for (int s = 0; s < ns; ++s) {
-      const u64* q = pb + ((size_t)s * G + hv) * PSTATE;
-      softmax_merge(M, Lsum, O, get_tagged_f64(q), get_tagged_f64(q + 2),
-                    get_tagged_f64(q + 4 + 2 * dv), sh.expc);
-    }
+      poll_range(part + (size_t)s0 * HPI * PSTATE, c0, c1, HPI * PSTATE,
+                 sh.stage + ATT_KV + c0 * 8, A.err, lane, epoch);
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();
+    if (mine)
+      for (int s = 0; s < ns; ++s) {
+        const u64* q = pb + ((size_t)s * HPI + oh) * PSTATE;
+        softmax_merge(M, Lsum, O, get_tagged_f64(q), get_tagged_f64(q + 2),
+                      get_tagged_f64(q + 4 + 2 * od), sh.expc);
+      }
   }
   if (tid == 0) stamp(tr, 4, lane);
-  xput_rep(xl + OFF_ATT, Q, (g * G + hv) * D + dv, (float)(O / Lsum), epoch);
+  if (mine) xput_rep(xl + OFF_ATT, Q, (h0 + oh) * D + od, (float)(O / Lsum), epoch);
 }
 
 // ------------------------------------------------------------ the kernel --
@@ -815,14 +986,14 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
   int lane16 = lane * 16;
   int s = wave;
 
-  // attention items: (KV head g, item sp < NI) on workgroup g * NI + sp when
-  // chunk sp holds a key at or before the position
+  // attention items (see attention_item): workgroup w < NATT holds item
+  // sp = w % NIH of head group hh = (w / NIH) % HH of KV head g = w / (NIH HH)
   const int nchunk = A.pos / KEYS + 1;
-  const int nitem = min(NI, nchunk);
-  const bool att = w < NKV * NI && (w % NI) < nitem;
+  const int nitem = min(NIH, (nchunk + 1) / 2);
+  const bool att = w < NATT && (w % NIH) < nitem;
   // gate/up rows: rg per workgroup without attention work, by rank
-  const int natt = NKV * nitem;
-  const int rank = w - (w >= NKV * NI ? natt : (w / NI) * nitem + min(w % NI, nitem));
+  const int natt = NKV * HH * nitem;
+  const int rank = w - (w >= NATT ? natt : (w / NIH) * nitem + min(w % NIH, nitem));
   const int rg = ((I + (NWG - natt) - 1) / (NWG - natt) + 3) & ~3;  // whole code words
   const int nprod = (I + rg - 1) / rg;                                  // ranks with rows
   const int gu0 = att ? 0 : rank * rg;
@@ -948,10 +1119,11 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
 
     // ---- q, k, v
     trace_at(A, w, l, 0);
-    if (att) load_kv(A, l, w / NI, (w % NI) * KEYS, sh, wave, lane);
+    if (att) load_kv(A, l, w / (NIH * HH), (w % NIH) * KEYS, sh, wave, lane);
     load_gain(Lw.ln1, sh.gain, wave, lane16);
     QParam qp = poll_norm(xl + OFF_X0 + rep * H, R_D, sh.xs, sh, A.eps, lane, wave, tid, epoch,
-                          A.err, trace_sub(A, w, l, 27), trace_stat(A, w, l, 11));
+                          A.err, trace_sub(A, w, l, 27), trace_stat(A, w, l, 11),
+                          trace_sub(A, w, l, 11), trace_sub(A, w, l, 12), trace_sub(A, w, l, 13));
     trace_at(A, w, l, 2);
     {
       int accs[1];
@@ -967,9 +1139,10 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
     // ---- attention; the other workgroups stream the o rows and their
     // gate/up rows meanwhile
     if (att) {
-      __syncthreads();
-      attention_item(A, epoch, l, w, nitem, nchunk, sh, xl, tid, lane, wave);
-      __syncthreads();
+      lds_barrier();  // the codes are used (the stores of the q|k|v rows stay in flight)
+      attention_item(A, epoch, l, w / (NIH * HH), (w / NIH) % HH, w % NIH, nitem, nchunk, sh, xl,
+                     trace_sub(A, w, l, 22), tid, lane, wave);
+      lds_barrier();  // the staging area is free again
       issue_o(l);
       issue_down_lds(l);
     } else {
@@ -981,7 +1154,7 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
     // ---- o projection + residual
     asm volatile("" : "+v"(lane16), "+v"(tid), "+v"(lane));
     trace_at(A, w, l, 4);
-    qp = poll_quant(xl + OFF_ATT + rep * Q, Q, G * D, sh, lane, wave, epoch, A.err, nullptr, nullptr,
+    qp = poll_quant(xl + OFF_ATT + rep * Q, Q, HPI * D, sh, lane, wave, epoch, A.err, nullptr, nullptr,
                     trace_stat(A, w, l, 12));
     trace_at(A, w, l, 5);
     {
@@ -1001,7 +1174,8 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
     asm volatile("" : "+v"(lane16), "+v"(tid), "+v"(lane));
     load_gain(Lw.ln2, sh.gain, wave, lane16);
     qp = poll_norm(xl + OFF_X1 + rep * H, R_O, sh.x1s, sh, A.eps, lane, wave, tid, epoch, A.err,
-                   trace_sub(A, w, l, 16), trace_stat(A, w, l, 13));
+                   trace_sub(A, w, l, 16), trace_stat(A, w, l, 13), trace_sub(A, w, l, 14),
+                   trace_sub(A, w, l, 15), trace_sub(A, w, l, 30));
     trace_at(A, w, l, 7);
     if (!att) {
       const int zc = 128 - qp.z;
@@ -1027,37 +1201,43 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
         aggs[k] = wave_sum(aggs[k]);
         aus[k] = wave_sum(aus[k]);
       }
-      float lo = INFINITY, hi = -INFINITY;
+      // SwiGLU of row s + 16 k on lane k (the rows' exponentials side by side)
+      int ag = aggs[0], au = aus[0], cgk = cg[0], cuk = cu[0];
+      float sgk = sg[0], suk = su[0];
 #pragma unroll
-      for (int k = 0; k < GU_ROWS; ++k) {
-        const int i = s + NW * k;
-        if (lane == 0 && i < ngu) {
-          const float gv = dequant(aggs[k] + zc * cg[k], qp.s, sg[k]);
-          const float uv = dequant(aus[k] + zc * cu[k], qp.s, su[k]);
-          const double gd = gv;
-          const float a = (float)(gd / (1.0 + exp_t(-gd, sh.expc)) * (double)uv);
-          sh.aval[i] = a;
-          lo = fminf(lo, a);
-          hi = fmaxf(hi, a);
+      for (int k = 1; k < GU_ROWS; ++k)
+        if (lane == k) {
+          ag = aggs[k];
+          au = aus[k];
+          cgk = cg[k];
+          cuk = cu[k];
+          sgk = sg[k];
+          suk = su[k];
         }
-      }
+      const int i = s + NW * lane;
+      const bool live = lane < GU_ROWS && i < ngu;
+      const float gv = dequant(ag + zc * cgk, qp.s, sgk);
+      const float uv = dequant(au + zc * cuk, qp.s, suk);
+      const double gd = gv;
+      const float a = (float)(gd / (1.0 + exp_t(-gd, sh.expc)) * (double)uv);
+      if (live) sh.aval[i] = a;
+      float lo = live ? a : INFINITY, hi = live ? a : -INFINITY;
+      lo = fminf(lo, fminf(dpp::mov<dpp::kXor1>(lo), dpp::mov<dpp::kXor2>(lo)));
+      hi = fmaxf(hi, fmaxf(dpp::mov<dpp::kXor1>(hi), dpp::mov<dpp::kXor2>(hi)));
       if (lane == 0) {
         sh.redf[2 * s] = lo;
         sh.redf[2 * s + 1] = hi;
       }
       trace_done(A, w, l, 8, lane);
-      __syncthreads();
-      // round 1: this workgroup's min and max
-      if (tid < NREP && rank < nprod) {
-        lo = sh.redf[0];
-        hi = sh.redf[1];
-        for (int k = 1; k < NW; ++k) {
-          lo = fminf(lo, sh.redf[2 * k]);
-          hi = fmaxf(hi, sh.redf[2 * k + 1]);
+      lds_barrier();  // the down units bound for LDS may still be in flight
+      // round 1: this workgroup's min and max, one replica per lane
+      if (wave == 0 && rank < nprod) {
+        minmax16(sh.redf, lane, lo, hi);
+        if (lane < NREP) {
+          u64* mm = xl + OFF_AMM + lane * 2 * NWG + 2 * rank;
+          xput(mm, lo, epoch);
+          xput(mm + 1, hi, epoch);
         }
-        u64* mm = xl + OFF_AMM + tid * 2 * NWG + 2 * rank;
-        xput(mm, lo, epoch);
-        xput(mm + 1, hi, epoch);
       }
       issue_down(l);
     }
@@ -1276,7 +1456,7 @@ static size_t mega_xch_words(int L) {
 
 size_t decode_mega_ws_bytes(int L, int T) {
   const size_t xch = mega_xch_words(L) * 8;
-  const size_t part = (size_t)L * mk::NKV * mk::NI * mk::G * mk::PSTATE * 8;
+  const size_t part = (size_t)L * mk::NKV * mk::HH * mk::NIH * mk::HPI * mk::PSTATE * 8;
   const size_t ctr = (size_t)(2 * L + 64) * 4;
   const size_t amax = (size_t)mk::NWG * 8;
   const size_t table = (size_t)L * sizeof(mk::LayerW);
@@ -1311,7 +1491,7 @@ static MegaLayout mega_layout(void* ws, int L, int T) {
   m.xch = (mk::u64*)p;
   p += al(mega_xch_words(L) * 8);
   m.part = (mk::u64*)p;
-  p += al((size_t)L * mk::NKV * mk::NI * mk::G * mk::PSTATE * 8);
+  p += al((size_t)L * mk::NKV * mk::HH * mk::NIH * mk::HPI * mk::PSTATE * 8);
   m.ctr = (uint32_t*)p;
   m.err = m.ctr + 2 * L + 32;
   m.marker = (mk::u64*)(m.ctr + 2 * L + 48);
@@ -1348,7 +1528,7 @@ hipError_t decode_mega_launch(hipStream_t st, void* ws, const MegaStep& S, hipEv
                               hipEvent_t ev_end) {
   MegaLayout lay = mega_layout(ws, S.L, S.T);
   // the exchange words and the partial attention states that follow them
-  const size_t part_words = (size_t)S.L * mk::NKV * mk::NI * mk::G * mk::PSTATE;
+  const size_t part_words = (size_t)S.L * mk::NKV * mk::HH * mk::NIH * mk::HPI * mk::PSTATE;
   const size_t nwords = (size_t)(lay.part - lay.xch) + part_words;
   const mk::u64 marker = mk::MAGIC ^ (mk::u64)nwords ^ ((mk::u64)S.T << 40);
   hipLaunchKernelGGL(mk::k_decode_prep, dim3(mk::NWG), dim3(256), 0, st, lay.xch, nwords, lay.ctr,
