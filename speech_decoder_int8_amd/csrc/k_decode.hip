@@ -460,12 +460,16 @@ __device__ QParam prologue_plain(const unsigned char* stage, int n, Shared& sh, 
 // then runs once per SIMD instead of once per wave.  Four barriers.
 constexpr int NORM_WAVES = 4;
 constexpr int NORM_PER_LANE = H / (NORM_WAVES * 64);
+// `after_poll` runs in every wave once its share of the vector has arrived
+// (loads it issues then do not delay this wait).
+template <typename AfterPoll>
 __device__ QParam poll_norm(const u64* v, int blk, float* x, Shared& sh, double eps, int lane,
-                            int wave, int tid, uint32_t tag, uint32_t* err, u64* tr = nullptr,
-                            uint32_t* stat = nullptr, u64* tn0 = nullptr, u64* tn1 = nullptr,
-                            u64* tn2 = nullptr) {
+                            int wave, int tid, uint32_t tag, uint32_t* err, AfterPoll after_poll,
+                            u64* tr = nullptr, uint32_t* stat = nullptr, u64* tn0 = nullptr,
+                            u64* tn1 = nullptr, u64* tn2 = nullptr) {
   static_assert(H == NW * 128, "one 128-word chunk per wave");
   const uint32_t r = poll_all(v, H, blk, sh.stage, err, lane, wave, tag, tr);
+  after_poll();
   if (stat && tid == 0) *stat = r;
   lds_barrier();
   const u64* st = (const u64*)sh.stage;
@@ -572,6 +576,59 @@ __device__ QParam poll_quant(const u64* v, int n, int blk, Shared& sh, int lane,
     sh.codes[i] = shift_code(quant_code(__uint_as_float((uint32_t)st[i]), p));
   lds_barrier();
   return p;
+}
+
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+// All waves: wait for the (min, max) word pairs of all NWG workgroups in v
+// (workgroups without SwiGLU rows publish +inf, -inf) and reduce them to the
+// quantisation parameters (every wave gets them).  The words are read with
+// coherent scalar loads: they take the scalar path to memory, so this wait
+// does not queue behind the vector loads (weights) the workgroup has in
+// flight.  Wave w checks words [32 w, 32 w + 32) with four 64-byte loads per
+// round.  Bounded like poll_range.
+__device__ QParam poll_amm(const u64* v, Shared& sh, int lane, int wave, uint32_t tag,
+                           uint32_t* err, u64* tr = nullptr) {
+  static_assert(NW * 32 == 2 * NWG, "one 32-word slice per wave covers every workgroup");
+  if (wave == 0) stamp(tr, 0, lane);
+  i32x16 q[4];
+  uint32_t spins = 0;
+  for (;;) {
+    asm volatile(
+        "s_load_dwordx16 %0, %4, 0x0 glc\n\t"
+        "s_load_dwordx16 %1, %4, 0x40 glc\n\t"
+        "s_load_dwordx16 %2, %4, 0x80 glc\n\t"
+        "s_load_dwordx16 %3, %4, 0xc0 glc\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&s"(q[0]), "=&s"(q[1]), "=&s"(q[2]), "=&s"(q[3])
+        : "s"(v + wave * 32)
+        : "memory");
+    uint32_t bad = 0;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) bad |= (uint32_t)q[k / 8][2 * (k % 8) + 1] ^ tag;
+    if (bad == 0) break;
+    if (++spins > SPIN_LIMIT) {
+      if (lane == 0) atomicOr(err, 8u);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(4);  // ~0.1 us: 4096 polling waves would crowd the scalar path
+  }
+  // word 2 i is workgroup i's min, word 2 i + 1 its max
+  float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < 32; k += 2) {
+    lo = fminf(lo, __int_as_float(q[k / 8][2 * (k % 8)]));
+    hi = fmaxf(hi, __int_as_float(q[k / 8][2 * (k % 8) + 2]));
+  }
+  if (wave == 0) stamp(tr, 1, lane);
+  if (lane == 0) {
+    sh.redf[2 * wave] = lo;
+    sh.redf[2 * wave + 1] = hi;
+  }
+  lds_barrier();
+  if (wave == 0) stamp(tr, 2, lane);
+  minmax16(sh.redf, lane, lo, hi);
+  return quant_param(lo, hi);
 }
 
 // Waves below NPOLL: poll n words of packed codes (4 per word, producer
@@ -700,10 +757,11 @@ static_assert(SC_SLICES * 16 == D && PV_SLICES * 16 == KEYS && HPI * D <= NT, "a
 __device__ __forceinline__ int kv_row(int k) { return (k >> 1) * 260 + (k & 1) * D; }
 
 // All waves: start copying the live cache rows of KV head g in the chunk
-// starting at j0 into LDS (two keys per 1 KiB instruction, pairs spread over
-// the waves).  Completes by the wave's next full wait.
+// starting at j0 into LDS, keys (which = 0) or values (which = 1) or both
+// (which = 2); two rows per 1 KiB instruction, pairs spread over the waves.
+// Completes by the wave's next full wait.
 __device__ __forceinline__ void load_kv(const MegaArgs& A, int l, int g, int j0, Shared& sh,
-                                        int wave, int lane) {
+                                        int wave, int lane, int which = 2) {
   const int npair = (min(KEYS, A.pos + 1 - j0) + 1) / 2;
   const LayerW& Lw = sh.lt[l & 1];
   float* Ks = (float*)(sh.stage + ATT_KV);
@@ -711,12 +769,14 @@ __device__ __forceinline__ void load_kv(const MegaArgs& A, int l, int g, int j0,
   for (int pr = wave; pr < npair; pr += NW) {
     const int j = j0 + 2 * pr + (lane >> 5);
     const size_t off = ((size_t)j * NKV + g) * D + (lane & 31) * 4;
-    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(Lw.kc + off),
-                                     (void __attribute__((address_space(3)))*)(Ks + pr * 260), 16,
-                                     0, 0);
-    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(Lw.vc + off),
-                                     (void __attribute__((address_space(3)))*)(Vs + pr * 260), 16,
-                                     0, 0);
+    if (which != 1)
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(Lw.kc + off),
+                                       (void __attribute__((address_space(3)))*)(Ks + pr * 260),
+                                       16, 0, 0);
+    if (which != 0)
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(Lw.vc + off),
+                                       (void __attribute__((address_space(3)))*)(Vs + pr * 260),
+                                       16, 0, 0);
   }
 }
 
@@ -775,13 +835,18 @@ __device__ void attention_item(const MegaArgs& A, uint32_t epoch, int l, int g, 
   double* red = (double*)(sh.stage + ATT_RED);
   const int h0 = g * G + hh * HPI;
 
+  // The first chunk's keys are requested first; the wait for q|k|v queues
+  // only behind them (a workgroup's loads are served in order), and the
+  // values, first needed for the weighted sum, are requested after it.
+  load_kv(A, l, g, sp * KEYS, sh, wave, lane, 0);
   // q of heads h0..h0+3 (waves 0..3), k and v of KV head g (waves 4, 5)
   if (wave < HPI + 2) {
     const int n0 = wave < HPI ? (h0 + wave) * D : (wave == HPI ? Q + g * D : Q + KVD + g * D);
     poll_range(xl + OFF_QKV, n0, n0 + D, R_QKV, qst + wave * D * 8, A.err, lane, epoch);
   }
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the first chunk's rows
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the first chunk's keys
   lds_barrier();
+  load_kv(A, l, g, sp * KEYS, sh, wave, lane, 1);
   if (tid == 0) stamp(tr, 0, lane);
   // rotary embedding (fp64) at position p, rounded to fp32; q kept widened
   {
@@ -824,12 +889,10 @@ __device__ void attention_item(const MegaArgs& A, uint32_t epoch, int l, int g, 
       __builtin_amdgcn_s_waitcnt(0);
       lds_barrier();
     }
-    // this call's row replaces cache row p
-    if (p >= j0 && p < j0 + KEYS)
-      for (int t = tid; t < D; t += NT) {
-        Ks[kv_row(p - j0) + t] = kr[t];
-        Vs[kv_row(p - j0) + t] = vv[t];
-      }
+    // this call's key row replaces cache row p
+    const bool here = p >= j0 && p < j0 + KEYS;
+    if (here)
+      for (int t = tid; t < D; t += NT) Ks[kv_row(p - j0) + t] = kr[t];
     lds_barrier();
     if (tid == 0) stamp(tr, 1, lane);
     // scores, partial over dims [16 w, 16 w + 16) on waves 0..7, lane = key;
@@ -880,38 +943,44 @@ __device__ void attention_item(const MegaArgs& A, uint32_t epoch, int l, int g, 
         hm[2 * wave + 1] = ls;
       }
     }
+    // this wave's copies of the values are in (the first chunk's were
+    // requested after the keys)
+    __builtin_amdgcn_s_waitcnt(0);
     lds_barrier();
     if (tid == 0) stamp(tr, 2, lane);
-    // weighted values, partial over keys [16 ks, 16 ks + 16) on waves 0..7:
-    // lane = dim within half (w & 1), all four heads per lane
+    // this call's value row replaces cache row p; the value rows past it
+    // (stale LDS, weight 0) are zeroed so that the weighted sum needs no mask
+    if (here) {
+      for (int t = tid; t < D; t += NT) Vs[kv_row(p - j0) + t] = vv[t];
+      for (int t = tid + nk * D; t < KEYS * D; t += NT) Vs[kv_row(t >> 7) + (t & (D - 1))] = 0.f;
+      lds_barrier();
+    }
+    // weighted values, partial over keys [16 ks, 16 ks + 16) on waves 0..7
+    // (ks = w / 2): lane = dim within half w % 2, all four heads per lane;
+    // keys past the position have weight 0 and zeroed rows
     if (wave < 2 * PV_SLICES) {
       const int d = 64 * (wave & 1) + lane, ks = wave >> 1;
       double acc[HPI];
 #pragma unroll
       for (int h = 0; h < HPI; ++h) acc[h] = 0.0;
-      // keys past the position have weight 0 but stale rows: skipped, in
-      // groups of 4 whose loads are all requested before the first use
       for (int k4 = 16 * ks; k4 < min(nk, 16 * ks + 16); k4 += 4) {
         float vf[4];
         double2 pa[4], pb[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int k = min(k4 + i, nk - 1);  // a key past the end repeats one with weight use below
-          vf[i] = Vs[kv_row(k) + d];
-          pa[i] = *(const double2*)(pw + k * HPI);
-          pb[i] = *(const double2*)(pw + k * HPI + 2);
+        for (int i = 0; i < 4; ++i) {  // the group's loads are requested together
+          vf[i] = Vs[kv_row(k4 + i) + d];
+          pa[i] = *(const double2*)(pw + (k4 + i) * HPI);
+          pb[i] = *(const double2*)(pw + (k4 + i) * HPI + 2);
         }
-        asm volatile("" ::"v"(vf[0]), "v"(vf[1]), "v"(vf[2]), "v"(vf[3]), "v"(pa[0].x), "v"(pa[1].x),
-                     "v"(pa[2].x), "v"(pa[3].x), "v"(pb[0].x), "v"(pb[1].x), "v"(pb[2].x), "v"(pb[3].x));
+        asm volatile("" ::"v"(vf[0]), "v"(vf[1]), "v"(vf[2]), "v"(vf[3]), "v"(pa[0].x),
+                     "v"(pa[3].x), "v"(pb[0].x), "v"(pb[3].x));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          if (k4 + i < nk) {
-            const double v = vf[i];
-            acc[0] = fma(pa[i].x, v, acc[0]);
-            acc[1] = fma(pa[i].y, v, acc[1]);
-            acc[2] = fma(pb[i].x, v, acc[2]);
-            acc[3] = fma(pb[i].y, v, acc[3]);
-          }
+          const double v = vf[i];
+          acc[0] = fma(pa[i].x, v, acc[0]);
+          acc[1] = fma(pa[i].y, v, acc[1]);
+          acc[2] = fma(pb[i].x, v, acc[2]);
+          acc[3] = fma(pb[i].y, v, acc[3]);
         }
       }
 #pragma unroll
@@ -1051,9 +1120,14 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
       su[k] = valid ? ldc(Lw.sw[5], gu0 + r) : 0.f;
       cu[k] = valid ? ldc(Lw.cs[5], gu0 + r) : 0;
     }
-    // units 0..7 into registers, the last row's four units into this wave's
-    // 4 KiB of LDS (stage bytes [16K, 80K) are free until the gate/up phase)
+    // units 0..7 into registers
     prime_units<W, W>(win, [&](int i) { return gu_addr(Lw, i); });
+  };
+  // the last row's four units into this wave's 4 KiB of LDS (stage bytes
+  // [16K, 80K) are free from the o projection on); requested after the wait
+  // for the attention output, which would otherwise queue behind them
+  auto issue_gate_up_lds = [&](int l) {
+    const LayerW& Lw = sh.lt[l & 1];
     if (s + NW * 2 < ngu) {
 #pragma unroll
       for (int i = W; i < NGU; ++i)
@@ -1119,10 +1193,9 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
 
     // ---- q, k, v
     trace_at(A, w, l, 0);
-    if (att) load_kv(A, l, w / (NIH * HH), (w % NIH) * KEYS, sh, wave, lane);
     load_gain(Lw.ln1, sh.gain, wave, lane16);
     QParam qp = poll_norm(xl + OFF_X0 + rep * H, R_D, sh.xs, sh, A.eps, lane, wave, tid, epoch,
-                          A.err, trace_sub(A, w, l, 27), trace_stat(A, w, l, 11),
+                          A.err, [] {}, trace_sub(A, w, l, 27), trace_stat(A, w, l, 11),
                           trace_sub(A, w, l, 11), trace_sub(A, w, l, 12), trace_sub(A, w, l, 13));
     trace_at(A, w, l, 2);
     {
@@ -1141,8 +1214,16 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
     if (att) {
       lds_barrier();  // the codes are used (the stores of the q|k|v rows stay in flight)
       attention_item(A, epoch, l, w / (NIH * HH), (w / NIH) % HH, w % NIH, nitem, nchunk, sh, xl,
-                     trace_sub(A, w, l, 22), tid, lane, wave);
+                     trace_sub(A, w, l, 22), tid, lane, s);  // s: wave index, opaque per layer
       lds_barrier();  // the staging area is free again
+      // no SwiGLU rows here: the neutral (min, max) pair, one replica per lane
+      if (wave == 0 && lane < NREP) {
+        float pinf = INFINITY;
+        asm volatile("" : "+v"(pinf));  // made here, not kept (spilled) across the loop
+        u64* mm = xl + OFF_AMM + lane * 2 * NWG + 2 * w;
+        xput(mm, pinf, epoch);
+        xput(mm + 1, -pinf, epoch);
+      }
       issue_o(l);
       issue_down_lds(l);
     } else {
@@ -1156,6 +1237,7 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
     trace_at(A, w, l, 4);
     qp = poll_quant(xl + OFF_ATT + rep * Q, Q, HPI * D, sh, lane, wave, epoch, A.err, nullptr, nullptr,
                     trace_stat(A, w, l, 12));
+    if (!att) issue_gate_up_lds(l);
     trace_at(A, w, l, 5);
     {
       int accs[1];
@@ -1174,7 +1256,7 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
     asm volatile("" : "+v"(lane16), "+v"(tid), "+v"(lane));
     load_gain(Lw.ln2, sh.gain, wave, lane16);
     qp = poll_norm(xl + OFF_X1 + rep * H, R_O, sh.x1s, sh, A.eps, lane, wave, tid, epoch, A.err,
-                   trace_sub(A, w, l, 16), trace_stat(A, w, l, 13), trace_sub(A, w, l, 14),
+                   [] {}, trace_sub(A, w, l, 16), trace_stat(A, w, l, 13), trace_sub(A, w, l, 14),
                    trace_sub(A, w, l, 15), trace_sub(A, w, l, 30));
     trace_at(A, w, l, 7);
     if (!att) {
@@ -1230,22 +1312,21 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
       }
       trace_done(A, w, l, 8, lane);
       lds_barrier();  // the down units bound for LDS may still be in flight
-      // round 1: this workgroup's min and max, one replica per lane
-      if (wave == 0 && rank < nprod) {
+      // round 1: this workgroup's min and max (+inf, -inf without rows), one
+      // replica per lane
+      if (wave == 0) {
         minmax16(sh.redf, lane, lo, hi);
         if (lane < NREP) {
-          u64* mm = xl + OFF_AMM + lane * 2 * NWG + 2 * rank;
+          u64* mm = xl + OFF_AMM + lane * 2 * NWG + 2 * w;
           xput(mm, lo, epoch);
           xput(mm + 1, hi, epoch);
         }
       }
-      issue_down(l);
     }
 
     // ---- SwiGLU quantisation parameters from all producers' min/max
     asm volatile("" : "+v"(lane16), "+v"(tid), "+v"(lane));
-    qp = poll_quant(xl + OFF_AMM + rep * 2 * NWG, 2 * nprod, 2, sh, lane, wave, epoch, A.err,
-                    trace_sub(A, w, l, 19), nullptr, trace_stat(A, w, l, 14), NPOLL, true);
+    qp = poll_amm(xl + OFF_AMM + rep * 2 * NWG, sh, lane, wave, epoch, A.err, trace_sub(A, w, l, 19));
     // round 2: producers quantise their rows and publish the packed codes
     if (!att && tid < ngu / 4) {
       uint32_t word = 0;
@@ -1257,6 +1338,13 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
       for (int r = 0; r < NREP; ++r)
         __hip_atomic_store(xl + OFF_AC + (size_t)r * (I / 4) + k, ((u64)epoch << 32) | word,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // the down rows are requested only now: a workgroup's memory requests
+    // are served in order, and issuing them stalls the loader waves until
+    // the queue drains, so the (min, max) wait and the codes' stores go first
+    if (!att) {
+      lds_barrier();
+      issue_down(l);
     }
 
     // ---- down + residual: waves 0..7 poll and quantise the SwiGLU vector
