@@ -238,9 +238,13 @@ int ark_test_dynquant(int32_t B, int32_t R, int32_t K, const float* x, uint8_t* 
 /* One int8 MatMul on given codes: rows r of sequence b = r / R use (scale[b],
  * zp[b]).  codes [B*R][W->k] uint8; acc [B*R][W->n] int32 (or NULL): the
  * exact sum_k (code - zp) * w; y [B*R][W->n] fp32 dequantised output with
- * bias.  use_gemm selects the MFMA GEMM (1) or the decode GEMV (0, requires
- * B*R <= 4).  workspace >= B*R*(W->k + 8) + 256 bytes.  Errors: ARK_E_NULL,
+ * bias.  use_gemm selects the kernel: 0 the decode GEMV (requires B*R <= 4);
+ * 1 the matrix-core GEMM as the decoder dispatches it (few-row kernel for
+ * B*R <= 32 and W->k % 128 == 0, large-tile kernel for B*R >= 128, tiled
+ * kernel otherwise); 2 the tiled kernel for any B*R.  workspace >=
+ * ark_test_qlinear_workspace_bytes(B*R, W->k, use_gemm).  Errors: ARK_E_NULL,
  * ARK_E_SHAPE, ARK_E_WORKSPACE. */
+size_t ark_test_qlinear_workspace_bytes(int32_t rows, int32_t k, int32_t use_gemm);
 int ark_test_qlinear(int32_t B, int32_t R, const uint8_t* codes, const float* scale,
                      const uint8_t* zp, const ark_qlinear* W, int32_t* acc, float* y,
                      int32_t use_gemm, void* workspace, size_t workspace_bytes,

@@ -69,6 +69,7 @@ _SIGS = {
     "ark_greedy_decode": (C.c_int, [C.POINTER(ArkModel), I32, P, PI32, PP, PP, P, P, P, P, I32,
                                     I32, I32, P, P, C.c_size_t, P]),
     "ark_test_dynquant": (C.c_int, [I32, I32, I32, P, P, P, P, P, C.c_size_t, P]),
+    "ark_test_qlinear_workspace_bytes": (C.c_size_t, [I32, I32, I32]),
     "ark_test_qlinear": (C.c_int, [I32, I32, P, P, P, C.POINTER(ArkQLinear), P, P, I32, P,
                                    C.c_size_t, P]),
     "ark_profile_arm": (C.c_int, [PP, I32]),
@@ -341,14 +342,16 @@ def test_dynquant(x, stream=None):
     return codes, scale, zp
 
 
-def test_qlinear(codes, scale, zp, W: QLinear, use_gemm: bool, stream=None):
-    """codes [B][R][k] uint8, scale [B], zp [B] uint8 -> (acc int32, y fp32) [B*R][n]."""
+def test_qlinear(codes, scale, zp, W: QLinear, use_gemm, stream=None):
+    """codes [B][R][k] uint8, scale [B], zp [B] uint8 -> (acc int32, y fp32) [B*R][n].
+    use_gemm: 0 decode GEMV, 1 GEMM as dispatched by the decoder, 2 tiled GEMM."""
     import torch
     B, R, k = codes.shape
     n = W.codes.shape[0]
     acc = torch.empty((B * R, n), dtype=torch.int32, device=codes.device)
     y = torch.empty((B * R, n), dtype=torch.float32, device=codes.device)
-    ws = torch.empty(B * R * (k + 8) + 256, dtype=torch.uint8, device=codes.device)
+    nbytes = lib().ark_test_qlinear_workspace_bytes(B * R, k, int(use_gemm))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
     wc = W.c()
     _check("ark_test_qlinear", lib().ark_test_qlinear(B, R, _ptr(codes), _ptr(scale), _ptr(zp), C.byref(wc),
                                                        _ptr(acc), _ptr(y), int(use_gemm), _ptr(ws),

@@ -19,7 +19,7 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
 struct Plan {
-  size_t x, h, codes, qkv, q, attn, a, rmin, rmax, qs, qz, part, done, mega, total;
+  size_t x, h, codes, qkv, q, attn, a, rmin, rmax, qs, qz, part, done, gsk, mega, total;
 };
 
 bool use_mega(const ark_dims& d, int B, int S) {
@@ -58,6 +58,7 @@ Plan plan(const ark_dims& d, int B, int S) {
   // prefill of B sequences also serves their decode steps
   p.part = take(attention_ws_bytes(B, 1, d.n_heads, d.max_total_len));
   p.done = take((size_t)kMaxBatch * 4);
+  p.gsk = take(gemm_skinny_ws_bytes());
   p.mega = take(B == 1 ? decode_mega_ws_bytes(d.n_layers, d.max_total_len) : 0);
   p.total = o;
   return p;
@@ -176,6 +177,9 @@ int run_forward(const ark_model* m, int B, int S, float* x, const int32_t* pos_h
   const int R = B * S, H = d.hidden, NH = d.n_heads, NKV = d.n_kv_heads;
   const int Q = NH * kHeadDim, KV = NKV * kHeadDim, I = d.intermediate, T = d.max_total_len;
   const bool gemv = (S == 1 && B <= 4);
+  // one row per sequence: norm and quantisation fused per row
+  const bool rowq = S == 1 && norm_quant_row_supported(H) && norm_quant_row_supported(Q) &&
+                    norm_quant_row_supported(I);
   float* h = (float*)(ws + p.h);
   int8_t* codes = (int8_t*)(ws + p.codes);
   float* qkv = (float*)(ws + p.qkv);
@@ -187,6 +191,8 @@ int run_forward(const ark_model* m, int B, int S, float* x, const int32_t* pos_h
   float* qs = (float*)(ws + p.qs);
   int* qz = (int*)(ws + p.qz);
   void* part = ws + p.part;
+  void* gsk = ws + p.gsk;  // few-row GEMM scratch
+  HIP_TRY(gemm_skinny_reset(st, gsk));
   PosArgs pos;
   memset(&pos, 0, sizeof(pos));
   for (int b = 0; b < B; ++b) pos.p[b] = pos_host[b];
@@ -203,10 +209,13 @@ int run_forward(const ark_model* m, int B, int S, float* x, const int32_t* pos_h
     Seg ds[1] = {seg_of(L.down, x, H)};
     if (gemv) {
       HIP_TRY(launch_gemv(st, B, H, x, H, L.ln1, d.rms_eps, qkvs, 3, EPI_STORE));
+    } else if (rowq) {
+      HIP_TRY(launch_norm_quant_row(st, B, H, x, H, L.ln1, d.rms_eps, codes, qs, qz));
+      HIP_TRY(launch_gemm(st, R, H, codes, qs, qz, S, qkvs, 3, EPI_STORE, nullptr, gsk));
     } else {
       HIP_TRY(launch_rmsnorm_rows(st, R, H, x, H, L.ln1, d.rms_eps, h, rmin, rmax));
       HIP_TRY(launch_quant_rows(st, B, S, H, h, rmin, rmax, codes, nullptr, qs, qz));
-      HIP_TRY(launch_gemm(st, R, H, codes, qs, qz, S, qkvs, 3, EPI_STORE, nullptr));
+      HIP_TRY(launch_gemm(st, R, H, codes, qs, qz, S, qkvs, 3, EPI_STORE, nullptr, gsk));
     }
     HIP_TRY(launch_rope(st, B, S, NH, NKV, qkv, m->rope_cos, m->rope_sin, pos, q, kdl, vdl));
     HIP_TRY(launch_attention(st, B, S, NH, NKV, T, q, kc[l], vc[l], kdl, vdl, pos, attn, part));
@@ -216,16 +225,23 @@ int run_forward(const ark_model* m, int B, int S, float* x, const int32_t* pos_h
       HIP_TRY(launch_gemv(st, B, H, x, H, L.ln2, d.rms_eps, gus, 2, EPI_SWIGLU));
       prof_end(st, B == 1);
       HIP_TRY(launch_gemv(st, B, I, a, I, nullptr, 0.0, ds, 1, EPI_RESID));
+    } else if (rowq) {
+      HIP_TRY(launch_norm_quant_row(st, B, Q, attn, Q, nullptr, 0.0, codes, qs, qz));
+      HIP_TRY(launch_gemm(st, R, Q, codes, qs, qz, S, os, 1, EPI_RESID, nullptr, gsk));
+      HIP_TRY(launch_norm_quant_row(st, B, H, x, H, L.ln2, d.rms_eps, codes, qs, qz));
+      HIP_TRY(launch_gemm(st, R, H, codes, qs, qz, S, gus, 2, EPI_SWIGLU, nullptr, gsk));
+      HIP_TRY(launch_norm_quant_row(st, B, I, a, I, nullptr, 0.0, codes, qs, qz));
+      HIP_TRY(launch_gemm(st, R, I, codes, qs, qz, S, ds, 1, EPI_RESID, nullptr, gsk));
     } else {
       HIP_TRY(launch_rowminmax(st, R, Q, attn, rmin, rmax));
       HIP_TRY(launch_quant_rows(st, B, S, Q, attn, rmin, rmax, codes, nullptr, qs, qz));
-      HIP_TRY(launch_gemm(st, R, Q, codes, qs, qz, S, os, 1, EPI_RESID, nullptr));
+      HIP_TRY(launch_gemm(st, R, Q, codes, qs, qz, S, os, 1, EPI_RESID, nullptr, gsk));
       HIP_TRY(launch_rmsnorm_rows(st, R, H, x, H, L.ln2, d.rms_eps, h, rmin, rmax));
       HIP_TRY(launch_quant_rows(st, B, S, H, h, rmin, rmax, codes, nullptr, qs, qz));
-      HIP_TRY(launch_gemm(st, R, H, codes, qs, qz, S, gus, 2, EPI_SWIGLU, nullptr));
+      HIP_TRY(launch_gemm(st, R, H, codes, qs, qz, S, gus, 2, EPI_SWIGLU, nullptr, gsk));
       HIP_TRY(launch_rowminmax(st, R, I, a, rmin, rmax));
       HIP_TRY(launch_quant_rows(st, B, S, I, a, rmin, rmax, codes, nullptr, qs, qz));
-      HIP_TRY(launch_gemm(st, R, I, codes, qs, qz, S, ds, 1, EPI_RESID, nullptr));
+      HIP_TRY(launch_gemm(st, R, I, codes, qs, qz, S, ds, 1, EPI_RESID, nullptr, gsk));
     }
   }
 
@@ -235,9 +251,14 @@ int run_forward(const ark_model* m, int B, int S, float* x, const int32_t* pos_h
     if (B <= 4) {
       HIP_TRY(launch_gemv(st, B, H, last, S * H, m->final_norm, d.rms_eps, lm, 1, EPI_STORE));
     } else {
-      HIP_TRY(launch_rmsnorm_rows(st, B, H, last, S * H, m->final_norm, d.rms_eps, h, rmin, rmax));
-      HIP_TRY(launch_quant_rows(st, B, 1, H, h, rmin, rmax, codes, nullptr, qs, qz));
-      HIP_TRY(launch_gemm(st, B, H, codes, qs, qz, 1, lm, 1, EPI_STORE, nullptr));
+      if (norm_quant_row_supported(H)) {
+        HIP_TRY(launch_norm_quant_row(st, B, H, last, S * H, m->final_norm, d.rms_eps, codes, qs,
+                                      qz));
+      } else {
+        HIP_TRY(launch_rmsnorm_rows(st, B, H, last, S * H, m->final_norm, d.rms_eps, h, rmin, rmax));
+        HIP_TRY(launch_quant_rows(st, B, 1, H, h, rmin, rmax, codes, nullptr, qs, qz));
+      }
+      HIP_TRY(launch_gemm(st, B, H, codes, qs, qz, 1, lm, 1, EPI_STORE, nullptr, gsk));
     }
   }
   return ARK_OK;
@@ -537,6 +558,11 @@ int ark_test_dynquant(int32_t B, int32_t R, int32_t K, const float* x, uint8_t* 
   return ARK_OK;
 }
 
+size_t ark_test_qlinear_workspace_bytes(int32_t rows, int32_t k, int32_t use_gemm) {
+  if (rows < 1 || k < 1) return 0;
+  return align_up((size_t)rows * (k + 8) + 256) + (use_gemm == 1 ? gemm_skinny_ws_bytes() : 0);
+}
+
 int ark_test_qlinear(int32_t B, int32_t R, const uint8_t* codes, const float* scale,
                      const uint8_t* zp, const ark_qlinear* W, int32_t* acc, float* y,
                      int32_t use_gemm, void* workspace, size_t workspace_bytes, void* stream) {
@@ -545,7 +571,9 @@ int ark_test_qlinear(int32_t B, int32_t R, const uint8_t* codes, const float* sc
   if (B < 1 || R < 1 || W->n < 1 || W->k < 64 || W->k % 64) return ARK_E_SHAPE;
   const int rows = B * R;
   if (!use_gemm && rows > 4) return ARK_E_SHAPE;
-  const size_t need = (size_t)rows * (W->k + 8) + 256;
+  if (use_gemm < 0 || use_gemm > 2) return ARK_E_SHAPE;
+  const size_t base = align_up((size_t)rows * (W->k + 8) + 256);
+  const size_t need = base + (use_gemm == 1 ? gemm_skinny_ws_bytes() : 0);
   if (workspace_bytes < need) return ARK_E_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
@@ -555,9 +583,17 @@ int ark_test_qlinear(int32_t B, int32_t R, const uint8_t* codes, const float* sc
   if (launch_test_codes(st, rows, W->k, R, codes, sc, scale, zp, srow, zrow) != hipSuccess)
     return ARK_E_HIP;
   Seg s = seg_of(*W, y, W->n);
-  hipError_t err = use_gemm ? launch_gemm(st, rows, W->k, sc, srow, zrow, 1, &s, 1, EPI_STORE, acc)
-                            : launch_gemv_codes(st, rows, W->k, sc, srow, zrow, &s, 1, EPI_STORE,
-                                                acc);
+  hipError_t err;
+  if (use_gemm == 1) {
+    void* gsk = ws + base;
+    err = gemm_skinny_reset(st, gsk);
+    if (err == hipSuccess)
+      err = launch_gemm(st, rows, W->k, sc, srow, zrow, 1, &s, 1, EPI_STORE, acc, gsk);
+  } else if (use_gemm == 2) {
+    err = launch_gemm(st, rows, W->k, sc, srow, zrow, 1, &s, 1, EPI_STORE, acc, nullptr, true);
+  } else {
+    err = launch_gemv_codes(st, rows, W->k, sc, srow, zrow, &s, 1, EPI_STORE, acc);
+  }
   return err == hipSuccess ? ARK_OK : ARK_E_HIP;
 }
 

@@ -108,7 +108,11 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
 #pragma unroll
   for (int e = 0; e < DPT; ++e) o[e] = 0.0;
 
-  const int jbeg = split * P.tsplit, jend = min(T, jbeg + P.tsplit);
+  // keys past the last query row's position carry zero weight: they are
+  // neither loaded nor scored (a split that starts past it leaves an empty
+  // state, which the merge skips)
+  const int jbeg = split * P.tsplit;
+  const int jend = min(min(T, jbeg + P.tsplit), p + min(S, i0 + QT));
   for (int j0 = jbeg; j0 < jend; j0 += KC) {
     __syncthreads();
     // K/V rows j0 .. j0 + KC - 1 (cache or this call's deltas)

@@ -12,8 +12,6 @@
 // the 64-wide K step.  Because A and B use the same lane->K assignment, the
 // product is sum_k A[i][k] * B[j][k] whatever order the instruction walks K.
 // The 16x16 result sits in lane (j + 16*(i/4)), register i % 4.
-#include <stdlib.h>
-
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -188,7 +186,10 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
 
 hipError_t launch_gemm(hipStream_t st, int M, int K, const int8_t* codes, const float* s,
                        const int* z, int rows_per_seq, const Seg* segs, int nseg, Epi epi,
-                       int32_t* acc_out) {
+                       int32_t* acc_out, void* scratch, bool tiled_only) {
+  if (!tiled_only && scratch && gemm_skinny_supported(M, K))
+    return launch_gemm_skinny(st, M, K, codes, s, z, rows_per_seq, segs, nseg, epi, acc_out,
+                              scratch);
   GemmParams P = {};
   P.M = M;
   P.K = K;
@@ -205,7 +206,7 @@ hipError_t launch_gemm(hipStream_t st, int M, int K, const int8_t* codes, const 
     P.seg_start[i + 1] = P.seg_start[i] + segs[i].n;
   }
   P.ncols = (epi == EPI_SWIGLU) ? segs[0].n : P.seg_start[nseg];
-  if (gemm_big_supported(M, K) && !getenv("ARK_GEMM_SMALL"))
+  if (!tiled_only && gemm_big_supported(M, K))
     return launch_gemm_big(st, M, K, codes, s, z, rows_per_seq, segs, nseg, epi, acc_out);
   if (M <= 32) {
     constexpr int BM = 32, BN = 128;

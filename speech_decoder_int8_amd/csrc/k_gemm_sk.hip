@@ -1,0 +1,295 @@
+// int8 x int8 -> int32 GEMM for few activation rows (M <= 32: batched decode
+// and the LM head of a batch), weight-stream bound, on gfx950 matrix cores
+// (v_mfma_i32_32x32x32_i8), with the same dequantising epilogues as k_gemm
+// (store (+bias), residual add, SwiGLU over paired gate/up rows).
+//
+// One 32x32x32 instruction covers all M rows, so every weight byte is read
+// from HBM exactly once and feeds one instruction.  A workgroup of 4 waves
+// owns 128 weight rows (wave w: rows 32 w .. 32 w + 31; for SwiGLU 16 gate
+// rows and the 16 up rows of the same outputs) and a range of K, walked in
+// 128-byte steps.  Each step's tiles (128 weight rows and the 32 activation
+// rows, 128 bytes each) go from global memory straight into LDS with
+// 16-byte LDS-DMA loads: one instruction moves 8 whole 128-byte row
+// segments; three steps are in flight.  In LDS the 16-byte chunk c of row r
+// sits at chunk c ^ ((r >> 1) & 7), so the 16 rows one fragment read
+// touches cover all 64 banks; each lane fetches the global chunk that
+// belongs at its LDS position.  Fragment layout: lane l supplies row l % 32
+// of its activation and weight fragments with K bytes 32 c + 16 (l / 32) ..
+// +16 for instruction c = 0..3 of the step.
+//
+// Small weight matrices are split along K over ks workgroups per row tile
+// (so that a launch still spreads over the whole chip): each adds its int32
+// sums into the tile's block with device-scope atomic additions, and the
+// last one to arrive (tile counter) reads the block, clears it and the
+// counter for the next launch, and runs the epilogue.  Integer sums are
+// exact, so the result does not depend on the split or the order.
+//
+// Accumulator layout (32x32 int32 in 16 registers): register r of lane l
+// holds row (r / 4) * 8 + (l / 32) * 4 + r % 4, column l % 32.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ark {
+
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+namespace sk {
+constexpr int NT = 256, ROWS = 128, SS = 128, NS = 3;
+constexpr int B_BYTES = ROWS * SS, A_BYTES = 32 * SS, STAGE = B_BYTES + A_BYTES;
+constexpr int LDS = NS * STAGE;
+}  // namespace sk
+
+struct GemmSkParams {
+  int M, K, ncols, epi, rows_per_seq, nseg, tiles, ks, nss;
+  const int8_t* A;
+  const float* qs;
+  const int* qz;
+  Seg seg[3];
+  int seg_start[4];
+  int32_t* part;     // [tiles][32][ROWS] int32 sums of split launches, zero between launches
+  uint32_t* ctr;     // [tiles] arrival counters, zero between launches
+  int32_t* acc_out;  // optional [M][ncols]: raw sums (tests)
+};
+
+__device__ __forceinline__ int sk_swz(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+
+template <int N>
+__device__ __forceinline__ void sk_wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+__global__ __launch_bounds__(256, 2) void k_gemm_sk(GemmSkParams P) {
+  using namespace sk;
+  extern __shared__ __align__(16) int8_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool swiglu = P.epi == EPI_SWIGLU;
+  const int tile = blockIdx.x % P.tiles, kp = blockIdx.x / P.tiles;
+  const int K = P.K;
+  const int j = lane & 31, half = lane >> 5;
+
+  // DMA sources: weight instruction i (0..3) of this wave covers tile rows
+  // 8 (4 w + i) .. +8, the activation instruction rows 8 w .. 8 w + 7; lane l
+  // lands at LDS chunk l % 8 of row l / 8 and fetches the chunk stored there.
+  // Rows past ncols or M read row 0 instead (their products only reach
+  // outputs that are never stored), so every wave issues exactly 5 loads per
+  // step and the waits below can count them.
+  const int8_t* bsrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * (4 * wave + i) + (lane >> 3);  // tile row
+    const int c = (lane & 7) ^ ((r >> 1) & 7);       // global chunk at this position
+    bsrc[i] = P.seg[0].w + 16 * c;
+    if (swiglu) {
+      // tile rows 32 v .. 32 v + 15: gate outputs 16 v.., rows 32 v + 16..: up
+      const int v = r >> 5, q = r & 31;
+      const int n = tile * (ROWS / 2) + v * 16 + (q & 15);
+      if (n < P.ncols) bsrc[i] = (q < 16 ? P.seg[0].w : P.seg[1].w) + (size_t)n * K + 16 * c;
+    } else {
+      const int n = tile * ROWS + r;
+      if (n < P.ncols) {
+        int s = 0;
+        while (s + 1 < P.nseg && n >= P.seg_start[s + 1]) ++s;
+        bsrc[i] = P.seg[s].w + (size_t)(n - P.seg_start[s]) * K + 16 * c;
+      }
+    }
+  }
+  const int8_t* asrc;
+  {
+    const int r = 8 * wave + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    asrc = P.A + (size_t)(r < P.M ? r : 0) * K + 16 * c;
+  }
+  const int s0 = kp * P.nss, s1 = min(s0 + P.nss, K / SS);
+  const int nk = s1 - s0;
+
+  auto issue = [&](int st, int buf) {
+    int8_t* base = lds + buf * STAGE;
+    const size_t o = (size_t)(s0 + st) * SS;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(bsrc[i] + o),
+          (void __attribute__((address_space(3)))*)(base + (4 * wave + i) * 1024), 16, 0, 2);
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(asrc + o),
+                                     (void __attribute__((address_space(3)))*)(base + B_BYTES +
+                                                                               wave * 1024),
+                                     16, 0, 0);
+  };
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < nk) issue(st, st);
+
+  i32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0;
+  for (int st = 0; st < nk; ++st) {
+    if (st + 1 < nk)
+      sk_wait_vm<5>();  // this wave's loads of step st are done (step st+1's may be in flight)
+    else
+      sk_wait_vm<0>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();         // every wave's step-st loads landed; buffer st+2 free
+    if (st + NS - 1 < nk) issue(st + NS - 1, (st + NS - 1) % NS);
+    const int8_t* Bs = lds + (st % NS) * STAGE;
+    const int8_t* As = Bs + B_BYTES;
+    i32x4 fa[4], fb[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      fa[c] = *(const i32x4*)(As + sk_swz(j, 2 * c + half));
+      fb[c] = *(const i32x4*)(Bs + sk_swz(32 * wave + j, 2 * c + half));
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[c], fb[c], acc, 0, 0, 0);
+  }
+
+  if (P.ks > 1) {
+    // add this K range's sums into the tile's block (device-scope atomics,
+    // performed at the coherence point); the last arrival reads the block
+    // back, clears it for the next launch and runs the epilogue
+    int32_t* blk = P.part + (size_t)tile * 32 * ROWS;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = (r / 4) * 8 + half * 4 + r % 4;
+      __hip_atomic_fetch_add(blk + m * ROWS + wave * 32 + j, acc[r], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's additions are performed
+    __syncthreads();
+    __shared__ uint32_t last;
+    if (tid == 0) {
+      const uint32_t old = __hip_atomic_fetch_add(P.ctr + tile, 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+      last = (old == (uint32_t)P.ks - 1);
+    }
+    __syncthreads();
+    if (!last) return;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = (r / 4) * 8 + half * 4 + r % 4;
+      int32_t* a = blk + m * ROWS + wave * 32 + j;
+      acc[r] = __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = (r / 4) * 8 + half * 4 + r % 4;
+      __hip_atomic_store(blk + m * ROWS + wave * 32 + j, 0, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (tid == 0)
+      __hip_atomic_store(P.ctr + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // ---- epilogue: row m = (r / 4) * 8 + half * 4 + r % 4, weight row j
+  if (swiglu) {
+    const int n = tile * (ROWS / 2) + wave * 16 + (j & 15);
+    const Seg& G = P.seg[0];
+    const Seg& U = P.seg[1];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int up = __shfl_down(acc[r], 16, 32);  // lane j < 16 gets row j's up sum
+      const int m = (r / 4) * 8 + half * 4 + r % 4;
+      if (j < 16 && m < P.M && n < P.ncols) {
+        const int b = m / P.rows_per_seq;
+        const float s = P.qs[b];
+        const int zc = 128 - P.qz[b];
+        const int ag = acc[r] + zc * G.cs[n];
+        const int au = up + zc * U.cs[n];
+        const float g = dequant(ag, s, G.sw[n]);
+        const float u = dequant(au, s, U.sw[n]);
+        const double gd = g;
+        G.out[(size_t)m * G.ldo + n] = (float)(gd / (1.0 + exp(-gd)) * (double)u);
+        if (P.acc_out) P.acc_out[(size_t)m * P.ncols + n] = ag;
+      }
+    }
+  } else {
+    const int col = tile * ROWS + wave * 32 + j;
+    if (col < P.ncols) {
+      int si = 0;
+      while (si + 1 < P.nseg && col >= P.seg_start[si + 1]) ++si;
+      const Seg& S = P.seg[si];
+      const int n = col - P.seg_start[si];
+      const float sw = S.sw[n];
+      const int cs = S.cs[n];
+      const float bias = S.bias ? S.bias[n] : 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = (r / 4) * 8 + half * 4 + r % 4;
+        if (m >= P.M) continue;
+        const int b = m / P.rows_per_seq;
+        const int at = acc[r] + (128 - P.qz[b]) * cs;
+        float y = dequant(at, P.qs[b], sw);
+        if (S.bias) y = y + bias;
+        float* o = S.out + (size_t)m * S.ldo + n;
+        if (P.epi == EPI_RESID)
+          *o = *o + y;
+        else
+          *o = y;
+        if (P.acc_out) P.acc_out[(size_t)m * P.ncols + col] = at;
+      }
+    }
+  }
+}
+
+bool gemm_skinny_supported(int M, int K) { return M >= 1 && M <= 32 && K % sk::SS == 0; }
+
+constexpr int SK_MAX_SPLIT_TILES = 256;  // row tiles of a K-split launch
+
+size_t gemm_skinny_ws_bytes() {
+  // sum blocks of the tiles of a split launch, then the tile counters
+  return (size_t)SK_MAX_SPLIT_TILES * 32 * sk::ROWS * 4 + SK_MAX_SPLIT_TILES * 4;
+}
+
+__global__ void k_zero_u32(uint32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+hipError_t gemm_skinny_reset(hipStream_t st, void* scratch) {
+  const int n = (int)(gemm_skinny_ws_bytes() / 4);
+  hipLaunchKernelGGL(k_zero_u32, dim3(256), dim3(256), 0, st, (uint32_t*)scratch, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_skinny(hipStream_t st, int M, int K, const int8_t* codes, const float* s,
+                              const int* z, int rows_per_seq, const Seg* segs, int nseg, Epi epi,
+                              int32_t* acc_out, void* scratch) {
+  using namespace sk;
+  GemmSkParams P = {};
+  P.M = M;
+  P.K = K;
+  P.A = codes;
+  P.qs = s;
+  P.qz = z;
+  P.rows_per_seq = rows_per_seq;
+  P.nseg = nseg;
+  P.epi = epi;
+  P.acc_out = acc_out;
+  P.seg_start[0] = 0;
+  for (int i = 0; i < nseg; ++i) {
+    P.seg[i] = segs[i];
+    P.seg_start[i + 1] = P.seg_start[i] + segs[i].n;
+  }
+  P.ncols = (epi == EPI_SWIGLU) ? segs[0].n : P.seg_start[nseg];
+  const int per_tile = epi == EPI_SWIGLU ? ROWS / 2 : ROWS;
+  P.tiles = (P.ncols + per_tile - 1) / per_tile;
+  const int nss = K / SS;
+  // split K until the launch has ~512 workgroups (two per CU) with at least
+  // 2 steps per split; launches of more than SK_MAX_SPLIT_TILES tiles are
+  // not split
+  int ks = 1;
+  if (P.tiles <= SK_MAX_SPLIT_TILES)
+    while (ks < 16 && P.tiles * ks * 2 <= 512 && nss / (ks * 2) >= 2) ks *= 2;
+  P.nss = (nss + ks - 1) / ks;
+  P.ks = (nss + P.nss - 1) / P.nss;
+  P.part = (int32_t*)scratch;
+  P.ctr = (uint32_t*)((char*)scratch + (size_t)SK_MAX_SPLIT_TILES * 32 * ROWS * 4);
+  static bool attr = false;
+  if (!attr) {
+    const hipError_t e =
+        hipFuncSetAttribute((const void*)k_gemm_sk, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL(k_gemm_sk, dim3(P.tiles * P.ks), dim3(NT), LDS, st, P);
+  return hipGetLastError();
+}
+
+}  // namespace ark

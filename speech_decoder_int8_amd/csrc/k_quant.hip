@@ -115,4 +115,60 @@ hipError_t launch_quant_rows(hipStream_t st, int B, int S, int K, const float* x
   return hipGetLastError();
 }
 
+// Decode form (one row per sequence, so the row is the whole tensor of its
+// sequence): RMSNorm (when g != nullptr) and the dynamic quantiser in one
+// pass, values kept in registers.  One workgroup of 256 threads per row;
+// K <= 256 * QMAX.  Same arithmetic as k_rmsnorm_rows + k_quant_rows.
+constexpr int QMAX = 48;
+__global__ __launch_bounds__(256) void k_norm_quant_row(int K, const float* __restrict__ x, int ldx,
+                                                        const float* __restrict__ g, double eps,
+                                                        int8_t* __restrict__ codes,
+                                                        float* __restrict__ s_out,
+                                                        int* __restrict__ z_out) {
+  __shared__ double redd[4];
+  __shared__ float redf[8];
+  const int r = blockIdx.x, t = threadIdx.x;
+  const float* xr = x + (size_t)r * ldx;
+  float v[QMAX];
+#pragma unroll
+  for (int k = 0; k < QMAX; ++k) v[k] = (t + 256 * k < K) ? xr[t + 256 * k] : 0.f;
+  if (g) {
+    double ss = 0.0;
+#pragma unroll
+    for (int k = 0; k < QMAX; ++k) ss += (double)v[k] * (double)v[k];
+    ss = block_sum<256>(ss, redd);
+    const double rs = 1.0 / sqrt(ss / (double)K + eps);
+#pragma unroll
+    for (int k = 0; k < QMAX; ++k)
+      if (t + 256 * k < K) v[k] = (float)(((double)v[k] * rs) * (double)g[t + 256 * k]);
+  }
+  float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < QMAX; ++k)
+    if (t + 256 * k < K) {
+      lo = fminf(lo, v[k]);
+      hi = fmaxf(hi, v[k]);
+    }
+  block_minmax<256>(lo, hi, redf);
+  const QParam p = quant_param(lo, hi);
+  if (t == 0) {
+    s_out[r] = p.s;
+    z_out[r] = p.z;
+  }
+  int8_t* cr = codes + (size_t)r * K;
+#pragma unroll
+  for (int k = 0; k < QMAX; ++k)
+    if (t + 256 * k < K) cr[t + 256 * k] = shift_code(quant_code(v[k], p));
+}
+
+bool norm_quant_row_supported(int K) { return K >= 1 && K <= 256 * QMAX; }
+
+hipError_t launch_norm_quant_row(hipStream_t st, int B, int K, const float* x, int ldx,
+                                 const float* gain, double eps, int8_t* codes, float* s_out,
+                                 int* z_out) {
+  hipLaunchKernelGGL(k_norm_quant_row, dim3(B), dim3(256), 0, st, K, x, ldx, gain, eps, codes,
+                     s_out, z_out);
+  return hipGetLastError();
+}
+
 }  // namespace ark

@@ -52,6 +52,13 @@ hipError_t launch_quant_rows(hipStream_t st, int B, int S, int K, const float* x
                              const float* rmin, const float* rmax, int8_t* codes,
                              uint8_t* codes_u8, float* s_out, int* z_out);
 
+// One row per sequence (decode): optional RMSNorm (gain != nullptr) and the
+// row's dynamic quantisation in one kernel; shifted codes [B][K], s/z [B].
+bool norm_quant_row_supported(int K);
+hipError_t launch_norm_quant_row(hipStream_t st, int B, int K, const float* x, int ldx,
+                                 const float* gain, double eps, int8_t* codes, float* s_out,
+                                 int* z_out);
+
 // ---- int8 projections
 // Decode GEMV (k_gemv.hip): B <= 4 rows of input x (row stride ldx), fused
 // prologue (RMSNorm when gain != nullptr, then per-row quantisation), segments
@@ -70,9 +77,21 @@ bool gemm_big_supported(int M, int K);
 hipError_t launch_gemm_big(hipStream_t st, int M, int K, const int8_t* codes, const float* s,
                            const int* z, int rows_per_seq, const Seg* segs, int nseg, Epi epi,
                            int32_t* acc_out);
+// Few-row GEMM (k_gemm_sk.hip, M <= 32: batched decode, LM head of a
+// batch): same contract; scratch = gemm_skinny_ws_bytes() bytes whose
+// counter words are zero (gemm_skinny_reset) and stay zero between launches.
+bool gemm_skinny_supported(int M, int K);
+size_t gemm_skinny_ws_bytes();
+hipError_t gemm_skinny_reset(hipStream_t st, void* scratch);
+hipError_t launch_gemm_skinny(hipStream_t st, int M, int K, const int8_t* codes, const float* s,
+                              const int* z, int rows_per_seq, const Seg* segs, int nseg, Epi epi,
+                              int32_t* acc_out, void* scratch);
+// Dispatch: few-row GEMM when scratch is given and the shape allows it, the
+// large-tile GEMM for M >= 128, else the tiled GEMM; tiled_only forces the
+// latter (tests).
 hipError_t launch_gemm(hipStream_t st, int M, int K, const int8_t* codes, const float* s,
                        const int* z, int rows_per_seq, const Seg* segs, int nseg, Epi epi,
-                       int32_t* acc_out);
+                       int32_t* acc_out, void* scratch = nullptr, bool tiled_only = false);
 
 // ---- rotary + attention (k_attn.hip)
 // qkv_raw [R][q_dim + 2*kv_dim] (bias added) -> q_rot [R][q_dim], k_delta /

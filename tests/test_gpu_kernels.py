@@ -67,13 +67,17 @@ def test_dynquant_all_zero_tensor():
     assert not host(codes).any() and host(scale)[0] == 0 and host(zp)[0] == 0
 
 
-@pytest.mark.parametrize("use_gemm", [False, True])
+# use_gemm: 0 decode GEMV, 1 the GEMM as the decoder dispatches it, 2 the tiled GEMM
+@pytest.mark.parametrize("use_gemm", [0, 1, 2])
 @pytest.mark.parametrize("B,R,n,k", [(1, 1, 300, 2048), (2, 2, 2560, 2048), (1, 3, 96, 11008),
                                      (3, 67, 333, 2048), (2, 16, 130, 1024),
+                                     # M <= 32: the few-row kernel (K split, ragged rows, one step)
+                                     (32, 1, 700, 2048), (4, 8, 256, 128), (1, 31, 4100, 256),
+                                     (16, 1, 2048, 11008),
                                      # M >= 128: the large-tile prefill GEMM (ragged and whole tiles)
                                      (2, 100, 2560, 2048), (1, 256, 512, 1024), (1, 130, 200, 11008)])
 def test_qlinear_bit_exact(use_gemm, B, R, n, k):
-    if not use_gemm and B * R > 4:
+    if use_gemm == 0 and B * R > 4:
         pytest.skip("the decode GEMV takes at most 4 rows")
     rng = np.random.default_rng(n + k + B * R)
     w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
