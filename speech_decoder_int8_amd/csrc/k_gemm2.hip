@@ -33,7 +33,7 @@ namespace ark {
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 namespace g2 {
-constexpr int BN = 256, BK = 64, NT = 256;
+constexpr int BN = 256, BK = 64;
 }  // namespace g2
 
 struct Gemm2Params {
@@ -64,13 +64,19 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-template <int BM, int NS>
-__global__ __launch_bounds__(256, 2) void k_gemm_big(Gemm2Params P) {
+// BM x 256 tiles on NTH / 64 waves arranged (BM / 64) x 2: every wave owns
+// a 64 x 128 block (2 x 4 accumulators of 32 x 32).
+template <int BM, int NS, int NTH>
+__global__ __launch_bounds__(NTH, NTH == 256 ? 2 : 1) void k_gemm_big(Gemm2Params P) {
   using namespace g2;
-  constexpr int FM = BM / 64;               // 32-row blocks per wave
+  constexpr int NWV = NTH / 64;             // waves
+  constexpr int RW = 64;                    // rows per wave
+  static_assert(NWV * RW == BM * 2, "(BM / 64) x 2 waves");
+  constexpr int FM = RW / 32;               // 32-row blocks per wave
   constexpr int FN = 4;                     // 32-column blocks per wave
   constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK, STAGE = A_BYTES + B_BYTES;
-  constexpr int A_INS = A_BYTES / 1024 / 4, B_INS = B_BYTES / 1024 / 4;  // per wave per stage
+  constexpr int A_INS = A_BYTES / 1024 / NWV, B_INS = B_BYTES / 1024 / NWV;  // per wave per stage
+  static_assert(A_INS * NWV * 1024 == A_BYTES && B_INS * NWV * 1024 == B_BYTES, "DMA split");
   constexpr int INS = A_INS + B_INS;
   extern __shared__ __align__(16) int8_t lds[];
 
@@ -169,7 +175,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(Gemm2Params P) {
       const int c = 2 * kk + lc;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        fa[kk][i] = *(const i32x4*)(As + swz(wm * (BM / 2) + i * 32 + lr, c));
+        fa[kk][i] = *(const i32x4*)(As + swz(wm * RW + i * 32 + lr, c));
 #pragma unroll
       for (int j = 0; j < FN; ++j) fb[kk][j] = *(const i32x4*)(Bs + swz(wn * 128 + j * 32 + lr, c));
     }
@@ -232,7 +238,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(Gemm2Params P) {
       cldo[j] = S.ldo;
     }
   }
-  const int rbase = m0 + wm * (BM / 2) + lc * 4;
+  const int rbase = m0 + wm * RW + lc * 4;
   float rs[FM][4];
   int rz[FM][4];
 #pragma unroll
@@ -297,12 +303,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(Gemm2Params P) {
 
 static constexpr int kStages = 3;
 
-template <int BM>
+template <int BM, int NTH>
 static hipError_t launch_big(hipStream_t st, Gemm2Params P) {
   constexpr int bytes = kStages * (BM + g2::BN) * g2::BK;
   static bool attr = false;
   if (!attr) {
-    const hipError_t e = hipFuncSetAttribute((const void*)k_gemm_big<BM, kStages>,
+    const hipError_t e = hipFuncSetAttribute((const void*)k_gemm_big<BM, kStages, NTH>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e != hipSuccess) return e;
     attr = true;
@@ -311,7 +317,7 @@ static hipError_t launch_big(hipStream_t st, Gemm2Params P) {
   P.tiles_m = (P.M + BM - 1) / BM;
   P.tiles = P.tiles_m * ((P.ncols + tn - 1) / tn);
   const int grid = 8 * ((P.tiles + 7) / 8);
-  hipLaunchKernelGGL((k_gemm_big<BM, kStages>), dim3(grid), dim3(g2::NT), bytes, st, P);
+  hipLaunchKernelGGL((k_gemm_big<BM, kStages, NTH>), dim3(grid), dim3(NTH), bytes, st, P);
   return hipGetLastError();
 }
 
@@ -336,7 +342,10 @@ hipError_t launch_gemm_big(hipStream_t st, int M, int K, const int8_t* codes, co
     P.seg_start[i + 1] = P.seg_start[i] + segs[i].n;
   }
   P.ncols = (epi == EPI_SWIGLU) ? segs[0].n : P.seg_start[nseg];
-  return launch_big<128>(st, P);
+  // 128-row tiles, two workgroups per CU (a 256-row tile on 8 waves, one
+  // workgroup per CU, moves a third fewer bytes per product but measured
+  // slower: the per-step barrier then stalls the whole CU)
+  return launch_big<128, 256>(st, P);
 }
 
 }  // namespace ark

@@ -75,7 +75,8 @@ def test_dynquant_all_zero_tensor():
                                      (32, 1, 700, 2048), (4, 8, 256, 128), (1, 31, 4100, 256),
                                      (16, 1, 2048, 11008),
                                      # M >= 128: the large-tile prefill GEMM (ragged and whole tiles)
-                                     (2, 100, 2560, 2048), (1, 256, 512, 1024), (1, 130, 200, 11008)])
+                                     (2, 100, 2560, 2048), (1, 256, 512, 1024), (1, 130, 200, 11008),
+                                     (3, 101, 700, 2048), (1, 600, 513, 1024)])
 def test_qlinear_bit_exact(use_gemm, B, R, n, k):
     if use_gemm == 0 and B * R > 4:
         pytest.skip("the decode GEMV takes at most 4 rows")
