@@ -227,10 +227,12 @@ int ark_greedy_decode(const ark_model* m, int32_t B, int32_t* token_ids,
 /* --------------------------------------------------------- test access -- */
 
 /* Dynamic quantisation of B tensors x[b] of R*K fp32 values each (one
- * (s, z) per tensor), with the kernels of the prefill path.  codes
- * [B][R][K] uint8, scale [B] fp32, zp [B] int32.  workspace >=
- * 16 * B * (R + 1) bytes.  Errors: ARK_E_NULL, ARK_E_SHAPE,
- * ARK_E_WORKSPACE. */
+ * (s, z) per tensor; model card "Files": activations quantised at run
+ * time), with the kernels of the prefill path.  codes [B][R][K] uint8,
+ * scale [B] fp32, zp [B] int32.  B <= 64.  workspace >=
+ * ark_test_dynquant_workspace_bytes() bytes.  Errors: ARK_E_NULL,
+ * ARK_E_SHAPE, ARK_E_WORKSPACE. */
+size_t ark_test_dynquant_workspace_bytes(void);
 int ark_test_dynquant(int32_t B, int32_t R, int32_t K, const float* x, uint8_t* codes,
                       float* scale, int32_t* zp, void* workspace, size_t workspace_bytes,
                       void* stream);
@@ -249,6 +251,40 @@ int ark_test_qlinear(int32_t B, int32_t R, const uint8_t* codes, const float* sc
                      const uint8_t* zp, const ark_qlinear* W, int32_t* acc, float* y,
                      int32_t use_gemm, void* workspace, size_t workspace_bytes,
                      void* stream);
+
+/* SwiGLU half of the MLP on given codes, as the prefill runs it (cookbook
+ * "ARK-ASR-3B" introduction: Qwen2 MLP; model card "Files": int8 MatMuls on
+ * dynamically quantised activations): y = silu(gate(x)) * up(x) with rows r
+ * of sequence b = r / R using (scale[b], zp[b]) for both products, plus the
+ * per-sequence min / max of y that the next dynamic quantisation takes
+ * (produced inside the GEMM where the dispatch allows it).  codes
+ * [B*R][k] uint8; gate, up: [n][k] with equal shapes, k % 64 == 0; y
+ * [B*R][n] fp32; seq_min, seq_max [B] fp32.  B <= 64.  workspace >=
+ * ark_test_gate_up_workspace_bytes(B, R, k).  Errors: ARK_E_NULL,
+ * ARK_E_SHAPE, ARK_E_WORKSPACE. */
+size_t ark_test_gate_up_workspace_bytes(int32_t B, int32_t R, int32_t k);
+int ark_test_gate_up(int32_t B, int32_t R, const uint8_t* codes, const float* scale,
+                     const uint8_t* zp, const ark_qlinear* gate, const ark_qlinear* up, float* y,
+                     float* seq_min, float* seq_max, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* Full-cache GQA attention of B sequences of S rows, as the decoder runs it
+ * (model card "ark-asr-3b-onnx", section "Shapes": row i of sequence b
+ * sits at cache_position[b] + i and sees every cache row up to its own,
+ * rows [p, p + S) taken from this call's deltas), plus the per-sequence
+ * min / max of the output.  head_dim 128, n_heads / n_kv_heads <= 8, T a
+ * multiple of 32 up to 8192; q [B*S][n_heads*128]; k_cache,
+ * v_cache [B][T][n_kv_heads][128]; k_delta, v_delta [B*S][n_kv_heads][128];
+ * out [B*S][n_heads*128] fp32; seq_min, seq_max [B].  cache_position is
+ * host memory.  workspace >= ark_test_attention_workspace_bytes(B, S,
+ * n_heads, T).  Errors: ARK_E_NULL, ARK_E_SHAPE, ARK_E_RANGE (a sequence
+ * that does not fit in T), ARK_E_WORKSPACE. */
+size_t ark_test_attention_workspace_bytes(int32_t B, int32_t S, int32_t n_heads, int32_t T);
+int ark_test_attention(int32_t B, int32_t S, int32_t n_heads, int32_t n_kv_heads, int32_t T,
+                       const int32_t* cache_position, const float* q, const float* k_cache,
+                       const float* v_cache, const float* k_delta, const float* v_delta,
+                       float* out, float* seq_min, float* seq_max, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------- instrumentation ---- */
 

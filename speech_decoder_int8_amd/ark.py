@@ -72,6 +72,13 @@ _SIGS = {
     "ark_test_qlinear_workspace_bytes": (C.c_size_t, [I32, I32, I32]),
     "ark_test_qlinear": (C.c_int, [I32, I32, P, P, P, C.POINTER(ArkQLinear), P, P, I32, P,
                                    C.c_size_t, P]),
+    "ark_test_dynquant_workspace_bytes": (C.c_size_t, []),
+    "ark_test_gate_up_workspace_bytes": (C.c_size_t, [I32, I32, I32]),
+    "ark_test_gate_up": (C.c_int, [I32, I32, P, P, P, C.POINTER(ArkQLinear), C.POINTER(ArkQLinear),
+                                   P, P, P, P, C.c_size_t, P]),
+    "ark_test_attention_workspace_bytes": (C.c_size_t, [I32, I32, I32, I32]),
+    "ark_test_attention": (C.c_int, [I32, I32, I32, I32, I32, C.POINTER(C.c_int32), P, P, P, P, P,
+                                     P, P, P, P, C.c_size_t, P]),
     "ark_profile_arm": (C.c_int, [PP, I32]),
     "ark_profile_count": (C.c_int32, []),
     "ark_dominant_kernel": (C.c_char_p, []),
@@ -336,7 +343,7 @@ def test_dynquant(x, stream=None):
     codes = torch.empty((B, R, K), dtype=torch.uint8, device=x.device)
     scale = torch.empty(B, dtype=torch.float32, device=x.device)
     zp = torch.empty(B, dtype=torch.int32, device=x.device)
-    ws = torch.empty(16 * B * (R + 1), dtype=torch.uint8, device=x.device)
+    ws = torch.empty(lib().ark_test_dynquant_workspace_bytes(), dtype=torch.uint8, device=x.device)
     _check("ark_test_dynquant", lib().ark_test_dynquant(B, R, K, _ptr(x), _ptr(codes), _ptr(scale),
                                                          _ptr(zp), _ptr(ws), ws.numel(), _stream(stream)))
     return codes, scale, zp
@@ -357,6 +364,46 @@ def test_qlinear(codes, scale, zp, W: QLinear, use_gemm, stream=None):
                                                        _ptr(acc), _ptr(y), int(use_gemm), _ptr(ws),
                                                        ws.numel(), _stream(stream)))
     return acc, y
+
+
+def test_gate_up(codes, scale, zp, gate: QLinear, up: QLinear, stream=None):
+    """codes [B][R][k] uint8, scale [B], zp [B] uint8 -> (y [B*R][n] fp32 =
+    silu(gate) * up, seq_min [B], seq_max [B] of y) as the prefill computes them."""
+    import torch
+    B, R, k = codes.shape
+    n = gate.codes.shape[0]
+    y = torch.empty((B * R, n), dtype=torch.float32, device=codes.device)
+    lo = torch.empty(B, dtype=torch.float32, device=codes.device)
+    hi = torch.empty(B, dtype=torch.float32, device=codes.device)
+    ws = torch.empty(lib().ark_test_gate_up_workspace_bytes(B, R, k), dtype=torch.uint8,
+                     device=codes.device)
+    gc, uc = gate.c(), up.c()
+    _check("ark_test_gate_up", lib().ark_test_gate_up(B, R, _ptr(codes), _ptr(scale), _ptr(zp),
+                                                       C.byref(gc), C.byref(uc), _ptr(y), _ptr(lo),
+                                                       _ptr(hi), _ptr(ws), ws.numel(),
+                                                       _stream(stream)))
+    return y, lo, hi
+
+
+def test_attention(q, k_cache, v_cache, k_delta, v_delta, pos, n_kv_heads: int, stream=None):
+    """q [B][S][NH*128]; caches [B][T][NKV][128]; deltas [B][S][NKV][128];
+    pos: B host ints -> (out [B*S][NH*128], seq_min [B], seq_max [B])."""
+    import torch
+    B, S, QD = q.shape
+    NH = QD // 128
+    T = k_cache.shape[1]
+    out = torch.empty((B * S, QD), dtype=torch.float32, device=q.device)
+    lo = torch.empty(B, dtype=torch.float32, device=q.device)
+    hi = torch.empty(B, dtype=torch.float32, device=q.device)
+    ws = torch.empty(lib().ark_test_attention_workspace_bytes(B, S, NH, T), dtype=torch.uint8,
+                     device=q.device)
+    p = (C.c_int32 * B)(*[int(v) for v in pos])
+    _check("ark_test_attention", lib().ark_test_attention(B, S, NH, n_kv_heads, T, p, _ptr(q),
+                                                           _ptr(k_cache), _ptr(v_cache),
+                                                           _ptr(k_delta), _ptr(v_delta), _ptr(out),
+                                                           _ptr(lo), _ptr(hi), _ptr(ws), ws.numel(),
+                                                           _stream(stream)))
+    return out, lo, hi
 
 
 # ------------------------------------------------------- instrumentation --

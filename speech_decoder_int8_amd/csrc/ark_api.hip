@@ -19,7 +19,7 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
 struct Plan {
-  size_t x, h, codes, qkv, q, attn, a, rmin, rmax, qs, qz, part, done, gsk, mega, total;
+  size_t x, rs, codes, qkv, q, attn, a, stats, qs, qz, part, done, gsk, mega, total;
 };
 
 bool use_mega(const ark_dims& d, int B, int S) {
@@ -44,14 +44,13 @@ Plan plan(const ark_dims& d, int B, int S) {
     return at;
   };
   p.x = take(R * H * 4);
-  p.h = take(R * H * 4);
+  p.rs = take(R * 8);
   p.codes = take(R * Kmax);
   p.qkv = take(R * (Q + 2 * KV) * 4);
   p.q = take(R * Q * 4);
   p.attn = take(R * Q * 4);
   p.a = take(R * I * 4);
-  p.rmin = take(R * 4);
-  p.rmax = take(R * 4);
+  p.stats = take(2 * (size_t)kStatsSetInts * 4);
   p.qs = take((size_t)std::max(B, 64) * 4);
   p.qz = take((size_t)std::max(B, 64) * 4);
   // decode-only regions are always reserved, so a workspace sized for a
@@ -180,19 +179,23 @@ int run_forward(const ark_model* m, int B, int S, float* x, const int32_t* pos_h
   // one row per sequence: norm and quantisation fused per row
   const bool rowq = S == 1 && norm_quant_row_supported(H) && norm_quant_row_supported(Q) &&
                     norm_quant_row_supported(I);
-  float* h = (float*)(ws + p.h);
+  double* rs = (double*)(ws + p.rs);
   int8_t* codes = (int8_t*)(ws + p.codes);
   float* qkv = (float*)(ws + p.qkv);
   float* q = (float*)(ws + p.q);
   float* attn = (float*)(ws + p.attn);
   float* a = (float*)(ws + p.a);
-  float* rmin = (float*)(ws + p.rmin);
-  float* rmax = (float*)(ws + p.rmax);
+  // per-sequence activation ranges: two sets filled in turn, each producer
+  // clearing the other set for the producer after it
+  int* stw = (int*)(ws + p.stats);
+  const SeqStats sa = {stw, stw + kStatsSetInts, B};
+  const SeqStats sb = {stw + kStatsSetInts, stw, B};
   float* qs = (float*)(ws + p.qs);
   int* qz = (int*)(ws + p.qz);
   void* part = ws + p.part;
   void* gsk = ws + p.gsk;  // few-row GEMM scratch
   HIP_TRY(gemm_skinny_reset(st, gsk));
+  if (!gemv && !rowq) HIP_TRY(launch_seq_stats_init(st, sa.cur));
   PosArgs pos;
   memset(&pos, 0, sizeof(pos));
   for (int b = 0; b < B; ++b) pos.p[b] = pos_host[b];
@@ -213,12 +216,14 @@ int run_forward(const ark_model* m, int B, int S, float* x, const int32_t* pos_h
       HIP_TRY(launch_norm_quant_row(st, B, H, x, H, L.ln1, d.rms_eps, codes, qs, qz));
       HIP_TRY(launch_gemm(st, R, H, codes, qs, qz, S, qkvs, 3, EPI_STORE, nullptr, gsk));
     } else {
-      HIP_TRY(launch_rmsnorm_rows(st, R, H, x, H, L.ln1, d.rms_eps, h, rmin, rmax));
-      HIP_TRY(launch_quant_rows(st, B, S, H, h, rmin, rmax, codes, nullptr, qs, qz));
+      HIP_TRY(launch_row_stats(st, R, H, S, x, H, L.ln1, d.rms_eps, rs, sa));
+      HIP_TRY(launch_quant_seq(st, R, H, S, x, H, rs, L.ln1, sa.cur, codes, nullptr, qs, qz));
       HIP_TRY(launch_gemm(st, R, H, codes, qs, qz, S, qkvs, 3, EPI_STORE, nullptr, gsk));
     }
     HIP_TRY(launch_rope(st, B, S, NH, NKV, qkv, m->rope_cos, m->rope_sin, pos, q, kdl, vdl));
-    HIP_TRY(launch_attention(st, B, S, NH, NKV, T, q, kc[l], vc[l], kdl, vdl, pos, attn, part));
+    const bool att_stats = !gemv && !rowq && attention_stats(S, NH, NKV);
+    HIP_TRY(launch_attention(st, B, S, NH, NKV, T, q, kc[l], vc[l], kdl, vdl, pos, attn, part,
+                             att_stats ? &sb : nullptr));
     if (gemv) {
       HIP_TRY(launch_gemv(st, B, Q, attn, Q, nullptr, 0.0, os, 1, EPI_RESID));
       prof_begin(st, B == 1);
@@ -233,14 +238,17 @@ int run_forward(const ark_model* m, int B, int S, float* x, const int32_t* pos_h
       HIP_TRY(launch_norm_quant_row(st, B, I, a, I, nullptr, 0.0, codes, qs, qz));
       HIP_TRY(launch_gemm(st, R, I, codes, qs, qz, S, ds, 1, EPI_RESID, nullptr, gsk));
     } else {
-      HIP_TRY(launch_rowminmax(st, R, Q, attn, rmin, rmax));
-      HIP_TRY(launch_quant_rows(st, B, S, Q, attn, rmin, rmax, codes, nullptr, qs, qz));
+      if (!att_stats) HIP_TRY(launch_row_stats(st, R, Q, S, attn, Q, nullptr, 0.0, nullptr, sb));
+      HIP_TRY(launch_quant_seq(st, R, Q, S, attn, Q, nullptr, nullptr, sb.cur, codes, nullptr, qs,
+                               qz));
       HIP_TRY(launch_gemm(st, R, Q, codes, qs, qz, S, os, 1, EPI_RESID, nullptr, gsk));
-      HIP_TRY(launch_rmsnorm_rows(st, R, H, x, H, L.ln2, d.rms_eps, h, rmin, rmax));
-      HIP_TRY(launch_quant_rows(st, B, S, H, h, rmin, rmax, codes, nullptr, qs, qz));
-      HIP_TRY(launch_gemm(st, R, H, codes, qs, qz, S, gus, 2, EPI_SWIGLU, nullptr, gsk));
-      HIP_TRY(launch_rowminmax(st, R, I, a, rmin, rmax));
-      HIP_TRY(launch_quant_rows(st, B, S, I, a, rmin, rmax, codes, nullptr, qs, qz));
+      HIP_TRY(launch_row_stats(st, R, H, S, x, H, L.ln2, d.rms_eps, rs, sa));
+      HIP_TRY(launch_quant_seq(st, R, H, S, x, H, rs, L.ln2, sa.cur, codes, nullptr, qs, qz));
+      const bool gu_stats = gemm_swiglu_stats(R, H, gsk);
+      HIP_TRY(launch_gemm(st, R, H, codes, qs, qz, S, gus, 2, EPI_SWIGLU, nullptr, gsk, false,
+                          gu_stats ? &sb : nullptr));
+      if (!gu_stats) HIP_TRY(launch_row_stats(st, R, I, S, a, I, nullptr, 0.0, nullptr, sb));
+      HIP_TRY(launch_quant_seq(st, R, I, S, a, I, nullptr, nullptr, sb.cur, codes, nullptr, qs, qz));
       HIP_TRY(launch_gemm(st, R, I, codes, qs, qz, S, ds, 1, EPI_RESID, nullptr, gsk));
     }
   }
@@ -255,8 +263,10 @@ int run_forward(const ark_model* m, int B, int S, float* x, const int32_t* pos_h
         HIP_TRY(launch_norm_quant_row(st, B, H, last, S * H, m->final_norm, d.rms_eps, codes, qs,
                                       qz));
       } else {
-        HIP_TRY(launch_rmsnorm_rows(st, B, H, last, S * H, m->final_norm, d.rms_eps, h, rmin, rmax));
-        HIP_TRY(launch_quant_rows(st, B, 1, H, h, rmin, rmax, codes, nullptr, qs, qz));
+        // set A is clear here: the last producer of the layers (if any) filled B
+        HIP_TRY(launch_row_stats(st, B, H, 1, last, S * H, m->final_norm, d.rms_eps, rs, sa));
+        HIP_TRY(launch_quant_seq(st, B, H, 1, last, S * H, rs, m->final_norm, sa.cur, codes,
+                                 nullptr, qs, qz));
       }
       HIP_TRY(launch_gemm(st, B, H, codes, qs, qz, 1, lm, 1, EPI_STORE, nullptr, gsk));
     }
@@ -543,17 +553,23 @@ const char* ark_dominant_kernel(void) {
   return "ark::mk::k_decode";
 }
 
+size_t ark_test_dynquant_workspace_bytes(void) { return 2 * (size_t)kStatsSetInts * 4; }
+
 int ark_test_dynquant(int32_t B, int32_t R, int32_t K, const float* x, uint8_t* codes,
                       float* scale, int32_t* zp, void* workspace, size_t workspace_bytes,
                       void* stream) {
   if (!x || !codes || !scale || !zp || !workspace) return ARK_E_NULL;
   if (B < 1 || R < 1 || K < 1) return ARK_E_SHAPE;
-  if (workspace_bytes < 16 * (size_t)B * (R + 1)) return ARK_E_WORKSPACE;
+  if (workspace_bytes < ark_test_dynquant_workspace_bytes()) return ARK_E_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
-  float* rmin = (float*)workspace;
-  float* rmax = rmin + (size_t)B * R;
-  if (launch_rowminmax(st, B * R, K, x, rmin, rmax) != hipSuccess) return ARK_E_HIP;
-  if (launch_quant_rows(st, B, R, K, x, rmin, rmax, nullptr, codes, scale, zp) != hipSuccess)
+  if (B > kMaxBatch) return ARK_E_SHAPE;
+  int* stw = (int*)workspace;
+  const SeqStats sa = {stw, stw + kStatsSetInts, B};
+  if (launch_seq_stats_init(st, sa.cur) != hipSuccess) return ARK_E_HIP;
+  if (launch_row_stats(st, B * R, K, R, x, K, nullptr, 0.0, nullptr, sa) != hipSuccess)
+    return ARK_E_HIP;
+  if (launch_quant_seq(st, B * R, K, R, x, K, nullptr, nullptr, sa.cur, nullptr, codes, scale,
+                       zp) != hipSuccess)
     return ARK_E_HIP;
   return ARK_OK;
 }
@@ -595,6 +611,94 @@ int ark_test_qlinear(int32_t B, int32_t R, const uint8_t* codes, const float* sc
     err = launch_gemv_codes(st, rows, W->k, sc, srow, zrow, &s, 1, EPI_STORE, acc);
   }
   return err == hipSuccess ? ARK_OK : ARK_E_HIP;
+}
+
+size_t ark_test_gate_up_workspace_bytes(int32_t B, int32_t R, int32_t k) {
+  if (B < 1 || R < 1 || k < 1) return 0;
+  const size_t rows = (size_t)B * R;
+  return align_up(rows * k) + 2 * align_up(rows * 4) + 3 * align_up((size_t)B * 4) +
+         ark_test_dynquant_workspace_bytes() + gemm_skinny_ws_bytes();
+}
+
+int ark_test_gate_up(int32_t B, int32_t R, const uint8_t* codes, const float* scale,
+                     const uint8_t* zp, const ark_qlinear* gate, const ark_qlinear* up, float* y,
+                     float* seq_min, float* seq_max, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  if (!codes || !scale || !zp || !gate || !up || !y || !seq_min || !seq_max || !workspace)
+    return ARK_E_NULL;
+  if (!gate->w || !gate->scale || !gate->colsum || !up->w || !up->scale || !up->colsum)
+    return ARK_E_NULL;
+  if (B < 1 || R < 1 || B > kMaxBatch) return ARK_E_SHAPE;
+  const int n = gate->n, k = gate->k;
+  if (up->n != n || up->k != k || n < 1 || k < 64 || k % 64) return ARK_E_SHAPE;
+  if (workspace_bytes < ark_test_gate_up_workspace_bytes(B, R, k)) return ARK_E_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const int rows = B * R;
+  char* ws = (char*)workspace;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    char* at = ws + o;
+    o += align_up(bytes);
+    return at;
+  };
+  int8_t* sc = (int8_t*)take((size_t)rows * k);
+  float* srow = (float*)take((size_t)rows * 4);
+  int* zrow = (int*)take((size_t)rows * 4);
+  float* sseq = (float*)take((size_t)B * 4);
+  int* zseq = (int*)take((size_t)B * 4);
+  int8_t* junk = (int8_t*)take((size_t)B * 4);
+  int* stw = (int*)take(ark_test_dynquant_workspace_bytes());
+  void* gsk = take(gemm_skinny_ws_bytes());
+  const SeqStats sa = {stw, stw + kStatsSetInts, B};
+  // shifted codes, then the per-sequence (s, z) as one-column "rows"
+  HIP_TRY(launch_test_codes(st, rows, k, R, codes, sc, scale, zp, srow, zrow));
+  HIP_TRY(launch_test_codes(st, B, 1, 1, codes, junk, scale, zp, sseq, zseq));
+  HIP_TRY(gemm_skinny_reset(st, gsk));
+  HIP_TRY(launch_seq_stats_init(st, sa.cur));
+  Seg gus[2] = {seg_of(*gate, y, n), seg_of(*up, y, n)};
+  const bool fused = gemm_swiglu_stats(rows, k, gsk);
+  HIP_TRY(launch_gemm(st, rows, k, sc, sseq, zseq, R, gus, 2, EPI_SWIGLU, nullptr, gsk, false,
+                      fused ? &sa : nullptr));
+  if (!fused) HIP_TRY(launch_row_stats(st, rows, n, R, y, n, nullptr, 0.0, nullptr, sa));
+  HIP_TRY(launch_seq_stats_read(st, sa.cur, B, seq_min, seq_max));
+  return ARK_OK;
+}
+
+size_t ark_test_attention_workspace_bytes(int32_t B, int32_t S, int32_t n_heads, int32_t T) {
+  if (B < 1 || S < 1 || n_heads < 1 || T < 1) return 0;
+  return align_up(attention_ws_bytes(B, S, n_heads, T)) + ark_test_dynquant_workspace_bytes();
+}
+
+int ark_test_attention(int32_t B, int32_t S, int32_t n_heads, int32_t n_kv_heads, int32_t T,
+                       const int32_t* cache_position, const float* q, const float* k_cache,
+                       const float* v_cache, const float* k_delta, const float* v_delta,
+                       float* out, float* seq_min, float* seq_max, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (!cache_position || !q || !k_cache || !v_cache || !k_delta || !v_delta || !out || !seq_min ||
+      !seq_max || !workspace)
+    return ARK_E_NULL;
+  if (B < 1 || B > kMaxBatch || S < 1 || n_kv_heads < 1 || n_heads % n_kv_heads ||
+      n_heads / n_kv_heads > 8 || T < 32 || T % 32 || T > 8192)
+    return ARK_E_SHAPE;
+  for (int b = 0; b < B; ++b)
+    if (cache_position[b] < 0 || cache_position[b] + S > T) return ARK_E_RANGE;
+  if (workspace_bytes < ark_test_attention_workspace_bytes(B, S, n_heads, T))
+    return ARK_E_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  int* stw = (int*)(ws + align_up(attention_ws_bytes(B, S, n_heads, T)));
+  const SeqStats sa = {stw, stw + kStatsSetInts, B};
+  PosArgs pos;
+  memset(&pos, 0, sizeof(pos));
+  for (int b = 0; b < B; ++b) pos.p[b] = cache_position[b];
+  HIP_TRY(launch_seq_stats_init(st, sa.cur));
+  const bool fused = attention_stats(S, n_heads, n_kv_heads);
+  HIP_TRY(launch_attention(st, B, S, n_heads, n_kv_heads, T, q, k_cache, v_cache, k_delta,
+                           v_delta, pos, out, ws, fused ? &sa : nullptr));
+  const int Q = n_heads * kHeadDim;
+  if (!fused) HIP_TRY(launch_row_stats(st, B * S, Q, S, out, Q, nullptr, 0.0, nullptr, sa));
+  HIP_TRY(launch_seq_stats_read(st, sa.cur, B, seq_min, seq_max));
+  return ARK_OK;
 }
 
 }  // extern "C"

@@ -170,5 +170,7 @@ __device__ __forceinline__ int float_to_ordered(float f) {
 __device__ __forceinline__ float ordered_to_float(int i) {
   return __int_as_float(i >= 0 ? i : i ^ 0x7fffffff);
 }
+constexpr int kOrdPosInf = 0x7f800000;         // float_to_ordered(+inf)
+constexpr int kOrdNegInf = (int)0x807fffffu;  // float_to_ordered(-inf)
 
 }  // namespace ark

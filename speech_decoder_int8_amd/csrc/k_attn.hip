@@ -10,7 +10,6 @@
 // One workgroup serves the 8 query heads of one KV head, so each K/V chunk is
 // staged in LDS once for all of them.  Decode (S = 1) splits T across
 // workgroups and merges the partial softmax states in a second kernel.
-#include <stdlib.h>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -237,9 +236,14 @@ size_t attention_ws_bytes(int B, int S, int NH, int T) {
   return (size_t)B * NH * decode_split(T) * kPart * sizeof(double);
 }
 
+bool attention_stats(int S, int NH, int NKV) {
+  return S > 1 && attention_prefill_supported(NH, NKV);
+}
+
 hipError_t launch_attention(hipStream_t st, int B, int S, int NH, int NKV, int T, const float* q,
                             const float* k_cache, const float* v_cache, const float* k_delta,
-                            const float* v_delta, const PosArgs& pos, float* out, void* ws) {
+                            const float* v_delta, const PosArgs& pos, float* out, void* ws,
+                            const SeqStats* stats) {
   AttnParams P;
   P.B = B;
   P.S = S;
@@ -261,9 +265,9 @@ hipError_t launch_attention(hipStream_t st, int B, int S, int NH, int NKV, int T
     hipLaunchKernelGGL((k_attn<1, 32>), dim3(P.nsplit, B * NKV), dim3(256), 0, st, P);
     hipLaunchKernelGGL(k_attn_combine, dim3(B * NH), dim3(128), 0, st, 1, NH, P.nsplit, P.part,
                        out);
-  } else if (attention_prefill_supported(NH, NKV) && !getenv("ARK_ATTN_VALU")) {
+  } else if (attention_prefill_supported(NH, NKV)) {
     return launch_attention_prefill(st, B, S, NH, NKV, T, q, k_cache, v_cache, k_delta, v_delta,
-                                    pos, out);
+                                    pos, out, stats);
   } else {
     P.nsplit = 1;
     P.tsplit = T;

@@ -42,6 +42,7 @@ struct Attn2Params {
   const float* vd;
   PosArgs pos;
   float* out;
+  SeqStats stats;  // per-sequence min/max of out (cur == nullptr: off)
 };
 
 __global__ __launch_bounds__(512) void k_attn_prefill(Attn2Params P) {
@@ -50,6 +51,7 @@ __global__ __launch_bounds__(512) void k_attn_prefill(Attn2Params P) {
   float* Ks = (float*)smem;                      // [KC][KP]
   float* Vs = Ks + KC * KP;                      // [KC][VP]
   double* Pt = (double*)(Vs + KC * VP);          // [G][KC keys][QT rows]
+  if (P.stats.cur) stats_clear_other(P.stats);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nthr = blockDim.x;
@@ -164,13 +166,25 @@ __global__ __launch_bounds__(512) void k_attn_prefill(Attn2Params P) {
         o[d] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)vr[16 * d], pb, o[d], 0, 0, 0);
     }
   }
-  if (!rowok) return;
   // o[d][i] = O^T[dim 16 d + 4 i + q4][qrow]
   float* dst = P.out + ((size_t)(b * S + qrow) * P.NH + h) * kHeadDim;
+  float lo = INFINITY, hi = -INFINITY;
+  if (rowok) {
 #pragma unroll
-  for (int d = 0; d < 8; ++d)
+    for (int d = 0; d < 8; ++d)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[16 * d + 4 * i + q4] = (float)(o[d][i] / l);
+      for (int i = 0; i < 4; ++i) {
+        const float y = (float)(o[d][i] / l);
+        dst[16 * d + 4 * i + q4] = y;
+        lo = fminf(lo, y);
+        hi = fmaxf(hi, y);
+      }
+  }
+  if (P.stats.cur) {
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    if (lane == 0) stats_fold(P.stats, blockIdx.x * 8 + wave, b, lo, hi);
+  }
 }
 
 bool attention_prefill_supported(int NH, int NKV) {
@@ -180,7 +194,7 @@ bool attention_prefill_supported(int NH, int NKV) {
 hipError_t launch_attention_prefill(hipStream_t st, int B, int S, int NH, int NKV, int T,
                                     const float* q, const float* k_cache, const float* v_cache,
                                     const float* k_delta, const float* v_delta,
-                                    const PosArgs& pos, float* out) {
+                                    const PosArgs& pos, float* out, const SeqStats* stats) {
   static bool attr = false;
   if (!attr) {
     const hipError_t e = hipFuncSetAttribute((const void*)k_attn_prefill,
@@ -189,7 +203,7 @@ hipError_t launch_attention_prefill(hipStream_t st, int B, int S, int NH, int NK
     if (e != hipSuccess) return e;
     attr = true;
   }
-  Attn2Params P;
+  Attn2Params P = {};
   P.B = B;
   P.S = S;
   P.NH = NH;
@@ -204,6 +218,7 @@ hipError_t launch_attention_prefill(hipStream_t st, int B, int S, int NH, int NK
   P.vd = v_delta;
   P.pos = pos;
   P.out = out;
+  if (stats) P.stats = *stats;
   const int lds = a2::KC * a2::KP * 4 + a2::KC * a2::VP * 4 + P.G * a2::KC * a2::QT * 8;
   hipLaunchKernelGGL(k_attn_prefill, dim3(B * NKV * P.nqt), dim3(64 * P.G), lds, st, P);
   return hipGetLastError();

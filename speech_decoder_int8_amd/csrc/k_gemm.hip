@@ -184,9 +184,13 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
   }
 }
 
+bool gemm_swiglu_stats(int M, int K, const void* scratch) {
+  return !(scratch && gemm_skinny_supported(M, K)) && gemm_big_supported(M, K);
+}
+
 hipError_t launch_gemm(hipStream_t st, int M, int K, const int8_t* codes, const float* s,
                        const int* z, int rows_per_seq, const Seg* segs, int nseg, Epi epi,
-                       int32_t* acc_out, void* scratch, bool tiled_only) {
+                       int32_t* acc_out, void* scratch, bool tiled_only, const SeqStats* stats) {
   if (!tiled_only && scratch && gemm_skinny_supported(M, K))
     return launch_gemm_skinny(st, M, K, codes, s, z, rows_per_seq, segs, nseg, epi, acc_out,
                               scratch);
@@ -207,7 +211,7 @@ hipError_t launch_gemm(hipStream_t st, int M, int K, const int8_t* codes, const 
   }
   P.ncols = (epi == EPI_SWIGLU) ? segs[0].n : P.seg_start[nseg];
   if (!tiled_only && gemm_big_supported(M, K))
-    return launch_gemm_big(st, M, K, codes, s, z, rows_per_seq, segs, nseg, epi, acc_out);
+    return launch_gemm_big(st, M, K, codes, s, z, rows_per_seq, segs, nseg, epi, acc_out, stats);
   if (M <= 32) {
     constexpr int BM = 32, BN = 128;
     const int tn = epi == EPI_SWIGLU ? BN / 2 : BN;

@@ -44,6 +44,7 @@ struct Gemm2Params {
   Seg seg[3];
   int seg_start[4];
   int32_t* acc_out;
+  SeqStats stats;  // EPI_SWIGLU: per-sequence min/max of the output (cur == nullptr: off)
 };
 
 // 16-byte chunk c of tile row r sits at chunk c ^ ((r >> 2) & 3): the 16
@@ -88,6 +89,7 @@ __global__ __launch_bounds__(NTH, NTH == 256 ? 2 : 1) void k_gemm_big(Gemm2Param
   // contiguous run of tiles, and runs walk groups of 8 m-tiles x all
   // n-tiles m-fastest, so the ~64 concurrent workgroups of an XCD share
   // about 8 activation and 8 weight tiles in their L2.
+  if (P.stats.cur) stats_clear_other(P.stats);
   const int per = (P.tiles + 7) / 8;
   const int t = (blockIdx.x % 8) * per + blockIdx.x / 8;
   if (t >= P.tiles) return;
@@ -251,10 +253,14 @@ __global__ __launch_bounds__(NTH, NTH == 256 ? 2 : 1) void k_gemm_big(Gemm2Param
       rs[i][q] = P.qs[b];
       rz[i][q] = 128 - P.qz[b];
     }
+  // SwiGLU outputs' min / max per row of this lane (neutral where no output)
+  float elo[FM][16], ehi[FM][16];
 #pragma clang loop unroll(full)
   for (int i = 0; i < FM; ++i) {
 #pragma clang loop unroll(full)
     for (int v = 0; v < 16; ++v) {
+      elo[i][v] = INFINITY;
+      ehi[i][v] = -INFINITY;
       const int row = rbase + i * 32 + (v >> 2) * 8 + (v & 3);
       if (row >= P.M) continue;
       float s = rs[i][v >> 2];
@@ -272,7 +278,10 @@ __global__ __launch_bounds__(NTH, NTH == 256 ? 2 : 1) void k_gemm_big(Gemm2Param
             const float g = dequant(agc, s, csw[j]);
             const float u = dequant(acc[i][j + 1][v] + zc * ucs[j / 2], s, usw[j / 2]);
             const double gd = g;
-            cout[j][(size_t)row * cldo[j]] = (float)(gd / (1.0 + exp(-gd)) * (double)u);
+            const float y = (float)(gd / (1.0 + exp(-gd)) * (double)u);
+            cout[j][(size_t)row * cldo[j]] = y;
+            elo[i][v] = fminf(elo[i][v], y);
+            ehi[i][v] = fmaxf(ehi[i][v], y);
             if (P.acc_out) P.acc_out[(size_t)row * P.ncols + nb + (wn * 2 + j / 2) * 32 + lr] = agc;
           }
         }
@@ -297,6 +306,30 @@ __global__ __launch_bounds__(NTH, NTH == 256 ? 2 : 1) void k_gemm_big(Gemm2Param
           }
         }
       }
+    }
+  }
+  if (swiglu && P.stats.cur) {
+    // fold this wave's 64 rows into their sequences (one or two unless
+    // sequences are shorter than the wave's rows): lanes' values of rows in
+    // sequence b, then the wave's min / max, one atomic pair per sequence
+    const int r0 = m0 + wm * RW;
+    const int rl = min(r0 + RW, P.M) - 1;
+    const int rps = P.rows_per_seq;
+    for (int b = r0 / rps; b <= rl / rps; ++b) {
+      const int ra = b * rps, rb = ra + rps;
+      float lo = INFINITY, hi = -INFINITY;
+#pragma clang loop unroll(full)
+      for (int i = 0; i < FM; ++i)
+#pragma clang loop unroll(full)
+        for (int v = 0; v < 16; ++v) {
+          const int row = rbase + i * 32 + (v >> 2) * 8 + (v & 3);
+          const bool in = row >= ra && row < rb;
+          lo = fminf(lo, in ? elo[i][v] : INFINITY);
+          hi = fmaxf(hi, in ? ehi[i][v] : -INFINITY);
+        }
+      lo = wave_min(lo);
+      hi = wave_max(hi);
+      if (lane == 0) stats_fold(P.stats, blockIdx.x * NWV + wave, b, lo, hi);
     }
   }
 }
@@ -325,8 +358,9 @@ bool gemm_big_supported(int M, int K) { return M >= 128 && K % g2::BK == 0; }
 
 hipError_t launch_gemm_big(hipStream_t st, int M, int K, const int8_t* codes, const float* s,
                            const int* z, int rows_per_seq, const Seg* segs, int nseg, Epi epi,
-                           int32_t* acc_out) {
+                           int32_t* acc_out, const SeqStats* stats) {
   Gemm2Params P = {};
+  if (stats && epi == EPI_SWIGLU) P.stats = *stats;
   P.M = M;
   P.K = K;
   P.A = codes;

@@ -1,5 +1,5 @@
-// Row-parallel RMSNorm and per-sequence dynamic quantisation (prefill and
-// batched paths).  The decode GEMV fuses the same arithmetic into its
+// Row-parallel RMSNorm statistics and per-sequence dynamic quantisation
+// (prefill and batched paths).  The decode GEMV fuses the same arithmetic into its
 // prologue; both use the helpers of common.hpp so the results agree.
 #include <float.h>
 
@@ -8,117 +8,263 @@
 
 namespace ark {
 
+__global__ void k_seq_stats_init(int* set) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < kStatsSetInts) set[t] = (t % (2 * kMaxBatch)) < kMaxBatch ? kOrdPosInf : kOrdNegInf;
+}
+
+hipError_t launch_seq_stats_init(hipStream_t st, int* set) {
+  hipLaunchKernelGGL(k_seq_stats_init, dim3((kStatsSetInts + 255) / 256), dim3(256), 0, st, set);
+  return hipGetLastError();
+}
+
+// one wave per sequence
+__global__ void k_seq_stats_read(const int* set, int n, float* flo, float* fhi) {
+  const int b = blockIdx.x;
+  float lo, hi;
+  stats_range(set, b, lo, hi);
+  if (threadIdx.x == 0) {
+    flo[b] = lo;
+    fhi[b] = hi;
+  }
+}
+
+hipError_t launch_seq_stats_read(hipStream_t st, const int* set, int n, float* flo, float* fhi) {
+  hipLaunchKernelGGL(k_seq_stats_read, dim3(n), dim3(64), 0, st, set, n, flo, fhi);
+  return hipGetLastError();
+}
+
+// Row kernels.  Statistics: rows of K <= 256 * RV floats (16-byte aligned)
+// take one wave each, four rows per workgroup, the row held in registers as
+// float4 per lane (columns 4 * lane + 256 * c); other rows take a workgroup
+// each and read the row again where they need it twice.  Quantisation: one
+// wave per row when there are many rows, else a workgroup per row.
+constexpr int kRowsPerBlock = 4;
+constexpr int kStatsRV = 8;  // float4 per lane: rows up to 2048 floats
+
+__device__ __forceinline__ float4 ld4(const float* p) { return *(const float4*)p; }
+
 // Qwen2 RMSNorm (cookbook "ARK-ASR-3B" introduction: dense Qwen2 decoder):
-// h = x / sqrt(mean(x^2) + eps) * g, fp64 inside, fp32 out; also the row's
-// min and max of h for the quantiser.  One workgroup per row.
-__global__ __launch_bounds__(256) void k_rmsnorm_rows(int H, const float* __restrict__ x, int ldx,
-                                                      const float* __restrict__ g, double eps,
-                                                      float* __restrict__ h,
-                                                      float* __restrict__ rmin,
-                                                      float* __restrict__ rmax) {
+// h = x / sqrt(mean(x^2) + eps) * g, fp64 inside, fp32 out.  Statistics
+// pass: rs = 1 / sqrt(mean(x^2) + eps) per row and the sequence's min/max of
+// h (or, without g, of x itself).
+template <int RV>
+__global__ __launch_bounds__(256) void k_row_stats(int R, int K, int rps,
+                                                   const float* __restrict__ x, int ldx,
+                                                   const float* __restrict__ g, double eps,
+                                                   double* __restrict__ rs_out, SeqStats S) {
+  stats_clear_other(S);
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (r >= R) return;
+  const float* xr = x + (size_t)r * ldx;
+  float lo = INFINITY, hi = -INFINITY;
+  {
+    float4 v[RV];
+#pragma unroll
+    for (int c = 0; c < RV; ++c) {
+      const int i = 4 * lane + 256 * c;
+      v[c] = i < K ? ld4(xr + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (g) {
+      double ss = 0.0;
+#pragma unroll
+      for (int c = 0; c < RV; ++c)
+        ss += (double)v[c].x * v[c].x + (double)v[c].y * v[c].y + (double)v[c].z * v[c].z +
+              (double)v[c].w * v[c].w;
+      ss = wave_sum(ss);
+      const double rs = 1.0 / sqrt(ss / (double)K + eps);
+      if (lane == 0) rs_out[r] = rs;
+#pragma unroll
+      for (int c = 0; c < RV; ++c) {
+        const int i = 4 * lane + 256 * c;
+        if (i < K) {
+          const float4 gg = ld4(g + i);
+          v[c].x = (float)(((double)v[c].x * rs) * (double)gg.x);
+          v[c].y = (float)(((double)v[c].y * rs) * (double)gg.y);
+          v[c].z = (float)(((double)v[c].z * rs) * (double)gg.z);
+          v[c].w = (float)(((double)v[c].w * rs) * (double)gg.w);
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < RV; ++c)
+      if (4 * lane + 256 * c < K) {
+        lo = fminf(lo, fminf(fminf(v[c].x, v[c].y), fminf(v[c].z, v[c].w)));
+        hi = fmaxf(hi, fmaxf(fmaxf(v[c].x, v[c].y), fmaxf(v[c].z, v[c].w)));
+      }
+  }
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  if (lane == 0) stats_fold(S, r, r / rps, lo, hi);
+}
+
+// workgroup per row: any K, stride and alignment (float4 accesses when VEC)
+template <bool VEC>
+__global__ __launch_bounds__(256) void k_row_stats_wide(int K, int rps,
+                                                        const float* __restrict__ x, int ldx,
+                                                        const float* __restrict__ g, double eps,
+                                                        double* __restrict__ rs_out, SeqStats S) {
   __shared__ double redd[4];
   __shared__ float redf[8];
-  const int r = blockIdx.x;
+  stats_clear_other(S);
+  const int r = blockIdx.x, t = threadIdx.x;
   const float* xr = x + (size_t)r * ldx;
-  double ss = 0.0;
-  for (int i = threadIdx.x; i < H; i += 256) {
-    const double v = xr[i];
-    ss += v * v;
+  double rs = 1.0;
+  if (g) {
+    double ss = 0.0;
+    if constexpr (VEC) {
+      for (int i = 4 * t; i < K; i += 1024) {
+        const float4 v = ld4(xr + i);
+        ss += (double)v.x * v.x + (double)v.y * v.y + (double)v.z * v.z + (double)v.w * v.w;
+      }
+    } else {
+      for (int i = t; i < K; i += 256) ss += (double)xr[i] * (double)xr[i];
+    }
+    ss = block_sum<256>(ss, redd);
+    rs = 1.0 / sqrt(ss / (double)K + eps);
+    if (t == 0) rs_out[r] = rs;
   }
-  ss = block_sum<256>(ss, redd);
-  const double rs = 1.0 / sqrt(ss / (double)H + eps);
   float lo = INFINITY, hi = -INFINITY;
-  float* hr = h + (size_t)r * H;
-  for (int i = threadIdx.x; i < H; i += 256) {
-    const float y = (float)(((double)xr[i] * rs) * (double)g[i]);
-    hr[i] = y;
-    lo = fminf(lo, y);
-    hi = fmaxf(hi, y);
+  if constexpr (VEC) {
+    for (int i = 4 * t; i < K; i += 1024) {
+      float4 v = ld4(xr + i);
+      if (g) {
+        const float4 gg = ld4(g + i);
+        v.x = (float)(((double)v.x * rs) * (double)gg.x);
+        v.y = (float)(((double)v.y * rs) * (double)gg.y);
+        v.z = (float)(((double)v.z * rs) * (double)gg.z);
+        v.w = (float)(((double)v.w * rs) * (double)gg.w);
+      }
+      lo = fminf(lo, fminf(fminf(v.x, v.y), fminf(v.z, v.w)));
+      hi = fmaxf(hi, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+    }
+  } else {
+    for (int i = t; i < K; i += 256) {
+      const float y = g ? (float)(((double)xr[i] * rs) * (double)g[i]) : xr[i];
+      lo = fminf(lo, y);
+      hi = fmaxf(hi, y);
+    }
   }
   block_minmax<256>(lo, hi, redf);
-  if (threadIdx.x == 0) {
-    rmin[r] = lo;
-    rmax[r] = hi;
-  }
+  if (t == 0) stats_fold(S, r, r / rps, lo, hi);
 }
 
-hipError_t launch_rmsnorm_rows(hipStream_t st, int R, int H, const float* x, int ldx,
-                               const float* gain, double eps, float* h, float* rmin, float* rmax) {
-  hipLaunchKernelGGL(k_rmsnorm_rows, dim3(R), dim3(256), 0, st, H, x, ldx, gain, eps, h, rmin,
-                     rmax);
+static bool vec_ok(const void* p, int K, int ld) {
+  return ((uintptr_t)p % 16) == 0 && K % 4 == 0 && ld % 4 == 0;
+}
+
+hipError_t launch_row_stats(hipStream_t st, int R, int K, int rps, const float* x, int ldx,
+                            const float* gain, double eps, double* rs_out, const SeqStats& S) {
+  const bool vec = vec_ok(x, K, ldx) && (!gain || (uintptr_t)gain % 16 == 0);
+  if (vec && K <= 256 * kStatsRV)
+    hipLaunchKernelGGL((k_row_stats<kStatsRV>), dim3((R + kRowsPerBlock - 1) / kRowsPerBlock),
+                       dim3(256), 0, st, R, K, rps, x, ldx, gain, eps, rs_out, S);
+  else if (vec)
+    hipLaunchKernelGGL((k_row_stats_wide<true>), dim3(R), dim3(256), 0, st, K, rps, x, ldx, gain,
+                       eps, rs_out, S);
+  else
+    hipLaunchKernelGGL((k_row_stats_wide<false>), dim3(R), dim3(256), 0, st, K, rps, x, ldx, gain,
+                       eps, rs_out, S);
   return hipGetLastError();
 }
 
-__global__ __launch_bounds__(256) void k_rowminmax(int K, const float* __restrict__ x,
-                                                   float* __restrict__ rmin,
-                                                   float* __restrict__ rmax) {
-  __shared__ float redf[8];
-  const int r = blockIdx.x;
-  const float* xr = x + (size_t)r * K;
-  float lo = INFINITY, hi = -INFINITY;
-  for (int i = threadIdx.x; i < K; i += 256) {
-    const float v = xr[i];
-    lo = fminf(lo, v);
-    hi = fmaxf(hi, v);
-  }
-  block_minmax<256>(lo, hi, redf);
-  if (threadIdx.x == 0) {
-    rmin[r] = lo;
-    rmax[r] = hi;
-  }
-}
-
-hipError_t launch_rowminmax(hipStream_t st, int R, int K, const float* x, float* rmin,
-                            float* rmax) {
-  hipLaunchKernelGGL(k_rowminmax, dim3(R), dim3(256), 0, st, K, x, rmin, rmax);
-  return hipGetLastError();
+__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
+  return (uint32_t)(a & 255) | ((uint32_t)(b & 255) << 8) | ((uint32_t)(c & 255) << 16) |
+         ((uint32_t)(d & 255) << 24);
 }
 
 // Dynamic uint8 quantisation with one (s, z) per sequence (model card "Files":
 // activations are quantised at run time; one scale per tensor, here per
-// sequence): reduce the row min/max of the sequence, then quantise row r.
-__global__ __launch_bounds__(256) void k_quant_rows(int S, int K, const float* __restrict__ x,
-                                                    const float* __restrict__ rmin,
-                                                    const float* __restrict__ rmax,
-                                                    int8_t* __restrict__ codes,
-                                                    uint8_t* __restrict__ codes_u8,
-                                                    float* __restrict__ s_out,
-                                                    int* __restrict__ z_out) {
-  __shared__ float redf[8];
-  const int r = blockIdx.x;
-  const int b = r / S;
-  float lo = INFINITY, hi = -INFINITY;
-  for (int i = threadIdx.x; i < S; i += 256) {
-    lo = fminf(lo, rmin[b * S + i]);
-    hi = fmaxf(hi, rmax[b * S + i]);
-  }
-  block_minmax<256>(lo, hi, redf);
+// sequence), from the sequence's min/max; h = fp32((x * rs) * g) is
+// recomputed with the statistics pass's arithmetic when rs is given.
+template <bool VEC, int WPR>
+__global__ __launch_bounds__(256) void k_quant_seq(int R, int K, int rps,
+                                                   const float* __restrict__ x, int ldx,
+                                                   const double* __restrict__ rs,
+                                                   const float* __restrict__ g,
+                                                   const int* __restrict__ set,
+                                                   int8_t* __restrict__ codes,
+                                                   uint8_t* __restrict__ codes_u8,
+                                                   float* __restrict__ s_out,
+                                                   int* __restrict__ z_out) {
+  constexpr int TPR = 64 * WPR;  // threads per row
+  const int lt = threadIdx.x % TPR;
+  const int r = blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  if (r >= R) return;
+  const int b = r / rps;
+  float lo, hi;
+  stats_range(set, b, lo, hi);
   const QParam p = quant_param(lo, hi);
-  if (threadIdx.x == 0 && r == b * S) {
+  if (lt == 0 && r == b * rps) {
     s_out[b] = p.s;
     z_out[b] = p.z;
   }
-  const float* xr = x + (size_t)r * K;
-  int8_t* cr = codes ? codes + (size_t)r * K : nullptr;
-  for (int i = threadIdx.x; i < K; i += 256) {
-    const int c = quant_code(xr[i], p);
-    if (codes) cr[i] = shift_code(c);
-    if (codes_u8) codes_u8[(size_t)r * K + i] = (uint8_t)c;
+  const float* xr = x + (size_t)r * ldx;
+  const double rr = rs ? rs[r] : 0.0;
+  if constexpr (VEC) {
+    // four float4 loads in flight per thread
+    for (int i0 = 4 * lt; i0 < K; i0 += 16 * TPR) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (i0 + 4 * TPR * u < K) v[u] = ld4(xr + i0 + 4 * TPR * u);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + 4 * TPR * u;
+        if (i >= K) continue;
+        if (rs) {
+          const float4 gg = ld4(g + i);
+          v[u].x = (float)(((double)v[u].x * rr) * (double)gg.x);
+          v[u].y = (float)(((double)v[u].y * rr) * (double)gg.y);
+          v[u].z = (float)(((double)v[u].z * rr) * (double)gg.z);
+          v[u].w = (float)(((double)v[u].w * rr) * (double)gg.w);
+        }
+        const int c0 = quant_code(v[u].x, p), c1 = quant_code(v[u].y, p);
+        const int c2 = quant_code(v[u].z, p), c3 = quant_code(v[u].w, p);
+        if (codes)
+          *(uint32_t*)(codes + (size_t)r * K + i) =
+              pack4(shift_code(c0), shift_code(c1), shift_code(c2), shift_code(c3));
+        if (codes_u8) *(uint32_t*)(codes_u8 + (size_t)r * K + i) = pack4(c0, c1, c2, c3);
+      }
+    }
+  } else {
+    for (int i = lt; i < K; i += TPR) {
+      const float y = rs ? (float)(((double)xr[i] * rr) * (double)g[i]) : xr[i];
+      const int c = quant_code(y, p);
+      if (codes) codes[(size_t)r * K + i] = shift_code(c);
+      if (codes_u8) codes_u8[(size_t)r * K + i] = (uint8_t)c;
+    }
   }
 }
 
-hipError_t launch_quant_rows(hipStream_t st, int B, int S, int K, const float* x,
-                             const float* rmin, const float* rmax, int8_t* codes,
-                             uint8_t* codes_u8, float* s_out, int* z_out) {
-  hipLaunchKernelGGL(k_quant_rows, dim3(B * S), dim3(256), 0, st, S, K, x, rmin, rmax, codes,
-                     codes_u8, s_out, z_out);
+hipError_t launch_quant_seq(hipStream_t st, int R, int K, int rps, const float* x, int ldx,
+                            const double* rs, const float* gain, const int* set, int8_t* codes,
+                            uint8_t* codes_u8, float* s_out, int* z_out) {
+  const bool vec = vec_ok(x, K, ldx) && (!codes || (uintptr_t)codes % 4 == 0) &&
+                   (!codes_u8 || (uintptr_t)codes_u8 % 4 == 0) &&
+                   (!rs || (uintptr_t)gain % 16 == 0);
+  // a wave per row once the rows fill the chip, else a workgroup per row
+  const bool wide = R < 1024;
+#define ARK_QUANT_LAUNCH(V, W)                                                                   \
+  hipLaunchKernelGGL((k_quant_seq<V, W>), dim3((R * W + 3) / 4), dim3(256), 0, st, R, K, rps, x, \
+                     ldx, rs, gain, set, codes, codes_u8, s_out, z_out)
+  if (vec && wide)
+    ARK_QUANT_LAUNCH(true, 4);
+  else if (vec)
+    ARK_QUANT_LAUNCH(true, 1);
+  else if (wide)
+    ARK_QUANT_LAUNCH(false, 4);
+  else
+    ARK_QUANT_LAUNCH(false, 1);
+#undef ARK_QUANT_LAUNCH
   return hipGetLastError();
 }
 
 // Decode form (one row per sequence, so the row is the whole tensor of its
 // sequence): RMSNorm (when g != nullptr) and the dynamic quantiser in one
 // pass, values kept in registers.  One workgroup of 256 threads per row;
-// K <= 256 * QMAX.  Same arithmetic as k_rmsnorm_rows + k_quant_rows.
+// K <= 256 * QMAX.  Same arithmetic as k_row_stats + k_quant_seq.
 constexpr int QMAX = 48;
 __global__ __launch_bounds__(256) void k_norm_quant_row(int K, const float* __restrict__ x, int ldx,
                                                         const float* __restrict__ g, double eps,

@@ -32,7 +32,6 @@ hipError_t launch_test_codes(hipStream_t st, int rows, int K, int R, const uint8
                              int8_t* out, const float* s_in, const uint8_t* z_in, float* s_row,
                              int* z_row);
 constexpr int kMaxLayers = 64;
-constexpr int kMaxBatch = 64;
 hipError_t launch_cache_write(hipStream_t st, int L, int B, int S, int T, int row_floats,
                               const int32_t* pos_host, float* const* k_cache,
                               float* const* v_cache, const float* k_delta, const float* v_delta);
@@ -42,15 +41,64 @@ hipError_t launch_greedy_post(hipStream_t st, int B, int32_t* tokens, int32_t* o
                               int32_t end_id, int32_t* done);
 
 // ---- quantisation (k_quant.hip)
-// h[r] = rmsnorm(x[r]) (fp64 inside), plus per-row min/max of h.
-hipError_t launch_rmsnorm_rows(hipStream_t st, int R, int H, const float* x, int ldx,
-                               const float* gain, double eps, float* h, float* rmin, float* rmax);
-hipError_t launch_rowminmax(hipStream_t st, int R, int K, const float* x, float* rmin, float* rmax);
-// Rows r of sequence b = r / S share one (s, z) from the min/max of all their
-// rows; writes shifted codes (code - 128) and, if non-null, plain uint8 codes.
-hipError_t launch_quant_rows(hipStream_t st, int B, int S, int K, const float* x,
-                             const float* rmin, const float* rmax, int8_t* codes,
-                             uint8_t* codes_u8, float* s_out, int* z_out);
+// Per-sequence running min / max of an activation tensor, kept as ordered
+// ints (float_to_ordered) so that producers combine partial results with
+// integer atomics.  Atomics on one cache line serialise, so a set holds
+// kStatsRep replicas, each a 512-byte block of lo[kMaxBatch], hi[kMaxBatch];
+// a producer spreads its atomics over the replicas and a consumer folds
+// them.  A producer accumulates into `cur` and resets `clr` (the other set)
+// for the next producer: two sets used in turn, each cleared by the producer
+// before the one that fills it.
+constexpr int kMaxBatch = 64;
+constexpr int kStatsRep = 64;
+constexpr int kStatsSetInts = kStatsRep * 2 * kMaxBatch;
+struct SeqStats {
+  int* cur;  // [kStatsRep][2][kMaxBatch]
+  int* clr;  // same shape
+  int nseq;  // <= kMaxBatch
+};
+// Producer side (callers include common.hpp first): fold a wave's (lo, hi)
+// of sequence b into replica rep; reset the other set (one workgroup).
+__device__ __forceinline__ void stats_fold(const SeqStats& S, int rep, int b, float lo, float hi) {
+  int* blk = S.cur + (rep % kStatsRep) * 2 * kMaxBatch;
+  atomicMin(blk + b, float_to_ordered(lo));
+  atomicMax(blk + kMaxBatch + b, float_to_ordered(hi));
+}
+__device__ __forceinline__ void stats_clear_other(const SeqStats& S) {
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int t = threadIdx.x; t < kStatsSetInts; t += blockDim.x)
+      S.clr[t] = (t % (2 * kMaxBatch)) < kMaxBatch ? kOrdPosInf : kOrdNegInf;
+}
+// Consumer side: the range of sequence b, folded over the replicas by one
+// wave (every lane gets it).
+__device__ __forceinline__ void stats_range(const int* set, int b, float& lo, float& hi) {
+  const int l = threadIdx.x & 63;
+  float a = INFINITY, z = -INFINITY;
+  for (int r = l; r < kStatsRep; r += 64) {
+    a = fminf(a, ordered_to_float(set[r * 2 * kMaxBatch + b]));
+    z = fmaxf(z, ordered_to_float(set[r * 2 * kMaxBatch + kMaxBatch + b]));
+  }
+  lo = wave_min(a);
+  hi = wave_max(z);
+}
+// set = (+inf, -inf) everywhere
+hipError_t launch_seq_stats_init(hipStream_t st, int* set);
+// folded range of sequences 0..n-1 as fp32 (tests)
+hipError_t launch_seq_stats_read(hipStream_t st, const int* set, int n, float* flo, float* fhi);
+// Stats producer for R rows of K floats (row stride ldx), rows r of sequence
+// r / rows_per_seq.  With gain: RMSNorm statistics (fp64 inside): rs_out[r] =
+// 1 / sqrt(mean(x^2) + eps) and the min/max of h = fp32((x * rs) * gain);
+// h itself is not written.  Without gain: the min/max of x.
+hipError_t launch_row_stats(hipStream_t st, int R, int K, int rows_per_seq, const float* x,
+                            int ldx, const float* gain, double eps, double* rs_out,
+                            const SeqStats& stats);
+// Dynamic uint8 quantisation with one (s, z) per sequence from the range in
+// `set`: codes of x (or of h recomputed from x, rs and gain when rs !=
+// nullptr), shifted codes (code - 128) [R][K] and/or plain codes; s_out /
+// z_out [nseq].
+hipError_t launch_quant_seq(hipStream_t st, int R, int K, int rows_per_seq, const float* x,
+                            int ldx, const double* rs, const float* gain, const int* set,
+                            int8_t* codes, uint8_t* codes_u8, float* s_out, int* z_out);
 
 // One row per sequence (decode): optional RMSNorm (gain != nullptr) and the
 // row's dynamic quantisation in one kernel; shifted codes [B][K], s/z [B].
@@ -76,7 +124,7 @@ hipError_t launch_gemv_codes(hipStream_t st, int B, int K, const int8_t* codes, 
 bool gemm_big_supported(int M, int K);
 hipError_t launch_gemm_big(hipStream_t st, int M, int K, const int8_t* codes, const float* s,
                            const int* z, int rows_per_seq, const Seg* segs, int nseg, Epi epi,
-                           int32_t* acc_out);
+                           int32_t* acc_out, const SeqStats* stats = nullptr);
 // Few-row GEMM (k_gemm_sk.hip, M <= 32: batched decode, LM head of a
 // batch): same contract; scratch = gemm_skinny_ws_bytes() bytes whose
 // counter words are zero (gemm_skinny_reset) and stay zero between launches.
@@ -88,10 +136,14 @@ hipError_t launch_gemm_skinny(hipStream_t st, int M, int K, const int8_t* codes,
                               int32_t* acc_out, void* scratch);
 // Dispatch: few-row GEMM when scratch is given and the shape allows it, the
 // large-tile GEMM for M >= 128, else the tiled GEMM; tiled_only forces the
-// latter (tests).
+// latter (tests).  stats (EPI_SWIGLU only): the large-tile GEMM also
+// produces the per-sequence min / max of its output into *stats;
+// gemm_swiglu_stats(M, K, scratch) tells whether this call's dispatch does.
+bool gemm_swiglu_stats(int M, int K, const void* scratch);
 hipError_t launch_gemm(hipStream_t st, int M, int K, const int8_t* codes, const float* s,
                        const int* z, int rows_per_seq, const Seg* segs, int nseg, Epi epi,
-                       int32_t* acc_out, void* scratch = nullptr, bool tiled_only = false);
+                       int32_t* acc_out, void* scratch = nullptr, bool tiled_only = false,
+                       const SeqStats* stats = nullptr);
 
 // ---- rotary + attention (k_attn.hip)
 // qkv_raw [R][q_dim + 2*kv_dim] (bias added) -> q_rot [R][q_dim], k_delta /
@@ -102,19 +154,24 @@ struct PosArgs {
 
 // Prefill attention (S > 1) on fp64 matrix cores; G = NH / NKV <= 8.
 bool attention_prefill_supported(int NH, int NKV);
+// stats (optional): per-sequence min / max of out, as a stats producer.
 hipError_t launch_attention_prefill(hipStream_t st, int B, int S, int NH, int NKV, int T,
                                     const float* q, const float* k_cache, const float* v_cache,
                                     const float* k_delta, const float* v_delta,
-                                    const PosArgs& pos, float* out);
+                                    const PosArgs& pos, float* out,
+                                    const SeqStats* stats = nullptr);
 hipError_t launch_rope(hipStream_t st, int B, int S, int NH, int NKV, const float* qkv,
                        const double* cosT, const double* sinT, const PosArgs& pos, float* q,
                        float* k_delta, float* v_delta);
 // Full-cache GQA attention.  out [B*S][NH*128] fp32.  ws: scratch for split
-// partials (decode); attention_ws_bytes gives its size.
+// partials (decode); attention_ws_bytes gives its size.  stats: as for
+// launch_attention_prefill, honoured when attention_stats(S, NH, NKV).
 size_t attention_ws_bytes(int B, int S, int NH, int T);
+bool attention_stats(int S, int NH, int NKV);
 hipError_t launch_attention(hipStream_t st, int B, int S, int NH, int NKV, int T, const float* q,
                             const float* k_cache, const float* v_cache, const float* k_delta,
-                            const float* v_delta, const PosArgs& pos, float* out, void* ws);
+                            const float* v_delta, const PosArgs& pos, float* out, void* ws,
+                            const SeqStats* stats = nullptr);
 
 // ---- persistent batch-1 decode step for the ARK geometry (k_decode.hip)
 struct MegaLayer {

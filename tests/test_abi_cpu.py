@@ -173,3 +173,18 @@ def test_small_call_error_paths():
     q = ark.ArkQLinear(FAKE, FAKE, FAKE, None, 64, 128)
     assert lib.ark_test_qlinear(1, 5, FAKE, FAKE, FAKE, C.byref(q), None, FAKE, 0, FAKE, 1 << 20,
                                 None) == ark.ARK_E_SHAPE
+    q2 = ark.ArkQLinear(FAKE, FAKE, FAKE, None, 64, 192)
+    assert lib.ark_test_gate_up(1, 4, FAKE, FAKE, FAKE, C.byref(q), C.byref(q2), FAKE, FAKE, FAKE,
+                                FAKE, 1 << 30, None) == ark.ARK_E_SHAPE
+    assert lib.ark_test_gate_up(1, 4, FAKE, FAKE, FAKE, C.byref(q), C.byref(q), FAKE, None, FAKE,
+                                FAKE, 1 << 30, None) == ark.ARK_E_NULL
+    assert lib.ark_test_gate_up(1, 4, FAKE, FAKE, FAKE, C.byref(q), C.byref(q), FAKE, FAKE, FAKE,
+                                FAKE, 16, None) == ark.ARK_E_WORKSPACE
+    p1 = (C.c_int32 * 1)(500)
+    assert lib.ark_test_attention(1, 20, 16, 2, 512, p1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  FAKE, FAKE, 1 << 30, None) == ark.ARK_E_RANGE
+    assert lib.ark_test_attention(1, 2, 18, 2, 512, p1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  FAKE, FAKE, 1 << 30, None) == ark.ARK_E_SHAPE
+    assert lib.ark_test_attention(1, 2, 16, 2, 500, p1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  FAKE, FAKE, 1 << 30, None) == ark.ARK_E_SHAPE
+    assert lib.ark_test_attention_workspace_bytes(0, 1, 16, 512) == 0

@@ -47,7 +47,11 @@ def test_rope_table_matches_oracle():
         assert np.allclose(host(s), so, rtol=0, atol=4e-16 * np.maximum(1, np.arange(T))[:, None])
 
 
-@pytest.mark.parametrize("B,R,K", [(1, 1, 2048), (3, 7, 2048), (2, 49, 11008), (1, 5, 300)])
+# row kernels: rows held in registers (K <= 2048) or a workgroup per row;
+# quantisation a workgroup per row (few rows) or a wave per row (>= 1024
+# rows); K % 4 != 0 takes the scalar forms
+@pytest.mark.parametrize("B,R,K", [(1, 1, 2048), (3, 7, 2048), (2, 49, 11008), (1, 5, 300),
+                                   (2, 3, 301), (2, 600, 256), (3, 400, 3001)])
 def test_dynquant_bit_exact(B, R, K):
     rng = np.random.default_rng(B * 100 + R)
     x = (rng.standard_normal((B, R, K)) * rng.uniform(0.1, 5, (B, 1, 1))).astype(np.float32)
@@ -143,3 +147,55 @@ def test_embed_splice_bit_exact():
     ark.embed_splice(ark.dims_of(cfg), t(ids), t(table.view(np.int16)), t(audio),
                      cfg.audio_offset, out)
     assert np.array_equal(host(out), oracle.embed_splice(table, ids, audio, cfg.audio_offset))
+
+
+# M >= 128 takes the large-tile GEMM, whose epilogue also yields the
+# per-sequence range (sequence boundaries inside a wave's rows, and many
+# short sequences per wave); the others take a separate range pass
+@pytest.mark.parametrize("B,R,n,k", [(3, 101, 200, 2048), (2, 200, 130, 1024), (40, 4, 96, 512),
+                                     (1, 128, 64, 256), (4, 8, 96, 1024), (2, 30, 70, 2048)])
+def test_gate_up_swiglu_and_sequence_range(B, R, n, k):
+    rng = np.random.default_rng(7 * n + k + B * R)
+    wg = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    wu = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    codes = rng.integers(0, 256, (B, R, k)).astype(np.uint8)
+    scale = rng.uniform(0.001, 0.05, B).astype(np.float32)
+    zp = rng.integers(0, 256, B).astype(np.uint8)
+    G = ark.QLinear.from_f32(t(wg))
+    U = ark.QLinear.from_f32(t(wu))
+    y, lo, hi = ark.test_gate_up(t(codes), t(scale), t(zp), G, U)
+    y, lo, hi = host(y), host(lo), host(hi)
+    qg, sg = oracle.prep_weight(wg)
+    qu, su = oracle.prep_weight(wu)
+    for b in range(B):
+        g = oracle.qlinear(codes[b], scale[b], zp[b], qg, sg)
+        u = oracle.qlinear(codes[b], scale[b], zp[b], qu, su)
+        yb = y[b * R:(b + 1) * R]
+        # the products are exact; only exp may differ in its last fp64 bit
+        np.testing.assert_allclose(yb, oracle.swiglu(g, u), rtol=2.5e-7, atol=0)
+        # the range is exactly that of the values written
+        assert lo[b] == yb.min() and hi[b] == yb.max()
+
+
+# S > 1: the fp64 matrix-core kernel (range from its epilogue); S = 1: the
+# split decode kernel and a separate range pass
+@pytest.mark.parametrize("B,S,T,pos", [(2, 37, 512, (0, 300)), (3, 20, 64, (44, 0, 10)),
+                                       (1, 1, 512, (100,)), (2, 1, 1024, (0, 1023)),
+                                       (1, 70, 128, (58,))])
+def test_attention_and_sequence_range(B, S, T, pos):
+    NH, NKV, D = 16, 2, 128
+    rng = np.random.default_rng(B * 1000 + S * 10 + T)
+    q = rng.standard_normal((B, S, NH * D)).astype(np.float32)
+    kc = rng.standard_normal((B, T, NKV, D)).astype(np.float32)
+    vc = rng.standard_normal((B, T, NKV, D)).astype(np.float32)
+    kd = rng.standard_normal((B, S, NKV, D)).astype(np.float32)
+    vd = rng.standard_normal((B, S, NKV, D)).astype(np.float32)
+    out, lo, hi = ark.test_attention(t(q), t(kc), t(vc), t(kd), t(vd), pos, NKV)
+    out, lo, hi = host(out), host(lo), host(hi)
+    for b in range(B):
+        kh = oracle.cache_write(kc[b:b + 1], kd[b:b + 1], np.array(pos[b:b + 1]))[0]
+        vh = oracle.cache_write(vc[b:b + 1], vd[b:b + 1], np.array(pos[b:b + 1]))[0]
+        ref = oracle.attention(q[b].reshape(S, NH, D), kh, vh, int(pos[b]))
+        ob = out[b * S:(b + 1) * S]
+        np.testing.assert_allclose(ob, ref, rtol=1e-5, atol=1e-6)
+        assert lo[b] == ob.min() and hi[b] == ob.max()
