@@ -65,6 +65,199 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+// Global-memory pointers: accesses through them compile to global (not
+// flat) instructions, whose completion the compiler can count exactly.
+template <typename T>
+using gptr = T __attribute__((address_space(1)))*;
+
+// a wave-uniform pointer taken through scalar registers (readfirstlane), as
+// a global pointer
+template <typename T>
+__device__ __forceinline__ gptr<T> uniform_ptr(T* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (gptr<T>)(((uint64_t)hi << 32) | lo);
+}
+
+// Epilogue of one BM x BN tile held as FM x FN 32x32 accumulators per wave
+// (wave (wm, wn) owns rows wm * 64 + [0, 64) and columns wn * 128 + [0,
+// 128)): dequantisation, bias, residual add or SwiGLU, and for SwiGLU the
+// per-sequence range of the output into P.stats (replica rep).
+template <int FM, int FN>
+__device__ __forceinline__ void g2_epilogue(const Gemm2Params& P, i32x16 (&acc)[FM][FN], int m0,
+                                            int nb, int wm, int wn, int lane, int rep) {
+  constexpr int RW = 64;
+  const bool swiglu = P.epi == EPI_SWIGLU, resid = P.epi == EPI_RESID;
+  const int lr = lane & 31, lc = lane >> 5;
+  const int rps = P.rows_per_seq;
+  // Row i of a 32x32 block is in register (i/8)*4 + i%4 of lanes with
+  // (l/32) == (i/4)%2 (every index below is a compile-time constant, so the
+  // accumulators stay in registers).  Every parameter and every residual
+  // input is requested in one batch before the first is used: a kernel that
+  // keeps operand loads in flight behind the epilogue pays one wait for the
+  // batch, not one per request.  Segment fields are taken as wave-uniform
+  // values (a per-lane choice between parameter-block fields would become a
+  // vector load of the parameter block).
+  const int nseg = P.nseg;
+  const int sb1 = __builtin_amdgcn_readfirstlane(nseg > 1 ? P.seg_start[1] : P.ncols);
+  const int sb2 = __builtin_amdgcn_readfirstlane(nseg > 2 ? P.seg_start[2] : P.ncols);
+  struct {
+    gptr<const float> sw[3];
+    gptr<const int32_t> cs[3];
+    gptr<const float> bias[3];
+    gptr<float> out[3];
+    int ldo[3];
+  } U;
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const Seg& S = P.seg[k < nseg ? k : 0];
+    U.sw[k] = uniform_ptr(S.sw);
+    U.cs[k] = uniform_ptr(S.cs);
+    U.bias[k] = uniform_ptr(S.bias);
+    U.out[k] = uniform_ptr(S.out);
+    U.ldo[k] = __builtin_amdgcn_readfirstlane(S.ldo);
+  }
+  const gptr<const float> qs = uniform_ptr(P.qs);
+  const gptr<const int> qz = uniform_ptr(P.qz);
+  const gptr<int32_t> acc_out = uniform_ptr(P.acc_out);
+  float csw[FN], cbias[FN], usw[FN / 2];
+  int ccs[FN], ucs[FN / 2];
+  gptr<float> cout[FN];
+  int cldo[FN];
+  bool cok[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    cbias[j] = 0.f;
+    if (swiglu) {
+      if (j % 2 == 0) {
+        const int n = nb + (wn * 2 + j / 2) * 32 + lr;
+        const int nn = min(n, P.ncols - 1);
+        cok[j] = n < P.ncols;
+        csw[j] = U.sw[0][nn];
+        ccs[j] = U.cs[0][nn];
+        usw[j / 2] = U.sw[1][nn];
+        ucs[j / 2] = U.cs[1][nn];
+        cout[j] = U.out[0] + nn;
+        cldo[j] = U.ldo[0];
+      }
+    } else {
+      const int col = nb + wn * 128 + j * 32 + lr;
+      const int cc = min(col, P.ncols - 1);
+      const bool in1 = cc >= sb1, in2 = cc >= sb2;
+      const int n = cc - (in2 ? sb2 : (in1 ? sb1 : 0));
+      const gptr<const float> sw = in2 ? U.sw[2] : (in1 ? U.sw[1] : U.sw[0]);
+      const gptr<const int32_t> cs = in2 ? U.cs[2] : (in1 ? U.cs[1] : U.cs[0]);
+      const gptr<const float> bias = in2 ? U.bias[2] : (in1 ? U.bias[1] : U.bias[0]);
+      const gptr<float> out = in2 ? U.out[2] : (in1 ? U.out[1] : U.out[0]);
+      cldo[j] = in2 ? U.ldo[2] : (in1 ? U.ldo[1] : U.ldo[0]);
+      cok[j] = col < P.ncols;
+      csw[j] = sw[n];
+      ccs[j] = cs[n];
+      if (bias) cbias[j] = bias[n];
+      cout[j] = out + n;
+    }
+  }
+  // per group (i, q) of 4 rows: the parameters of the first row's sequence
+  // (rows past its end, where a sequence starts inside the group, load their
+  // own below)
+  const int rbase = m0 + wm * RW + lc * 4;
+  float rs[FM][4];
+  int rz[FM][4], rnext[FM][4];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int b = min(rbase + i * 32 + q * 8, P.M - 1) / rps;
+      rnext[i][q] = (b + 1) * rps;
+      rs[i][q] = qs[b];
+      rz[i][q] = 128 - qz[b];
+    }
+  // SwiGLU outputs' min / max per row of this lane (neutral where no output)
+  float elo[FM][16], ehi[FM][16];
+#pragma clang loop unroll(full)
+  for (int i = 0; i < FM; ++i) {
+#pragma clang loop unroll(full)
+   for (int vh = 0; vh < 16; vh += 4) {
+    // residual inputs of these 4 rows, all requested before any store
+    float old[4][FN];
+    if (resid) {
+#pragma clang loop unroll(full)
+      for (int v = vh; v < vh + 4; ++v) {
+        const int row = min(rbase + i * 32 + (v >> 2) * 8 + (v & 3), P.M - 1);
+#pragma clang loop unroll(full)
+        for (int j = 0; j < FN; ++j) old[v - vh][j] = cout[j][(size_t)row * cldo[j]];
+      }
+    }
+#pragma clang loop unroll(full)
+    for (int v = vh; v < vh + 4; ++v) {
+      elo[i][v] = INFINITY;
+      ehi[i][v] = -INFINITY;
+      const int row = rbase + i * 32 + (v >> 2) * 8 + (v & 3);
+      if (row >= P.M) continue;
+      float s = rs[i][v >> 2];
+      int zc = rz[i][v >> 2];
+      if (row >= rnext[i][v >> 2]) {
+        const int b = row / rps;
+        s = qs[b];
+        zc = 128 - qz[b];
+      }
+      if (swiglu) {
+#pragma clang loop unroll(full)
+        for (int j = 0; j < FN; j += 2) {
+          if (cok[j]) {
+            const int agc = acc[i][j][v] + zc * ccs[j];
+            const float g = dequant(agc, s, csw[j]);
+            const float u = dequant(acc[i][j + 1][v] + zc * ucs[j / 2], s, usw[j / 2]);
+            const double gd = g;
+            const float y = (float)(gd / (1.0 + exp(-gd)) * (double)u);
+            cout[j][(size_t)row * cldo[j]] = y;
+            elo[i][v] = fminf(elo[i][v], y);
+            ehi[i][v] = fmaxf(ehi[i][v], y);
+            if (acc_out) acc_out[(size_t)row * P.ncols + nb + (wn * 2 + j / 2) * 32 + lr] = agc;
+          }
+        }
+      } else {
+#pragma clang loop unroll(full)
+        for (int j = 0; j < FN; ++j) {
+          if (cok[j]) {
+            const int at = acc[i][j][v] + zc * ccs[j];
+            float y = dequant(at, s, csw[j]);
+            y = y + cbias[j];
+            const gptr<float> o = cout[j] + (size_t)row * cldo[j];
+            *o = resid ? old[v - vh][j] + y : y;
+            if (acc_out) acc_out[(size_t)row * P.ncols + nb + wn * 128 + j * 32 + lr] = at;
+          }
+        }
+      }
+    }
+   }
+  }
+  if (swiglu && P.stats.cur) {
+    // fold this wave's 64 rows into their sequences (one or two unless
+    // sequences are shorter than the wave's rows): lanes' values of rows in
+    // sequence b, then the wave's min / max, one atomic pair per sequence
+    const int r0 = m0 + wm * RW;
+    const int rl = min(r0 + RW, P.M) - 1;
+    for (int b = r0 / rps; b <= rl / rps; ++b) {
+      const int ra = b * rps, rb = ra + rps;
+      float lo = INFINITY, hi = -INFINITY;
+#pragma clang loop unroll(full)
+      for (int i = 0; i < FM; ++i)
+#pragma clang loop unroll(full)
+        for (int v = 0; v < 16; ++v) {
+          const int row = rbase + i * 32 + (v >> 2) * 8 + (v & 3);
+          const bool in = row >= ra && row < rb;
+          lo = fminf(lo, in ? elo[i][v] : INFINITY);
+          hi = fmaxf(hi, in ? ehi[i][v] : -INFINITY);
+        }
+      lo = wave_min(lo);
+      hi = wave_max(hi);
+      if (lane == 0) stats_fold(P.stats, rep, b, lo, hi);
+    }
+  }
+}
+
 // BM x 256 tiles on NTH / 64 waves arranged (BM / 64) x 2: every wave owns
 // a 64 x 128 block (2 x 4 accumulators of 32 x 32).
 template <int BM, int NS, int NTH>
@@ -198,140 +391,7 @@ __global__ __launch_bounds__(NTH, NTH == 256 ? 2 : 1) void k_gemm_big(Gemm2Param
           acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
   }
 
-  // ---- epilogue: row i of a 32x32 block is in register (i/8)*4 + i%4 of
-  // lanes with (l/32) == (i/4)%2 (every index below is a compile-time
-  // constant, so the accumulators stay in registers).  All per-column and
-  // per-row parameters are loaded up front: the output stores may alias
-  // them as far as the compiler knows, which would otherwise chain every
-  // load behind the previous store.
-  float csw[FN], cbias[FN], usw[FN / 2];
-  bool hasb[FN];
-  int ccs[FN], ucs[FN / 2];
-  float* cout[FN];
-  int cldo[FN];
-  bool cok[FN];
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    if (swiglu) {
-      if (j % 2 == 0) {
-        const int n = nb + (wn * 2 + j / 2) * 32 + lr;
-        const int nn = min(n, P.ncols - 1);
-        cok[j] = n < P.ncols;
-        csw[j] = P.seg[0].sw[nn];
-        ccs[j] = P.seg[0].cs[nn];
-        usw[j / 2] = P.seg[1].sw[nn];
-        ucs[j / 2] = P.seg[1].cs[nn];
-        cout[j] = P.seg[0].out + nn;
-        cldo[j] = P.seg[0].ldo;
-      }
-    } else {
-      const int col = nb + wn * 128 + j * 32 + lr;
-      const int cc = min(col, P.ncols - 1);
-      int si = 0;
-      while (si + 1 < P.nseg && cc >= P.seg_start[si + 1]) ++si;
-      const Seg& S = P.seg[si];
-      const int n = cc - P.seg_start[si];
-      cok[j] = col < P.ncols;
-      csw[j] = S.sw[n];
-      ccs[j] = S.cs[n];
-      hasb[j] = S.bias != nullptr;
-      cbias[j] = hasb[j] ? S.bias[n] : 0.f;
-      cout[j] = S.out + n;
-      cldo[j] = S.ldo;
-    }
-  }
-  const int rbase = m0 + wm * RW + lc * 4;
-  float rs[FM][4];
-  int rz[FM][4];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      // rows rbase + i*32 + q*8 + (0..3) all lie in one sequence unless a
-      // sequence boundary falls inside; take the first row's and check below
-      const int b = min(rbase + i * 32 + q * 8, P.M - 1) / P.rows_per_seq;
-      rs[i][q] = P.qs[b];
-      rz[i][q] = 128 - P.qz[b];
-    }
-  // SwiGLU outputs' min / max per row of this lane (neutral where no output)
-  float elo[FM][16], ehi[FM][16];
-#pragma clang loop unroll(full)
-  for (int i = 0; i < FM; ++i) {
-#pragma clang loop unroll(full)
-    for (int v = 0; v < 16; ++v) {
-      elo[i][v] = INFINITY;
-      ehi[i][v] = -INFINITY;
-      const int row = rbase + i * 32 + (v >> 2) * 8 + (v & 3);
-      if (row >= P.M) continue;
-      float s = rs[i][v >> 2];
-      int zc = rz[i][v >> 2];
-      if ((row / P.rows_per_seq) != (min(rbase + i * 32 + (v >> 2) * 8, P.M - 1) / P.rows_per_seq)) {
-        const int b = row / P.rows_per_seq;  // a sequence starts inside this group of 4 rows
-        s = P.qs[b];
-        zc = 128 - P.qz[b];
-      }
-      if (swiglu) {
-#pragma clang loop unroll(full)
-        for (int j = 0; j < FN; j += 2) {
-          if (cok[j]) {
-            const int agc = acc[i][j][v] + zc * ccs[j];
-            const float g = dequant(agc, s, csw[j]);
-            const float u = dequant(acc[i][j + 1][v] + zc * ucs[j / 2], s, usw[j / 2]);
-            const double gd = g;
-            const float y = (float)(gd / (1.0 + exp(-gd)) * (double)u);
-            cout[j][(size_t)row * cldo[j]] = y;
-            elo[i][v] = fminf(elo[i][v], y);
-            ehi[i][v] = fmaxf(ehi[i][v], y);
-            if (P.acc_out) P.acc_out[(size_t)row * P.ncols + nb + (wn * 2 + j / 2) * 32 + lr] = agc;
-          }
-        }
-      } else {
-        // residual: the old values of this row are read before any store
-        float old[FN];
-#pragma clang loop unroll(full)
-        for (int j = 0; j < FN; ++j)
-          old[j] = (P.epi == EPI_RESID && cok[j]) ? cout[j][(size_t)row * cldo[j]] : 0.f;
-#pragma clang loop unroll(full)
-        for (int j = 0; j < FN; ++j) {
-          if (cok[j]) {
-            const int at = acc[i][j][v] + zc * ccs[j];
-            float y = dequant(at, s, csw[j]);
-            if (hasb[j]) y = y + cbias[j];
-            float* o = cout[j] + (size_t)row * cldo[j];
-            if (P.epi == EPI_RESID)
-              *o = old[j] + y;
-            else
-              *o = y;
-            if (P.acc_out) P.acc_out[(size_t)row * P.ncols + nb + wn * 128 + j * 32 + lr] = at;
-          }
-        }
-      }
-    }
-  }
-  if (swiglu && P.stats.cur) {
-    // fold this wave's 64 rows into their sequences (one or two unless
-    // sequences are shorter than the wave's rows): lanes' values of rows in
-    // sequence b, then the wave's min / max, one atomic pair per sequence
-    const int r0 = m0 + wm * RW;
-    const int rl = min(r0 + RW, P.M) - 1;
-    const int rps = P.rows_per_seq;
-    for (int b = r0 / rps; b <= rl / rps; ++b) {
-      const int ra = b * rps, rb = ra + rps;
-      float lo = INFINITY, hi = -INFINITY;
-#pragma clang loop unroll(full)
-      for (int i = 0; i < FM; ++i)
-#pragma clang loop unroll(full)
-        for (int v = 0; v < 16; ++v) {
-          const int row = rbase + i * 32 + (v >> 2) * 8 + (v & 3);
-          const bool in = row >= ra && row < rb;
-          lo = fminf(lo, in ? elo[i][v] : INFINITY);
-          hi = fmaxf(hi, in ? ehi[i][v] : -INFINITY);
-        }
-      lo = wave_min(lo);
-      hi = wave_max(hi);
-      if (lane == 0) stats_fold(P.stats, blockIdx.x * NWV + wave, b, lo, hi);
-    }
-  }
+  g2_epilogue<FM, FN>(P, acc, m0, nb, wm, wn, lane, blockIdx.x * NWV + wave);
 }
 
 static constexpr int kStages = 3;

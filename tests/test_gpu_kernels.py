@@ -78,9 +78,11 @@ def test_dynquant_all_zero_tensor():
                                      # M <= 32: the few-row kernel (K split, ragged rows, one step)
                                      (32, 1, 700, 2048), (4, 8, 256, 128), (1, 31, 4100, 256),
                                      (16, 1, 2048, 11008),
-                                     # M >= 128: the large-tile prefill GEMM (ragged and whole tiles)
+                                     # M >= 128: the large-tile prefill GEMM (ragged and whole tiles,
+                                     # several tiles per CU, K of 3 steps)
                                      (2, 100, 2560, 2048), (1, 256, 512, 1024), (1, 130, 200, 11008),
-                                     (3, 101, 700, 2048), (1, 600, 513, 1024)])
+                                     (3, 101, 700, 2048), (1, 600, 513, 1024), (3, 400, 8000, 256),
+                                     (1, 200, 300, 192)])
 def test_qlinear_bit_exact(use_gemm, B, R, n, k):
     if use_gemm == 0 and B * R > 4:
         pytest.skip("the decode GEMV takes at most 4 rows")
@@ -153,7 +155,8 @@ def test_embed_splice_bit_exact():
 # per-sequence range (sequence boundaries inside a wave's rows, and many
 # short sequences per wave); the others take a separate range pass
 @pytest.mark.parametrize("B,R,n,k", [(3, 101, 200, 2048), (2, 200, 130, 1024), (40, 4, 96, 512),
-                                     (1, 128, 64, 256), (4, 8, 96, 1024), (2, 30, 70, 2048)])
+                                     (1, 128, 64, 256), (4, 8, 96, 1024), (2, 30, 70, 2048),
+                                     (2, 300, 8000, 256), (2, 100, 100, 192)])
 def test_gate_up_swiglu_and_sequence_range(B, R, n, k):
     rng = np.random.default_rng(7 * n + k + B * R)
     wg = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
