@@ -241,9 +241,9 @@ int ark_test_dynquant(int32_t B, int32_t R, int32_t K, const float* x, uint8_t* 
  * zp[b]).  codes [B*R][W->k] uint8; acc [B*R][W->n] int32 (or NULL): the
  * exact sum_k (code - zp) * w; y [B*R][W->n] fp32 dequantised output with
  * bias.  use_gemm selects the kernel: 0 the decode GEMV (requires B*R <= 4);
- * 1 the matrix-core GEMM as the decoder dispatches it (few-row kernel for
- * B*R <= 32 and W->k % 128 == 0, large-tile kernel for B*R >= 128, tiled
- * kernel otherwise); 2 the tiled kernel for any B*R.  workspace >=
+ * 1 the matrix-core GEMM as the decoder dispatches it (few-row kernel, one
+ * pass per 32 rows, for B*R < 128 and W->k % 128 == 0, large-tile kernel for
+ * B*R >= 128, tiled kernel otherwise); 2 the tiled kernel for any B*R.  workspace >=
  * ark_test_qlinear_workspace_bytes(B*R, W->k, use_gemm).  Errors: ARK_E_NULL,
  * ARK_E_SHAPE, ARK_E_WORKSPACE. */
 size_t ark_test_qlinear_workspace_bytes(int32_t rows, int32_t k, int32_t use_gemm);

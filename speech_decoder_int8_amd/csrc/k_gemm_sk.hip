@@ -41,6 +41,7 @@ constexpr int LDS = NS * STAGE;
 
 struct GemmSkParams {
   int M, K, ncols, epi, rows_per_seq, nseg, tiles, ks, nss;
+  int row0;  // first row of this launch in the caller's row space (sequence of row m: (row0 + m) / rows_per_seq)
   const int8_t* A;
   const float* qs;
   const int* qz;
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_sk(GemmSkParams P) {
       const int up = __shfl_down(acc[r], 16, 32);  // lane j < 16 gets row j's up sum
       const int m = (r / 4) * 8 + half * 4 + r % 4;
       if (j < 16 && m < P.M && n < P.ncols) {
-        const int b = m / P.rows_per_seq;
+        const int b = (P.row0 + m) / P.rows_per_seq;
         const float s = P.qs[b];
         const int zc = 128 - P.qz[b];
         const int ag = acc[r] + zc * G.cs[n];
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_sk(GemmSkParams P) {
       for (int r = 0; r < 16; ++r) {
         const int m = (r / 4) * 8 + half * 4 + r % 4;
         if (m >= P.M) continue;
-        const int b = m / P.rows_per_seq;
+        const int b = (P.row0 + m) / P.rows_per_seq;
         const int at = acc[r] + (128 - P.qz[b]) * cs;
         float y = dequant(at, P.qs[b], sw);
         if (S.bias) y = y + bias;
@@ -229,7 +230,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_sk(GemmSkParams P) {
   }
 }
 
-bool gemm_skinny_supported(int M, int K) { return M >= 1 && M <= 32 && K % sk::SS == 0; }
+bool gemm_skinny_supported(int M, int K) { return M >= 1 && M < 128 && K % sk::SS == 0; }
 
 constexpr int SK_MAX_SPLIT_TILES = 256;  // row tiles of a K-split launch
 
@@ -248,12 +249,47 @@ hipError_t gemm_skinny_reset(hipStream_t st, void* scratch) {
   return hipGetLastError();
 }
 
+static hipError_t launch_gemm_skinny_rows(hipStream_t st, int M, int row0, int K,
+                                          const int8_t* codes, const float* s, const int* z,
+                                          int rows_per_seq, const Seg* segs, int nseg, Epi epi,
+                                          int32_t* acc_out, void* scratch);
+
 hipError_t launch_gemm_skinny(hipStream_t st, int M, int K, const int8_t* codes, const float* s,
                               const int* z, int rows_per_seq, const Seg* segs, int nseg, Epi epi,
                               int32_t* acc_out, void* scratch) {
   using namespace sk;
+  // more than 32 rows: one launch per 32 rows (the weights are streamed once
+  // per launch; a few extra passes cost far less than a row-tiled GEMM with
+  // a handful of workgroups)
+  if (M > 32) {
+    for (int r0 = 0; r0 < M; r0 += 32) {
+      Seg sub[3];
+      for (int i = 0; i < nseg; ++i) {
+        sub[i] = segs[i];
+        sub[i].out = segs[i].out + (size_t)r0 * segs[i].ldo;
+      }
+      int ncols = 0;
+      for (int i = 0; i < nseg; ++i) ncols += segs[i].n;
+      if (epi == EPI_SWIGLU) ncols = segs[0].n;
+      const hipError_t e = launch_gemm_skinny_rows(
+          st, min(32, M - r0), r0, K, codes + (size_t)r0 * K, s, z, rows_per_seq, sub, nseg, epi,
+          acc_out ? acc_out + (size_t)r0 * ncols : nullptr, scratch);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  return launch_gemm_skinny_rows(st, M, 0, K, codes, s, z, rows_per_seq, segs, nseg, epi, acc_out,
+                                 scratch);
+}
+
+static hipError_t launch_gemm_skinny_rows(hipStream_t st, int M, int row0, int K,
+                                          const int8_t* codes, const float* s, const int* z,
+                                          int rows_per_seq, const Seg* segs, int nseg, Epi epi,
+                                          int32_t* acc_out, void* scratch) {
+  using namespace sk;
   GemmSkParams P = {};
   P.M = M;
+  P.row0 = row0;
   P.K = K;
   P.A = codes;
   P.qs = s;

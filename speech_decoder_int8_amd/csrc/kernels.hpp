@@ -125,9 +125,10 @@ bool gemm_big_supported(int M, int K);
 hipError_t launch_gemm_big(hipStream_t st, int M, int K, const int8_t* codes, const float* s,
                            const int* z, int rows_per_seq, const Seg* segs, int nseg, Epi epi,
                            int32_t* acc_out, const SeqStats* stats = nullptr);
-// Few-row GEMM (k_gemm_sk.hip, M <= 32: batched decode, LM head of a
-// batch): same contract; scratch = gemm_skinny_ws_bytes() bytes whose
-// counter words are zero (gemm_skinny_reset) and stay zero between launches.
+// Few-row GEMM (k_gemm_sk.hip, M < 128: batched decode, LM head of a
+// batch, short prompts; one pass per 32 rows): same contract; scratch =
+// gemm_skinny_ws_bytes() bytes whose counter words are zero
+// (gemm_skinny_reset) and stay zero between launches.
 bool gemm_skinny_supported(int M, int K);
 size_t gemm_skinny_ws_bytes();
 hipError_t gemm_skinny_reset(hipStream_t st, void* scratch);

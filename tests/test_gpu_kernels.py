@@ -78,6 +78,8 @@ def test_dynquant_all_zero_tensor():
                                      # M <= 32: the few-row kernel (K split, ragged rows, one step)
                                      (32, 1, 700, 2048), (4, 8, 256, 128), (1, 31, 4100, 256),
                                      (16, 1, 2048, 11008),
+                                     # 32 < M < 128: the few-row kernel once per 32 rows
+                                     (1, 49, 700, 2048), (3, 41, 300, 1024),
                                      # M >= 128: the large-tile prefill GEMM (ragged and whole tiles,
                                      # several tiles per CU, K of 3 steps)
                                      (2, 100, 2560, 2048), (1, 256, 512, 1024), (1, 130, 200, 11008),
