@@ -14,9 +14,10 @@
 // Work split: 256 workgroups x 16 waves.  In the layers every wave streams
 // weights: it owns fixed output rows (or, for the down projection, half a
 // row) of each phase and issues the loads of a phase's weights into
-// registers ahead of the phase's input.  The attention of a token runs on
-// 2 x (live 64-key items, at most 8) workgroups; the gate/up rows are spread
-// over the other workgroups only, which stream them while the attention runs.
+// registers ahead of the phase's input.  The attention of a token runs on at
+// most 16 workgroups (items of 4 query heads of one KV head over a share of
+// the live 64-key chunks); the gate/up rows are spread over the other
+// workgroups only, which stream them while the attention runs.
 //
 // Data exchange between workgroups (which sit on different XCDs with
 // separate L2s) uses 64-bit words (fp32 value | tag << 32) written with
