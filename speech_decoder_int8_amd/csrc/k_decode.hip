@@ -73,14 +73,21 @@ static_assert((((I + (NWG - NATT) - 1) / (NWG - NATT) + 3) & ~3) <= GU_ROWS * NW
 constexpr int STAGE = 112 * 1024;             // LDS staging bytes
 constexpr int GU_LDS = 16 * 1024;             // stage offset of the gate/up units in LDS
 // down projection: waves 8..15 ("loaders") each own one of the 8 rows (11
-// units of 1 KiB, the last one partial): units 0..7 in registers, 8..10 in
-// LDS at DN_LDS + 3 KiB x loader; waves 0..7 poll and quantise its input
+// units of 1 KiB, the last one partial), all in LDS: units 8..10 at DN_LDS +
+// 3 KiB x loader (requested early, while the attention runs), units 0..7 at
+// DN_HEAD + 8 KiB x loader (requested once the gate/up units in LDS are
+// used, so they are in before the SwiGLU codes are awaited); waves 0..7
+// poll and unpack its input
 constexpr int D_UNITS = (I + 1023) / 1024;    // 11
-constexpr int D_LDS_UNITS = D_UNITS - 8;      // 3
+constexpr int D_HEAD_UNITS = 8;
+constexpr int D_LDS_UNITS = D_UNITS - D_HEAD_UNITS;  // 3
 constexpr int NPOLL = NW - R_D;               // 8 polling waves
 constexpr int DN_LDS = 88 * 1024;
+constexpr int DN_HEAD = 24 * 1024;
 static_assert(DN_LDS + R_D * D_LDS_UNITS * 1024 <= STAGE, "down units exceed LDS stage");
 static_assert(GU_LDS + NW * 4096 <= DN_LDS, "gate/up units overlap the down units");
+static_assert(DN_HEAD >= (I / 4) * 8 && DN_HEAD + R_D * D_HEAD_UNITS * 1024 <= DN_LDS,
+              "down head units between the codes' staging and the early down units");
 
 typedef unsigned long long u64;
 typedef __attribute__((address_space(1))) const i32x4 gi32x4;
@@ -1143,20 +1150,28 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
     if (s < NPOLL) return;
     const LayerW& Lw = sh.lt[l & 1];
 #pragma unroll
-    for (int u = W; u < D_UNITS; ++u)
+    for (int u = D_HEAD_UNITS; u < D_UNITS; ++u)
       __builtin_amdgcn_global_load_lds(
           (const void __attribute__((address_space(1)))*)down_addr(Lw, u),
           (void __attribute__((address_space(3)))*)(sh.stage + DN_LDS +
-                                                    ((s - NPOLL) * D_LDS_UNITS + u - W) * 1024),
+                                                    ((s - NPOLL) * D_LDS_UNITS + u - D_HEAD_UNITS) *
+                                                        1024),
           16, 0, 2);
   };
-  // loaders: the register part (needs the weight registers free)
-  auto issue_down = [&](int l) {
+  // loaders: the other units of their down row, into LDS as well (the stage
+  // region between the codes' staging and DN_LDS must be free)
+  auto issue_down_head = [&](int l) {
     if (s < NPOLL) return;
     const LayerW& Lw = sh.lt[l & 1];
     sd = ldc(Lw.sw[6], w * R_D + s - NPOLL);
     cd = ldc(Lw.cs[6], w * R_D + s - NPOLL);
-    prime_units<W, W>(win, [&](int u) { return down_addr(Lw, u); });
+#pragma unroll
+    for (int u = 0; u < D_HEAD_UNITS; ++u)
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)down_addr(Lw, u),
+          (void __attribute__((address_space(3)))*)(sh.stage + DN_HEAD +
+                                                    ((s - NPOLL) * D_HEAD_UNITS + u) * 1024),
+          16, 0, 2);
   };
 
   const size_t rep = xcc_id();
@@ -1251,7 +1266,7 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
     }
     trace_done(A, w, l, 6, lane);
     // attention workgroups have no gate/up rows: their down rows next
-    if (att) issue_down(l);
+    if (att) issue_down_head(l);
 
     // ---- gate/up + SwiGLU
     asm volatile("" : "+v"(lane16), "+v"(tid), "+v"(lane));
@@ -1323,6 +1338,13 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
           xput(mm + 1, hi, epoch);
         }
       }
+      // the rest of the down rows are requested now, behind the (min, max)
+      // stores (a workgroup's memory requests are served in order) and into
+      // the LDS the gate/up units have left: they stream during the
+      // (min, max) wait (which takes the scalar path) and are in before the
+      // codes are awaited
+      lds_barrier();
+      issue_down_head(l);
     }
 
     // ---- SwiGLU quantisation parameters from all producers' min/max
@@ -1340,30 +1362,26 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
         __hip_atomic_store(xl + OFF_AC + (size_t)r * (I / 4) + k, ((u64)epoch << 32) | word,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    // the down rows are requested only now: a workgroup's memory requests
-    // are served in order, and issuing them stalls the loader waves until
-    // the queue drains, so the (min, max) wait and the codes' stores go first
-    if (!att) {
-      lds_barrier();
-      issue_down(l);
-    }
-
-    // ---- down + residual: waves 0..7 poll and quantise the SwiGLU vector
-    // while the loaders' down rows arrive; loader 8 + r computes row r
+    // ---- down + residual: waves 0..7 poll and unpack the SwiGLU codes;
+    // loader 8 + r computes row r from its units in LDS
     asm volatile("" : "+v"(lane16), "+v"(tid), "+v"(lane));
     poll_codes(xl + OFF_AC + rep * (I / 4), I / 4, rg / 4, sh, lane, wave, epoch, A.err);
     trace_at(A, w, l, 9);
     if (s >= NPOLL) {
       int acc = 0;
       const int8_t* cb = sh.codes + lane16;
-      run_units<W, W>(win, [&](int u) { return down_addr(Lw, u); }, [&](int u, const i32x4 v) {
-        acc = dot16(v, *(const i32x4*)(cb + u * 1024), acc);
-      });
       __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS units
 #pragma unroll
-      for (int u = W; u < D_UNITS; ++u) {
+      for (int u = 0; u < D_HEAD_UNITS; ++u) {
+        const i32x4 v =
+            *(const i32x4*)(sh.stage + DN_HEAD + ((s - NPOLL) * D_HEAD_UNITS + u) * 1024 + lane16);
+        acc = dot16(v, *(const i32x4*)(cb + u * 1024), acc);
+      }
+#pragma unroll
+      for (int u = D_HEAD_UNITS; u < D_UNITS; ++u) {
         const i32x4 v = *(const i32x4*)(sh.stage + DN_LDS +
-                                        ((s - NPOLL) * D_LDS_UNITS + u - W) * 1024 + lane16);
+                                        ((s - NPOLL) * D_LDS_UNITS + u - D_HEAD_UNITS) * 1024 +
+                                        lane16);
         acc = dot16(v, *(const i32x4*)(cb + u * 1024), acc);
       }
       acc = wave_sum(acc);
