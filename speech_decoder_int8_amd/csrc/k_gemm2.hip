@@ -2,11 +2,11 @@
 // (v_mfma_i32_32x32x32_i8), with the same dequantising epilogues as k_gemm
 // (store (+bias), residual add, SwiGLU over paired gate/up columns).
 //
-// Tiles of BM x 256 x 64 (BM = 128), 256 threads as 2 x 2 waves, each
-// wave (BM/2) x 128 of 32x32 accumulators.  Operand tiles go from global
-// memory straight into LDS with 16-byte LDS-DMA loads (no register staging),
-// NS stages deep, so the loads of step k+NS-1 overlap the matrix work of
-// step k; one barrier per 64-wide K step.
+// Tiles of 128 x 256 x 64, 256 threads as 2 x 2 waves, each wave 64 x 128
+// of 32x32 accumulators.  Operand tiles go from global memory straight into
+// LDS with 16-byte LDS-DMA loads (no register staging), three stages deep,
+// so the loads of step k+2 overlap the matrix work of step k; one barrier
+// per K step.
 //
 // LDS tile layout: 64-byte rows; the 16-byte chunk c of row r sits at chunk
 // position c ^ ((r >> 2) & 3), so the 16 lanes served together by a 16-byte
@@ -32,10 +32,6 @@ namespace ark {
 
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 
-namespace g2 {
-constexpr int BN = 256, BK = 64;
-}  // namespace g2
-
 struct Gemm2Params {
   int M, K, ncols, epi, rows_per_seq, nseg, tiles_m, tiles;
   const int8_t* A;
@@ -46,12 +42,6 @@ struct Gemm2Params {
   int32_t* acc_out;
   SeqStats stats;  // EPI_SWIGLU: per-sequence min/max of the output (cur == nullptr: off)
 };
-
-// 16-byte chunk c of tile row r sits at chunk c ^ ((r >> 2) & 3): the 16
-// lanes of one fragment read (rows r..r+15 of one chunk column) then cover
-// all 64 LDS banks without a conflict
-__device__ __forceinline__ int swz(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
-__device__ __forceinline__ int swzc(int r, int p) { return p ^ ((r >> 2) & 3); }
 
 __device__ __forceinline__ void dma16(const int8_t* src, int8_t* lds_base) {
   __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
@@ -131,7 +121,7 @@ __device__ __forceinline__ void g2_epilogue(const Gemm2Params& P, i32x16 (&acc)[
     cbias[j] = 0.f;
     if (swiglu) {
       if (j % 2 == 0) {
-        const int n = nb + (wn * 2 + j / 2) * 32 + lr;
+        const int n = nb + (wn * (FN / 2) + j / 2) * 32 + lr;
         const int nn = min(n, P.ncols - 1);
         cok[j] = n < P.ncols;
         csw[j] = U.sw[0][nn];
@@ -142,7 +132,7 @@ __device__ __forceinline__ void g2_epilogue(const Gemm2Params& P, i32x16 (&acc)[
         cldo[j] = U.ldo[0];
       }
     } else {
-      const int col = nb + wn * 128 + j * 32 + lr;
+      const int col = nb + wn * (FN * 32) + j * 32 + lr;
       const int cc = min(col, P.ncols - 1);
       const bool in1 = cc >= sb1, in2 = cc >= sb2;
       const int n = cc - (in2 ? sb2 : (in1 ? sb1 : 0));
@@ -214,7 +204,7 @@ __device__ __forceinline__ void g2_epilogue(const Gemm2Params& P, i32x16 (&acc)[
             cout[j][(size_t)row * cldo[j]] = y;
             elo[i][v] = fminf(elo[i][v], y);
             ehi[i][v] = fmaxf(ehi[i][v], y);
-            if (acc_out) acc_out[(size_t)row * P.ncols + nb + (wn * 2 + j / 2) * 32 + lr] = agc;
+            if (acc_out) acc_out[(size_t)row * P.ncols + nb + (wn * (FN / 2) + j / 2) * 32 + lr] = agc;
           }
         }
       } else {
@@ -226,7 +216,7 @@ __device__ __forceinline__ void g2_epilogue(const Gemm2Params& P, i32x16 (&acc)[
             y = y + cbias[j];
             const gptr<float> o = cout[j] + (size_t)row * cldo[j];
             *o = resid ? old[v - vh][j] + y : y;
-            if (acc_out) acc_out[(size_t)row * P.ncols + nb + wn * 128 + j * 32 + lr] = at;
+            if (acc_out) acc_out[(size_t)row * P.ncols + nb + wn * (FN * 32) + j * 32 + lr] = at;
           }
         }
       }
@@ -258,21 +248,31 @@ __device__ __forceinline__ void g2_epilogue(const Gemm2Params& P, i32x16 (&acc)[
   }
 }
 
-// BM x 256 tiles on NTH / 64 waves arranged (BM / 64) x 2: every wave owns
-// a 64 x 128 block (2 x 4 accumulators of 32 x 32).
-template <int BM, int NS, int NTH>
+// BM x BN x BK tiles on NTH / 64 waves arranged (BM / 64) x 2: every wave
+// owns a 64 x BN/2 block (2 x BN/64 accumulators of 32 x 32).  Tile rows are
+// BK bytes in LDS; one LDS-DMA instruction moves 1024 / BK rows, each lane
+// the 16-byte chunk that belongs at its LDS position (chunk c of row r sits
+// at chunk c ^ ((r / (256 / BK)) % (BK / 16)), so the 16 rows of one
+// fragment read fall on all 64 banks).  128-byte rows make every request a
+// whole cache line, which streams markedly faster than 64-byte halves.
+template <int BM, int BN, int BK, int NS, int NTH>
 __global__ __launch_bounds__(NTH, NTH == 256 ? 2 : 1) void k_gemm_big(Gemm2Params P) {
-  using namespace g2;
   constexpr int NWV = NTH / 64;             // waves
   constexpr int RW = 64;                    // rows per wave
   static_assert(NWV * RW == BM * 2, "(BM / 64) x 2 waves");
   constexpr int FM = RW / 32;               // 32-row blocks per wave
-  constexpr int FN = 4;                     // 32-column blocks per wave
+  constexpr int FN = BN / 64;               // 32-column blocks per wave
+  constexpr int KK = BK / 32;               // 32-wide K substeps per step
+  constexpr int CPR = BK / 16;              // 16-byte chunks per tile row
+  constexpr int RPI = 1024 / BK;            // tile rows per DMA instruction
+  constexpr int RPL = 256 / BK;             // tile rows per 256 bytes (all banks)
   constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK, STAGE = A_BYTES + B_BYTES;
   constexpr int A_INS = A_BYTES / 1024 / NWV, B_INS = B_BYTES / 1024 / NWV;  // per wave per stage
   static_assert(A_INS * NWV * 1024 == A_BYTES && B_INS * NWV * 1024 == B_BYTES, "DMA split");
+  static_assert(FN % 2 == 0 && (BK == 64 || BK == 128), "tile shape");
   constexpr int INS = A_INS + B_INS;
   extern __shared__ __align__(16) int8_t lds[];
+  auto sw = [](int r, int c) { return r * BK + ((c ^ ((r / RPL) % CPR)) << 4); };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -295,20 +295,19 @@ __global__ __launch_bounds__(NTH, NTH == 256 ? 2 : 1) void k_gemm_big(Gemm2Param
   const int K = P.K, nk = K / BK;
 
   // per-lane DMA sources: A instructions wave*A_INS + i, B instructions
-  // wave*B_INS + i; instruction u covers rows 16u .. 16u+15
+  // wave*B_INS + i; instruction u covers rows RPI u .. RPI u + RPI - 1
   const int8_t* asrc[A_INS];
-  int achunk[A_INS];
 #pragma unroll
   for (int i = 0; i < A_INS; ++i) {
-    const int r = 16 * (wave * A_INS + i) + (lane >> 2);
-    achunk[i] = swzc(r, lane & 3);
-    asrc[i] = P.A + (size_t)min(m0 + r, P.M - 1) * K + 16 * achunk[i];
+    const int r = RPI * (wave * A_INS + i) + lane / CPR;
+    const int c = (lane % CPR) ^ ((r / RPL) % CPR);
+    asrc[i] = P.A + (size_t)min(m0 + r, P.M - 1) * K + 16 * c;
   }
   const int8_t* bsrc[B_INS];
 #pragma unroll
   for (int i = 0; i < B_INS; ++i) {
-    const int r = 16 * (wave * B_INS + i) + (lane >> 2);
-    const int c = swzc(r, lane & 3);
+    const int r = RPI * (wave * B_INS + i) + lane / CPR;
+    const int c = (lane % CPR) ^ ((r / RPL) % CPR);
     const int8_t* w;
     if (swiglu) {
       const int blk = r >> 5;
@@ -361,29 +360,28 @@ __global__ __launch_bounds__(NTH, NTH == 256 ? 2 : 1) void k_gemm_big(Gemm2Param
     if (ks + NS - 1 < nk) issue(ks + NS - 1, (ks + NS - 1) % NS);
     const int8_t* As = lds + (ks % NS) * STAGE;
     const int8_t* Bs = As + A_BYTES;
-    // both 32-wide K substeps' fragments are read up front into separate
-    // registers, so no read waits for a matrix instruction still using its
-    // source registers
-    i32x4 fa[2][FM], fb[2][FN];
+    // the K substeps' fragments are read up front into separate registers,
+    // so no read waits for a matrix instruction still using its sources
+    i32x4 fa[KK][FM], fb[KK][FN];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < KK; ++kk) {
       const int c = 2 * kk + lc;
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        fa[kk][i] = *(const i32x4*)(As + swz(wm * RW + i * 32 + lr, c));
+      for (int i = 0; i < FM; ++i) fa[kk][i] = *(const i32x4*)(As + sw(wm * RW + i * 32 + lr, c));
 #pragma unroll
-      for (int j = 0; j < FN; ++j) fb[kk][j] = *(const i32x4*)(Bs + swz(wn * 128 + j * 32 + lr, c));
+      for (int j = 0; j < FN; ++j)
+        fb[kk][j] = *(const i32x4*)(Bs + sw(wn * (BN / 2) + j * 32 + lr, c));
     }
     // pin all fragments live at once (keeps the reads ahead of the MFMAs)
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(fa[kk][i]));
 #pragma unroll
       for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(fb[kk][j]));
     }
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -394,27 +392,25 @@ __global__ __launch_bounds__(NTH, NTH == 256 ? 2 : 1) void k_gemm_big(Gemm2Param
   g2_epilogue<FM, FN>(P, acc, m0, nb, wm, wn, lane, blockIdx.x * NWV + wave);
 }
 
-static constexpr int kStages = 3;
-
-template <int BM, int NTH>
+template <int BM, int BN, int BK, int NS, int NTH>
 static hipError_t launch_big(hipStream_t st, Gemm2Params P) {
-  constexpr int bytes = kStages * (BM + g2::BN) * g2::BK;
+  constexpr int bytes = NS * (BM + BN) * BK;
   static bool attr = false;
   if (!attr) {
-    const hipError_t e = hipFuncSetAttribute((const void*)k_gemm_big<BM, kStages, NTH>,
+    const hipError_t e = hipFuncSetAttribute((const void*)k_gemm_big<BM, BN, BK, NS, NTH>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  const int tn = P.epi == EPI_SWIGLU ? g2::BN / 2 : g2::BN;
+  const int tn = P.epi == EPI_SWIGLU ? BN / 2 : BN;
   P.tiles_m = (P.M + BM - 1) / BM;
   P.tiles = P.tiles_m * ((P.ncols + tn - 1) / tn);
   const int grid = 8 * ((P.tiles + 7) / 8);
-  hipLaunchKernelGGL((k_gemm_big<BM, kStages, NTH>), dim3(grid), dim3(NTH), bytes, st, P);
+  hipLaunchKernelGGL((k_gemm_big<BM, BN, BK, NS, NTH>), dim3(grid), dim3(NTH), bytes, st, P);
   return hipGetLastError();
 }
 
-bool gemm_big_supported(int M, int K) { return M >= 128 && K % g2::BK == 0; }
+bool gemm_big_supported(int M, int K) { return M >= 128 && K % 64 == 0; }
 
 hipError_t launch_gemm_big(hipStream_t st, int M, int K, const int8_t* codes, const float* s,
                            const int* z, int rows_per_seq, const Seg* segs, int nseg, Epi epi,
@@ -436,10 +432,13 @@ hipError_t launch_gemm_big(hipStream_t st, int M, int K, const int8_t* codes, co
     P.seg_start[i + 1] = P.seg_start[i] + segs[i].n;
   }
   P.ncols = (epi == EPI_SWIGLU) ? segs[0].n : P.seg_start[nseg];
-  // 128-row tiles, two workgroups per CU (a 256-row tile on 8 waves, one
-  // workgroup per CU, moves a third fewer bytes per product but measured
-  // slower: the per-step barrier then stalls the whole CU)
-  return launch_big<128, 256>(st, P);
+  // 128 x 256 tiles with 64-byte K steps, three stages, two workgroups per
+  // CU.  Measured alternatives, all slower: 256-row tiles on 8 waves (the
+  // per-step barrier then stalls the whole CU); 128 x 128 tiles with 128-byte
+  // steps in two stages (whole-line loads, but one stage ahead and more
+  // bytes per product); any shape with one workgroup per CU (nothing covers
+  // its epilogue and prologue).
+  return launch_big<128, 256, 64, 3, 256>(st, P);
 }
 
 }  // namespace ark
