@@ -91,14 +91,26 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
   const int h = g * P.G + hh;
   const int qpos = p + i0 + qi;  // absolute position of this query row
 
-  // stage the queries of this workgroup
-  for (int e = tid; e < NQ * kHeadDim; e += 256) {
-    const int v = e / kHeadDim, d = e % kHeadDim;
-    const int vqi = v >> 3, vhh = v & 7;
-    float val = 0.0f;
-    if (vhh < P.G && i0 + vqi < S)
-      val = P.q[((size_t)(b * S + i0 + vqi) * NH + g * P.G + vhh) * kHeadDim + d];
-    Qs[v][d] = val;
+  // stage the queries of this workgroup (every load requested before the
+  // first store, so the loads overlap)
+  {
+    constexpr int QIT = NQ * kHeadDim / 256;
+    static_assert(QIT * 256 == NQ * kHeadDim, "query staging split");
+    float qvals[QIT];
+#pragma unroll
+    for (int k = 0; k < QIT; ++k) {
+      const int e = tid + 256 * k;
+      const int v = e / kHeadDim, d = e % kHeadDim;
+      const int vqi = v >> 3, vhh = v & 7;
+      qvals[k] = (vhh < P.G && i0 + vqi < S)
+                     ? P.q[((size_t)(b * S + i0 + vqi) * NH + g * P.G + vhh) * kHeadDim + d]
+                     : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < QIT; ++k) {
+      const int e = tid + 256 * k;
+      Qs[e / kHeadDim][e % kHeadDim] = qvals[k];
+    }
   }
 
   const double scale = 1.0 / sqrt((double)kHeadDim);
@@ -114,11 +126,18 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
   const int jend = min(min(T, jbeg + P.tsplit), p + min(S, i0 + QT));
   for (int j0 = jbeg; j0 < jend; j0 += KC) {
     __syncthreads();
-    // K/V rows j0 .. j0 + KC - 1 (cache or this call's deltas)
-    for (int e = tid; e < KC * (kHeadDim / 4); e += 256) {
+    // K/V rows j0 .. j0 + KC - 1 (cache or this call's deltas); every load
+    // is requested before the first store
+    constexpr int KIT = KC * (kHeadDim / 4) / 256;
+    static_assert(KIT * 256 == KC * (kHeadDim / 4), "K/V staging split");
+    float4 kvs[KIT], vvs[KIT];
+#pragma unroll
+    for (int k = 0; k < KIT; ++k) {
+      const int e = tid + 256 * k;
       const int jj = e / (kHeadDim / 4), d4 = e % (kHeadDim / 4);
       const int j = j0 + jj;
-      float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
+      kvs[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      vvs[k] = kvs[k];
       if (j < jend) {
         size_t off;
         const float *ks, *vs;
@@ -131,11 +150,16 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
           ks = P.kc;
           vs = P.vc;
         }
-        kv = ((const float4*)(ks + off))[d4];
-        vv = ((const float4*)(vs + off))[d4];
+        kvs[k] = ((const float4*)(ks + off))[d4];
+        vvs[k] = ((const float4*)(vs + off))[d4];
       }
-      ((float4*)Ks[jj])[d4] = kv;
-      ((float4*)Vs[jj])[d4] = vv;
+    }
+#pragma unroll
+    for (int k = 0; k < KIT; ++k) {
+      const int e = tid + 256 * k;
+      const int jj = e / (kHeadDim / 4), d4 = e % (kHeadDim / 4);
+      ((float4*)Ks[jj])[d4] = kvs[k];
+      ((float4*)Vs[jj])[d4] = vvs[k];
     }
     __syncthreads();
 
@@ -148,9 +172,16 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
       const int j = j0 + jj;
       double s = -INFINITY;
       if (active && j < jend && j <= qpos) {
+        // the threads of a query vector read different key rows: each walks
+        // the dimensions from its own offset, so their reads of one step
+        // fall on different LDS banks (rows are 512 bytes, a whole number of
+        // bank rounds)
         double dot = 0.0;
 #pragma unroll 8
-        for (int d = 0; d < kHeadDim; ++d) dot = fma((double)Qs[qv][d], (double)Ks[jj][d], dot);
+        for (int dd = 0; dd < kHeadDim; ++dd) {
+          const int d = (dd + sub) & (kHeadDim - 1);
+          dot = fma((double)Qs[qv][d], (double)Ks[jj][d], dot);
+        }
         s = dot * scale;
       }
       sc[t] = s;
@@ -215,16 +246,36 @@ __global__ __launch_bounds__(128) void k_attn_combine(int S, int NH, int nsplit,
   const int idx = blockIdx.x;  // (b * NH + h) * S + i
   const int i = idx % S, h = (idx / S) % NH, b = idx / (S * NH);
   const double* src = part + (size_t)idx * nsplit * kPart;
-  double M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmax(M, src[s * kPart]);
-  double L = 0.0, O = 0.0;
   const int d = threadIdx.x;
-  for (int s = 0; s < nsplit; ++s) {
-    const double ms = src[s * kPart];
-    if (ms == -INFINITY) continue;
-    const double w = exp(ms - M);
-    L += src[s * kPart + 1] * w;
-    O += src[s * kPart + 2 + d] * w;
+  // the splits' states are requested 8 at a time, so the loads overlap
+  // instead of each waiting for the previous one
+  constexpr int U = 8;
+  double M = -INFINITY;
+  for (int s0 = 0; s0 < nsplit; s0 += U) {
+    double mv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) mv[u] = s0 + u < nsplit ? src[(s0 + u) * kPart] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) M = fmax(M, mv[u]);
+  }
+  double L = 0.0, O = 0.0;
+  for (int s0 = 0; s0 < nsplit; s0 += U) {
+    double ms[U], ls[U], os[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = s0 + u < nsplit;
+      const double* q = src + (size_t)(ok ? s0 + u : 0) * kPart;
+      ms[u] = ok ? q[0] : -INFINITY;
+      ls[u] = q[1];
+      os[u] = q[2 + d];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (ms[u] == -INFINITY) continue;
+      const double w = exp(ms[u] - M);
+      L += ls[u] * w;
+      O += os[u] * w;
+    }
   }
   out[((size_t)(b * S + i) * NH + h) * kHeadDim + d] = (float)(O / L);
 }

@@ -50,7 +50,9 @@ def _caches(cfg, lengths, rng):
     return kc, vc
 
 
-@pytest.mark.parametrize("p0", [0, 100, 510])
+# live 64-key chunks 1, 2 (one item folding two), 3 (two items, uneven),
+# 5 (three items) and 8 (four items, cache full after the second step)
+@pytest.mark.parametrize("p0", [0, 100, 150, 300, 510])
 def test_decode_steps_match_oracle(models, path, p0):
     om, gm = models
     rng = np.random.default_rng(p0 + 5)
