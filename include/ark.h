@@ -252,6 +252,13 @@ int ark_test_qlinear(int32_t B, int32_t R, const uint8_t* codes, const float* sc
                      int32_t use_gemm, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/* The MLP gate's elementwise part as the GEMM epilogues compute it (cookbook
+ * "ARK-ASR-3B" introduction: Qwen2 MLP, silu(g) * u = g / (1 + e^-g) * u),
+ * in fp64 and rounded once to fp32: y[i] for g[i], u[i], i < n, all three
+ * fp32 device arrays of n elements (n == 0: nothing is read or written).
+ * Errors: ARK_E_SHAPE (n < 0), ARK_E_NULL. */
+int ark_test_swiglu(int64_t n, const float* g, const float* u, float* y, void* stream);
+
 /* SwiGLU half of the MLP on given codes, as the prefill runs it (cookbook
  * "ARK-ASR-3B" introduction: Qwen2 MLP; model card "Files": int8 MatMuls on
  * dynamically quantised activations): y = silu(gate(x)) * up(x) with rows r

@@ -73,6 +73,7 @@ _SIGS = {
     "ark_test_qlinear": (C.c_int, [I32, I32, P, P, P, C.POINTER(ArkQLinear), P, P, I32, P,
                                    C.c_size_t, P]),
     "ark_test_dynquant_workspace_bytes": (C.c_size_t, []),
+    "ark_test_swiglu": (C.c_int, [C.c_int64, P, P, P, P]),
     "ark_test_gate_up_workspace_bytes": (C.c_size_t, [I32, I32, I32]),
     "ark_test_gate_up": (C.c_int, [I32, I32, P, P, P, C.POINTER(ArkQLinear), C.POINTER(ArkQLinear),
                                    P, P, P, P, C.c_size_t, P]),
@@ -364,6 +365,19 @@ def test_qlinear(codes, scale, zp, W: QLinear, use_gemm, stream=None):
                                                        _ptr(acc), _ptr(y), int(use_gemm), _ptr(ws),
                                                        ws.numel(), _stream(stream)))
     return acc, y
+
+
+def test_swiglu(g, u, stream=None):
+    """g, u fp32 device tensors of one shape -> silu(g) * u as the GEMM
+    epilogues compute it (fp64 inside, fp32 out)."""
+    import torch
+    g = g.contiguous()
+    u = u.contiguous()
+    assert g.shape == u.shape and g.dtype == u.dtype == torch.float32
+    y = torch.empty_like(g)
+    _check("ark_test_swiglu", lib().ark_test_swiglu(g.numel(), _ptr(g), _ptr(u), _ptr(y),
+                                                     _stream(stream)))
+    return y
 
 
 def test_gate_up(codes, scale, zp, gate: QLinear, up: QLinear, stream=None):

@@ -620,6 +620,12 @@ size_t ark_test_gate_up_workspace_bytes(int32_t B, int32_t R, int32_t k) {
          ark_test_dynquant_workspace_bytes() + gemm_skinny_ws_bytes();
 }
 
+int ark_test_swiglu(int64_t n, const float* g, const float* u, float* y, void* stream) {
+  if (n < 0) return ARK_E_SHAPE;
+  if (n > 0 && (!g || !u || !y)) return ARK_E_NULL;
+  return launch_swiglu((hipStream_t)stream, n, g, u, y) == hipSuccess ? ARK_OK : ARK_E_HIP;
+}
+
 int ark_test_gate_up(int32_t B, int32_t R, const uint8_t* codes, const float* scale,
                      const uint8_t* zp, const ark_qlinear* gate, const ark_qlinear* up, float* y,
                      float* seq_min, float* seq_max, void* workspace, size_t workspace_bytes,

@@ -12,6 +12,8 @@
 // the 64-wide K step.  Because A and B use the same lane->K assignment, the
 // product is sum_k A[i][k] * B[j][k] whatever order the instruction walks K.
 // The 16x16 result sits in lane (j + 16*(i/4)), register i % 4.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -136,6 +138,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
   }
 
   // ---- epilogue
+  const SwigluK SK = swiglu_consts();
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
@@ -156,8 +159,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
           const int au = acc[fm][fn + FN / 2][v] + zc * U.cs[n];
           const float g = dequant(ag, s, G.sw[n]);
           const float u = dequant(au, s, U.sw[n]);
-          const double gd = g;
-          G.out[(size_t)row * G.ldo + n] = (float)(gd / (1.0 + exp(-gd)) * (double)u);
+          G.out[(size_t)row * G.ldo + n] = swiglu_f64(g, u, SK);
           if (P.acc_out) P.acc_out[(size_t)row * P.ncols + n] = ag;
         }
       } else {
@@ -182,6 +184,21 @@ __global__ __launch_bounds__(256) void k_gemm(GemmParams P) {
       }
     }
   }
+}
+
+__global__ __launch_bounds__(256) void k_swiglu(int64_t n, const float* g, const float* u,
+                                                float* y) {
+  const SwigluK SK = swiglu_consts();
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    y[i] = swiglu_f64(g[i], u[i], SK);
+}
+
+hipError_t launch_swiglu(hipStream_t st, int64_t n, const float* g, const float* u, float* y) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_swiglu, dim3((unsigned)blocks), dim3(256), 0, st, n, g, u, y);
+  return hipGetLastError();
 }
 
 bool gemm_swiglu_stats(int M, int K, const void* scratch) {

@@ -165,6 +165,7 @@ __device__ __forceinline__ void g2_epilogue(const Gemm2Params& P, i32x16 (&acc)[
     }
   // SwiGLU outputs' min / max per row of this lane (neutral where no output)
   float elo[FM][16], ehi[FM][16];
+  const SwigluK SK = swiglu_consts();
 #pragma clang loop unroll(full)
   for (int i = 0; i < FM; ++i) {
 #pragma clang loop unroll(full)
@@ -179,6 +180,60 @@ __device__ __forceinline__ void g2_epilogue(const Gemm2Params& P, i32x16 (&acc)[
         for (int j = 0; j < FN; ++j) old[v - vh][j] = cout[j][(size_t)row * cldo[j]];
       }
     }
+    if (swiglu) {
+      // the 4 rows' values first, with no branch between them (independent
+      // fp64 chains the scheduler can interleave), then the guarded stores
+      float sv[4];
+      int zv[4];
+#pragma clang loop unroll(full)
+      for (int v = vh; v < vh + 4; ++v) {
+        const int row = rbase + i * 32 + (v >> 2) * 8 + (v & 3);
+        float s = rs[i][v >> 2];
+        int zc = rz[i][v >> 2];
+        if (row < P.M && row >= rnext[i][v >> 2]) {
+          const int b = row / rps;
+          s = qs[b];
+          zc = 128 - qz[b];
+        }
+        sv[v - vh] = s;
+        zv[v - vh] = zc;
+      }
+      float y[4][FN / 2];
+      int agc[4][FN / 2];
+#pragma clang loop unroll(full)
+      for (int v = vh; v < vh + 4; ++v)
+#pragma clang loop unroll(full)
+        for (int j = 0; j < FN; j += 2) {
+          agc[v - vh][j / 2] = acc[i][j][v] + zv[v - vh] * ccs[j];
+          const float g = dequant(agc[v - vh][j / 2], sv[v - vh], csw[j]);
+          const float u = dequant(acc[i][j + 1][v] + zv[v - vh] * ucs[j / 2], sv[v - vh], usw[j / 2]);
+          y[v - vh][j / 2] = swiglu_f64(g, u, SK);
+        }
+      // computed here for every lane (not sunk into the guarded stores)
+#pragma clang loop unroll(full)
+      for (int v = 0; v < 4; ++v)
+#pragma clang loop unroll(full)
+        for (int j = 0; j < FN / 2; ++j) asm volatile("" : "+v"(y[v][j]));
+#pragma clang loop unroll(full)
+      for (int v = vh; v < vh + 4; ++v) {
+        elo[i][v] = INFINITY;
+        ehi[i][v] = -INFINITY;
+        const int row = rbase + i * 32 + (v >> 2) * 8 + (v & 3);
+        if (row >= P.M) continue;
+#pragma clang loop unroll(full)
+        for (int j = 0; j < FN; j += 2) {
+          if (cok[j]) {
+            const float yv = y[v - vh][j / 2];
+            cout[j][(size_t)row * cldo[j]] = yv;
+            elo[i][v] = fminf(elo[i][v], yv);
+            ehi[i][v] = fmaxf(ehi[i][v], yv);
+            if (acc_out)
+              acc_out[(size_t)row * P.ncols + nb + (wn * (FN / 2) + j / 2) * 32 + lr] = agc[v - vh][j / 2];
+          }
+        }
+      }
+      continue;
+    }
 #pragma clang loop unroll(full)
     for (int v = vh; v < vh + 4; ++v) {
       elo[i][v] = INFINITY;
@@ -192,22 +247,7 @@ __device__ __forceinline__ void g2_epilogue(const Gemm2Params& P, i32x16 (&acc)[
         s = qs[b];
         zc = 128 - qz[b];
       }
-      if (swiglu) {
-#pragma clang loop unroll(full)
-        for (int j = 0; j < FN; j += 2) {
-          if (cok[j]) {
-            const int agc = acc[i][j][v] + zc * ccs[j];
-            const float g = dequant(agc, s, csw[j]);
-            const float u = dequant(acc[i][j + 1][v] + zc * ucs[j / 2], s, usw[j / 2]);
-            const double gd = g;
-            const float y = (float)(gd / (1.0 + exp(-gd)) * (double)u);
-            cout[j][(size_t)row * cldo[j]] = y;
-            elo[i][v] = fminf(elo[i][v], y);
-            ehi[i][v] = fmaxf(ehi[i][v], y);
-            if (acc_out) acc_out[(size_t)row * P.ncols + nb + (wn * (FN / 2) + j / 2) * 32 + lr] = agc;
-          }
-        }
-      } else {
+      {
 #pragma clang loop unroll(full)
         for (int j = 0; j < FN; ++j) {
           if (cok[j]) {

@@ -184,6 +184,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_sk(GemmSkParams P) {
     const int n = tile * (ROWS / 2) + wave * 16 + (j & 15);
     const Seg& G = P.seg[0];
     const Seg& U = P.seg[1];
+    const SwigluK SK = swiglu_consts();
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int up = __shfl_down(acc[r], 16, 32);  // lane j < 16 gets row j's up sum
@@ -196,8 +197,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_sk(GemmSkParams P) {
         const int au = up + zc * U.cs[n];
         const float g = dequant(ag, s, G.sw[n]);
         const float u = dequant(au, s, U.sw[n]);
-        const double gd = g;
-        G.out[(size_t)m * G.ldo + n] = (float)(gd / (1.0 + exp(-gd)) * (double)u);
+        G.out[(size_t)m * G.ldo + n] = swiglu_f64(g, u, SK);
         if (P.acc_out) P.acc_out[(size_t)m * P.ncols + n] = ag;
       }
     }

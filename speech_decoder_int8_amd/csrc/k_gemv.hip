@@ -169,8 +169,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams P) {
         const int au = acc[NR + r][b] + zc * U.cs[row];
         const float g = dequant(ag, s, G.sw[row]);
         const float u = dequant(au, s, U.sw[row]);
-        const double gd = g;
-        G.out[(size_t)b * G.ldo + row] = (float)(gd / (1.0 + exp(-gd)) * (double)u);
+        G.out[(size_t)b * G.ldo + row] = swiglu_f64(g, u, swiglu_consts_literal());
         if (P.acc_out) P.acc_out[(size_t)b * P.rows_total + row] = ag;
       } else {
         int si = 0;

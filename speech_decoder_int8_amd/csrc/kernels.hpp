@@ -81,6 +81,70 @@ __device__ __forceinline__ void stats_range(const int* set, int b, float& lo, fl
   lo = wave_min(a);
   hi = wave_max(z);
 }
+// Constants of swiglu_f64: 1/k! for k = 12 down to 3 (each rounded to
+// nearest), ln2_hi (ln2 with its low 21 mantissa bits cleared), ln2_lo =
+// ln2 - ln2_hi, 1/ln2, and the clamp of the exponent's argument.
+#define ARK_SWIGLU_CONSTS                                                                   \
+  0x1.1eed8eff8d898p-29, 0x1.ae64567f544e4p-26, 0x1.27e4fb7789f5cp-22, 0x1.71de3a556c734p-19, \
+      0x1.a01a01a01a01ap-16, 0x1.a01a01a01a01ap-13, 0x1.6c16c16c16c17p-10,                    \
+      0x1.1111111111111p-7, 0x1.5555555555555p-5, 0x1.5555555555555p-3,                       \
+      0x1.62e42fee00000p-1, 0x1.a39ef35793c76p-33, 0x1.71547652b82fep+0, -746.0
+static __constant__ double kSwigluTab[14] = {ARK_SWIGLU_CONSTS};
+struct SwigluK {
+  double c[14];
+};
+// The table loaded once (a caller does it outside its loops) into scalar
+// registers, from where the VALU instructions take the constants as scalar
+// operands; as literals every use would first be copied into vector
+// registers.  The table's address is made opaque so its values are not
+// folded back into literals, and kept in the constant address space so
+// the loads are scalar.
+__device__ __forceinline__ SwigluK swiglu_consts() {
+  typedef const double __attribute__((address_space(4))) * cptr;
+  cptr c = (cptr)kSwigluTab;
+  asm("" : "+s"(c));
+  SwigluK K;
+#pragma unroll
+  for (int i = 0; i < 14; ++i) K.c[i] = c[i];
+  return K;
+}
+
+// The same constants as literals, for code whose scalar registers are taken.
+__device__ __forceinline__ SwigluK swiglu_consts_literal() {
+  return SwigluK{{ARK_SWIGLU_CONSTS}};
+}
+
+// Qwen2 MLP gate, silu(g) * u = g / (1 + e^-g) * u, in fp64 and rounded
+// once to fp32 (fp32 g and u).  Written as (g >= 0 ? g u : g u t) / (1 + t)
+// with t = e^-|g| in [0, 1]: the denominator lies in [1, 2], so its
+// reciprocal estimate needs two Newton steps and none of a general
+// division's scaling or special cases.  g u is exact in fp64.
+// e^-|g|: -|g| = k ln2 + r with |r| <= ln2 / 2 (ln2 in two parts, k ln2_hi
+// exact), e^r by its Taylor series to degree 12 (first dropped term below
+// 2e-16), times 2^k; below -746 the argument is clamped (t underflows to 0).
+// NaN in g or u propagates through g u.  A few fp64 ulp from the exact value.
+__device__ __forceinline__ float swiglu_f64(float g, float u, const SwigluK& K) {
+  const double* c = K.c;
+  const double gd = g;
+  const double x = fmax(-fabs(gd), c[13]);
+  const double k = rint(x * c[12]);
+  const double r = fma(-k, c[11], fma(-k, c[10], x));
+  double p = c[0];
+#pragma unroll
+  for (int i = 1; i < 10; ++i) p = fma(p, r, c[i]);
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  const double t = ldexp(p, (int)k);
+  const double n = gd * (double)u;
+  const double num = gd >= 0.0 ? n : n * t;
+  const double d = 1.0 + t;
+  double q = __builtin_amdgcn_rcp(d);
+  q = fma(q, fma(-d, q, 1.0), q);
+  q = fma(q, fma(-d, q, 1.0), q);
+  return (float)(num * q);
+}
+
 // set = (+inf, -inf) everywhere
 hipError_t launch_seq_stats_init(hipStream_t st, int* set);
 // folded range of sequences 0..n-1 as fp32 (tests)
@@ -141,6 +205,8 @@ hipError_t launch_gemm_skinny(hipStream_t st, int M, int K, const int8_t* codes,
 // produces the per-sequence min / max of its output into *stats;
 // gemm_swiglu_stats(M, K, scratch) tells whether this call's dispatch does.
 bool gemm_swiglu_stats(int M, int K, const void* scratch);
+// y[i] = swiglu_f64(g[i], u[i]) for i < n (tests of the GEMM epilogues' gate)
+hipError_t launch_swiglu(hipStream_t st, int64_t n, const float* g, const float* u, float* y);
 hipError_t launch_gemm(hipStream_t st, int M, int K, const int8_t* codes, const float* s,
                        const int* z, int rows_per_seq, const Seg* segs, int nseg, Epi epi,
                        int32_t* acc_out, void* scratch = nullptr, bool tiled_only = false,

@@ -173,6 +173,9 @@ def test_small_call_error_paths():
     q = ark.ArkQLinear(FAKE, FAKE, FAKE, None, 64, 128)
     assert lib.ark_test_qlinear(1, 5, FAKE, FAKE, FAKE, C.byref(q), None, FAKE, 0, FAKE, 1 << 20,
                                 None) == ark.ARK_E_SHAPE
+    assert lib.ark_test_swiglu(-1, FAKE, FAKE, FAKE, None) == ark.ARK_E_SHAPE
+    assert lib.ark_test_swiglu(4, FAKE, None, FAKE, None) == ark.ARK_E_NULL
+    assert lib.ark_test_swiglu(0, None, None, None, None) == ark.ARK_OK   # nothing to do
     q2 = ark.ArkQLinear(FAKE, FAKE, FAKE, None, 64, 192)
     assert lib.ark_test_gate_up(1, 4, FAKE, FAKE, FAKE, C.byref(q), C.byref(q2), FAKE, FAKE, FAKE,
                                 FAKE, 1 << 30, None) == ark.ARK_E_SHAPE

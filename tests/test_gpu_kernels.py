@@ -153,6 +153,44 @@ def test_embed_splice_bit_exact():
     assert np.array_equal(host(out), oracle.embed_splice(table, ids, audio, cfg.audio_offset))
 
 
+@pytest.mark.gpu
+def test_swiglu_elementwise_over_every_range():
+    """The gate the GEMM epilogues compute (t = e^-|g| with a clamped
+    argument, a reciprocal on [1, 2]) against the oracle's plain
+    g / (1 + exp(-g)) * u: the working range, both underflow edges of e^-|g|,
+    |g| near 0, fp32 subnormals and extremes, infinities and NaN.  The values
+    are within 2.5e-7 (or one subnormal step) everywhere and bit-identical in
+    all but a handful of cases (both are a few fp64 ulp from exact).  u is
+    finite or NaN: with u infinite and -746 < g < -709.8 the oracle's
+    e^-g overflows and yields NaN where the exact value is infinite."""
+    rng = np.random.default_rng(11)
+    sign = lambda n: np.where(rng.random(n) < 0.5, -1.0, 1.0)  # noqa: E731
+    special = np.array([0.0, -0.0, 1e-45, -1e-45, 1.17e-38, -1.17e-38, np.inf, -np.inf, np.nan,
+                        3.4e38, -3.4e38, 88.7, -88.7, 103.9, -103.9, 745.1, -745.1, 746.0,
+                        -746.0, 800.0, -800.0])
+    g = np.concatenate([
+        rng.uniform(-30, 30, 200_000),
+        rng.uniform(-760, -700, 20_000), rng.uniform(700, 760, 20_000),
+        rng.uniform(-1e-3, 1e-3, 20_000),
+        sign(40_000) * 10.0 ** rng.uniform(-45, 38.5, 40_000),
+        np.repeat(special, 16)]).astype(np.float32)
+    u = (rng.standard_normal(g.size) * 10.0 ** rng.uniform(-3, 3, g.size)).astype(np.float32)
+    u[-16 * special.size::16] = 1.0
+    u[-16 * special.size + 1::16] = -0.0
+    u[-16 * special.size + 2::16] = 3e38
+    u[-16 * special.size + 3::16] = np.nan
+    y = host(ark.test_swiglu(torch.from_numpy(g).cuda(), torch.from_numpy(u).cuda()))
+    with np.errstate(all="ignore"):
+        yo = oracle.swiglu(g, u)
+    assert np.array_equal(np.isnan(y), np.isnan(yo))
+    fin = np.isfinite(yo)
+    assert np.array_equal(y[~fin & ~np.isnan(yo)], yo[~fin & ~np.isnan(yo)])
+    d = np.abs(y[fin].astype(np.float64) - yo[fin])
+    assert np.all((d <= 2.5e-7 * np.abs(yo[fin])) | (d <= 1.5e-45))
+    same = (y.view(np.uint32) == yo.view(np.uint32)) | (np.isnan(y) & np.isnan(yo))
+    assert np.count_nonzero(~same) <= 3, np.nonzero(~same)[0][:10]
+
+
 # M >= 128 takes the large-tile GEMM, whose epilogue also yields the
 # per-sequence range (sequence boundaries inside a wave's rows, and many
 # short sequences per wave); the others take a separate range pass
