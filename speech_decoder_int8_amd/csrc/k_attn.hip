@@ -209,16 +209,30 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
     m = mnew;
     __syncthreads();
 
-    // weighted values (masked rows selected out, never multiplied)
+    // weighted values: a masked row's value is replaced by 0 before the
+    // product (its contents never reach a result; o starts at +0, so the
+    // added 0 * 0 changes nothing).  Four keys' weights and values are read
+    // before the first product, with no branch between them.
+    static_assert(KC % 4 == 0, "weighted-sum key groups");
 #pragma unroll
     for (int e = 0; e < DPT; ++e) o[e] *= alpha;
-    for (int jj = 0; jj < KC; ++jj) {
-      const double w = Ps[qv][jj];
+#pragma unroll 2
+    for (int jj = 0; jj < KC; jj += 4) {
+      double w[4];
+      float vf[4][DPT];
 #pragma unroll
-      for (int e = 0; e < DPT; ++e) {
-        const double v = (double)Vs[jj][sub + e * TPQ];
-        o[e] = (w != 0.0) ? fma(w, v, o[e]) : o[e];
+      for (int i = 0; i < 4; ++i) {
+        w[i] = Ps[qv][jj + i];
+#pragma unroll
+        for (int e = 0; e < DPT; ++e) vf[i][e] = Vs[jj + i][sub + e * TPQ];
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < DPT; ++e) {
+          const double v = (w[i] != 0.0) ? (double)vf[i][e] : 0.0;
+          o[e] = fma(w[i], v, o[e]);
+        }
     }
   }
 
@@ -237,6 +251,143 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
 #pragma unroll
     for (int e = 0; e < DPT; ++e) dst[2 + sub + e * TPQ] = o[e];
   }
+}
+
+// Decode form (one query row per sequence): one workgroup per (sequence b,
+// KV head g, 32-key split of the cache), 256 threads = 8 query heads x 32
+// lanes.  The heads' query rows are widened to fp64 once, in LDS, and read
+// as broadcasts; key rows are padded to 132 floats so that the 16-byte reads
+// of 16 lanes (one key each) fall in distinct banks; in the weighted sum a
+// lane owns 4 consecutive dims and reads them with one 16-byte load per key.
+// Only rows at or before the position are staged (the rest of the split's
+// rows are zero and carry zero weight), so no row needs selecting out.  A
+// split past the position leaves an empty state, which the merge skips.
+namespace ad {
+constexpr int DK = 32;       // keys per split
+constexpr int KPITCH = 132;  // floats per staged key row
+}  // namespace ad
+
+__global__ __launch_bounds__(256) void k_attn_dec(AttnParams P) {
+  using namespace ad;
+  __shared__ __align__(16) double Qd[8][kHeadDim];  // reused for the weights
+  __shared__ __align__(16) float Ks[DK][KPITCH];
+  __shared__ __align__(16) float Vs[DK][kHeadDim];
+  double(*Ps)[DK] = (double(*)[DK])&Qd[0][0];
+
+  const int tid = threadIdx.x, hh = tid >> 5, sub = tid & 31;
+  const int b = blockIdx.y / P.NKV, g = blockIdx.y % P.NKV;
+  const int split = blockIdx.x;
+  const int p = P.pos.p[b];
+  const int NH = P.NH, NKV = P.NKV, G = P.G, T = P.T;
+  const bool active = hh < G;
+  const int h = g * G + hh;
+  const int jbeg = split * DK;
+  const int nk = min(min(T, jbeg + DK), p + 1) - jbeg;  // live keys of this split
+  double* dst = P.part + ((size_t)(b * NH + h) * P.nsplit + split) * kPart;
+  if (nk <= 0) {  // past the position: the empty state
+    if (active && sub == 0) {
+      dst[0] = -INFINITY;
+      dst[1] = 0.0;
+    }
+    if (active)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[2 + 4 * sub + e] = 0.0;
+    return;
+  }
+
+  // stage q (8 heads x 128), the keys and the values: every load is issued,
+  // with no branch or wait between them, before the first store (sources
+  // are wave-uniform pointers chosen per lane with selects; rows past the
+  // live keys load a live row and are zeroed afterwards)
+  const gptr<const float> qp = uniform_ptr(P.q), kcp = uniform_ptr(P.kc), vcp = uniform_ptr(P.vc);
+  const gptr<const float> kdp = uniform_ptr(P.kd), vdp = uniform_ptr(P.vd);
+  float qf[4];
+  float4 kv[4], vv[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int e = tid + 256 * k;
+    const int qh = min(e >> 7, G - 1), d = e & (kHeadDim - 1);
+    qf[k] = qp[((size_t)b * NH + g * G + qh) * kHeadDim + d];
+    const int jj = e >> 5, d4 = e & 31;
+    const int j = jbeg + min(jj, nk - 1);
+    const bool dl = j == p;  // this call's row replaces cache row p
+    const size_t off = dl ? ((size_t)b * NKV + g) * kHeadDim
+                          : ((size_t)(b * T + j) * NKV + g) * kHeadDim;
+    kv[k] = ld4((dl ? kdp : kcp) + off, d4);
+    vv[k] = ld4((dl ? vdp : vcp) + off, d4);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int e = tid + 256 * k;
+    if ((e >> 7) >= G) qf[k] = 0.f;
+    if ((e >> 5) >= nk) {
+      kv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      vv[k] = kv[k];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int e = tid + 256 * k;
+    Qd[e >> 7][e & (kHeadDim - 1)] = (double)qf[k];
+    const int jj = e >> 5, d4 = e & 31;
+    *(float4*)&Ks[jj][4 * d4] = kv[k];
+    *(float4*)&Vs[jj][4 * d4] = vv[k];
+  }
+  __syncthreads();
+
+  // score of key sub for head hh
+  double dot = 0.0;
+  {
+    const float4* kr = (const float4*)&Ks[sub][0];
+    const double2* qr = (const double2*)&Qd[hh][0];
+#pragma unroll 8
+    for (int d4 = 0; d4 < kHeadDim / 4; ++d4) {
+      const float4 k4 = kr[d4];
+      const double2 qa = qr[2 * d4], qb = qr[2 * d4 + 1];
+      dot = fma(qa.x, (double)k4.x, dot);
+      dot = fma(qa.y, (double)k4.y, dot);
+      dot = fma(qb.x, (double)k4.z, dot);
+      dot = fma(qb.y, (double)k4.w, dot);
+    }
+  }
+  const double sc = sub < nk ? dot * (1.0 / sqrt((double)kHeadDim)) : -INFINITY;
+  double m = sc;
+#pragma unroll
+  for (int off = 16; off > 0; off >>= 1) m = fmax(m, __shfl_xor(m, off, kWave));
+  const double ev = sub < nk ? exp(sc - m) : 0.0;
+  double l = ev;
+#pragma unroll
+  for (int off = 16; off > 0; off >>= 1) l += __shfl_xor(l, off, kWave);
+  __syncthreads();  // every query read is done: the weights take its place
+  Ps[hh][sub] = ev;
+  __syncthreads();
+
+  // weighted values of dims 4 sub .. 4 sub + 3, four keys per group (the
+  // rows past nk are zero and their weights 0)
+  double o[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int jj = 0; jj < nk; jj += 4) {
+    double w[4];
+    float4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w[i] = Ps[hh][jj + i];
+      v[i] = *(const float4*)&Vs[jj + i][4 * sub];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[0] = fma(w[i], (double)v[i].x, o[0]);
+      o[1] = fma(w[i], (double)v[i].y, o[1]);
+      o[2] = fma(w[i], (double)v[i].z, o[2]);
+      o[3] = fma(w[i], (double)v[i].w, o[3]);
+    }
+  }
+  if (!active) return;
+  if (sub == 0) {
+    dst[0] = m;
+    dst[1] = l;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) dst[2 + 4 * sub + e] = o[e];
 }
 
 // Merge the split partial softmax states of one (sequence, head, row).
@@ -310,10 +461,10 @@ hipError_t launch_attention(hipStream_t st, int B, int S, int NH, int NKV, int T
   P.pos = pos;
   P.out = out;
   P.part = (double*)ws;
-  if (S == 1) {
+  if (S == 1 && P.G <= 8) {
     P.nsplit = decode_split(T);
-    P.tsplit = 32;
-    hipLaunchKernelGGL((k_attn<1, 32>), dim3(P.nsplit, B * NKV), dim3(256), 0, st, P);
+    P.tsplit = ad::DK;
+    hipLaunchKernelGGL(k_attn_dec, dim3(P.nsplit, B * NKV), dim3(256), 0, st, P);
     hipLaunchKernelGGL(k_attn_combine, dim3(B * NH), dim3(128), 0, st, 1, NH, P.nsplit, P.part,
                        out);
   } else if (attention_prefill_supported(NH, NKV)) {

@@ -55,21 +55,6 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-// Global-memory pointers: accesses through them compile to global (not
-// flat) instructions, whose completion the compiler can count exactly.
-template <typename T>
-using gptr = T __attribute__((address_space(1)))*;
-
-// a wave-uniform pointer taken through scalar registers (readfirstlane), as
-// a global pointer
-template <typename T>
-__device__ __forceinline__ gptr<T> uniform_ptr(T* p) {
-  const uint64_t v = (uint64_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (gptr<T>)(((uint64_t)hi << 32) | lo);
-}
-
 // Epilogue of one BM x BN tile held as FM x FN 32x32 accumulators per wave
 // (wave (wm, wn) owns rows wm * 64 + [0, 64) and columns wn * 128 + [0,
 // 128)): dequantisation, bias, residual add or SwiGLU, and for SwiGLU the

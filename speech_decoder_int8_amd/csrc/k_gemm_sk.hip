@@ -179,52 +179,128 @@ __global__ __launch_bounds__(256, 2) void k_gemm_sk(GemmSkParams P) {
       __hip_atomic_store(P.ctr + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  // ---- epilogue: row m = (r / 4) * 8 + half * 4 + r % 4, weight row j
+  // ---- epilogue: row m = (r / 4) * 8 + half * 4 + r % 4, weight row j.
+  // Parameter-block fields are taken as wave-uniform values (a per-lane
+  // choice between them would become a vector load of the block), and every
+  // per-row parameter and residual input is requested in one batch before
+  // the first is used: the rows share one wait instead of one each.
+  const gptr<const float> qs = uniform_ptr(P.qs);
+  const gptr<const int> qz = uniform_ptr(P.qz);
+  const int M = P.M, rps = P.rows_per_seq, row0 = P.row0;
+  const gptr<int32_t> acc_out = uniform_ptr(P.acc_out);
+  float rs[16];
+  int rz[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int m = min((r / 4) * 8 + half * 4 + r % 4, M - 1);
+    const int b = (row0 + m) / rps;
+    rs[r] = qs[b];
+    rz[r] = qz[b];
+  }
+  // one wait for the whole batch: the values pass through this (empty)
+  // statement, so no use of them can be scheduled before every load is out
+  asm volatile("" : "+v"(rs[0]), "+v"(rs[1]), "+v"(rs[2]), "+v"(rs[3]), "+v"(rs[4]), "+v"(rs[5]),
+               "+v"(rs[6]), "+v"(rs[7]), "+v"(rs[8]), "+v"(rs[9]), "+v"(rs[10]), "+v"(rs[11]),
+               "+v"(rs[12]), "+v"(rs[13]), "+v"(rs[14]), "+v"(rs[15]));
+  asm volatile("" : "+v"(rz[0]), "+v"(rz[1]), "+v"(rz[2]), "+v"(rz[3]), "+v"(rz[4]), "+v"(rz[5]),
+               "+v"(rz[6]), "+v"(rz[7]), "+v"(rz[8]), "+v"(rz[9]), "+v"(rz[10]), "+v"(rz[11]),
+               "+v"(rz[12]), "+v"(rz[13]), "+v"(rz[14]), "+v"(rz[15]));
+#pragma unroll
+  for (int r = 0; r < 16; ++r) rz[r] = 128 - rz[r];
   if (swiglu) {
+    const gptr<const float> gsw = uniform_ptr(P.seg[0].sw), usw = uniform_ptr(P.seg[1].sw);
+    const gptr<const int32_t> gcs = uniform_ptr(P.seg[0].cs), ucs = uniform_ptr(P.seg[1].cs);
+    const gptr<float> out = uniform_ptr(P.seg[0].out);
+    const int ldo = __builtin_amdgcn_readfirstlane(P.seg[0].ldo);
     const int n = tile * (ROWS / 2) + wave * 16 + (j & 15);
-    const Seg& G = P.seg[0];
-    const Seg& U = P.seg[1];
+    const int nn = min(n, P.ncols - 1);
+    const float sg = gsw[nn], su = usw[nn];
+    const int cg = gcs[nn], cu = ucs[nn];
     const SwigluK SK = swiglu_consts();
+    float y[16];
+    int ag[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int up = __shfl_down(acc[r], 16, 32);  // lane j < 16 gets row j's up sum
-      const int m = (r / 4) * 8 + half * 4 + r % 4;
-      if (j < 16 && m < P.M && n < P.ncols) {
-        const int b = (P.row0 + m) / P.rows_per_seq;
-        const float s = P.qs[b];
-        const int zc = 128 - P.qz[b];
-        const int ag = acc[r] + zc * G.cs[n];
-        const int au = up + zc * U.cs[n];
-        const float g = dequant(ag, s, G.sw[n]);
-        const float u = dequant(au, s, U.sw[n]);
-        G.out[(size_t)m * G.ldo + n] = swiglu_f64(g, u, SK);
-        if (P.acc_out) P.acc_out[(size_t)m * P.ncols + n] = ag;
+      ag[r] = acc[r] + rz[r] * cg;
+      const float g = dequant(ag[r], rs[r], sg);
+      const float u = dequant(up + rz[r] * cu, rs[r], su);
+      y[r] = swiglu_f64(g, u, SK);
+    }
+    // computed here, ahead of the guarded stores (sunk into them, each
+    // store would wait for every earlier memory operation, stores included)
+    asm volatile("" : "+v"(y[0]), "+v"(y[1]), "+v"(y[2]), "+v"(y[3]), "+v"(y[4]), "+v"(y[5]),
+                 "+v"(y[6]), "+v"(y[7]), "+v"(y[8]), "+v"(y[9]), "+v"(y[10]), "+v"(y[11]),
+                 "+v"(y[12]), "+v"(y[13]), "+v"(y[14]), "+v"(y[15]));
+    if (j < 16 && n < P.ncols) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = (r / 4) * 8 + half * 4 + r % 4;
+        if (m >= M) continue;
+        out[(size_t)m * ldo + n] = y[r];
+        if (acc_out) acc_out[(size_t)m * P.ncols + n] = ag[r];
       }
     }
   } else {
     const int col = tile * ROWS + wave * 32 + j;
+    const int cc = min(col, P.ncols - 1);
+    const int nseg = P.nseg;
+    const int sb1 = __builtin_amdgcn_readfirstlane(nseg > 1 ? P.seg_start[1] : P.ncols);
+    const int sb2 = __builtin_amdgcn_readfirstlane(nseg > 2 ? P.seg_start[2] : P.ncols);
+    gptr<const float> usw[3], ubias[3];
+    gptr<const int32_t> ucs[3];
+    gptr<float> uout[3];
+    int uldo[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const Seg& S = P.seg[k < nseg ? k : 0];
+      usw[k] = uniform_ptr(S.sw);
+      ucs[k] = uniform_ptr(S.cs);
+      ubias[k] = uniform_ptr(S.bias);
+      uout[k] = uniform_ptr(S.out);
+      uldo[k] = __builtin_amdgcn_readfirstlane(S.ldo);
+    }
+    const bool in1 = cc >= sb1, in2 = cc >= sb2;
+    const int n = cc - (in2 ? sb2 : (in1 ? sb1 : 0));
+    const gptr<const float> sw = in2 ? usw[2] : (in1 ? usw[1] : usw[0]);
+    const gptr<const int32_t> cs = in2 ? ucs[2] : (in1 ? ucs[1] : ucs[0]);
+    const gptr<const float> bias = in2 ? ubias[2] : (in1 ? ubias[1] : ubias[0]);
+    const gptr<float> out = in2 ? uout[2] : (in1 ? uout[1] : uout[0]);
+    const int ldo = in2 ? uldo[2] : (in1 ? uldo[1] : uldo[0]);
+    const bool resid = P.epi == EPI_RESID;
+    const float swv = sw[n];
+    const int csv = cs[n];
+    const float bv = bias ? bias[n] : 0.f;
+    float old[16];
+    if (resid) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = min((r / 4) * 8 + half * 4 + r % 4, M - 1);
+        old[r] = out[(size_t)m * ldo + n];
+      }
+    }
+    // every row's value first (one wait for the residual inputs), then the
+    // guarded stores
+    float val[16];
+    int at[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      at[r] = acc[r] + rz[r] * csv;
+      float y = dequant(at[r], rs[r], swv);
+      if (bias) y = y + bv;
+      val[r] = resid ? old[r] + y : y;
+    }
+    asm volatile("" : "+v"(val[0]), "+v"(val[1]), "+v"(val[2]), "+v"(val[3]), "+v"(val[4]),
+                 "+v"(val[5]), "+v"(val[6]), "+v"(val[7]), "+v"(val[8]), "+v"(val[9]),
+                 "+v"(val[10]), "+v"(val[11]), "+v"(val[12]), "+v"(val[13]), "+v"(val[14]),
+                 "+v"(val[15]));
     if (col < P.ncols) {
-      int si = 0;
-      while (si + 1 < P.nseg && col >= P.seg_start[si + 1]) ++si;
-      const Seg& S = P.seg[si];
-      const int n = col - P.seg_start[si];
-      const float sw = S.sw[n];
-      const int cs = S.cs[n];
-      const float bias = S.bias ? S.bias[n] : 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = (r / 4) * 8 + half * 4 + r % 4;
-        if (m >= P.M) continue;
-        const int b = (P.row0 + m) / P.rows_per_seq;
-        const int at = acc[r] + (128 - P.qz[b]) * cs;
-        float y = dequant(at, P.qs[b], sw);
-        if (S.bias) y = y + bias;
-        float* o = S.out + (size_t)m * S.ldo + n;
-        if (P.epi == EPI_RESID)
-          *o = *o + y;
-        else
-          *o = y;
-        if (P.acc_out) P.acc_out[(size_t)m * P.ncols + col] = at;
+        if (m >= M) continue;
+        out[(size_t)m * ldo + n] = val[r];
+        if (acc_out) acc_out[(size_t)m * P.ncols + col] = at[r];
       }
     }
   }
@@ -307,12 +383,14 @@ static hipError_t launch_gemm_skinny_rows(hipStream_t st, int M, int row0, int K
   const int per_tile = epi == EPI_SWIGLU ? ROWS / 2 : ROWS;
   P.tiles = (P.ncols + per_tile - 1) / per_tile;
   const int nss = K / SS;
-  // split K until the launch has ~512 workgroups (two per CU) with at least
-  // 2 steps per split; launches of more than SK_MAX_SPLIT_TILES tiles are
-  // not split
+  // split K until the launch has about one workgroup per CU, with at least
+  // 2 steps per split (a split costs every workgroup its atomic additions,
+  // so a launch that already covers the chip, such as the 172 gate/up
+  // tiles of an 11008-wide MLP, is not split); launches of more than
+  // SK_MAX_SPLIT_TILES tiles are not split
   int ks = 1;
   if (P.tiles <= SK_MAX_SPLIT_TILES)
-    while (ks < 16 && P.tiles * ks * 2 <= 512 && nss / (ks * 2) >= 2) ks *= 2;
+    while (ks < 16 && P.tiles * ks * 2 <= 256 && nss / (ks * 2) >= 2) ks *= 2;
   P.nss = (nss + ks - 1) / ks;
   P.ks = (nss + P.nss - 1) / P.nss;
   P.part = (int32_t*)scratch;

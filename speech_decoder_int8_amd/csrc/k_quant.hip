@@ -263,39 +263,47 @@ hipError_t launch_quant_seq(hipStream_t st, int R, int K, int rps, const float* 
 
 // Decode form (one row per sequence, so the row is the whole tensor of its
 // sequence): RMSNorm (when g != nullptr) and the dynamic quantiser in one
-// pass, values kept in registers.  One workgroup of 256 threads per row;
-// K <= 256 * QMAX.  Same arithmetic as k_row_stats + k_quant_seq.
-constexpr int QMAX = 48;
-__global__ __launch_bounds__(256) void k_norm_quant_row(int K, const float* __restrict__ x, int ldx,
+// pass, values kept in registers.  One workgroup of 1024 threads per row
+// (four waves per SIMD: with a few dozen rows per launch, one wave per SIMD
+// would leave every latency exposed); K <= 1024 * QMAX.  The gain is
+// requested together with the row.  Same arithmetic as k_row_stats +
+// k_quant_seq.
+constexpr int QNT = 1024, QMAX = 12;
+__global__ __launch_bounds__(QNT) void k_norm_quant_row(int K, const float* __restrict__ x, int ldx,
                                                         const float* __restrict__ g, double eps,
                                                         int8_t* __restrict__ codes,
                                                         float* __restrict__ s_out,
                                                         int* __restrict__ z_out) {
-  __shared__ double redd[4];
-  __shared__ float redf[8];
+  __shared__ double redd[QNT / 64];
+  __shared__ float redf[2 * (QNT / 64)];
   const int r = blockIdx.x, t = threadIdx.x;
   const float* xr = x + (size_t)r * ldx;
-  float v[QMAX];
+  const float* gp = g ? g : xr;  // without a gain these loads are not used
+  float v[QMAX], gv[QMAX];
 #pragma unroll
-  for (int k = 0; k < QMAX; ++k) v[k] = (t + 256 * k < K) ? xr[t + 256 * k] : 0.f;
+  for (int k = 0; k < QMAX; ++k) {
+    const bool in = t + QNT * k < K;
+    v[k] = in ? xr[t + QNT * k] : 0.f;
+    gv[k] = in ? gp[t + QNT * k] : 0.f;
+  }
   if (g) {
     double ss = 0.0;
 #pragma unroll
     for (int k = 0; k < QMAX; ++k) ss += (double)v[k] * (double)v[k];
-    ss = block_sum<256>(ss, redd);
+    ss = block_sum<QNT>(ss, redd);
     const double rs = 1.0 / sqrt(ss / (double)K + eps);
 #pragma unroll
     for (int k = 0; k < QMAX; ++k)
-      if (t + 256 * k < K) v[k] = (float)(((double)v[k] * rs) * (double)g[t + 256 * k]);
+      if (t + QNT * k < K) v[k] = (float)(((double)v[k] * rs) * (double)gv[k]);
   }
   float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
   for (int k = 0; k < QMAX; ++k)
-    if (t + 256 * k < K) {
+    if (t + QNT * k < K) {
       lo = fminf(lo, v[k]);
       hi = fmaxf(hi, v[k]);
     }
-  block_minmax<256>(lo, hi, redf);
+  block_minmax<QNT>(lo, hi, redf);
   const QParam p = quant_param(lo, hi);
   if (t == 0) {
     s_out[r] = p.s;
@@ -304,15 +312,15 @@ __global__ __launch_bounds__(256) void k_norm_quant_row(int K, const float* __re
   int8_t* cr = codes + (size_t)r * K;
 #pragma unroll
   for (int k = 0; k < QMAX; ++k)
-    if (t + 256 * k < K) cr[t + 256 * k] = shift_code(quant_code(v[k], p));
+    if (t + QNT * k < K) cr[t + QNT * k] = shift_code(quant_code(v[k], p));
 }
 
-bool norm_quant_row_supported(int K) { return K >= 1 && K <= 256 * QMAX; }
+bool norm_quant_row_supported(int K) { return K >= 1 && K <= QNT * QMAX; }
 
 hipError_t launch_norm_quant_row(hipStream_t st, int B, int K, const float* x, int ldx,
                                  const float* gain, double eps, int8_t* codes, float* s_out,
                                  int* z_out) {
-  hipLaunchKernelGGL(k_norm_quant_row, dim3(B), dim3(256), 0, st, K, x, ldx, gain, eps, codes,
+  hipLaunchKernelGGL(k_norm_quant_row, dim3(B), dim3(QNT), 0, st, K, x, ldx, gain, eps, codes,
                      s_out, z_out);
   return hipGetLastError();
 }

@@ -20,6 +20,28 @@ struct Seg {
 
 enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
 
+// Global-memory pointers: accesses through them compile to global (not
+// flat) instructions, whose completion the compiler can count exactly.
+template <typename T>
+using gptr = T __attribute__((address_space(1)))*;
+
+// a wave-uniform pointer taken through scalar registers (readfirstlane), as
+// a global pointer
+template <typename T>
+__device__ __forceinline__ gptr<T> uniform_ptr(T* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (gptr<T>)(((uint64_t)hi << 32) | lo);
+}
+
+// 16-byte load through a global pointer (element i of float4s at p)
+__device__ __forceinline__ float4 ld4(gptr<const float> p, int i) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  const f4 v = ((const f4 __attribute__((address_space(1)))*)p)[i];
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
 // ---- prep / misc (k_misc.hip)
 hipError_t launch_prep_weight(hipStream_t st, const float* w, int n, int k, int8_t* codes,
                               float* scale, int32_t* colsum);

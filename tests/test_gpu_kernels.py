@@ -224,6 +224,7 @@ def test_gate_up_swiglu_and_sequence_range(B, R, n, k):
 # split decode kernel and a separate range pass
 @pytest.mark.parametrize("B,S,T,pos", [(2, 37, 512, (0, 300)), (3, 20, 64, (44, 0, 10)),
                                        (1, 1, 512, (100,)), (2, 1, 1024, (0, 1023)),
+                                       (3, 1, 512, (31, 32, 511)), (4, 1, 64, (0, 63, 5, 33)),
                                        (1, 70, 128, (58,))])
 def test_attention_and_sequence_range(B, S, T, pos):
     NH, NKV, D = 16, 2, 128
