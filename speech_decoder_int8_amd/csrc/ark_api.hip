@@ -220,10 +220,14 @@ int run_forward(const ark_model* m, int B, int S, float* x, const int32_t* pos_h
       HIP_TRY(launch_quant_seq(st, R, H, S, x, H, rs, L.ln1, sa.cur, codes, nullptr, qs, qz));
       HIP_TRY(launch_gemm(st, R, H, codes, qs, qz, S, qkvs, 3, EPI_STORE, nullptr, gsk));
     }
-    HIP_TRY(launch_rope(st, B, S, NH, NKV, qkv, m->rope_cos, m->rope_sin, pos, q, kdl, vdl));
+    // decode: the rotary step runs inside the attention kernel
+    const bool rope_in_attn = S == 1 && NH / NKV <= 8;
+    if (!rope_in_attn)
+      HIP_TRY(launch_rope(st, B, S, NH, NKV, qkv, m->rope_cos, m->rope_sin, pos, q, kdl, vdl));
+    const RopeIn ri = {qkv, ldqkv, m->rope_cos, m->rope_sin, kdl, vdl};
     const bool att_stats = !gemv && !rowq && attention_stats(S, NH, NKV);
     HIP_TRY(launch_attention(st, B, S, NH, NKV, T, q, kc[l], vc[l], kdl, vdl, pos, attn, part,
-                             att_stats ? &sb : nullptr));
+                             att_stats ? &sb : nullptr, rope_in_attn ? &ri : nullptr));
     if (gemv) {
       HIP_TRY(launch_gemv(st, B, Q, attn, Q, nullptr, 0.0, os, 1, EPI_RESID));
       prof_begin(st, B == 1);

@@ -63,6 +63,7 @@ struct AttnParams {
   float* out;
   int nsplit, tsplit;
   double* part;  // [B][NH][S][nsplit][2 + 128]
+  RopeIn rope;   // decode with the rotary step folded in (rope.qkv != nullptr)
 };
 
 constexpr int kPart = 2 + kHeadDim;
@@ -262,6 +263,10 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
 // Only rows at or before the position are staged (the rest of the split's
 // rows are zero and carry zero weight), so no row needs selecting out.  A
 // split past the position leaves an empty state, which the merge skips.
+// With P.rope.qkv set, q, k and v come unrotated from the projection rows:
+// the workgroup rotates its heads' q rows in LDS, and the split holding the
+// position rotates this call's key row and writes the key and value deltas
+// (the arithmetic of k_rope: fp64 products, rounded once to fp32).
 namespace ad {
 constexpr int DK = 32;       // keys per split
 constexpr int KPITCH = 132;  // floats per staged key row
@@ -299,22 +304,35 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnParams P) {
   // with no branch or wait between them, before the first store (sources
   // are wave-uniform pointers chosen per lane with selects; rows past the
   // live keys load a live row and are zeroed afterwards)
-  const gptr<const float> qp = uniform_ptr(P.q), kcp = uniform_ptr(P.kc), vcp = uniform_ptr(P.vc);
-  const gptr<const float> kdp = uniform_ptr(P.kd), vdp = uniform_ptr(P.vd);
+  const bool raw = P.rope.qkv != nullptr;
+  const gptr<const float> kcp = uniform_ptr(P.kc), vcp = uniform_ptr(P.vc);
+  // q rows of heads g G .. and this call's k / v rows of KV head g
+  const gptr<const float> qp = uniform_ptr(raw ? P.rope.qkv : P.q);
+  const gptr<const float> kdp = uniform_ptr(raw ? P.rope.qkv : P.kd);
+  const gptr<const float> vdp = uniform_ptr(raw ? P.rope.qkv : P.vd);
+  const size_t qbase = raw ? (size_t)b * P.rope.ld + (size_t)g * G * kHeadDim
+                           : ((size_t)b * NH + g * G) * kHeadDim;
+  const size_t dko = raw ? (size_t)b * P.rope.ld + (size_t)(NH + g) * kHeadDim
+                         : ((size_t)b * NKV + g) * kHeadDim;
+  const size_t dvo = raw ? (size_t)b * P.rope.ld + (size_t)(NH + NKV + g) * kHeadDim : dko;
   float qf[4];
   float4 kv[4], vv[4];
+  double rc = 0.0, rsn = 0.0;  // rotation of pair (tid & 63) at position p
+  if (raw) {
+    rc = uniform_ptr(P.rope.cosT)[(size_t)p * (kHeadDim / 2) + (tid & 63)];
+    rsn = uniform_ptr(P.rope.sinT)[(size_t)p * (kHeadDim / 2) + (tid & 63)];
+  }
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int e = tid + 256 * k;
     const int qh = min(e >> 7, G - 1), d = e & (kHeadDim - 1);
-    qf[k] = qp[((size_t)b * NH + g * G + qh) * kHeadDim + d];
+    qf[k] = qp[qbase + (size_t)qh * kHeadDim + d];
     const int jj = e >> 5, d4 = e & 31;
     const int j = jbeg + min(jj, nk - 1);
     const bool dl = j == p;  // this call's row replaces cache row p
-    const size_t off = dl ? ((size_t)b * NKV + g) * kHeadDim
-                          : ((size_t)(b * T + j) * NKV + g) * kHeadDim;
-    kv[k] = ld4((dl ? kdp : kcp) + off, d4);
-    vv[k] = ld4((dl ? vdp : vcp) + off, d4);
+    const size_t off = ((size_t)(b * T + j) * NKV + g) * kHeadDim;
+    kv[k] = ld4(dl ? kdp + dko : kcp + off, d4);
+    vv[k] = ld4(dl ? vdp + dvo : vcp + off, d4);
   }
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -334,6 +352,32 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnParams P) {
     *(float4*)&Vs[jj][4 * d4] = vv[k];
   }
   __syncthreads();
+  if (raw) {
+    // rotary at position p: pair (jj, jj + 64) of each q row (two rows per
+    // thread), and of this call's key row in the split that holds it
+    const int jj = tid & 63;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int qh = (tid >> 6) + 4 * k;
+      const double x1 = Qd[qh][jj], x2 = Qd[qh][jj + 64];
+      Qd[qh][jj] = (double)(float)(x1 * rc - x2 * rsn);
+      Qd[qh][jj + 64] = (double)(float)(x2 * rc + x1 * rsn);
+    }
+    const int r = p - jbeg;
+    if (r < nk && tid < 64) {
+      const double x1 = Ks[r][jj], x2 = Ks[r][jj + 64];
+      const float o1 = (float)(x1 * rc - x2 * rsn), o2 = (float)(x2 * rc + x1 * rsn);
+      Ks[r][jj] = o1;
+      Ks[r][jj + 64] = o2;
+      float* kd = P.rope.kd_out + ((size_t)b * NKV + g) * kHeadDim;
+      float* vd = P.rope.vd_out + ((size_t)b * NKV + g) * kHeadDim;
+      kd[jj] = o1;
+      kd[jj + 64] = o2;
+      vd[jj] = Vs[r][jj];
+      vd[jj + 64] = Vs[r][jj + 64];
+    }
+    __syncthreads();
+  }
 
   // score of key sub for head hh
   double dot = 0.0;
@@ -445,8 +489,8 @@ bool attention_stats(int S, int NH, int NKV) {
 hipError_t launch_attention(hipStream_t st, int B, int S, int NH, int NKV, int T, const float* q,
                             const float* k_cache, const float* v_cache, const float* k_delta,
                             const float* v_delta, const PosArgs& pos, float* out, void* ws,
-                            const SeqStats* stats) {
-  AttnParams P;
+                            const SeqStats* stats, const RopeIn* rope) {
+  AttnParams P = {};
   P.B = B;
   P.S = S;
   P.NH = NH;
@@ -461,6 +505,8 @@ hipError_t launch_attention(hipStream_t st, int B, int S, int NH, int NKV, int T
   P.pos = pos;
   P.out = out;
   P.part = (double*)ws;
+  if (rope && !(S == 1 && P.G <= 8)) return hipErrorInvalidValue;
+  if (rope) P.rope = *rope;
   if (S == 1 && P.G <= 8) {
     P.nsplit = decode_split(T);
     P.tsplit = ad::DK;

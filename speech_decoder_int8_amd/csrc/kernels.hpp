@@ -256,11 +256,23 @@ hipError_t launch_rope(hipStream_t st, int B, int S, int NH, int NKV, const floa
 // partials (decode); attention_ws_bytes gives its size.  stats: as for
 // launch_attention_prefill, honoured when attention_stats(S, NH, NKV).
 size_t attention_ws_bytes(int B, int S, int NH, int T);
+// Decode (S = 1, NH / NKV <= 8) with the rotary step folded in: q, k and v
+// are read unrotated from the q|k|v projection rows (stride ld) and the
+// rotated key and the value of each sequence are written to kd_out / vd_out
+// ([B][NKV][128]), as launch_rope would (same arithmetic).
+struct RopeIn {
+  const float* qkv;
+  int ld;
+  const double* cosT;
+  const double* sinT;
+  float* kd_out;
+  float* vd_out;
+};
 bool attention_stats(int S, int NH, int NKV);
 hipError_t launch_attention(hipStream_t st, int B, int S, int NH, int NKV, int T, const float* q,
                             const float* k_cache, const float* v_cache, const float* k_delta,
                             const float* v_delta, const PosArgs& pos, float* out, void* ws,
-                            const SeqStats* stats = nullptr);
+                            const SeqStats* stats = nullptr, const RopeIn* rope = nullptr);
 
 // ---- persistent batch-1 decode step for the ARK geometry (k_decode.hip)
 struct MegaLayer {
