@@ -105,6 +105,10 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
 }
 
 // One 1024-thread workgroup per row: the row (<= 0.6 MB) streams once.
+// Where the rows are 16-byte aligned, ids are taken in groups of 4 (one
+// 16-byte logit load and one 4-byte mask load), four groups per thread
+// requested together (indices clamped, so no branch separates the loads);
+// the comparison breaks ties by id, so the visiting order does not matter.
 __global__ __launch_bounds__(1024) void k_masked_argmax(int V, const float* __restrict__ logits,
                                                         const uint8_t* __restrict__ mask,
                                                         int32_t* __restrict__ out) {
@@ -114,11 +118,42 @@ __global__ __launch_bounds__(1024) void k_masked_argmax(int V, const float* __re
   const float* row = logits + (size_t)b * V;
   float bv = -INFINITY;
   int bi = INT_MAX;
-  for (int i = threadIdx.x; i < V; i += 1024) {
-    const float v = row[i];
-    if (mask[i] == 0 && !isnan(v) && better(v, i, bv, bi)) {
-      bv = v;
-      bi = i;
+  const bool vec = (V & 3) == 0 && (((uintptr_t)logits | (uintptr_t)mask) & 15) == 0;
+  if (vec) {
+    const int n4 = V >> 2;
+    const float4* r4 = (const float4*)row;
+    const uint32_t* m4 = (const uint32_t*)mask;
+    for (int g0 = threadIdx.x; g0 < n4; g0 += 4 * 1024) {
+      float4 v[4];
+      uint32_t mk[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int g = min(g0 + u * 1024, n4 - 1);
+        v[u] = r4[g];
+        mk[u] = m4[g];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int g = g0 + u * 1024;
+        if (g >= n4) continue;
+        const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int i = 4 * g + c;
+          if (((mk[u] >> (8 * c)) & 0xff) == 0 && !isnan(e[c]) && better(e[c], i, bv, bi)) {
+            bv = e[c];
+            bi = i;
+          }
+        }
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < V; i += 1024) {
+      const float v = row[i];
+      if (mask[i] == 0 && !isnan(v) && better(v, i, bv, bi)) {
+        bv = v;
+        bi = i;
+      }
     }
   }
 #pragma unroll

@@ -106,6 +106,21 @@ def test_qlinear_bit_exact(use_gemm, B, R, n, k):
         assert np.array_equal(host(y)[b * R:(b + 1) * R], y_o)
 
 
+@pytest.mark.parametrize("V", [1003, 4096])
+def test_masked_argmax_small_vocabularies(V):
+    """A vocabulary that is not a multiple of 4 (the element-wise scan) and
+    one that is (16-byte groups), with ties across groups and masked ids."""
+    rng = np.random.default_rng(V)
+    mask = (rng.random(V) < 0.1).astype(np.uint8)
+    lg = rng.standard_normal((3, V)).astype(np.float32)
+    lg[0, [3, 4, V - 2]] = 9.0                        # tie across groups -> id 3
+    lg[1, :] = 2.0                                    # all equal -> first unmasked id
+    lg[2, np.nonzero(mask == 0)[0][-1]] = 7.0         # maximum at the last unmasked id
+    out = torch.empty(3, dtype=torch.int32, device=DEV)
+    ark.masked_argmax(t(lg), t(mask), out)
+    assert host(out).tolist() == oracle.masked_argmax(lg, mask).tolist()
+
+
 def test_masked_argmax_bit_exact_and_forced_cases():
     V = 151936
     mask = synth.CONFIGS["c1"].mask()
