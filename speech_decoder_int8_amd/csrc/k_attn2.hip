@@ -14,9 +14,12 @@
 // wave computes S^T = K Q^T as 16x16 blocks (A = 16 keys x 4 dims of K,
 // B = 4 dims x 16 rows of Q^T, kept in registers), the online-softmax update
 // per row, and O^T += V^T P^T (A = 16 dims x 4 keys of V^T, B = 4 keys x 16
-// rows of P^T through LDS).  Fragment layout (16x16x4 f64): lane l supplies
+// rows of P^T).  Fragment layout (16x16x4 f64): lane l supplies
 // A[l % 16][l / 16] and B[l / 16][l % 16]; the 16x16 result holds
-// C[4 i + l / 16][l % 16] in register i.
+// C[4 i + l / 16][l % 16] in register i.  So the score block kb leaves
+// P^T[16 kb + 4 i + l / 16][l % 16] in lane l's register i, which is the B
+// operand that lane supplies for keys 4 t .. 4 t + 3 with t = 4 kb + i: the
+// weights never leave the registers.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -30,7 +33,7 @@ constexpr int KP = 132;   // K row pitch (floats): 16 keys x 4 dims reads hit di
 constexpr int VP = 128;   // V row pitch (floats)
 constexpr int QT = 16;    // query rows per workgroup
 constexpr int GMAX = 8;   // query heads per KV head
-constexpr int LDS_BYTES = KC * KP * 4 + KC * VP * 4 + GMAX * KC * QT * 8;
+constexpr int LDS_BYTES = KC * KP * 4 + KC * VP * 4;
 }  // namespace a2
 
 struct Attn2Params {
@@ -50,7 +53,6 @@ __global__ __launch_bounds__(512) void k_attn_prefill(Attn2Params P) {
   extern __shared__ __align__(16) unsigned char smem[];
   float* Ks = (float*)smem;                      // [KC][KP]
   float* Vs = Ks + KC * KP;                      // [KC][VP]
-  double* Pt = (double*)(Vs + KC * VP);          // [G][KC keys][QT rows]
   if (P.stats.cur) stats_clear_other(P.stats);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -70,20 +72,26 @@ __global__ __launch_bounds__(512) void k_attn_prefill(Attn2Params P) {
   const int qpos = p + qrow;
   const int maxq = p + min(i0 + QT - 1, S - 1);  // last key any row of the tile sees
   const int live_end = min(p + S, T);            // rows at or past it are never seen
-  double* Pw = Pt + wave * KC * QT;
 
   // B operand of S^T = K Q^T: Q[qrow][4s + q4], s = 0..31
+  // (all 32 loads issued before the first use; a row past S loads row S - 1
+  // and is zeroed)
   double qv[32];
   {
-    const float* src = P.q + ((size_t)(b * S + min(qrow, S - 1)) * P.NH + h) * kHeadDim;
+    const gptr<const float> src =
+        uniform_ptr(P.q) + ((size_t)(b * S + min(qrow, S - 1)) * P.NH + h) * kHeadDim;
+    float qf[32];
 #pragma unroll
-    for (int s = 0; s < 32; ++s) qv[s] = rowok ? (double)src[4 * s + q4] : 0.0;
+    for (int s = 0; s < 32; ++s) qf[s] = src[4 * s + q4];
+#pragma unroll
+    for (int s = 0; s < 32; ++s) qv[s] = rowok ? (double)qf[s] : 0.0;
   }
   f64x4 o[8];
 #pragma unroll
   for (int d = 0; d < 8; ++d) o[d] = f64x4{0.0, 0.0, 0.0, 0.0};
   double m = -INFINITY, l = 0.0;
   const double scale = 1.0 / sqrt((double)kHeadDim);
+  const SwigluK EK = swiglu_consts();  // constants of the exponential below
 
   const int nch = maxq / KC + 1;
   for (int c = 0; c < nch; ++c) {
@@ -136,15 +144,16 @@ __global__ __launch_bounds__(512) void k_attn_prefill(Attn2Params P) {
     cmax = fmax(cmax, __shfl_xor(cmax, 16, kWave));
     cmax = fmax(cmax, __shfl_xor(cmax, 32, kWave));
     const double mnew = fmax(m, cmax);
-    const double alpha = (m == -INFINITY) ? 0.0 : exp(m - mnew);
+    // every argument of the exponential is <= 0 (m, scores <= mnew)
+    const double alpha = (m == -INFINITY) ? 0.0 : exp_nonpos_f64(m - mnew, EK);
     double lsum = 0.0;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const double e = (sc[kb][i] == -INFINITY) ? 0.0 : exp(sc[kb][i] - mnew);
+        const double e = (sc[kb][i] == -INFINITY) ? 0.0 : exp_nonpos_f64(sc[kb][i] - mnew, EK);
         lsum += e;
-        Pw[(16 * kb + 4 * i + q4) * QT + c16] = e;
+        sc[kb][i] = e;  // P^T[key 16 kb + 4 i + q4][qrow]
       }
     lsum += __shfl_xor(lsum, 16, kWave);
     lsum += __shfl_xor(lsum, 32, kWave);
@@ -152,14 +161,10 @@ __global__ __launch_bounds__(512) void k_attn_prefill(Attn2Params P) {
     m = mnew;
 #pragma unroll
     for (int d = 0; d < 8; ++d) o[d] *= alpha;
-    // this wave's P^T writes (other lanes' values) before its reads: LDS
-    // accesses of a wave complete in order; the clobber keeps the compiler
-    // from moving the reads up
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     // O^T[dim][row] += V^T[dim][key] P^T[key][row], 16 steps of 4 keys
-#pragma unroll 4
+#pragma unroll
     for (int t = 0; t < KC / 4; ++t) {
-      const double pb = Pw[(4 * t + q4) * QT + c16];
+      const double pb = sc[t >> 2][t & 3];
       const float* vr = Vs + (4 * t + q4) * VP + c16;
 #pragma unroll
       for (int d = 0; d < 8; ++d)
@@ -219,7 +224,7 @@ hipError_t launch_attention_prefill(hipStream_t st, int B, int S, int NH, int NK
   P.pos = pos;
   P.out = out;
   if (stats) P.stats = *stats;
-  const int lds = a2::KC * a2::KP * 4 + a2::KC * a2::VP * 4 + P.G * a2::KC * a2::QT * 8;
+  const int lds = a2::LDS_BYTES;
   hipLaunchKernelGGL(k_attn_prefill, dim3(B * NKV * P.nqt), dim3(64 * P.G), lds, st, P);
   return hipGetLastError();
 }

@@ -141,23 +141,35 @@ __device__ __forceinline__ SwigluK swiglu_consts_literal() {
 // with t = e^-|g| in [0, 1]: the denominator lies in [1, 2], so its
 // reciprocal estimate needs two Newton steps and none of a general
 // division's scaling or special cases.  g u is exact in fp64.
-// e^-|g|: -|g| = k ln2 + r with |r| <= ln2 / 2 (ln2 in two parts, k ln2_hi
-// exact), e^r by its Taylor series to degree 12 (first dropped term below
-// 2e-16), times 2^k; below -746 the argument is clamped (t underflows to 0).
-// NaN in g or u propagates through g u.  A few fp64 ulp from the exact value.
-__device__ __forceinline__ float swiglu_f64(float g, float u, const SwigluK& K) {
+// e^-|g| by exp_nonpos_core (NaN in g or u propagates through g u).  A few
+// fp64 ulp from the exact value.
+// e^x for x <= 0 (x = -inf gives 0; NaN is not handled), fp64: x = k ln2 +
+// r with |r| <= ln2 / 2 (ln2 in two parts, k ln2_hi exact), e^r by its
+// Taylor series to degree 12 (first dropped term below 2e-16), times 2^k;
+// below -746 the argument is clamped (the result underflows to 0).  A few
+// fp64 ulp from the exact value.
+__device__ __forceinline__ double exp_nonpos_core(double x, const SwigluK& K) {
   const double* c = K.c;
-  const double gd = g;
-  const double x = fmax(-fabs(gd), c[13]);
-  const double k = rint(x * c[12]);
-  const double r = fma(-k, c[11], fma(-k, c[10], x));
+  const double xc = fmax(x, c[13]);
+  const double k = rint(xc * c[12]);
+  const double r = fma(-k, c[11], fma(-k, c[10], xc));
   double p = c[0];
 #pragma unroll
   for (int i = 1; i < 10; ++i) p = fma(p, r, c[i]);
   p = fma(p, r, 0.5);
   p = fma(p, r, 1.0);
   p = fma(p, r, 1.0);
-  const double t = ldexp(p, (int)k);
+  return ldexp(p, (int)k);
+}
+// The same with NaN passed through.
+__device__ __forceinline__ double exp_nonpos_f64(double x, const SwigluK& K) {
+  const double t = exp_nonpos_core(x, K);
+  return x != x ? x : t;
+}
+
+__device__ __forceinline__ float swiglu_f64(float g, float u, const SwigluK& K) {
+  const double gd = g;
+  const double t = exp_nonpos_core(-fabs(gd), K);
   const double n = gd * (double)u;
   const double num = gd >= 0.0 ? n : n * t;
   const double d = 1.0 + t;
