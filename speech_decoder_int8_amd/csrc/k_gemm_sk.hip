@@ -383,14 +383,14 @@ static hipError_t launch_gemm_skinny_rows(hipStream_t st, int M, int row0, int K
   const int per_tile = epi == EPI_SWIGLU ? ROWS / 2 : ROWS;
   P.tiles = (P.ncols + per_tile - 1) / per_tile;
   const int nss = K / SS;
-  // split K until the launch has about one workgroup per CU, with at least
-  // 2 steps per split (a split costs every workgroup its atomic additions,
-  // so a launch that already covers the chip, such as the 172 gate/up
-  // tiles of an 11008-wide MLP, is not split); launches of more than
-  // SK_MAX_SPLIT_TILES tiles are not split
+  // split K (at most 8 ways) until the launch has about one workgroup per
+  // CU, with at least 2 steps per split (a split costs every workgroup its
+  // atomic additions, so a launch that already covers the chip, such as the
+  // 172 gate/up tiles of an 11008-wide MLP, is not split); launches of more
+  // than SK_MAX_SPLIT_TILES tiles are not split
   int ks = 1;
   if (P.tiles <= SK_MAX_SPLIT_TILES)
-    while (ks < 16 && P.tiles * ks * 2 <= 256 && nss / (ks * 2) >= 2) ks *= 2;
+    while (ks < 8 && P.tiles * ks * 2 <= 256 && nss / (ks * 2) >= 2) ks *= 2;
   P.nss = (nss + ks - 1) / ks;
   P.ks = (nss + P.nss - 1) / P.nss;
   P.part = (int32_t*)scratch;
