@@ -322,6 +322,28 @@ def gpu_bench(args):
     return result
 
 
+def prefill_probe() -> None:
+    """Only the coalesced 16 x 387 prefill at T = 512: one untimed call, then
+    one timed call (for counter passes, which slow every dispatch)."""
+    import torch
+
+    import synth
+    from speech_decoder_int8_amd import ark
+
+    ark.lib()
+    torch.cuda.set_device(0)
+    cfg = synth.CONFIGS["c1"]
+    gm = ark.load_model(cfg, synth)
+    c4 = synth.CONFIGS["c4"]
+    xe = torch.randn((c4.batch, c4.prefill_len, cfg.hidden), device="cuda")
+    run = Run(torch, ark, gm, c4.batch, c4.prefill_len)
+    run.prefill(xe, [0] * c4.batch)
+    t = timed(torch, lambda: run.prefill(xe, [0] * c4.batch))
+    R = c4.batch * c4.prefill_len
+    print(json.dumps({"workload": "prefill 16x387, T=512", "ms": round(t * 1e3, 3),
+                      "int8_ops": prefill_int8_ops(cfg, R, c4.batch)}), flush=True)
+
+
 def copy_probe(mib: int) -> None:
     """A plain device-to-device copy of `mib` MiB, 8 times: under
     `rocprofv3 --pmc FETCH_SIZE` (or WRITE_SIZE) each dispatch should read
@@ -393,6 +415,8 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a device buffer of MIB MiB 8 times and exit (a plain copy "
                          "kernel of known size, to scale the HBM byte counters)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only run the 16x387 prefill twice and exit (for counter passes)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -404,6 +428,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.prefill_only:
+        prefill_probe()
         return
     result = gpu_bench(args)
     result["cpu_baseline"] = cpu_baseline(args.cpu_layers) if args.cpu else None
