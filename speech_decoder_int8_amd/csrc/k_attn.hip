@@ -442,28 +442,38 @@ __global__ __launch_bounds__(128) void k_attn_combine(int S, int NH, int nsplit,
   const int i = idx % S, h = (idx / S) % NH, b = idx / (S * NH);
   const double* src = part + (size_t)idx * nsplit * kPart;
   const int d = threadIdx.x;
-  // the splits' states are requested 8 at a time, so the loads overlap
-  // instead of each waiting for the previous one
-  constexpr int U = 8;
-  double M = -INFINITY;
-  for (int s0 = 0; s0 < nsplit; s0 += U) {
-    double mv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) mv[u] = s0 + u < nsplit ? src[(s0 + u) * kPart] : -INFINITY;
-#pragma unroll
-    for (int u = 0; u < U; ++u) M = fmax(M, mv[u]);
-  }
-  double L = 0.0, O = 0.0;
+  // the states of up to 16 splits are requested together before any is
+  // used (one round trip for a 512-row cache); each split is weighted by
+  // exp(m_s - M) with M the maximum of the m_s seen so far, and a later
+  // group with a larger maximum rescales what was summed before it
+  constexpr int U = 16;
+  double M = -INFINITY, L = 0.0, O = 0.0;
   for (int s0 = 0; s0 < nsplit; s0 += U) {
     double ms[U], ls[U], os[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool ok = s0 + u < nsplit;
       const double* q = src + (size_t)(ok ? s0 + u : 0) * kPart;
-      ms[u] = ok ? q[0] : -INFINITY;
+      ms[u] = q[0];
       ls[u] = q[1];
       os[u] = q[2 + d];
     }
+    // every load is out before any value is used (not sunk into the
+    // per-split branches below, each with its own wait)
+#pragma unroll
+    for (int u = 0; u < U; ++u) asm volatile("" : "+v"(ms[u]), "+v"(ls[u]), "+v"(os[u]));
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (s0 + u >= nsplit) ms[u] = -INFINITY;
+    double Mg = M;
+#pragma unroll
+    for (int u = 0; u < U; ++u) Mg = fmax(Mg, ms[u]);
+    if (Mg != M && M != -INFINITY) {
+      const double a = exp(M - Mg);
+      L *= a;
+      O *= a;
+    }
+    M = Mg;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (ms[u] == -INFINITY) continue;
