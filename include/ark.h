@@ -242,7 +242,7 @@ int ark_test_dynquant(int32_t B, int32_t R, int32_t K, const float* x, uint8_t* 
  * exact sum_k (code - zp) * w; y [B*R][W->n] fp32 dequantised output with
  * bias.  use_gemm selects the kernel: 0 the decode GEMV (requires B*R <= 4);
  * 1 the matrix-core GEMM as the decoder dispatches it (few-row kernel, one
- * pass per 32 rows, for B*R < 128 and W->k % 128 == 0, large-tile kernel for
+ * pass per 64 rows, for B*R < 128 and W->k % 128 == 0, large-tile kernel for
  * B*R >= 128, tiled kernel otherwise); 2 the tiled kernel for any B*R.  workspace >=
  * ark_test_qlinear_workspace_bytes(B*R, W->k, use_gemm).  Errors: ARK_E_NULL,
  * ARK_E_SHAPE, ARK_E_WORKSPACE. */

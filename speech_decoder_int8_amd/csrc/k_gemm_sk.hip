@@ -1,10 +1,11 @@
-// int8 x int8 -> int32 GEMM for few activation rows (M <= 32: batched decode
+// int8 x int8 -> int32 GEMM for few activation rows (M <= 64: batched decode
 // and the LM head of a batch), weight-stream bound, on gfx950 matrix cores
 // (v_mfma_i32_32x32x32_i8), with the same dequantising epilogues as k_gemm
 // (store (+bias), residual add, SwiGLU over paired gate/up rows).
 //
-// One 32x32x32 instruction covers all M rows, so every weight byte is read
-// from HBM exactly once and feeds one instruction.  A workgroup of 4 waves
+// One 32x32x32 instruction covers a block of 32 rows; up to two blocks (MB)
+// share each weight fragment, so every weight byte is read from HBM once
+// per pass of up to 64 rows.  A workgroup of 4 waves
 // owns 128 weight rows (wave w: rows 32 w .. 32 w + 31; for SwiGLU 16 gate
 // rows and the 16 up rows of the same outputs) and a range of K, walked in
 // 128-byte steps.  Each step's tiles (128 weight rows and the 32 activation
@@ -35,8 +36,15 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 namespace sk {
 constexpr int NT = 256, ROWS = 128, SS = 128, NS = 3;
-constexpr int B_BYTES = ROWS * SS, A_BYTES = 32 * SS, STAGE = B_BYTES + A_BYTES;
-constexpr int LDS = NS * STAGE;
+constexpr int B_BYTES = ROWS * SS;
+// MB blocks of 32 activation rows (1, or 2 for 33..64 rows: the weights are
+// streamed once for all of them)
+template <int MB>
+struct Cfg {
+  static constexpr int A_BYTES = 32 * MB * SS, STAGE = B_BYTES + A_BYTES, LDS = NS * STAGE;
+  static constexpr int LPW = 4 + MB;  // loads per wave per step
+};
+constexpr int MAX_MB = 2;
 }  // namespace sk
 
 struct GemmSkParams {
@@ -47,7 +55,7 @@ struct GemmSkParams {
   const int* qz;
   Seg seg[3];
   int seg_start[4];
-  int32_t* part;     // [tiles][32][ROWS] int32 sums of split launches, zero between launches
+  int32_t* part;     // [tiles][32 MB][ROWS] int32 sums of split launches, zero between launches
   uint32_t* ctr;     // [tiles] arrival counters, zero between launches
   int32_t* acc_out;  // optional [M][ncols]: raw sums (tests)
 };
@@ -59,8 +67,10 @@ __device__ __forceinline__ void sk_wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+template <int MB>
 __global__ __launch_bounds__(256, 2) void k_gemm_sk(GemmSkParams P) {
   using namespace sk;
+  constexpr int STAGE = Cfg<MB>::STAGE, LPW = Cfg<MB>::LPW;
   extern __shared__ __align__(16) int8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool swiglu = P.epi == EPI_SWIGLU;
@@ -94,11 +104,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm_sk(GemmSkParams P) {
       }
     }
   }
-  const int8_t* asrc;
-  {
-    const int r = 8 * wave + (lane >> 3);
+  // activation instruction a of this wave covers rows 8 (MB wave + a) .. + 7
+  const int8_t* asrc[MB];
+#pragma unroll
+  for (int a = 0; a < MB; ++a) {
+    const int r = 8 * (MB * wave + a) + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
-    asrc = P.A + (size_t)(r < P.M ? r : 0) * K + 16 * c;
+    asrc[a] = P.A + (size_t)(r < P.M ? r : 0) * K + 16 * c;
   }
   const int s0 = kp * P.nss, s1 = min(s0 + P.nss, K / SS);
   const int nk = s1 - s0;
@@ -111,20 +123,24 @@ __global__ __launch_bounds__(256, 2) void k_gemm_sk(GemmSkParams P) {
       __builtin_amdgcn_global_load_lds(
           (const void __attribute__((address_space(1)))*)(bsrc[i] + o),
           (void __attribute__((address_space(3)))*)(base + (4 * wave + i) * 1024), 16, 0, 2);
-    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(asrc + o),
-                                     (void __attribute__((address_space(3)))*)(base + B_BYTES +
-                                                                               wave * 1024),
-                                     16, 0, 0);
+#pragma unroll
+    for (int a = 0; a < MB; ++a)
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(asrc[a] + o),
+          (void __attribute__((address_space(3)))*)(base + B_BYTES + (MB * wave + a) * 1024), 16,
+          0, 0);
   };
   for (int st = 0; st < NS - 1; ++st)
     if (st < nk) issue(st, st);
 
-  i32x16 acc;
+  i32x16 acc[MB];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0;
+  for (int bI = 0; bI < MB; ++bI)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[bI][r] = 0;
   for (int st = 0; st < nk; ++st) {
     if (st + 1 < nk)
-      sk_wait_vm<5>();  // this wave's loads of step st are done (step st+1's may be in flight)
+      sk_wait_vm<LPW>();  // this wave's loads of step st are done (step st+1's may be in flight)
     else
       sk_wait_vm<0>();
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
@@ -132,27 +148,34 @@ __global__ __launch_bounds__(256, 2) void k_gemm_sk(GemmSkParams P) {
     if (st + NS - 1 < nk) issue(st + NS - 1, (st + NS - 1) % NS);
     const int8_t* Bs = lds + (st % NS) * STAGE;
     const int8_t* As = Bs + B_BYTES;
-    i32x4 fa[4], fb[4];
+    i32x4 fa[MB][4], fb[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      fa[c] = *(const i32x4*)(As + sk_swz(j, 2 * c + half));
+#pragma unroll
+      for (int bI = 0; bI < MB; ++bI)
+        fa[bI][c] = *(const i32x4*)(As + sk_swz(32 * bI + j, 2 * c + half));
       fb[c] = *(const i32x4*)(Bs + sk_swz(32 * wave + j, 2 * c + half));
     }
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[c], fb[c], acc, 0, 0, 0);
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int bI = 0; bI < MB; ++bI)
+        acc[bI] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[bI][c], fb[c], acc[bI], 0, 0, 0);
   }
 
   if (P.ks > 1) {
     // add this K range's sums into the tile's block (device-scope atomics,
     // performed at the coherence point); the last arrival reads the block
     // back, clears it for the next launch and runs the epilogue
-    int32_t* blk = P.part + (size_t)tile * 32 * ROWS;
+    int32_t* blk = P.part + (size_t)tile * 32 * MB * ROWS;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = (r / 4) * 8 + half * 4 + r % 4;
-      __hip_atomic_fetch_add(blk + m * ROWS + wave * 32 + j, acc[r], __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-    }
+    for (int bI = 0; bI < MB; ++bI)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = 32 * bI + (r / 4) * 8 + half * 4 + r % 4;
+        __hip_atomic_fetch_add(blk + m * ROWS + wave * 32 + j, acc[bI][r], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+      }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's additions are performed
     __syncthreads();
     __shared__ uint32_t last;
@@ -164,22 +187,31 @@ __global__ __launch_bounds__(256, 2) void k_gemm_sk(GemmSkParams P) {
     __syncthreads();
     if (!last) return;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = (r / 4) * 8 + half * 4 + r % 4;
-      int32_t* a = blk + m * ROWS + wave * 32 + j;
-      acc[r] = __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    for (int bI = 0; bI < MB; ++bI)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = (r / 4) * 8 + half * 4 + r % 4;
-      __hip_atomic_store(blk + m * ROWS + wave * 32 + j, 0, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    }
+      for (int r = 0; r < 16; ++r) {
+        const int m = 32 * bI + (r / 4) * 8 + half * 4 + r % 4;
+        int32_t* a = blk + m * ROWS + wave * 32 + j;
+        acc[bI][r] = __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+#pragma unroll
+    for (int bI = 0; bI < MB; ++bI)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = 32 * bI + (r / 4) * 8 + half * 4 + r % 4;
+        __hip_atomic_store(blk + m * ROWS + wave * 32 + j, 0, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
     if (tid == 0)
       __hip_atomic_store(P.ctr + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  // ---- epilogue: row m = (r / 4) * 8 + half * 4 + r % 4, weight row j.
+  // ---- epilogue, once per block of 32 activation rows (rows mb .. mb + 31)
+#pragma unroll
+  for (int bI = 0; bI < MB; ++bI) {
+  const int mb = 32 * bI;
+  const i32x16 accb = acc[bI];
+  // ---- epilogue: row m = mb + (r / 4) * 8 + half * 4 + r % 4, weight row j.
   // Parameter-block fields are taken as wave-uniform values (a per-lane
   // choice between them would become a vector load of the block), and every
   // per-row parameter and residual input is requested in one batch before
@@ -192,7 +224,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_sk(GemmSkParams P) {
   int rz[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const int m = min((r / 4) * 8 + half * 4 + r % 4, M - 1);
+    const int m = min(mb + (r / 4) * 8 + half * 4 + r % 4, M - 1);
     const int b = (row0 + m) / rps;
     rs[r] = qs[b];
     rz[r] = qz[b];
@@ -221,8 +253,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_sk(GemmSkParams P) {
     int ag[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int up = __shfl_down(acc[r], 16, 32);  // lane j < 16 gets row j's up sum
-      ag[r] = acc[r] + rz[r] * cg;
+      const int up = __shfl_down(accb[r], 16, 32);  // lane j < 16 gets row j's up sum
+      ag[r] = accb[r] + rz[r] * cg;
       const float g = dequant(ag[r], rs[r], sg);
       const float u = dequant(up + rz[r] * cu, rs[r], su);
       y[r] = swiglu_f64(g, u, SK);
@@ -235,7 +267,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_sk(GemmSkParams P) {
     if (j < 16 && n < P.ncols) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = (r / 4) * 8 + half * 4 + r % 4;
+        const int m = mb + (r / 4) * 8 + half * 4 + r % 4;
         if (m >= M) continue;
         out[(size_t)m * ldo + n] = y[r];
         if (acc_out) acc_out[(size_t)m * P.ncols + n] = ag[r];
@@ -275,7 +307,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_sk(GemmSkParams P) {
     if (resid) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = min((r / 4) * 8 + half * 4 + r % 4, M - 1);
+        const int m = min(mb + (r / 4) * 8 + half * 4 + r % 4, M - 1);
         old[r] = out[(size_t)m * ldo + n];
       }
     }
@@ -285,7 +317,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_sk(GemmSkParams P) {
     int at[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      at[r] = acc[r] + rz[r] * csv;
+      at[r] = accb[r] + rz[r] * csv;
       float y = dequant(at[r], rs[r], swv);
       if (bias) y = y + bv;
       val[r] = resid ? old[r] + y : y;
@@ -297,12 +329,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm_sk(GemmSkParams P) {
     if (col < P.ncols) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = (r / 4) * 8 + half * 4 + r % 4;
+        const int m = mb + (r / 4) * 8 + half * 4 + r % 4;
         if (m >= M) continue;
         out[(size_t)m * ldo + n] = val[r];
         if (acc_out) acc_out[(size_t)m * P.ncols + col] = at[r];
       }
     }
+  }
   }
 }
 
@@ -312,7 +345,7 @@ constexpr int SK_MAX_SPLIT_TILES = 256;  // row tiles of a K-split launch
 
 size_t gemm_skinny_ws_bytes() {
   // sum blocks of the tiles of a split launch, then the tile counters
-  return (size_t)SK_MAX_SPLIT_TILES * 32 * sk::ROWS * 4 + SK_MAX_SPLIT_TILES * 4;
+  return (size_t)SK_MAX_SPLIT_TILES * 32 * sk::MAX_MB * sk::ROWS * 4 + SK_MAX_SPLIT_TILES * 4;
 }
 
 __global__ void k_zero_u32(uint32_t* p, int n) {
@@ -334,11 +367,11 @@ hipError_t launch_gemm_skinny(hipStream_t st, int M, int K, const int8_t* codes,
                               const int* z, int rows_per_seq, const Seg* segs, int nseg, Epi epi,
                               int32_t* acc_out, void* scratch) {
   using namespace sk;
-  // more than 32 rows: one launch per 32 rows (the weights are streamed once
+  // more than 64 rows: one launch per 64 rows (the weights are streamed once
   // per launch; a few extra passes cost far less than a row-tiled GEMM with
   // a handful of workgroups)
-  if (M > 32) {
-    for (int r0 = 0; r0 < M; r0 += 32) {
+  if (M > 32 * MAX_MB) {
+    for (int r0 = 0; r0 < M; r0 += 32 * MAX_MB) {
       Seg sub[3];
       for (int i = 0; i < nseg; ++i) {
         sub[i] = segs[i];
@@ -348,7 +381,7 @@ hipError_t launch_gemm_skinny(hipStream_t st, int M, int K, const int8_t* codes,
       for (int i = 0; i < nseg; ++i) ncols += segs[i].n;
       if (epi == EPI_SWIGLU) ncols = segs[0].n;
       const hipError_t e = launch_gemm_skinny_rows(
-          st, min(32, M - r0), r0, K, codes + (size_t)r0 * K, s, z, rows_per_seq, sub, nseg, epi,
+          st, min(32 * MAX_MB, M - r0), r0, K, codes + (size_t)r0 * K, s, z, rows_per_seq, sub, nseg, epi,
           acc_out ? acc_out + (size_t)r0 * ncols : nullptr, scratch);
       if (e != hipSuccess) return e;
     }
@@ -356,6 +389,20 @@ hipError_t launch_gemm_skinny(hipStream_t st, int M, int K, const int8_t* codes,
   }
   return launch_gemm_skinny_rows(st, M, 0, K, codes, s, z, rows_per_seq, segs, nseg, epi, acc_out,
                                  scratch);
+}
+
+template <int MB>
+static hipError_t launch_sk(hipStream_t st, const GemmSkParams& P) {
+  static bool attr = false;
+  if (!attr) {
+    const hipError_t e = hipFuncSetAttribute((const void*)k_gemm_sk<MB>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             sk::Cfg<MB>::LDS);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL(k_gemm_sk<MB>, dim3(P.tiles * P.ks), dim3(sk::NT), sk::Cfg<MB>::LDS, st, P);
+  return hipGetLastError();
 }
 
 static hipError_t launch_gemm_skinny_rows(hipStream_t st, int M, int row0, int K,
@@ -394,16 +441,8 @@ static hipError_t launch_gemm_skinny_rows(hipStream_t st, int M, int row0, int K
   P.nss = (nss + ks - 1) / ks;
   P.ks = (nss + P.nss - 1) / P.nss;
   P.part = (int32_t*)scratch;
-  P.ctr = (uint32_t*)((char*)scratch + (size_t)SK_MAX_SPLIT_TILES * 32 * ROWS * 4);
-  static bool attr = false;
-  if (!attr) {
-    const hipError_t e =
-        hipFuncSetAttribute((const void*)k_gemm_sk, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
-  hipLaunchKernelGGL(k_gemm_sk, dim3(P.tiles * P.ks), dim3(NT), LDS, st, P);
-  return hipGetLastError();
+  P.ctr = (uint32_t*)((char*)scratch + (size_t)SK_MAX_SPLIT_TILES * 32 * MAX_MB * ROWS * 4);
+  return M > 32 ? launch_sk<2>(st, P) : launch_sk<1>(st, P);
 }
 
 }  // namespace ark

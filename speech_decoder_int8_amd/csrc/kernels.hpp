@@ -224,7 +224,7 @@ hipError_t launch_gemm_big(hipStream_t st, int M, int K, const int8_t* codes, co
                            const int* z, int rows_per_seq, const Seg* segs, int nseg, Epi epi,
                            int32_t* acc_out, const SeqStats* stats = nullptr);
 // Few-row GEMM (k_gemm_sk.hip, M < 128: batched decode, LM head of a
-// batch, short prompts; one pass per 32 rows): same contract; scratch =
+// batch, short prompts; one pass per 64 rows): same contract; scratch =
 // gemm_skinny_ws_bytes() bytes whose counter words are zero
 // (gemm_skinny_reset) and stay zero between launches.
 bool gemm_skinny_supported(int M, int K);
