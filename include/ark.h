@@ -35,7 +35,11 @@
  *
  * Conventions for every entry point:
  *   - Pointers are device memory unless marked [host].  The caller owns all
- *     memory; the library allocates nothing and keeps no state between calls.
+ *     memory; the library allocates no device memory.  State kept between
+ *     calls lives in the caller's workspace (the persistent decode kernel's
+ *     exchange area, its launch counter and error word), except for
+ *     process-wide one-time kernel set-up (guarded, thread-safe) and the
+ *     benchmark instrumentation of ark_profile_arm (not thread-safe).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls only enqueue work on it; results are valid once the caller has
  *     synchronised the stream.  The host arrays passed in are read before
@@ -64,7 +68,10 @@ enum ark_status {
   ARK_E_RANGE = -3,       /* cache_position < 0 or cache_position + S > T */
   ARK_E_WORKSPACE = -4,   /* workspace smaller than ark_workspace_bytes() */
   ARK_E_HIP = -5,         /* a HIP launch failed */
-  ARK_E_ALIGN = -6        /* a pointer is not aligned as documented */
+  ARK_E_ALIGN = -6,       /* a pointer is not aligned as documented */
+  ARK_E_TIMEOUT = -7      /* a bounded wait of the persistent batch-1 decode
+                             kernel gave up: the outputs of that step (and of
+                             every greedy step fed from it) are invalid */
 };
 
 /* Model geometry.  Supported: 1 <= n_layers <= 64, head_dim == 128,
@@ -172,12 +179,30 @@ int ark_prefill(const ark_model* m, int32_t B, int32_t S, const float* embeds,
 /* One decode step (S = 1) for B sequences: token_ids [B] int32 (device) are
  * gathered from m->embed_f16, then the same computation as ark_prefill.
  * k_delta, v_delta: [n_layers][B][1][n_kv][128].  Other arguments and
- * errors as ark_prefill with S = 1. */
+ * errors as ark_prefill with S = 1.  At B = 1 with the ARK geometry the
+ * step is one persistent cooperative kernel (ark_decode_path) whose
+ * workgroups exchange data through bounded waits; the return value reports
+ * only the launch, so a caller that needs to know that every wait was met
+ * calls ark_decode_check afterwards. */
 int ark_decode_step(const ark_model* m, int32_t B, const int32_t* token_ids,
                     const int32_t* cache_position, const float* const* k_cache,
                     const float* const* v_cache, float* k_delta, float* v_delta,
                     float* logits, float* hidden_out, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/* Status of the last decode step enqueued on this workspace for B
+ * sequences: synchronises `stream`, then returns ARK_E_TIMEOUT if the
+ * persistent kernel (ark_decode_path(m, B) == 1) had a wait give up, else
+ * ARK_OK (the multi-kernel path has no bounded waits).  Errors: ARK_E_NULL,
+ * ARK_E_SHAPE, ARK_E_WORKSPACE, ARK_E_HIP. */
+int ark_decode_check(const ark_model* m, int32_t B, const void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* Which decode path ark_decode_step / ark_greedy_decode take for B
+ * sequences: 1 = the persistent batch-1 kernel, 0 = the multi-kernel path;
+ * negative: ARK_E_NULL / ARK_E_SHAPE.  (The environment variable
+ * ARK_DECODE_PATH=multi forces the multi-kernel path.) */
+int ark_decode_path(const ark_model* m, int32_t B);
 
 /* ----------------------------------------------------------------- a12 -- */
 
@@ -216,7 +241,9 @@ int ark_cache_write(const ark_dims* d, int32_t B, int32_t S, const int32_t* cach
  * [B][vocab] (last step's logits on return).  mask: [vocab] uint8.
  * check_every (>= 1): the host reads the finished flags every this many
  * steps; larger values avoid a host round trip per step but may run up to
- * check_every - 1 steps after the last sequence finished. */
+ * check_every - 1 steps after the last sequence finished.  On the
+ * persistent path the kernel's error word is read at the same points and at
+ * the end: a timed-out wait returns ARK_E_TIMEOUT instead of a count. */
 int ark_greedy_decode(const ark_model* m, int32_t B, int32_t* token_ids,
                       int32_t* cache_position, float* const* k_cache,
                       float* const* v_cache, float* k_delta, float* v_delta,
@@ -311,10 +338,71 @@ const char* ark_dominant_kernel(void);
 
 /* Diagnostics of the persistent batch-1 decode kernel: when the environment
  * variable ARK_MEGA_TRACE is "1", each decode step records 100 MHz
- * real-time-counter stamps at its phase boundaries (workgroups 0, 1 and 255;
- * uint64 [3][n_layers + 1][16]) at this byte offset of the workspace.
- * 0 if the dims are invalid. */
+ * real-time-counter stamps at this byte offset of the workspace: uint64
+ * [3][n_layers + 1][32] (workgroups 0, 1 and 255: events 0..15 at the
+ * phase boundaries of every layer, 16..31 inside phases), then uint64
+ * [256][16] (every workgroup, for layer 2 only).  0 if the dims are
+ * invalid.  The test-only environment variable ARK_TEST_SPIN_LIMIT (rounds,
+ * >= 0) replaces the bound of the kernel's waits; 0 makes every wait give
+ * up at once (the kernel still runs to completion, and the step reports
+ * ARK_E_TIMEOUT through ark_decode_check / ark_greedy_decode). */
 size_t ark_decode_trace_offset(const ark_dims* d);
+
+/* ------------------------------------------- re-anchored parity record --
+ * Test access (the parity protocol "bit-exact codes on the GPU's own
+ * tensors"): the dump variants of prefill and decode run the same kernels
+ * as ark_prefill / ark_decode_step (the persistent decode kernel as an
+ * instantiation that also stores its record) and also write, for every
+ * layer l whose bit is set in layer_mask, one record of the tensors each
+ * of the layer's four dynamic quantisations saw and produced (model card
+ * "Files": int8 MatMuls on activations quantised at run time), and, when
+ * logits are requested, one record of the LM head's input quantisation.
+ * Layer records follow each other in increasing l, then the head record;
+ * every field starts 256-byte aligned at the offsets ark_dump_layout
+ * gives.  R = B * S rows, row r of sequence r / S.  Codes are stored as
+ * int8 (code - 128).  s / z: [4][B], point order h1, attention, h2, SwiGLU. */
+enum ark_dump_field {
+  ARK_DUMP_H1 = 0,    /* f32 [R][hidden]  RMSNorm 1 output (quantised for q|k|v) */
+  ARK_DUMP_QKV = 1,   /* f32 [R][q+2kv]   q|k|v projections with bias, before rotary */
+  ARK_DUMP_ATTN = 2,  /* f32 [R][q]       attention output (quantised for o) */
+  ARK_DUMP_X1 = 3,    /* f32 [R][hidden]  x + o */
+  ARK_DUMP_H2 = 4,    /* f32 [R][hidden]  RMSNorm 2 output (quantised for gate|up) */
+  ARK_DUMP_A = 5,     /* f32 [R][inter]   SwiGLU output (quantised for down) */
+  ARK_DUMP_X2 = 6,    /* f32 [R][hidden]  x1 + down: the layer's output */
+  ARK_DUMP_C1 = 7,    /* i8  [R][hidden]  codes of h1 */
+  ARK_DUMP_C2 = 8,    /* i8  [R][q]       codes of the attention output */
+  ARK_DUMP_C3 = 9,    /* i8  [R][hidden]  codes of h2 */
+  ARK_DUMP_C4 = 10,   /* i8  [R][inter]   codes of the SwiGLU output */
+  ARK_DUMP_S = 11,    /* f32 [4][B]       scales */
+  ARK_DUMP_Z = 12,    /* i32 [4][B]       zero points */
+  ARK_DUMP_NFIELDS = 13
+};
+/* Head record: f32 [B][hidden] final-norm output of each last row, i8
+ * [B][hidden] its codes, f32 [B] scales, i32 [B] zero points. */
+
+/* Bytes of the record for B sequences of S rows with the layers of
+ * layer_mask (bits >= n_layers ignored); fills field_off[ARK_DUMP_NFIELDS]
+ * (offsets inside a layer record), *record_bytes (one layer record) and
+ * head_off[4] (absolute offsets of the head fields) when not NULL.  0 if the
+ * dims or sizes are invalid. */
+size_t ark_dump_layout(const ark_dims* d, int32_t B, int32_t S, uint64_t layer_mask,
+                       size_t* field_off, size_t* record_bytes, size_t* head_off);
+
+/* ark_prefill / ark_decode_step plus the record described above, written to
+ * dump (device, 256-byte aligned, >= ark_dump_layout(...) bytes).  Errors
+ * as the plain calls, plus ARK_E_WORKSPACE when dump_bytes is too small. */
+int ark_prefill_dump(const ark_model* m, int32_t B, int32_t S, const float* embeds,
+                     const int32_t* cache_position, const float* const* k_cache,
+                     const float* const* v_cache, float* k_delta, float* v_delta,
+                     float* logits, float* hidden_out, void* workspace,
+                     size_t workspace_bytes, void* stream, void* dump, size_t dump_bytes,
+                     uint64_t layer_mask);
+int ark_decode_step_dump(const ark_model* m, int32_t B, const int32_t* token_ids,
+                         const int32_t* cache_position, const float* const* k_cache,
+                         const float* const* v_cache, float* k_delta, float* v_delta,
+                         float* logits, float* hidden_out, void* workspace,
+                         size_t workspace_bytes, void* stream, void* dump,
+                         size_t dump_bytes, uint64_t layer_mask);
 
 #ifdef __cplusplus
 }

@@ -17,6 +17,10 @@ LIB_PATH = os.path.join(HERE, "libark.so")
 
 ARK_OK, ARK_E_NULL, ARK_E_SHAPE, ARK_E_RANGE, ARK_E_WORKSPACE, ARK_E_HIP, ARK_E_ALIGN = \
     0, -1, -2, -3, -4, -5, -6
+ARK_E_TIMEOUT = -7
+
+# fields of a layer record of the parity dump (enum ark_dump_field)
+DUMP_FIELDS = ("h1", "qkv", "attn", "x1", "h2", "a", "x2", "c1", "c2", "c3", "c4", "s", "z")
 
 
 class ArkError(RuntimeError):
@@ -53,6 +57,7 @@ P = C.c_void_p
 I32 = C.c_int32
 PP = C.POINTER(C.c_void_p)
 PI32 = C.POINTER(C.c_int32)
+PSZ = C.POINTER(C.c_size_t)
 
 _SIGS = {
     "ark_workspace_bytes": (C.c_size_t, [C.POINTER(ArkDims), I32, I32]),
@@ -84,6 +89,13 @@ _SIGS = {
     "ark_profile_count": (C.c_int32, []),
     "ark_dominant_kernel": (C.c_char_p, []),
     "ark_decode_trace_offset": (C.c_size_t, [C.POINTER(ArkDims)]),
+    "ark_decode_check": (C.c_int, [C.POINTER(ArkModel), I32, P, C.c_size_t, P]),
+    "ark_decode_path": (C.c_int, [C.POINTER(ArkModel), I32]),
+    "ark_dump_layout": (C.c_size_t, [C.POINTER(ArkDims), I32, I32, C.c_uint64, PSZ, PSZ, PSZ]),
+    "ark_prefill_dump": (C.c_int, [C.POINTER(ArkModel), I32, I32, P, PI32, PP, PP, P, P, P, P, P,
+                                   C.c_size_t, P, P, C.c_size_t, C.c_uint64]),
+    "ark_decode_step_dump": (C.c_int, [C.POINTER(ArkModel), I32, P, PI32, PP, PP, P, P, P, P, P,
+                                       C.c_size_t, P, P, C.c_size_t, C.c_uint64]),
 }
 
 _LIB = None
@@ -306,6 +318,99 @@ def decode_step(model: DeviceModel, token_ids, cache_position, k_cache, v_cache,
         C.byref(model.c), B, _ptr(token_ids), _pos_array(cache_position), _ptr_array(k_cache),
         _ptr_array(v_cache), _ptr(k_delta), _ptr(v_delta), _ptr(logits), _ptr(hidden_out),
         _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def decode_check(model: DeviceModel, B: int, ws, stream=None) -> int:
+    """Status of the last decode step on ws (synchronises the stream):
+    ARK_OK or ARK_E_TIMEOUT; raises on other errors."""
+    st = lib().ark_decode_check(C.byref(model.c), B, _ptr(ws), ws.numel(), _stream(stream))
+    if st not in (ARK_OK, ARK_E_TIMEOUT):
+        _check("ark_decode_check", st)
+    return st
+
+
+def decode_path(model: DeviceModel, B: int) -> int:
+    """1: the persistent batch-1 kernel serves B sequences; 0: the multi-kernel path."""
+    return _check("ark_decode_path", lib().ark_decode_path(C.byref(model.c), B))
+
+
+class DumpRecord:
+    """Device buffer of a re-anchored parity record and its layout
+    (ark_dump_layout); read() copies it to host numpy arrays."""
+
+    def __init__(self, model: DeviceModel, B: int, S: int, layers):
+        import torch
+        self.model, self.B, self.S = model, B, S
+        self.layers = sorted(set(int(l) for l in layers))
+        self.mask = 0
+        for l in self.layers:
+            self.mask |= 1 << l
+        f = (C.c_size_t * 13)()
+        rec = C.c_size_t()
+        head = (C.c_size_t * 4)()
+        self.nbytes = lib().ark_dump_layout(C.byref(model.dims), B, S, C.c_uint64(self.mask), f,
+                                            C.byref(rec), head)
+        if self.nbytes == 0:
+            raise ArkError("ark_dump_layout", ARK_E_SHAPE, "invalid dims")
+        self.field_off, self.rec, self.head_off = list(f), rec.value, list(head)
+        self.buf = torch.zeros(self.nbytes, dtype=torch.uint8, device="cuda")
+
+    def read(self):
+        """{layer: {field: array}} and the head record {hn, hc, s, z}; codes
+        as uint8 (code - 128 stored, 128 added back)."""
+        import torch
+        torch.cuda.synchronize()
+        raw = self.buf.cpu().numpy()
+        cfg = self.model.cfg
+        B, R = self.B, self.B * self.S
+        H, Q = cfg.hidden, cfg.n_heads * cfg.head_dim
+        KV, I = cfg.n_kv_heads * cfg.head_dim, cfg.intermediate
+        shapes = {"h1": (R, H), "qkv": (R, Q + 2 * KV), "attn": (R, Q), "x1": (R, H), "h2": (R, H),
+                  "a": (R, I), "x2": (R, H), "c1": (R, H), "c2": (R, Q), "c3": (R, H), "c4": (R, I),
+                  "s": (4, B), "z": (4, B)}
+        out = {}
+        for i, l in enumerate(self.layers):
+            base = i * self.rec
+            d = {}
+            for k, name in enumerate(DUMP_FIELDS):
+                shp = shapes[name]
+                n = int(np.prod(shp))
+                o = base + self.field_off[k]
+                if name[0] == "c":
+                    d[name] = (raw[o:o + n].view(np.int8).astype(np.int16) + 128).astype(np.uint8).reshape(shp)
+                elif name == "z":
+                    d[name] = raw[o:o + 4 * n].view(np.int32).reshape(shp).copy()
+                else:
+                    d[name] = raw[o:o + 4 * n].view(np.float32).reshape(shp).copy()
+            out[l] = d
+        ho = self.head_off
+        head = {"hn": raw[ho[0]:ho[0] + 4 * B * H].view(np.float32).reshape(B, H).copy(),
+                "hc": (raw[ho[1]:ho[1] + B * H].view(np.int8).astype(np.int16) + 128).astype(np.uint8).reshape(B, H),
+                "s": raw[ho[2]:ho[2] + 4 * B].view(np.float32).copy(),
+                "z": raw[ho[3]:ho[3] + 4 * B].view(np.int32).copy()}
+        return out, head
+
+
+def prefill_dump(model: DeviceModel, embeds, cache_position, k_cache, v_cache, k_delta, v_delta,
+                 rec: DumpRecord, logits=None, hidden_out=None, ws=None, stream=None):
+    B, S = embeds.shape[0], embeds.shape[1]
+    if ws is None:
+        ws = workspace(model, B, S)
+    _check("ark_prefill_dump", lib().ark_prefill_dump(
+        C.byref(model.c), B, S, _ptr(embeds), _pos_array(cache_position), _ptr_array(k_cache),
+        _ptr_array(v_cache), _ptr(k_delta), _ptr(v_delta), _ptr(logits), _ptr(hidden_out),
+        _ptr(ws), ws.numel(), _stream(stream), _ptr(rec.buf), rec.nbytes, C.c_uint64(rec.mask)))
+
+
+def decode_step_dump(model: DeviceModel, token_ids, cache_position, k_cache, v_cache, k_delta,
+                     v_delta, rec: DumpRecord, logits=None, hidden_out=None, ws=None, stream=None):
+    B = token_ids.shape[0]
+    if ws is None:
+        ws = workspace(model, B, 1)
+    _check("ark_decode_step_dump", lib().ark_decode_step_dump(
+        C.byref(model.c), B, _ptr(token_ids), _pos_array(cache_position), _ptr_array(k_cache),
+        _ptr_array(v_cache), _ptr(k_delta), _ptr(v_delta), _ptr(logits), _ptr(hidden_out),
+        _ptr(ws), ws.numel(), _stream(stream), _ptr(rec.buf), rec.nbytes, C.c_uint64(rec.mask)))
 
 
 def masked_argmax(logits, mask, out_ids, stream=None):

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <vector>
 
 #include "../../include/ark.h"
@@ -61,6 +62,61 @@ Plan plan(const ark_dims& d, int B, int S) {
   p.mega = take(B == 1 ? decode_mega_ws_bytes(d.n_layers, d.max_total_len) : 0);
   p.total = o;
   return p;
+}
+
+// Re-anchored parity record layout (ark_dump_layout): per recorded layer
+// the fields of ark_dump_field, each 256-byte aligned; after the layer
+// records the LM-head record.
+struct DumpLayout {
+  size_t f[ARK_DUMP_NFIELDS];
+  size_t rec;
+  size_t head[4];  // relative to the head record
+  size_t head_bytes;
+};
+
+DumpLayout dump_layout(const ark_dims& d, int B, int S) {
+  const size_t R = (size_t)B * S, H = d.hidden, Q = (size_t)d.n_heads * d.head_dim;
+  const size_t KV = (size_t)d.n_kv_heads * d.head_dim, I = d.intermediate;
+  const size_t sz[ARK_DUMP_NFIELDS] = {R * H * 4, R * (Q + 2 * KV) * 4, R * Q * 4, R * H * 4,
+                                       R * H * 4, R * I * 4,            R * H * 4, R * H,
+                                       R * Q,     R * H,                R * I,     4 * (size_t)B * 4,
+                                       4 * (size_t)B * 4};
+  DumpLayout L;
+  size_t o = 0;
+  for (int i = 0; i < ARK_DUMP_NFIELDS; ++i) {
+    L.f[i] = o;
+    o += align_up(sz[i]);
+  }
+  L.rec = o;
+  const size_t hs[4] = {(size_t)B * H * 4, (size_t)B * H, (size_t)B * 4, (size_t)B * 4};
+  o = 0;
+  for (int i = 0; i < 4; ++i) {
+    L.head[i] = o;
+    o += align_up(hs[i]);
+  }
+  L.head_bytes = o;
+  return L;
+}
+
+int popcount_below(uint64_t mask, int l) {
+  return __builtin_popcountll(l >= 64 ? mask : (mask & ((1ull << l) - 1)));
+}
+
+size_t dump_total(const ark_dims& d, int B, int S, uint64_t mask) {
+  const DumpLayout L = dump_layout(d, B, S);
+  return (size_t)popcount_below(mask, d.n_layers) * L.rec + L.head_bytes;
+}
+
+DumpRec dump_rec(const ark_dims& d, int B, int S, uint64_t mask, void* base) {
+  const DumpLayout L = dump_layout(d, B, S);
+  DumpRec r;
+  r.base = (char*)base;
+  r.mask = d.n_layers >= 64 ? mask : (mask & ((1ull << d.n_layers) - 1));
+  r.rec = L.rec;
+  for (int i = 0; i < ARK_DUMP_NFIELDS; ++i) r.f[i] = L.f[i];
+  const size_t h0 = (size_t)popcount_below(r.mask, d.n_layers) * L.rec;
+  for (int i = 0; i < 4; ++i) r.head[i] = h0 + L.head[i];
+  return r;
 }
 
 bool dims_ok(const ark_dims& d) {
@@ -145,21 +201,26 @@ inline Seg seg_of(const ark_qlinear& q, float* out, int ldo) {
 }
 
 // Benchmark instrumentation (see ark_profile_arm).
+// Process-wide and meant for one benchmarking thread; the members are
+// atomic so that decode calls on other threads, which only read them while
+// nothing is armed, never race with the arming.
 struct Profiler {
-  hipEvent_t* ev = nullptr;
-  int n = 0;
-  int count = 0;
+  std::atomic<hipEvent_t*> ev{nullptr};
+  std::atomic<int> n{0};
+  std::atomic<int> count{0};
 };
 Profiler g_prof;
 
-inline void prof_begin(hipStream_t st, bool dominant) {
-  if (dominant && g_prof.ev && g_prof.count < g_prof.n) hipEventRecord(g_prof.ev[2 * g_prof.count], st);
-}
-inline void prof_end(hipStream_t st, bool dominant) {
-  if (dominant && g_prof.ev && g_prof.count < g_prof.n) {
-    hipEventRecord(g_prof.ev[2 * g_prof.count + 1], st);
-    ++g_prof.count;
-  }
+// The event pair of the next recorded launch, or false when not armed or full.
+inline bool prof_claim(hipEvent_t& b, hipEvent_t& e) {
+  hipEvent_t* ev = g_prof.ev.load();
+  if (!ev) return false;
+  const int i = g_prof.count.load();
+  if (i >= g_prof.n.load()) return false;
+  g_prof.count.store(i + 1);
+  b = ev[2 * i];
+  e = ev[2 * i + 1];
+  return true;
 }
 
 #define HIP_TRY(expr)                       \
@@ -168,11 +229,49 @@ inline void prof_end(hipStream_t st, bool dominant) {
   } while (0)
 
 // All layers and the LM head over the rows already in x ([B*S][H]).
+#define D2D(dst, src, bytes)                                                                  \
+  do {                                                                                        \
+    char* dst_ = (dst);                                                                       \
+    if (dst_) HIP_TRY(hipMemcpyAsync(dst_, (src), (bytes), hipMemcpyDeviceToDevice, st));     \
+  } while (0)
+
+// All layers and the LM head over the rows already in x ([B*S][H]).  dr
+// (optional): the parity record to fill (copies of the workspace tensors
+// after each step; the quantisers also write the values they quantised).
 int run_forward(const ark_model* m, int B, int S, float* x, const int32_t* pos_host,
                 const float* const* kc, const float* const* vc, float* kd, float* vd,
-                float* logits, char* ws, hipStream_t st) {
+                float* logits, char* ws, hipStream_t st, const DumpRec* dr = nullptr) {
   const ark_dims& d = m->d;
   const Plan p = plan(d, B, S);
+  // field f of layer l's record, or nullptr when layer l is not recorded
+  auto dptr = [&](int l, int f) -> char* {
+    if (!dr || !dr->base || !((dr->mask >> l) & 1)) return nullptr;
+    return dr->base + (size_t)popcount_below(dr->mask, l) * dr->rec + dr->f[f];
+  };
+  // quantisation record of point pt (0: h1, 1: attention, 2: h2, 3: SwiGLU)
+  QDump qd[4];
+  auto qdp = [&](int l, int pt) -> const QDump* {
+    char* c = dptr(l, ARK_DUMP_C1 + pt);
+    if (!c) return nullptr;
+    const int hf[4] = {ARK_DUMP_H1, -1, ARK_DUMP_H2, -1};
+    qd[pt].h = hf[pt] >= 0 ? (float*)dptr(l, hf[pt]) : nullptr;
+    qd[pt].codes = (int8_t*)c;
+    qd[pt].s = (float*)dptr(l, ARK_DUMP_S) + (size_t)pt * B;
+    qd[pt].z = (int*)dptr(l, ARK_DUMP_Z) + (size_t)pt * B;
+    return &qd[pt];
+  };
+  // after a workspace quantiser: its codes [R][K] and (s, z)
+  auto qcopy = [&](int l, int pt, const int8_t* codes, const float* qs, const int* qz, int K) {
+    const QDump* q = qdp(l, pt);
+    if (!q) return (int)ARK_OK;
+    const size_t R = (size_t)B * S;
+    if (hipMemcpyAsync(q->codes, codes, R * K, hipMemcpyDeviceToDevice, st) != hipSuccess ||
+        hipMemcpyAsync(q->s, qs, (size_t)B * 4, hipMemcpyDeviceToDevice, st) != hipSuccess ||
+        hipMemcpyAsync(q->z, qz, (size_t)B * 4, hipMemcpyDeviceToDevice, st) != hipSuccess)
+      return (int)ARK_E_HIP;
+    return (int)ARK_OK;
+  };
+#define QCOPY(l, pt, K) HIP_TRY(qcopy((l), (pt), codes, qs, qz, (K)) == ARK_OK ? hipSuccess : hipErrorUnknown)
   const int R = B * S, H = d.hidden, NH = d.n_heads, NKV = d.n_kv_heads;
   const int Q = NH * kHeadDim, KV = NKV * kHeadDim, I = d.intermediate, T = d.max_total_len;
   const bool gemv = (S == 1 && B <= 4);
@@ -211,15 +310,20 @@ int run_forward(const ark_model* m, int B, int S, float* x, const int32_t* pos_h
     Seg gus[2] = {seg_of(L.gate, a, I), seg_of(L.up, a, I)};
     Seg ds[1] = {seg_of(L.down, x, H)};
     if (gemv) {
-      HIP_TRY(launch_gemv(st, B, H, x, H, L.ln1, d.rms_eps, qkvs, 3, EPI_STORE));
+      HIP_TRY(launch_gemv(st, B, H, x, H, L.ln1, d.rms_eps, qkvs, 3, EPI_STORE, qdp(l, 0)));
     } else if (rowq) {
-      HIP_TRY(launch_norm_quant_row(st, B, H, x, H, L.ln1, d.rms_eps, codes, qs, qz));
+      HIP_TRY(launch_norm_quant_row(st, B, H, x, H, L.ln1, d.rms_eps, codes, qs, qz,
+                                    (float*)dptr(l, ARK_DUMP_H1)));
+      QCOPY(l, 0, H);
       HIP_TRY(launch_gemm(st, R, H, codes, qs, qz, S, qkvs, 3, EPI_STORE, nullptr, gsk));
     } else {
       HIP_TRY(launch_row_stats(st, R, H, S, x, H, L.ln1, d.rms_eps, rs, sa));
-      HIP_TRY(launch_quant_seq(st, R, H, S, x, H, rs, L.ln1, sa.cur, codes, nullptr, qs, qz));
+      HIP_TRY(launch_quant_seq(st, R, H, S, x, H, rs, L.ln1, sa.cur, codes, nullptr, qs, qz,
+                               (float*)dptr(l, ARK_DUMP_H1)));
+      QCOPY(l, 0, H);
       HIP_TRY(launch_gemm(st, R, H, codes, qs, qz, S, qkvs, 3, EPI_STORE, nullptr, gsk));
     }
+    D2D(dptr(l, ARK_DUMP_QKV), qkv, (size_t)R * ldqkv * 4);
     // decode: the rotary step runs inside the attention kernel
     const bool rope_in_attn = S == 1 && NH / NKV <= 8;
     if (!rope_in_attn)
@@ -228,55 +332,87 @@ int run_forward(const ark_model* m, int B, int S, float* x, const int32_t* pos_h
     const bool att_stats = !gemv && !rowq && attention_stats(S, NH, NKV);
     HIP_TRY(launch_attention(st, B, S, NH, NKV, T, q, kc[l], vc[l], kdl, vdl, pos, attn, part,
                              att_stats ? &sb : nullptr, rope_in_attn ? &ri : nullptr));
+    D2D(dptr(l, ARK_DUMP_ATTN), attn, (size_t)R * Q * 4);
     if (gemv) {
-      HIP_TRY(launch_gemv(st, B, Q, attn, Q, nullptr, 0.0, os, 1, EPI_RESID));
-      prof_begin(st, B == 1);
-      HIP_TRY(launch_gemv(st, B, H, x, H, L.ln2, d.rms_eps, gus, 2, EPI_SWIGLU));
-      prof_end(st, B == 1);
-      HIP_TRY(launch_gemv(st, B, I, a, I, nullptr, 0.0, ds, 1, EPI_RESID));
+      HIP_TRY(launch_gemv(st, B, Q, attn, Q, nullptr, 0.0, os, 1, EPI_RESID, qdp(l, 1)));
+      D2D(dptr(l, ARK_DUMP_X1), x, (size_t)R * H * 4);
+      hipEvent_t eb = nullptr, ee = nullptr;
+      const bool prof = B == 1 && prof_claim(eb, ee);
+      if (prof) HIP_TRY(hipEventRecord(eb, st));
+      HIP_TRY(launch_gemv(st, B, H, x, H, L.ln2, d.rms_eps, gus, 2, EPI_SWIGLU, qdp(l, 2)));
+      if (prof) HIP_TRY(hipEventRecord(ee, st));
+      D2D(dptr(l, ARK_DUMP_A), a, (size_t)R * I * 4);
+      HIP_TRY(launch_gemv(st, B, I, a, I, nullptr, 0.0, ds, 1, EPI_RESID, qdp(l, 3)));
     } else if (rowq) {
       HIP_TRY(launch_norm_quant_row(st, B, Q, attn, Q, nullptr, 0.0, codes, qs, qz));
+      QCOPY(l, 1, Q);
       HIP_TRY(launch_gemm(st, R, Q, codes, qs, qz, S, os, 1, EPI_RESID, nullptr, gsk));
-      HIP_TRY(launch_norm_quant_row(st, B, H, x, H, L.ln2, d.rms_eps, codes, qs, qz));
+      D2D(dptr(l, ARK_DUMP_X1), x, (size_t)R * H * 4);
+      HIP_TRY(launch_norm_quant_row(st, B, H, x, H, L.ln2, d.rms_eps, codes, qs, qz,
+                                    (float*)dptr(l, ARK_DUMP_H2)));
+      QCOPY(l, 2, H);
       HIP_TRY(launch_gemm(st, R, H, codes, qs, qz, S, gus, 2, EPI_SWIGLU, nullptr, gsk));
+      D2D(dptr(l, ARK_DUMP_A), a, (size_t)R * I * 4);
       HIP_TRY(launch_norm_quant_row(st, B, I, a, I, nullptr, 0.0, codes, qs, qz));
+      QCOPY(l, 3, I);
       HIP_TRY(launch_gemm(st, R, I, codes, qs, qz, S, ds, 1, EPI_RESID, nullptr, gsk));
     } else {
       if (!att_stats) HIP_TRY(launch_row_stats(st, R, Q, S, attn, Q, nullptr, 0.0, nullptr, sb));
       HIP_TRY(launch_quant_seq(st, R, Q, S, attn, Q, nullptr, nullptr, sb.cur, codes, nullptr, qs,
                                qz));
+      QCOPY(l, 1, Q);
       HIP_TRY(launch_gemm(st, R, Q, codes, qs, qz, S, os, 1, EPI_RESID, nullptr, gsk));
+      D2D(dptr(l, ARK_DUMP_X1), x, (size_t)R * H * 4);
       HIP_TRY(launch_row_stats(st, R, H, S, x, H, L.ln2, d.rms_eps, rs, sa));
-      HIP_TRY(launch_quant_seq(st, R, H, S, x, H, rs, L.ln2, sa.cur, codes, nullptr, qs, qz));
+      HIP_TRY(launch_quant_seq(st, R, H, S, x, H, rs, L.ln2, sa.cur, codes, nullptr, qs, qz,
+                               (float*)dptr(l, ARK_DUMP_H2)));
+      QCOPY(l, 2, H);
       const bool gu_stats = gemm_swiglu_stats(R, H, gsk);
       HIP_TRY(launch_gemm(st, R, H, codes, qs, qz, S, gus, 2, EPI_SWIGLU, nullptr, gsk, false,
                           gu_stats ? &sb : nullptr));
+      D2D(dptr(l, ARK_DUMP_A), a, (size_t)R * I * 4);
       if (!gu_stats) HIP_TRY(launch_row_stats(st, R, I, S, a, I, nullptr, 0.0, nullptr, sb));
       HIP_TRY(launch_quant_seq(st, R, I, S, a, I, nullptr, nullptr, sb.cur, codes, nullptr, qs, qz));
+      QCOPY(l, 3, I);
       HIP_TRY(launch_gemm(st, R, I, codes, qs, qz, S, ds, 1, EPI_RESID, nullptr, gsk));
     }
+    D2D(dptr(l, ARK_DUMP_X2), x, (size_t)R * H * 4);
   }
 
   if (logits) {
     Seg lm[1] = {seg_of(m->lm_head, logits, d.vocab)};
     const float* last = x + (size_t)(S - 1) * H;  // row S-1 of each sequence, stride S*H
+    QDump hq = {nullptr, nullptr, nullptr, nullptr};
+    if (dr && dr->base) {
+      hq.h = (float*)(dr->base + dr->head[0]);
+      hq.codes = (int8_t*)(dr->base + dr->head[1]);
+      hq.s = (float*)(dr->base + dr->head[2]);
+      hq.z = (int*)(dr->base + dr->head[3]);
+    }
     if (B <= 4) {
-      HIP_TRY(launch_gemv(st, B, H, last, S * H, m->final_norm, d.rms_eps, lm, 1, EPI_STORE));
+      HIP_TRY(launch_gemv(st, B, H, last, S * H, m->final_norm, d.rms_eps, lm, 1, EPI_STORE,
+                          hq.codes ? &hq : nullptr));
     } else {
       if (norm_quant_row_supported(H)) {
         HIP_TRY(launch_norm_quant_row(st, B, H, last, S * H, m->final_norm, d.rms_eps, codes, qs,
-                                      qz));
+                                      qz, hq.h));
       } else {
         // set A is clear here: the last producer of the layers (if any) filled B
         HIP_TRY(launch_row_stats(st, B, H, 1, last, S * H, m->final_norm, d.rms_eps, rs, sa));
         HIP_TRY(launch_quant_seq(st, B, H, 1, last, S * H, rs, m->final_norm, sa.cur, codes,
-                                 nullptr, qs, qz));
+                                 nullptr, qs, qz, hq.h));
+      }
+      if (hq.codes) {
+        HIP_TRY(hipMemcpyAsync(hq.codes, codes, (size_t)B * H, hipMemcpyDeviceToDevice, st));
+        HIP_TRY(hipMemcpyAsync(hq.s, qs, (size_t)B * 4, hipMemcpyDeviceToDevice, st));
+        HIP_TRY(hipMemcpyAsync(hq.z, qz, (size_t)B * 4, hipMemcpyDeviceToDevice, st));
       }
       HIP_TRY(launch_gemm(st, B, H, codes, qs, qz, 1, lm, 1, EPI_STORE, nullptr, gsk));
     }
   }
   return ARK_OK;
 }
+#undef QCOPY
 
 int mega_upload(const ark_model* m, const float* const* kc, const float* const* vc, char* ws,
                 hipStream_t st) {
@@ -304,9 +440,19 @@ int mega_upload(const ark_model* m, const float* const* kc, const float* const* 
              : ARK_E_HIP;
 }
 
+// Bound of the persistent kernel's waits: the default, or the value of
+// ARK_TEST_SPIN_LIMIT (tests of the time-out report set it, e.g. to 0).
+int64_t mega_spin_limit() {
+  const char* e = getenv("ARK_TEST_SPIN_LIMIT");
+  if (!e || !*e) return -1;
+  char* end = nullptr;
+  const long long v = strtoll(e, &end, 10);
+  return (end && *end == 0 && v >= 0) ? (int64_t)v : -1;
+}
+
 int mega_step(const ark_model* m, const int32_t* token, int pos, float* kd, float* vd,
               float* logits, float* hidden_out, const uint8_t* mask, int32_t* out_token, char* ws,
-              hipStream_t st) {
+              hipStream_t st, const DumpRec* dr = nullptr) {
   const ark_dims& d = m->d;
   const Plan p = plan(d, 1, 1);
   MegaStep S;
@@ -329,18 +475,88 @@ int mega_step(const ark_model* m, const int32_t* token, int pos, float* kd, floa
   S.hidden_out = hidden_out;
   S.mask = logits ? mask : nullptr;
   S.out_token = out_token;
+  memset(&S.dump, 0, sizeof(S.dump));
+  if (dr) S.dump = *dr;
+  S.spin_limit = mega_spin_limit();
   hipEvent_t eb = nullptr, ee = nullptr;
-  if (g_prof.ev && g_prof.count < g_prof.n) {
-    eb = g_prof.ev[2 * g_prof.count];
-    ee = g_prof.ev[2 * g_prof.count + 1];
-    ++g_prof.count;
-  }
+  prof_claim(eb, ee);
   const hipError_t e = decode_mega_launch(st, ws + p.mega, S, eb, ee);
   return e == hipSuccess ? ARK_OK : ARK_E_HIP;
 }
 
 bool mega_ready(const ark_model* m, int B) {
   return use_mega(m->d, B, 1) && decode_mega_init() == hipSuccess;
+}
+
+// Synchronise the stream, then read the persistent kernel's error word.
+int mega_check(const ark_model* m, const char* ws, hipStream_t st) {
+  const Plan p = plan(m->d, 1, 1);
+  uint32_t word = 0;
+  const uint32_t* w = decode_mega_err_word(ws + p.mega, m->d.n_layers, m->d.max_total_len);
+  if (hipStreamSynchronize(st) != hipSuccess ||
+      hipMemcpy(&word, w, 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return ARK_E_HIP;
+  return word ? ARK_E_TIMEOUT : ARK_OK;
+}
+
+int prefill_impl(const ark_model* m, int32_t B, int32_t S, const float* embeds,
+                 const int32_t* cache_position, const float* const* k_cache,
+                 const float* const* v_cache, float* k_delta, float* v_delta, float* logits,
+                 float* hidden_out, void* workspace, size_t workspace_bytes, void* stream,
+                 const DumpRec* dr) {
+  int e = check_model(m, false);
+  if (e) return e;
+  if (!embeds) return ARK_E_NULL;
+  e = check_step(m, B, S, cache_position, k_cache, v_cache, k_delta, v_delta, logits, workspace,
+                 workspace_bytes);
+  if (e) return e;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const Plan p = plan(m->d, B, S);
+  float* x = hidden_out ? hidden_out : (float*)(ws + p.x);
+  const size_t xb = (size_t)B * S * m->d.hidden * 4;
+  if (hipMemcpyAsync(x, embeds, xb, hipMemcpyDeviceToDevice, st) != hipSuccess) return ARK_E_HIP;
+  return run_forward(m, B, S, x, cache_position, k_cache, v_cache, k_delta, v_delta, logits, ws,
+                     st, dr);
+}
+
+int decode_impl(const ark_model* m, int32_t B, const int32_t* token_ids,
+                const int32_t* cache_position, const float* const* k_cache,
+                const float* const* v_cache, float* k_delta, float* v_delta, float* logits,
+                float* hidden_out, void* workspace, size_t workspace_bytes, void* stream,
+                const DumpRec* dr) {
+  int e = check_model(m, true);
+  if (e) return e;
+  if (!token_ids) return ARK_E_NULL;
+  e = check_step(m, B, 1, cache_position, k_cache, v_cache, k_delta, v_delta, logits, workspace,
+                 workspace_bytes);
+  if (e) return e;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  if (mega_ready(m, B)) {
+    if ((e = mega_upload(m, k_cache, v_cache, ws, st))) return e;
+    return mega_step(m, token_ids, cache_position[0], k_delta, v_delta, logits, hidden_out, nullptr,
+                     nullptr, ws, st, dr);
+  }
+  const Plan p = plan(m->d, B, 1);
+  float* x = hidden_out ? hidden_out : (float*)(ws + p.x);
+  if (launch_embed(st, B, 1, m->d.hidden, m->d.vocab, token_ids, m->embed_f16, nullptr, 0, 0, x) !=
+      hipSuccess)
+    return ARK_E_HIP;
+  return run_forward(m, B, 1, x, cache_position, k_cache, v_cache, k_delta, v_delta, logits, ws,
+                     st, dr);
+}
+
+// Validate a parity record request and build its descriptor.
+int dump_check(const ark_model* m, int B, int S, void* dump, size_t dump_bytes, uint64_t mask,
+               DumpRec* out) {
+  if (!m) return ARK_E_NULL;
+  if (!dump) return ARK_E_NULL;
+  if (!dims_ok(m->d) || B < 1 || B > kMaxBatch || S < 1) return ARK_E_SHAPE;
+  if (!aligned(dump, kAlign)) return ARK_E_ALIGN;
+  if (dump_bytes < dump_total(m->d, B, S, mask)) return ARK_E_WORKSPACE;
+  *out = dump_rec(m->d, B, S, mask, dump);
+  return ARK_OK;
 }
 
 }  // namespace
@@ -356,6 +572,8 @@ const char* ark_status_string(int status) {
     case ARK_E_WORKSPACE: return "workspace too small";
     case ARK_E_HIP: return "HIP launch failed";
     case ARK_E_ALIGN: return "pointer misaligned";
+    case ARK_E_TIMEOUT:
+      return "a bounded wait of the persistent decode kernel timed out; that step's outputs are invalid";
     default: return "unknown status";
   }
 }
@@ -400,46 +618,69 @@ int ark_prefill(const ark_model* m, int32_t B, int32_t S, const float* embeds,
                 const int32_t* cache_position, const float* const* k_cache,
                 const float* const* v_cache, float* k_delta, float* v_delta, float* logits,
                 float* hidden_out, void* workspace, size_t workspace_bytes, void* stream) {
-  int e = check_model(m, false);
-  if (e) return e;
-  if (!embeds) return ARK_E_NULL;
-  e = check_step(m, B, S, cache_position, k_cache, v_cache, k_delta, v_delta, logits, workspace,
-                 workspace_bytes);
-  if (e) return e;
-  hipStream_t st = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-  const Plan p = plan(m->d, B, S);
-  float* x = hidden_out ? hidden_out : (float*)(ws + p.x);
-  const size_t xb = (size_t)B * S * m->d.hidden * 4;
-  if (hipMemcpyAsync(x, embeds, xb, hipMemcpyDeviceToDevice, st) != hipSuccess) return ARK_E_HIP;
-  return run_forward(m, B, S, x, cache_position, k_cache, v_cache, k_delta, v_delta, logits, ws,
-                     st);
+  return prefill_impl(m, B, S, embeds, cache_position, k_cache, v_cache, k_delta, v_delta, logits,
+                      hidden_out, workspace, workspace_bytes, stream, nullptr);
 }
 
 int ark_decode_step(const ark_model* m, int32_t B, const int32_t* token_ids,
                     const int32_t* cache_position, const float* const* k_cache,
                     const float* const* v_cache, float* k_delta, float* v_delta, float* logits,
                     float* hidden_out, void* workspace, size_t workspace_bytes, void* stream) {
-  int e = check_model(m, true);
-  if (e) return e;
-  if (!token_ids) return ARK_E_NULL;
-  e = check_step(m, B, 1, cache_position, k_cache, v_cache, k_delta, v_delta, logits, workspace,
-                 workspace_bytes);
-  if (e) return e;
+  return decode_impl(m, B, token_ids, cache_position, k_cache, v_cache, k_delta, v_delta, logits,
+                     hidden_out, workspace, workspace_bytes, stream, nullptr);
+}
+
+int ark_decode_check(const ark_model* m, int32_t B, const void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  if (!m || !workspace) return ARK_E_NULL;
+  if (!dims_ok(m->d) || B < 1 || B > kMaxBatch) return ARK_E_SHAPE;
+  if (workspace_bytes < plan(m->d, B, 1).total) return ARK_E_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-  if (mega_ready(m, B)) {
-    if ((e = mega_upload(m, k_cache, v_cache, ws, st))) return e;
-    return mega_step(m, token_ids, cache_position[0], k_delta, v_delta, logits, hidden_out, nullptr,
-                     nullptr, ws, st);
-  }
-  const Plan p = plan(m->d, B, 1);
-  float* x = hidden_out ? hidden_out : (float*)(ws + p.x);
-  if (launch_embed(st, B, 1, m->d.hidden, m->d.vocab, token_ids, m->embed_f16, nullptr, 0, 0, x) !=
-      hipSuccess)
-    return ARK_E_HIP;
-  return run_forward(m, B, 1, x, cache_position, k_cache, v_cache, k_delta, v_delta, logits, ws,
-                     st);
+  if (!mega_ready(m, B)) return hipStreamSynchronize(st) == hipSuccess ? ARK_OK : ARK_E_HIP;
+  return mega_check(m, (const char*)workspace, st);
+}
+
+int ark_decode_path(const ark_model* m, int32_t B) {
+  if (!m) return ARK_E_NULL;
+  if (!dims_ok(m->d) || B < 1 || B > kMaxBatch) return ARK_E_SHAPE;
+  return mega_ready(m, B) ? 1 : 0;
+}
+
+size_t ark_dump_layout(const ark_dims* d, int32_t B, int32_t S, uint64_t layer_mask,
+                       size_t* field_off, size_t* record_bytes, size_t* head_off) {
+  if (!d || !dims_ok(*d) || B < 1 || B > kMaxBatch || S < 1) return 0;
+  const DumpRec r = dump_rec(*d, B, S, layer_mask, nullptr);
+  if (field_off)
+    for (int i = 0; i < ARK_DUMP_NFIELDS; ++i) field_off[i] = r.f[i];
+  if (record_bytes) *record_bytes = r.rec;
+  if (head_off)
+    for (int i = 0; i < 4; ++i) head_off[i] = r.head[i];
+  return dump_total(*d, B, S, layer_mask);
+}
+
+int ark_prefill_dump(const ark_model* m, int32_t B, int32_t S, const float* embeds,
+                     const int32_t* cache_position, const float* const* k_cache,
+                     const float* const* v_cache, float* k_delta, float* v_delta, float* logits,
+                     float* hidden_out, void* workspace, size_t workspace_bytes, void* stream,
+                     void* dump, size_t dump_bytes, uint64_t layer_mask) {
+  DumpRec dr;
+  const int e = dump_check(m, B, S, dump, dump_bytes, layer_mask, &dr);
+  if (e) return e;
+  return prefill_impl(m, B, S, embeds, cache_position, k_cache, v_cache, k_delta, v_delta, logits,
+                      hidden_out, workspace, workspace_bytes, stream, &dr);
+}
+
+int ark_decode_step_dump(const ark_model* m, int32_t B, const int32_t* token_ids,
+                         const int32_t* cache_position, const float* const* k_cache,
+                         const float* const* v_cache, float* k_delta, float* v_delta,
+                         float* logits, float* hidden_out, void* workspace,
+                         size_t workspace_bytes, void* stream, void* dump, size_t dump_bytes,
+                         uint64_t layer_mask) {
+  DumpRec dr;
+  const int e = dump_check(m, B, 1, dump, dump_bytes, layer_mask, &dr);
+  if (e) return e;
+  return decode_impl(m, B, token_ids, cache_position, k_cache, v_cache, k_delta, v_delta, logits,
+                     hidden_out, workspace, workspace_bytes, stream, &dr);
 }
 
 int ark_masked_argmax(int32_t B, int32_t V, const float* logits, const uint8_t* mask,
@@ -527,24 +768,34 @@ int ark_greedy_decode(const ark_model* m, int32_t B, int32_t* token_ids, int32_t
               hipSuccess ||
           hipStreamSynchronize(st) != hipSuccess)
         return ARK_E_HIP;
+      // a timed-out wait of the persistent kernel invalidates its step (and
+      // every token fed back after it): report it instead of the count
+      if (mega && (e = mega_check(m, ws, st))) return e;
       bool all = true;
       for (int b = 0; b < B; ++b) all = all && flags[b];
       if (all) break;
     }
   }
+  // the loop may have ended on the room check without a final sync
+  if (mega && steps > 0 && (e = mega_check(m, ws, st))) return e;
   for (int b = 0; b < B; ++b) cache_position[b] = pos[b];
   return steps;
 }
 
 int ark_profile_arm(void* const* events, int32_t n_pairs) {
   if (events && n_pairs < 1) return ARK_E_SHAPE;
-  g_prof.ev = events ? (hipEvent_t*)events : nullptr;
-  g_prof.n = events ? n_pairs : 0;
-  if (events) g_prof.count = 0;  // disarming keeps the count of the last armed run
+  if (events) {
+    g_prof.ev.store(nullptr);
+    g_prof.n.store(n_pairs);
+    g_prof.count.store(0);
+    g_prof.ev.store((hipEvent_t*)events);
+  } else {
+    g_prof.ev.store(nullptr);  // disarming keeps the count of the last armed run
+  }
   return ARK_OK;
 }
 
-int32_t ark_profile_count(void) { return g_prof.count; }
+int32_t ark_profile_count(void) { return g_prof.count.load(); }
 
 size_t ark_decode_trace_offset(const ark_dims* d) {
   if (!d || !dims_ok(*d)) return 0;

@@ -29,6 +29,9 @@
 #include <limits.h>
 #include <stdlib.h>
 
+#include <algorithm>
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -46,6 +49,12 @@ constexpr int NIH = 4;                    // items per (KV head, head group) alo
 constexpr int NATT = NKV * HH * NIH;      // workgroups that may hold an attention item
 constexpr int PART = 2 + D;               // fp64 words of one partial softmax state
 constexpr uint32_t SPIN_LIMIT = 1u << 15;  // ~30-60 ms per wait: a failure ends in seconds
+// The error word of a launch and the bound of its waits (rounds): a wait
+// that gives up sets a bit of the word and the kernel runs to completion.
+struct Err {
+  uint32_t* word;
+  uint32_t limit;
+};
 constexpr int NREP = 8;                   // replicas of each broadcast vector (one per XCD)
 constexpr unsigned long long MAGIC = 0x41524b5f58434831ull;
 
@@ -176,12 +185,23 @@ struct MegaArgs {
   uint32_t* ctr;
   float* amax_v;
   int* amax_i;
-  uint32_t* err;
+  Err err;
   u64* trace;  // optional phase timestamps [3 workgroups][L + 1][16]
   u64* marker;
   u64 marker_value;
   uint32_t* epoch;  // [0] last launch's tag, [1] this launch's tag
+  DumpRec dump;     // re-anchored parity record (instantiation with DUMP only)
 };
+
+// Fields of a layer record of the parity dump (the order of the public
+// layout: h1, q|k|v, attention output, x1, h2, SwiGLU output, x2, the four
+// code arrays, then s and z of the four quantisation points).
+enum { F_H1, F_QKV, F_ATTN, F_X1, F_H2, F_A, F_X2, F_C1, F_C2, F_C3, F_C4, F_S, F_Z };
+template <typename T>
+__device__ __forceinline__ T* dump_at(const DumpRec& d, int l, int f) {
+  if (!d.base || !((d.mask >> l) & 1)) return nullptr;
+  return (T*)(d.base + (size_t)__popcll(d.mask & ((1ull << l) - 1)) * d.rec + d.f[f]);
+}
 
 // Phase timestamps (100 MHz real-time counter) of workgroups 0, 1 and the
 // last one for every layer, and of every workgroup for one layer, when a
@@ -343,7 +363,7 @@ __device__ __forceinline__ void minmax16(const float* red, int lane, float& lo, 
 // SPIN_LIMIT rounds the error word is set and the wave goes on.  Returns
 // the number of sparse polls plus 65536 x the number of copies.
 __device__ uint32_t poll_range(const u64* v, int c0, int c1, int blk, unsigned char* dst,
-                               uint32_t* err, int lane, uint32_t tag, u64* tr = nullptr,
+                               Err err, int lane, uint32_t tag, u64* tr = nullptr,
                                const u64* flags = nullptr) {
   uint32_t spins = 0;
   const int b0 = c0 / blk, b1 = (c1 - 1) / blk;
@@ -352,8 +372,8 @@ __device__ uint32_t poll_range(const u64* v, int c0, int c1, int blk, unsigned c
     for (int b = b0 + lane; b <= b1; b += 64)
       ok &= (uint32_t)(xget(flags ? flags + b : v + max(c0, b * blk)) >> 32) == tag;
     if (__all(ok)) break;
-    if (++spins > SPIN_LIMIT) {
-      if (lane == 0) atomicOr(err, 1u);
+    if (++spins > err.limit) {
+      if (lane == 0) atomicOr(err.word, 1u);
       break;
     }
   }
@@ -368,8 +388,8 @@ __device__ uint32_t poll_range(const u64* v, int c0, int c1, int blk, unsigned c
 #pragma unroll 4
     for (int i = lane; i < c1 - c0; i += 64) ok &= (uint32_t)(s[i] >> 32) == tag;
     if (__all(ok)) break;
-    if (++spins > SPIN_LIMIT) {
-      if (lane == 0) atomicOr(err, 2u);
+    if (++spins > err.limit) {
+      if (lane == 0) atomicOr(err.word, 2u);
       break;
     }
   }
@@ -379,7 +399,7 @@ __device__ uint32_t poll_range(const u64* v, int c0, int c1, int blk, unsigned c
 // All waves: poll_range over words [0, n) of v, split into one chunk of
 // whole KiB per wave, staged at stage + 8 i.  Also waits for every load the
 // wave has in flight.  Returns wave 0's poll_range count.
-__device__ uint32_t poll_all(const u64* v, int n, int blk, unsigned char* stage, uint32_t* err,
+__device__ uint32_t poll_all(const u64* v, int n, int blk, unsigned char* stage, Err err,
                              int lane, int wave, uint32_t tag, u64* tr = nullptr,
                              const u64* flags = nullptr, int np = NW) {
   if (wave >= np) return 0;  // not a polling wave: its loads in flight stay in flight
@@ -411,8 +431,9 @@ __device__ __forceinline__ void unstage(const unsigned char* stage, float* dst, 
 // ----------------------------------------------------------- prologues --
 // RMSNorm (fp64 inside) of x with gain g, then the dynamic uint8 quantiser;
 // shifted codes to sh.codes.  All 512 threads.
+template <bool DUMP>
 __device__ QParam prologue_norm(const float* x, const float* g, double eps, Shared& sh, int tid,
-                                u64* tr = nullptr) {
+                                u64* tr = nullptr, const DumpRec* dump = nullptr) {
   if (tid == 0) stamp(tr, 0, 0);
   double ss = 0.0;
   for (int i = tid; i < H; i += NT) {
@@ -436,6 +457,19 @@ __device__ QParam prologue_norm(const float* x, const float* g, double eps, Shar
   const QParam p = quant_param(lo, hi);
 #pragma unroll
   for (int j = 0; j < H / NT; ++j) sh.codes[tid + j * NT] = shift_code(quant_code(hv[j], p));
+  if constexpr (DUMP) {
+    if (dump && dump->base) {
+#pragma unroll
+      for (int j = 0; j < H / NT; ++j) {
+        ((float*)(dump->base + dump->head[0]))[tid + j * NT] = hv[j];
+        ((int8_t*)(dump->base + dump->head[1]))[tid + j * NT] = sh.codes[tid + j * NT];
+      }
+      if (tid == 0) {
+        *(float*)(dump->base + dump->head[2]) = p.s;
+        *(int*)(dump->base + dump->head[3]) = p.z;
+      }
+    }
+  }
   __syncthreads();
   if (tid == 0) stamp(tr, 3, 0);
   return p;
@@ -470,11 +504,14 @@ constexpr int NORM_WAVES = 4;
 constexpr int NORM_PER_LANE = H / (NORM_WAVES * 64);
 // `after_poll` runs in every wave once its share of the vector has arrived
 // (loads it issues then do not delay this wait).
-template <typename AfterPoll>
+// With DUMP and dh != nullptr the values, codes and (s, z) are also written
+// to dh, dc, ds, dz.
+template <bool DUMP, typename AfterPoll>
 __device__ QParam poll_norm(const u64* v, int blk, float* x, Shared& sh, double eps, int lane,
-                            int wave, int tid, uint32_t tag, uint32_t* err, AfterPoll after_poll,
+                            int wave, int tid, uint32_t tag, Err err, AfterPoll after_poll,
                             u64* tr = nullptr, uint32_t* stat = nullptr, u64* tn0 = nullptr,
-                            u64* tn1 = nullptr, u64* tn2 = nullptr) {
+                            u64* tn1 = nullptr, u64* tn2 = nullptr, float* dh = nullptr,
+                            int8_t* dc = nullptr, float* ds = nullptr, int* dz = nullptr) {
   static_assert(H == NW * 128, "one 128-word chunk per wave");
   const uint32_t r = poll_all(v, H, blk, sh.stage, err, lane, wave, tag, tr);
   after_poll();
@@ -529,6 +566,19 @@ __device__ QParam poll_norm(const u64* v, int blk, float* x, Shared& sh, double 
       sh.qpf = p.s;
       sh.qpz = p.z;
     }
+    if constexpr (DUMP) {
+      if (dh) {
+#pragma unroll
+        for (int k = 0; k < NORM_PER_LANE; ++k) {
+          dh[i0 + 64 * k] = hv[k];
+          dc[i0 + 64 * k] = sh.codes[i0 + 64 * k];
+        }
+        if (wave == 0 && lane == 0) {
+          *ds = p.s;
+          *dz = p.z;
+        }
+      }
+    }
   }
   lds_barrier();
   if (tid == 0) stamp(tn2, 0, 0);
@@ -543,10 +593,12 @@ __device__ QParam poll_norm(const u64* v, int blk, float* x, Shared& sh, double 
 // then the dynamic uint8 quantiser on it (each wave on its own chunk when
 // all waves poll, else all waves on the whole vector after a barrier);
 // shifted codes to sh.codes.
+template <bool DUMP>
 __device__ QParam poll_quant(const u64* v, int n, int blk, Shared& sh, int lane, int wave,
-                             uint32_t tag, uint32_t* err, u64* tr = nullptr,
+                             uint32_t tag, Err err, u64* tr = nullptr,
                              const u64* flags = nullptr, uint32_t* stat = nullptr, int np = NW,
-                             bool pairs = false) {
+                             bool pairs = false, float* dh = nullptr, int8_t* dc = nullptr,
+                             float* ds = nullptr, int* dz = nullptr) {
   const int tid = wave * 64 + lane;
   const uint32_t r = poll_all(v, n, blk, sh.stage, err, lane, wave, tag, tr, flags, np);
   if (stat && tid == 0) *stat = r;
@@ -582,6 +634,18 @@ __device__ QParam poll_quant(const u64* v, int n, int blk, Shared& sh, int lane,
   if (pairs) return p;  // the quantisation parameters only
   for (int i = c0; i < c1; i += step)
     sh.codes[i] = shift_code(quant_code(__uint_as_float((uint32_t)st[i]), p));
+  if constexpr (DUMP) {
+    if (dh) {
+      for (int i = c0; i < c1; i += step) {
+        dh[i] = __uint_as_float((uint32_t)st[i]);
+        dc[i] = sh.codes[i];
+      }
+      if (tid == 0) {
+        *ds = p.s;
+        *dz = p.z;
+      }
+    }
+  }
   lds_barrier();
   return p;
 }
@@ -596,9 +660,12 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 // flight.  Wave w checks words [32 w, 32 w + 32) with four 64-byte loads per
 // round.  Bounded like poll_range.
 __device__ QParam poll_amm(const u64* v, Shared& sh, int lane, int wave, uint32_t tag,
-                           uint32_t* err, u64* tr = nullptr) {
+                           Err err, u64* tr = nullptr) {
   static_assert(NW * 32 == 2 * NWG, "one 32-word slice per wave covers every workgroup");
   if (wave == 0) stamp(tr, 0, lane);
+  // the address in scalar registers (readfirstlane) whether or not this
+  // function is inlined into a caller that knows it is wave-uniform
+  const u64* vw = (const u64*)uniform_ptr(v + wave * 32);
   i32x16 q[4];
   uint32_t spins = 0;
   for (;;) {
@@ -609,14 +676,14 @@ __device__ QParam poll_amm(const u64* v, Shared& sh, int lane, int wave, uint32_
         "s_load_dwordx16 %3, %4, 0xc0 glc\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&s"(q[0]), "=&s"(q[1]), "=&s"(q[2]), "=&s"(q[3])
-        : "s"(v + wave * 32)
+        : "s"(vw)
         : "memory");
     uint32_t bad = 0;
 #pragma unroll
     for (int k = 0; k < 32; ++k) bad |= (uint32_t)q[k / 8][2 * (k % 8) + 1] ^ tag;
     if (bad == 0) break;
-    if (++spins > SPIN_LIMIT) {
-      if (lane == 0) atomicOr(err, 8u);
+    if (++spins > err.limit) {
+      if (lane == 0) atomicOr(err.word, 8u);
       break;
     }
     __builtin_amdgcn_s_sleep(4);  // ~0.1 us: 4096 polling waves would crowd the scalar path
@@ -643,7 +710,7 @@ __device__ QParam poll_amm(const u64* v, Shared& sh, int lane, int wave, uint32_
 // blocks of blk words) and unpack them to sh.codes; all waves end at a
 // barrier.  The staging of each polling wave ends before DN_LDS.
 __device__ void poll_codes(const u64* v, int n, int blk, Shared& sh, int lane, int wave,
-                           uint32_t tag, uint32_t* err) {
+                           uint32_t tag, Err err) {
   poll_all(v, n, blk, sh.stage, err, lane, wave, tag, nullptr, nullptr, NPOLL);
   if (wave < NPOLL) {
     const int chunk = ((n + NPOLL - 1) / NPOLL + 127) & ~127;
@@ -1051,6 +1118,7 @@ __device__ void attention_item(const MegaArgs& A, uint32_t epoch, int l, int g, 
 }
 
 // ------------------------------------------------------------ the kernel --
+template <bool DUMP>
 __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Shared& sh = *(Shared*)smem_raw;
@@ -1207,12 +1275,31 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
     if (l >= 1 && l + 1 < A.L && tid < LTW)
       ((u64*)&sh.lt[(l + 1) & 1])[tid] = ((const u64*)&A.layers[l + 1])[tid];
 
+    // parity record of this layer (workgroup 0 records what every
+    // workgroup computes alike; the producers record their own rows)
+    float *d_qkv = nullptr, *d_x1 = nullptr, *d_a = nullptr, *d_x2 = nullptr, *d_s = nullptr;
+    int8_t* d_c4 = nullptr;
+    int* d_z = nullptr;
+    const bool d0 = DUMP && w == 0;
+    if constexpr (DUMP) {
+      d_qkv = dump_at<float>(A.dump, l, F_QKV);
+      d_x1 = dump_at<float>(A.dump, l, F_X1);
+      d_a = dump_at<float>(A.dump, l, F_A);
+      d_x2 = dump_at<float>(A.dump, l, F_X2);
+      d_c4 = dump_at<int8_t>(A.dump, l, F_C4);
+      d_s = dump_at<float>(A.dump, l, F_S);
+      d_z = dump_at<int>(A.dump, l, F_Z);
+    }
+
     // ---- q, k, v
     trace_at(A, w, l, 0);
     load_gain(Lw.ln1, sh.gain, wave, lane16);
-    QParam qp = poll_norm(xl + OFF_X0 + rep * H, R_D, sh.xs, sh, A.eps, lane, wave, tid, epoch,
+    QParam qp = poll_norm<DUMP>(xl + OFF_X0 + rep * H, R_D, sh.xs, sh, A.eps, lane, wave, tid, epoch,
                           A.err, [] {}, trace_sub(A, w, l, 27), trace_stat(A, w, l, 11),
-                          trace_sub(A, w, l, 11), trace_sub(A, w, l, 12), trace_sub(A, w, l, 13));
+                          trace_sub(A, w, l, 11), trace_sub(A, w, l, 12), trace_sub(A, w, l, 13),
+                          d0 ? dump_at<float>(A.dump, l, F_H1) : nullptr,
+                          d0 ? dump_at<int8_t>(A.dump, l, F_C1) : nullptr, d0 ? d_s : nullptr,
+                          d0 ? d_z : nullptr);
     trace_at(A, w, l, 2);
     {
       int accs[1];
@@ -1221,6 +1308,8 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
         float y = dequant(accs[0] + (128 - qp.z) * cq[0], qp.s, sq[0]);
         y = y + bq[0];
         xput(xl + OFF_QKV + w * R_QKV + s, y, epoch);
+        if constexpr (DUMP)
+          if (d_qkv) d_qkv[w * R_QKV + s] = y;
       }
     }
     trace_done(A, w, l, 3, lane);
@@ -1251,8 +1340,11 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
     // ---- o projection + residual
     asm volatile("" : "+v"(lane16), "+v"(tid), "+v"(lane));
     trace_at(A, w, l, 4);
-    qp = poll_quant(xl + OFF_ATT + rep * Q, Q, HPI * D, sh, lane, wave, epoch, A.err, nullptr, nullptr,
-                    trace_stat(A, w, l, 12));
+    qp = poll_quant<DUMP>(xl + OFF_ATT + rep * Q, Q, HPI * D, sh, lane, wave, epoch, A.err, nullptr,
+                          nullptr, trace_stat(A, w, l, 12), NW, false,
+                          d0 ? dump_at<float>(A.dump, l, F_ATTN) : nullptr,
+                          d0 ? dump_at<int8_t>(A.dump, l, F_C2) : nullptr, d0 ? d_s + 1 : nullptr,
+                          d0 ? d_z + 1 : nullptr);
     if (!att) issue_gate_up_lds(l);
     trace_at(A, w, l, 5);
     {
@@ -1262,6 +1354,8 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
         const int n = w * R_O + s;
         const float y = dequant(accs[0] + (128 - qp.z) * co[0], qp.s, so[0]);
         xput_rep(xl + OFF_X1, H, n, sh.xs[n] + y, epoch);
+        if constexpr (DUMP)
+          if (d_x1) d_x1[n] = sh.xs[n] + y;
       }
     }
     trace_done(A, w, l, 6, lane);
@@ -1271,9 +1365,12 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
     // ---- gate/up + SwiGLU
     asm volatile("" : "+v"(lane16), "+v"(tid), "+v"(lane));
     load_gain(Lw.ln2, sh.gain, wave, lane16);
-    qp = poll_norm(xl + OFF_X1 + rep * H, R_O, sh.x1s, sh, A.eps, lane, wave, tid, epoch, A.err,
-                   [] {}, trace_sub(A, w, l, 16), trace_stat(A, w, l, 13), trace_sub(A, w, l, 14),
-                   trace_sub(A, w, l, 15), trace_sub(A, w, l, 30));
+    qp = poll_norm<DUMP>(xl + OFF_X1 + rep * H, R_O, sh.x1s, sh, A.eps, lane, wave, tid, epoch,
+                         A.err, [] {}, trace_sub(A, w, l, 16), trace_stat(A, w, l, 13),
+                         trace_sub(A, w, l, 14), trace_sub(A, w, l, 15), trace_sub(A, w, l, 30),
+                         d0 ? dump_at<float>(A.dump, l, F_H2) : nullptr,
+                         d0 ? dump_at<int8_t>(A.dump, l, F_C3) : nullptr, d0 ? d_s + 2 : nullptr,
+                         d0 ? d_z + 2 : nullptr);
     trace_at(A, w, l, 7);
     if (!att) {
       const int zc = 128 - qp.z;
@@ -1319,6 +1416,8 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
       const double gd = gv;
       const float a = (float)(gd / (1.0 + exp_t(-gd, sh.expc)) * (double)uv);
       if (live) sh.aval[i] = a;
+      if constexpr (DUMP)
+        if (live && d_a) d_a[gu0 + i] = a;
       float lo = live ? a : INFINITY, hi = live ? a : -INFINITY;
       lo = fminf(lo, fminf(dpp::mov<dpp::kXor1>(lo), dpp::mov<dpp::kXor2>(lo)));
       hi = fmaxf(hi, fmaxf(dpp::mov<dpp::kXor1>(hi), dpp::mov<dpp::kXor2>(hi)));
@@ -1350,6 +1449,11 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
     // ---- SwiGLU quantisation parameters from all producers' min/max
     asm volatile("" : "+v"(lane16), "+v"(tid), "+v"(lane));
     qp = poll_amm(xl + OFF_AMM + rep * 2 * NWG, sh, lane, wave, epoch, A.err, trace_sub(A, w, l, 19));
+    if constexpr (DUMP)
+      if (d0 && d_s && tid == 0) {
+        d_s[3] = qp.s;
+        d_z[3] = qp.z;
+      }
     // round 2: producers quantise their rows and publish the packed codes
     if (!att && tid < ngu / 4) {
       uint32_t word = 0;
@@ -1357,6 +1461,8 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
       for (int j = 0; j < 4; ++j)
         word |= (uint32_t)(uint8_t)shift_code(quant_code(sh.aval[4 * tid + j], qp)) << (8 * j);
       const int k = gu0 / 4 + tid;
+      if constexpr (DUMP)
+        if (d_c4) ((uint32_t*)d_c4)[k] = word;
 #pragma unroll
       for (int r = 0; r < NREP; ++r)
         __hip_atomic_store(xl + OFF_AC + (size_t)r * (I / 4) + k, ((u64)epoch << 32) | word,
@@ -1389,6 +1495,8 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
         const int n = w * R_D + s - NPOLL;
         const float y = dequant(acc + (128 - qp.z) * cd, qp.s, sd);
         xput_rep(xn + OFF_X0, H, n, sh.x1s[n] + y, epoch);
+        if constexpr (DUMP)
+          if (d_x2) d_x2[n] = sh.x1s[n] + y;
       }
     }
     trace_done(A, w, l, 10, lane);
@@ -1406,7 +1514,8 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
   if (w == 0 && A.hidden_out)
     for (int i = tid; i < H; i += NT) A.hidden_out[i] = sh.xs[i];
   if (!A.lm_w) return;
-  const QParam qp = prologue_norm(sh.xs, sh.gain, A.eps, sh, tid);
+  const QParam qp = prologue_norm<DUMP>(sh.xs, sh.gain, A.eps, sh, tid, nullptr,
+                                        (DUMP && w == 0) ? &A.dump : nullptr);
   const int r0 = (int)(((long long)w * A.V) / NWG), r1 = (int)(((long long)(w + 1) * A.V) / NWG);
   float bv = -INFINITY;
   int bi = INT_MAX;
@@ -1666,7 +1775,9 @@ hipError_t decode_mega_launch(hipStream_t st, void* ws, const MegaStep& S, hipEv
   A.ctr = lay.ctr;
   A.amax_v = lay.amax_v;
   A.amax_i = lay.amax_i;
-  A.err = lay.err;
+  A.err.word = lay.err;
+  A.err.limit = S.spin_limit < 0 ? mk::SPIN_LIMIT : (uint32_t)std::min<int64_t>(S.spin_limit, 0xffffffffll);
+  A.dump = S.dump;
   const char* tr = getenv("ARK_MEGA_TRACE");
   A.trace = (tr && tr[0] == '1') ? lay.trace : nullptr;
   A.marker = lay.marker;
@@ -1674,10 +1785,14 @@ hipError_t decode_mega_launch(hipStream_t st, void* ws, const MegaStep& S, hipEv
   A.epoch = lay.epoch;
   void* args[] = {&A};
   if (ev_begin) hipEventRecord(ev_begin, st);
-  e = hipLaunchCooperativeKernel((const void*)mk::k_decode, dim3(mk::NWG), dim3(mk::NT), args,
-                                 sizeof(mk::Shared), st);
+  const void* fn = S.dump.base ? (const void*)mk::k_decode<true> : (const void*)mk::k_decode<false>;
+  e = hipLaunchCooperativeKernel(fn, dim3(mk::NWG), dim3(mk::NT), args, sizeof(mk::Shared), st);
   if (ev_end) hipEventRecord(ev_end, st);
   return e;
+}
+
+const uint32_t* decode_mega_err_word(const void* ws, int L, int T) {
+  return mega_layout(const_cast<void*>(ws), L, T).err;
 }
 
 size_t decode_mega_trace_offset(int L, int T) {
@@ -1685,23 +1800,30 @@ size_t decode_mega_trace_offset(int L, int T) {
   return (size_t)((char*)lay.trace - (char*)nullptr);
 }
 
+// One-time set-up of both instantiations (the record-writing one only for
+// the parity tests): dynamic LDS size, and the check that all NWG
+// workgroups fit on the device at once, which the exchanges rely on.
+// Thread-safe: std::call_once.
 hipError_t decode_mega_init() {
-  static bool done = false;
+  static std::once_flag once;
   static hipError_t status = hipSuccess;
-  if (!done) {
-    done = true;
-    status = hipFuncSetAttribute((const void*)mk::k_decode,
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, sizeof(mk::Shared));
-    if (status == hipSuccess) {
+  std::call_once(once, [] {
+    const void* fns[2] = {(const void*)mk::k_decode<false>, (const void*)mk::k_decode<true>};
+    for (const void* fn : fns) {
+      status = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   sizeof(mk::Shared));
+      if (status != hipSuccess) return;
       int dev = 0, ncu = 0, coop = 0, nblk = 0;
       hipGetDevice(&dev);
       hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
       hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&nblk, (const void*)mk::k_decode, mk::NT,
-                                                   sizeof(mk::Shared));
-      if (!coop || (long)ncu * nblk < mk::NWG) status = hipErrorCooperativeLaunchTooLarge;
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&nblk, fn, mk::NT, sizeof(mk::Shared));
+      if (!coop || (long)ncu * nblk < mk::NWG) {
+        status = hipErrorCooperativeLaunchTooLarge;
+        return;
+      }
     }
-  }
+  });
   return status;
 }
 

@@ -29,6 +29,7 @@ struct GemvParams {
   int rows_total;  // output rows iterated (gate rows for SWIGLU)
   int epi;
   int32_t* acc_out;  // optional [B][rows_total] accumulators (tests)
+  QDump dump;        // optional record of the prologue's quantisation (workgroup 0)
 };
 
 __device__ __forceinline__ int dot16(const i32x4 w, const i32x4 a, int acc) {
@@ -85,6 +86,16 @@ __global__ __launch_bounds__(256) void k_gemv(GemvParams P) {
       }
       const float* src = P.gain ? hb + b * K : xr;
       for (int i = tid; i < K; i += 256) cl[b * K + i] = shift_code(quant_code(src[i], q));
+      if (P.dump.codes && blockIdx.x == 0) {
+        for (int i = tid; i < K; i += 256) {
+          P.dump.codes[(size_t)b * K + i] = cl[b * K + i];
+          if (P.dump.h && P.gain) P.dump.h[(size_t)b * K + i] = src[i];
+        }
+        if (tid == 0) {
+          P.dump.s[b] = q.s;
+          P.dump.z[b] = q.z;
+        }
+      }
     }
   } else {
     const int n16 = (B * K) >> 4;
@@ -229,8 +240,9 @@ static hipError_t gemv_dispatch(hipStream_t st, GemvParams& P, const Seg* segs, 
 }
 
 hipError_t launch_gemv(hipStream_t st, int B, int K, const float* x, int ldx, const float* gain,
-                       double eps, const Seg* segs, int nseg, Epi epi) {
+                       double eps, const Seg* segs, int nseg, Epi epi, const QDump* qd) {
   GemvParams P = {};
+  if (qd) P.dump = *qd;
   P.B = B;
   P.K = K;
   P.x = x;

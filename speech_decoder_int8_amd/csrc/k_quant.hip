@@ -187,7 +187,8 @@ __global__ __launch_bounds__(256) void k_quant_seq(int R, int K, int rps,
                                                    int8_t* __restrict__ codes,
                                                    uint8_t* __restrict__ codes_u8,
                                                    float* __restrict__ s_out,
-                                                   int* __restrict__ z_out) {
+                                                   int* __restrict__ z_out,
+                                                   float* __restrict__ h_out) {
   constexpr int TPR = 64 * WPR;  // threads per row
   const int lt = threadIdx.x % TPR;
   const int r = blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
@@ -220,6 +221,7 @@ __global__ __launch_bounds__(256) void k_quant_seq(int R, int K, int rps,
           v[u].z = (float)(((double)v[u].z * rr) * (double)gg.z);
           v[u].w = (float)(((double)v[u].w * rr) * (double)gg.w);
         }
+        if (h_out) *(float4*)(h_out + (size_t)r * K + i) = v[u];
         const int c0 = quant_code(v[u].x, p), c1 = quant_code(v[u].y, p);
         const int c2 = quant_code(v[u].z, p), c3 = quant_code(v[u].w, p);
         if (codes)
@@ -231,6 +233,7 @@ __global__ __launch_bounds__(256) void k_quant_seq(int R, int K, int rps,
   } else {
     for (int i = lt; i < K; i += TPR) {
       const float y = rs ? (float)(((double)xr[i] * rr) * (double)g[i]) : xr[i];
+      if (h_out) h_out[(size_t)r * K + i] = y;
       const int c = quant_code(y, p);
       if (codes) codes[(size_t)r * K + i] = shift_code(c);
       if (codes_u8) codes_u8[(size_t)r * K + i] = (uint8_t)c;
@@ -240,7 +243,7 @@ __global__ __launch_bounds__(256) void k_quant_seq(int R, int K, int rps,
 
 hipError_t launch_quant_seq(hipStream_t st, int R, int K, int rps, const float* x, int ldx,
                             const double* rs, const float* gain, const int* set, int8_t* codes,
-                            uint8_t* codes_u8, float* s_out, int* z_out) {
+                            uint8_t* codes_u8, float* s_out, int* z_out, float* h_out) {
   const bool vec = vec_ok(x, K, ldx) && (!codes || (uintptr_t)codes % 4 == 0) &&
                    (!codes_u8 || (uintptr_t)codes_u8 % 4 == 0) &&
                    (!rs || (uintptr_t)gain % 16 == 0);
@@ -248,7 +251,7 @@ hipError_t launch_quant_seq(hipStream_t st, int R, int K, int rps, const float* 
   const bool wide = R < 1024;
 #define ARK_QUANT_LAUNCH(V, W)                                                                   \
   hipLaunchKernelGGL((k_quant_seq<V, W>), dim3((R * W + 3) / 4), dim3(256), 0, st, R, K, rps, x, \
-                     ldx, rs, gain, set, codes, codes_u8, s_out, z_out)
+                     ldx, rs, gain, set, codes, codes_u8, s_out, z_out, h_out)
   if (vec && wide)
     ARK_QUANT_LAUNCH(true, 4);
   else if (vec)
@@ -273,7 +276,8 @@ __global__ __launch_bounds__(QNT) void k_norm_quant_row(int K, const float* __re
                                                         const float* __restrict__ g, double eps,
                                                         int8_t* __restrict__ codes,
                                                         float* __restrict__ s_out,
-                                                        int* __restrict__ z_out) {
+                                                        int* __restrict__ z_out,
+                                                        float* __restrict__ h_out) {
   __shared__ double redd[QNT / 64];
   __shared__ float redf[2 * (QNT / 64)];
   const int r = blockIdx.x, t = threadIdx.x;
@@ -313,15 +317,19 @@ __global__ __launch_bounds__(QNT) void k_norm_quant_row(int K, const float* __re
 #pragma unroll
   for (int k = 0; k < QMAX; ++k)
     if (t + QNT * k < K) cr[t + QNT * k] = shift_code(quant_code(v[k], p));
+  if (h_out)
+#pragma unroll
+    for (int k = 0; k < QMAX; ++k)
+      if (t + QNT * k < K) h_out[(size_t)r * K + t + QNT * k] = v[k];
 }
 
 bool norm_quant_row_supported(int K) { return K >= 1 && K <= QNT * QMAX; }
 
 hipError_t launch_norm_quant_row(hipStream_t st, int B, int K, const float* x, int ldx,
                                  const float* gain, double eps, int8_t* codes, float* s_out,
-                                 int* z_out) {
+                                 int* z_out, float* h_out) {
   hipLaunchKernelGGL(k_norm_quant_row, dim3(B), dim3(QNT), 0, st, K, x, ldx, gain, eps, codes,
-                     s_out, z_out);
+                     s_out, z_out, h_out);
   return hipGetLastError();
 }
 

@@ -20,6 +20,17 @@ struct Seg {
 
 enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
 
+// Optional record of one dynamic quantisation for the re-anchored parity
+// tests: the fp32 tensor the quantiser saw (h: only where the quantiser
+// itself computes it, i.e. behind an RMSNorm), the shifted codes it produced
+// and its (s, z) per sequence.  Null members are not written.
+struct QDump {
+  float* h;
+  int8_t* codes;
+  float* s;
+  int* z;
+};
+
 // Global-memory pointers: accesses through them compile to global (not
 // flat) instructions, whose completion the compiler can count exactly.
 template <typename T>
@@ -194,24 +205,28 @@ hipError_t launch_row_stats(hipStream_t st, int R, int K, int rows_per_seq, cons
 // `set`: codes of x (or of h recomputed from x, rs and gain when rs !=
 // nullptr), shifted codes (code - 128) [R][K] and/or plain codes; s_out /
 // z_out [nseq].
+// h_out (optional, [R][K]): the values quantised (h where it is recomputed).
 hipError_t launch_quant_seq(hipStream_t st, int R, int K, int rows_per_seq, const float* x,
                             int ldx, const double* rs, const float* gain, const int* set,
-                            int8_t* codes, uint8_t* codes_u8, float* s_out, int* z_out);
+                            int8_t* codes, uint8_t* codes_u8, float* s_out, int* z_out,
+                            float* h_out = nullptr);
 
 // One row per sequence (decode): optional RMSNorm (gain != nullptr) and the
 // row's dynamic quantisation in one kernel; shifted codes [B][K], s/z [B].
 bool norm_quant_row_supported(int K);
+// h_out (optional, [B][K]): the values quantised (the normed row with a gain).
 hipError_t launch_norm_quant_row(hipStream_t st, int B, int K, const float* x, int ldx,
                                  const float* gain, double eps, int8_t* codes, float* s_out,
-                                 int* z_out);
+                                 int* z_out, float* h_out = nullptr);
 
 // ---- int8 projections
 // Decode GEMV (k_gemv.hip): B <= 4 rows of input x (row stride ldx), fused
 // prologue (RMSNorm when gain != nullptr, then per-row quantisation), segments
 // concatenated along the output dimension (EPI_SWIGLU: seg[0] gate, seg[1] up,
 // result to seg[0].out).  acc_out (optional) receives raw int32 accumulators.
+// qd (optional): workgroup 0 records its prologue's quantisation ([B][K]).
 hipError_t launch_gemv(hipStream_t st, int B, int K, const float* x, int ldx, const float* gain,
-                       double eps, const Seg* segs, int nseg, Epi epi);
+                       double eps, const Seg* segs, int nseg, Epi epi, const QDump* qd = nullptr);
 // Same GEMV on precomputed shifted codes [B][K] with per-row (s, z).
 hipError_t launch_gemv_codes(hipStream_t st, int B, int K, const int8_t* codes, const float* s,
                              const int* z, const Seg* segs, int nseg, Epi epi, int32_t* acc_out);
@@ -287,6 +302,17 @@ hipError_t launch_attention(hipStream_t st, int B, int S, int NH, int NKV, int T
                             const SeqStats* stats = nullptr, const RopeIn* rope = nullptr);
 
 // ---- persistent batch-1 decode step for the ARK geometry (k_decode.hip)
+// Re-anchored parity record (layout of ark_dump_layout in ark.h): layer l
+// with bit l of mask set has its record at base + (index among the recorded
+// layers) * rec; f[] are the field offsets inside a record and head[] the
+// offsets of the LM-head fields from base.  base == nullptr: none.
+struct DumpRec {
+  char* base;
+  uint64_t mask;
+  size_t rec;
+  size_t f[13];
+  size_t head[4];
+};
 struct MegaLayer {
   const int8_t* w[7];  // q, k, v, o, gate, up, down
   const float* sw[7];
@@ -314,6 +340,8 @@ struct MegaStep {
   float* hidden_out;
   const uint8_t* mask;
   int32_t* out_token;
+  DumpRec dump;         // base == nullptr: the production kernel, no record
+  int64_t spin_limit;   // rounds per bounded wait; < 0: the default bound
 };
 bool decode_mega_supported(int H, int NH, int NKV, int D, int I, int T, int L);
 size_t decode_mega_ws_bytes(int L, int T);
@@ -324,5 +352,8 @@ hipError_t decode_mega_upload(hipStream_t st, void* ws, int L, int T, const Mega
 // alone (not its preparation kernel).
 hipError_t decode_mega_launch(hipStream_t st, void* ws, const MegaStep& S, hipEvent_t ev_begin,
                               hipEvent_t ev_end);
+// Error word of the last persistent launch on this workspace (0: every
+// bounded wait was met; read after the stream has completed that launch).
+const uint32_t* decode_mega_err_word(const void* ws, int L, int T);
 
 }  // namespace ark

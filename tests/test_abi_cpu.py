@@ -29,8 +29,8 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings():
-    for s in (0, -1, -2, -3, -4, -5, -6):
-        assert ark.status_string(s)
+    for s in (0, -1, -2, -3, -4, -5, -6, -7):
+        assert ark.status_string(s) != "unknown status"
     assert ark.status_string(-99) == "unknown status"
 
 
@@ -191,3 +191,65 @@ def test_small_call_error_paths():
     assert lib.ark_test_attention(1, 2, 16, 2, 500, p1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                   FAKE, FAKE, 1 << 30, None) == ark.ARK_E_SHAPE
     assert lib.ark_test_attention_workspace_bytes(0, 1, 16, 512) == 0
+
+
+def test_dump_layout():
+    """The parity record layout: 13 fields per recorded layer, 256-byte
+    aligned, each large enough for its array, then the head record."""
+    lib = ark.lib()
+    d = real_dims(n_layers=36)
+    B, S = 3, 5
+    R = B * S
+    f = (C.c_size_t * 13)()
+    rec = C.c_size_t()
+    head = (C.c_size_t * 4)()
+    mask = (1 << 0) | (1 << 17) | (1 << 35) | (1 << 40)     # bit 40 is past n_layers: ignored
+    total = lib.ark_dump_layout(C.byref(d), B, S, C.c_uint64(mask), f, C.byref(rec), head)
+    H, Q, KV, I = 2048, 2048, 256, 11008
+    sizes = [R * H * 4, R * (Q + 2 * KV) * 4, R * Q * 4, R * H * 4, R * H * 4, R * I * 4, R * H * 4,
+             R * H, R * Q, R * H, R * I, 4 * B * 4, 4 * B * 4]
+    offs = list(f)
+    assert offs[0] == 0 and all(o % 256 == 0 for o in offs)
+    for i in range(12):
+        assert offs[i + 1] - offs[i] >= sizes[i]
+    assert rec.value >= offs[12] + sizes[12] and rec.value % 256 == 0
+    hs = [B * H * 4, B * H, B * 4, B * 4]
+    h = list(head)
+    assert h[0] == 3 * rec.value and all(o % 256 == 0 for o in h)
+    for i in range(3):
+        assert h[i + 1] - h[i] >= hs[i]
+    assert total >= h[3] + hs[3]
+    assert lib.ark_dump_layout(C.byref(d), B, S, C.c_uint64(0), None, None, None) == total - 3 * rec.value
+    assert lib.ark_dump_layout(C.byref(d), 0, S, C.c_uint64(1), None, None, None) == 0
+    assert lib.ark_dump_layout(None, 1, 1, C.c_uint64(1), None, None, None) == 0
+
+
+def test_dump_and_status_error_paths():
+    lib = ark.lib()
+    m = fake_model()
+    L = 2
+    kc = (C.c_void_p * L)(FAKE, FAKE)
+    pos = (C.c_int32 * 1)(3)
+    ws = lib.ark_workspace_bytes(C.byref(m.d), 1, 4)
+    need = lib.ark_dump_layout(C.byref(m.d), 1, 4, C.c_uint64(3), None, None, None)
+    args = (C.byref(m), 1, 4, FAKE, pos, kc, kc, FAKE, FAKE, None, None, FAKE, ws, None)
+    assert lib.ark_prefill_dump(*args, None, need, C.c_uint64(3)) == ark.ARK_E_NULL
+    assert lib.ark_prefill_dump(*args, FAKE, need - 1, C.c_uint64(3)) == ark.ARK_E_WORKSPACE
+    assert lib.ark_prefill_dump(*args, FAKE + 64, need, C.c_uint64(3)) == ark.ARK_E_ALIGN
+    # the plain call's own validation still applies
+    bad = (C.byref(m), 1, 4, None, pos, kc, kc, FAKE, FAKE, None, None, FAKE, ws, None)
+    assert lib.ark_prefill_dump(*bad, FAKE, need, C.c_uint64(3)) == ark.ARK_E_NULL
+    ws1 = lib.ark_workspace_bytes(C.byref(m.d), 1, 1)
+    need1 = lib.ark_dump_layout(C.byref(m.d), 1, 1, C.c_uint64(1), None, None, None)
+    full = (C.c_int32 * 1)(512)
+    assert lib.ark_decode_step_dump(C.byref(m), 1, FAKE, full, kc, kc, FAKE, FAKE, None, None, FAKE,
+                                    ws1, None, FAKE, need1, C.c_uint64(1)) == ark.ARK_E_RANGE
+    assert lib.ark_decode_step_dump(C.byref(m), 1, FAKE, pos, kc, kc, FAKE, FAKE, None, None, FAKE,
+                                    ws1, None, FAKE, 16, C.c_uint64(1)) == ark.ARK_E_WORKSPACE
+    # status and path queries validate before any GPU call
+    assert lib.ark_decode_check(None, 1, FAKE, ws1, None) == ark.ARK_E_NULL
+    assert lib.ark_decode_check(C.byref(m), 1, None, ws1, None) == ark.ARK_E_NULL
+    assert lib.ark_decode_check(C.byref(m), 0, FAKE, ws1, None) == ark.ARK_E_SHAPE
+    assert lib.ark_decode_check(C.byref(m), 1, FAKE, 16, None) == ark.ARK_E_WORKSPACE
+    assert lib.ark_decode_path(None, 1) == ark.ARK_E_NULL
+    assert lib.ark_decode_path(C.byref(m), 65) == ark.ARK_E_SHAPE

@@ -55,6 +55,7 @@ def _caches(cfg, lengths, rng):
 @pytest.mark.parametrize("p0", [0, 100, 150, 300, 510])
 def test_decode_steps_match_oracle(models, path, p0):
     om, gm = models
+    assert ark.decode_path(gm, 1) == (1 if path == "mega" else 0)
     rng = np.random.default_rng(p0 + 5)
     kc, vc = _caches(CFG, [p0], rng)
     gs = GpuState(gm, 1, 1)
@@ -64,6 +65,7 @@ def test_decode_steps_match_oracle(models, path, p0):
     p = np.array([p0])
     for step in range(min(2, CFG.max_total_len - p0)):
         kd, vd, hid = gs.decode(t(tok), p)
+        assert ark.decode_check(gm, 1, gs.ws) == ark.ARK_OK
         lo, kdo, vdo, hido = oracle.decode_step(om, tok, p, kc, vc)
         for l in range(CFG.n_layers):
             assert_close(host(kd[l]), kdo[l], f"{path} step {step} k_delta {l}")
@@ -82,6 +84,7 @@ def test_decode_steps_match_oracle(models, path, p0):
 
 def test_greedy_loop_matches_oracle(models, path):
     om, gm = models
+    assert ark.decode_path(gm, 1) == (1 if path == "mega" else 0)
     rng = np.random.default_rng(9)
     kc, vc = _caches(CFG, [60], rng)
     mask = CFG.mask()
@@ -143,3 +146,34 @@ def test_long_cache_decode_matches_oracle(models_long, path, p0):
         vc = [oracle.cache_write(vc[l], vdo[l], p) for l in range(CFG_LONG.n_layers)]
         tok = oracle.masked_argmax(lo, mask)
         p = p + 1
+
+
+def test_persistent_wait_timeout_is_reported(models, monkeypatch):
+    """A bounded wait of the persistent kernel that gives up is reported:
+    the test-only spin limit 0 makes the waits give up at their first
+    unmet check (every workgroup still runs to its end), ark_decode_check
+    returns ARK_E_TIMEOUT and the greedy loop fails with it; the next
+    ordinary step reports ARK_OK again."""
+    om, gm = models
+    monkeypatch.delenv("ARK_DECODE_PATH", raising=False)
+    assert ark.decode_path(gm, 1) == 1
+    rng = np.random.default_rng(3)
+    kc, vc = _caches(CFG, [200], rng)
+    gs = GpuState(gm, 1, 1)
+    gs.load_caches(kc, vc)
+    tok = t(np.array([17], np.int32))
+    gs.decode(tok, [200])
+    assert ark.decode_check(gm, 1, gs.ws) == ark.ARK_OK
+    monkeypatch.setenv("ARK_TEST_SPIN_LIMIT", "0")
+    gs.decode(tok, [200])
+    assert ark.decode_check(gm, 1, gs.ws) == ark.ARK_E_TIMEOUT
+    out = torch.empty((3, 1), dtype=torch.int32, device="cuda")
+    kd1, vd1 = gs.deltas(1)
+    with pytest.raises(ark.ArkError) as err:
+        ark.greedy_decode(gm, tok, [200], gs.kc, gs.vc, kd1, vd1, gs.logits, t(CFG.mask()),
+                          CFG.end_id, 3, out, ws=gs.ws, check_every=2)
+    assert err.value.status == ark.ARK_E_TIMEOUT
+    monkeypatch.delenv("ARK_TEST_SPIN_LIMIT")
+    gs.load_caches(kc, vc)
+    gs.decode(t(np.array([17], np.int32)), [200])
+    assert ark.decode_check(gm, 1, gs.ws) == ark.ARK_OK
