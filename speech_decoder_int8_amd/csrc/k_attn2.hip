@@ -200,14 +200,11 @@ hipError_t launch_attention_prefill(hipStream_t st, int B, int S, int NH, int NK
                                     const float* q, const float* k_cache, const float* v_cache,
                                     const float* k_delta, const float* v_delta,
                                     const PosArgs& pos, float* out, const SeqStats* stats) {
-  static bool attr = false;
-  if (!attr) {
-    const hipError_t e = hipFuncSetAttribute((const void*)k_attn_prefill,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             a2::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  // one-time attribute set-up (a function-local static: initialised once,
+  // thread-safe)
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)k_attn_prefill, hipFuncAttributeMaxDynamicSharedMemorySize, a2::LDS_BYTES);
+  if (attr != hipSuccess) return attr;
   Attn2Params P = {};
   P.B = B;
   P.S = S;

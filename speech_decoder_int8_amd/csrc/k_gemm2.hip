@@ -420,13 +420,12 @@ __global__ __launch_bounds__(NTH, NTH == 256 ? 2 : 1) void k_gemm_big(Gemm2Param
 template <int BM, int BN, int BK, int NS, int NTH>
 static hipError_t launch_big(hipStream_t st, Gemm2Params P) {
   constexpr int bytes = NS * (BM + BN) * BK;
-  static bool attr = false;
-  if (!attr) {
-    const hipError_t e = hipFuncSetAttribute((const void*)k_gemm_big<BM, BN, BK, NS, NTH>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  // one-time attribute set-up (a function-local static: initialised once,
+  // thread-safe)
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)k_gemm_big<BM, BN, BK, NS, NTH>, hipFuncAttributeMaxDynamicSharedMemorySize,
+      bytes);
+  if (attr != hipSuccess) return attr;
   const int tn = P.epi == EPI_SWIGLU ? BN / 2 : BN;
   P.tiles_m = (P.M + BM - 1) / BM;
   P.tiles = P.tiles_m * ((P.ncols + tn - 1) / tn);

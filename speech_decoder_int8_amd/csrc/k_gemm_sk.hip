@@ -393,14 +393,11 @@ hipError_t launch_gemm_skinny(hipStream_t st, int M, int K, const int8_t* codes,
 
 template <int MB>
 static hipError_t launch_sk(hipStream_t st, const GemmSkParams& P) {
-  static bool attr = false;
-  if (!attr) {
-    const hipError_t e = hipFuncSetAttribute((const void*)k_gemm_sk<MB>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             sk::Cfg<MB>::LDS);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  // one-time attribute set-up (a function-local static: initialised once,
+  // thread-safe)
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)k_gemm_sk<MB>, hipFuncAttributeMaxDynamicSharedMemorySize, sk::Cfg<MB>::LDS);
+  if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(k_gemm_sk<MB>, dim3(P.tiles * P.ks), dim3(sk::NT), sk::Cfg<MB>::LDS, st, P);
   return hipGetLastError();
 }
