@@ -69,9 +69,11 @@ enum ark_status {
   ARK_E_WORKSPACE = -4,   /* workspace smaller than ark_workspace_bytes() */
   ARK_E_HIP = -5,         /* a HIP launch failed */
   ARK_E_ALIGN = -6,       /* a pointer is not aligned as documented */
-  ARK_E_TIMEOUT = -7      /* a bounded wait of the persistent batch-1 decode
+  ARK_E_TIMEOUT = -7,     /* a bounded wait of the persistent batch-1 decode
                              kernel gave up: the outputs of that step (and of
                              every greedy step fed from it) are invalid */
+  ARK_E_NOALLOC = -8      /* ark_decode_step_noalloc: the call needs more
+                             scratch than ark_noalloc_max_bytes() */
 };
 
 /* Model geometry.  Supported: 1 <= n_layers <= 64, head_dim == 128,
@@ -189,6 +191,27 @@ int ark_decode_step(const ark_model* m, int32_t B, const int32_t* token_ids,
                     const float* const* v_cache, float* k_delta, float* v_delta,
                     float* logits, float* hidden_out, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * step as ark_decode_step, with the library's own scratch in place of the
+ * workspace.  The scratch is one static device array per GPU of
+ * ark_noalloc_max_bytes() bytes (64 MiB), held until the process ends; its
+ * address is resolved on the first call on each device.  The call
+ * allocates nothing.  A call whose ark_workspace_bytes(&m->d, B, 1) exceeds
+ * that size returns ARK_E_NOALLOC (the ARK geometry at T = 512 needs about
+ * 34 MiB at B = 1 and less at 2 <= B <= 64).  Every call on a GPU shares
+ * that GPU's array and it keeps the last call's contents (the step clears
+ * what must start at zero): calls that overlap on one GPU - concurrent
+ * streams or threads - race and give undefined results.  Status of a
+ * persistent-kernel step: ark_decode_check is not available (no workspace);
+ * use ark_decode_step when the time-out status is needed.  Other arguments
+ * and errors as ark_decode_step. */
+size_t ark_noalloc_max_bytes(void);
+int ark_decode_step_noalloc(const ark_model* m, int32_t B, const int32_t* token_ids,
+                            const int32_t* cache_position, const float* const* k_cache,
+                            const float* const* v_cache, float* k_delta, float* v_delta,
+                            float* logits, float* hidden_out, void* stream);
 
 /* Status of the last decode step enqueued on this workspace for B
  * sequences: synchronises `stream`, then returns ARK_E_TIMEOUT if the

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(HERE, "libark.so")
 ARK_OK, ARK_E_NULL, ARK_E_SHAPE, ARK_E_RANGE, ARK_E_WORKSPACE, ARK_E_HIP, ARK_E_ALIGN = \
     0, -1, -2, -3, -4, -5, -6
 ARK_E_TIMEOUT = -7
+ARK_E_NOALLOC = -8
 
 # fields of a layer record of the parity dump (enum ark_dump_field)
 DUMP_FIELDS = ("h1", "qkv", "attn", "x1", "h2", "a", "x2", "c1", "c2", "c3", "c4", "s", "z")
@@ -90,6 +91,8 @@ _SIGS = {
     "ark_dominant_kernel": (C.c_char_p, []),
     "ark_decode_trace_offset": (C.c_size_t, [C.POINTER(ArkDims)]),
     "ark_decode_check": (C.c_int, [C.POINTER(ArkModel), I32, P, C.c_size_t, P]),
+    "ark_noalloc_max_bytes": (C.c_size_t, []),
+    "ark_decode_step_noalloc": (C.c_int, [C.POINTER(ArkModel), I32, P, PI32, PP, PP, P, P, P, P, P]),
     "ark_decode_path": (C.c_int, [C.POINTER(ArkModel), I32]),
     "ark_dump_layout": (C.c_size_t, [C.POINTER(ArkDims), I32, I32, C.c_uint64, PSZ, PSZ, PSZ]),
     "ark_prefill_dump": (C.c_int, [C.POINTER(ArkModel), I32, I32, P, PI32, PP, PP, P, P, P, P, P,
@@ -318,6 +321,16 @@ def decode_step(model: DeviceModel, token_ids, cache_position, k_cache, v_cache,
         C.byref(model.c), B, _ptr(token_ids), _pos_array(cache_position), _ptr_array(k_cache),
         _ptr_array(v_cache), _ptr(k_delta), _ptr(v_delta), _ptr(logits), _ptr(hidden_out),
         _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def decode_step_noalloc(model: DeviceModel, token_ids, cache_position, k_cache, v_cache, k_delta,
+                        v_delta, logits=None, hidden_out=None, stream=None):
+    """ark_decode_step on the library's static scratch (no workspace)."""
+    B = token_ids.shape[0]
+    _check("ark_decode_step_noalloc", lib().ark_decode_step_noalloc(
+        C.byref(model.c), B, _ptr(token_ids), _pos_array(cache_position), _ptr_array(k_cache),
+        _ptr_array(v_cache), _ptr(k_delta), _ptr(v_delta), _ptr(logits), _ptr(hidden_out),
+        _stream(stream)))
 
 
 def decode_check(model: DeviceModel, B: int, ws, stream=None) -> int:

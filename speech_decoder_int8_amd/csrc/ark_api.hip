@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <vector>
 
 #include "../../include/ark.h"
@@ -13,6 +14,14 @@
 #include "kernels.hpp"
 
 using namespace ark;
+
+// Scratch of ark_decode_step_noalloc, for callers that cannot allocate
+// device memory (code under graph capture, tight serving loops, harnesses
+// that forbid hipMalloc): one copy per device, held until the process ends.
+// In host code the name is a stand-in, not a device address: the device
+// address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kNoAllocBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
 
 namespace {
 
@@ -559,9 +568,75 @@ int dump_check(const ark_model* m, int B, int S, void* dump, size_t dump_bytes, 
   return ARK_OK;
 }
 
+// Device address of `scratch` on each device (resolved on the entry
+// point's first call there, with that device current) and the kind of the
+// last call made with it: a persistent-kernel step of one layout, or not.
+constexpr int kMaxDevices = 64;
+struct DeviceScratch {
+  char* ptr = nullptr;
+  uint64_t last = 0;
+};
+DeviceScratch g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_of_device(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ARK_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev].ptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ARK_E_HIP;
+    g_scratch[dev].ptr = (char*)p;
+  }
+  *out = g_scratch[dev].ptr;
+  return ARK_OK;
+}
+
+// Record the kind of this call on the current device; true when the
+// persistent kernel's exchange area must be re-initialised (the array last
+// served another layout or the multi-kernel path, whose buffers overlap it).
+bool scratch_switch(uint64_t key) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return true;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  const bool changed = key != 0 && g_scratch[dev].last != key;
+  g_scratch[dev].last = key;
+  return changed;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t ark_noalloc_max_bytes(void) { return kNoAllocBytes; }
+
+int ark_decode_step_noalloc(const ark_model* m, int32_t B, const int32_t* token_ids,
+                            const int32_t* cache_position, const float* const* k_cache,
+                            const float* const* v_cache, float* k_delta, float* v_delta,
+                            float* logits, float* hidden_out, void* stream) {
+  if (!m) return ARK_E_NULL;
+  if (!dims_ok(m->d) || B < 1 || B > kMaxBatch) return ARK_E_SHAPE;
+  const size_t need = plan(m->d, B, 1).total;
+  if (need > kNoAllocBytes) return ARK_E_NOALLOC;
+  int e = check_model(m, true);
+  if (e) return e;
+  if (!token_ids) return ARK_E_NULL;
+  char* ws = nullptr;
+  if ((e = scratch_of_device(&ws))) return e;
+  e = check_step(m, B, 1, cache_position, k_cache, v_cache, k_delta, v_delta, logits, ws, need);
+  if (e) return e;
+  hipStream_t st = (hipStream_t)stream;
+  const bool mega = mega_ready(m, B);
+  const uint64_t key =
+      mega ? ((1ull << 63) | ((uint64_t)m->d.n_layers << 32) | (uint32_t)m->d.max_total_len) : 0;
+  if (scratch_switch(key)) {
+    const Plan p = plan(m->d, 1, 1);
+    uint64_t* marker = decode_mega_marker(ws + p.mega, m->d.n_layers, m->d.max_total_len);
+    if (launch_zero_u32(st, (uint32_t*)marker, 2) != hipSuccess) return ARK_E_HIP;
+  }
+  return decode_impl(m, B, token_ids, cache_position, k_cache, v_cache, k_delta, v_delta, logits,
+                     hidden_out, ws, need, stream, nullptr);
+}
 
 const char* ark_status_string(int status) {
   switch (status) {
@@ -572,6 +647,9 @@ const char* ark_status_string(int status) {
     case ARK_E_WORKSPACE: return "workspace too small";
     case ARK_E_HIP: return "HIP launch failed";
     case ARK_E_ALIGN: return "pointer misaligned";
+    case ARK_E_NOALLOC:
+      return "the call needs more scratch than the library's static array holds "
+             "(ark_noalloc_max_bytes)";
     case ARK_E_TIMEOUT:
       return "a bounded wait of the persistent decode kernel timed out; that step's outputs are invalid";
     default: return "unknown status";

@@ -1791,6 +1791,8 @@ hipError_t decode_mega_launch(hipStream_t st, void* ws, const MegaStep& S, hipEv
   return e;
 }
 
+uint64_t* decode_mega_marker(void* ws, int L, int T) { return (uint64_t*)mega_layout(ws, L, T).marker; }
+
 const uint32_t* decode_mega_err_word(const void* ws, int L, int T) {
   return mega_layout(const_cast<void*>(ws), L, T).err;
 }

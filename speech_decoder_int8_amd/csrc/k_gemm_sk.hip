@@ -27,6 +27,8 @@
 //
 // Accumulator layout (32x32 int32 in 16 registers): register r of lane l
 // holds row (r / 4) * 8 + (l / 32) * 4 + r % 4, column l % 32.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -350,6 +352,12 @@ size_t gemm_skinny_ws_bytes() {
 
 __global__ void k_zero_u32(uint32_t* p, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+hipError_t launch_zero_u32(hipStream_t st, uint32_t* p, int n) {
+  hipLaunchKernelGGL(k_zero_u32, dim3(std::max(1, std::min(256, (n + 255) / 256))), dim3(256), 0, st,
+                     p, n);
+  return hipGetLastError();
 }
 
 hipError_t gemm_skinny_reset(hipStream_t st, void* scratch) {

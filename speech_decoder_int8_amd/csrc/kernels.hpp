@@ -245,6 +245,8 @@ hipError_t launch_gemm_big(hipStream_t st, int M, int K, const int8_t* codes, co
 bool gemm_skinny_supported(int M, int K);
 size_t gemm_skinny_ws_bytes();
 hipError_t gemm_skinny_reset(hipStream_t st, void* scratch);
+// p[0..n) = 0 with a small kernel (no memset node, so it may be captured)
+hipError_t launch_zero_u32(hipStream_t st, uint32_t* p, int n);
 hipError_t launch_gemm_skinny(hipStream_t st, int M, int K, const int8_t* codes, const float* s,
                               const int* z, int rows_per_seq, const Seg* segs, int nseg, Epi epi,
                               int32_t* acc_out, void* scratch);
@@ -355,5 +357,9 @@ hipError_t decode_mega_launch(hipStream_t st, void* ws, const MegaStep& S, hipEv
 // Error word of the last persistent launch on this workspace (0: every
 // bounded wait was met; read after the stream has completed that launch).
 const uint32_t* decode_mega_err_word(const void* ws, int L, int T);
+// The word that marks the workspace's exchange area as initialised for this
+// layout; zeroing it makes the next launch clear the area and restart its
+// tags.
+uint64_t* decode_mega_marker(void* ws, int L, int T);
 
 }  // namespace ark

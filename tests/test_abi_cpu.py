@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings():
-    for s in (0, -1, -2, -3, -4, -5, -6, -7):
+    for s in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert ark.status_string(s) != "unknown status"
     assert ark.status_string(-99) == "unknown status"
 
@@ -253,3 +253,27 @@ def test_dump_and_status_error_paths():
     assert lib.ark_decode_check(C.byref(m), 1, FAKE, 16, None) == ark.ARK_E_WORKSPACE
     assert lib.ark_decode_path(None, 1) == ark.ARK_E_NULL
     assert lib.ark_decode_path(C.byref(m), 65) == ark.ARK_E_SHAPE
+
+
+def test_noalloc_limit_and_validation():
+    """The no-allocation decode step rejects, before any GPU call, a call
+    whose scratch would exceed the static array, and invalid arguments."""
+    lib = ark.lib()
+    cap = lib.ark_noalloc_max_bytes()
+    assert cap == 64 << 20
+    m = fake_model(L=36)
+    assert lib.ark_workspace_bytes(C.byref(m.d), 1, 1) <= cap
+    assert lib.ark_workspace_bytes(C.byref(m.d), 32, 1) <= cap
+    kc = (C.c_void_p * 36)(*([FAKE] * 36))
+    pos = (C.c_int32 * 64)(*([3] * 64))
+    big = fake_model(L=64, max_total_len=8192)
+    kc64 = (C.c_void_p * 64)(*([FAKE] * 64))
+    assert lib.ark_workspace_bytes(C.byref(big.d), 64, 1) > cap
+    assert lib.ark_decode_step_noalloc(C.byref(big), 64, FAKE, pos, kc64, kc64, FAKE, FAKE, None,
+                                       None, None) == ark.ARK_E_NOALLOC
+    assert lib.ark_decode_step_noalloc(None, 1, FAKE, pos, kc, kc, FAKE, FAKE, None, None,
+                                       None) == ark.ARK_E_NULL
+    assert lib.ark_decode_step_noalloc(C.byref(m), 0, FAKE, pos, kc, kc, FAKE, FAKE, None, None,
+                                       None) == ark.ARK_E_SHAPE
+    assert lib.ark_decode_step_noalloc(C.byref(m), 1, None, pos, kc, kc, FAKE, FAKE, None, None,
+                                       None) == ark.ARK_E_NULL
