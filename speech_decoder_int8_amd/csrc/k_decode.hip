@@ -354,17 +354,32 @@ __device__ __forceinline__ void minmax16(const float* red, int lane, float& lo, 
 
 // ------------------------------------------------------------- waiting --
 // One wave: wait until words [c0, c1) of v carry the tag and copy them to
-// dst (word c0 first).  Producers write v in blocks of blk words (block b =
-// words [b*blk, b*blk + blk)); the wave first polls the first word of each
-// block that meets the range (or, given flags, the block's flag word), then
-// reads the range with device-scope loads
-// straight into LDS and checks every tag, again until all match.  The copy
-// is whole KiB: dst needs room up to the next KiB boundary.  Bounded: after
-// SPIN_LIMIT rounds the error word is set and the wave goes on.  Returns
-// the number of sparse polls plus 65536 x the number of copies.
+// dst (word c0 first).  The range is first copied straight into LDS with
+// device-scope loads and every tag checked: data that is already there (the
+// usual case) costs one round trip.  Otherwise producers write v in blocks
+// of blk words (block b = words [b*blk, b*blk + blk)): the wave polls the
+// first word of each block that meets the range (or, given flags, the
+// block's flag word), which keeps the polling traffic small, then copies
+// and checks again until all tags match.  The copy is whole KiB: dst needs
+// room up to the next KiB boundary.  Bounded: after err.limit rounds the
+// error word is set and the wave goes on.  Returns the number of sparse
+// polls plus 65536 x the number of copies.
 __device__ uint32_t poll_range(const u64* v, int c0, int c1, int blk, unsigned char* dst,
                                Err err, int lane, uint32_t tag, u64* tr = nullptr,
                                const u64* flags = nullptr) {
+  const int bytes = ((c1 - c0) * 8 + 1023) & ~1023;
+  {
+    dma_wave<true>(v + c0, dst, bytes, lane * 16);
+    __builtin_amdgcn_s_waitcnt(0);
+    const u64* s = (const u64*)dst;
+    bool ok = true;
+#pragma unroll 4
+    for (int i = lane; i < c1 - c0; i += 64) ok &= (uint32_t)(s[i] >> 32) == tag;
+    if (__all(ok)) {
+      stamp(tr, 1, lane);
+      return 1u << 16;
+    }
+  }
   uint32_t spins = 0;
   const int b0 = c0 / blk, b1 = (c1 - 1) / blk;
   for (;;) {
@@ -379,7 +394,6 @@ __device__ uint32_t poll_range(const u64* v, int c0, int c1, int blk, unsigned c
   }
   const uint32_t pre = spins;
   stamp(tr, 1, lane);
-  const int bytes = ((c1 - c0) * 8 + 1023) & ~1023;
   for (;;) {
     dma_wave<true>(v + c0, dst, bytes, lane * 16);
     __builtin_amdgcn_s_waitcnt(0);
@@ -393,7 +407,7 @@ __device__ uint32_t poll_range(const u64* v, int c0, int c1, int blk, unsigned c
       break;
     }
   }
-  return pre + ((spins - pre + 1) << 16);
+  return pre + ((spins - pre + 2) << 16);
 }
 
 // All waves: poll_range over words [0, n) of v, split into one chunk of
@@ -710,8 +724,8 @@ __device__ QParam poll_amm(const u64* v, Shared& sh, int lane, int wave, uint32_
 // blocks of blk words) and unpack them to sh.codes; all waves end at a
 // barrier.  The staging of each polling wave ends before DN_LDS.
 __device__ void poll_codes(const u64* v, int n, int blk, Shared& sh, int lane, int wave,
-                           uint32_t tag, Err err) {
-  poll_all(v, n, blk, sh.stage, err, lane, wave, tag, nullptr, nullptr, NPOLL);
+                           uint32_t tag, Err err, u64* tr = nullptr) {
+  poll_all(v, n, blk, sh.stage, err, lane, wave, tag, tr, nullptr, NPOLL);
   if (wave < NPOLL) {
     const int chunk = ((n + NPOLL - 1) / NPOLL + 127) & ~127;
     const int c1 = min(n, wave * chunk + chunk);
@@ -1443,6 +1457,7 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
       // (min, max) wait (which takes the scalar path) and are in before the
       // codes are awaited
       lds_barrier();
+      if (tid == 0) stamp(trace_sub(A, w, l, 31), 0, 0);
       issue_down_head(l);
     }
 
@@ -1455,6 +1470,7 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
         d_z[3] = qp.z;
       }
     // round 2: producers quantise their rows and publish the packed codes
+    if (!att && tid == 0) stamp(trace_sub(A, w, l, 25), 0, 0);
     if (!att && tid < ngu / 4) {
       uint32_t word = 0;
 #pragma unroll
@@ -1471,7 +1487,8 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
     // ---- down + residual: waves 0..7 poll and unpack the SwiGLU codes;
     // loader 8 + r computes row r from its units in LDS
     asm volatile("" : "+v"(lane16), "+v"(tid), "+v"(lane));
-    poll_codes(xl + OFF_AC + rep * (I / 4), I / 4, rg / 4, sh, lane, wave, epoch, A.err);
+    poll_codes(xl + OFF_AC + rep * (I / 4), I / 4, rg / 4, sh, lane, wave, epoch, A.err,
+               att ? nullptr : trace_sub(A, w, l, 22));
     trace_at(A, w, l, 9);
     if (s >= NPOLL) {
       int acc = 0;
