@@ -366,9 +366,11 @@ __device__ __forceinline__ void minmax16(const float* red, int lane, float& lo, 
 // polls plus 65536 x the number of copies.
 __device__ uint32_t poll_range(const u64* v, int c0, int c1, int blk, unsigned char* dst,
                                Err err, int lane, uint32_t tag, u64* tr = nullptr,
-                               const u64* flags = nullptr) {
+                               const u64* flags = nullptr, bool dense = false) {
   const int bytes = ((c1 - c0) * 8 + 1023) & ~1023;
-  {
+  // dense: copy again until every tag matches, without the sparse phase
+  // (for short waits while little else is in flight)
+  for (uint32_t n = 0;; ++n) {
     dma_wave<true>(v + c0, dst, bytes, lane * 16);
     __builtin_amdgcn_s_waitcnt(0);
     const u64* s = (const u64*)dst;
@@ -377,8 +379,14 @@ __device__ uint32_t poll_range(const u64* v, int c0, int c1, int blk, unsigned c
     for (int i = lane; i < c1 - c0; i += 64) ok &= (uint32_t)(s[i] >> 32) == tag;
     if (__all(ok)) {
       stamp(tr, 1, lane);
-      return 1u << 16;
+      return (n + 1) << 16;
     }
+    if (!dense) break;
+    if (n >= err.limit) {
+      if (lane == 0) atomicOr(err.word, 2u);
+      return (n + 1) << 16;
+    }
+    __builtin_amdgcn_s_sleep(2);
   }
   uint32_t spins = 0;
   const int b0 = c0 / blk, b1 = (c1 - 1) / blk;
@@ -415,7 +423,7 @@ __device__ uint32_t poll_range(const u64* v, int c0, int c1, int blk, unsigned c
 // wave has in flight.  Returns wave 0's poll_range count.
 __device__ uint32_t poll_all(const u64* v, int n, int blk, unsigned char* stage, Err err,
                              int lane, int wave, uint32_t tag, u64* tr = nullptr,
-                             const u64* flags = nullptr, int np = NW) {
+                             const u64* flags = nullptr, int np = NW, bool dense = false) {
   if (wave >= np) return 0;  // not a polling wave: its loads in flight stay in flight
   if (wave == 0) stamp(tr, 0, lane);
   const int chunk = ((n + np - 1) / np + 127) & ~127;
@@ -423,7 +431,7 @@ __device__ uint32_t poll_all(const u64* v, int n, int blk, unsigned char* stage,
   uint32_t r = 0;
   if (c0 < c1)
     r = poll_range(v, c0, c1, blk, stage + (size_t)c0 * 8, err, lane, tag, wave == 0 ? tr : nullptr,
-                   flags);
+                   flags, dense);
   __builtin_amdgcn_s_waitcnt(0);
   if (wave == 0) stamp(tr, 2, lane);
   return r;
@@ -725,7 +733,7 @@ __device__ QParam poll_amm(const u64* v, Shared& sh, int lane, int wave, uint32_
 // barrier.  The staging of each polling wave ends before DN_LDS.
 __device__ void poll_codes(const u64* v, int n, int blk, Shared& sh, int lane, int wave,
                            uint32_t tag, Err err, u64* tr = nullptr) {
-  poll_all(v, n, blk, sh.stage, err, lane, wave, tag, tr, nullptr, NPOLL);
+  poll_all(v, n, blk, sh.stage, err, lane, wave, tag, tr, nullptr, NPOLL, true);
   if (wave < NPOLL) {
     const int chunk = ((n + NPOLL - 1) / NPOLL + 127) & ~127;
     const int c1 = min(n, wave * chunk + chunk);
@@ -1214,8 +1222,10 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
     prime_units<W, W>(win, [&](int i) { return gu_addr(Lw, i); });
   };
   // the last row's four units into this wave's 4 KiB of LDS (stage bytes
-  // [16K, 80K) are free from the o projection on); requested after the wait
-  // for the attention output, which would otherwise queue behind them
+  // [16K, 80K): on workgroups without attention work they are free from the
+  // end of the q|k|v phase); requested with the register units, so that they
+  // are in before the o projection's stores, which would otherwise queue
+  // behind them
   auto issue_gate_up_lds = [&](int l) {
     const LayerW& Lw = sh.lt[l & 1];
     if (s + NW * 2 < ngu) {
@@ -1348,6 +1358,7 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
     } else {
       issue_o(l);
       issue_gate_up(l);
+      issue_gate_up_lds(l);
       issue_down_lds(l);
     }
 
@@ -1359,7 +1370,6 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
                           d0 ? dump_at<float>(A.dump, l, F_ATTN) : nullptr,
                           d0 ? dump_at<int8_t>(A.dump, l, F_C2) : nullptr, d0 ? d_s + 1 : nullptr,
                           d0 ? d_z + 1 : nullptr);
-    if (!att) issue_gate_up_lds(l);
     trace_at(A, w, l, 5);
     {
       int accs[1];
