@@ -1084,6 +1084,7 @@ __device__ void attention_item(const MegaArgs& A, uint32_t epoch, int l, int g, 
       for (int h = 0; h < HPI; ++h) red[(ks * HPI + h) * D + d] = acc[h];
     }
     lds_barrier();
+    if (nitem == 1 && tid == 0) stamp(tr, 3, lane);
     // fold the chunk into the running state of output (h, d)
     if (mine) {
       double o = 0.0;
@@ -1099,6 +1100,7 @@ __device__ void attention_item(const MegaArgs& A, uint32_t epoch, int l, int g, 
     }
   }
   if (nitem == 1) {
+    if (tid == 0) stamp(tr, 4, lane);
     if (mine) xput_rep(xl + OFF_ATT, Q, (h0 + oh) * D + od, (float)(O / Lsum), epoch);
     return;
   }
@@ -1437,8 +1439,18 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
       const bool live = lane < GU_ROWS && i < ngu;
       const float gv = dequant(ag + zc * cgk, qp.s, sgk);
       const float uv = dequant(au + zc * cuk, qp.s, suk);
+      // silu(g) u = (g >= 0 ? g u : g u t) / (1 + t) with t = e^-|g| in
+      // [0, 1]: the denominator lies in [1, 2], so two Newton steps on the
+      // reciprocal estimate replace a general fp64 division
       const double gd = gv;
-      const float a = (float)(gd / (1.0 + exp_t(-gd, sh.expc)) * (double)uv);
+      const double t = exp_t(-fabs(gd), sh.expc);
+      const double gu = gd * (double)uv;
+      const double num = gd >= 0.0 ? gu : gu * t;
+      const double den = 1.0 + t;
+      double rq = __builtin_amdgcn_rcp(den);
+      rq = fma(rq, fma(-den, rq, 1.0), rq);
+      rq = fma(rq, fma(-den, rq, 1.0), rq);
+      const float a = (float)(num * rq);
       if (live) sh.aval[i] = a;
       if constexpr (DUMP)
         if (live && d_a) d_a[gu0 + i] = a;
