@@ -2,10 +2,11 @@
 // (v_mfma_i32_32x32x32_i8), with the same dequantising epilogues as k_gemm
 // (store (+bias), residual add, SwiGLU over paired gate/up columns).
 //
-// Tiles of 128 x 256 x 64, 256 threads as 2 x 2 waves, each wave 64 x 128
-// of 32x32 accumulators.  Operand tiles go from global memory straight into
-// LDS with 16-byte LDS-DMA loads (no register staging), three stages deep,
-// so the loads of step k+2 overlap the matrix work of step k; one barrier
+// Tiles of BM x BN x BK (128 x 256 x 64 on 256 threads as 2 x 2 waves, or
+// 256 x 256 x 128 on 512 threads as 4 x 2 waves), each wave 64 x 128 of
+// 32x32 accumulators.  Operand tiles go from global memory straight into
+// LDS with 16-byte LDS-DMA loads (no register staging), NS stages deep, so
+// the loads of step k+NS-1 overlap the matrix work of step k; one barrier
 // per K step.
 //
 // LDS tile layout: 64-byte rows; the 16-byte chunk c of row r sits at chunk
@@ -14,8 +15,9 @@
 // The DMA writes 1 KiB per instruction at lane-contiguous positions; each
 // lane picks the global (row, chunk) that belongs at its position.
 //
-// Two workgroups share a CU (launch bounds 256 x 2), so one's epilogue and
-// prologue overlap the other's main loop.  Workgroup ids are dealt
+// With 256 threads two workgroups share a CU (launch bounds 256 x 2), so
+// one's epilogue and prologue overlap the other's main loop; with 512 one
+// workgroup has the CU (and its LDS) alone.  Workgroup ids are dealt
 // round-robin over the 8 XCDs, so the tile order gives each XCD a
 // contiguous run of tiles (groups of 8 M-tiles, M fastest) and its L2 sees
 // few distinct operand tiles at a time.
@@ -456,12 +458,19 @@ hipError_t launch_gemm_big(hipStream_t st, int M, int K, const int8_t* codes, co
     P.seg_start[i + 1] = P.seg_start[i] + segs[i].n;
   }
   P.ncols = (epi == EPI_SWIGLU) ? segs[0].n : P.seg_start[nseg];
-  // 128 x 256 tiles with 64-byte K steps, three stages, two workgroups per
-  // CU.  Measured alternatives, all slower: 256-row tiles on 8 waves (the
-  // per-step barrier then stalls the whole CU); 128 x 128 tiles with 128-byte
-  // steps in two stages (whole-line loads, but one stage ahead and more
-  // bytes per product); any shape with one workgroup per CU (nothing covers
-  // its epilogue and prologue).
+  // The main loop is bound by the operand bytes a CU keeps in flight over
+  // their latency (LDS holds the stages).  Store and residual epilogues are
+  // light: one workgroup per CU with 256 x 256 tiles and whole 128-byte K
+  // steps in two stages (256 int8 ops per operand byte, whole-line loads)
+  // is fastest there, once the rows fill enough tiles (16x387 prefill: q|k|v
+  // 60 -> 54 us, o 68 -> 64.5 us, down 201 -> 179 us per layer).  The SwiGLU
+  // epilogue's fp64 gate is as long as a good part of the main loop, so there
+  // two workgroups share each CU (one's epilogue overlaps the other's main
+  // loop): 128 x 256 tiles with 64-byte K steps in three stages.  Measured
+  // alternatives, slower for both: 256 x 256 with 64-byte steps in three or
+  // four stages, 256 x 128 with 128-byte steps in three stages, 128 x 256 or
+  // 128 x 128 with 128-byte steps in two stages.
+  if (epi != EPI_SWIGLU && M >= 1024) return launch_big<256, 256, 128, 2, 512>(st, P);
   return launch_big<128, 256, 64, 3, 256>(st, P);
 }
 
