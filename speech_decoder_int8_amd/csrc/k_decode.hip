@@ -830,9 +830,9 @@ __device__ __forceinline__ void run_units(i32x4 (&buf)[W], Addr addr, Use use) {
 // ---------------------------------------------------------- attention --
 // Work items: (KV head g, head group hh of 4 query heads, item sp < 4) on
 // workgroup 8 g + 4 hh + sp.  With nchunk live 64-key chunks (those holding
-// a key at or before the position) each (g, hh) uses nitem = min(4,
-// ceil(nchunk / 2)) items, item sp taking chunks sp, sp + nitem, ...; so up
-// to 127 rows are attended without a merge between workgroups.
+// a key at or before the position) each (g, hh) uses nitem = min(4, nchunk)
+// items, item sp taking chunks sp, sp + nitem, ...: a second chunk in the
+// same item costs more than the merge of two items' states.
 constexpr int ATT_RED = 0;                             // fp64 partial sums, 16 KiB
 constexpr int ATT_KV = 16 * 1024;                      // byte offset in stage
 constexpr int ATT_QKV = ATT_KV + 2 * (KEYS / 2) * 260 * 4;
@@ -1158,7 +1158,7 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
   // attention items (see attention_item): workgroup w < NATT holds item
   // sp = w % NIH of head group hh = (w / NIH) % HH of KV head g = w / (NIH HH)
   const int nchunk = A.pos / KEYS + 1;
-  const int nitem = min(NIH, (nchunk + 1) / 2);
+  const int nitem = min(NIH, nchunk);
   const bool att = w < NATT && (w % NIH) < nitem;
   // gate/up rows: rg per workgroup without attention work, by rank
   const int natt = NKV * HH * nitem;
