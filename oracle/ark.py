@@ -6,7 +6,8 @@ Pages cited (by title and section):
   [card]   model card "ark-asr-3b-onnx": sections "Files" (int8 dynamic
            quantisation, per-channel MatMul weights), "Shapes" (geometry,
            static cache, deltas), "Inference" (prompt, slot count, masked
-           greedy loop), "Revision history" (fp16 table, int8 LM head).
+           greedy loop), "Revision history" (fp16 table, int8 LM head, the
+           weight-only int4 LM tier).
   [cook]   sglang-omni cookbook "ARK-ASR-3B": intro (Qwen2 decoder), "Audio
            Handling" (token count), "Marker-Token Suppression" (mask set).
   [readme] "ARK-ASR-3B" README: "vLLM" section (<|im_end|> is the stop token).
@@ -33,6 +34,8 @@ __all__ = [
     "apply_rope", "attention", "swiglu", "masked_argmax", "cache_write",
     "embed_splice", "embed_ids", "OracleLayer", "OracleModel", "build_model",
     "layer_forward", "forward", "prefill", "decode_step", "layer_param_count",
+    "INT4_BLOCK", "prep_weight_int4", "dequant_weight_int4", "lm_head_int4",
+    "int4_size_ratio",
 ]
 
 F32 = np.float32
@@ -70,6 +73,61 @@ def prep_weight(w: np.ndarray):
     q = np.clip(q, -127, 127).astype(np.int8)
     q[s == 0] = 0
     return q, s
+
+
+# ------------------------------------------------ weight-only int4 tier --
+# [card] "Revision history": v2 added a weight-only int4 LM tier.  Reading
+# (the page names the tier, not its format): the LM head's weights are
+# stored as uint4 codes in blocks of INT4_BLOCK consecutive weights along K,
+# each block with an fp32 scale and a uint4 zero point (the asymmetric block
+# format of an ONNX 4-bit MatMul); "weight-only" means the activation stays
+# fp32: logits = h . dequant(W4)^T with no activation quantisation.  The
+# block is quantised like a dynamic activation tensor with 15 levels: range
+# widened to include 0, s = (max - min) / 15, z = sat(rne(-min / s)),
+# q = sat(rne(w / s) + z); a block of zeros has s = 0, z = 0, q = 0.
+INT4_BLOCK = 128
+
+
+def int4_size_ratio(block: int, zero_point: bool = True) -> float:
+    """fp32 bytes over int4-tier bytes per weight: 4 bits per code plus one
+    fp32 scale (and a 4-bit zero point) per block."""
+    per = 0.5 + 4.0 / block + (0.5 / block if zero_point else 0.0)
+    return 4.0 / per
+
+
+def prep_weight_int4(w: np.ndarray, block: int = INT4_BLOCK):
+    """uint4 codes [n][k] (one per byte here, values 0..15), scales
+    fp32 [n][k / block], zero points uint8 [n][k / block] of W [n][k]."""
+    w = np.asarray(w, F32)
+    n, k = w.shape
+    assert k % block == 0
+    wb = w.reshape(n, k // block, block)
+    lo = np.minimum(wb.min(axis=2), F32(0.0)).astype(F32)
+    hi = np.maximum(wb.max(axis=2), F32(0.0)).astype(F32)
+    s = ((hi - lo).astype(F32) / F32(15.0)).astype(F32)
+    safe = np.where(s > 0, s, F32(1.0)).astype(F32)
+    z = np.clip(np.rint((-lo / safe).astype(F32)), 0, 15)
+    q = np.rint((wb / safe[:, :, None]).astype(F32)) + z[:, :, None].astype(F32)
+    q = np.clip(q, 0, 15)
+    q[s == 0] = 0
+    z[s == 0] = 0
+    return q.reshape(n, k).astype(np.uint8), s, z.astype(np.uint8)
+
+
+def dequant_weight_int4(codes, scale, zp, block: int = INT4_BLOCK) -> np.ndarray:
+    """w' = fp32((q - z) * s) per element (the weights the int4 tier
+    multiplies)."""
+    n, k = codes.shape
+    qz = codes.reshape(n, k // block, block).astype(F32) - zp[:, :, None].astype(F32)
+    return (qz * scale[:, :, None].astype(F32)).astype(F32).reshape(n, k)
+
+
+def lm_head_int4(h: np.ndarray, codes, scale, zp, block: int = INT4_BLOCK) -> np.ndarray:
+    """Weight-only int4 LM head: logits[b, n] = fp32(sum_k h[b, k] w'[n, k])
+    with the products summed in float64 (one rounding to fp32).  h [B, K]
+    fp32 (the final-normed last rows, not quantised)."""
+    wd = dequant_weight_int4(codes, scale, zp, block).astype(F64)
+    return (np.asarray(h, F32).astype(F64) @ wd.T).astype(F32)
 
 
 # --------------------------------------------------- activation quantiser --
@@ -274,6 +332,7 @@ class OracleModel:
     layers: list
     final_norm: np.ndarray | None = None
     lm_head: tuple | None = None              # (codes, scale) or None
+    lm_head4: tuple | None = None             # int4 tier (codes, scale, zp) or None
     embed: np.ndarray | None = None           # fp16 table
     cos: np.ndarray | None = None
     sin: np.ndarray | None = None
@@ -281,9 +340,10 @@ class OracleModel:
 
 
 def build_model(cfg, synth, layers=None, with_embed=True, linear="int8",
-                keep_fp32=False) -> OracleModel:
+                keep_fp32=False, lm_head4=False) -> OracleModel:
     """Quantise the seeded fp32 weights of `cfg` into an oracle model.
-    `layers` (iterable of layer indices) restricts the layers built."""
+    `layers` (iterable of layer indices) restricts the layers built;
+    `lm_head4` selects the weight-only int4 tier for the LM head."""
     idx = range(cfg.n_layers) if layers is None else layers
     out = []
     for l in idx:
@@ -295,7 +355,11 @@ def build_model(cfg, synth, layers=None, with_embed=True, linear="int8",
     m = OracleModel(cfg=cfg, layers=out, linear=linear)
     if cfg.lm_head:
         m.final_norm = synth.final_norm(cfg)
-        m.lm_head = prep_weight(synth.lm_head(cfg))
+        w = synth.lm_head(cfg)
+        m.lm_head = prep_weight(w)
+        if lm_head4:
+            m.lm_head4 = prep_weight_int4(w)
+        del w
     if with_embed:
         m.embed = synth.embed_table_f16(cfg)
     m.cos, m.sin = rope_tables(cfg.max_total_len, cfg.head_dim, cfg.rope_theta)
@@ -394,7 +458,11 @@ def forward(model: OracleModel, x: np.ndarray, p, k_caches, v_caches, trace=None
         kd.append(k)
         vd.append(v)
     logits = None
-    if model.lm_head is not None:
+    if model.lm_head4 is not None:
+        # the weight-only int4 tier: fp32 rows, no activation quantisation
+        hn = rmsnorm(x[:, -1, :], model.final_norm, model.cfg.rms_eps)
+        logits = lm_head_int4(hn, *model.lm_head4)
+    elif model.lm_head is not None:
         last = x[:, -1, :]                                      # [B, H]
         hn = rmsnorm(last, model.final_norm, model.cfg.rms_eps)
         codes_w, sw = model.lm_head
