@@ -14,7 +14,9 @@
  *   - section "Inference": prompt embeddings with the audio slots overwritten,
  *     prefill, then greedy decoding with every added-vocab <...> token masked
  *     except <|im_end|>;
- *   - section "Revision history": fp16 embedding table, int8 LM head.
+ *   - section "Revision history": fp16 embedding table, int8 LM head, and a
+ *     weight-only int4 LM tier (ark_qlinear4; its format is a reading, stated
+ *     at ark_prep_weight_int4).
  * The block structure is the dense Qwen2 decoder named by the sglang-omni
  * cookbook page "ARK-ASR-3B" (introduction): RMSNorm -> q/k/v (with bias) ->
  * rotary embedding -> grouped-query attention -> o -> residual; RMSNorm ->
@@ -99,6 +101,19 @@ typedef struct {
   int32_t n, k;
 } ark_qlinear;
 
+/* The weight-only int4 LM head W[n][k] (model card "ark-asr-3b-onnx",
+ * "Revision history": the int4 LM tier), prepared by ark_prep_weight_int4.
+ * Blocks of 128 consecutive weights along k; k % 256 == 0.  All arrays
+ * 16-byte aligned. */
+typedef struct {
+  const uint8_t* w;       /* [n][k/2] uint4 codes, two per byte: byte i of a
+                             row holds k = 2i (low nibble) and 2i + 1 (high) */
+  const float* scale;     /* [n][k/128] fp32 scale per block */
+  const uint8_t* zp;      /* [n][k/256] uint4 zero points, two per byte:
+                             byte j holds block 2j (low nibble) and 2j + 1 */
+  int32_t n, k;
+} ark_qlinear4;
+
 /* One decoder layer.  q: n = n_heads*head_dim (head h owns rows
  * [h*head_dim, (h+1)*head_dim)), k and v: n = n_kv_heads*head_dim, all with
  * bias; o: [hidden][n_heads*head_dim]; gate, up: [intermediate][hidden];
@@ -117,6 +132,11 @@ typedef struct {
   const uint16_t* embed_f16;  /* [vocab][hidden] IEEE fp16 bits (decode gather) */
   const double* rope_cos;     /* [max_total_len][head_dim/2] from ark_rope_table */
   const double* rope_sin;     /* [max_total_len][head_dim/2] */
+  ark_qlinear4 lm_head4;      /* [vocab][hidden] int4 tier; w == NULL: none.
+                                 At most one of lm_head and lm_head4 is set;
+                                 with lm_head4 the LM head multiplies the
+                                 final-normed fp32 rows (not quantised) by
+                                 the dequantised int4 weights */
 } ark_model;
 
 /* Workspace bytes needed by ark_prefill / ark_decode_step for B sequences
@@ -134,6 +154,32 @@ const char* ark_status_string(int status);
  * scale: [n], colsum: [n]; k % 16 == 0.  Errors: ARK_E_NULL, ARK_E_SHAPE. */
 int ark_prep_weight(const float* w, int32_t n, int32_t k, int8_t* codes,
                     float* scale, int32_t* colsum, void* stream);
+
+/* Quantise an fp32 weight W[n][k] (device) into the int4 LM tier's blocks
+ * (model card "ark-asr-3b-onnx", "Revision history"; the page names the
+ * tier, not its format).  Reading: each block of 128 weights along k is
+ * quantised like an activation tensor with 15 levels -- range widened to
+ * include 0, s = (max - min) / 15, z = sat(rne(-min / s)) in [0, 15],
+ * q = sat(rne(w / s) + z) in [0, 15], fp32 with correctly rounded division;
+ * a block of zeros gets s = 0, z = 0, codes 0.  The weights multiplied are
+ * w' = fp32((q - z) * s).  Outputs as ark_qlinear4 describes (codes
+ * [n][k/2], scale [n][k/128], zp [n][k/256]); k % 256 == 0, all pointers
+ * 16-byte aligned.  Errors: ARK_E_NULL, ARK_E_SHAPE, ARK_E_ALIGN. */
+int ark_prep_weight_int4(const float* w, int32_t n, int32_t k, uint8_t* codes, float* scale,
+                         uint8_t* zp, void* stream);
+
+/* The weight-only int4 LM head on B given rows: logits[b][j] =
+ * sum_i h[b][i] w'[j][i] in fp32 arithmetic.  The order of the sums, and at
+ * k == 2048 the form s (sum h q - z sum h) per 32-weight chunk, are the
+ * kernel's; the result lies within (32 ceil(k / 2048) + 12) u
+ * sum_i s_i |h[b][i]| (q_i + z_i) of the exact sum (u = 2^-24; s, q, z of
+ * weight i's block).  h:
+ * [B][ldh] fp32 (the final-normed last rows; the decoder calls this after
+ * its final RMSNorm); logits: [B][ldl].  1 <= B <= 64, ldh >= k, ldl >= n,
+ * h 16-byte aligned.  Errors: ARK_E_NULL, ARK_E_SHAPE, ARK_E_ALIGN,
+ * ARK_E_HIP. */
+int ark_lm_head_int4(int32_t B, const float* h, int32_t ldh, const ark_qlinear4* W,
+                     float* logits, int32_t ldl, void* stream);
 
 /* Rotary tables: cos/sin[pos][j] of pos * theta^(-2j/head_dim), fp64, for
  * pos < T and j < head_dim/2.  Errors: ARK_E_NULL, ARK_E_SHAPE. */

@@ -42,6 +42,11 @@ class ArkQLinear(C.Structure):
                 ("bias", C.c_void_p), ("n", C.c_int32), ("k", C.c_int32)]
 
 
+class ArkQLinear4(C.Structure):
+    _fields_ = [("w", C.c_void_p), ("scale", C.c_void_p), ("zp", C.c_void_p),
+                ("n", C.c_int32), ("k", C.c_int32)]
+
+
 class ArkLayer(C.Structure):
     _fields_ = [("ln1", C.c_void_p), ("ln2", C.c_void_p), ("q", ArkQLinear), ("k", ArkQLinear),
                 ("v", ArkQLinear), ("o", ArkQLinear), ("gate", ArkQLinear), ("up", ArkQLinear),
@@ -51,7 +56,7 @@ class ArkLayer(C.Structure):
 class ArkModel(C.Structure):
     _fields_ = [("d", ArkDims), ("layers", C.POINTER(ArkLayer)), ("final_norm", C.c_void_p),
                 ("lm_head", ArkQLinear), ("embed_f16", C.c_void_p), ("rope_cos", C.c_void_p),
-                ("rope_sin", C.c_void_p)]
+                ("rope_sin", C.c_void_p), ("lm_head4", ArkQLinear4)]
 
 
 P = C.c_void_p
@@ -65,6 +70,8 @@ _SIGS = {
     "ark_status_string": (C.c_char_p, [C.c_int]),
     "ark_prep_weight": (C.c_int, [P, I32, I32, P, P, P, P]),
     "ark_rope_table": (C.c_int, [I32, I32, C.c_double, P, P, P]),
+    "ark_prep_weight_int4": (C.c_int, [P, I32, I32, P, P, P, P]),
+    "ark_lm_head_int4": (C.c_int, [I32, P, I32, C.POINTER(ArkQLinear4), P, I32, P]),
     "ark_embed_splice": (C.c_int, [C.POINTER(ArkDims), I32, I32, P, P, P, I32, I32, P, P]),
     "ark_prefill": (C.c_int, [C.POINTER(ArkModel), I32, I32, P, PI32, PP, PP, P, P, P, P, P,
                               C.c_size_t, P]),
@@ -177,6 +184,42 @@ def prep_weight(w, stream=None):
     return codes, scale, colsum
 
 
+INT4_BLOCK = 128
+
+
+def prep_weight_int4(w, stream=None):
+    """fp32 [n][k] device tensor -> the int4 tier's (codes uint8 [n][k/2],
+    two uint4 per byte; scale fp32 [n][k/128]; zero points uint8 [n][k/256],
+    two uint4 per byte)."""
+    import torch
+    n, k = w.shape
+    codes = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    scale = torch.empty((n, k // INT4_BLOCK), dtype=torch.float32, device=w.device)
+    zp = torch.empty((n, k // (2 * INT4_BLOCK)), dtype=torch.uint8, device=w.device)
+    _check("ark_prep_weight_int4", lib().ark_prep_weight_int4(_ptr(w), n, k, _ptr(codes), _ptr(scale),
+                                                               _ptr(zp), _stream(stream)))
+    return codes, scale, zp
+
+
+class QLinear4:
+    """Device tensors of the int4 LM tier's weight and its ctypes view."""
+
+    def __init__(self, codes, scale, zp):
+        self.codes, self.scale, self.zp = codes, scale, zp
+
+    def c(self) -> ArkQLinear4:
+        n, k2 = self.codes.shape
+        return ArkQLinear4(_ptr(self.codes), _ptr(self.scale), _ptr(self.zp), n, 2 * k2)
+
+
+def lm_head_int4(h, W: QLinear4, logits, stream=None):
+    """logits [B][n] = h [B][k] . dequant(W)^T (ark_lm_head_int4)."""
+    B, k = h.shape
+    c = W.c()
+    _check("ark_lm_head_int4", lib().ark_lm_head_int4(B, _ptr(h), h.stride(0), C.byref(c), _ptr(logits),
+                                                       logits.stride(0), _stream(stream)))
+
+
 def rope_table(T: int, head_dim: int, theta: float, device="cuda", stream=None):
     import torch
     c = torch.empty((T, head_dim // 2), dtype=torch.float64, device=device)
@@ -204,11 +247,13 @@ class DeviceModel:
     """A prepared decoder on the GPU: int8 weights, gains, rope tables,
     embedding table, plus the ark_model struct that points at them."""
 
-    def __init__(self, cfg, layers, final_norm, lm_head, embed_f16, rope_cos, rope_sin):
+    def __init__(self, cfg, layers, final_norm, lm_head, embed_f16, rope_cos, rope_sin,
+                 lm_head4=None):
         self.cfg = cfg
         self.layers = layers              # list of dicts of QLinear / tensors
         self.final_norm = final_norm
         self.lm_head = lm_head            # QLinear or None
+        self.lm_head4 = lm_head4          # QLinear4 or None (the int4 tier)
         self.embed_f16 = embed_f16        # int16 tensor (fp16 bits) or None
         self.rope_cos, self.rope_sin = rope_cos, rope_sin
         self.dims = dims_of(cfg)
@@ -219,13 +264,15 @@ class DeviceModel:
                                           L["down"].c())
         self.c = ArkModel(self.dims, self._layer_arr, _ptr(final_norm),
                           lm_head.c() if lm_head is not None else ArkQLinear(),
-                          _ptr(embed_f16), _ptr(rope_cos), _ptr(rope_sin))
+                          _ptr(embed_f16), _ptr(rope_cos), _ptr(rope_sin),
+                          lm_head4.c() if lm_head4 is not None else ArkQLinear4())
 
     def with_max_total_len(self, T: int) -> "DeviceModel":
         """The same weights with a static cache of T rows (new rotary tables)."""
         cfg = self.cfg.with_(max_total_len=T)
         rc, rs = rope_table(T, cfg.head_dim, cfg.rope_theta, self.rope_cos.device)
-        return DeviceModel(cfg, self.layers, self.final_norm, self.lm_head, self.embed_f16, rc, rs)
+        return DeviceModel(cfg, self.layers, self.final_norm, self.lm_head, self.embed_f16, rc, rs,
+                           self.lm_head4)
 
     def view(self, layers=None) -> "DeviceModel":
         """The same weights restricted to some layers (no LM head)."""
@@ -239,12 +286,42 @@ class DeviceModel:
         sub.c = ArkModel(sub.dims, sub._layer_arr, None, ArkQLinear(), _ptr(self.embed_f16),
                          _ptr(self.rope_cos), _ptr(self.rope_sin))
         sub.lm_head = None
+        sub.lm_head4 = None
         return sub
 
+    def with_lm_head(self, lm_head=None, lm_head4=None) -> "DeviceModel":
+        """The same layers with another LM head (an int8 QLinear, an int4
+        QLinear4, or neither)."""
+        return DeviceModel(self.cfg, self.layers, self.final_norm, lm_head, self.embed_f16,
+                           self.rope_cos, self.rope_sin, lm_head4)
 
-def load_model(cfg, synth, device="cuda", stream=None, layers=None) -> DeviceModel:
+
+def load_lm_head_int4(cfg, synth, device="cuda", stream=None) -> QLinear4:
+    """The seeded fp32 LM-head rows prepared into the int4 tier on the GPU
+    (ark_prep_weight_int4), a slice of rows at a time."""
+    import torch
+    H = cfg.hidden
+    codes = torch.empty((cfg.vocab, H // 2), dtype=torch.uint8, device=device)
+    scale = torch.empty((cfg.vocab, H // INT4_BLOCK), dtype=torch.float32, device=device)
+    zp = torch.empty((cfg.vocab, H // (2 * INT4_BLOCK)), dtype=torch.uint8, device=device)
+    step = 16 * synth.ROW_CHUNK
+    for r0 in range(0, cfg.vocab, step):
+        r1 = min(cfg.vocab, r0 + step)
+        wt = torch.from_numpy(np.ascontiguousarray(synth.lm_head_rows(cfg, r0, r1))).to(device)
+        c, s, z = prep_weight_int4(wt, stream)
+        codes[r0:r1].copy_(c)
+        scale[r0:r1].copy_(s)
+        zp[r0:r1].copy_(z)
+        del wt, c, s, z
+    return QLinear4(codes, scale, zp)
+
+
+def load_model(cfg, synth, device="cuda", stream=None, layers=None,
+               lm_head4: bool = False) -> DeviceModel:
     """Upload the seeded fp32 weights of `cfg` layer by layer and prepare them
-    on the GPU (ark_prep_weight); the fp32 copies are released as it goes."""
+    on the GPU (ark_prep_weight); the fp32 copies are released as it goes.
+    lm_head4: prepare the LM head as the weight-only int4 tier instead of
+    int8."""
     import torch
 
     def up(a):
@@ -262,8 +339,11 @@ def load_model(cfg, synth, device="cuda", stream=None, layers=None) -> DeviceMod
             del wt
         out.append(L)
         del w
-    final_norm, lm = None, None
-    if cfg.lm_head:
+    final_norm, lm, lm4 = None, None, None
+    if cfg.lm_head and lm_head4:
+        final_norm = up(synth.final_norm(cfg))
+        lm4 = load_lm_head_int4(cfg, synth, device, stream)
+    elif cfg.lm_head:
         final_norm = up(synth.final_norm(cfg))
         codes = torch.empty((cfg.vocab, cfg.hidden), dtype=torch.int8, device=device)
         scale = torch.empty(cfg.vocab, dtype=torch.float32, device=device)
@@ -281,7 +361,7 @@ def load_model(cfg, synth, device="cuda", stream=None, layers=None) -> DeviceMod
     emb = up(synth.embed_table_f16(cfg).view(np.int16))
     rc, rs = rope_table(cfg.max_total_len, cfg.head_dim, cfg.rope_theta, device, stream)
     torch.cuda.current_stream().synchronize()
-    return DeviceModel(cfg, out, final_norm, lm, emb, rc, rs)
+    return DeviceModel(cfg, out, final_norm, lm, emb, rc, rs, lm4)
 
 
 # ------------------------------------------------------------- the path --

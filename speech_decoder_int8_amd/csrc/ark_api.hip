@@ -29,7 +29,7 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
 struct Plan {
-  size_t x, rs, codes, qkv, q, attn, a, stats, qs, qz, part, done, gsk, mega, total;
+  size_t x, rs, codes, qkv, q, attn, a, stats, qs, qz, part, done, gsk, mega, hn, total;
 };
 
 bool use_mega(const ark_dims& d, int B, int S) {
@@ -69,6 +69,7 @@ Plan plan(const ark_dims& d, int B, int S) {
   p.done = take((size_t)kMaxBatch * 4);
   p.gsk = take(gemm_skinny_ws_bytes());
   p.mega = take(B == 1 ? decode_mega_ws_bytes(d.n_layers, d.max_total_len) : 0);
+  p.hn = take((size_t)B * H * 4);  // final-normed rows of the int4 LM tier
   p.total = o;
   return p;
 }
@@ -151,6 +152,15 @@ int check_qlinear(const ark_qlinear& q, int n, int k, bool bias_allowed) {
   return ARK_OK;
 }
 
+int check_qlinear4(const ark_qlinear4& q, int n, int k) {
+  if (!q.w || !q.scale || !q.zp) return ARK_E_NULL;
+  if (q.n != n || q.k != k || !lm4_supported(k)) return ARK_E_SHAPE;
+  if (!aligned(q.w, 16) || !aligned(q.scale, 4)) return ARK_E_ALIGN;
+  return ARK_OK;
+}
+
+bool has_head(const ark_model* m) { return m->lm_head.w || m->lm_head4.w; }
+
 int check_model(const ark_model* m, bool need_embed) {
   if (!m) return ARK_E_NULL;
   const ark_dims& d = m->d;
@@ -171,10 +181,17 @@ int check_model(const ark_model* m, bool need_embed) {
     if ((e = check_qlinear(L.up, I, H, false))) return e;
     if ((e = check_qlinear(L.down, H, I, false))) return e;
   }
+  if (m->lm_head.w && m->lm_head4.w) return ARK_E_SHAPE;
   if (m->lm_head.w) {
     if (!m->final_norm) return ARK_E_NULL;
     int e;
     if ((e = check_qlinear(m->lm_head, d.vocab, H, false))) return e;
+  }
+  if (m->lm_head4.w) {
+    if (!m->final_norm) return ARK_E_NULL;
+    if (!norm_quant_row_supported(H)) return ARK_E_SHAPE;
+    int e;
+    if ((e = check_qlinear4(m->lm_head4, d.vocab, H))) return e;
   }
   return ARK_OK;
 }
@@ -187,7 +204,7 @@ int check_step(const ark_model* m, int B, int S, const int32_t* pos, const float
   const ark_dims& d = m->d;
   for (int l = 0; l < d.n_layers; ++l)
     if (!kc[l] || !vc[l]) return ARK_E_NULL;
-  if (logits && !m->lm_head.w) return ARK_E_SHAPE;
+  if (logits && !has_head(m)) return ARK_E_SHAPE;
   for (int b = 0; b < B; ++b)
     if (pos[b] < 0 || (int64_t)pos[b] + S > d.max_total_len) return ARK_E_RANGE;
   if (!aligned(ws, kAlign) || !aligned(kd, 16) || !aligned(vd, 16)) return ARK_E_ALIGN;
@@ -236,6 +253,28 @@ inline bool prof_claim(hipEvent_t& b, hipEvent_t& e) {
   do {                                      \
     if ((expr) != hipSuccess) return ARK_E_HIP; \
   } while (0)
+
+// The int4 tier's LM head over B rows (row b at last + b * ldx): the final
+// RMSNorm into the workspace's hn rows (its uint8 quantisation, which the
+// fused row kernel also writes, goes to the code scratch and is not used),
+// then the weight-only int4 head.  A parity record gets the normed rows.
+int head_int4(const ark_model* m, int B, const float* last, int ldx, float* logits, char* ws,
+              const Plan& p, hipStream_t st, const DumpRec* dr) {
+  const ark_dims& d = m->d;
+  const int H = d.hidden;
+  float* hn = (float*)(ws + p.hn);
+  if (launch_norm_quant_row(st, B, H, last, ldx, m->final_norm, d.rms_eps, (int8_t*)(ws + p.codes),
+                            (float*)(ws + p.qs), (int*)(ws + p.qz), hn) != hipSuccess)
+    return ARK_E_HIP;
+  if (dr && dr->base &&
+      hipMemcpyAsync(dr->base + dr->head[0], hn, (size_t)B * H * 4, hipMemcpyDeviceToDevice, st) !=
+          hipSuccess)
+    return ARK_E_HIP;
+  const ark_qlinear4& W = m->lm_head4;
+  return launch_lm4(st, B, H, d.vocab, hn, H, W.w, W.scale, W.zp, logits, d.vocab) == hipSuccess
+             ? ARK_OK
+             : ARK_E_HIP;
+}
 
 // All layers and the LM head over the rows already in x ([B*S][H]).
 #define D2D(dst, src, bytes)                                                                  \
@@ -388,6 +427,8 @@ int run_forward(const ark_model* m, int B, int S, float* x, const int32_t* pos_h
     D2D(dptr(l, ARK_DUMP_X2), x, (size_t)R * H * 4);
   }
 
+  if (logits && m->lm_head4.w)
+    return head_int4(m, B, x + (size_t)(S - 1) * H, S * H, logits, ws, p, st, dr);
   if (logits) {
     Seg lm[1] = {seg_of(m->lm_head, logits, d.vocab)};
     const float* last = x + (size_t)(S - 1) * H;  // row S-1 of each sequence, stride S*H
@@ -464,6 +505,10 @@ int mega_step(const ark_model* m, const int32_t* token, int pos, float* kd, floa
               hipStream_t st, const DumpRec* dr = nullptr) {
   const ark_dims& d = m->d;
   const Plan p = plan(d, 1, 1);
+  // int4 tier: the kernel stops after the layers (its hidden row goes to
+  // hidden_out or the workspace's x row); the head and the argmax follow
+  const bool h4 = logits && m->lm_head4.w;
+  float* x_last = hidden_out ? hidden_out : (h4 ? (float*)(ws + p.x) : nullptr);
   MegaStep S;
   S.L = d.n_layers;
   S.T = d.max_total_len;
@@ -472,25 +517,29 @@ int mega_step(const ark_model* m, const int32_t* token, int pos, float* kd, floa
   S.eps = d.rms_eps;
   S.token = token;
   S.table = m->embed_f16;
-  S.final_norm = logits ? m->final_norm : nullptr;
-  S.lm_w = logits ? m->lm_head.w : nullptr;
+  S.final_norm = (logits && !h4) ? m->final_norm : nullptr;
+  S.lm_w = (logits && !h4) ? m->lm_head.w : nullptr;
   S.lm_sw = m->lm_head.scale;
   S.lm_cs = m->lm_head.colsum;
   S.rcos = m->rope_cos;
   S.rsin = m->rope_sin;
   S.kdelta = kd;
   S.vdelta = vd;
-  S.logits = logits;
-  S.hidden_out = hidden_out;
-  S.mask = logits ? mask : nullptr;
-  S.out_token = out_token;
+  S.logits = h4 ? nullptr : logits;
+  S.hidden_out = x_last;
+  S.mask = (logits && !h4) ? mask : nullptr;
+  S.out_token = h4 ? nullptr : out_token;
   memset(&S.dump, 0, sizeof(S.dump));
   if (dr) S.dump = *dr;
   S.spin_limit = mega_spin_limit();
   hipEvent_t eb = nullptr, ee = nullptr;
   prof_claim(eb, ee);
-  const hipError_t e = decode_mega_launch(st, ws + p.mega, S, eb, ee);
-  return e == hipSuccess ? ARK_OK : ARK_E_HIP;
+  if (decode_mega_launch(st, ws + p.mega, S, eb, ee) != hipSuccess) return ARK_E_HIP;
+  if (!h4) return ARK_OK;
+  const int e = head_int4(m, 1, x_last, d.hidden, logits, ws, p, st, dr);
+  if (e || !out_token) return e;
+  return launch_masked_argmax(st, 1, d.vocab, logits, mask, out_token) == hipSuccess ? ARK_OK
+                                                                                     : ARK_E_HIP;
 }
 
 bool mega_ready(const ark_model* m, int B) {
@@ -670,6 +719,30 @@ int ark_prep_weight(const float* w, int32_t n, int32_t k, int8_t* codes, float* 
              : ARK_E_HIP;
 }
 
+int ark_prep_weight_int4(const float* w, int32_t n, int32_t k, uint8_t* codes, float* scale,
+                         uint8_t* zp, void* stream) {
+  if (!w || !codes || !scale || !zp) return ARK_E_NULL;
+  if (n < 1 || k < 256 || k % 256) return ARK_E_SHAPE;
+  if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(scale, 16) || !aligned(zp, 16))
+    return ARK_E_ALIGN;
+  return launch_prep_w4((hipStream_t)stream, w, n, k, codes, scale, zp) == hipSuccess ? ARK_OK
+                                                                                      : ARK_E_HIP;
+}
+
+int ark_lm_head_int4(int32_t B, const float* h, int32_t ldh, const ark_qlinear4* W,
+                     float* logits, int32_t ldl, void* stream) {
+  if (!h || !W || !logits) return ARK_E_NULL;
+  if (B < 1 || B > kMaxBatch || W->n < 1) return ARK_E_SHAPE;
+  int e = check_qlinear4(*W, W->n, W->k);
+  if (e) return e;
+  if (ldh < W->k || ldl < W->n) return ARK_E_SHAPE;
+  if (!aligned(h, 16)) return ARK_E_ALIGN;
+  return launch_lm4((hipStream_t)stream, B, W->k, W->n, h, ldh, W->w, W->scale, W->zp, logits,
+                    ldl) == hipSuccess
+             ? ARK_OK
+             : ARK_E_HIP;
+}
+
 int ark_rope_table(int32_t T, int32_t head_dim, double theta, double* cos_out, double* sin_out,
                    void* stream) {
   if (!cos_out || !sin_out) return ARK_E_NULL;
@@ -798,7 +871,7 @@ int ark_greedy_decode(const ark_model* m, int32_t B, int32_t* token_ids, int32_t
   int e = check_model(m, true);
   if (e) return e;
   if (!token_ids || !logits || !mask || !out_tokens) return ARK_E_NULL;
-  if (!m->lm_head.w) return ARK_E_SHAPE;
+  if (!has_head(m)) return ARK_E_SHAPE;
   if (max_steps < 0 || check_every < 1) return ARK_E_SHAPE;
   e = check_step(m, B, 1, cache_position, (const float* const*)k_cache,
                  (const float* const*)v_cache, k_delta, v_delta, logits, workspace,

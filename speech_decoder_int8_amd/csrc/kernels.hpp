@@ -59,6 +59,15 @@ hipError_t launch_prep_weight(hipStream_t st, const float* w, int n, int k, int8
 hipError_t launch_rope_table(hipStream_t st, int T, int D, double theta, double* c, double* s);
 hipError_t launch_embed(hipStream_t st, int B, int S, int H, int V, const int32_t* ids,
                         const uint16_t* table, const float* audio, int a0, int N, float* out);
+// Weight-only int4 LM tier (k_lm4.hip): block quantisation of an fp32
+// weight into packed uint4 codes [n][k/2], fp32 scales [n][k/128] and
+// packed uint4 zero points [n][k/256]; the head over B fp32 rows.
+hipError_t launch_prep_w4(hipStream_t st, const float* w, int n, int k, uint8_t* codes,
+                          float* scale, uint8_t* zp);
+bool lm4_supported(int K);
+hipError_t launch_lm4(hipStream_t st, int B, int K, int N, const float* h, int ldh,
+                      const uint8_t* w, const float* sc, const uint8_t* zp, float* logits,
+                      int ldl);
 hipError_t launch_masked_argmax(hipStream_t st, int B, int V, const float* logits,
                                 const uint8_t* mask, int32_t* out_ids);
 hipError_t launch_test_codes(hipStream_t st, int rows, int K, int R, const uint8_t* in,

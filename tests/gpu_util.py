@@ -60,7 +60,7 @@ class GpuState:
                               dtype=torch.float32, device=DEV)
         self.vd = torch.empty_like(self.kd)
         self.logits = torch.empty((B, cfg.vocab), dtype=torch.float32, device=DEV) \
-            if model.lm_head is not None else None
+            if (model.lm_head is not None or getattr(model, "lm_head4", None) is not None) else None
         self.ws = ark.workspace(model, B, S_max)
 
     def load_caches(self, kc, vc):

@@ -277,3 +277,49 @@ def test_noalloc_limit_and_validation():
                                        None) == ark.ARK_E_SHAPE
     assert lib.ark_decode_step_noalloc(C.byref(m), 1, None, pos, kc, kc, FAKE, FAKE, None, None,
                                        None) == ark.ARK_E_NULL
+
+
+def fake_qlinear4(n, k, **kw):
+    a = dict(w=FAKE, scale=FAKE, zp=FAKE, n=n, k=k)
+    a.update(kw)
+    return ark.ArkQLinear4(**a)
+
+
+def test_int4_tier_validation():
+    # the int4 LM tier replaces the int8 head: logits allowed, both heads not
+    m = fake_model(lm=False)
+    m.lm_head4 = fake_qlinear4(m.d.vocab, m.d.hidden)
+    hid = prefill_status(m, logits=FAKE, ws=None)
+    assert hid == ark.ARK_E_NULL            # got past the model checks to the workspace check
+    both = fake_model(lm=True)
+    both.lm_head4 = fake_qlinear4(both.d.vocab, both.d.hidden)
+    assert prefill_status(both) == ark.ARK_E_SHAPE
+    for bad, want in ((dict(zp=None), ark.ARK_E_NULL), (dict(scale=None), ark.ARK_E_NULL),
+                      (dict(n=1000), ark.ARK_E_SHAPE), (dict(k=1024), ark.ARK_E_SHAPE),
+                      (dict(w=FAKE + 8), ark.ARK_E_ALIGN), (dict(scale=FAKE + 2), ark.ARK_E_ALIGN)):
+        mb = fake_model(lm=False)
+        a = dict(n=mb.d.vocab, k=mb.d.hidden)
+        a.update(bad)
+        mb.lm_head4 = fake_qlinear4(**a)
+        assert prefill_status(mb) == want, bad
+    mn = fake_model(lm=False)
+    mn.lm_head4 = fake_qlinear4(mn.d.vocab, mn.d.hidden)
+    mn.final_norm = None
+    assert prefill_status(mn) == ark.ARK_E_NULL
+
+
+def test_int4_entry_points_error_paths():
+    lib = ark.lib()
+    assert lib.ark_prep_weight_int4(None, 4, 256, FAKE, FAKE, FAKE, None) == ark.ARK_E_NULL
+    assert lib.ark_prep_weight_int4(FAKE, 4, 384, FAKE, FAKE, FAKE, None) == ark.ARK_E_SHAPE
+    assert lib.ark_prep_weight_int4(FAKE, 0, 256, FAKE, FAKE, FAKE, None) == ark.ARK_E_SHAPE
+    assert lib.ark_prep_weight_int4(FAKE, 4, 256, FAKE + 4, FAKE, FAKE, None) == ark.ARK_E_ALIGN
+    W = fake_qlinear4(1000, 2048)
+    assert lib.ark_lm_head_int4(1, None, 2048, C.byref(W), FAKE, 1000, None) == ark.ARK_E_NULL
+    assert lib.ark_lm_head_int4(0, FAKE, 2048, C.byref(W), FAKE, 1000, None) == ark.ARK_E_SHAPE
+    assert lib.ark_lm_head_int4(65, FAKE, 2048, C.byref(W), FAKE, 1000, None) == ark.ARK_E_SHAPE
+    assert lib.ark_lm_head_int4(2, FAKE, 2047, C.byref(W), FAKE, 1000, None) == ark.ARK_E_SHAPE
+    assert lib.ark_lm_head_int4(2, FAKE, 2048, C.byref(W), FAKE, 999, None) == ark.ARK_E_SHAPE
+    assert lib.ark_lm_head_int4(1, FAKE + 4, 2048, C.byref(W), FAKE, 1000, None) == ark.ARK_E_ALIGN
+    Wk = fake_qlinear4(1000, 2000)
+    assert lib.ark_lm_head_int4(1, FAKE, 2048, C.byref(Wk), FAKE, 1000, None) == ark.ARK_E_SHAPE
