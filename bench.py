@@ -277,6 +277,33 @@ def gpu_bench(args):
 
     if args.extras:
         ex = {}
+        # the int4 LM tier: the same bs1 greedy steps with the head prepared
+        # as weight-only int4 blocks, and its head kernel alone
+        q4 = ark.load_lm_head_int4(cfg, synth)
+        gm4 = gm.with_lm_head(lm_head4=q4)
+        run.model = gm4
+        run.greedy(S, 4, out)
+        t4 = timed(torch, lambda: run.greedy(pos0, K, out))
+        run.model = gm
+        ex["decode_bs1_int4_head_tok_s"] = round(K / t4, 1)
+        ex["decode_bs1_int4_head_ms_per_step"] = round(t4 * 1e3 / K, 4)
+        H, V = cfg.hidden, cfg.vocab
+        hn = torch.randn((1, H), device="cuda")
+        lg4 = torch.empty((1, V), device="cuda")
+        lm4_bytes = V * H // 2 + V * (H // 128) * 4 + V * (H // 256) + H * 4 + V * 4
+        ark.lm_head_int4(hn, q4, lg4)
+        e0.record(st)
+        for _ in range(20):
+            ark.lm_head_int4(hn, q4, lg4)
+        e1.record(st)
+        torch.cuda.synchronize()
+        us4 = e0.elapsed_time(e1) * 1e3 / 20
+        ex["lm_head_int4_bs1_us"] = round(us4, 2)
+        ex["lm_head_int4_bytes"] = lm4_bytes
+        ex["lm_head_int4_frac_of_8TBps"] = round(lm4_bytes / (us4 * 1e-6) / PEAK_HBM, 4)
+        ex["lm_head_int8_bytes"] = V * H + V * 8 + H * 4 + V * 4
+        del gm4, q4, hn, lg4
+        torch.cuda.empty_cache()
         # prompt prefill of the 3 s clip
         t = timed(torch, lambda: run.prefill(x, [0]), reps=5)
         ex["prefill_c1_tok_s"] = round(S / t, 1)

@@ -505,10 +505,9 @@ int mega_step(const ark_model* m, const int32_t* token, int pos, float* kd, floa
               hipStream_t st, const DumpRec* dr = nullptr) {
   const ark_dims& d = m->d;
   const Plan p = plan(d, 1, 1);
-  // int4 tier: the kernel stops after the layers (its hidden row goes to
-  // hidden_out or the workspace's x row); the head and the argmax follow
+  // int4 tier: the kernel's tail runs the final norm, the int4 head and
+  // the masked argmax in place of the int8 head
   const bool h4 = logits && m->lm_head4.w;
-  float* x_last = hidden_out ? hidden_out : (h4 ? (float*)(ws + p.x) : nullptr);
   MegaStep S;
   S.L = d.n_layers;
   S.T = d.max_total_len;
@@ -517,29 +516,28 @@ int mega_step(const ark_model* m, const int32_t* token, int pos, float* kd, floa
   S.eps = d.rms_eps;
   S.token = token;
   S.table = m->embed_f16;
-  S.final_norm = (logits && !h4) ? m->final_norm : nullptr;
+  S.final_norm = logits ? m->final_norm : nullptr;
   S.lm_w = (logits && !h4) ? m->lm_head.w : nullptr;
+  S.lm4_w = h4 ? m->lm_head4.w : nullptr;
+  S.lm4_s = m->lm_head4.scale;
+  S.lm4_z = m->lm_head4.zp;
   S.lm_sw = m->lm_head.scale;
   S.lm_cs = m->lm_head.colsum;
   S.rcos = m->rope_cos;
   S.rsin = m->rope_sin;
   S.kdelta = kd;
   S.vdelta = vd;
-  S.logits = h4 ? nullptr : logits;
-  S.hidden_out = x_last;
-  S.mask = (logits && !h4) ? mask : nullptr;
-  S.out_token = h4 ? nullptr : out_token;
+  S.logits = logits;
+  S.hidden_out = hidden_out;
+  S.mask = logits ? mask : nullptr;
+  S.out_token = out_token;
   memset(&S.dump, 0, sizeof(S.dump));
   if (dr) S.dump = *dr;
   S.spin_limit = mega_spin_limit();
   hipEvent_t eb = nullptr, ee = nullptr;
   prof_claim(eb, ee);
-  if (decode_mega_launch(st, ws + p.mega, S, eb, ee) != hipSuccess) return ARK_E_HIP;
-  if (!h4) return ARK_OK;
-  const int e = head_int4(m, 1, x_last, d.hidden, logits, ws, p, st, dr);
-  if (e || !out_token) return e;
-  return launch_masked_argmax(st, 1, d.vocab, logits, mask, out_token) == hipSuccess ? ARK_OK
-                                                                                     : ARK_E_HIP;
+  const hipError_t e = decode_mega_launch(st, ws + p.mega, S, eb, ee);
+  return e == hipSuccess ? ARK_OK : ARK_E_HIP;
 }
 
 bool mega_ready(const ark_model* m, int B) {

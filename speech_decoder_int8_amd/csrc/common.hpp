@@ -67,6 +67,11 @@ __device__ __forceinline__ T all_reduce(T v, Op op) {
 __device__ __forceinline__ double wave_sum(double v) {
   return dpp::all_reduce(v, [](double a, double b) { return a + b; });
 }
+// fp32 sum over the wave (the same reduction tree wherever it is used, so
+// two kernels that feed it the same lane values agree bit for bit).
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  return dpp::all_reduce(v, [](float a, float b) { return a + b; });
+}
 __device__ __forceinline__ int wave_sum(int v) {
   return dpp::all_reduce(v, [](int a, int b) { return a + b; });
 }

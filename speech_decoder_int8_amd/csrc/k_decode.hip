@@ -172,6 +172,9 @@ struct MegaArgs {
   const int8_t* lm_w;
   const float* lm_sw;
   const int32_t* lm_cs;
+  const uint8_t* lm4_w;
+  const float* lm4_s;
+  const uint8_t* lm4_z;
   const double* rcos;
   const double* rsin;
   float* kdelta;
@@ -495,6 +498,29 @@ __device__ QParam prologue_norm(const float* x, const float* g, double eps, Shar
   __syncthreads();
   if (tid == 0) stamp(tr, 3, 0);
   return p;
+}
+
+// The final RMSNorm of the int4 LM tier: x (in LDS) replaced by
+// fp32((x * rs) * g), the arithmetic of prologue_norm, without quantisation
+// (the int4 tier's activations stay fp32).
+template <bool DUMP>
+__device__ void norm_in_place(float* x, const float* g, double eps, Shared& sh, int tid,
+                              const DumpRec* dump = nullptr) {
+  double ss = 0.0;
+  for (int i = tid; i < H; i += NT) {
+    const double v = x[i];
+    ss += v * v;
+  }
+  ss = block_sum<NT>(ss, sh.redd);
+  const double rs = 1.0 / sqrt(ss / (double)H + eps);
+#pragma unroll
+  for (int j = 0; j < H / NT; ++j) {
+    const int i = tid + j * NT;
+    x[i] = (float)(((double)x[i] * rs) * (double)g[i]);
+    if constexpr (DUMP)
+      if (dump && dump->base) ((float*)(dump->base + dump->head[0]))[i] = x[i];
+  }
+  __syncthreads();
 }
 
 // Dynamic uint8 quantiser straight from the staged exchange words.
@@ -1552,12 +1578,91 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
   trace_at(A, w, A.L, 0);
   if (w == 0 && A.hidden_out)
     for (int i = tid; i < H; i += NT) A.hidden_out[i] = sh.xs[i];
-  if (!A.lm_w) return;
-  const QParam qp = prologue_norm<DUMP>(sh.xs, sh.gain, A.eps, sh, tid, nullptr,
-                                        (DUMP && w == 0) ? &A.dump : nullptr);
+  if (!A.lm_w && !A.lm4_w) return;
   const int r0 = (int)(((long long)w * A.V) / NWG), r1 = (int)(((long long)(w + 1) * A.V) / NWG);
   float bv = -INFINITY;
   int bi = INT_MAX;
+  if (A.lm4_w) {
+    // int4 LM tier: the normed row stays fp32; each streamer wave takes
+    // whole 1 KB code rows (lane l: codes of k = 32 l .. 32 l + 31, block
+    // l / 4) and forms s (sum h q - z sum h) per lane, then the wave sum
+    norm_in_place<DUMP>(sh.xs, sh.gain, A.eps, sh, tid, (DUMP && w == 0) ? &A.dump : nullptr);
+    if (wave > 0) {
+      const int s = wave - 1;
+      float hv[32];
+#pragma unroll
+      for (int i = 0; i < 32; i += 4) {
+        const float4 t = *(const float4*)(sh.xs + 32 * lane + i);
+        hv[i] = t.x;
+        hv[i + 1] = t.y;
+        hv[i + 2] = t.z;
+        hv[i + 3] = t.w;
+      }
+      float hsum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) hsum += hv[i];
+      const int blk = lane / 4;
+      constexpr int GR = 4;
+      i32x4 b0[GR], b1[GR];
+      float s0[GR], s1[GR];
+      uint32_t z0[GR], z1[GR];
+      int m0[GR], m1[GR];
+      const int nmine = (r1 - r0 - s + NS - 1) / NS;
+      const int ngroups = (nmine + GR - 1) / GR;
+      auto load_group = [&](int gidx, i32x4 (&b)[GR], float (&sc)[GR], uint32_t (&zb)[GR],
+                            int (&mk)[GR]) {
+#pragma unroll
+        for (int k = 0; k < GR; ++k) {
+          const int n = r0 + s + NS * (gidx * GR + k);
+          const bool valid = n < r1;
+          const int nn = valid ? n : r0;
+          b[k] = ldg_nt((const int8_t*)A.lm4_w + (size_t)nn * (H / 2) + 16 * lane);
+          sc[k] = ldg(A.lm4_s + (size_t)nn * (H / 128) + blk);
+          zb[k] = A.lm4_z[(size_t)nn * (H / 256) + blk / 2];
+          mk[k] = (valid && A.mask) ? (int)ldg(A.mask + n) : 1;
+        }
+      };
+      auto use_group = [&](int gidx, const i32x4 (&b)[GR], const float (&sc)[GR],
+                           const uint32_t (&zb)[GR], const int (&mk)[GR]) {
+#pragma unroll
+        for (int k = 0; k < GR; ++k) {
+          float a = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t x = (uint32_t)b[k][j];
+            uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
+            asm volatile("" : "+v"(lo), "+v"(hi));  // keeps the byte conversions direct
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              a = fmaf(hv[8 * j + 2 * m], (float)((lo >> (8 * m)) & 0xffu), a);
+              a = fmaf(hv[8 * j + 2 * m + 1], (float)((hi >> (8 * m)) & 0xffu), a);
+            }
+          }
+          const float zf = (float)((zb[k] >> (4 * (blk & 1))) & 15u);
+          const float y = wave_sum_f32(sc[k] * (a - zf * hsum));
+          const int n = r0 + s + NS * (gidx * GR + k);
+          if (lane == 0 && n < r1) {
+            A.logits[n] = y;
+            if (mk[k] == 0 && !isnan(y) && (y > bv || (y == bv && n < bi))) {
+              bv = y;
+              bi = n;
+            }
+          }
+        }
+      };
+      if (ngroups > 0) load_group(0, b0, s0, z0, m0);
+      for (int gg = 0; gg < ngroups; gg += 2) {
+        if (gg + 1 < ngroups) load_group(gg + 1, b1, s1, z1, m1);
+        use_group(gg, b0, s0, z0, m0);
+        if (gg + 1 < ngroups) {
+          if (gg + 2 < ngroups) load_group(gg + 2, b0, s0, z0, m0);
+          use_group(gg + 1, b1, s1, z1, m1);
+        }
+      }
+    }
+  } else {
+  const QParam qp = prologue_norm<DUMP>(sh.xs, sh.gain, A.eps, sh, tid, nullptr,
+                                        (DUMP && w == 0) ? &A.dump : nullptr);
   if (wave > 0) {
     const int s = wave - 1;  // streamer 0..14
     const int zc = 128 - qp.z;
@@ -1612,6 +1717,7 @@ __global__ __launch_bounds__(1024, 1) void k_decode(MegaArgs A) {
         use_group(gg + 1, b1, w1, c1, m1);
       }
     }
+  }
   }
   trace_at(A, w, A.L, 1);
   if (!A.mask) return;
@@ -1801,6 +1907,9 @@ hipError_t decode_mega_launch(hipStream_t st, void* ws, const MegaStep& S, hipEv
   A.lm_w = S.lm_w;
   A.lm_sw = S.lm_sw;
   A.lm_cs = S.lm_cs;
+  A.lm4_w = S.lm4_w;
+  A.lm4_s = S.lm4_s;
+  A.lm4_z = S.lm4_z;
   A.rcos = S.rcos;
   A.rsin = S.rsin;
   A.kdelta = S.kdelta;

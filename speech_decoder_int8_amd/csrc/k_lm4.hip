@@ -64,10 +64,6 @@ hipError_t launch_prep_w4(hipStream_t st, const float* w, int n, int k, uint8_t*
   return hipGetLastError();
 }
 
-__device__ __forceinline__ float wave_sum_f(float v) {
-  return dpp::all_reduce(v, [](float a, float b) { return a + b; });
-}
-
 // The 32 weights of a 16-byte chunk (codes of k = 32 c .. 32 c + 31 of one
 // row, all in block c / 4), dequantised: w'[i] = fp32((q_i - z) * s).
 __device__ __forceinline__ void dequant32(const i32x4 v, float s, int z, float (&wq)[32]) {
@@ -157,7 +153,7 @@ __global__ __launch_bounds__(256) void k_lm4_k2048(int N, const float* __restric
       const float zf = (float)((zb[r] >> (4 * (blk & 1))) & 15u);
 #pragma unroll
       for (int b = 0; b < RB; ++b) {
-        const float t = wave_sum_f(s[r] * (a[b] - zf * hsum[b]));
+        const float t = wave_sum_f32(s[r] * (a[b] - zf * hsum[b]));
         if (lane == 0 && n0 + r < N) logits[(size_t)b * ldl + n0 + r] = t;
       }
     }
@@ -211,7 +207,7 @@ __global__ __launch_bounds__(256) void k_lm4_rows(int B, int K, int N,
 #pragma unroll
     for (int b = 0; b < kLm4MaxRows; ++b) {
       if (b < B) {
-        const float t = wave_sum_f(acc[b]);
+        const float t = wave_sum_f32(acc[b]);
         if (lane == 0) logits[(size_t)b * ldl + n] = t;
       }
     }

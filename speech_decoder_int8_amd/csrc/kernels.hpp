@@ -343,6 +343,11 @@ struct MegaStep {
   const int8_t* lm_w;
   const float* lm_sw;
   const int32_t* lm_cs;
+  // the int4 LM tier (lm4_w != nullptr, lm_w == nullptr): packed codes
+  // [V][H/2], scales [V][H/128], packed zero points [V][H/256]
+  const uint8_t* lm4_w;
+  const float* lm4_s;
+  const uint8_t* lm4_z;
   const double* rcos;
   const double* rsin;
   float* kdelta;
