@@ -9,7 +9,11 @@ Parity status per function (see each docstring for the passage it follows):
   closed forms, brute force on tiny inputs, invariants fixed by the pages, or
   the pages' printed numbers.  The behaviour of the trained model (its
   transcripts, the verification table missing from the model card) is parity
-  unpinned: no trained weights exist in this environment.
+  unpinned: no trained weights exist in this environment.  Two readings of
+  the 3B adapter are parity unpinned as choices (the functions themselves
+  are pinned): the GELU between its layers and its 4096 inner width (the
+  pages print neither; the 0.6B parameter count pins the two-layer
+  structure and an inner width of twice the hidden width there).
 """
 from .ark import *  # noqa: F401,F403
 from .ark import __all__  # noqa: F401

@@ -11,6 +11,9 @@ Pages cited (by title and section):
   [cook]   sglang-omni cookbook "ARK-ASR-3B": intro (Qwen2 decoder), "Audio
            Handling" (token count), "Marker-Token Suppression" (mask set).
   [readme] "ARK-ASR-3B" README: "vLLM" section (<|im_end|> is the stop token).
+  [audio8] article "Audio8: eight checkpoints, one broken link, and a 3B
+           model with nowhere to ship": "What arkasr actually is" (the
+           frame-merging MLP adapter, its parameter count at 0.6B).
 
 Numeric conventions of this oracle (readings of what the pages leave open):
   * Tensors between operations are fp32, as in the card's fp32 ONNX graph.
@@ -35,7 +38,8 @@ __all__ = [
     "embed_splice", "embed_ids", "OracleLayer", "OracleModel", "build_model",
     "layer_forward", "forward", "prefill", "decode_step", "layer_param_count",
     "INT4_BLOCK", "prep_weight_int4", "dequant_weight_int4", "lm_head_int4",
-    "int4_size_ratio",
+    "int4_size_ratio", "MERGE", "n_encoder_frames", "frame_merge", "gelu",
+    "OracleAdapter", "build_adapter", "adapter", "adapter_param_count",
 ]
 
 F32 = np.float32
@@ -494,3 +498,78 @@ def layer_param_count(hidden: int, kv_dim: int, intermediate: int, q_dim=None) -
     q_dim = hidden if q_dim is None else q_dim
     return (q_dim * hidden + q_dim) + 2 * (kv_dim * hidden + kv_dim) + hidden * q_dim \
         + 3 * intermediate * hidden + 2 * hidden
+
+
+# ----------------------------------------------- frame merge and adapter --
+# [card] "Inference", steps 2-3: the encoder output [1, seq, 1280] is cut to
+# a multiple of 4 frames, every 4 consecutive frames become one 5120-wide
+# row, and the adapter maps the rows to the decoder's width (2048); their
+# outputs overwrite the <|audio|> slots (step 5, embed_splice).  [card]
+# "Files": the adapter's MatMuls are int8 with dynamic activations, like
+# the decoder's.  [audio8] "What arkasr actually is": an MLP adapter that
+# merges merge_factor consecutive frames; the 0.6B model's adapter holds
+# 10,783,360 parameters, which is 5120 x 1792 + 1792 + 1792 x 896 + 896: two
+# linear layers with biases whose inner width is twice the decoder's hidden
+# width.  Readings for the 3B adapter (the pages give no widths or
+# activation): inner width 2 x 2048 = 4096; between the two layers the erf
+# GELU of the Whisper encoder the frames come from, in float64 rounded once
+# to fp32 (as the decoder's float operations); one (s, z) per sequence and
+# quantisation point (merged rows; GELU output).
+MERGE = 4
+
+
+def n_encoder_frames(samples: int) -> int:
+    """Encoder frames of a clip: [card] "Inference" step 4's count before its
+    division by the merge factor, ((samples // 160) + 1) // 2."""
+    return ((int(samples) // 160) + 1) // 2
+
+
+def frame_merge(frames: np.ndarray, merge: int = MERGE) -> np.ndarray:
+    """[seq][D] frames -> [seq // merge][merge * D]: row r is frames
+    merge*r .. merge*r + merge - 1 side by side; trailing frames dropped."""
+    frames = np.asarray(frames, F32)
+    seq, D = frames.shape
+    n = seq // merge
+    return frames[:n * merge].reshape(n, merge * D).copy()
+
+
+def gelu(x: np.ndarray) -> np.ndarray:
+    """x Phi(x) = 0.5 x (1 + erf(x / sqrt 2)) in float64, rounded to fp32."""
+    from scipy.special import erf
+    xd = np.asarray(x, F32).astype(F64)
+    return (0.5 * xd * (1.0 + erf(xd / np.sqrt(2.0)))).astype(F32)
+
+
+@dataclass
+class OracleAdapter:
+    up: tuple            # (int8 codes [inner][merge*D], fp32 scales [inner])
+    up_bias: np.ndarray  # [inner]
+    down: tuple          # (int8 codes [hidden][inner], fp32 scales [hidden])
+    down_bias: np.ndarray
+    merge: int = MERGE
+
+
+def build_adapter(cfg, synth) -> OracleAdapter:
+    """The seeded fp32 adapter weights of `cfg`, quantised per channel."""
+    w = synth.adapter_weights(cfg)
+    return OracleAdapter(prep_weight(w["w1"]), w["b1"], prep_weight(w["w2"]), w["b2"])
+
+
+def adapter(ad: OracleAdapter, frames: np.ndarray) -> np.ndarray:
+    """Merged rows -> int8 linear (+ bias) -> GELU -> int8 linear (+ bias),
+    per sequence.  frames [B][seq][D] fp32 -> [B][seq // merge][hidden]."""
+    frames = np.asarray(frames, F32)
+    out = []
+    for b in range(frames.shape[0]):
+        m = frame_merge(frames[b], ad.merge)
+        c, s, z = dynquant(m)
+        y = qlinear(c, s, z, ad.up[0], ad.up[1], ad.up_bias)
+        a = gelu(y)
+        c2, s2, z2 = dynquant(a)
+        out.append(qlinear(c2, s2, z2, ad.down[0], ad.down[1], ad.down_bias))
+    return np.stack(out)
+
+
+def adapter_param_count(frame_dim: int, merge: int, inner: int, hidden: int) -> int:
+    """Parameters of the two-layer adapter with biases."""
+    return merge * frame_dim * inner + inner + inner * hidden + hidden

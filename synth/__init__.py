@@ -21,6 +21,12 @@ Distributions:
   * audio stand-ins, embeddings N(0, 1) fp32
   * pre-filled caches           rows < valid length N(0, 1) fp32, other rows 0
   * token ids                   uniform over the unmasked vocabulary
+  * adapter weights, biases     N(0, 0.02) fp32 ([out][in] row-major)
+  * encoder frames              N(0, 1) fp32 [B][frames][frame_dim]
+
+Adapter geometry: frames of width 1280 (the encoder output of the model
+card's "Inference" step 1), 4 frames per merged row (step 2), an inner width
+of 4096; encoder frame counts 150 and 1500 for the 3 s and 30 s clips.
 """
 from __future__ import annotations
 
@@ -39,6 +45,7 @@ TAG_LM_HEAD, TAG_EMBED = 14, 15
 TAG_PROMPT_IDS, TAG_AUDIO, TAG_PREFILL_EMBEDS = 16, 17, 18
 TAG_DECODE_IDS, TAG_CACHE_LEN, TAG_CACHE_K, TAG_CACHE_V = 19, 20, 21, 22
 TAG_START_IDS = 23
+TAG_AD_W1, TAG_AD_B1, TAG_AD_W2, TAG_AD_B2, TAG_FRAMES = 24, 25, 26, 27, 28
 
 ROW_CHUNK = 2048          # rows per independent random stream of a big matrix
 WEIGHT_STD = 0.02
@@ -81,6 +88,10 @@ class ArkConfig:
     n_added: int = 64            # added-vocab ids at the top of the vocabulary
     cache_fill: tuple = ()       # (lo, hi): pre-filled valid length per sequence
     decode_ids_fixed: bool = False      # decode ids are drawn, not greedy
+    frame_dim: int = 1280        # encoder output width
+    merge: int = 4               # frames per merged adapter row
+    adapter_inner: int = 4096    # adapter's inner width
+    enc_frames: int = 0          # encoder frames per sequence (0: no adapter input)
 
     # Added-vocab convention: ids [vocab - n_added, vocab) are the "<...>"
     # added tokens; the first of them is the end token, which stays unmasked.
@@ -112,10 +123,13 @@ class ArkConfig:
 
 
 # Audio-slot counts of a 3 s and a 30 s clip at 16 kHz (48000 and 480000
-# samples).  The oracle owns the slot-count formula of the model card's
-# "Inference" step 4; its tests check that it gives these two numbers.
+# samples) and their encoder frame counts.  The oracle owns the formulas of
+# the model card's "Inference" steps 2-4; its tests check that they give
+# these numbers.
 _N3S = 37
 _N30S = 375
+_F3S = 150
+_F30S = 1500
 
 CONFIGS = {
     # Single layer at real shape, one sequence: 64-row prefill of N(0,1)
@@ -125,16 +139,16 @@ CONFIGS = {
                     n_added=0, decode_ids_fixed=True),
     # 3 s clip: 2 + 37 + 10 prompt rows, 32 greedy steps.
     "c1": ArkConfig(name="c1", seed=1001, prefill_len=2 + _N3S + 10, n_decode=32,
-                    audio_slots=_N3S),
+                    audio_slots=_N3S, enc_frames=_F3S),
     # 30 s clip: 2 + 375 + 10 prompt rows, greedy until the 512 cache is full.
     "c2": ArkConfig(name="c2", seed=1002, prefill_len=2 + _N30S + 10,
-                    n_decode=512 - (2 + _N30S + 10), audio_slots=_N30S),
+                    n_decode=512 - (2 + _N30S + 10), audio_slots=_N30S, enc_frames=_F30S),
     # 32 independent sequences with pre-filled caches, 64 lockstep steps.
     "c3": ArkConfig(name="c3", seed=1003, batch=32, prefill_len=0, n_decode=64,
                     cache_fill=(50, 400)),
     # Coalesced prefill of 16 x 387 N(0,1) rows, then 16 decode steps.
     "c4": ArkConfig(name="c4", seed=1004, batch=16, prefill_len=2 + _N30S + 10,
-                    n_decode=16, prefill_from_embeds=True),
+                    n_decode=16, prefill_from_embeds=True, enc_frames=_F30S),
     "c4_t1024": ArkConfig(name="c4_t1024", seed=1004, batch=16,
                           prefill_len=2 + _N30S + 10, n_decode=16,
                           prefill_from_embeds=True, max_total_len=1024),
@@ -145,11 +159,12 @@ CONFIGS = {
 # ragged tail while the oracle still finishes in seconds.
 TINY = ArkConfig(name="tiny", seed=7, n_layers=2, hidden=64, n_heads=4, n_kv_heads=2,
                  head_dim=16, intermediate=96, vocab=50, max_total_len=16,
-                 prefill_len=5, n_decode=4, n_added=8, audio_slots=2)
+                 prefill_len=5, n_decode=4, n_added=8, audio_slots=2,
+                 frame_dim=8, adapter_inner=24, enc_frames=10)
 SMALL = ArkConfig(name="small", seed=11, n_layers=2, hidden=512, n_heads=4,
                   n_kv_heads=2, head_dim=128, intermediate=1344, vocab=3000,
                   max_total_len=64, prefill_len=21, n_decode=6, n_added=64,
-                  audio_slots=9)
+                  audio_slots=9, frame_dim=320, adapter_inner=1024, enc_frames=39)
 
 
 # ---------------------------------------------------------------- weights --
@@ -237,7 +252,27 @@ def embed_table_f16(cfg: ArkConfig) -> np.ndarray:
     return t.astype(np.float16)
 
 
+def adapter_weights(cfg: ArkConfig) -> dict:
+    """fp32 adapter weights: w1 [inner][merge * frame_dim], b1 [inner],
+    w2 [hidden][inner], b2 [hidden]."""
+    K1, I, H = cfg.merge * cfg.frame_dim, cfg.adapter_inner, cfg.hidden
+    s = WEIGHT_STD
+    return {
+        "w1": _normal_rows(cfg, TAG_AD_W1, 0, I, K1, s),
+        "b1": _normal_vec(cfg, TAG_AD_B1, 0, I, s),
+        "w2": _normal_rows(cfg, TAG_AD_W2, 0, H, I, s),
+        "b2": _normal_vec(cfg, TAG_AD_B2, 0, H, s),
+    }
+
+
 # ------------------------------------------------------------------ inputs --
+def encoder_frames(cfg: ArkConfig, frames: int | None = None) -> np.ndarray:
+    """[B, frames, frame_dim] fp32 N(0, 1) stand-ins for the encoder output."""
+    n = cfg.enc_frames if frames is None else int(frames)
+    return _rng(cfg.seed, TAG_FRAMES, n, 0).standard_normal(
+        (cfg.batch, n, cfg.frame_dim), dtype=np.float32)
+
+
 def unmasked_ids(cfg: ArkConfig, rng: np.random.Generator, shape) -> np.ndarray:
     """Token ids drawn uniformly from the ids that are neither masked nor the
     end token (so a drawn prompt never contains a stop token)."""
