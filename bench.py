@@ -304,6 +304,24 @@ def gpu_bench(args):
         ex["lm_head_int8_bytes"] = V * H + V * 8 + H * 4 + V * 4
         del gm4, q4, hn, lg4
         torch.cuda.empty_cache()
+        # the frame merge + int8 adapter in front of the decoder: the 3 s
+        # clip's 150 encoder frames and sixteen 30 s clips' 1500 frames
+        ad = ark.load_adapter(cfg, synth)
+        for name, Bq, F in (("c1", 1, 150), ("c4", 16, 1500)):
+            fr = torch.randn((Bq, F, cfg.frame_dim), device="cuda")
+            n = F // cfg.merge
+            rows = torch.empty((Bq, n, cfg.hidden), device="cuda")
+            aws = ad.workspace(Bq, F)
+            ark.audio_adapter(ad, fr, rows, ws=aws)
+            t_ad = timed(torch, lambda: ark.audio_adapter(ad, fr, rows, ws=aws), reps=10)
+            ops = 2 * Bq * n * (cfg.merge * cfg.frame_dim * cfg.adapter_inner +
+                                cfg.adapter_inner * cfg.hidden)
+            ex[f"adapter_{name}_us"] = round(t_ad * 1e6, 1)
+            ex[f"adapter_{name}_rows"] = Bq * n
+            ex[f"adapter_{name}_int8_frac_of_5POPS"] = round(ops / t_ad / PEAK_INT8, 4)
+            del fr, rows, aws
+        del ad
+        torch.cuda.empty_cache()
         # prompt prefill of the 3 s clip
         t = timed(torch, lambda: run.prefill(x, [0]), reps=5)
         ex["prefill_c1_tok_s"] = round(S / t, 1)

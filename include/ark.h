@@ -186,6 +186,43 @@ int ark_lm_head_int4(int32_t B, const float* h, int32_t ldh, const ark_qlinear4*
 int ark_rope_table(int32_t T, int32_t head_dim, double theta, double* cos_out,
                    double* sin_out, void* stream);
 
+/* ------------------------------------------------------ audio adapter -- */
+
+/* The frame-merging int8 MLP adapter in front of the decoder (model card
+ * "ark-asr-3b-onnx", "Inference" steps 2-3: the encoder output cut to a
+ * multiple of `merge` frames, every `merge` consecutive frames side by side
+ * in one row, the adapter mapping the rows to the decoder's width; "Files":
+ * its MatMuls are int8 with dynamic activations; Audio8 article, "What
+ * arkasr actually is": two linear layers with biases).  Readings (the
+ * pages give no 3B widths and no activation): up is [inner][merge *
+ * frame_dim] with inner = 4096 for the ARK geometry, then the erf GELU
+ * x Phi(x) computed in fp64 and rounded once to fp32, then down
+ * [hidden][inner]; each of the two quantisation points takes one (s, z)
+ * per sequence, as in the decoder.  Both projections carry a bias. */
+typedef struct {
+  ark_qlinear up;       /* [inner][merge * frame_dim], bias [inner] */
+  ark_qlinear down;     /* [hidden][inner], bias [hidden] */
+  int32_t frame_dim;    /* encoder output width (1280) */
+  int32_t merge;        /* frames per merged row (4) */
+} ark_adapter;
+
+/* Workspace bytes of ark_audio_adapter for B sequences of `frames` encoder
+ * frames each; 0 if the arguments are invalid. */
+size_t ark_adapter_workspace_bytes(const ark_adapter* A, int32_t B, int32_t frames);
+
+/* Adapter rows of B sequences: enc [B][frames][frame_dim] fp32 (sequence b
+ * at enc + b * frames * frame_dim); n = frames / merge rows per sequence
+ * (trailing frames dropped, n >= 1); out [B][n][hidden] fp32, the rows
+ * ark_embed_splice writes into the <|audio|> slots; mid (optional, NULL:
+ * not written) [B][n][inner] fp32, the GELU output that the second
+ * quantisation sees.  1 <= B <= 64; up.k == merge * frame_dim, up.n ==
+ * down.k, both with a bias, k % 16 == 0; pointers 16-byte aligned,
+ * workspace 256-byte aligned.  Errors: ARK_E_NULL, ARK_E_SHAPE,
+ * ARK_E_WORKSPACE, ARK_E_ALIGN, ARK_E_HIP. */
+int ark_audio_adapter(const ark_adapter* A, int32_t B, int32_t frames, const float* enc,
+                      float* out, float* mid, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
 /* --------------------------------------------------------------- a1 ---- */
 
 /* Prompt embeddings with audio rows spliced in (model card "Inference",

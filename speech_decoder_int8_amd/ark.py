@@ -47,6 +47,11 @@ class ArkQLinear4(C.Structure):
                 ("n", C.c_int32), ("k", C.c_int32)]
 
 
+class ArkAdapter(C.Structure):
+    _fields_ = [("up", ArkQLinear), ("down", ArkQLinear), ("frame_dim", C.c_int32),
+                ("merge", C.c_int32)]
+
+
 class ArkLayer(C.Structure):
     _fields_ = [("ln1", C.c_void_p), ("ln2", C.c_void_p), ("q", ArkQLinear), ("k", ArkQLinear),
                 ("v", ArkQLinear), ("o", ArkQLinear), ("gate", ArkQLinear), ("up", ArkQLinear),
@@ -71,6 +76,8 @@ _SIGS = {
     "ark_prep_weight": (C.c_int, [P, I32, I32, P, P, P, P]),
     "ark_rope_table": (C.c_int, [I32, I32, C.c_double, P, P, P]),
     "ark_prep_weight_int4": (C.c_int, [P, I32, I32, P, P, P, P]),
+    "ark_adapter_workspace_bytes": (C.c_size_t, [C.POINTER(ArkAdapter), I32, I32]),
+    "ark_audio_adapter": (C.c_int, [C.POINTER(ArkAdapter), I32, I32, P, P, P, P, C.c_size_t, P]),
     "ark_lm_head_int4": (C.c_int, [I32, P, I32, C.POINTER(ArkQLinear4), P, I32, P]),
     "ark_embed_splice": (C.c_int, [C.POINTER(ArkDims), I32, I32, P, P, P, I32, I32, P, P]),
     "ark_prefill": (C.c_int, [C.POINTER(ArkModel), I32, I32, P, PI32, PP, PP, P, P, P, P, P,
@@ -362,6 +369,46 @@ def load_model(cfg, synth, device="cuda", stream=None, layers=None,
     rc, rs = rope_table(cfg.max_total_len, cfg.head_dim, cfg.rope_theta, device, stream)
     torch.cuda.current_stream().synchronize()
     return DeviceModel(cfg, out, final_norm, lm, emb, rc, rs, lm4)
+
+
+# ----------------------------------------------------------- the adapter --
+class DeviceAdapter:
+    """The prepared audio adapter on the GPU and its ark_adapter struct."""
+
+    def __init__(self, up: QLinear, down: QLinear, frame_dim: int, merge: int):
+        self.up, self.down, self.frame_dim, self.merge = up, down, frame_dim, merge
+        self.c = ArkAdapter(up.c(), down.c(), frame_dim, merge)
+
+    def workspace(self, B: int, frames: int):
+        import torch
+        n = lib().ark_adapter_workspace_bytes(C.byref(self.c), B, frames)
+        if n == 0:
+            raise ArkError("ark_adapter_workspace_bytes", ARK_E_SHAPE, "invalid adapter call")
+        return torch.empty(n, dtype=torch.uint8, device="cuda")
+
+
+def load_adapter(cfg, synth, device="cuda", stream=None) -> DeviceAdapter:
+    """The seeded fp32 adapter weights of `cfg`, prepared on the GPU."""
+    import torch
+    w = synth.adapter_weights(cfg)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    ad = DeviceAdapter(QLinear.from_f32(up(w["w1"]), up(w["b1"]), stream),
+                       QLinear.from_f32(up(w["w2"]), up(w["b2"]), stream), cfg.frame_dim, cfg.merge)
+    torch.cuda.current_stream().synchronize()
+    return ad
+
+
+def audio_adapter(ad: DeviceAdapter, enc, out, mid=None, ws=None, stream=None):
+    """enc [B][frames][frame_dim] -> out [B][frames // merge][hidden]
+    (ark_audio_adapter); mid: optional [B][frames // merge][inner]."""
+    B, frames = enc.shape[0], enc.shape[1]
+    if ws is None:
+        ws = ad.workspace(B, frames)
+    _check("ark_audio_adapter", lib().ark_audio_adapter(
+        C.byref(ad.c), B, frames, _ptr(enc), _ptr(out), _ptr(mid), _ptr(ws), ws.numel(),
+        _stream(stream)))
 
 
 # ------------------------------------------------------------- the path --

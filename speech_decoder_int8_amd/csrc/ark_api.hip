@@ -603,6 +603,51 @@ int decode_impl(const ark_model* m, int32_t B, const int32_t* token_ids,
                      st, dr);
 }
 
+// ---- audio adapter
+struct AdapterPlan {
+  size_t merged, codes, y, rs, stats, qs, qz, gsk, total;
+};
+
+// Workspace layout of ark_audio_adapter; `compact`: the merged rows are
+// copied together first (frames not a multiple of merge, several sequences).
+AdapterPlan adapter_plan(const ark_adapter& A, int B, int frames, bool* compact = nullptr) {
+  const size_t n = (size_t)(frames / A.merge), R = (size_t)B * n;
+  const size_t K1 = (size_t)A.merge * A.frame_dim, I = (size_t)A.up.n;
+  const bool c = B > 1 && frames % A.merge != 0;
+  if (compact) *compact = c;
+  AdapterPlan p;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align_up(bytes);
+    return at;
+  };
+  p.merged = take(c ? R * K1 * 4 : 0);
+  p.codes = take(R * std::max(K1, I));
+  p.y = take(R * I * 4);
+  p.rs = take(R * 8);
+  p.stats = take(2 * (size_t)kStatsSetInts * 4);
+  p.qs = take((size_t)kMaxBatch * 4);
+  p.qz = take((size_t)kMaxBatch * 4);
+  p.gsk = take(gemm_skinny_ws_bytes());
+  p.total = o;
+  return p;
+}
+
+int check_adapter(const ark_adapter* A, int B, int frames) {
+  if (!A) return ARK_E_NULL;
+  if (B < 1 || B > kMaxBatch || A->merge < 1 || A->frame_dim < 1) return ARK_E_SHAPE;
+  if (frames < A->merge) return ARK_E_SHAPE;
+  if ((int64_t)B * (frames / A->merge) > 65535) return ARK_E_SHAPE;
+  const int K1 = A->merge * A->frame_dim;
+  int e;
+  if ((e = check_qlinear(A->up, A->up.n, K1, true))) return e;
+  if ((e = check_qlinear(A->down, A->down.n, A->up.n, true))) return e;
+  if (!A->up.bias || !A->down.bias) return ARK_E_NULL;
+  if (A->up.n < 1 || A->down.n < 1 || K1 % 16 || A->up.n % 16) return ARK_E_SHAPE;
+  return ARK_OK;
+}
+
 // Validate a parity record request and build its descriptor.
 int dump_check(const ark_model* m, int B, int S, void* dump, size_t dump_bytes, uint64_t mask,
                DumpRec* out) {
@@ -739,6 +784,63 @@ int ark_lm_head_int4(int32_t B, const float* h, int32_t ldh, const ark_qlinear4*
                     ldl) == hipSuccess
              ? ARK_OK
              : ARK_E_HIP;
+}
+
+size_t ark_adapter_workspace_bytes(const ark_adapter* A, int32_t B, int32_t frames) {
+  if (check_adapter(A, B, frames) != ARK_OK) return 0;
+  return adapter_plan(*A, B, frames).total;
+}
+
+int ark_audio_adapter(const ark_adapter* A, int32_t B, int32_t frames, const float* enc,
+                      float* out, float* mid, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  int e = check_adapter(A, B, frames);
+  if (e) return e;
+  if (!enc || !out || !workspace) return ARK_E_NULL;
+  if (!aligned(enc, 16) || !aligned(out, 16) || (mid && !aligned(mid, 16)) ||
+      !aligned(workspace, kAlign))
+    return ARK_E_ALIGN;
+  bool compact = false;
+  const AdapterPlan p = adapter_plan(*A, B, frames, &compact);
+  if (workspace_bytes < p.total) return ARK_E_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int n = frames / A->merge, R = B * n, K1 = A->merge * A->frame_dim, I = A->up.n;
+  const int H = A->down.n;
+  // merged rows: row i of sequence b is frames merge*i .. merge*i + merge - 1
+  // of that sequence side by side, i.e. enc + (b * frames + merge * i) *
+  // frame_dim read K1 wide; with frames % merge == 0 (or one sequence) every
+  // row is K1 floats after the one before
+  const float* x = enc;
+  if (compact) {
+    float* m = (float*)(ws + p.merged);
+    if (hipMemcpy2DAsync(m, (size_t)n * K1 * 4, enc, (size_t)frames * A->frame_dim * 4,
+                         (size_t)n * K1 * 4, B, hipMemcpyDeviceToDevice, st) != hipSuccess)
+      return ARK_E_HIP;
+    x = m;
+  }
+  int8_t* codes = (int8_t*)(ws + p.codes);
+  float* y = mid ? mid : (float*)(ws + p.y);
+  double* rs = (double*)(ws + p.rs);
+  int* stw = (int*)(ws + p.stats);
+  const SeqStats sa = {stw, stw + kStatsSetInts, B};
+  const SeqStats sb = {stw + kStatsSetInts, stw, B};
+  float* qs = (float*)(ws + p.qs);
+  int* qz = (int*)(ws + p.qz);
+  void* gsk = ws + p.gsk;
+  HIP_TRY(gemm_skinny_reset(st, gsk));
+  HIP_TRY(launch_seq_stats_init(st, sa.cur));
+  // merged rows: range per sequence, codes, up projection (+ bias)
+  HIP_TRY(launch_row_stats(st, R, K1, n, x, K1, nullptr, 0.0, rs, sa));
+  HIP_TRY(launch_quant_seq(st, R, K1, n, x, K1, nullptr, nullptr, sa.cur, codes, nullptr, qs, qz));
+  Seg up[1] = {seg_of(A->up, y, I)};
+  HIP_TRY(launch_gemm(st, R, K1, codes, qs, qz, n, up, 1, EPI_STORE, nullptr, gsk));
+  // GELU in place with its range, codes, down projection (+ bias)
+  HIP_TRY(launch_gelu_stats(st, R, I, n, y, I, sb));
+  HIP_TRY(launch_quant_seq(st, R, I, n, y, I, nullptr, nullptr, sb.cur, codes, nullptr, qs, qz));
+  Seg dn[1] = {seg_of(A->down, out, H)};
+  HIP_TRY(launch_gemm(st, R, I, codes, qs, qz, n, dn, 1, EPI_STORE, nullptr, gsk));
+  return ARK_OK;
 }
 
 int ark_rope_table(int32_t T, int32_t head_dim, double theta, double* cos_out, double* sin_out,

@@ -210,6 +210,12 @@ hipError_t launch_seq_stats_read(hipStream_t st, const int* set, int n, float* f
 hipError_t launch_row_stats(hipStream_t st, int R, int K, int rows_per_seq, const float* x,
                             int ldx, const float* gain, double eps, double* rs_out,
                             const SeqStats& stats);
+// Adapter activation (k_adapter.hip): y <- GELU(y) in place over R rows of
+// N values (row stride ldy), the per-sequence range of the result folded
+// into S (rows r of sequence r / rows_per_seq; clears S.clr).
+hipError_t launch_gelu_stats(hipStream_t st, int R, int N, int rows_per_seq, float* y, int ldy,
+                             const SeqStats& S);
+
 // Dynamic uint8 quantisation with one (s, z) per sequence from the range in
 // `set`: codes of x (or of h recomputed from x, rs and gain when rs !=
 // nullptr), shifted codes (code - 128) [R][K] and/or plain codes; s_out /

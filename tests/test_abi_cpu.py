@@ -323,3 +323,43 @@ def test_int4_entry_points_error_paths():
     assert lib.ark_lm_head_int4(1, FAKE + 4, 2048, C.byref(W), FAKE, 1000, None) == ark.ARK_E_ALIGN
     Wk = fake_qlinear4(1000, 2000)
     assert lib.ark_lm_head_int4(1, FAKE, 2048, C.byref(Wk), FAKE, 1000, None) == ark.ARK_E_SHAPE
+
+
+def fake_adapter(frame_dim=1280, merge=4, inner=4096, hidden=2048, **over):
+    up = fake_qlinear(inner, merge * frame_dim, bias=True)
+    down = fake_qlinear(hidden, inner, bias=True)
+    a = dict(up=up, down=down, frame_dim=frame_dim, merge=merge)
+    a.update(over)
+    return ark.ArkAdapter(**a)
+
+
+def test_adapter_validation():
+    lib = ark.lib()
+    A = fake_adapter()
+    n16 = lib.ark_adapter_workspace_bytes(C.byref(A), 16, 1500)
+    assert n16 > lib.ark_adapter_workspace_bytes(C.byref(A), 1, 150) > 0
+    # ragged frame counts of several sequences need a compacted copy
+    assert lib.ark_adapter_workspace_bytes(C.byref(A), 2, 150) > lib.ark_adapter_workspace_bytes(C.byref(A), 2, 148)
+    for B, frames in ((0, 150), (65, 150), (1, 3), (64, 4100)):
+        assert lib.ark_adapter_workspace_bytes(C.byref(A), B, frames) == 0, (B, frames)
+    assert lib.ark_adapter_workspace_bytes(None, 1, 150) == 0
+
+    def call(A, B=1, frames=150, enc=FAKE, out=FAKE, mid=None, ws=FAKE, nbytes=None):
+        if nbytes is None:
+            nbytes = lib.ark_adapter_workspace_bytes(C.byref(A), max(B, 1), max(frames, 4)) or (1 << 30)
+        return lib.ark_audio_adapter(C.byref(A), B, frames, enc, out, mid, ws, nbytes, None)
+
+    assert call(A, enc=None) == ark.ARK_E_NULL
+    assert call(A, out=None) == ark.ARK_E_NULL
+    assert call(A, ws=None) == ark.ARK_E_NULL
+    assert call(A, enc=FAKE + 4) == ark.ARK_E_ALIGN
+    assert call(A, mid=FAKE + 8) == ark.ARK_E_ALIGN
+    assert call(A, ws=FAKE + 16) == ark.ARK_E_ALIGN
+    assert call(A, nbytes=1024) == ark.ARK_E_WORKSPACE
+    assert call(A, frames=3) == ark.ARK_E_SHAPE
+    assert call(A, B=0) == ark.ARK_E_SHAPE
+    assert call(fake_adapter(up=fake_qlinear(4096, 5120, bias=False))) == ark.ARK_E_NULL
+    assert call(fake_adapter(up=fake_qlinear(4096, 5000, bias=True))) == ark.ARK_E_SHAPE
+    assert call(fake_adapter(down=fake_qlinear(2048, 4000, bias=True))) == ark.ARK_E_SHAPE
+    assert call(fake_adapter(merge=0)) == ark.ARK_E_SHAPE
+    assert lib.ark_audio_adapter(None, 1, 150, FAKE, FAKE, None, FAKE, 1 << 30, None) == ark.ARK_E_NULL
