@@ -13,7 +13,11 @@ Parity status per function (see each docstring for the passage it follows):
   the 3B adapter are parity unpinned as choices (the functions themselves
   are pinned): the GELU between its layers and its 4096 inner width (the
   pages print neither; the 0.6B parameter count pins the two-layer
-  structure and an inner width of twice the hidden width there).
+  structure and an inner width of twice the hidden width there).  The
+  audio encoder's structure is pinned by its printed parameter count; its
+  readings of what the count cannot see are parity unpinned as choices:
+  20 heads, rotary embedding (theta 10000) on q and k in every layer in
+  addition to the positional table, int8 convolutions, LayerNorm eps 1e-5.
 """
 from .ark import *  # noqa: F401,F403
 from .ark import __all__  # noqa: F401

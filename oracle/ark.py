@@ -13,7 +13,10 @@ Pages cited (by title and section):
   [readme] "ARK-ASR-3B" README: "vLLM" section (<|im_end|> is the stop token).
   [audio8] article "Audio8: eight checkpoints, one broken link, and a 3B
            model with nowhere to ship": "What arkasr actually is" (the
-           frame-merging MLP adapter, its parameter count at 0.6B).
+           frame-merging MLP adapter, the Whisper-style encoder with
+           RoPE-augmented layers, their parameter counts at 0.6B).
+  [clover] article "Inside ARK-ASR-3B's Whisper and Qwen architecture"
+           (a Whisper-style audio encoder with rotary position embeddings).
 
 Numeric conventions of this oracle (readings of what the pages leave open):
   * Tensors between operations are fp32, as in the card's fp32 ONNX graph.
@@ -40,6 +43,9 @@ __all__ = [
     "INT4_BLOCK", "prep_weight_int4", "dequant_weight_int4", "lm_head_int4",
     "int4_size_ratio", "MERGE", "n_encoder_frames", "frame_merge", "gelu",
     "OracleAdapter", "build_adapter", "adapter", "adapter_param_count",
+    "ENC_LN_EPS", "ENC_ROPE_THETA", "encoder_param_count", "layernorm", "conv_out_len",
+    "im2col", "enc_attention", "OracleEncLayer", "OracleEncoder", "build_encoder",
+    "encoder_forward",
 ]
 
 F32 = np.float32
@@ -573,3 +579,158 @@ def adapter(ad: OracleAdapter, frames: np.ndarray) -> np.ndarray:
 def adapter_param_count(frame_dim: int, merge: int, inner: int, hidden: int) -> int:
     """Parameters of the two-layer adapter with biases."""
     return merge * frame_dim * inner + inner + inner * hidden + hidden
+
+
+# ---------------------------------------------------------- audio encoder --
+# [card] "Inference" step 1: the encoder maps log-mel features (128 bins,
+# hop 160, the unpadded clip) to [1, seq, 1280]; "Files": the audio encoder
+# is dynamically quantised int8 with per-channel MatMul weights.  [cook]
+# introduction and [clover]: a Whisper-style audio tower with rotary
+# self-attention.  [audio8] "What arkasr actually is": Whisper-style layers
+# with RoPE, and the audio_encoder.whisper.* tensors hold 636,968,960
+# parameters -- exactly the Whisper large encoder: two width-3 convolutions
+# with biases (128 -> 1280, stride 1; 1280 -> 1280, stride 2), a
+# 1500 x 1280 positional table, 32 pre-LayerNorm layers of self-attention
+# (q, v, o with bias, k without) and a 5120-wide GELU MLP, and a final
+# LayerNorm (encoder_param_count pins it).  Readings: 20 heads of 64; the
+# positional rows are added after the convolutions and rotary embedding
+# (rotate-half, theta 10000, positions 0..F-1) is applied to q and k in
+# every layer; attention is bidirectional (a clip attends to all its
+# frames); scores are q.k / sqrt(64); LayerNorm eps 1e-5; the convolutions
+# are int8 too (the dynamic quantiser's integer convolution: one (s, z) over
+# the layer input, per-output-channel weights, zero padding contributing 0);
+# GELU is the erf form; LayerNorm, rotary embedding, softmax and GELU in
+# float64 rounded once to fp32 (as the decoder's float steps); one (s, z)
+# per sequence at every quantisation point.
+ENC_LN_EPS = 1e-5
+ENC_ROPE_THETA = 10000.0
+
+
+def encoder_param_count(n_mels: int, d: int, layers: int, ffn: int, max_pos: int) -> int:
+    """Parameters of the encoder as built here."""
+    attn = 4 * d * d + 3 * d                  # q, k, v, o; q, v, o biases
+    layer = attn + 2 * 2 * d + (d * ffn + ffn) + (ffn * d + d)
+    convs = (3 * n_mels * d + d) + (3 * d * d + d)
+    return layers * layer + convs + max_pos * d + 2 * d
+
+
+def layernorm(x: np.ndarray, g: np.ndarray, b: np.ndarray, eps: float = ENC_LN_EPS) -> np.ndarray:
+    """(x - mean) / sqrt(var + eps) * g + b over the last axis (population
+    variance), float64 inside, fp32 out."""
+    x64 = np.asarray(x, F32).astype(F64)
+    mu = np.mean(x64, axis=-1, keepdims=True)
+    xc = x64 - mu
+    var = np.mean(xc * xc, axis=-1, keepdims=True)
+    r = 1.0 / np.sqrt(var + F64(eps))
+    return ((xc * r) * np.asarray(g, F32).astype(F64) + np.asarray(b, F32).astype(F64)).astype(F32)
+
+
+def conv_out_len(T: int, stride: int) -> int:
+    """Output length of a width-3 convolution with padding 1."""
+    return (int(T) + 2 - 3) // int(stride) + 1
+
+
+def im2col(x: np.ndarray, stride: int) -> np.ndarray:
+    """Rows of a width-3, padding-1 convolution: x [T][C] -> [T_out][3 C]
+    with element (j, c) of row t = x[t * stride - 1 + j][c] (0 outside)."""
+    x = np.asarray(x, F32)
+    T, C = x.shape
+    To = conv_out_len(T, stride)
+    xp = np.zeros((T + 2, C), F32)
+    xp[1:T + 1] = x
+    rows = np.empty((To, 3 * C), F32)
+    for j in range(3):
+        rows[:, j * C:(j + 1) * C] = xp[j:j + stride * (To - 1) + 1:stride]
+    return rows
+
+
+def enc_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """Bidirectional attention of one clip: q, k, v [F, H, Dh] fp32 (q and k
+    rotated) -> [F, H * Dh]: softmax(q.k / sqrt(Dh)) v over all F frames,
+    float64 inside."""
+    F_, H, Dh = q.shape
+    out = np.empty((F_, H, Dh), F64)
+    scale = 1.0 / np.sqrt(F64(Dh))
+    for h in range(H):
+        sc = (q[:, h, :].astype(F64) @ k[:, h, :].astype(F64).T) * scale
+        m = np.max(sc, axis=1, keepdims=True)
+        e = np.exp(sc - m)
+        out[:, h, :] = (e @ v[:, h, :].astype(F64)) / np.sum(e, axis=1, keepdims=True)
+    return out.reshape(F_, H * Dh).astype(F32)
+
+
+@dataclass
+class OracleEncLayer:
+    ln1: tuple
+    ln2: tuple
+    mats: dict           # name -> (int8 codes, fp32 scales): wq wk wv wo w1 w2
+    bias: dict           # bq bv bo b1 b2
+
+
+@dataclass
+class OracleEncoder:
+    cfg: object
+    conv1: tuple
+    conv1_b: np.ndarray
+    conv2: tuple
+    conv2_b: np.ndarray
+    pos: np.ndarray
+    layers: list
+    lnf: tuple
+    cos: np.ndarray
+    sin: np.ndarray
+
+
+def build_encoder(cfg, synth, layers=None) -> OracleEncoder:
+    """The seeded encoder of `cfg` with int8 per-channel weights; `layers`
+    (optional) limits the stack to those layer indices, in order."""
+    fr = synth.encoder_front(cfg)
+    idx = range(cfg.enc_layers) if layers is None else layers
+    ls = []
+    for l in idx:
+        w = synth.encoder_layer_weights(cfg, l)
+        ls.append(OracleEncLayer((w["ln1_g"], w["ln1_b"]), (w["ln2_g"], w["ln2_b"]),
+                                 {n: prep_weight(w[n]) for n in ("wq", "wk", "wv", "wo", "w1", "w2")},
+                                 {n: w[n] for n in ("bq", "bv", "bo", "b1", "b2")}))
+    cos, sin = rope_tables(cfg.enc_max_pos, cfg.enc_dim // cfg.enc_heads, ENC_ROPE_THETA)
+    return OracleEncoder(cfg, prep_weight(fr["conv1"]), fr["conv1_b"], prep_weight(fr["conv2"]),
+                         fr["conv2_b"], fr["pos"], ls, (fr["lnf_g"], fr["lnf_b"]), cos, sin)
+
+
+def _enc_linear(x, mat, bias=None):
+    c, s, z = dynquant(x)
+    return qlinear(c, s, z, mat[0], mat[1], bias)
+
+
+def encoder_forward(enc: OracleEncoder, mel: np.ndarray, trace=None) -> np.ndarray:
+    """mel [B][M][n_mels] fp32 -> [B][F][d], F = conv_out_len(M, 2), one clip
+    at a time (one (s, z) per clip and quantisation point)."""
+    cfg = enc.cfg
+    H = cfg.enc_heads
+    Dh = cfg.enc_dim // H
+    out = []
+    for b in range(mel.shape[0]):
+        a = gelu(_enc_linear(im2col(mel[b], 1), enc.conv1, enc.conv1_b))
+        x = gelu(_enc_linear(im2col(a, 2), enc.conv2, enc.conv2_b))
+        F_ = x.shape[0]
+        assert F_ <= enc.pos.shape[0]
+        x = (x + enc.pos[:F_]).astype(F32)
+        pos = np.arange(F_)
+        for li, L in enumerate(enc.layers):
+            h = layernorm(x, *L.ln1)
+            c, s, z = dynquant(h)
+            q = qlinear(c, s, z, *L.mats["wq"], L.bias["bq"]).reshape(F_, H, Dh)
+            k = qlinear(c, s, z, *L.mats["wk"]).reshape(F_, H, Dh)
+            v = qlinear(c, s, z, *L.mats["wv"], L.bias["bv"]).reshape(F_, H, Dh)
+            qr = apply_rope(q, pos, enc.cos, enc.sin)
+            kr = apply_rope(k, pos, enc.cos, enc.sin)
+            att = enc_attention(qr, kr, v)
+            x = (x + _enc_linear(att, L.mats["wo"], L.bias["bo"])).astype(F32)
+            h2 = layernorm(x, *L.ln2)
+            f = gelu(_enc_linear(h2, L.mats["w1"], L.bias["b1"]))
+            x = (x + _enc_linear(f, L.mats["w2"], L.bias["b2"])).astype(F32)
+            if trace is not None:
+                trace.append({"seq": b, "layer": li, "h1": h, "q": qr, "k": kr, "v": v,
+                              "attn": att, "h2": h2, "f": f, "x": x})
+        out.append(layernorm(x, *enc.lnf))
+    return np.stack(out)

@@ -23,10 +23,15 @@ Distributions:
   * token ids                   uniform over the unmasked vocabulary
   * adapter weights, biases     N(0, 0.02) fp32 ([out][in] row-major)
   * encoder frames              N(0, 1) fp32 [B][frames][frame_dim]
+  * audio encoder weights       N(0, 0.02) fp32 (LayerNorm gains 1 + N(0, 0.02),
+                                LayerNorm biases and positional rows N(0, 0.02))
+  * log-mel features            N(0, 1) fp32 [B][mel_frames][n_mels]
 
 Adapter geometry: frames of width 1280 (the encoder output of the model
 card's "Inference" step 1), 4 frames per merged row (step 2), an inner width
 of 4096; encoder frame counts 150 and 1500 for the 3 s and 30 s clips.
+Audio encoder geometry: 128 mel bins, width 1280, 20 heads, FFN 5120, 32
+layers, 1500 positions; 300 and 3000 mel frames for the 3 s and 30 s clips.
 """
 from __future__ import annotations
 
@@ -46,6 +51,9 @@ TAG_PROMPT_IDS, TAG_AUDIO, TAG_PREFILL_EMBEDS = 16, 17, 18
 TAG_DECODE_IDS, TAG_CACHE_LEN, TAG_CACHE_K, TAG_CACHE_V = 19, 20, 21, 22
 TAG_START_IDS = 23
 TAG_AD_W1, TAG_AD_B1, TAG_AD_W2, TAG_AD_B2, TAG_FRAMES = 24, 25, 26, 27, 28
+TAG_ENC_W = 40            # + index of the tensor within a layer (see ENC_LAYER_TENSORS)
+TAG_ENC_FRONT = 60        # + index within ENC_FRONT_TENSORS
+TAG_MEL = 70
 
 ROW_CHUNK = 2048          # rows per independent random stream of a big matrix
 WEIGHT_STD = 0.02
@@ -92,6 +100,13 @@ class ArkConfig:
     merge: int = 4               # frames per merged adapter row
     adapter_inner: int = 4096    # adapter's inner width
     enc_frames: int = 0          # encoder frames per sequence (0: no adapter input)
+    n_mels: int = 128            # audio encoder input bins
+    enc_dim: int = 1280          # audio encoder width
+    enc_heads: int = 20
+    enc_ffn: int = 5120
+    enc_layers: int = 32
+    enc_max_pos: int = 1500      # rows of the encoder's positional table
+    mel_frames: int = 0          # log-mel frames per sequence (0: no encoder input)
 
     # Added-vocab convention: ids [vocab - n_added, vocab) are the "<...>"
     # added tokens; the first of them is the end token, which stays unmasked.
@@ -139,16 +154,18 @@ CONFIGS = {
                     n_added=0, decode_ids_fixed=True),
     # 3 s clip: 2 + 37 + 10 prompt rows, 32 greedy steps.
     "c1": ArkConfig(name="c1", seed=1001, prefill_len=2 + _N3S + 10, n_decode=32,
-                    audio_slots=_N3S, enc_frames=_F3S),
+                    audio_slots=_N3S, enc_frames=_F3S, mel_frames=2 * _F3S),
     # 30 s clip: 2 + 375 + 10 prompt rows, greedy until the 512 cache is full.
     "c2": ArkConfig(name="c2", seed=1002, prefill_len=2 + _N30S + 10,
-                    n_decode=512 - (2 + _N30S + 10), audio_slots=_N30S, enc_frames=_F30S),
+                    n_decode=512 - (2 + _N30S + 10), audio_slots=_N30S, enc_frames=_F30S,
+                    mel_frames=2 * _F30S),
     # 32 independent sequences with pre-filled caches, 64 lockstep steps.
     "c3": ArkConfig(name="c3", seed=1003, batch=32, prefill_len=0, n_decode=64,
                     cache_fill=(50, 400)),
     # Coalesced prefill of 16 x 387 N(0,1) rows, then 16 decode steps.
     "c4": ArkConfig(name="c4", seed=1004, batch=16, prefill_len=2 + _N30S + 10,
-                    n_decode=16, prefill_from_embeds=True, enc_frames=_F30S),
+                    n_decode=16, prefill_from_embeds=True, enc_frames=_F30S,
+                    mel_frames=2 * _F30S),
     "c4_t1024": ArkConfig(name="c4_t1024", seed=1004, batch=16,
                           prefill_len=2 + _N30S + 10, n_decode=16,
                           prefill_from_embeds=True, max_total_len=1024),
@@ -160,11 +177,15 @@ CONFIGS = {
 TINY = ArkConfig(name="tiny", seed=7, n_layers=2, hidden=64, n_heads=4, n_kv_heads=2,
                  head_dim=16, intermediate=96, vocab=50, max_total_len=16,
                  prefill_len=5, n_decode=4, n_added=8, audio_slots=2,
-                 frame_dim=8, adapter_inner=24, enc_frames=10)
+                 frame_dim=8, adapter_inner=24, enc_frames=10,
+                 n_mels=4, enc_dim=8, enc_heads=2, enc_ffn=16, enc_layers=2, enc_max_pos=16,
+                 mel_frames=19)
 SMALL = ArkConfig(name="small", seed=11, n_layers=2, hidden=512, n_heads=4,
                   n_kv_heads=2, head_dim=128, intermediate=1344, vocab=3000,
                   max_total_len=64, prefill_len=21, n_decode=6, n_added=64,
-                  audio_slots=9, frame_dim=320, adapter_inner=1024, enc_frames=39)
+                  audio_slots=9, frame_dim=320, adapter_inner=1024, enc_frames=39,
+                  n_mels=32, enc_dim=320, enc_heads=5, enc_ffn=640, enc_layers=2,
+                  enc_max_pos=128, mel_frames=77)
 
 
 # ---------------------------------------------------------------- weights --
@@ -265,7 +286,54 @@ def adapter_weights(cfg: ArkConfig) -> dict:
     }
 
 
+ENC_LAYER_TENSORS = ("ln1_g", "ln1_b", "wq", "bq", "wk", "wv", "bv", "wo", "bo",
+                     "ln2_g", "ln2_b", "w1", "b1", "w2", "b2")
+ENC_FRONT_TENSORS = ("conv1", "conv1_b", "conv2", "conv2_b", "pos", "lnf_g", "lnf_b")
+
+
+def encoder_layer_weights(cfg: ArkConfig, layer: int) -> dict:
+    """fp32 weights of one audio encoder layer ([out][in] row-major; the
+    key projection has no bias)."""
+    D, F = cfg.enc_dim, cfg.enc_ffn
+    s = WEIGHT_STD
+    shapes = {"wq": (D, D), "wk": (D, D), "wv": (D, D), "wo": (D, D), "w1": (F, D), "w2": (D, F)}
+    out = {}
+    for i, name in enumerate(ENC_LAYER_TENSORS):
+        tag = TAG_ENC_W + i
+        if name in shapes:
+            out[name] = _normal_rows(cfg, tag, layer, *shapes[name], s)
+        elif name.endswith("_g"):
+            out[name] = _normal_vec(cfg, tag, layer, D, s, 1.0)
+        else:
+            out[name] = _normal_vec(cfg, tag, layer, F if name == "b1" else D, s)
+    return out
+
+
+def encoder_front(cfg: ArkConfig) -> dict:
+    """fp32 convolution weights [out][3][in] (tap-major: element (j, c) of an
+    output row is tap j of input channel c), their biases, the positional
+    table [max_pos][D] and the final LayerNorm."""
+    D, M = cfg.enc_dim, cfg.n_mels
+    s = WEIGHT_STD
+    t = {n: TAG_ENC_FRONT + i for i, n in enumerate(ENC_FRONT_TENSORS)}
+    return {
+        "conv1": _normal_rows(cfg, t["conv1"], 0, D, 3 * M, s),
+        "conv1_b": _normal_vec(cfg, t["conv1_b"], 0, D, s),
+        "conv2": _normal_rows(cfg, t["conv2"], 0, D, 3 * D, s),
+        "conv2_b": _normal_vec(cfg, t["conv2_b"], 0, D, s),
+        "pos": _normal_rows(cfg, t["pos"], 0, cfg.enc_max_pos, D, s),
+        "lnf_g": _normal_vec(cfg, t["lnf_g"], 0, D, s, 1.0),
+        "lnf_b": _normal_vec(cfg, t["lnf_b"], 0, D, s),
+    }
+
+
 # ------------------------------------------------------------------ inputs --
+def mel_features(cfg: ArkConfig, frames: int | None = None) -> np.ndarray:
+    """[B, mel_frames, n_mels] fp32 N(0, 1) stand-ins for log-mel features."""
+    n = cfg.mel_frames if frames is None else int(frames)
+    return _rng(cfg.seed, TAG_MEL, n, 0).standard_normal((cfg.batch, n, cfg.n_mels), dtype=np.float32)
+
+
 def encoder_frames(cfg: ArkConfig, frames: int | None = None) -> np.ndarray:
     """[B, frames, frame_dim] fp32 N(0, 1) stand-ins for the encoder output."""
     n = cfg.enc_frames if frames is None else int(frames)
