@@ -216,12 +216,73 @@ size_t ark_adapter_workspace_bytes(const ark_adapter* A, int32_t B, int32_t fram
  * ark_embed_splice writes into the <|audio|> slots; mid (optional, NULL:
  * not written) [B][n][inner] fp32, the GELU output that the second
  * quantisation sees.  1 <= B <= 64; up.k == merge * frame_dim, up.n ==
- * down.k, both with a bias, k % 16 == 0; pointers 16-byte aligned,
+ * down.k, both with a bias, k % 64 == 0; pointers 16-byte aligned,
  * workspace 256-byte aligned.  Errors: ARK_E_NULL, ARK_E_SHAPE,
  * ARK_E_WORKSPACE, ARK_E_ALIGN, ARK_E_HIP. */
 int ark_audio_adapter(const ark_adapter* A, int32_t B, int32_t frames, const float* enc,
                       float* out, float* mid, void* workspace, size_t workspace_bytes,
                       void* stream);
+
+/* ------------------------------------------------------ audio encoder -- */
+
+/* The Whisper-style audio encoder in front of the adapter (model card
+ * "ark-asr-3b-onnx", "Inference" step 1: log-mel features to [1, seq, 1280];
+ * "Files": dynamically quantised int8 with per-channel MatMul weights;
+ * cookbook "ARK-ASR-3B" introduction: a Whisper-style tower with rotary
+ * self-attention; Audio8 article, "What arkasr actually is": 636,968,960
+ * parameters, the Whisper large encoder's count).  Per clip:
+ *   a = GELU(conv1(mel))            width 3, stride 1, padding 1, + bias
+ *   x = GELU(conv2(a)) + pos[t]     width 3, stride 2, padding 1, + bias
+ *   32 x: x += o(attn(rope(q), rope(k), v))   of LayerNorm1(x)
+ *         x += fc2(GELU(fc1(LayerNorm2(x))))
+ *   out = LayerNorm_f(x)
+ * Readings (the pages fix the structure by its parameter count, not these):
+ * 20 heads of 64; q, v, o, fc1, fc2 and the convolutions carry biases, k
+ * does not; rotary embedding (rotate-half, pairs (d, d + 32), the tables
+ * of ark_rope_table(max_pos, 64, theta)) on q and k at positions 0..F-1 in
+ * every layer, in addition to the positional rows; attention is
+ * bidirectional with scores q.k / 8; every MatMul and both convolutions
+ * are int8 with one (s, z) per clip and quantisation point (the
+ * convolutions as GEMMs over tap-major im2col rows); LayerNorm, rotary
+ * embedding, softmax and GELU (erf form) compute in fp64 and round once to
+ * fp32.  Convolution weights are stored tap-major: conv1 is [d][3 n_mels]
+ * with element (j, c) = tap j of input channel c (a transpose of the usual
+ * [d][n_mels][3]), conv2 [d][3 d] likewise. */
+typedef struct {
+  const float* ln1_g;
+  const float* ln1_b;
+  const float* ln2_g;
+  const float* ln2_b;
+  ark_qlinear q, k, v, o;   /* [d][d]; k without bias */
+  ark_qlinear fc1;          /* [ffn][d] */
+  ark_qlinear fc2;          /* [d][ffn] */
+} ark_enc_layer;
+
+typedef struct {
+  int32_t n_mels, d_model, n_heads, ffn, n_layers, max_pos;
+  double ln_eps;               /* LayerNorm epsilon (1e-5) */
+  ark_qlinear conv1;           /* [d][3 n_mels], bias [d] */
+  ark_qlinear conv2;           /* [d][3 d], bias [d] */
+  const float* pos;            /* [max_pos][d] positional rows */
+  const ark_enc_layer* layers; /* [host] n_layers entries */
+  const float* lnf_g;          /* [d] final LayerNorm */
+  const float* lnf_b;
+  const double* rope_cos;      /* [max_pos][32] from ark_rope_table(max_pos, 64, theta) */
+  const double* rope_sin;
+} ark_encoder;
+
+/* Workspace bytes of ark_audio_encoder for B clips of M mel frames each; 0
+ * if the arguments are invalid. */
+size_t ark_encoder_workspace_bytes(const ark_encoder* E, int32_t B, int32_t mel_frames);
+
+/* Encoder frames of B clips: mel [B][M][n_mels] fp32 (time-major log-mel
+ * features); out [B][F][d_model] fp32 with F = (M - 1) / 2 + 1 <= max_pos
+ * (the adapter's input).  Supported: d_model == 64 n_heads, n_mels % 64 ==
+ * 0, ffn % 64 == 0, 1 <= B <= 64, B * M <= 2^24;
+ * pointers 16-byte aligned, workspace 256-byte aligned.  Errors:
+ * ARK_E_NULL, ARK_E_SHAPE, ARK_E_WORKSPACE, ARK_E_ALIGN, ARK_E_HIP. */
+int ark_audio_encoder(const ark_encoder* E, int32_t B, int32_t mel_frames, const float* mel,
+                      float* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* --------------------------------------------------------------- a1 ---- */
 
@@ -365,6 +426,25 @@ int ark_greedy_decode(const ark_model* m, int32_t B, int32_t* token_ids,
  * scale [B] fp32, zp [B] int32.  B <= 64.  workspace >=
  * ark_test_dynquant_workspace_bytes() bytes.  Errors: ARK_E_NULL,
  * ARK_E_SHAPE, ARK_E_WORKSPACE. */
+/* The audio encoder's LayerNorm on B sequences of S rows of D values
+ * (fp64 inside, one rounding): y [B][S][D] and each sequence's (min, max)
+ * of y in lo[B], hi[B] (the range its dynamic quantisation takes).
+ * workspace >= ark_test_dynquant_workspace_bytes().  Errors: ARK_E_NULL,
+ * ARK_E_SHAPE, ARK_E_WORKSPACE, ARK_E_HIP. */
+int ark_test_layernorm(int32_t B, int32_t S, int32_t D, const float* x, const float* g,
+                       const float* b, double eps, float* y, float* lo, float* hi,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* The audio encoder's rotary bidirectional self-attention on B clips of F
+ * frames and H heads of 64: qkv [B][F][3 H 64] (q | k | v rows as the
+ * projections write them), rotary tables [>= F][32] fp64; out [B][F][H 64]
+ * and each clip's (min, max) of out in lo[B], hi[B].  workspace >=
+ * ark_test_dynquant_workspace_bytes().  Errors: ARK_E_NULL, ARK_E_SHAPE,
+ * ARK_E_WORKSPACE, ARK_E_HIP. */
+int ark_test_enc_attention(int32_t B, int32_t F, int32_t H, const float* qkv,
+                           const double* rope_cos, const double* rope_sin, float* out, float* lo,
+                           float* hi, void* workspace, size_t workspace_bytes, void* stream);
+
 size_t ark_test_dynquant_workspace_bytes(void);
 int ark_test_dynquant(int32_t B, int32_t R, int32_t K, const float* x, uint8_t* codes,
                       float* scale, int32_t* zp, void* workspace, size_t workspace_bytes,

@@ -52,6 +52,20 @@ class ArkAdapter(C.Structure):
                 ("merge", C.c_int32)]
 
 
+class ArkEncLayer(C.Structure):
+    _fields_ = [("ln1_g", C.c_void_p), ("ln1_b", C.c_void_p), ("ln2_g", C.c_void_p),
+                ("ln2_b", C.c_void_p), ("q", ArkQLinear), ("k", ArkQLinear), ("v", ArkQLinear),
+                ("o", ArkQLinear), ("fc1", ArkQLinear), ("fc2", ArkQLinear)]
+
+
+class ArkEncoder(C.Structure):
+    _fields_ = [("n_mels", C.c_int32), ("d_model", C.c_int32), ("n_heads", C.c_int32),
+                ("ffn", C.c_int32), ("n_layers", C.c_int32), ("max_pos", C.c_int32),
+                ("ln_eps", C.c_double), ("conv1", ArkQLinear), ("conv2", ArkQLinear),
+                ("pos", C.c_void_p), ("layers", C.POINTER(ArkEncLayer)), ("lnf_g", C.c_void_p),
+                ("lnf_b", C.c_void_p), ("rope_cos", C.c_void_p), ("rope_sin", C.c_void_p)]
+
+
 class ArkLayer(C.Structure):
     _fields_ = [("ln1", C.c_void_p), ("ln2", C.c_void_p), ("q", ArkQLinear), ("k", ArkQLinear),
                 ("v", ArkQLinear), ("o", ArkQLinear), ("gate", ArkQLinear), ("up", ArkQLinear),
@@ -77,6 +91,8 @@ _SIGS = {
     "ark_rope_table": (C.c_int, [I32, I32, C.c_double, P, P, P]),
     "ark_prep_weight_int4": (C.c_int, [P, I32, I32, P, P, P, P]),
     "ark_adapter_workspace_bytes": (C.c_size_t, [C.POINTER(ArkAdapter), I32, I32]),
+    "ark_encoder_workspace_bytes": (C.c_size_t, [C.POINTER(ArkEncoder), I32, I32]),
+    "ark_audio_encoder": (C.c_int, [C.POINTER(ArkEncoder), I32, I32, P, P, P, C.c_size_t, P]),
     "ark_audio_adapter": (C.c_int, [C.POINTER(ArkAdapter), I32, I32, P, P, P, P, C.c_size_t, P]),
     "ark_lm_head_int4": (C.c_int, [I32, P, I32, C.POINTER(ArkQLinear4), P, I32, P]),
     "ark_embed_splice": (C.c_int, [C.POINTER(ArkDims), I32, I32, P, P, P, I32, I32, P, P]),
@@ -93,6 +109,8 @@ _SIGS = {
     "ark_test_qlinear": (C.c_int, [I32, I32, P, P, P, C.POINTER(ArkQLinear), P, P, I32, P,
                                    C.c_size_t, P]),
     "ark_test_dynquant_workspace_bytes": (C.c_size_t, []),
+    "ark_test_layernorm": (C.c_int, [I32, I32, I32, P, P, P, C.c_double, P, P, P, P, C.c_size_t, P]),
+    "ark_test_enc_attention": (C.c_int, [I32, I32, I32, P, P, P, P, P, P, P, C.c_size_t, P]),
     "ark_test_swiglu": (C.c_int, [C.c_int64, P, P, P, P]),
     "ark_test_gate_up_workspace_bytes": (C.c_size_t, [I32, I32, I32]),
     "ark_test_gate_up": (C.c_int, [I32, I32, P, P, P, C.POINTER(ArkQLinear), C.POINTER(ArkQLinear),
@@ -411,6 +429,66 @@ def audio_adapter(ad: DeviceAdapter, enc, out, mid=None, ws=None, stream=None):
         _stream(stream)))
 
 
+# ------------------------------------------------------------ the encoder --
+class DeviceEncoder:
+    """The prepared audio encoder on the GPU and its ark_encoder struct."""
+
+    def __init__(self, cfg, conv1, conv2, pos, layers, lnf, rope):
+        self.cfg = cfg
+        self.conv1, self.conv2, self.pos, self.layers, self.lnf = conv1, conv2, pos, layers, lnf
+        self.rope_cos, self.rope_sin = rope
+        self._arr = (ArkEncLayer * len(layers))()
+        for i, L in enumerate(layers):
+            self._arr[i] = ArkEncLayer(_ptr(L["ln1_g"]), _ptr(L["ln1_b"]), _ptr(L["ln2_g"]),
+                                       _ptr(L["ln2_b"]), L["q"].c(), L["k"].c(), L["v"].c(),
+                                       L["o"].c(), L["fc1"].c(), L["fc2"].c())
+        self.c = ArkEncoder(cfg.n_mels, cfg.enc_dim, cfg.enc_heads, cfg.enc_ffn, len(layers),
+                            cfg.enc_max_pos, cfg.enc_ln_eps, conv1.c(), conv2.c(), _ptr(pos), self._arr,
+                            _ptr(lnf[0]), _ptr(lnf[1]), _ptr(self.rope_cos), _ptr(self.rope_sin))
+
+    def workspace(self, B: int, mel_frames: int):
+        import torch
+        n = lib().ark_encoder_workspace_bytes(C.byref(self.c), B, mel_frames)
+        if n == 0:
+            raise ArkError("ark_encoder_workspace_bytes", ARK_E_SHAPE, "invalid encoder call")
+        return torch.empty(n, dtype=torch.uint8, device="cuda")
+
+
+def load_encoder(cfg, synth, device="cuda", stream=None, layers=None) -> DeviceEncoder:
+    """The seeded fp32 encoder weights of `cfg` (convolutions tap-major),
+    prepared on the GPU layer by layer; `layers` limits the stack."""
+    import torch
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    fr = synth.encoder_front(cfg)
+    conv1 = QLinear.from_f32(up(fr["conv1"]), up(fr["conv1_b"]), stream)
+    conv2 = QLinear.from_f32(up(fr["conv2"]), up(fr["conv2_b"]), stream)
+    out = []
+    for l in (range(cfg.enc_layers) if layers is None else layers):
+        w = synth.encoder_layer_weights(cfg, l)
+        L = {n: up(w[n]) for n in ("ln1_g", "ln1_b", "ln2_g", "ln2_b")}
+        for name, key, bias in (("q", "wq", "bq"), ("k", "wk", None), ("v", "wv", "bv"),
+                                ("o", "wo", "bo"), ("fc1", "w1", "b1"), ("fc2", "w2", "b2")):
+            L[name] = QLinear.from_f32(up(w[key]), up(w[bias]) if bias else None, stream)
+        out.append(L)
+        del w
+    rope = rope_table(cfg.enc_max_pos, cfg.enc_dim // cfg.enc_heads, cfg.enc_rope_theta, device, stream)
+    enc = DeviceEncoder(cfg, conv1, conv2, up(fr["pos"]), out, (up(fr["lnf_g"]), up(fr["lnf_b"])),
+                        rope)
+    torch.cuda.current_stream().synchronize()
+    return enc
+
+
+def audio_encoder(enc: DeviceEncoder, mel, out, ws=None, stream=None):
+    """mel [B][M][n_mels] -> out [B][(M - 1) // 2 + 1][d] (ark_audio_encoder)."""
+    B, M = mel.shape[0], mel.shape[1]
+    if ws is None:
+        ws = enc.workspace(B, M)
+    _check("ark_audio_encoder", lib().ark_audio_encoder(
+        C.byref(enc.c), B, M, _ptr(mel), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
 # ------------------------------------------------------------- the path --
 def workspace(model: DeviceModel, B: int, S: int):
     import torch
@@ -610,6 +688,39 @@ def test_qlinear(codes, scale, zp, W: QLinear, use_gemm, stream=None):
                                                        _ptr(acc), _ptr(y), int(use_gemm), _ptr(ws),
                                                        ws.numel(), _stream(stream)))
     return acc, y
+
+
+def _stats_ws():
+    import torch
+    return torch.empty(lib().ark_test_dynquant_workspace_bytes(), dtype=torch.uint8, device="cuda")
+
+
+def test_layernorm(x, g, b, eps, stream=None):
+    """x [B][S][D] -> (y [B][S][D], lo [B], hi [B]) (ark_test_layernorm)."""
+    import torch
+    B, S, D = x.shape
+    y = torch.empty_like(x)
+    lo = torch.empty(B, dtype=torch.float32, device=x.device)
+    hi = torch.empty_like(lo)
+    ws = _stats_ws()
+    _check("ark_test_layernorm", lib().ark_test_layernorm(B, S, D, _ptr(x), _ptr(g), _ptr(b), eps,
+                                                           _ptr(y), _ptr(lo), _ptr(hi), _ptr(ws),
+                                                           ws.numel(), _stream(stream)))
+    return y, lo, hi
+
+
+def test_enc_attention(qkv, H, cos, sin, stream=None):
+    """qkv [B][F][3 H 64] -> (out [B][F][H 64], lo [B], hi [B])."""
+    import torch
+    B, F = qkv.shape[0], qkv.shape[1]
+    out = torch.empty((B, F, H * 64), dtype=torch.float32, device=qkv.device)
+    lo = torch.empty(B, dtype=torch.float32, device=qkv.device)
+    hi = torch.empty_like(lo)
+    ws = _stats_ws()
+    _check("ark_test_enc_attention", lib().ark_test_enc_attention(
+        B, F, H, _ptr(qkv), _ptr(cos), _ptr(sin), _ptr(out), _ptr(lo), _ptr(hi), _ptr(ws),
+        ws.numel(), _stream(stream)))
+    return out, lo, hi
 
 
 def test_swiglu(g, u, stream=None):

@@ -644,7 +644,69 @@ int check_adapter(const ark_adapter* A, int B, int frames) {
   if ((e = check_qlinear(A->up, A->up.n, K1, true))) return e;
   if ((e = check_qlinear(A->down, A->down.n, A->up.n, true))) return e;
   if (!A->up.bias || !A->down.bias) return ARK_E_NULL;
-  if (A->up.n < 1 || A->down.n < 1 || K1 % 16 || A->up.n % 16) return ARK_E_SHAPE;
+  // both GEMMs take K in whole 64-byte steps
+  if (A->up.n < 1 || A->down.n < 1 || K1 % 64 || A->up.n % 64) return ARK_E_SHAPE;
+  return ARK_OK;
+}
+
+// ---- audio encoder
+struct EncoderPlan {
+  size_t cols, a1, x, h, qkv, attn, f, codes, rs, stats, qs, qz, gsk, total;
+};
+
+EncoderPlan encoder_plan(const ark_encoder& E, int B, int M) {
+  const size_t F = (size_t)(M - 1) / 2 + 1, R1 = (size_t)B * M, R = (size_t)B * F;
+  const size_t D = E.d_model, C = E.n_mels, FF = E.ffn;
+  EncoderPlan p;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align_up(bytes);
+    return at;
+  };
+  p.cols = take(std::max(R1 * 3 * C, R * 3 * D) * 4);
+  p.a1 = take(R1 * D * 4);
+  p.x = take(R * D * 4);
+  p.h = take(R * D * 4);
+  p.qkv = take(R * 3 * D * 4);
+  p.attn = take(R * D * 4);
+  p.f = take(R * FF * 4);
+  p.codes = take(std::max(std::max(R1 * 3 * C, R * 3 * D), R * std::max(FF, D)));
+  p.rs = take(std::max(R1, R) * 8);
+  p.stats = take(2 * (size_t)kStatsSetInts * 4);
+  p.qs = take((size_t)kMaxBatch * 4);
+  p.qz = take((size_t)kMaxBatch * 4);
+  p.gsk = take(gemm_skinny_ws_bytes());
+  p.total = o;
+  return p;
+}
+
+int check_encoder(const ark_encoder* E, int B, int M) {
+  if (!E) return ARK_E_NULL;
+  const int D = E->d_model, C = E->n_mels, FF = E->ffn;
+  if (B < 1 || B > kMaxBatch || M < 1 || (int64_t)B * M > (1 << 24)) return ARK_E_SHAPE;
+  // every GEMM here takes K in whole 64-byte steps: 3 n_mels, 3 d, d, ffn
+  if (E->n_heads < 1 || D != 64 * E->n_heads || C < 64 || C % 64 || FF < 64 || FF % 64 ||
+      E->n_layers < 1 || E->max_pos < 1 || !(E->ln_eps >= 0.0))
+    return ARK_E_SHAPE;
+  if ((M - 1) / 2 + 1 > E->max_pos) return ARK_E_SHAPE;
+  if (!E->pos || !E->layers || !E->lnf_g || !E->lnf_b || !E->rope_cos || !E->rope_sin)
+    return ARK_E_NULL;
+  int e;
+  if ((e = check_qlinear(E->conv1, D, 3 * C, true))) return e;
+  if ((e = check_qlinear(E->conv2, D, 3 * D, true))) return e;
+  if (!E->conv1.bias || !E->conv2.bias) return ARK_E_NULL;
+  for (int l = 0; l < E->n_layers; ++l) {
+    const ark_enc_layer& L = E->layers[l];
+    if (!L.ln1_g || !L.ln1_b || !L.ln2_g || !L.ln2_b) return ARK_E_NULL;
+    if ((e = check_qlinear(L.q, D, D, true))) return e;
+    if ((e = check_qlinear(L.k, D, D, false))) return e;
+    if ((e = check_qlinear(L.v, D, D, true))) return e;
+    if ((e = check_qlinear(L.o, D, D, true))) return e;
+    if ((e = check_qlinear(L.fc1, FF, D, true))) return e;
+    if ((e = check_qlinear(L.fc2, D, FF, true))) return e;
+    if (!L.q.bias || !L.v.bias || !L.o.bias || !L.fc1.bias || !L.fc2.bias) return ARK_E_NULL;
+  }
   return ARK_OK;
 }
 
@@ -840,6 +902,85 @@ int ark_audio_adapter(const ark_adapter* A, int32_t B, int32_t frames, const flo
   HIP_TRY(launch_quant_seq(st, R, I, n, y, I, nullptr, nullptr, sb.cur, codes, nullptr, qs, qz));
   Seg dn[1] = {seg_of(A->down, out, H)};
   HIP_TRY(launch_gemm(st, R, I, codes, qs, qz, n, dn, 1, EPI_STORE, nullptr, gsk));
+  return ARK_OK;
+}
+
+size_t ark_encoder_workspace_bytes(const ark_encoder* E, int32_t B, int32_t mel_frames) {
+  if (check_encoder(E, B, mel_frames) != ARK_OK) return 0;
+  return encoder_plan(*E, B, mel_frames).total;
+}
+
+int ark_audio_encoder(const ark_encoder* E, int32_t B, int32_t mel_frames, const float* mel,
+                      float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  int e = check_encoder(E, B, mel_frames);
+  if (e) return e;
+  if (!mel || !out || !workspace) return ARK_E_NULL;
+  if (!aligned(mel, 16) || !aligned(out, 16) || !aligned(workspace, kAlign)) return ARK_E_ALIGN;
+  const EncoderPlan p = encoder_plan(*E, B, mel_frames);
+  if (workspace_bytes < p.total) return ARK_E_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int M = mel_frames, F = (M - 1) / 2 + 1, R1 = B * M, R = B * F;
+  const int D = E->d_model, C = E->n_mels, FF = E->ffn, H = E->n_heads;
+  float* cols = (float*)(ws + p.cols);
+  float* a1 = (float*)(ws + p.a1);
+  float* x = (float*)(ws + p.x);
+  float* h = (float*)(ws + p.h);
+  float* qkv = (float*)(ws + p.qkv);
+  float* attn = (float*)(ws + p.attn);
+  float* f = (float*)(ws + p.f);
+  int8_t* codes = (int8_t*)(ws + p.codes);
+  double* rs = (double*)(ws + p.rs);
+  int* stw = (int*)(ws + p.stats);
+  const SeqStats sa = {stw, stw + kStatsSetInts, B};
+  const SeqStats sb = {stw + kStatsSetInts, stw, B};
+  const SeqStats none = {nullptr, nullptr, B};
+  float* qs = (float*)(ws + p.qs);
+  int* qz = (int*)(ws + p.qz);
+  void* gsk = ws + p.gsk;
+  HIP_TRY(gemm_skinny_reset(st, gsk));
+  HIP_TRY(launch_seq_stats_init(st, sa.cur));
+  // conv1: tap-major rows of the mel frames, their range and codes per clip,
+  // the int8 GEMM (+ bias), GELU with its range (for conv2's codes)
+  HIP_TRY(launch_im2col(st, B, M, C, 1, mel, cols));
+  HIP_TRY(launch_row_stats(st, R1, 3 * C, M, cols, 3 * C, nullptr, 0.0, rs, sa));
+  HIP_TRY(launch_quant_seq(st, R1, 3 * C, M, cols, 3 * C, nullptr, nullptr, sa.cur, codes, nullptr,
+                           qs, qz));
+  Seg c1[1] = {seg_of(E->conv1, a1, D)};
+  HIP_TRY(launch_gemm(st, R1, 3 * C, codes, qs, qz, M, c1, 1, EPI_STORE, nullptr, gsk));
+  HIP_TRY(launch_gelu_stats(st, R1, D, M, a1, D, sb));
+  // conv2 (stride 2): its rows hold the GELU values (and zero padding), so
+  // the GELU's range is theirs; GELU, then the positional rows
+  HIP_TRY(launch_im2col(st, B, M, D, 2, a1, cols));
+  HIP_TRY(launch_quant_seq(st, R, 3 * D, F, cols, 3 * D, nullptr, nullptr, sb.cur, codes, nullptr,
+                           qs, qz));
+  Seg c2[1] = {seg_of(E->conv2, x, D)};
+  HIP_TRY(launch_gemm(st, R, 3 * D, codes, qs, qz, F, c2, 1, EPI_STORE, nullptr, gsk));
+  HIP_TRY(launch_gelu_stats(st, R, D, F, x, D, none, E->pos, D));
+  // the layers; ranges alternate between the two sets (each producer clears
+  // the other for the producer after it)
+  for (int l = 0; l < E->n_layers; ++l) {
+    const ark_enc_layer& L = E->layers[l];
+    HIP_TRY(launch_layernorm(st, R, D, F, x, L.ln1_g, L.ln1_b, E->ln_eps, h, sa));
+    HIP_TRY(launch_quant_seq(st, R, D, F, h, D, nullptr, nullptr, sa.cur, codes, nullptr, qs, qz));
+    Seg qkvs[3] = {seg_of(L.q, qkv, 3 * D), seg_of(L.k, qkv + D, 3 * D),
+                   seg_of(L.v, qkv + 2 * D, 3 * D)};
+    HIP_TRY(launch_gemm(st, R, D, codes, qs, qz, F, qkvs, 3, EPI_STORE, nullptr, gsk));
+    HIP_TRY(launch_enc_attention(st, B, F, H, qkv, E->rope_cos, E->rope_sin, attn, sb));
+    HIP_TRY(launch_quant_seq(st, R, D, F, attn, D, nullptr, nullptr, sb.cur, codes, nullptr, qs,
+                             qz));
+    Seg os[1] = {seg_of(L.o, x, D)};
+    HIP_TRY(launch_gemm(st, R, D, codes, qs, qz, F, os, 1, EPI_RESID, nullptr, gsk));
+    HIP_TRY(launch_layernorm(st, R, D, F, x, L.ln2_g, L.ln2_b, E->ln_eps, h, sa));
+    HIP_TRY(launch_quant_seq(st, R, D, F, h, D, nullptr, nullptr, sa.cur, codes, nullptr, qs, qz));
+    Seg f1[1] = {seg_of(L.fc1, f, FF)};
+    HIP_TRY(launch_gemm(st, R, D, codes, qs, qz, F, f1, 1, EPI_STORE, nullptr, gsk));
+    HIP_TRY(launch_gelu_stats(st, R, FF, F, f, FF, sb));
+    HIP_TRY(launch_quant_seq(st, R, FF, F, f, FF, nullptr, nullptr, sb.cur, codes, nullptr, qs, qz));
+    Seg f2[1] = {seg_of(L.fc2, x, D)};
+    HIP_TRY(launch_gemm(st, R, FF, codes, qs, qz, F, f2, 1, EPI_RESID, nullptr, gsk));
+  }
+  HIP_TRY(launch_layernorm(st, R, D, F, x, E->lnf_g, E->lnf_b, E->ln_eps, out, none));
   return ARK_OK;
 }
 
@@ -1077,6 +1218,37 @@ int ark_test_dynquant(int32_t B, int32_t R, int32_t K, const float* x, uint8_t* 
   if (launch_quant_seq(st, B * R, K, R, x, K, nullptr, nullptr, sa.cur, nullptr, codes, scale,
                        zp) != hipSuccess)
     return ARK_E_HIP;
+  return ARK_OK;
+}
+
+int ark_test_layernorm(int32_t B, int32_t S, int32_t D, const float* x, const float* g,
+                       const float* b, double eps, float* y, float* lo, float* hi,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x || !g || !b || !y || !lo || !hi || !workspace) return ARK_E_NULL;
+  if (B < 1 || B > kMaxBatch || S < 1 || D < 1 || !(eps >= 0.0)) return ARK_E_SHAPE;
+  if (workspace_bytes < ark_test_dynquant_workspace_bytes()) return ARK_E_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  int* stw = (int*)workspace;
+  const SeqStats sa = {stw, stw + kStatsSetInts, B};
+  HIP_TRY(launch_seq_stats_init(st, sa.cur));
+  HIP_TRY(launch_layernorm(st, B * S, D, S, x, g, b, eps, y, sa));
+  HIP_TRY(launch_seq_stats_read(st, sa.cur, B, lo, hi));
+  return ARK_OK;
+}
+
+int ark_test_enc_attention(int32_t B, int32_t F, int32_t H, const float* qkv,
+                           const double* rope_cos, const double* rope_sin, float* out, float* lo,
+                           float* hi, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!qkv || !rope_cos || !rope_sin || !out || !lo || !hi || !workspace) return ARK_E_NULL;
+  if (B < 1 || B > kMaxBatch || F < 1 || H < 1) return ARK_E_SHAPE;
+  if (!aligned(qkv, 16)) return ARK_E_ALIGN;
+  if (workspace_bytes < ark_test_dynquant_workspace_bytes()) return ARK_E_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  int* stw = (int*)workspace;
+  const SeqStats sa = {stw, stw + kStatsSetInts, B};
+  HIP_TRY(launch_seq_stats_init(st, sa.cur));
+  HIP_TRY(launch_enc_attention(st, B, F, H, qkv, rope_cos, rope_sin, out, sa));
+  HIP_TRY(launch_seq_stats_read(st, sa.cur, B, lo, hi));
   return ARK_OK;
 }
 

@@ -1,0 +1,284 @@
+// Kernels of the Whisper-style audio encoder (model card "ark-asr-3b-onnx",
+// "Inference" step 1 and "Files"; cookbook "ARK-ASR-3B" introduction: a
+// Whisper-style audio tower with rotary self-attention; Audio8 article,
+// "What arkasr actually is": the encoder's parameter count, which fixes the
+// Whisper large structure).  The int8 projections and convolutions run on
+// the library's GEMMs; this file holds the pieces around them:
+//   * im2col of the width-3 convolutions (tap-major rows),
+//   * LayerNorm in fp64 with the per-sequence range of its output,
+//   * bidirectional rotary self-attention on fp64 matrix cores.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ark {
+
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
+// ---- im2col: one thread per 4 floats of an output row
+__global__ __launch_bounds__(256) void k_im2col(int B, int T, int C, int To, int stride,
+                                                const float* __restrict__ x,
+                                                float* __restrict__ rows) {
+  const int C4 = C / 4;
+  const long n = (long)B * To * 3 * C4;
+  for (long e = (long)blockIdx.x * 256 + threadIdx.x; e < n; e += (long)gridDim.x * 256) {
+    const int c4 = (int)(e % C4);
+    const long rest = e / C4;
+    const int j = (int)(rest % 3);
+    const long bt = rest / 3;
+    const int t = (int)(bt % To), b = (int)(bt / To);
+    const int src = t * stride - 1 + j;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (src >= 0 && src < T) v = ((const float4*)(x + ((size_t)b * T + src) * C))[c4];
+    ((float4*)(rows + (size_t)bt * 3 * C + (size_t)j * C))[c4] = v;
+  }
+}
+
+hipError_t launch_im2col(hipStream_t st, int B, int T, int C, int stride, const float* x,
+                         float* rows) {
+  const int To = (T - 1) / stride + 1;
+  const long n = (long)B * To * 3 * (C / 4);
+  const int grid = (int)std::min<long>(16384, (n + 255) / 256);
+  hipLaunchKernelGGL(k_im2col, dim3(grid), dim3(256), 0, st, B, T, C, To, stride, x, rows);
+  return hipGetLastError();
+}
+
+// ---- LayerNorm: one wave per row, four rows per workgroup
+__global__ __launch_bounds__(256) void k_layernorm(int R, int D, int rows_per_seq,
+                                                   const float* __restrict__ x,
+                                                   const float* __restrict__ g,
+                                                   const float* __restrict__ bb, double eps,
+                                                   float* __restrict__ y, SeqStats S) {
+  const bool stats = S.cur != nullptr;
+  if (stats) stats_clear_other(S);
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= R) return;
+  const float* xr = x + (size_t)row * D;
+  double s = 0.0;
+  for (int i = lane; i < D; i += 64) s += (double)xr[i];
+  const double mu = wave_sum(s) / (double)D;
+  double v = 0.0;
+  for (int i = lane; i < D; i += 64) {
+    const double c = (double)xr[i] - mu;
+    v += c * c;
+  }
+  const double r = 1.0 / sqrt(wave_sum(v) / (double)D + eps);
+  float lo = INFINITY, hi = -INFINITY;
+  float* yr = y + (size_t)row * D;
+  for (int i = lane; i < D; i += 64) {
+    const float o = (float)((((double)xr[i] - mu) * r) * (double)g[i] + (double)bb[i]);
+    yr[i] = o;
+    lo = fminf(lo, o);
+    hi = fmaxf(hi, o);
+  }
+  if (stats) {
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    if (lane == 0) stats_fold(S, row, row / rows_per_seq, lo, hi);
+  }
+}
+
+hipError_t launch_layernorm(hipStream_t st, int R, int D, int rows_per_seq, const float* x,
+                            const float* g, const float* b, double eps, float* y,
+                            const SeqStats& S) {
+  hipLaunchKernelGGL(k_layernorm, dim3((R + 3) / 4), dim3(256), 0, st, R, D, rows_per_seq, x, g, b,
+                     eps, y, S);
+  return hipGetLastError();
+}
+
+// ---- bidirectional rotary self-attention on fp64 matrix cores
+//
+// One workgroup = one (clip b, head h, group of 8 query tiles of 16 rows),
+// one wave per query tile; each 64-key chunk of K (rotated) and V is staged
+// in LDS once for the 8 waves.  A wave forms S^T = K Q^T in 16x16 blocks
+// (v_mfma_f64_16x16x4f64: lane l supplies A[l % 16][l / 16] and
+// B[l / 16][l % 16]; the result holds C[4 i + l / 16][l % 16] in register
+// i), the online softmax per query row, and O^T += V^T P^T with P^T taken
+// straight from the score registers (register i of score block kb is the B
+// operand the lane supplies for keys 4 t .. 4 t + 3, t = 4 kb + i).
+// Keys past the clip's F frames score -inf (no other mask: every frame sees
+// every frame).  Rotary pairs are (d, d + 32); q and k are rotated in fp64
+// and rounded to fp32 (the tensors the method's rotary step produces), then
+// widened for the products.
+namespace ea {
+constexpr int DH = 64;    // head dim
+constexpr int KC = 64;    // keys per chunk
+constexpr int KP = 68;    // K row pitch (floats): 16 keys x 4 dims of a fragment read hit distinct banks
+constexpr int VP = 80;    // V row pitch (floats): 4 keys x 16 dims hit distinct banks
+constexpr int QT = 16;    // query rows per wave
+constexpr int NW = 8;     // waves (query tiles) per workgroup
+}  // namespace ea
+
+struct EncAttnParams {
+  int B, F, H, ngrp;
+  const float* qkv;
+  const double* cos;
+  const double* sin;
+  float* out;
+  SeqStats stats;
+};
+
+__global__ __launch_bounds__(512) void k_enc_attn(EncAttnParams P) {
+  using namespace ea;
+  __shared__ __align__(16) float Ks[KC * KP];
+  __shared__ __align__(16) float Vs[KC * VP];
+  if (P.stats.cur) stats_clear_other(P.stats);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = blockIdx.x % P.ngrp;
+  const int bh = blockIdx.x / P.ngrp;
+  const int b = bh / P.H, h = bh % P.H;
+  const int F = P.F, W3 = 3 * P.H * DH;
+  const int c16 = lane & 15, q4 = lane >> 4;
+  const int qrow = (grp * NW + wave) * QT + c16;
+  const bool rowok = qrow < F;
+  const float* base = P.qkv + (size_t)b * F * W3;
+
+  // this lane's query dims 4 s + q4, s = 0..15, rotated: dim d < 32 pairs
+  // with d + 32, held at s + 8
+  double qv[16];
+  {
+    const int qr = min(qrow, F - 1);
+    const float* src = base + (size_t)qr * W3 + h * DH;
+    float qf[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) qf[s] = src[4 * s + q4];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int d = 4 * s + q4;
+      const double c = P.cos[(size_t)qr * (DH / 2) + d], sn = P.sin[(size_t)qr * (DH / 2) + d];
+      const double a = qf[s], bq = qf[s + 8];
+      const float ra = (float)(a * c - bq * sn), rb = (float)(bq * c + a * sn);
+      qv[s] = rowok ? (double)ra : 0.0;
+      qv[s + 8] = rowok ? (double)rb : 0.0;
+    }
+  }
+  f64x4_t o[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) o[d] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+  double m = -INFINITY, l = 0.0;
+  const double scale = 0.125;  // 1 / sqrt(64), exact
+  const SwigluK EK = swiglu_consts();
+
+  const int nch = (F + KC - 1) / KC;
+  for (int c = 0; c < nch; ++c) {
+    const int j0 = c * KC;
+    __syncthreads();  // the previous chunk's K and V are used
+    {
+      // 64 keys x 8 pairs of float4 (dims 4 p .. 4 p + 3 with their
+      // partners 32 on): one item per thread
+      const int jj = tid >> 3, p4 = tid & 7;
+      const int j = j0 + jj;
+      float4 ka = make_float4(0.f, 0.f, 0.f, 0.f), kb = ka, va = ka, vb = ka;
+      if (j < F) {
+        const float* kr = base + (size_t)j * W3 + P.H * DH + h * DH;
+        const float* vr = kr + P.H * DH;
+        const float4 k0 = ((const float4*)kr)[p4], k1 = ((const float4*)kr)[p4 + 8];
+        va = ((const float4*)vr)[p4];
+        vb = ((const float4*)vr)[p4 + 8];
+        const double* cr = P.cos + (size_t)j * (DH / 2) + 4 * p4;
+        const double* sr = P.sin + (size_t)j * (DH / 2) + 4 * p4;
+        const float a[4] = {k0.x, k0.y, k0.z, k0.w}, bq[4] = {k1.x, k1.y, k1.z, k1.w};
+        float ra[4], rb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const double cc = cr[e], ss = sr[e];
+          ra[e] = (float)((double)a[e] * cc - (double)bq[e] * ss);
+          rb[e] = (float)((double)bq[e] * cc + (double)a[e] * ss);
+        }
+        ka = make_float4(ra[0], ra[1], ra[2], ra[3]);
+        kb = make_float4(rb[0], rb[1], rb[2], rb[3]);
+      }
+      *(float4*)(Ks + jj * KP + 4 * p4) = ka;
+      *(float4*)(Ks + jj * KP + 4 * p4 + 32) = kb;
+      *(float4*)(Vs + jj * VP + 4 * p4) = va;
+      *(float4*)(Vs + jj * VP + 4 * p4 + 32) = vb;
+    }
+    __syncthreads();
+
+    f64x4_t sc[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      sc[kb] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+      const float* kr = Ks + (16 * kb + c16) * KP + q4;
+#pragma unroll
+      for (int s = 0; s < 16; ++s)
+        sc[kb] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kr[4 * s], qv[s], sc[kb], 0, 0, 0);
+    }
+    double cmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = j0 + 16 * kb + 4 * i + q4;
+        const double v = (rowok && j < F) ? sc[kb][i] * scale : -INFINITY;
+        sc[kb][i] = v;
+        cmax = fmax(cmax, v);
+      }
+    cmax = fmax(cmax, __shfl_xor(cmax, 16, kWave));
+    cmax = fmax(cmax, __shfl_xor(cmax, 32, kWave));
+    const double mnew = fmax(m, cmax);
+    const double alpha = (m == -INFINITY) ? 0.0 : exp_nonpos_f64(m - mnew, EK);
+    double lsum = 0.0;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const double e = (sc[kb][i] == -INFINITY) ? 0.0 : exp_nonpos_f64(sc[kb][i] - mnew, EK);
+        lsum += e;
+        sc[kb][i] = e;
+      }
+    lsum += __shfl_xor(lsum, 16, kWave);
+    lsum += __shfl_xor(lsum, 32, kWave);
+    l = l * alpha + lsum;
+    m = mnew;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) o[d] *= alpha;
+#pragma unroll
+    for (int t = 0; t < KC / 4; ++t) {
+      const double pb = sc[t >> 2][t & 3];
+      const float* vr = Vs + (4 * t + q4) * VP + c16;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        o[d] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)vr[16 * d], pb, o[d], 0, 0, 0);
+    }
+  }
+  // o[d][i] = O^T[dim 16 d + 4 i + q4][qrow]
+  float lo = INFINITY, hi = -INFINITY;
+  if (rowok) {
+    float* dst = P.out + ((size_t)b * F + qrow) * (P.H * DH) + h * DH;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float y = (float)(o[d][i] / l);
+        dst[16 * d + 4 * i + q4] = y;
+        lo = fminf(lo, y);
+        hi = fmaxf(hi, y);
+      }
+  }
+  if (P.stats.cur) {
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    if (lane == 0) stats_fold(P.stats, blockIdx.x * NW + wave, b, lo, hi);
+  }
+}
+
+hipError_t launch_enc_attention(hipStream_t st, int B, int F, int H, const float* qkv,
+                                const double* cos, const double* sin, float* out,
+                                const SeqStats& S) {
+  EncAttnParams P = {};
+  P.B = B;
+  P.F = F;
+  P.H = H;
+  const int nqt = (F + ea::QT - 1) / ea::QT;
+  P.ngrp = (nqt + ea::NW - 1) / ea::NW;
+  P.qkv = qkv;
+  P.cos = cos;
+  P.sin = sin;
+  P.out = out;
+  P.stats = S;
+  hipLaunchKernelGGL(k_enc_attn, dim3(B * H * P.ngrp), dim3(64 * ea::NW), 0, st, P);
+  return hipGetLastError();
+}
+
+}  // namespace ark

@@ -210,11 +210,32 @@ hipError_t launch_seq_stats_read(hipStream_t st, const int* set, int n, float* f
 hipError_t launch_row_stats(hipStream_t st, int R, int K, int rows_per_seq, const float* x,
                             int ldx, const float* gain, double eps, double* rs_out,
                             const SeqStats& stats);
-// Adapter activation (k_adapter.hip): y <- GELU(y) in place over R rows of
-// N values (row stride ldy), the per-sequence range of the result folded
-// into S (rows r of sequence r / rows_per_seq; clears S.clr).
+// GELU (k_adapter.hip): y <- GELU(y) in place over R rows of N values (row
+// stride ldy), plus row r % rows_per_seq of `add` when add != nullptr; the
+// per-sequence range of the result folded into S (rows r of sequence
+// r / rows_per_seq; clears S.clr) when S.cur != nullptr.
 hipError_t launch_gelu_stats(hipStream_t st, int R, int N, int rows_per_seq, float* y, int ldy,
-                             const SeqStats& S);
+                             const SeqStats& S, const float* add = nullptr, int ldadd = 0);
+
+// Audio encoder (k_encoder.hip).
+// im2col of a width-3, padding-1 convolution: x [B][T][C] -> rows
+// [B][To][3 C] with element (j, c) of row t = x[b][t * stride - 1 + j][c]
+// (0 outside); C % 4 == 0.
+hipError_t launch_im2col(hipStream_t st, int B, int T, int C, int stride, const float* x,
+                         float* rows);
+// LayerNorm of R rows of D values (fp64 inside, one rounding):
+// y = fp32(((x - mean) / sqrt(var + eps)) * g + b); per-sequence range of y
+// into S when S.cur != nullptr.
+hipError_t launch_layernorm(hipStream_t st, int R, int D, int rows_per_seq, const float* x,
+                            const float* g, const float* b, double eps, float* y,
+                            const SeqStats& S);
+// Bidirectional self-attention of B clips of F frames, H heads of 64: qkv
+// rows [B][F][3 H 64] (q | k | v), q and k rotated (fp64 tables
+// [>= F][32]) and rounded to fp32 before use, softmax(q.k / 8) v in fp64;
+// out [B][F][H 64] and its per-sequence range into S (S.cur != nullptr).
+hipError_t launch_enc_attention(hipStream_t st, int B, int F, int H, const float* qkv,
+                                const double* cos, const double* sin, float* out,
+                                const SeqStats& S);
 
 // Dynamic uint8 quantisation with one (s, z) per sequence from the range in
 // `set`: codes of x (or of h recomputed from x, rs and gain when rs !=

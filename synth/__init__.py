@@ -107,6 +107,8 @@ class ArkConfig:
     enc_layers: int = 32
     enc_max_pos: int = 1500      # rows of the encoder's positional table
     mel_frames: int = 0          # log-mel frames per sequence (0: no encoder input)
+    enc_ln_eps: float = 1e-5     # encoder LayerNorm epsilon
+    enc_rope_theta: float = 1e4  # encoder rotary base
 
     # Added-vocab convention: ids [vocab - n_added, vocab) are the "<...>"
     # added tokens; the first of them is the end token, which stays unmasked.
@@ -184,7 +186,7 @@ SMALL = ArkConfig(name="small", seed=11, n_layers=2, hidden=512, n_heads=4,
                   n_kv_heads=2, head_dim=128, intermediate=1344, vocab=3000,
                   max_total_len=64, prefill_len=21, n_decode=6, n_added=64,
                   audio_slots=9, frame_dim=320, adapter_inner=1024, enc_frames=39,
-                  n_mels=32, enc_dim=320, enc_heads=5, enc_ffn=640, enc_layers=2,
+                  n_mels=64, enc_dim=320, enc_heads=5, enc_ffn=640, enc_layers=2,
                   enc_max_pos=128, mel_frames=77)
 
 

@@ -363,3 +363,62 @@ def test_adapter_validation():
     assert call(fake_adapter(down=fake_qlinear(2048, 4000, bias=True))) == ark.ARK_E_SHAPE
     assert call(fake_adapter(merge=0)) == ark.ARK_E_SHAPE
     assert lib.ark_audio_adapter(None, 1, 150, FAKE, FAKE, None, FAKE, 1 << 30, None) == ark.ARK_E_NULL
+
+
+def test_adapter_rejects_partial_k_steps():
+    lib = ark.lib()
+    A = fake_adapter(frame_dim=1288, up=fake_qlinear(4096, 5152, bias=True))
+    assert lib.ark_adapter_workspace_bytes(C.byref(A), 1, 150) == 0
+    A2 = fake_adapter(inner=4064)
+    assert lib.ark_adapter_workspace_bytes(C.byref(A2), 1, 150) == 0
+
+
+def fake_encoder(L=2, d=1280, heads=20, n_mels=128, ffn=5120, max_pos=1500, **over):
+    layers = (ark.ArkEncLayer * L)()
+    for i in range(L):
+        layers[i] = ark.ArkEncLayer(FAKE, FAKE, FAKE, FAKE, fake_qlinear(d, d, True),
+                                    fake_qlinear(d, d, False), fake_qlinear(d, d, True),
+                                    fake_qlinear(d, d, True), fake_qlinear(ffn, d, True),
+                                    fake_qlinear(d, ffn, True))
+    a = dict(n_mels=n_mels, d_model=d, n_heads=heads, ffn=ffn, n_layers=L, max_pos=max_pos,
+             ln_eps=1e-5, conv1=fake_qlinear(d, 3 * n_mels, True), conv2=fake_qlinear(d, 3 * d, True),
+             pos=FAKE, layers=layers, lnf_g=FAKE, lnf_b=FAKE, rope_cos=FAKE, rope_sin=FAKE)
+    a.update(over)
+    E = ark.ArkEncoder(**a)
+    E._keep = layers
+    return E
+
+
+def test_encoder_validation():
+    lib = ark.lib()
+    E = fake_encoder()
+    assert lib.ark_encoder_workspace_bytes(C.byref(E), 16, 3000) > lib.ark_encoder_workspace_bytes(C.byref(E), 1, 300) > 0
+    for B, M in ((0, 300), (65, 300), (1, 0), (1, 3001)):     # 3001 frames -> 1501 > max_pos
+        assert lib.ark_encoder_workspace_bytes(C.byref(E), B, M) == 0, (B, M)
+    bad = [dict(n_heads=16), dict(n_mels=96, conv1=fake_qlinear(1280, 288, True)),
+           dict(ffn=5000), dict(conv2=fake_qlinear(1280, 3000, True))]
+    for kw in bad:
+        assert lib.ark_encoder_workspace_bytes(C.byref(fake_encoder(**kw)), 1, 300) == 0, kw
+    assert lib.ark_encoder_workspace_bytes(C.byref(fake_encoder(pos=None)), 1, 300) == 0
+
+    def call(E, B=1, M=300, mel=FAKE, out=FAKE, ws=FAKE, nbytes=None):
+        if nbytes is None:
+            nbytes = lib.ark_encoder_workspace_bytes(C.byref(E), max(B, 1), max(M, 1)) or (1 << 40)
+        return lib.ark_audio_encoder(C.byref(E), B, M, mel, out, ws, nbytes, None)
+
+    assert call(E, mel=None) == ark.ARK_E_NULL
+    assert call(E, out=None) == ark.ARK_E_NULL
+    assert call(E, mel=FAKE + 4) == ark.ARK_E_ALIGN
+    assert call(E, ws=FAKE + 16) == ark.ARK_E_ALIGN
+    assert call(E, nbytes=4096) == ark.ARK_E_WORKSPACE
+    assert call(E, M=0) == ark.ARK_E_SHAPE
+    E2 = fake_encoder()
+    E2._keep[1].k = fake_qlinear(1280, 1280, True)                # the key projection has no bias
+    assert call(E2) == ark.ARK_E_SHAPE
+    E3 = fake_encoder()
+    E3._keep[0].fc1 = fake_qlinear(5120, 1280, False)             # fc1 needs its bias
+    assert call(E3) == ark.ARK_E_NULL
+    E4 = fake_encoder()
+    E4._keep[0].ln2_b = None
+    assert call(E4) == ark.ARK_E_NULL
+    assert lib.ark_audio_encoder(None, 1, 300, FAKE, FAKE, FAKE, 1 << 40, None) == ark.ARK_E_NULL

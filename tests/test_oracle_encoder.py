@@ -45,6 +45,11 @@ def test_structure_from_the_printed_parameter_count():
     assert hits == [(32, 5120, False, True, True)]
 
 
+def test_workload_settings_match_the_oracle_readings():
+    for cfg in (synth.CONFIGS["c1"], synth.TINY, synth.SMALL):
+        assert cfg.enc_ln_eps == oracle.ENC_LN_EPS and cfg.enc_rope_theta == oracle.ENC_ROPE_THETA
+
+
 def test_frame_counts():
     # 3 s and 30 s clips: samples // 160 mel frames, stride-2 second conv
     for samples, frames in ((48000, 150), (480000, 1500)):
