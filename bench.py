@@ -322,6 +322,8 @@ def gpu_bench(args):
             del fr, rows, aws
         del ad
         torch.cuda.empty_cache()
+        # the audio encoder (3 s clip; sixteen 30 s clips)
+        ex.update(encoder_bench(torch, ark, synth, cfg))
         # prompt prefill of the 3 s clip
         t = timed(torch, lambda: run.prefill(x, [0]), reps=5)
         ex["prefill_c1_tok_s"] = round(S / t, 1)
@@ -386,6 +388,53 @@ def gpu_bench(args):
         result["extras"] = ex
         log(f"extras: {ex}")
     return result
+
+
+def encoder_ops(cfg, B: int, M: int) -> int:
+    """int8 multiply-add ops (2 per MAC) of the audio encoder on B clips of M
+    mel frames: the two convolutions and every layer's projections."""
+    D, FF, L, C = cfg.enc_dim, cfg.enc_ffn, cfg.enc_layers, cfg.n_mels
+    F = (M - 1) // 2 + 1
+    return 2 * B * (M * 3 * C * D + F * 3 * D * D + L * F * (4 * D * D + 2 * D * FF))
+
+
+def encoder_attn_flops(cfg, B: int, M: int) -> int:
+    """fp64 flops of the encoder's attention products (QK^T and PV)."""
+    F = (M - 1) // 2 + 1
+    return 2 * 2 * B * cfg.enc_layers * cfg.enc_heads * F * F * (cfg.enc_dim // cfg.enc_heads)
+
+
+def encoder_bench(torch, ark, synth, cfg, reps=2):
+    """The audio encoder on the 3 s clip and on sixteen 30 s clips."""
+    enc = ark.load_encoder(cfg, synth)
+    ex = {}
+    for name, B, M in (("c1", 1, cfg.mel_frames), ("c4", 16, synth.CONFIGS["c4"].mel_frames)):
+        F = (M - 1) // 2 + 1
+        mel = torch.randn((B, M, cfg.n_mels), device="cuda")
+        out = torch.empty((B, F, cfg.enc_dim), device="cuda")
+        ws = enc.workspace(B, M)
+        ark.audio_encoder(enc, mel, out, ws=ws)
+        t = timed(torch, lambda: ark.audio_encoder(enc, mel, out, ws=ws), reps=reps)
+        ex[f"encoder_{name}_ms"] = round(t * 1e3, 3)
+        ex[f"encoder_{name}_clips"] = B
+        ex[f"encoder_{name}_int8_frac_of_5POPS"] = round(encoder_ops(cfg, B, M) / t / PEAK_INT8, 4)
+        ex[f"encoder_{name}_attn_fp64_tflop"] = round(encoder_attn_flops(cfg, B, M) / 1e12, 3)
+        del mel, out, ws
+    del enc
+    torch.cuda.empty_cache()
+    return ex
+
+
+def encoder_probe() -> None:
+    """Only the audio encoder workloads (for profiler runs)."""
+    import torch
+
+    import synth
+    from speech_decoder_int8_amd import ark
+    ark.lib()
+    torch.cuda.set_device(0)
+    ex = encoder_bench(torch, ark, synth, synth.CONFIGS["c1"], reps=1)
+    log(f"encoder: {ex}")
 
 
 def prefill_probe() -> None:
@@ -513,6 +562,8 @@ def main():
                          "kernel of known size, to scale the HBM byte counters)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only run the 16x387 prefill twice and exit (for counter passes)")
+    ap.add_argument("--encoder-only", action="store_true",
+                    help="only run the audio encoder workloads and exit (for profiler runs)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -527,6 +578,9 @@ def main():
         return
     if args.prefill_only:
         prefill_probe()
+        return
+    if args.encoder_only:
+        encoder_probe()
         return
     result = gpu_bench(args)
     result["cpu_baseline"] = cpu_baseline(args.cpu_layers) if args.cpu else None
