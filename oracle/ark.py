@@ -17,6 +17,8 @@ Pages cited (by title and section):
            RoPE-augmented layers, their parameter counts at 0.6B).
   [clover] article "Inside ARK-ASR-3B's Whisper and Qwen architecture"
            (a Whisper-style audio encoder with rotary position embeddings).
+  [cook]   also "dtype": the default serving dtype is bfloat16 (the
+           bf16-activation decoder variant at the end of this file).
 
 Numeric conventions of this oracle (readings of what the pages leave open):
   * Tensors between operations are fp32, as in the card's fp32 ONNX graph.
@@ -45,7 +47,9 @@ __all__ = [
     "OracleAdapter", "build_adapter", "adapter", "adapter_param_count",
     "ENC_LN_EPS", "ENC_ROPE_THETA", "encoder_param_count", "layernorm", "conv_out_len",
     "im2col", "enc_attention", "OracleEncLayer", "OracleEncoder", "build_encoder",
-    "encoder_forward",
+    "encoder_forward", "bf16_round", "Bf16Layer", "Bf16Model", "build_bf16_model",
+    "bf16_rmsnorm", "bf16_linear", "bf16_layer_forward", "bf16_forward", "bf16_prefill",
+    "bf16_decode_step",
 ]
 
 F32 = np.float32
@@ -734,3 +738,156 @@ def encoder_forward(enc: OracleEncoder, mel: np.ndarray, trace=None) -> np.ndarr
                               "attn": att, "h2": h2, "f": f, "x": x})
         out.append(layernorm(x, *enc.lnf))
     return np.stack(out)
+
+
+# ------------------------------------------------ bf16 serving variant --
+# [cook] "dtype": the model is served in bfloat16 by default (the validated
+# path); [clover] runs it the same way.  This variant is the decoder of the
+# functions above with the checkpoint's weights and every activation in
+# bf16 instead of int8 MatMuls over fp32 tensors: weights, biases, gains and
+# the embedding table rounded to bf16, the KV cache in bf16 (half the bytes
+# of the fp32 cache).  Reading of where values are rounded (each operation
+# of the bf16 model rounds its output to bf16 once; the operations compute
+# in float64 inside, with exact bf16 x bf16 products):
+#   RMSNorm      bf16(g * bf16(x / sqrt(mean(x^2) + eps)))
+#   linear       bf16(sum_k x w + b)
+#   rotary step  bf16 of the rotated pair (the fp64 tables of rope_tables)
+#   attention    bf16(softmax(q.k / sqrt(D)) v)
+#   residual add bf16(x + y)
+#   MLP gate     bf16(bf16(silu(g)) * u)
+#   LM head      fp32(sum_k h w) (the logits stay fp32: rounding them to bf16
+#                would make the greedy choice a tie far more often)
+BF16_MASK = np.uint32(0xFFFF0000)
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Nearest bfloat16 of fp32 values (ties to even), returned as fp32
+    holding the bf16 value; NaN stays NaN, +-inf stays +-inf."""
+    x = np.asarray(x, F32)
+    b = x.view(np.uint32).astype(np.uint64)
+    lsb = (b >> np.uint64(16)) & np.uint64(1)
+    r = ((b + np.uint64(0x7FFF) + lsb) & np.uint64(0xFFFF0000)).astype(np.uint32)
+    out = r.view(F32).copy()
+    nan = np.isnan(x)
+    out[nan] = x[nan]
+    return out.reshape(x.shape)
+
+
+@dataclass
+class Bf16Layer:
+    ln1: np.ndarray
+    ln2: np.ndarray
+    w: dict              # name -> bf16-valued fp32 [n][k]: wq wk wv wo wg wu wd
+    bq: np.ndarray
+    bk: np.ndarray
+    bv: np.ndarray
+
+
+@dataclass
+class Bf16Model:
+    cfg: object
+    layers: list
+    final_norm: np.ndarray | None = None
+    lm_head: np.ndarray | None = None
+    embed: np.ndarray | None = None      # bf16-valued fp32 [V][H]
+    cos: np.ndarray | None = None
+    sin: np.ndarray | None = None
+    round: object = None                 # the rounding function (bf16_round; identity in tests)
+
+
+def build_bf16_model(cfg, synth, layers=None, with_embed=True, rounding=None) -> Bf16Model:
+    """The seeded fp32 weights of `cfg` rounded to bf16 (`rounding` replaces
+    bf16_round everywhere, for tests)."""
+    rnd = bf16_round if rounding is None else rounding
+    idx = range(cfg.n_layers) if layers is None else layers
+    out = []
+    for l in idx:
+        w = synth.layer_weights(cfg, l)
+        out.append(Bf16Layer(rnd(w["ln1"]), rnd(w["ln2"]),
+                             {n: rnd(w[n]) for n in ("wq", "wk", "wv", "wo", "wg", "wu", "wd")},
+                             rnd(w["bq"]), rnd(w["bk"]), rnd(w["bv"])))
+    m = Bf16Model(cfg=cfg, layers=out, round=rnd)
+    if cfg.lm_head:
+        m.final_norm = rnd(synth.final_norm(cfg))
+        m.lm_head = rnd(synth.lm_head(cfg))
+    if with_embed:
+        m.embed = rnd(synth.embed_table_f16(cfg).astype(F32))
+    m.cos, m.sin = rope_tables(cfg.max_total_len, cfg.head_dim, cfg.rope_theta)
+    return m
+
+
+def bf16_rmsnorm(m: Bf16Model, x: np.ndarray, g: np.ndarray) -> np.ndarray:
+    x64 = np.asarray(x, F32).astype(F64)
+    r = 1.0 / np.sqrt(np.mean(x64 * x64, axis=-1, keepdims=True) + F64(m.cfg.rms_eps))
+    y = m.round((x64 * r).astype(F32))
+    return m.round((y.astype(F64) * np.asarray(g, F32).astype(F64)).astype(F32))
+
+
+def bf16_linear(m: Bf16Model, x: np.ndarray, w: np.ndarray, bias=None) -> np.ndarray:
+    y = np.asarray(x, F32).astype(F64) @ np.asarray(w, F32).astype(F64).T
+    if bias is not None:
+        y = y + np.asarray(bias, F32).astype(F64)
+    return m.round(y.astype(F32))
+
+
+def bf16_layer_forward(m: Bf16Model, l: int, x: np.ndarray, p: np.ndarray,
+                       k_cache: np.ndarray, v_cache: np.ndarray, trace: dict | None = None):
+    """One layer over B sequences of S rows (the wiring of layer_forward):
+    x [B, S, H] bf16-valued, caches [B, T, NKV, D] bf16-valued (read only).
+    Returns (x_out, k_delta, v_delta)."""
+    cfg = m.cfg
+    lay = m.layers[l]
+    B, S, H = x.shape
+    NH, NKV, D = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
+    h1 = bf16_rmsnorm(m, x, lay.ln1)
+    q = bf16_linear(m, h1, lay.w["wq"], lay.bq).reshape(B, S, NH, D)
+    k = bf16_linear(m, h1, lay.w["wk"], lay.bk).reshape(B, S, NKV, D)
+    v = bf16_linear(m, h1, lay.w["wv"], lay.bv).reshape(B, S, NKV, D)
+    pos = (np.asarray(p)[:, None] + np.arange(S)[None, :]).astype(np.int64)
+    q = m.round(apply_rope(q, pos, m.cos, m.sin))
+    k = m.round(apply_rope(k, pos, m.cos, m.sin))
+    attn = np.empty((B, S, NH * D), F32)
+    for b in range(B):
+        kh = cache_write(k_cache[b:b + 1], k[b:b + 1], p[b:b + 1])[0]
+        vh = cache_write(v_cache[b:b + 1], v[b:b + 1], p[b:b + 1])[0]
+        attn[b] = m.round(attention(q[b], kh, vh, int(p[b])))
+    o = bf16_linear(m, attn, lay.w["wo"])
+    x1 = m.round((x.astype(F64) + o.astype(F64)).astype(F32))
+    h2 = bf16_rmsnorm(m, x1, lay.ln2)
+    g = bf16_linear(m, h2, lay.w["wg"])
+    u = bf16_linear(m, h2, lay.w["wu"])
+    g64 = g.astype(F64)
+    sg = m.round((g64 / (1.0 + np.exp(-g64))).astype(F32))
+    a = m.round((sg.astype(F64) * u.astype(F64)).astype(F32))
+    d = bf16_linear(m, a, lay.w["wd"])
+    x2 = m.round((x1.astype(F64) + d.astype(F64)).astype(F32))
+    if trace is not None:
+        trace.update(h1=h1, q=q, k=k, v=v, attn=attn, x1=x1, h2=h2, g=g, u=u, a=a, x2=x2)
+    return x2, k, v
+
+
+def bf16_forward(m: Bf16Model, x: np.ndarray, p, k_caches, v_caches):
+    """All layers, then the LM head on each sequence's last row: (logits
+    [B, V] fp32 or None, k_deltas, v_deltas, hidden)."""
+    p = np.asarray(p, np.int64)
+    x = np.asarray(x, F32)
+    kd, vd = [], []
+    for l in range(len(m.layers)):
+        x, k, v = bf16_layer_forward(m, l, x, p, k_caches[l], v_caches[l])
+        kd.append(k)
+        vd.append(v)
+    logits = None
+    if m.lm_head is not None:
+        hn = bf16_rmsnorm(m, x[:, -1, :], m.final_norm)
+        logits = (hn.astype(F64) @ m.lm_head.astype(F64).T).astype(F32)
+    return logits, kd, vd, x
+
+
+def bf16_prefill(m: Bf16Model, embeds: np.ndarray, p, k_caches, v_caches):
+    """Prefill from bf16 rows (the caller's embeddings rounded to bf16)."""
+    return bf16_forward(m, m.round(np.asarray(embeds, F32)), p, k_caches, v_caches)
+
+
+def bf16_decode_step(m: Bf16Model, ids, p, k_caches, v_caches):
+    x = m.embed[np.asarray(ids).reshape(-1)][:, None, :]
+    return bf16_forward(m, x, p, k_caches, v_caches)
