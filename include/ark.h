@@ -381,6 +381,75 @@ int ark_decode_path(const ark_model* m, int32_t B);
 int ark_masked_argmax(int32_t B, int32_t V, const float* logits, const uint8_t* mask,
                       int32_t* out_ids, void* stream);
 
+/* ----------------------------------------------- bf16 serving variant -- */
+
+/* The decoder in bf16 (cookbook "ARK-ASR-3B", "dtype": bfloat16 is the
+ * default serving dtype): the checkpoint's weights, every activation and
+ * the KV cache in bf16 (IEEE bfloat16 bits in uint16_t), half the cache
+ * bytes of the fp32 path.  Each operation rounds its output once to bf16
+ * (nearest even): RMSNorm bf16(g * bf16(x / rms)), linear bf16(x W^T + b),
+ * the rotated q and k, attention bf16(softmax(q.k / sqrt(128)) v),
+ * residual adds, the MLP gate bf16(bf16(silu(g)) * u); the logits are the
+ * fp32 sums of the final-normed row with the head's rows.  Sums run in fp32
+ * (matrix cores, attention) or fp64 (norm statistics, rotary step), so
+ * results match a reference that rounds at the same points within bf16
+ * rounding (2e-2 relative, the serving dtype's tolerance).  Same geometry,
+ * cache contract and workspace rules as the int8 path. */
+typedef struct {
+  const uint16_t* w;     /* [n][k] bf16 */
+  const uint16_t* bias;  /* [n] bf16 or NULL (q, k, v only) */
+  int32_t n, k;
+} ark_linear_bf16;
+
+typedef struct {
+  const uint16_t* ln1;   /* [hidden] bf16 gains */
+  const uint16_t* ln2;
+  ark_linear_bf16 q, k, v, o, gate, up, down;
+} ark_layer_bf16;
+
+typedef struct {
+  ark_dims d;
+  const ark_layer_bf16* layers;  /* [host] d.n_layers entries */
+  const uint16_t* final_norm;    /* [hidden] bf16 */
+  ark_linear_bf16 lm_head;       /* [vocab][hidden]; w == NULL: none */
+  const uint16_t* embed;         /* [vocab][hidden] bf16 */
+  const double* rope_cos;        /* as ark_model */
+  const double* rope_sin;
+} ark_model_bf16;
+
+/* fp32 -> bf16 (nearest even; NaN stays NaN) of n values (weights, inputs).
+ * Errors: ARK_E_NULL, ARK_E_SHAPE (n < 0), ARK_E_HIP. */
+int ark_to_bf16(const float* x, int64_t n, uint16_t* out, void* stream);
+
+/* Workspace bytes of ark_prefill_bf16 / ark_decode_step_bf16 for B
+ * sequences of S rows; 0 if the dims are invalid. */
+size_t ark_workspace_bytes_bf16(const ark_dims* d, int32_t B, int32_t S);
+
+/* Prefill of B sequences of S bf16 rows, the bf16 counterpart of
+ * ark_prefill: embeds [B][S][hidden] bf16; k_cache, v_cache [host][L] of
+ * [B][T][n_kv][128] bf16 (read only); k_delta, v_delta
+ * [L][B][S][n_kv][128] bf16 out; logits [B][vocab] fp32 or NULL;
+ * hidden_out [B][S][hidden] bf16 or NULL.  1 <= B <= 64.  Errors as
+ * ark_prefill. */
+int ark_prefill_bf16(const ark_model_bf16* m, int32_t B, int32_t S, const uint16_t* embeds,
+                     const int32_t* cache_position, const uint16_t* const* k_cache,
+                     const uint16_t* const* v_cache, uint16_t* k_delta, uint16_t* v_delta,
+                     float* logits, uint16_t* hidden_out, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* One decode step of the bf16 variant: token_ids [B] gathered from
+ * m->embed, then as ark_prefill_bf16 with S = 1. */
+int ark_decode_step_bf16(const ark_model_bf16* m, int32_t B, const int32_t* token_ids,
+                         const int32_t* cache_position, const uint16_t* const* k_cache,
+                         const uint16_t* const* v_cache, uint16_t* k_delta, uint16_t* v_delta,
+                         float* logits, uint16_t* hidden_out, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* ark_cache_write for the bf16 caches and deltas. */
+int ark_cache_write_bf16(const ark_dims* d, int32_t B, int32_t S, const int32_t* cache_position,
+                         uint16_t* const* k_cache, uint16_t* const* v_cache,
+                         const uint16_t* k_delta, const uint16_t* v_delta, void* stream);
+
 /* ----------------------------------------------------------------- a13 -- */
 
 /* Host write-back of the deltas (model card "Shapes"): for every layer l and

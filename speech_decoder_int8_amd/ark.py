@@ -66,6 +66,16 @@ class ArkEncoder(C.Structure):
                 ("lnf_b", C.c_void_p), ("rope_cos", C.c_void_p), ("rope_sin", C.c_void_p)]
 
 
+class ArkLinearBf16(C.Structure):
+    _fields_ = [("w", C.c_void_p), ("bias", C.c_void_p), ("n", C.c_int32), ("k", C.c_int32)]
+
+
+class ArkLayerBf16(C.Structure):
+    _fields_ = [("ln1", C.c_void_p), ("ln2", C.c_void_p), ("q", ArkLinearBf16), ("k", ArkLinearBf16),
+                ("v", ArkLinearBf16), ("o", ArkLinearBf16), ("gate", ArkLinearBf16),
+                ("up", ArkLinearBf16), ("down", ArkLinearBf16)]
+
+
 class ArkLayer(C.Structure):
     _fields_ = [("ln1", C.c_void_p), ("ln2", C.c_void_p), ("q", ArkQLinear), ("k", ArkQLinear),
                 ("v", ArkQLinear), ("o", ArkQLinear), ("gate", ArkQLinear), ("up", ArkQLinear),
@@ -76,6 +86,12 @@ class ArkModel(C.Structure):
     _fields_ = [("d", ArkDims), ("layers", C.POINTER(ArkLayer)), ("final_norm", C.c_void_p),
                 ("lm_head", ArkQLinear), ("embed_f16", C.c_void_p), ("rope_cos", C.c_void_p),
                 ("rope_sin", C.c_void_p), ("lm_head4", ArkQLinear4)]
+
+
+class ArkModelBf16(C.Structure):
+    _fields_ = [("d", ArkDims), ("layers", C.POINTER(ArkLayerBf16)), ("final_norm", C.c_void_p),
+                ("lm_head", ArkLinearBf16), ("embed", C.c_void_p), ("rope_cos", C.c_void_p),
+                ("rope_sin", C.c_void_p)]
 
 
 P = C.c_void_p
@@ -90,6 +106,13 @@ _SIGS = {
     "ark_prep_weight": (C.c_int, [P, I32, I32, P, P, P, P]),
     "ark_rope_table": (C.c_int, [I32, I32, C.c_double, P, P, P]),
     "ark_prep_weight_int4": (C.c_int, [P, I32, I32, P, P, P, P]),
+    "ark_to_bf16": (C.c_int, [P, C.c_int64, P, P]),
+    "ark_workspace_bytes_bf16": (C.c_size_t, [C.POINTER(ArkDims), I32, I32]),
+    "ark_prefill_bf16": (C.c_int, [C.POINTER(ArkModelBf16), I32, I32, P, PI32, PP, PP, P, P, P, P, P,
+                                   C.c_size_t, P]),
+    "ark_decode_step_bf16": (C.c_int, [C.POINTER(ArkModelBf16), I32, P, PI32, PP, PP, P, P, P, P, P,
+                                       C.c_size_t, P]),
+    "ark_cache_write_bf16": (C.c_int, [C.POINTER(ArkDims), I32, I32, PI32, PP, PP, P, P, P]),
     "ark_adapter_workspace_bytes": (C.c_size_t, [C.POINTER(ArkAdapter), I32, I32]),
     "ark_encoder_workspace_bytes": (C.c_size_t, [C.POINTER(ArkEncoder), I32, I32]),
     "ark_audio_encoder": (C.c_int, [C.POINTER(ArkEncoder), I32, I32, P, P, P, C.c_size_t, P]),
@@ -487,6 +510,98 @@ def audio_encoder(enc: DeviceEncoder, mel, out, ws=None, stream=None):
         ws = enc.workspace(B, M)
     _check("ark_audio_encoder", lib().ark_audio_encoder(
         C.byref(enc.c), B, M, _ptr(mel), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+# ------------------------------------------------------ the bf16 variant --
+def to_bf16(x, stream=None):
+    """fp32 device tensor -> torch.bfloat16 tensor of the same shape (ark_to_bf16)."""
+    import torch
+    out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+    _check("ark_to_bf16", lib().ark_to_bf16(_ptr(x), x.numel(), _ptr(out), _stream(stream)))
+    return out
+
+
+class DeviceModelBf16:
+    """The decoder's weights in bf16 on the GPU and its ark_model_bf16 struct."""
+
+    def __init__(self, cfg, layers, final_norm, lm_head, embed, rope_cos, rope_sin):
+        self.cfg = cfg
+        self.layers, self.final_norm, self.lm_head, self.embed = layers, final_norm, lm_head, embed
+        self.rope_cos, self.rope_sin = rope_cos, rope_sin
+        self.dims = dims_of(cfg)
+
+        def lin(w, b=None):
+            return ArkLinearBf16(_ptr(w), _ptr(b), w.shape[0], w.shape[1])
+        self._arr = (ArkLayerBf16 * len(layers))()
+        for i, L in enumerate(layers):
+            self._arr[i] = ArkLayerBf16(_ptr(L["ln1"]), _ptr(L["ln2"]), lin(L["wq"], L["bq"]),
+                                        lin(L["wk"], L["bk"]), lin(L["wv"], L["bv"]), lin(L["wo"]),
+                                        lin(L["wg"]), lin(L["wu"]), lin(L["wd"]))
+        self.c = ArkModelBf16(self.dims, self._arr, _ptr(final_norm),
+                              lin(lm_head) if lm_head is not None else ArkLinearBf16(),
+                              _ptr(embed), _ptr(rope_cos), _ptr(rope_sin))
+
+    def workspace(self, B: int, S: int):
+        import torch
+        n = lib().ark_workspace_bytes_bf16(C.byref(self.dims), B, S)
+        if n == 0:
+            raise ArkError("ark_workspace_bytes_bf16", ARK_E_SHAPE, "invalid dims")
+        return torch.empty(n, dtype=torch.uint8, device="cuda")
+
+
+def load_model_bf16(cfg, synth, device="cuda", stream=None) -> DeviceModelBf16:
+    """The seeded fp32 weights of `cfg` converted to bf16 on the GPU."""
+    import torch
+
+    def bf(a):
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+        return to_bf16(t, stream)
+    layers = []
+    for l in range(cfg.n_layers):
+        w = synth.layer_weights(cfg, l)
+        layers.append({k: bf(v) for k, v in w.items()})
+        del w
+    final_norm = lm = None
+    if cfg.lm_head:
+        final_norm = bf(synth.final_norm(cfg))
+        lm = torch.empty((cfg.vocab, cfg.hidden), dtype=torch.bfloat16, device=device)
+        step = 16 * synth.ROW_CHUNK
+        for r0 in range(0, cfg.vocab, step):
+            r1 = min(cfg.vocab, r0 + step)
+            lm[r0:r1].copy_(bf(synth.lm_head_rows(cfg, r0, r1)))
+    emb = bf(synth.embed_table_f16(cfg).astype(np.float32))
+    rc, rs = rope_table(cfg.max_total_len, cfg.head_dim, cfg.rope_theta, device, stream)
+    torch.cuda.current_stream().synchronize()
+    return DeviceModelBf16(cfg, layers, final_norm, lm, emb, rc, rs)
+
+
+def prefill_bf16(model: DeviceModelBf16, embeds, cache_position, k_cache, v_cache, k_delta,
+                 v_delta, logits=None, hidden_out=None, ws=None, stream=None):
+    B, S = embeds.shape[0], embeds.shape[1]
+    if ws is None:
+        ws = model.workspace(B, S)
+    _check("ark_prefill_bf16", lib().ark_prefill_bf16(
+        C.byref(model.c), B, S, _ptr(embeds), _pos_array(cache_position), _ptr_array(k_cache),
+        _ptr_array(v_cache), _ptr(k_delta), _ptr(v_delta), _ptr(logits), _ptr(hidden_out),
+        _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def decode_step_bf16(model: DeviceModelBf16, token_ids, cache_position, k_cache, v_cache, k_delta,
+                     v_delta, logits=None, hidden_out=None, ws=None, stream=None):
+    B = token_ids.shape[0]
+    if ws is None:
+        ws = model.workspace(B, 1)
+    _check("ark_decode_step_bf16", lib().ark_decode_step_bf16(
+        C.byref(model.c), B, _ptr(token_ids), _pos_array(cache_position), _ptr_array(k_cache),
+        _ptr_array(v_cache), _ptr(k_delta), _ptr(v_delta), _ptr(logits), _ptr(hidden_out),
+        _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def cache_write_bf16(dims: ArkDims, cache_position, k_cache, v_cache, k_delta, v_delta, stream=None):
+    B, S = k_delta.shape[1], k_delta.shape[2]
+    _check("ark_cache_write_bf16", lib().ark_cache_write_bf16(
+        C.byref(dims), B, S, _pos_array(cache_position), _ptr_array(k_cache), _ptr_array(v_cache),
+        _ptr(k_delta), _ptr(v_delta), _stream(stream)))
 
 
 # ------------------------------------------------------------- the path --

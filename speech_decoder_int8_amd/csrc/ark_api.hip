@@ -710,6 +710,150 @@ int check_encoder(const ark_encoder* E, int B, int M) {
   return ARK_OK;
 }
 
+// ---- bf16 serving variant
+struct PlanBf16 {
+  size_t x, h, qkv, q, attn, a, total;
+};
+
+PlanBf16 plan_bf16(const ark_dims& d, int B, int S) {
+  const size_t R = (size_t)B * S, H = d.hidden, Q = (size_t)d.n_heads * d.head_dim;
+  const size_t KV = (size_t)d.n_kv_heads * d.head_dim, I = d.intermediate;
+  PlanBf16 p;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align_up(bytes);
+    return at;
+  };
+  p.x = take(R * H * 2);
+  p.h = take(R * H * 2);
+  p.qkv = take(R * (Q + 2 * KV) * 2);
+  p.q = take(R * Q * 2);
+  p.attn = take(R * Q * 2);
+  p.a = take(R * I * 2);
+  p.total = o;
+  return p;
+}
+
+int check_linear_bf16(const ark_linear_bf16& q, int n, int k, bool bias_allowed) {
+  if (!q.w) return ARK_E_NULL;
+  if (q.n != n || q.k != k || !gemm_bf16_supported(k)) return ARK_E_SHAPE;
+  if (q.bias && !bias_allowed) return ARK_E_SHAPE;
+  if (!aligned(q.w, 16)) return ARK_E_ALIGN;
+  return ARK_OK;
+}
+
+int check_model_bf16(const ark_model_bf16* m, bool need_embed) {
+  if (!m) return ARK_E_NULL;
+  const ark_dims& d = m->d;
+  if (!dims_ok(d) || !attn_bf16_supported(d.n_heads, d.n_kv_heads)) return ARK_E_SHAPE;
+  if (!m->layers || !m->rope_cos || !m->rope_sin) return ARK_E_NULL;
+  if (need_embed && !m->embed) return ARK_E_NULL;
+  const int H = d.hidden, Q = d.n_heads * d.head_dim, KV = d.n_kv_heads * d.head_dim;
+  const int I = d.intermediate;
+  for (int l = 0; l < d.n_layers; ++l) {
+    const ark_layer_bf16& L = m->layers[l];
+    if (!L.ln1 || !L.ln2) return ARK_E_NULL;
+    int e;
+    if ((e = check_linear_bf16(L.q, Q, H, true))) return e;
+    if ((e = check_linear_bf16(L.k, KV, H, true))) return e;
+    if ((e = check_linear_bf16(L.v, KV, H, true))) return e;
+    if ((e = check_linear_bf16(L.o, H, Q, false))) return e;
+    if ((e = check_linear_bf16(L.gate, I, H, false))) return e;
+    if ((e = check_linear_bf16(L.up, I, H, false))) return e;
+    if ((e = check_linear_bf16(L.down, H, I, false))) return e;
+  }
+  if (m->lm_head.w) {
+    if (!m->final_norm) return ARK_E_NULL;
+    int e;
+    if ((e = check_linear_bf16(m->lm_head, d.vocab, H, false))) return e;
+  }
+  return ARK_OK;
+}
+
+int check_step_bf16(const ark_model_bf16* m, int B, int S, const int32_t* pos,
+                    const uint16_t* const* kc, const uint16_t* const* vc, const uint16_t* kd,
+                    const uint16_t* vd, const float* logits, const void* ws, size_t ws_bytes) {
+  if (B < 1 || B > kMaxBatch || S < 1) return ARK_E_SHAPE;
+  if (!pos || !kc || !vc || !kd || !vd || !ws) return ARK_E_NULL;
+  const ark_dims& d = m->d;
+  for (int l = 0; l < d.n_layers; ++l)
+    if (!kc[l] || !vc[l]) return ARK_E_NULL;
+  if (logits && !m->lm_head.w) return ARK_E_SHAPE;
+  for (int b = 0; b < B; ++b)
+    if (pos[b] < 0 || (int64_t)pos[b] + S > d.max_total_len) return ARK_E_RANGE;
+  if (!aligned(ws, kAlign) || !aligned(kd, 16) || !aligned(vd, 16)) return ARK_E_ALIGN;
+  for (int l = 0; l < d.n_layers; ++l)
+    if (!aligned(kc[l], 16) || !aligned(vc[l], 16)) return ARK_E_ALIGN;
+  if (ws_bytes < plan_bf16(d, B, S).total) return ARK_E_WORKSPACE;
+  return ARK_OK;
+}
+
+inline BSeg bseg(const ark_linear_bf16& q, void* out, int ldo) {
+  BSeg s;
+  s.w = q.w;
+  s.bias = q.bias;
+  s.out = out;
+  s.n = q.n;
+  s.ldo = ldo;
+  return s;
+}
+
+// All layers and the LM head of the bf16 variant over the rows in x.
+int run_forward_bf16(const ark_model_bf16* m, int B, int S, uint16_t* x, const int32_t* pos_host,
+                     const uint16_t* const* kc, const uint16_t* const* vc, uint16_t* kd,
+                     uint16_t* vd, float* logits, char* ws, hipStream_t st) {
+  const ark_dims& d = m->d;
+  const PlanBf16 p = plan_bf16(d, B, S);
+  const int R = B * S, H = d.hidden, NH = d.n_heads, NKV = d.n_kv_heads;
+  const int Q = NH * kHeadDim, KV = NKV * kHeadDim, I = d.intermediate, W = Q + 2 * KV;
+  uint16_t* h = (uint16_t*)(ws + p.h);
+  uint16_t* qkv = (uint16_t*)(ws + p.qkv);
+  uint16_t* q = (uint16_t*)(ws + p.q);
+  uint16_t* attn = (uint16_t*)(ws + p.attn);
+  uint16_t* a = (uint16_t*)(ws + p.a);
+  PosArgs pos;
+  memset(&pos, 0, sizeof(pos));
+  for (int b = 0; b < B; ++b) pos.p[b] = pos_host[b];
+  for (int l = 0; l < d.n_layers; ++l) {
+    const ark_layer_bf16& L = m->layers[l];
+    uint16_t* kdl = kd + (size_t)l * R * KV;
+    uint16_t* vdl = vd + (size_t)l * R * KV;
+    HIP_TRY(launch_rmsnorm_bf16(st, R, H, x, H, L.ln1, d.rms_eps, h));
+    BSeg qs3[3] = {bseg(L.q, qkv, W), bseg(L.k, qkv + Q, W), bseg(L.v, qkv + Q + KV, W)};
+    HIP_TRY(launch_gemm_bf16(st, R, H, h, H, qs3, 3, BE_STORE));
+    HIP_TRY(launch_rope_bf16(st, B, S, NH, NKV, qkv, m->rope_cos, m->rope_sin, pos, q, kdl, vdl));
+    AttnBf16Params A;
+    A.B = B;
+    A.S = S;
+    A.NH = NH;
+    A.NKV = NKV;
+    A.T = d.max_total_len;
+    A.q = q;
+    A.kc = kc[l];
+    A.vc = vc[l];
+    A.kd = kdl;
+    A.vd = vdl;
+    A.pos = pos;
+    A.out = attn;
+    HIP_TRY(launch_attn_bf16(st, A));
+    BSeg os[1] = {bseg(L.o, x, H)};
+    HIP_TRY(launch_gemm_bf16(st, R, Q, attn, Q, os, 1, BE_RESID));
+    HIP_TRY(launch_rmsnorm_bf16(st, R, H, x, H, L.ln2, d.rms_eps, h));
+    BSeg gu[2] = {bseg(L.gate, a, I), bseg(L.up, a, I)};
+    HIP_TRY(launch_gemm_bf16(st, R, H, h, H, gu, 2, BE_SWIGLU));
+    BSeg ds[1] = {bseg(L.down, x, H)};
+    HIP_TRY(launch_gemm_bf16(st, R, I, a, I, ds, 1, BE_RESID));
+  }
+  if (logits) {
+    HIP_TRY(launch_rmsnorm_bf16(st, B, H, x + (size_t)(S - 1) * H, S * H, m->final_norm,
+                                d.rms_eps, h));
+    BSeg lm[1] = {bseg(m->lm_head, logits, d.vocab)};
+    HIP_TRY(launch_gemm_bf16(st, B, H, h, H, lm, 1, BE_F32));
+  }
+  return ARK_OK;
+}
+
 // Validate a parity record request and build its descriptor.
 int dump_check(const ark_model* m, int B, int S, void* dump, size_t dump_bytes, uint64_t mask,
                DumpRec* out) {
@@ -982,6 +1126,86 @@ int ark_audio_encoder(const ark_encoder* E, int32_t B, int32_t mel_frames, const
   }
   HIP_TRY(launch_layernorm(st, R, D, F, x, E->lnf_g, E->lnf_b, E->ln_eps, out, none));
   return ARK_OK;
+}
+
+int ark_to_bf16(const float* x, int64_t n, uint16_t* out, void* stream) {
+  if (!x || !out) return ARK_E_NULL;
+  if (n < 0) return ARK_E_SHAPE;
+  return launch_to_bf16((hipStream_t)stream, n, x, out) == hipSuccess ? ARK_OK : ARK_E_HIP;
+}
+
+size_t ark_workspace_bytes_bf16(const ark_dims* d, int32_t B, int32_t S) {
+  if (!d || !dims_ok(*d) || B < 1 || B > kMaxBatch || S < 1) return 0;
+  return plan_bf16(*d, B, S).total;
+}
+
+int ark_prefill_bf16(const ark_model_bf16* m, int32_t B, int32_t S, const uint16_t* embeds,
+                     const int32_t* cache_position, const uint16_t* const* k_cache,
+                     const uint16_t* const* v_cache, uint16_t* k_delta, uint16_t* v_delta,
+                     float* logits, uint16_t* hidden_out, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int e = check_model_bf16(m, false);
+  if (e) return e;
+  if (!embeds) return ARK_E_NULL;
+  e = check_step_bf16(m, B, S, cache_position, k_cache, v_cache, k_delta, v_delta, logits,
+                      workspace, workspace_bytes);
+  if (e) return e;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const PlanBf16 p = plan_bf16(m->d, B, S);
+  uint16_t* x = hidden_out ? hidden_out : (uint16_t*)(ws + p.x);
+  if (hipMemcpyAsync(x, embeds, (size_t)B * S * m->d.hidden * 2, hipMemcpyDeviceToDevice, st) !=
+      hipSuccess)
+    return ARK_E_HIP;
+  return run_forward_bf16(m, B, S, x, cache_position, k_cache, v_cache, k_delta, v_delta, logits,
+                          ws, st);
+}
+
+int ark_decode_step_bf16(const ark_model_bf16* m, int32_t B, const int32_t* token_ids,
+                         const int32_t* cache_position, const uint16_t* const* k_cache,
+                         const uint16_t* const* v_cache, uint16_t* k_delta, uint16_t* v_delta,
+                         float* logits, uint16_t* hidden_out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  int e = check_model_bf16(m, true);
+  if (e) return e;
+  if (!token_ids) return ARK_E_NULL;
+  e = check_step_bf16(m, B, 1, cache_position, k_cache, v_cache, k_delta, v_delta, logits,
+                      workspace, workspace_bytes);
+  if (e) return e;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const PlanBf16 p = plan_bf16(m->d, B, 1);
+  uint16_t* x = hidden_out ? hidden_out : (uint16_t*)(ws + p.x);
+  if (launch_embed_bf16(st, B, m->d.hidden, m->d.vocab, token_ids, m->embed, x) != hipSuccess)
+    return ARK_E_HIP;
+  return run_forward_bf16(m, B, 1, x, cache_position, k_cache, v_cache, k_delta, v_delta, logits,
+                          ws, st);
+}
+
+int ark_cache_write_bf16(const ark_dims* d, int32_t B, int32_t S, const int32_t* cache_position,
+                         uint16_t* const* k_cache, uint16_t* const* v_cache,
+                         const uint16_t* k_delta, const uint16_t* v_delta, void* stream) {
+  if (!d || !cache_position || !k_cache || !v_cache || !k_delta || !v_delta) return ARK_E_NULL;
+  if (!dims_ok(*d) || B < 1 || B > kMaxBatch || S < 1) return ARK_E_SHAPE;
+  CacheBf16Args A;
+  for (int l = 0; l < d->n_layers; ++l) {
+    if (!k_cache[l] || !v_cache[l]) return ARK_E_NULL;
+    if (!aligned(k_cache[l], 16) || !aligned(v_cache[l], 16)) return ARK_E_ALIGN;
+    A.k[l] = k_cache[l];
+    A.v[l] = v_cache[l];
+  }
+  if (!aligned(k_delta, 16) || !aligned(v_delta, 16)) return ARK_E_ALIGN;
+  PosArgs pos;
+  memset(&pos, 0, sizeof(pos));
+  for (int b = 0; b < B; ++b) {
+    if (cache_position[b] < 0 || (int64_t)cache_position[b] + S > d->max_total_len)
+      return ARK_E_RANGE;
+    pos.p[b] = cache_position[b];
+  }
+  return launch_cache_write_bf16((hipStream_t)stream, d->n_layers, B, S, d->max_total_len,
+                                 d->n_kv_heads * d->head_dim, pos, A, k_delta, v_delta) == hipSuccess
+             ? ARK_OK
+             : ARK_E_HIP;
 }
 
 int ark_rope_table(int32_t T, int32_t head_dim, double theta, double* cos_out, double* sin_out,

@@ -1,0 +1,604 @@
+// Kernels of the bf16 serving variant of the decoder (cookbook "ARK-ASR-3B",
+// "dtype": bfloat16 is the default serving dtype): weights, activations and
+// the KV cache in bf16, every operation rounding its output once to bf16
+// (round to nearest even), fp32 logits.  Products of bf16 values are exact
+// in fp32; sums run in fp32 (matrix cores) or fp64 (norms, rotary step).
+//   * k_to_bf16        fp32 -> bf16 of weights and inputs
+//   * k_gemv_bf16      up to 8 activation rows: one wave per pair of weight
+//                      rows, the rows of x read from cache
+//   * k_gemm_bf16      more rows: v_mfma_f32_16x16x32_bf16 tiles (the byte
+//                      layout of the int8 tiled GEMM: a 64-byte K step is
+//                      one matrix instruction per fragment pair)
+//   * k_rmsnorm_bf16, k_rope_bf16, k_attn_bf16, k_embed_bf16,
+//     k_cache_write_bf16
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ark {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+// nearest even; NaN stays a (quiet) NaN
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((b >> 16) | 0x40u);
+  b += 0x7fffu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+__device__ __forceinline__ float rbf(float f) { return bf2f(f2bf(f)); }
+
+// 8 bf16 in a 16-byte word -> floats
+__device__ __forceinline__ void unpack8(const i32x4 v, float (&f)[8]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t w = (uint32_t)v[j];
+    f[2 * j] = __uint_as_float(w << 16);
+    f[2 * j + 1] = __uint_as_float(w & 0xffff0000u);
+  }
+}
+
+// ---- fp32 -> bf16
+__global__ __launch_bounds__(256) void k_to_bf16(int64_t n, const float* __restrict__ x,
+                                                 uint16_t* __restrict__ y) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    y[i] = f2bf(x[i]);
+}
+
+hipError_t launch_to_bf16(hipStream_t st, int64_t n, const float* x, uint16_t* y) {
+  if (n <= 0) return hipSuccess;
+  const int64_t g = std::min<int64_t>((n + 255) / 256, 16384);
+  hipLaunchKernelGGL(k_to_bf16, dim3((unsigned)g), dim3(256), 0, st, n, x, y);
+  return hipGetLastError();
+}
+
+// ---- the epilogue of one output value
+// BE_STORE: bf16(acc + bias); BE_RESID: bf16(old + bf16(acc + bias));
+// BE_F32: fp32 acc (the logits); the SwiGLU pair is handled by the callers.
+__device__ __forceinline__ void bf_out(int epi, const BSeg& S, int row, int n, float acc) {
+  float y = acc;
+  if (epi == BE_F32) {
+    ((float*)S.out)[(size_t)row * S.ldo + n] = y;
+    return;
+  }
+  if (S.bias) y = y + bf2f(S.bias[n]);
+  uint16_t* o = (uint16_t*)S.out + (size_t)row * S.ldo + n;
+  if (epi == BE_RESID)
+    *o = f2bf(bf2f(*o) + rbf(y));
+  else
+    *o = f2bf(y);
+}
+// a = bf16(bf16(silu(bf16(g))) * bf16(u))
+__device__ __forceinline__ uint16_t bf_swiglu(float g, float u) {
+  const float gb = rbf(g), ub = rbf(u);
+  const float sg = rbf(gb / (1.0f + expf(-gb)));
+  return f2bf(sg * ub);
+}
+
+// ---- few rows: one wave per RB weight rows (per RB gate + RB up rows)
+constexpr int kGvMaxRows = 8;
+constexpr int kGvRB = 2;
+
+__global__ __launch_bounds__(256) void k_gemv_bf16(GemvBf16Params P) {
+  const int lane = threadIdx.x & 63;
+  const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const bool swiglu = P.epi == BE_SWIGLU;
+  const int n0 = wv * kGvRB;
+  if (n0 >= P.ncols) return;
+  const int K = P.K, NC = K / 8;
+  // the rows of this wave (column index in the concatenated output)
+  const uint16_t* wr[2 * kGvRB];
+  int nr = 0;
+#pragma unroll
+  for (int r = 0; r < kGvRB; ++r) {
+    const int col = min(n0 + r, P.ncols - 1);
+    if (swiglu) {
+      wr[r] = P.seg[0].w + (size_t)col * K;
+      wr[kGvRB + r] = P.seg[1].w + (size_t)col * K;
+    } else {
+      int si = 0;
+      while (si + 1 < P.nseg && col >= P.seg_start[si + 1]) ++si;
+      wr[r] = P.seg[si].w + (size_t)(col - P.seg_start[si]) * K;
+      wr[kGvRB + r] = wr[r];
+    }
+  }
+  nr = swiglu ? 2 * kGvRB : kGvRB;
+  float acc[2 * kGvRB][kGvMaxRows];
+#pragma unroll
+  for (int r = 0; r < 2 * kGvRB; ++r)
+#pragma unroll
+    for (int m = 0; m < kGvMaxRows; ++m) acc[r][m] = 0.0f;
+  for (int c = lane; c < NC; c += 64) {
+    float xf[kGvMaxRows][8];
+#pragma unroll
+    for (int m = 0; m < kGvMaxRows; ++m)
+      if (m < P.M) unpack8(*(const i32x4*)(P.x + (size_t)m * P.ldx + 8 * c), xf[m]);
+#pragma unroll
+    for (int r = 0; r < 2 * kGvRB; ++r) {
+      if (r < nr) {
+        float wf[8];
+        unpack8(__builtin_nontemporal_load((const i32x4*)(wr[r] + 8 * c)), wf);
+#pragma unroll
+        for (int m = 0; m < kGvMaxRows; ++m)
+          if (m < P.M) {
+            float a = acc[r][m];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a = fmaf(xf[m][i], wf[i], a);
+            acc[r][m] = a;
+          }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 2 * kGvRB; ++r)
+#pragma unroll
+    for (int m = 0; m < kGvMaxRows; ++m)
+      if (r < nr && m < P.M) acc[r][m] = wave_sum_f32(acc[r][m]);
+  if (lane != 0) return;
+#pragma unroll
+  for (int r = 0; r < kGvRB; ++r) {
+    const int col = n0 + r;
+    if (col >= P.ncols) continue;
+#pragma unroll
+    for (int m = 0; m < kGvMaxRows; ++m) {
+      if (m >= P.M) continue;
+      if (swiglu) {
+        ((uint16_t*)P.seg[0].out)[(size_t)m * P.seg[0].ldo + col] =
+            bf_swiglu(acc[r][m], acc[kGvRB + r][m]);
+      } else {
+        int si = 0;
+        while (si + 1 < P.nseg && col >= P.seg_start[si + 1]) ++si;
+        bf_out(P.epi, P.seg[si], m, col - P.seg_start[si], acc[r][m]);
+      }
+    }
+  }
+}
+
+// ---- more rows: matrix-core tiles (BM x BN x 32 bf16 per step)
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(256) void k_gemm_bf16(GemvBf16Params P) {
+  constexpr int BKB = 64, LW = BKB + 16;  // bytes per K step, LDS row pitch
+  constexpr int FM = BM / (16 * WM), FN = BN / (16 * WN);
+  constexpr int ACH = BM * 4, BCH = BN * 4;
+  constexpr int AP = (ACH + 255) / 256, BP = (BCH + 255) / 256;
+  __shared__ __align__(16) unsigned char As[BM * LW];
+  __shared__ __align__(16) unsigned char Bs[BN * LW];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const bool swiglu = P.epi == BE_SWIGLU;
+  const int m0 = blockIdx.y * BM;
+  const int nb = blockIdx.x * (swiglu ? BN / 2 : BN);
+  const size_t KB = (size_t)P.K * 2;  // bytes per row
+
+  const unsigned char* asrc[AP];
+  int aoff[AP];
+#pragma unroll
+  for (int p = 0; p < AP; ++p) {
+    const int c = tid + p * 256;
+    asrc[p] = nullptr;
+    aoff[p] = -1;
+    if (c < ACH) {
+      const int tr = c >> 2, q = c & 3;
+      aoff[p] = tr * LW + q * 16;
+      if (m0 + tr < P.M) asrc[p] = (const unsigned char*)(P.x + (size_t)(m0 + tr) * P.ldx) + q * 16;
+    }
+  }
+  const unsigned char* bsrc[BP];
+  int boff[BP];
+#pragma unroll
+  for (int p = 0; p < BP; ++p) {
+    const int c = tid + p * 256;
+    bsrc[p] = nullptr;
+    boff[p] = -1;
+    if (c < BCH) {
+      const int tr = c >> 2, q = c & 3;
+      boff[p] = tr * LW + q * 16;
+      if (swiglu) {
+        const int half = BN / 2;
+        const int n = nb + (tr < half ? tr : tr - half);
+        if (n < P.ncols)
+          bsrc[p] = (const unsigned char*)((tr < half ? P.seg[0].w : P.seg[1].w)) + (size_t)n * KB + q * 16;
+      } else {
+        const int n = nb + tr;
+        if (n < P.ncols) {
+          int s = 0;
+          while (s + 1 < P.nseg && n >= P.seg_start[s + 1]) ++s;
+          bsrc[p] = (const unsigned char*)P.seg[s].w + (size_t)(n - P.seg_start[s]) * KB + q * 16;
+        }
+      }
+    }
+  }
+  f32x4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  int brow[FN];
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) {
+    if (swiglu) {
+      const int h = FN / 2;
+      brow[fn] = (fn < h ? 0 : BN / 2) + wn * h * 16 + (fn % h) * 16 + (lane & 15);
+    } else {
+      brow[fn] = wn * FN * 16 + fn * 16 + (lane & 15);
+    }
+  }
+  const int kq = (lane >> 4) * 16;
+  for (size_t k0 = 0; k0 < KB; k0 += BKB) {
+    i32x4 ra[AP], rb[BP];
+#pragma unroll
+    for (int p = 0; p < AP; ++p) ra[p] = asrc[p] ? *(const i32x4*)(asrc[p] + k0) : i32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int p = 0; p < BP; ++p)
+      rb[p] = bsrc[p] ? __builtin_nontemporal_load((const i32x4*)(bsrc[p] + k0)) : i32x4{0, 0, 0, 0};
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < AP; ++p)
+      if (aoff[p] >= 0) *(i32x4*)(As + aoff[p]) = ra[p];
+#pragma unroll
+    for (int p = 0; p < BP; ++p)
+      if (boff[p] >= 0) *(i32x4*)(Bs + boff[p]) = rb[p];
+    __syncthreads();
+    i32x4 fa[FM], fb[FN];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+      fa[fm] = *(const i32x4*)(As + (wm * FM * 16 + fm * 16 + (lane & 15)) * LW + kq);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) fb[fn] = *(const i32x4*)(Bs + brow[fn] * LW + kq);
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, fa[fm]), __builtin_bit_cast(bf16x8_t, fb[fn]), acc[fm][fn],
+            0, 0, 0);
+  }
+  // C[4 (lane / 16) + v][lane % 16] of each 16x16 block
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = m0 + wm * FM * 16 + fm * 16 + (lane >> 4) * 4 + v;
+      if (row >= P.M) continue;
+      if (swiglu) {
+#pragma unroll
+        for (int fn = 0; fn < FN / 2; ++fn) {
+          const int n = nb + wn * (FN / 2) * 16 + fn * 16 + (lane & 15);
+          if (n >= P.ncols) continue;
+          ((uint16_t*)P.seg[0].out)[(size_t)row * P.seg[0].ldo + n] =
+              bf_swiglu(acc[fm][fn][v], acc[fm][fn + FN / 2][v]);
+        }
+      } else {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          const int col = nb + wn * FN * 16 + fn * 16 + (lane & 15);
+          if (col >= P.ncols) continue;
+          int si = 0;
+          while (si + 1 < P.nseg && col >= P.seg_start[si + 1]) ++si;
+          bf_out(P.epi, P.seg[si], row, col - P.seg_start[si], acc[fm][fn][v]);
+        }
+      }
+    }
+  }
+}
+
+bool gemm_bf16_supported(int K) { return K >= 32 && K % 32 == 0; }
+
+hipError_t launch_gemm_bf16(hipStream_t st, int M, int K, const uint16_t* x, int ldx,
+                            const BSeg* segs, int nseg, int epi) {
+  GemvBf16Params P = {};
+  P.M = M;
+  P.K = K;
+  P.x = x;
+  P.ldx = ldx;
+  P.nseg = nseg;
+  P.epi = epi;
+  P.seg_start[0] = 0;
+  for (int i = 0; i < nseg; ++i) {
+    P.seg[i] = segs[i];
+    P.seg_start[i + 1] = P.seg_start[i] + segs[i].n;
+  }
+  P.ncols = (epi == BE_SWIGLU) ? segs[0].n : P.seg_start[nseg];
+  if (M <= kGvMaxRows) {
+    const int waves = (P.ncols + kGvRB - 1) / kGvRB;
+    hipLaunchKernelGGL(k_gemv_bf16, dim3((waves + 3) / 4), dim3(256), 0, st, P);
+  } else if (M <= 32) {
+    constexpr int BM = 32, BN = 128;
+    const int tn = epi == BE_SWIGLU ? BN / 2 : BN;
+    hipLaunchKernelGGL((k_gemm_bf16<BM, BN, 1, 4>), dim3((P.ncols + tn - 1) / tn, (M + BM - 1) / BM),
+                       dim3(256), 0, st, P);
+  } else {
+    constexpr int BM = 128, BN = 128;
+    const int tn = epi == BE_SWIGLU ? BN / 2 : BN;
+    hipLaunchKernelGGL((k_gemm_bf16<BM, BN, 2, 2>), dim3((P.ncols + tn - 1) / tn, (M + BM - 1) / BM),
+                       dim3(256), 0, st, P);
+  }
+  return hipGetLastError();
+}
+
+// ---- RMSNorm: one wave per row; bf16(g * bf16(x / sqrt(mean(x^2) + eps)))
+__global__ __launch_bounds__(256) void k_rmsnorm_bf16(int R, int H, const uint16_t* __restrict__ x,
+                                                      int ldx, const uint16_t* __restrict__ g,
+                                                      double eps, uint16_t* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= R) return;
+  const uint16_t* xr = x + (size_t)row * ldx;
+  double s = 0.0;
+  for (int i = lane; i < H; i += 64) {
+    const double v = bf2f(xr[i]);
+    s += v * v;
+  }
+  const double r = 1.0 / sqrt(wave_sum(s) / (double)H + eps);
+  uint16_t* yr = y + (size_t)row * H;
+  for (int i = lane; i < H; i += 64) {
+    const float t = rbf((float)((double)bf2f(xr[i]) * r));
+    yr[i] = f2bf((float)((double)t * (double)bf2f(g[i])));
+  }
+}
+
+hipError_t launch_rmsnorm_bf16(hipStream_t st, int R, int H, const uint16_t* x, int ldx,
+                               const uint16_t* g, double eps, uint16_t* y) {
+  hipLaunchKernelGGL(k_rmsnorm_bf16, dim3((R + 3) / 4), dim3(256), 0, st, R, H, x, ldx, g, eps, y);
+  return hipGetLastError();
+}
+
+// ---- rotary step: q rotated into q_out; rotated keys and the values into
+// the deltas [B][S][NKV][128]; pairs (j, j + 64), fp64, one rounding
+__global__ __launch_bounds__(256) void k_rope_bf16(int B, int S, int NH, int NKV,
+                                                   const uint16_t* __restrict__ qkv,
+                                                   const double* __restrict__ cosT,
+                                                   const double* __restrict__ sinT, PosArgs pos,
+                                                   uint16_t* __restrict__ q_out,
+                                                   uint16_t* __restrict__ kd,
+                                                   uint16_t* __restrict__ vd) {
+  constexpr int D = 128, HD = 64;
+  const int Q = NH * D, KV = NKV * D, W = Q + 2 * KV;
+  const int heads = NH + NKV;  // rotated heads per row
+  const long n = (long)B * S * heads * HD;
+  for (long e = (long)blockIdx.x * 256 + threadIdx.x; e < n; e += (long)gridDim.x * 256) {
+    const int j = (int)(e % HD);
+    const long rh = e / HD;
+    const int hh = (int)(rh % heads);
+    const int r = (int)(rh / heads);
+    const int b = r / S, i = r % S;
+    const int p = pos.p[b] + i;
+    const double c = cosT[(size_t)p * HD + j], s = sinT[(size_t)p * HD + j];
+    const uint16_t* src = qkv + (size_t)r * W + (hh < NH ? hh * D : Q + (hh - NH) * D);
+    const double a = bf2f(src[j]), bb = bf2f(src[j + HD]);
+    const uint16_t ra = f2bf((float)(a * c - bb * s)), rb = f2bf((float)(bb * c + a * s));
+    uint16_t* dst = hh < NH ? q_out + (size_t)r * Q + hh * D
+                            : kd + ((size_t)r * NKV + (hh - NH)) * D;
+    dst[j] = ra;
+    dst[j + HD] = rb;
+    if (hh >= NH) {  // the value row of this KV head, copied once per pair slot
+      const uint16_t* vs = qkv + (size_t)r * W + Q + KV + (hh - NH) * D;
+      uint16_t* vdst = vd + ((size_t)r * NKV + (hh - NH)) * D;
+      vdst[j] = vs[j];
+      vdst[j + HD] = vs[j + HD];
+    }
+  }
+}
+
+hipError_t launch_rope_bf16(hipStream_t st, int B, int S, int NH, int NKV, const uint16_t* qkv,
+                            const double* cosT, const double* sinT, const PosArgs& pos,
+                            uint16_t* q_out, uint16_t* kd, uint16_t* vd) {
+  const long n = (long)B * S * (NH + NKV) * 64;
+  const int g = (int)std::min<long>((n + 255) / 256, 16384);
+  hipLaunchKernelGGL(k_rope_bf16, dim3(g), dim3(256), 0, st, B, S, NH, NKV, qkv, cosT, sinT, pos,
+                     q_out, kd, vd);
+  return hipGetLastError();
+}
+
+// ---- attention over the bf16 cache (fp32 scores, softmax and sums)
+// One workgroup = 16 query vectors sharing one KV head: for S > 1 the rows
+// i0 .. i0 + 15 of one query head, for S == 1 the G query heads of one KV
+// head.  256 threads = 16 vectors x 16 threads; each 64-key chunk of K and V
+// is staged in LDS as fp32.  A thread scores keys t, t + 16, t + 32, t + 48
+// of its vector and accumulates dims 8 t .. 8 t + 7 of the weighted sum.
+namespace ab {
+constexpr int D = 128, KC = 64, KP = 132, VPP = 128, NV = 16;
+constexpr int LDS = (NV * D + KC * KP + KC * VPP + NV * KC) * 4;
+}  // namespace ab
+
+__global__ __launch_bounds__(256) void k_attn_bf16(AttnBf16Params P) {
+  using namespace ab;
+  extern __shared__ __align__(16) float sm[];
+  float* Qs = sm;                 // [NV][D]
+  float* Ks = Qs + NV * D;        // [KC][KP]
+  float* Vs = Ks + KC * KP;       // [KC][VPP]
+  float* Ps = Vs + KC * VPP;      // [NV][KC]
+  const int tid = threadIdx.x, v = tid >> 4, t = tid & 15;
+  const int G = P.NH / P.NKV;
+  int b, g, head, row;
+  bool vok;
+  if (P.S > 1) {
+    const int nqt = (P.S + NV - 1) / NV;
+    const int qt = blockIdx.x % nqt;
+    const int bh = blockIdx.x / nqt;
+    b = bh / P.NH;
+    head = bh % P.NH;
+    g = head / G;
+    row = qt * NV + v;
+    vok = row < P.S;
+  } else {
+    b = blockIdx.x / P.NKV;
+    g = blockIdx.x % P.NKV;
+    head = g * G + v;
+    row = 0;
+    vok = v < G;
+  }
+  const int p = P.pos.p[b];
+  const int qpos = p + row;
+  // the last key any vector of this workgroup sees
+  int maxrow;
+  if (P.S > 1)
+    maxrow = min(((blockIdx.x % ((P.S + NV - 1) / NV)) + 1) * NV, P.S) - 1;
+  else
+    maxrow = 0;
+  const int maxq = p + maxrow;
+  // query vector -> LDS (fp32)
+  for (int e = tid; e < NV * D; e += 256) {
+    const int vv = e / D, d = e % D;
+    int hq, rq;
+    bool ok;
+    if (P.S > 1) {
+      hq = head;
+      rq = (blockIdx.x % ((P.S + NV - 1) / NV)) * NV + vv;
+      ok = rq < P.S;
+    } else {
+      hq = g * G + vv;
+      rq = 0;
+      ok = vv < G;
+    }
+    Qs[e] = ok ? bf2f(P.q[((size_t)(b * P.S + rq) * P.NH + hq) * D + d]) : 0.0f;
+  }
+  float acc[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) acc[d] = 0.0f;
+  float m = -INFINITY, l = 0.0f;
+  const float scale = 0.08838834764831845f;  // 1 / sqrt(128) rounded to fp32
+  const int nch = maxq / KC + 1;
+  for (int c = 0; c < nch; ++c) {
+    const int j0 = c * KC;
+    __syncthreads();
+    // 64 keys x 16 units of 8 dims, K and V: 4 units per thread
+    for (int e = tid; e < KC * (D / 8); e += 256) {
+      const int jj = e >> 4, u = e & 15;
+      const int j = j0 + jj;
+      float kf[8], vf[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kf[i] = vf[i] = 0.0f;
+      if (j < p + P.S && j < P.T) {
+        const uint16_t *ks, *vs;
+        if (j >= p) {
+          const size_t off = ((size_t)(b * P.S + (j - p)) * P.NKV + g) * D + 8 * u;
+          ks = P.kd + off;
+          vs = P.vd + off;
+        } else {
+          const size_t off = ((size_t)(b * P.T + j) * P.NKV + g) * D + 8 * u;
+          ks = P.kc + off;
+          vs = P.vc + off;
+        }
+        unpack8(*(const i32x4*)ks, kf);
+        unpack8(*(const i32x4*)vs, vf);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        Ks[jj * KP + 8 * u + i] = kf[i];
+        Vs[jj * VPP + 8 * u + i] = vf[i];
+      }
+    }
+    __syncthreads();
+    float sc[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int jj = t + 16 * kk;
+      const float* kr = Ks + jj * KP;
+      const float* qr = Qs + v * D;
+      float a = 0.0f;
+#pragma unroll 8
+      for (int d = 0; d < D; ++d) a = fmaf(qr[d], kr[d], a);
+      const int j = j0 + jj;
+      sc[kk] = (vok && j <= qpos) ? a * scale : -INFINITY;
+    }
+    float cmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, o, 16));
+    const float mnew = fmaxf(m, cmax);
+    const float alpha = (m == -INFINITY) ? 0.0f : expf(m - mnew);
+    float ls = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const float e = (sc[kk] == -INFINITY) ? 0.0f : expf(sc[kk] - mnew);
+      Ps[v * KC + t + 16 * kk] = e;
+      ls += e;
+    }
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) ls += __shfl_xor(ls, o, 16);
+    l = l * alpha + ls;
+    m = mnew;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) acc[d] *= alpha;
+    __syncthreads();
+    for (int jj = 0; jj < KC; ++jj) {
+      const float pw = Ps[v * KC + jj];
+      const float* vr = Vs + jj * VPP + 8 * t;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) acc[d] = fmaf(pw, vr[d], acc[d]);
+    }
+  }
+  if (vok) {
+    uint16_t* dst = P.out + ((size_t)(b * P.S + row) * P.NH + head) * D + 8 * t;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) dst[d] = f2bf(acc[d] / l);
+  }
+}
+
+hipError_t launch_attn_bf16(hipStream_t st, const AttnBf16Params& P) {
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)k_attn_bf16, hipFuncAttributeMaxDynamicSharedMemorySize, ab::LDS);
+  if (attr != hipSuccess) return attr;
+  const int grid = P.S > 1 ? P.B * P.NH * ((P.S + ab::NV - 1) / ab::NV) : P.B * P.NKV;
+  hipLaunchKernelGGL(k_attn_bf16, dim3(grid), dim3(256), ab::LDS, st, P);
+  return hipGetLastError();
+}
+
+bool attn_bf16_supported(int NH, int NKV) {
+  return NKV >= 1 && NH % NKV == 0 && NH / NKV <= ab::NV;
+}
+
+// ---- embedding rows from the bf16 table; ids out of range give NaN rows
+__global__ __launch_bounds__(256) void k_embed_bf16(int R, int H, int V, const int32_t* __restrict__ ids,
+                                                    const uint16_t* __restrict__ table,
+                                                    uint16_t* __restrict__ x) {
+  const long n = (long)R * H;
+  for (long e = (long)blockIdx.x * 256 + threadIdx.x; e < n; e += (long)gridDim.x * 256) {
+    const int r = (int)(e / H), i = (int)(e % H);
+    const int id = ids[r];
+    x[e] = (id >= 0 && id < V) ? table[(size_t)id * H + i] : (uint16_t)0x7fc0;
+  }
+}
+
+hipError_t launch_embed_bf16(hipStream_t st, int R, int H, int V, const int32_t* ids,
+                             const uint16_t* table, uint16_t* x) {
+  const long n = (long)R * H;
+  const int g = (int)std::min<long>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_embed_bf16, dim3(g), dim3(256), 0, st, R, H, V, ids, table, x);
+  return hipGetLastError();
+}
+
+// ---- deltas into the bf16 caches at each sequence's position
+__global__ __launch_bounds__(256) void k_cache_write_bf16(CacheBf16Args A, int B, int S, int T,
+                                                          int KVW, PosArgs pos,
+                                                          const uint16_t* __restrict__ kd,
+                                                          const uint16_t* __restrict__ vd) {
+  const int l = blockIdx.y;
+  const int units = KVW / 8;  // 16-byte units per row
+  const long n = (long)B * S * units;
+  uint16_t* kc = A.k[l];
+  uint16_t* vc = A.v[l];
+  const uint16_t* kdl = kd + (size_t)l * B * S * KVW;
+  const uint16_t* vdl = vd + (size_t)l * B * S * KVW;
+  for (long e = (long)blockIdx.x * 256 + threadIdx.x; e < n; e += (long)gridDim.x * 256) {
+    const int u = (int)(e % units);
+    const int r = (int)(e / units);
+    const int b = r / S, i = r % S;
+    const size_t dst = ((size_t)b * T + pos.p[b] + i) * KVW + 8 * u;
+    const size_t src = (size_t)r * KVW + 8 * u;
+    *(i32x4*)(kc + dst) = *(const i32x4*)(kdl + src);
+    *(i32x4*)(vc + dst) = *(const i32x4*)(vdl + src);
+  }
+}
+
+hipError_t launch_cache_write_bf16(hipStream_t st, int L, int B, int S, int T, int KVW,
+                                   const PosArgs& pos, const CacheBf16Args& A, const uint16_t* kd,
+                                   const uint16_t* vd) {
+  const long n = (long)B * S * (KVW / 8);
+  const int g = (int)std::min<long>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(k_cache_write_bf16, dim3(g, L), dim3(256), 0, st, A, B, S, T, KVW, pos, kd, vd);
+  return hipGetLastError();
+}
+
+}  // namespace ark

@@ -403,4 +403,53 @@ const uint32_t* decode_mega_err_word(const void* ws, int L, int T);
 // tags.
 uint64_t* decode_mega_marker(void* ws, int L, int T);
 
+// bf16 serving variant (k_bf16.hip).  A segment of output columns: bf16
+// weight rows [n][K], optional bf16 bias, output (bf16, or fp32 for
+// BE_F32) with row stride ldo.
+enum { BE_STORE = 0, BE_RESID = 1, BE_SWIGLU = 2, BE_F32 = 3 };
+struct BSeg {
+  const uint16_t* w;
+  const uint16_t* bias;
+  void* out;
+  int n, ldo;
+};
+struct GemvBf16Params {
+  int M, K, ldx, nseg, epi, ncols;
+  const uint16_t* x;
+  BSeg seg[3];
+  int seg_start[4];
+};
+hipError_t launch_to_bf16(hipStream_t st, int64_t n, const float* x, uint16_t* y);
+bool gemm_bf16_supported(int K);
+// y = x W^T over M rows of x (row stride ldx); epilogue epi (BE_SWIGLU: seg
+// 0 gate, seg 1 up, result to seg 0's output)
+hipError_t launch_gemm_bf16(hipStream_t st, int M, int K, const uint16_t* x, int ldx,
+                            const BSeg* segs, int nseg, int epi);
+hipError_t launch_rmsnorm_bf16(hipStream_t st, int R, int H, const uint16_t* x, int ldx,
+                               const uint16_t* g, double eps, uint16_t* y);
+hipError_t launch_rope_bf16(hipStream_t st, int B, int S, int NH, int NKV, const uint16_t* qkv,
+                            const double* cosT, const double* sinT, const PosArgs& pos,
+                            uint16_t* q_out, uint16_t* kd, uint16_t* vd);
+struct AttnBf16Params {
+  int B, S, NH, NKV, T;
+  const uint16_t* q;   // [B][S][NH][128] rotated
+  const uint16_t* kc;  // [B][T][NKV][128]
+  const uint16_t* vc;
+  const uint16_t* kd;  // [B][S][NKV][128]
+  const uint16_t* vd;
+  PosArgs pos;
+  uint16_t* out;       // [B][S][NH * 128]
+};
+bool attn_bf16_supported(int NH, int NKV);
+hipError_t launch_attn_bf16(hipStream_t st, const AttnBf16Params& P);
+hipError_t launch_embed_bf16(hipStream_t st, int R, int H, int V, const int32_t* ids,
+                             const uint16_t* table, uint16_t* x);
+struct CacheBf16Args {
+  uint16_t* k[kMaxLayers];
+  uint16_t* v[kMaxLayers];
+};
+hipError_t launch_cache_write_bf16(hipStream_t st, int L, int B, int S, int T, int KVW,
+                                   const PosArgs& pos, const CacheBf16Args& A, const uint16_t* kd,
+                                   const uint16_t* vd);
+
 }  // namespace ark

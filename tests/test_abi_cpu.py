@@ -422,3 +422,60 @@ def test_encoder_validation():
     E4._keep[0].ln2_b = None
     assert call(E4) == ark.ARK_E_NULL
     assert lib.ark_audio_encoder(None, 1, 300, FAKE, FAKE, FAKE, 1 << 40, None) == ark.ARK_E_NULL
+
+
+def fake_bf16_model(L=2, lm=True, **kw):
+    d = real_dims(n_layers=L, **kw)
+    H, Q, KV, I = d.hidden, d.n_heads * 128, d.n_kv_heads * 128, d.intermediate
+
+    def lin(n, k, bias=False):
+        return ark.ArkLinearBf16(FAKE, FAKE if bias else None, n, k)
+    layers = (ark.ArkLayerBf16 * L)()
+    for i in range(L):
+        layers[i] = ark.ArkLayerBf16(FAKE, FAKE, lin(Q, H, True), lin(KV, H, True), lin(KV, H, True),
+                                     lin(H, Q), lin(I, H), lin(I, H), lin(H, I))
+    m = ark.ArkModelBf16(d, layers, FAKE, lin(d.vocab, H) if lm else ark.ArkLinearBf16(), FAKE, FAKE,
+                         FAKE)
+    m._keep = layers
+    return m
+
+
+def test_bf16_validation():
+    lib = ark.lib()
+    m = fake_bf16_model()
+    L = 2
+    ws = lib.ark_workspace_bytes_bf16(C.byref(m.d), 1, 4)
+    assert ws > 0 and lib.ark_workspace_bytes_bf16(C.byref(m.d), 0, 4) == 0
+    kc = (C.c_void_p * L)(FAKE, FAKE)
+
+    def pre(m, B=1, S=4, pos=None, nbytes=None, logits=None, embeds=FAKE, kd=FAKE):
+        pos = [0] * B if pos is None else pos
+        nb = lib.ark_workspace_bytes_bf16(C.byref(m.d), max(B, 1), max(S, 1)) if nbytes is None else nbytes
+        return lib.ark_prefill_bf16(C.byref(m), B, S, embeds, (C.c_int32 * len(pos))(*pos), kc, kc, kd,
+                                    FAKE, logits, None, FAKE, nb, None)
+    assert pre(m, embeds=None) == ark.ARK_E_NULL
+    assert pre(m, B=0, pos=[0]) == ark.ARK_E_SHAPE
+    assert pre(m, pos=[510]) == ark.ARK_E_RANGE
+    assert pre(m, nbytes=1024) == ark.ARK_E_WORKSPACE
+    assert pre(m, kd=FAKE + 2) == ark.ARK_E_ALIGN
+    assert pre(fake_bf16_model(lm=False), logits=FAKE) == ark.ARK_E_SHAPE
+    m2 = fake_bf16_model()
+    m2._keep[0].o = ark.ArkLinearBf16(FAKE, FAKE, 2048, 2048)        # o carries no bias
+    assert pre(m2) == ark.ARK_E_SHAPE
+    m3 = fake_bf16_model()
+    m3._keep[1].down = ark.ArkLinearBf16(FAKE, None, 2048, 11000)
+    assert pre(m3) == ark.ARK_E_SHAPE
+    m4 = fake_bf16_model()
+    m4._keep[0].ln2 = None
+    assert pre(m4) == ark.ARK_E_NULL
+    assert pre(fake_bf16_model(n_heads=64, n_kv_heads=2)) == ark.ARK_E_SHAPE
+    pos = (C.c_int32 * 1)(3)
+    assert lib.ark_decode_step_bf16(C.byref(m), 1, None, pos, kc, kc, FAKE, FAKE, None, None, FAKE,
+                                    ws, None) == ark.ARK_E_NULL
+    assert lib.ark_to_bf16(None, 4, FAKE, None) == ark.ARK_E_NULL
+    assert lib.ark_to_bf16(FAKE, -1, FAKE, None) == ark.ARK_E_SHAPE
+    d = real_dims()
+    assert lib.ark_cache_write_bf16(C.byref(d), 1, 1, (C.c_int32 * 1)(512), kc, kc, FAKE, FAKE,
+                                    None) == ark.ARK_E_RANGE
+    assert lib.ark_cache_write_bf16(C.byref(d), 1, 1, (C.c_int32 * 1)(0), kc, kc, FAKE + 2, FAKE,
+                                    None) == ark.ARK_E_ALIGN
