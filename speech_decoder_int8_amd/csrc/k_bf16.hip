@@ -19,16 +19,6 @@ namespace ark {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-// nearest even; NaN stays a (quiet) NaN
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t b = __float_as_uint(f);
-  if ((b & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((b >> 16) | 0x40u);
-  b += 0x7fffu + ((b >> 16) & 1u);
-  return (uint16_t)(b >> 16);
-}
-__device__ __forceinline__ float rbf(float f) { return bf2f(f2bf(f)); }
-
 // 8 bf16 in a 16-byte word -> floats
 __device__ __forceinline__ void unpack8(const i32x4 v, float (&f)[8]) {
 #pragma unroll
@@ -53,43 +43,24 @@ hipError_t launch_to_bf16(hipStream_t st, int64_t n, const float* x, uint16_t* y
   return hipGetLastError();
 }
 
-// ---- the epilogue of one output value
-// BE_STORE: bf16(acc + bias); BE_RESID: bf16(old + bf16(acc + bias));
-// BE_F32: fp32 acc (the logits); the SwiGLU pair is handled by the callers.
-__device__ __forceinline__ void bf_out(int epi, const BSeg& S, int row, int n, float acc) {
-  float y = acc;
-  if (epi == BE_F32) {
-    ((float*)S.out)[(size_t)row * S.ldo + n] = y;
-    return;
-  }
-  if (S.bias) y = y + bf2f(S.bias[n]);
-  uint16_t* o = (uint16_t*)S.out + (size_t)row * S.ldo + n;
-  if (epi == BE_RESID)
-    *o = f2bf(bf2f(*o) + rbf(y));
-  else
-    *o = f2bf(y);
-}
-// a = bf16(bf16(silu(bf16(g))) * bf16(u))
-__device__ __forceinline__ uint16_t bf_swiglu(float g, float u) {
-  const float gb = rbf(g), ub = rbf(u);
-  const float sg = rbf(gb / (1.0f + expf(-gb)));
-  return f2bf(sg * ub);
-}
-
-// ---- few rows: one wave per RB weight rows (per RB gate + RB up rows)
+// ---- few rows: one wave per RB weight rows (per RB gate + RB up rows).
+// A lane takes 16-byte chunks of K; U chunks of every row (and of the MM
+// rows of x) are requested before any is used, so a wave keeps
+// U x rows x 1 KB of weights in flight.
 constexpr int kGvMaxRows = 8;
 constexpr int kGvRB = 2;
 
+template <int MM>
 __global__ __launch_bounds__(256) void k_gemv_bf16(GemvBf16Params P) {
+  constexpr int U = MM <= 2 ? 4 : (MM <= 4 ? 2 : 1);
+  constexpr int NR = 2 * kGvRB;
   const int lane = threadIdx.x & 63;
   const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
   const bool swiglu = P.epi == BE_SWIGLU;
   const int n0 = wv * kGvRB;
   if (n0 >= P.ncols) return;
-  const int K = P.K, NC = K / 8;
-  // the rows of this wave (column index in the concatenated output)
-  const uint16_t* wr[2 * kGvRB];
-  int nr = 0;
+  const int K = P.K, NC = K / 8, M = P.M;
+  const uint16_t* wr[NR];
 #pragma unroll
   for (int r = 0; r < kGvRB; ++r) {
     const int col = min(n0 + r, P.ncols - 1);
@@ -103,46 +74,59 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(GemvBf16Params P) {
       wr[kGvRB + r] = wr[r];
     }
   }
-  nr = swiglu ? 2 * kGvRB : kGvRB;
-  float acc[2 * kGvRB][kGvMaxRows];
+  const int nr = swiglu ? NR : kGvRB;
+  float acc[NR][MM];
 #pragma unroll
-  for (int r = 0; r < 2 * kGvRB; ++r)
+  for (int r = 0; r < NR; ++r)
 #pragma unroll
-    for (int m = 0; m < kGvMaxRows; ++m) acc[r][m] = 0.0f;
-  for (int c = lane; c < NC; c += 64) {
-    float xf[kGvMaxRows][8];
+    for (int m = 0; m < MM; ++m) acc[r][m] = 0.0f;
+  for (int c0 = lane; c0 < NC; c0 += 64 * U) {
+    i32x4 wq[U][NR], xq[U][MM];
 #pragma unroll
-    for (int m = 0; m < kGvMaxRows; ++m)
-      if (m < P.M) unpack8(*(const i32x4*)(P.x + (size_t)m * P.ldx + 8 * c), xf[m]);
+    for (int u = 0; u < U; ++u) {
+      const int c = min(c0 + 64 * u, NC - 1);
 #pragma unroll
-    for (int r = 0; r < 2 * kGvRB; ++r) {
-      if (r < nr) {
-        float wf[8];
-        unpack8(__builtin_nontemporal_load((const i32x4*)(wr[r] + 8 * c)), wf);
+      for (int r = 0; r < NR; ++r)
+        if (r < nr) wq[u][r] = __builtin_nontemporal_load((const i32x4*)(wr[r] + 8 * c));
 #pragma unroll
-        for (int m = 0; m < kGvMaxRows; ++m)
-          if (m < P.M) {
+      for (int m = 0; m < MM; ++m)
+        xq[u][m] = *(const i32x4*)(P.x + (size_t)min(m, M - 1) * P.ldx + 8 * c);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c0 + 64 * u >= NC) break;
+      float xf[MM][8];
+#pragma unroll
+      for (int m = 0; m < MM; ++m) unpack8(xq[u][m], xf[m]);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        if (r < nr) {
+          float wf[8];
+          unpack8(wq[u][r], wf);
+#pragma unroll
+          for (int m = 0; m < MM; ++m) {
             float a = acc[r][m];
 #pragma unroll
             for (int i = 0; i < 8; ++i) a = fmaf(xf[m][i], wf[i], a);
             acc[r][m] = a;
           }
+        }
       }
     }
   }
 #pragma unroll
-  for (int r = 0; r < 2 * kGvRB; ++r)
+  for (int r = 0; r < NR; ++r)
 #pragma unroll
-    for (int m = 0; m < kGvMaxRows; ++m)
-      if (r < nr && m < P.M) acc[r][m] = wave_sum_f32(acc[r][m]);
+    for (int m = 0; m < MM; ++m)
+      if (r < nr) acc[r][m] = wave_sum_f32(acc[r][m]);
   if (lane != 0) return;
 #pragma unroll
   for (int r = 0; r < kGvRB; ++r) {
     const int col = n0 + r;
     if (col >= P.ncols) continue;
 #pragma unroll
-    for (int m = 0; m < kGvMaxRows; ++m) {
-      if (m >= P.M) continue;
+    for (int m = 0; m < MM; ++m) {
+      if (m >= M) continue;
       if (swiglu) {
         ((uint16_t*)P.seg[0].out)[(size_t)m * P.seg[0].ldo + col] =
             bf_swiglu(acc[r][m], acc[kGvRB + r][m]);
@@ -225,13 +209,18 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemvBf16Params P) {
     }
   }
   const int kq = (lane >> 4) * 16;
-  for (size_t k0 = 0; k0 < KB; k0 += BKB) {
-    i32x4 ra[AP], rb[BP];
+  // the next step's operands are requested before this step's products, so
+  // one step of loads is always in flight behind the matrix instructions
+  i32x4 ra[AP], rb[BP];
+  auto load = [&](size_t k0) {
 #pragma unroll
     for (int p = 0; p < AP; ++p) ra[p] = asrc[p] ? *(const i32x4*)(asrc[p] + k0) : i32x4{0, 0, 0, 0};
 #pragma unroll
     for (int p = 0; p < BP; ++p)
       rb[p] = bsrc[p] ? __builtin_nontemporal_load((const i32x4*)(bsrc[p] + k0)) : i32x4{0, 0, 0, 0};
+  };
+  load(0);
+  for (size_t k0 = 0; k0 < KB; k0 += BKB) {
     __syncthreads();
 #pragma unroll
     for (int p = 0; p < AP; ++p)
@@ -240,6 +229,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemvBf16Params P) {
     for (int p = 0; p < BP; ++p)
       if (boff[p] >= 0) *(i32x4*)(Bs + boff[p]) = rb[p];
     __syncthreads();
+    if (k0 + BKB < KB) load(k0 + BKB);
     i32x4 fa[FM], fb[FN];
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
@@ -300,13 +290,22 @@ hipError_t launch_gemm_bf16(hipStream_t st, int M, int K, const uint16_t* x, int
     P.seg_start[i + 1] = P.seg_start[i] + segs[i].n;
   }
   P.ncols = (epi == BE_SWIGLU) ? segs[0].n : P.seg_start[nseg];
+  if (M >= 128 && ldx == K && (2 * K) % 64 == 0) return launch_gemm_big_bf16(st, M, K, x, segs, nseg, epi);
   if (M <= kGvMaxRows) {
     const int waves = (P.ncols + kGvRB - 1) / kGvRB;
-    hipLaunchKernelGGL(k_gemv_bf16, dim3((waves + 3) / 4), dim3(256), 0, st, P);
+    const dim3 g((waves + 3) / 4);
+    if (M == 1)
+      hipLaunchKernelGGL(k_gemv_bf16<1>, g, dim3(256), 0, st, P);
+    else if (M == 2)
+      hipLaunchKernelGGL(k_gemv_bf16<2>, g, dim3(256), 0, st, P);
+    else if (M <= 4)
+      hipLaunchKernelGGL(k_gemv_bf16<4>, g, dim3(256), 0, st, P);
+    else
+      hipLaunchKernelGGL(k_gemv_bf16<8>, g, dim3(256), 0, st, P);
   } else if (M <= 32) {
-    constexpr int BM = 32, BN = 128;
+    constexpr int BM = 32, BN = 64;
     const int tn = epi == BE_SWIGLU ? BN / 2 : BN;
-    hipLaunchKernelGGL((k_gemm_bf16<BM, BN, 1, 4>), dim3((P.ncols + tn - 1) / tn, (M + BM - 1) / BM),
+    hipLaunchKernelGGL((k_gemm_bf16<BM, BN, 2, 2>), dim3((P.ncols + tn - 1) / tn, (M + BM - 1) / BM),
                        dim3(256), 0, st, P);
   } else {
     constexpr int BM = 128, BN = 128;
@@ -317,30 +316,44 @@ hipError_t launch_gemm_bf16(hipStream_t st, int M, int K, const uint16_t* x, int
   return hipGetLastError();
 }
 
-// ---- RMSNorm: one wave per row; bf16(g * bf16(x / sqrt(mean(x^2) + eps)))
+// ---- RMSNorm: one workgroup per row, 16-byte loads;
+// bf16(g * bf16(x / sqrt(mean(x^2) + eps)))
 __global__ __launch_bounds__(256) void k_rmsnorm_bf16(int R, int H, const uint16_t* __restrict__ x,
                                                       int ldx, const uint16_t* __restrict__ g,
                                                       double eps, uint16_t* __restrict__ y) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= R) return;
+  __shared__ double red[4];
+  const int row = blockIdx.x, tid = threadIdx.x;
   const uint16_t* xr = x + (size_t)row * ldx;
+  const int NC = H / 8;
   double s = 0.0;
-  for (int i = lane; i < H; i += 64) {
-    const double v = bf2f(xr[i]);
-    s += v * v;
+  for (int c = tid; c < NC; c += 256) {
+    float f[8];
+    unpack8(*(const i32x4*)(xr + 8 * c), f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += (double)f[i] * (double)f[i];
   }
-  const double r = 1.0 / sqrt(wave_sum(s) / (double)H + eps);
+  s = block_sum<256>(s, red);
+  const double r = 1.0 / sqrt(s / (double)H + eps);
   uint16_t* yr = y + (size_t)row * H;
-  for (int i = lane; i < H; i += 64) {
-    const float t = rbf((float)((double)bf2f(xr[i]) * r));
-    yr[i] = f2bf((float)((double)t * (double)bf2f(g[i])));
+  for (int c = tid; c < NC; c += 256) {
+    float f[8], gf[8];
+    unpack8(*(const i32x4*)(xr + 8 * c), f);
+    unpack8(*(const i32x4*)(g + 8 * c), gf);
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t lo = f2bf((float)((double)rbf((float)((double)f[2 * i] * r)) * (double)gf[2 * i]));
+      const uint16_t hi =
+          f2bf((float)((double)rbf((float)((double)f[2 * i + 1] * r)) * (double)gf[2 * i + 1]));
+      o[i] = (uint32_t)lo | ((uint32_t)hi << 16);
+    }
+    *(i32x4*)(yr + 8 * c) = i32x4{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
   }
 }
 
 hipError_t launch_rmsnorm_bf16(hipStream_t st, int R, int H, const uint16_t* x, int ldx,
                                const uint16_t* g, double eps, uint16_t* y) {
-  hipLaunchKernelGGL(k_rmsnorm_bf16, dim3((R + 3) / 4), dim3(256), 0, st, R, H, x, ldx, g, eps, y);
+  hipLaunchKernelGGL(k_rmsnorm_bf16, dim3(R), dim3(256), 0, st, R, H, x, ldx, g, eps, y);
   return hipGetLastError();
 }
 

@@ -33,6 +33,8 @@
 namespace ark {
 
 typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8_t2 __attribute__((ext_vector_type(8)));
 
 struct Gemm2Params {
   int M, K, ncols, epi, rows_per_seq, nseg, tiles_m, tiles;
@@ -43,6 +45,11 @@ struct Gemm2Params {
   int seg_start[4];
   int32_t* acc_out;
   SeqStats stats;  // EPI_SWIGLU: per-sequence min/max of the output (cur == nullptr: off)
+  // bf16 operands (the instantiation with BF): A and the weight rows are bf16
+  // matrices read as bytes (K = 2 x the element count), the epilogue is
+  // bf_out / bf_swiglu over these segments
+  BSeg bs[3];
+  int bepi;
 };
 
 __device__ __forceinline__ void dma16(const int8_t* src, int8_t* lds_base) {
@@ -282,7 +289,70 @@ __device__ __forceinline__ void g2_epilogue(const Gemm2Params& P, i32x16 (&acc)[
 // at chunk c ^ ((r / (256 / BK)) % (BK / 16)), so the 16 rows of one
 // fragment read fall on all 64 banks).  128-byte rows make every request a
 // whole cache line, which streams markedly faster than 64-byte halves.
-template <int BM, int BN, int BK, int NS, int NTH>
+// Epilogue of the bf16 instantiation: fp32 sums of bf16 products, rounded
+// to bf16 by the variant's rules (bf_out), SwiGLU pairs by bf_swiglu.
+template <int FM, int FN>
+__device__ __forceinline__ void bf16_epilogue(const Gemm2Params& P, f32x16 (&acc)[FM][FN], int m0,
+                                              int nb, int wm, int wn, int lane) {
+  constexpr int RW = 64;
+  const bool swiglu = P.epi == EPI_SWIGLU;
+  const int lr = lane & 31, lc = lane >> 5;
+  const int rbase = m0 + wm * RW + lc * 4;
+  // output address, row stride and bias of each of this lane's columns,
+  // chosen once by selects (all indices into acc below are compile-time
+  // constants, so it stays in registers)
+  const int sb1 = P.nseg > 1 ? P.seg_start[1] : P.ncols;
+  const int sb2 = P.nseg > 2 ? P.seg_start[2] : P.ncols;
+  const int epi = P.bepi;
+  char* cout[FN];
+  int cldo[FN];
+  float cb[FN];
+  bool cok[FN];
+#pragma clang loop unroll(full)
+  for (int j = 0; j < FN; ++j) {
+    const int col = swiglu ? nb + (wn * (FN / 2) + j / 2) * 32 + lr : nb + wn * (FN * 32) + j * 32 + lr;
+    cok[j] = col < P.ncols;
+    const int cc = min(col, P.ncols - 1);
+    const bool in1 = cc >= sb1, in2 = cc >= sb2;
+    const int n = cc - (in2 ? sb2 : (in1 ? sb1 : 0));
+    const BSeg& S0 = P.bs[0];
+    const BSeg& S1 = P.bs[1];
+    const BSeg& S2 = P.bs[2];
+    char* base = (char*)(in2 ? S2.out : (in1 ? S1.out : S0.out));
+    const uint16_t* bias = in2 ? S2.bias : (in1 ? S1.bias : S0.bias);
+    cldo[j] = in2 ? S2.ldo : (in1 ? S1.ldo : S0.ldo);
+    cout[j] = base + (size_t)n * (epi == BE_F32 ? 4 : 2);
+    cb[j] = (bias && !swiglu && epi != BE_F32) ? bf2f(bias[n]) : 0.0f;
+  }
+#pragma clang loop unroll(full)
+  for (int i = 0; i < FM; ++i)
+#pragma clang loop unroll(full)
+    for (int v = 0; v < 16; ++v) {
+      const int row = rbase + i * 32 + (v >> 2) * 8 + (v & 3);
+      if (row < P.M) {
+        if (swiglu) {
+#pragma clang loop unroll(full)
+          for (int j = 0; j < FN; j += 2)
+            if (cok[j])
+              ((uint16_t*)cout[j])[(size_t)row * cldo[j]] = bf_swiglu(acc[i][j][v], acc[i][j + 1][v]);
+        } else if (epi == BE_F32) {
+#pragma clang loop unroll(full)
+          for (int j = 0; j < FN; ++j)
+            if (cok[j]) ((float*)cout[j])[(size_t)row * cldo[j]] = acc[i][j][v];
+        } else {
+#pragma clang loop unroll(full)
+          for (int j = 0; j < FN; ++j)
+            if (cok[j]) {
+              uint16_t* o = (uint16_t*)cout[j] + (size_t)row * cldo[j];
+              const float y = acc[i][j][v] + cb[j];
+              *o = epi == BE_RESID ? f2bf(bf2f(*o) + rbf(y)) : f2bf(y);
+            }
+        }
+      }
+    }
+}
+
+template <int BM, int BN, int BK, int NS, int NTH, bool BF = false>
 __global__ __launch_bounds__(NTH, NTH == 256 ? 2 : 1) void k_gemm_big(Gemm2Params P) {
   constexpr int NWV = NTH / 64;             // waves
   constexpr int RW = 64;                    // rows per wave
@@ -359,7 +429,8 @@ __global__ __launch_bounds__(NTH, NTH == 256 ? 2 : 1) void k_gemm_big(Gemm2Param
       dma16(bsrc[i] + k0, base + A_BYTES + (wave * B_INS + i) * 1024);
   };
 
-  i32x16 acc[FM][FN];
+  using AccT = typename std::conditional<BF, f32x16, i32x16>::type;
+  AccT acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -413,26 +484,34 @@ __global__ __launch_bounds__(NTH, NTH == 256 ? 2 : 1) void k_gemm_big(Gemm2Param
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
+          if constexpr (BF)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8_t2, fa[kk][i]), __builtin_bit_cast(bf16x8_t2, fb[kk][j]),
+                acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
   }
 
-  g2_epilogue<FM, FN>(P, acc, m0, nb, wm, wn, lane, blockIdx.x * NWV + wave);
+  if constexpr (BF)
+    bf16_epilogue<FM, FN>(P, acc, m0, nb, wm, wn, lane);
+  else
+    g2_epilogue<FM, FN>(P, acc, m0, nb, wm, wn, lane, blockIdx.x * NWV + wave);
 }
 
-template <int BM, int BN, int BK, int NS, int NTH>
+template <int BM, int BN, int BK, int NS, int NTH, bool BF = false>
 static hipError_t launch_big(hipStream_t st, Gemm2Params P) {
   constexpr int bytes = NS * (BM + BN) * BK;
   // one-time attribute set-up (a function-local static: initialised once,
   // thread-safe)
   static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)k_gemm_big<BM, BN, BK, NS, NTH>, hipFuncAttributeMaxDynamicSharedMemorySize,
+      (const void*)k_gemm_big<BM, BN, BK, NS, NTH, BF>, hipFuncAttributeMaxDynamicSharedMemorySize,
       bytes);
   if (attr != hipSuccess) return attr;
   const int tn = P.epi == EPI_SWIGLU ? BN / 2 : BN;
   P.tiles_m = (P.M + BM - 1) / BM;
   P.tiles = P.tiles_m * ((P.ncols + tn - 1) / tn);
   const int grid = 8 * ((P.tiles + 7) / 8);
-  hipLaunchKernelGGL((k_gemm_big<BM, BN, BK, NS, NTH>), dim3(grid), dim3(NTH), bytes, st, P);
+  hipLaunchKernelGGL((k_gemm_big<BM, BN, BK, NS, NTH, BF>), dim3(grid), dim3(NTH), bytes, st, P);
   return hipGetLastError();
 }
 
@@ -472,6 +551,31 @@ hipError_t launch_gemm_big(hipStream_t st, int M, int K, const int8_t* codes, co
   // 128 x 128 with 128-byte steps in two stages.
   if (epi != EPI_SWIGLU && M >= 1024) return launch_big<256, 256, 128, 2, 512>(st, P);
   return launch_big<128, 256, 64, 3, 256>(st, P);
+}
+
+// The bf16 variant's GEMM at 128+ rows on the same tiles: x [M][K] bf16
+// (row stride K), weight rows bf16; K counted in bytes for the byte-level
+// staging (one 32-byte K substep is one 32x32x16 bf16 instruction).
+hipError_t launch_gemm_big_bf16(hipStream_t st, int M, int K, const uint16_t* x, const BSeg* segs,
+                                int nseg, int epi) {
+  Gemm2Params P = {};
+  P.M = M;
+  P.K = 2 * K;
+  P.A = (const int8_t*)x;
+  P.rows_per_seq = M;
+  P.nseg = nseg;
+  P.epi = epi == BE_SWIGLU ? EPI_SWIGLU : EPI_STORE;
+  P.bepi = epi;
+  P.seg_start[0] = 0;
+  for (int i = 0; i < nseg; ++i) {
+    P.seg[i].w = (const int8_t*)segs[i].w;
+    P.seg[i].n = segs[i].n;
+    P.bs[i] = segs[i];
+    P.seg_start[i + 1] = P.seg_start[i] + segs[i].n;
+  }
+  P.ncols = (epi == BE_SWIGLU) ? segs[0].n : P.seg_start[nseg];
+  if (epi != BE_SWIGLU && M >= 1024) return launch_big<256, 256, 128, 2, 512, true>(st, P);
+  return launch_big<128, 256, 64, 3, 256, true>(st, P);
 }
 
 }  // namespace ark

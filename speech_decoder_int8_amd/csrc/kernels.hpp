@@ -413,6 +413,39 @@ struct BSeg {
   void* out;
   int n, ldo;
 };
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+// nearest even; NaN stays a (quiet) NaN
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((b >> 16) | 0x40u);
+  b += 0x7fffu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+__device__ __forceinline__ float rbf(float f) { return bf2f(f2bf(f)); }
+
+// ---- the epilogue of one output value
+// BE_STORE: bf16(acc + bias); BE_RESID: bf16(old + bf16(acc + bias));
+// BE_F32: fp32 acc (the logits); the SwiGLU pair is handled by the callers.
+__device__ __forceinline__ void bf_out(int epi, const BSeg& S, int row, int n, float acc) {
+  float y = acc;
+  if (epi == BE_F32) {
+    ((float*)S.out)[(size_t)row * S.ldo + n] = y;
+    return;
+  }
+  if (S.bias) y = y + bf2f(S.bias[n]);
+  uint16_t* o = (uint16_t*)S.out + (size_t)row * S.ldo + n;
+  if (epi == BE_RESID)
+    *o = f2bf(bf2f(*o) + rbf(y));
+  else
+    *o = f2bf(y);
+}
+// a = bf16(bf16(silu(bf16(g))) * bf16(u))
+__device__ __forceinline__ uint16_t bf_swiglu(float g, float u) {
+  const float gb = rbf(g), ub = rbf(u);
+  const float sg = rbf(gb / (1.0f + expf(-gb)));
+  return f2bf(sg * ub);
+}
+
 struct GemvBf16Params {
   int M, K, ldx, nseg, epi, ncols;
   const uint16_t* x;
@@ -425,6 +458,9 @@ bool gemm_bf16_supported(int K);
 // 0 gate, seg 1 up, result to seg 0's output)
 hipError_t launch_gemm_bf16(hipStream_t st, int M, int K, const uint16_t* x, int ldx,
                             const BSeg* segs, int nseg, int epi);
+// the same at M >= 128 rows on the large LDS-DMA tiles (x row stride K)
+hipError_t launch_gemm_big_bf16(hipStream_t st, int M, int K, const uint16_t* x, const BSeg* segs,
+                                int nseg, int epi);
 hipError_t launch_rmsnorm_bf16(hipStream_t st, int R, int H, const uint16_t* x, int ldx,
                                const uint16_t* g, double eps, uint16_t* y);
 hipError_t launch_rope_bf16(hipStream_t st, int B, int S, int NH, int NKV, const uint16_t* qkv,
