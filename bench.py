@@ -33,6 +33,7 @@ if ROOT not in sys.path:
 
 PEAK_HBM = 8.0e12        # MI355X HBM3E, bytes/s
 PEAK_INT8 = 5.0e15       # MI355X dense int8 MFMA, ops/s
+PEAK_BF16 = 2.5e15       # MI355X dense bf16 MFMA, flop/s
 
 
 def log(msg: str) -> None:
@@ -324,6 +325,8 @@ def gpu_bench(args):
         torch.cuda.empty_cache()
         # the audio encoder (3 s clip; sixteen 30 s clips)
         ex.update(encoder_bench(torch, ark, synth, cfg))
+        # the bf16 serving variant
+        ex.update(bf16_bench(torch, ark, synth, cfg))
         # prompt prefill of the 3 s clip
         t = timed(torch, lambda: run.prefill(x, [0]), reps=5)
         ex["prefill_c1_tok_s"] = round(S / t, 1)
@@ -402,6 +405,59 @@ def encoder_attn_flops(cfg, B: int, M: int) -> int:
     """fp64 flops of the encoder's attention products (QK^T and PV)."""
     F = (M - 1) // 2 + 1
     return 2 * 2 * B * cfg.enc_layers * cfg.enc_heads * F * F * (cfg.enc_dim // cfg.enc_heads)
+
+
+def decode_bytes_bf16(cfg) -> int:
+    """Bytes one bs1 step of the bf16 variant reads: bf16 weights, biases and
+    gains, the full-T bf16 cache of every layer, the LM head, one embedding
+    row, and the logits written."""
+    L, H, I, V, T = cfg.n_layers, cfg.hidden, cfg.intermediate, cfg.vocab, cfg.max_total_len
+    Q, KV = cfg.q_dim, cfg.kv_dim
+    per_layer = 2 * (Q * H + 2 * KV * H + H * Q + 3 * I * H + Q + 2 * KV + 2 * H)
+    return L * per_layer + L * 2 * T * KV * 2 + 2 * V * H + 2 * H + 2 * H + 4 * V
+
+
+def bf16_bench(torch, ark, synth, cfg):
+    """The bf16 serving variant: bs1 decode on the c1 prompt's cache length
+    and the 16 x 387 prefill."""
+    gm = ark.load_model_bf16(cfg, synth)
+    L, T = cfg.n_layers, cfg.max_total_len
+    ex = {}
+
+    def state(B, S):
+        kc = [torch.zeros((B, T, cfg.n_kv_heads, cfg.head_dim), dtype=torch.bfloat16, device="cuda")
+              for _ in range(L)]
+        vc = [torch.zeros_like(kc[0]) for _ in range(L)]
+        kd = torch.empty((L, B, S, cfg.n_kv_heads, cfg.head_dim), dtype=torch.bfloat16, device="cuda")
+        return kc, vc, kd, torch.empty_like(kd), torch.empty((B, cfg.vocab), device="cuda"), gm.workspace(B, S)
+
+    kc, vc, kd, vd, lg, ws = state(1, 1)
+    for l in range(L):
+        kc[l].normal_()
+        vc[l].normal_()
+    ids = torch.tensor([100], dtype=torch.int32, device="cuda")
+    p0 = cfg.prefill_len + 8
+    f = lambda: ark.decode_step_bf16(gm, ids, [p0], kc, vc, kd, vd, lg, None, ws)  # noqa: E731
+    f()
+    t = timed(torch, f, reps=16)
+    ex["bf16_decode_bs1_tok_s"] = round(1.0 / t, 1)
+    ex["bf16_decode_bs1_ms"] = round(t * 1e3, 3)
+    ex["bf16_decode_bs1_frac_of_8TBps"] = round(decode_bytes_bf16(cfg) / t / PEAK_HBM, 4)
+    del kc, vc, kd, vd, lg, ws
+    c4 = synth.CONFIGS["c4"]
+    B, S = c4.batch, c4.prefill_len
+    kc, vc, kd, vd, lg, ws = state(B, S)
+    x = torch.randn((B, S, cfg.hidden), device="cuda").to(torch.bfloat16)
+    f = lambda: ark.prefill_bf16(gm, x, [0] * B, kc, vc, kd, vd, lg, None, ws)  # noqa: E731
+    f()
+    t = timed(torch, f, reps=2)
+    flops = prefill_int8_ops(cfg, B * S, B)      # the same multiply-adds, in bf16
+    ex["bf16_prefill_16x387_ms"] = round(t * 1e3, 2)
+    ex["bf16_prefill_16x387_tok_s"] = round(B * S / t, 1)
+    ex["bf16_prefill_16x387_frac_of_2p5PFLOPs"] = round(flops / t / PEAK_BF16, 4)
+    del gm, kc, vc, kd, vd, lg, ws, x
+    torch.cuda.empty_cache()
+    return ex
 
 
 def encoder_bench(torch, ark, synth, cfg, reps=2):
