@@ -278,3 +278,86 @@ def test_encoder_per_clip_quantisation():
     both = oracle.encoder_forward(enc, mel)
     for b in range(3):
         assert np.array_equal(both[b], oracle.encoder_forward(enc, mel[b:b + 1])[0])
+
+
+def _gelu_tanh(x):
+    x64 = np.asarray(x, np.float32).astype(np.float64)
+    return (0.5 * x64 * (1 + np.tanh(math.sqrt(2 / math.pi) * (x64 + 0.044715 * x64 ** 3)))).astype(np.float32)
+
+
+def _rmsnorm_as_ln(x, g, b, eps=oracle.ENC_LN_EPS):
+    x64 = np.asarray(x, np.float32).astype(np.float64)
+    r = 1.0 / np.sqrt(np.mean(x64 * x64, axis=-1, keepdims=True) + eps)
+    return (x64 * r * g.astype(np.float64) + b.astype(np.float64)).astype(np.float32)
+
+
+def _interleaved_rope(x, pos, cos, sin):
+    # pairs (2j, 2j + 1) instead of (j, j + D/2)
+    D = x.shape[-1]
+    perm = np.concatenate([np.arange(0, D, 2), np.arange(1, D, 2)])
+    inv = np.argsort(perm)
+    return _ORIG["apply_rope"](x[..., perm], pos, cos, sin)[..., inv]
+
+
+def _per_row_dynquant(x):
+    x = np.asarray(x, np.float32)
+    rows = [_ORIG["dynquant"](x[i:i + 1]) for i in range(x.shape[0])]
+    return (np.concatenate([r[0] for r in rows]), np.array([r[1] for r in rows], np.float32)[:, None],
+            np.array([r[2] for r in rows], np.int32)[:, None])
+
+
+_ORIG = {}
+
+
+def _plants():
+    """Plausible slips in the oracle's encoder, each planted on the CPU by
+    replacing one function of oracle.ark (the encoder looks them up there)."""
+    import oracle.ark as oa
+
+    calls = {"n": 0}
+
+    def rope_q_only(x, pos, cos, sin):
+        calls["n"] += 1
+        return _ORIG["apply_rope"](x, pos, cos, sin) if calls["n"] % 2 else x
+
+    def attn_scale_1_over_d(q, k, v):
+        return _ORIG["enc_attention"](q / np.float32(np.sqrt(q.shape[-1])), k, v)
+
+    return {
+        "k not rotated": ("apply_rope", rope_q_only),
+        "rotary pairs interleaved": ("apply_rope", _interleaved_rope),
+        "scores scaled by 1/D": ("enc_attention", attn_scale_1_over_d),
+        "tanh GELU": ("gelu", _gelu_tanh),
+        "RMSNorm in place of LayerNorm": ("layernorm", _rmsnorm_as_ln),
+        "one (s, z) per frame": ("dynquant", _per_row_dynquant),
+    }, oa
+
+
+def test_brute_force_catches_planted_slips():
+    """Every slip above moves the oracle's encoder output past the 1e-5 bar
+    of the brute-force comparison, and the positional rows matter too.  The
+    features are scaled up so that the first GELU sees inputs of order one
+    (with the seeded 0.02 weights its inputs are otherwise near zero, where
+    the erf and tanh forms agree to 1e-7)."""
+    cfg = synth.TINY.with_(batch=1)
+    mel = synth.mel_features(cfg) * np.float32(30.0)
+    want = np.array(bf_encoder(cfg, mel[0].tolist()), np.float32)
+
+    def err(enc):
+        got = oracle.encoder_forward(enc, mel)[0]
+        return float(np.max(np.abs(got.astype(np.float64) - want)) / np.max(np.abs(want)))
+
+    enc = oracle.build_encoder(cfg, synth)
+    assert err(enc) <= 1e-5
+    plants, oa = _plants()
+    for name, (fn, repl) in plants.items():
+        _ORIG[fn] = getattr(oa, fn)
+        setattr(oa, fn, repl)
+        try:
+            e = err(enc)
+        finally:
+            setattr(oa, fn, _ORIG[fn])
+        assert e > 1e-4, (name, e)
+    nopos = oracle.build_encoder(cfg, synth)
+    nopos.pos = np.zeros_like(nopos.pos)
+    assert err(nopos) > 1e-4
