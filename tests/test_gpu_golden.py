@@ -91,3 +91,74 @@ def test_full_size_against_golden(name):
     print(f"{name}: {cfg.n_decode + (1 if cfg.prefill_len else 0)} steps, near ties: {near}")
     del gs, gm
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
+def test_full_size_free_running_greedy(name):
+    """The native greedy loop (ark_greedy_decode: the persistent kernel at
+    batch 1, the multi-kernel path above) run free on its own tokens from the
+    same start as the oracle's free-running loop stored in the golden file.
+    Every id must equal the oracle's; a different id is accepted only where
+    the oracle's top-2 gap lies within twice the logit tolerance (a near
+    tie), and that sequence, now on the other branch, is compared no
+    further."""
+    g = _golden(name)
+    cfg = synth.CONFIGS[name]
+    gm = ark.load_model(cfg, synth)
+    B, L = cfg.batch, cfg.n_layers
+    mask = cfg.mask()
+    gs = GpuState(gm, B, max(1, cfg.prefill_len))
+    frm = int(g.get("top_vals_from", 0))
+    live = np.ones(B, bool)        # sequences still compared
+    compared = 0
+    released = []
+
+    def follow(step, got):
+        nonlocal compared
+        k = step - frm
+        scale = float(np.max(np.abs(g["top_vals"][k])))
+        want = g["tokens"][step]
+        for b in np.nonzero(live)[0]:
+            compared += 1
+            if got[b] != want[b]:
+                gap = float(g["gap"][k][b])
+                assert gap <= 2 * TOL * scale, f"{name} step {step} seq {b}: {got[b]} != {want[b]}, gap {gap:.3g}"
+                live[b] = False
+                released.append((step, int(b), gap))
+
+    if cfg.prefill_len:
+        if cfg.prefill_from_embeds:
+            x = t(synth.prefill_embeds(cfg))
+        else:
+            x = torch.empty((B, cfg.prefill_len, cfg.hidden), dtype=torch.float32, device="cuda")
+            ark.embed_splice(gm.dims, t(synth.prompt_ids(cfg)), gm.embed_f16,
+                             t(synth.audio_rows(cfg)), cfg.audio_offset, x)
+        p = np.zeros(B, np.int64)
+        kd, vd, _ = gs.prefill(x, p)
+        tok = torch.empty(B, dtype=torch.int32, device="cuda")
+        ark.masked_argmax(gs.logits, t(mask), tok)
+        follow(0, host(tok))
+        gs.write_back(p, kd, vd)
+        p = p + cfg.prefill_len
+        del x
+    else:
+        lengths = synth.cache_lengths(cfg)
+        for l in range(L):
+            gs.kc[l].copy_(t(synth.prefilled_cache(cfg, l, "k", lengths)))
+            gs.vc[l].copy_(t(synth.prefilled_cache(cfg, l, "v", lengths)))
+        p = lengths.astype(np.int64)
+        tok = t(g["tokens"][0].astype(np.int32))
+    steps = cfg.n_decode
+    out = torch.empty((steps, B), dtype=torch.int32, device="cuda")
+    kd1, vd1 = gs.deltas(1)
+    ws1 = ark.workspace(gm, B, 1)
+    n, newpos = ark.greedy_decode(gm, tok, [int(v) for v in p], gs.kc, gs.vc, kd1, vd1, gs.logits,
+                                  t(mask), -1, steps, out, ws=ws1, check_every=steps)
+    assert n == steps and newpos.tolist() == [int(v) + steps for v in p]
+    got = host(out)
+    for s in range(steps):
+        follow(s + 1, got[s])
+    print(f"{name}: {compared} greedy ids compared with the oracle's free-running loop; "
+          f"sequences released at near ties: {released}")
+    del gs, gm
+    torch.cuda.empty_cache()
