@@ -13,7 +13,9 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libark.so")
+# ARK_LIBRARY selects another build of the same library (one built with host
+# sanitizers, for instance); by default the one built in-tree.
+LIB_PATH = os.environ.get("ARK_LIBRARY") or os.path.join(HERE, "libark.so")
 
 ARK_OK, ARK_E_NULL, ARK_E_SHAPE, ARK_E_RANGE, ARK_E_WORKSPACE, ARK_E_HIP, ARK_E_ALIGN = \
     0, -1, -2, -3, -4, -5, -6
