@@ -29,11 +29,16 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 namespace a2 {
 constexpr int KC = 64;    // keys per chunk
-constexpr int KP = 132;   // K row pitch (floats): 16 keys x 4 dims reads hit distinct banks
-constexpr int VP = 128;   // V row pitch (floats)
+// The chunk is staged widened to fp64 once for all waves (the matrix
+// operands are then read as they are, without a conversion per wave).
+// Row pitches in doubles: an 8-byte fragment read of K (16 keys x 2 dims
+// per half wave) and of V (16 dims x 2 keys per half wave) touches each
+// LDS bank once per half wave.
+constexpr int KP = 130;
+constexpr int VP = 144;
 constexpr int QT = 16;    // query rows per workgroup
 constexpr int GMAX = 8;   // query heads per KV head
-constexpr int LDS_BYTES = KC * KP * 4 + KC * VP * 4;
+constexpr int LDS_BYTES = KC * KP * 8 + KC * VP * 8;
 }  // namespace a2
 
 struct Attn2Params {
@@ -48,11 +53,17 @@ struct Attn2Params {
   SeqStats stats;  // per-sequence min/max of out (cur == nullptr: off)
 };
 
+// four fp32 values widened into LDS (exact)
+__device__ __forceinline__ void put4(double* dst, float4 v) {
+  *(double2*)dst = double2{(double)v.x, (double)v.y};
+  *(double2*)(dst + 2) = double2{(double)v.z, (double)v.w};
+}
+
 __global__ __launch_bounds__(512) void k_attn_prefill(Attn2Params P) {
   using namespace a2;
   extern __shared__ __align__(16) unsigned char smem[];
-  float* Ks = (float*)smem;                      // [KC][KP]
-  float* Vs = Ks + KC * KP;                      // [KC][VP]
+  double* Ks = (double*)smem;                    // [KC][KP]
+  double* Vs = Ks + KC * KP;                     // [KC][VP]
   if (P.stats.cur) stats_clear_other(P.stats);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -94,30 +105,54 @@ __global__ __launch_bounds__(512) void k_attn_prefill(Attn2Params P) {
   const SwigluK EK = swiglu_consts();  // constants of the exponential below
 
   const int nch = maxq / KC + 1;
+  // float4 e of a chunk (key jj = e / 32, dims 4 (e % 32) ..) from the cache
+  // or this call's deltas; zero past the rows any query sees
+  // (the four base pointers are wave-uniform values: a per-lane choice
+  // between them is a select, not a load of the parameter block)
+  const gptr<const float> kcp = uniform_ptr(P.kc), vcp = uniform_ptr(P.vc);
+  const gptr<const float> kdp = uniform_ptr(P.kd), vdp = uniform_ptr(P.vd);
+  auto fetch = [&](int j0, int e, float4& kv, float4& vv) {
+    const int jj = e >> 5, d4 = e & 31;
+    const int j = j0 + jj;
+    kv = make_float4(0.f, 0.f, 0.f, 0.f);
+    vv = kv;
+    if (j < live_end) {
+      const bool dl = j >= p;  // this call's rows come from the deltas
+      const size_t off = dl ? ((size_t)(b * S + (j - p)) * P.NKV + g) * kHeadDim
+                            : ((size_t)(b * T + j) * P.NKV + g) * kHeadDim;
+      kv = ld4((dl ? kdp : kcp) + off, d4);
+      vv = ld4((dl ? vdp : vcp) + off, d4);
+    }
+  };
+  // with 512 threads (8 query heads) each thread holds 4 float4 of K and of V
+  // of the next chunk in registers while the current one is computed
+  constexpr int PF = KC * (kHeadDim / 4) / 512;
+  const bool piped = nthr == 512;
+  float4 kn[PF], vn[PF];
+  if (piped)
+#pragma unroll
+    for (int u = 0; u < PF; ++u) fetch(0, tid + 512 * u, kn[u], vn[u]);
   for (int c = 0; c < nch; ++c) {
     const int j0 = c * KC;
     __syncthreads();  // the previous chunk's K, V and P are used
-    for (int e = tid; e < KC * (kHeadDim / 4); e += nthr) {
-      const int jj = e >> 5, d4 = e & 31;
-      const int j = j0 + jj;
-      float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
-      if (j < live_end) {
-        size_t off;
-        const float *ks, *vs;
-        if (j >= p) {
-          off = ((size_t)(b * S + (j - p)) * P.NKV + g) * kHeadDim;
-          ks = P.kd;
-          vs = P.vd;
-        } else {
-          off = ((size_t)(b * T + j) * P.NKV + g) * kHeadDim;
-          ks = P.kc;
-          vs = P.vc;
-        }
-        kv = ((const float4*)(ks + off))[d4];
-        vv = ((const float4*)(vs + off))[d4];
+    if (piped) {
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+        const int e = tid + 512 * u, jj = e >> 5, d4 = e & 31;
+        put4(Ks + jj * KP + 4 * d4, kn[u]);
+        put4(Vs + jj * VP + 4 * d4, vn[u]);
       }
-      *(float4*)(Ks + jj * KP + 4 * d4) = kv;
-      *(float4*)(Vs + jj * VP + 4 * d4) = vv;
+      if (c + 1 < nch)
+#pragma unroll
+        for (int u = 0; u < PF; ++u) fetch(j0 + KC, tid + 512 * u, kn[u], vn[u]);
+    } else {
+      for (int e = tid; e < KC * (kHeadDim / 4); e += nthr) {
+        float4 kv, vv;
+        fetch(j0, e, kv, vv);
+        const int jj = e >> 5, d4 = e & 31;
+        put4(Ks + jj * KP + 4 * d4, kv);
+        put4(Vs + jj * VP + 4 * d4, vv);
+      }
     }
     __syncthreads();
 
@@ -126,10 +161,10 @@ __global__ __launch_bounds__(512) void k_attn_prefill(Attn2Params P) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       sc[kb] = f64x4{0.0, 0.0, 0.0, 0.0};
-      const float* kr = Ks + (16 * kb + c16) * KP + q4;
+      const double* kr = Ks + (16 * kb + c16) * KP + q4;
 #pragma unroll
       for (int s = 0; s < 32; ++s)
-        sc[kb] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kr[4 * s], qv[s], sc[kb], 0, 0, 0);
+        sc[kb] = __builtin_amdgcn_mfma_f64_16x16x4f64(kr[4 * s], qv[s], sc[kb], 0, 0, 0);
     }
     double cmax = -INFINITY;
 #pragma unroll
@@ -165,10 +200,10 @@ __global__ __launch_bounds__(512) void k_attn_prefill(Attn2Params P) {
 #pragma unroll
     for (int t = 0; t < KC / 4; ++t) {
       const double pb = sc[t >> 2][t & 3];
-      const float* vr = Vs + (4 * t + q4) * VP + c16;
+      const double* vr = Vs + (4 * t + q4) * VP + c16;
 #pragma unroll
       for (int d = 0; d < 8; ++d)
-        o[d] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)vr[16 * d], pb, o[d], 0, 0, 0);
+        o[d] = __builtin_amdgcn_mfma_f64_16x16x4f64(vr[16 * d], pb, o[d], 0, 0, 0);
     }
   }
   // o[d][i] = O^T[dim 16 d + 4 i + q4][qrow]

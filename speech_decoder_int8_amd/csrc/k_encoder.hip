@@ -99,12 +99,17 @@ hipError_t launch_layernorm(hipStream_t st, int R, int D, int rows_per_seq, cons
 // Keys past the clip's F frames score -inf (no other mask: every frame sees
 // every frame).  Rotary pairs are (d, d + 32); q and k are rotated in fp64
 // and rounded to fp32 (the tensors the method's rotary step produces), then
-// widened for the products.
+// widened: the chunk is staged in LDS as fp64 once for the 8 waves, and the
+// next chunk's rows are fetched into registers while the current one is
+// used.
 namespace ea {
 constexpr int DH = 64;    // head dim
 constexpr int KC = 64;    // keys per chunk
-constexpr int KP = 68;    // K row pitch (floats): 16 keys x 4 dims of a fragment read hit distinct banks
-constexpr int VP = 80;    // V row pitch (floats): 4 keys x 16 dims hit distinct banks
+// row pitches in doubles: an 8-byte fragment read of K (16 keys x 2 dims per
+// half wave) and of V (16 dims x 2 keys per half wave) touches each LDS bank
+// once per half wave
+constexpr int KP = 66;
+constexpr int VP = 80;
 constexpr int QT = 16;    // query rows per wave
 constexpr int NW = 8;     // waves (query tiles) per workgroup
 }  // namespace ea
@@ -118,10 +123,13 @@ struct EncAttnParams {
   SeqStats stats;
 };
 
+constexpr int ENC_ATTN_LDS = (ea::KC * ea::KP + ea::KC * ea::VP) * 8;
+
 __global__ __launch_bounds__(512) void k_enc_attn(EncAttnParams P) {
   using namespace ea;
-  __shared__ __align__(16) float Ks[KC * KP];
-  __shared__ __align__(16) float Vs[KC * VP];
+  extern __shared__ __align__(16) unsigned char esm[];
+  double* Ks = (double*)esm;       // [KC][KP]
+  double* Vs = Ks + KC * KP;       // [KC][VP]
   if (P.stats.cur) stats_clear_other(P.stats);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = blockIdx.x % P.ngrp;
@@ -160,49 +168,65 @@ __global__ __launch_bounds__(512) void k_enc_attn(EncAttnParams P) {
   const SwigluK EK = swiglu_consts();
 
   const int nch = (F + KC - 1) / KC;
+  // 64 keys x 8 pairs of float4 (dims 4 p .. 4 p + 3 with their partners 32
+  // on): one item per thread, fetched a chunk ahead
+  const int jj = tid >> 3, p4 = tid & 7;
+  float4 k0, k1, va, vb;
+  double cc[4], sn[4];
+  auto fetch = [&](int j0) {
+    const int j = min(j0 + jj, F - 1);  // rows past F are zeroed when staged
+    const float* kr = base + (size_t)j * W3 + P.H * DH + h * DH;
+    const float* vr = kr + P.H * DH;
+    k0 = ((const float4*)kr)[p4];
+    k1 = ((const float4*)kr)[p4 + 8];
+    va = ((const float4*)vr)[p4];
+    vb = ((const float4*)vr)[p4 + 8];
+    const double* cr = P.cos + (size_t)j * (DH / 2) + 4 * p4;
+    const double* sr = P.sin + (size_t)j * (DH / 2) + 4 * p4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      cc[e] = cr[e];
+      sn[e] = sr[e];
+    }
+  };
+  fetch(0);
   for (int c = 0; c < nch; ++c) {
     const int j0 = c * KC;
     __syncthreads();  // the previous chunk's K and V are used
     {
-      // 64 keys x 8 pairs of float4 (dims 4 p .. 4 p + 3 with their
-      // partners 32 on): one item per thread
-      const int jj = tid >> 3, p4 = tid & 7;
-      const int j = j0 + jj;
-      float4 ka = make_float4(0.f, 0.f, 0.f, 0.f), kb = ka, va = ka, vb = ka;
-      if (j < F) {
-        const float* kr = base + (size_t)j * W3 + P.H * DH + h * DH;
-        const float* vr = kr + P.H * DH;
-        const float4 k0 = ((const float4*)kr)[p4], k1 = ((const float4*)kr)[p4 + 8];
-        va = ((const float4*)vr)[p4];
-        vb = ((const float4*)vr)[p4 + 8];
-        const double* cr = P.cos + (size_t)j * (DH / 2) + 4 * p4;
-        const double* sr = P.sin + (size_t)j * (DH / 2) + 4 * p4;
-        const float a[4] = {k0.x, k0.y, k0.z, k0.w}, bq[4] = {k1.x, k1.y, k1.z, k1.w};
-        float ra[4], rb[4];
+      const bool live = j0 + jj < F;
+      const float a[4] = {k0.x, k0.y, k0.z, k0.w}, bq[4] = {k1.x, k1.y, k1.z, k1.w};
+      const float v0[4] = {va.x, va.y, va.z, va.w}, v1[4] = {vb.x, vb.y, vb.z, vb.w};
+      double ka[4], kb[4], wa[4], wb[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const double cc = cr[e], ss = sr[e];
-          ra[e] = (float)((double)a[e] * cc - (double)bq[e] * ss);
-          rb[e] = (float)((double)bq[e] * cc + (double)a[e] * ss);
-        }
-        ka = make_float4(ra[0], ra[1], ra[2], ra[3]);
-        kb = make_float4(rb[0], rb[1], rb[2], rb[3]);
+      for (int e = 0; e < 4; ++e) {
+        ka[e] = live ? (double)(float)((double)a[e] * cc[e] - (double)bq[e] * sn[e]) : 0.0;
+        kb[e] = live ? (double)(float)((double)bq[e] * cc[e] + (double)a[e] * sn[e]) : 0.0;
+        wa[e] = live ? (double)v0[e] : 0.0;
+        wb[e] = live ? (double)v1[e] : 0.0;
       }
-      *(float4*)(Ks + jj * KP + 4 * p4) = ka;
-      *(float4*)(Ks + jj * KP + 4 * p4 + 32) = kb;
-      *(float4*)(Vs + jj * VP + 4 * p4) = va;
-      *(float4*)(Vs + jj * VP + 4 * p4 + 32) = vb;
+      double* kd = Ks + jj * KP + 4 * p4;
+      double* vd = Vs + jj * VP + 4 * p4;
+      *(double2*)kd = double2{ka[0], ka[1]};
+      *(double2*)(kd + 2) = double2{ka[2], ka[3]};
+      *(double2*)(kd + 32) = double2{kb[0], kb[1]};
+      *(double2*)(kd + 34) = double2{kb[2], kb[3]};
+      *(double2*)vd = double2{wa[0], wa[1]};
+      *(double2*)(vd + 2) = double2{wa[2], wa[3]};
+      *(double2*)(vd + 32) = double2{wb[0], wb[1]};
+      *(double2*)(vd + 34) = double2{wb[2], wb[3]};
     }
+    if (c + 1 < nch) fetch(j0 + KC);
     __syncthreads();
 
     f64x4_t sc[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       sc[kb] = f64x4_t{0.0, 0.0, 0.0, 0.0};
-      const float* kr = Ks + (16 * kb + c16) * KP + q4;
+      const double* kr = Ks + (16 * kb + c16) * KP + q4;
 #pragma unroll
       for (int s = 0; s < 16; ++s)
-        sc[kb] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kr[4 * s], qv[s], sc[kb], 0, 0, 0);
+        sc[kb] = __builtin_amdgcn_mfma_f64_16x16x4f64(kr[4 * s], qv[s], sc[kb], 0, 0, 0);
     }
     double cmax = -INFINITY;
 #pragma unroll
@@ -236,10 +260,10 @@ __global__ __launch_bounds__(512) void k_enc_attn(EncAttnParams P) {
 #pragma unroll
     for (int t = 0; t < KC / 4; ++t) {
       const double pb = sc[t >> 2][t & 3];
-      const float* vr = Vs + (4 * t + q4) * VP + c16;
+      const double* vr = Vs + (4 * t + q4) * VP + c16;
 #pragma unroll
       for (int d = 0; d < 4; ++d)
-        o[d] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)vr[16 * d], pb, o[d], 0, 0, 0);
+        o[d] = __builtin_amdgcn_mfma_f64_16x16x4f64(vr[16 * d], pb, o[d], 0, 0, 0);
     }
   }
   // o[d][i] = O^T[dim 16 d + 4 i + q4][qrow]
@@ -266,6 +290,11 @@ __global__ __launch_bounds__(512) void k_enc_attn(EncAttnParams P) {
 hipError_t launch_enc_attention(hipStream_t st, int B, int F, int H, const float* qkv,
                                 const double* cos, const double* sin, float* out,
                                 const SeqStats& S) {
+  // one-time attribute set-up (a function-local static: initialised once,
+  // thread-safe)
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)k_enc_attn, hipFuncAttributeMaxDynamicSharedMemorySize, ENC_ATTN_LDS);
+  if (attr != hipSuccess) return attr;
   EncAttnParams P = {};
   P.B = B;
   P.F = F;
@@ -277,7 +306,7 @@ hipError_t launch_enc_attention(hipStream_t st, int B, int F, int H, const float
   P.sin = sin;
   P.out = out;
   P.stats = S;
-  hipLaunchKernelGGL(k_enc_attn, dim3(B * H * P.ngrp), dim3(64 * ea::NW), 0, st, P);
+  hipLaunchKernelGGL(k_enc_attn, dim3(B * H * P.ngrp), dim3(64 * ea::NW), ENC_ATTN_LDS, st, P);
   return hipGetLastError();
 }
 
