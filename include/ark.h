@@ -326,10 +326,15 @@ int ark_prefill(const ark_model* m, int32_t B, int32_t S, const float* embeds,
  * gathered from m->embed_f16, then the same computation as ark_prefill.
  * k_delta, v_delta: [n_layers][B][1][n_kv][128].  Other arguments and
  * errors as ark_prefill with S = 1.  At B = 1 with the ARK geometry the
- * step is one persistent cooperative kernel (ark_decode_path) whose
- * workgroups exchange data through bounded waits; the return value reports
+ * step is one persistent kernel (ark_decode_path) whose 256 workgroups, one
+ * per CU, exchange data through bounded waits; the return value reports
  * only the launch, so a caller that needs to know that every wait was met
- * calls ark_decode_check afterwards. */
+ * calls ark_decode_check afterwards.  The kernel is launched as an ordinary
+ * kernel: its workgroups are all resident at once when no kernel on
+ * another stream holds CUs, and one held longer than the wait bound ends
+ * the step with ARK_E_TIMEOUT.  The environment variable ARK_DECODE_LAUNCH
+ * set to "cooperative" selects a cooperative launch, which guarantees
+ * residency at a cost of about 20 us per step. */
 int ark_decode_step(const ark_model* m, int32_t B, const int32_t* token_ids,
                     const int32_t* cache_position, const float* const* k_cache,
                     const float* const* v_cache, float* k_delta, float* v_delta,

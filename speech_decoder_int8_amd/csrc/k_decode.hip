@@ -1,6 +1,6 @@
 // Persistent decode step for the ARK-ASR-3B geometry at batch 1.
 //
-// One cooperative launch runs all 36 layers and the LM head of a decode
+// One launch runs all 36 layers and the LM head of a decode
 // token (model card "ark-asr-3b-onnx", sections Shapes and Files: hidden
 // 2048, 16 query / 2 KV heads of 128, int8 per-channel MatMuls with dynamic
 // activation quantisation, full static-cache attention, int8 LM head).
@@ -25,9 +25,18 @@
 // write-back/invalidate fence is needed.  The tag is a per-launch epoch kept
 // in the workspace, so words of earlier launches never match.  Every wait is
 // bounded: on time-out the kernel records an error and runs to completion.
+//
+// Residency: the exchanges need all 256 workgroups on the device at once.
+// One fits per CU (decode_mega_init checks it), so an ordinary launch on a
+// GPU that is not running another kernel places them all at once; a
+// kernel on another stream that holds CUs only delays the late
+// workgroups, and a delay beyond the wait bound ends the step with the
+// time-out error.  ARK_DECODE_LAUNCH=cooperative selects the cooperative
+// launch, which guarantees residency at about 20 us more per launch.
 #include <float.h>
 #include <limits.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include <algorithm>
 #include <mutex>
@@ -1885,6 +1894,11 @@ hipError_t decode_mega_upload(hipStream_t st, void* ws, int L, int T, const Mega
   return hipMemcpyAsync(lay.table, tab, sizeof(mk::LayerW) * L, hipMemcpyHostToDevice, st);
 }
 
+bool decode_mega_cooperative() {
+  const char* e = getenv("ARK_DECODE_LAUNCH");
+  return e && strcmp(e, "cooperative") == 0;
+}
+
 hipError_t decode_mega_launch(hipStream_t st, void* ws, const MegaStep& S, hipEvent_t ev_begin,
                               hipEvent_t ev_end) {
   MegaLayout lay = mega_layout(ws, S.L, S.T);
@@ -1934,7 +1948,9 @@ hipError_t decode_mega_launch(hipStream_t st, void* ws, const MegaStep& S, hipEv
   void* args[] = {&A};
   if (ev_begin) hipEventRecord(ev_begin, st);
   const void* fn = S.dump.base ? (const void*)mk::k_decode<true> : (const void*)mk::k_decode<false>;
-  e = hipLaunchCooperativeKernel(fn, dim3(mk::NWG), dim3(mk::NT), args, sizeof(mk::Shared), st);
+  e = decode_mega_cooperative()
+          ? hipLaunchCooperativeKernel(fn, dim3(mk::NWG), dim3(mk::NT), args, sizeof(mk::Shared), st)
+          : hipLaunchKernel(fn, dim3(mk::NWG), dim3(mk::NT), args, sizeof(mk::Shared), st);
   if (ev_end) hipEventRecord(ev_end, st);
   return e;
 }
@@ -1952,7 +1968,8 @@ size_t decode_mega_trace_offset(int L, int T) {
 
 // One-time set-up of both instantiations (the record-writing one only for
 // the parity tests): dynamic LDS size, and the check that all NWG
-// workgroups fit on the device at once, which the exchanges rely on.
+// workgroups fit on the device at once, which the exchanges rely on (and
+// that the device can launch them cooperatively, for ARK_DECODE_LAUNCH).
 // Thread-safe: std::call_once.
 hipError_t decode_mega_init() {
   static std::once_flag once;

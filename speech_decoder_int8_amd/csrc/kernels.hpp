@@ -390,6 +390,8 @@ bool decode_mega_supported(int H, int NH, int NKV, int D, int I, int T, int L);
 size_t decode_mega_ws_bytes(int L, int T);
 size_t decode_mega_trace_offset(int L, int T);
 hipError_t decode_mega_init();
+// ARK_DECODE_LAUNCH=cooperative: launch the persistent step cooperatively
+bool decode_mega_cooperative();
 hipError_t decode_mega_upload(hipStream_t st, void* ws, int L, int T, const MegaLayer* layers);
 // ev_begin / ev_end (nullable) are recorded around the persistent kernel
 // alone (not its preparation kernel).

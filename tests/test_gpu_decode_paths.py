@@ -25,13 +25,19 @@ def models():
     return oracle.build_model(CFG, synth), ark.load_model(CFG, synth)
 
 
-@pytest.fixture(params=["mega", "multi"])
+# "mega": the persistent kernel as an ordinary launch (the default);
+# "mega_coop": the same kernel launched cooperatively (ARK_DECODE_LAUNCH)
+@pytest.fixture(params=["mega", "mega_coop", "multi"])
 def path(request, monkeypatch):
     if request.param == "multi":
         monkeypatch.setenv("ARK_DECODE_PATH", "multi")
     else:
         monkeypatch.delenv("ARK_DECODE_PATH", raising=False)
-    return request.param
+    if request.param == "mega_coop":
+        monkeypatch.setenv("ARK_DECODE_LAUNCH", "cooperative")
+    else:
+        monkeypatch.delenv("ARK_DECODE_LAUNCH", raising=False)
+    return "mega" if request.param.startswith("mega") else "multi"
 
 
 def _caches(cfg, lengths, rng):
