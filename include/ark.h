@@ -483,8 +483,11 @@ int ark_cache_write(const ark_dims* d, int32_t B, int32_t S, const int32_t* cach
  * check_every (>= 1): the host reads the finished flags every this many
  * steps; larger values avoid a host round trip per step but may run up to
  * check_every - 1 steps after the last sequence finished.  On the
- * persistent path the kernel's error word is read at the same points and at
- * the end: a timed-out wait returns ARK_E_TIMEOUT instead of a count. */
+ * persistent path the kernel's error word is cleared once per call and read
+ * at the same points and at the end: a wait that timed out in any step
+ * returns ARK_E_TIMEOUT instead of a count.  On that path the write-back,
+ * the stop rule and the next step's preparation run as one small kernel
+ * between two persistent launches. */
 int ark_greedy_decode(const ark_model* m, int32_t B, int32_t* token_ids,
                       int32_t* cache_position, float* const* k_cache,
                       float* const* v_cache, float* k_delta, float* v_delta,

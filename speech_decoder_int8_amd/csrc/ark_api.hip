@@ -502,7 +502,7 @@ int64_t mega_spin_limit() {
 
 int mega_step(const ark_model* m, const int32_t* token, int pos, float* kd, float* vd,
               float* logits, float* hidden_out, const uint8_t* mask, int32_t* out_token, char* ws,
-              hipStream_t st, const DumpRec* dr = nullptr) {
+              hipStream_t st, const DumpRec* dr = nullptr, bool prep = true) {
   const ark_dims& d = m->d;
   const Plan p = plan(d, 1, 1);
   // int4 tier: the kernel's tail runs the final norm, the int4 head and
@@ -536,7 +536,28 @@ int mega_step(const ark_model* m, const int32_t* token, int pos, float* kd, floa
   S.spin_limit = mega_spin_limit();
   hipEvent_t eb = nullptr, ee = nullptr;
   prof_claim(eb, ee);
-  const hipError_t e = decode_mega_launch(st, ws + p.mega, S, eb, ee);
+  const hipError_t e = decode_mega_launch(st, ws + p.mega, S, eb, ee, prep);
+  return e == hipSuccess ? ARK_OK : ARK_E_HIP;
+}
+
+// After a greedy step on the persistent path: cache write-back of its
+// deltas, the stop rule, and (prep) the next step's preparation.
+int mega_between(const ark_model* m, int32_t* token, int pos, float* kd, float* vd,
+                 float* const* kc, float* const* vc, int32_t* out_row, int32_t end_id,
+                 int32_t* done, char* ws, hipStream_t st, bool prep) {
+  const ark_dims& d = m->d;
+  const Plan p = plan(d, 1, 1);
+  MegaStep S;
+  memset(&S, 0, sizeof(S));
+  S.L = d.n_layers;
+  S.T = d.max_total_len;
+  S.V = d.vocab;
+  S.pos = pos;
+  S.token = token;
+  S.table = m->embed_f16;
+  S.kdelta = kd;
+  S.vdelta = vd;
+  const hipError_t e = decode_mega_between(st, ws + p.mega, S, kc, vc, out_row, end_id, done, prep);
   return e == hipSuccess ? ARK_OK : ARK_E_HIP;
 }
 
@@ -1354,15 +1375,23 @@ int ark_greedy_decode(const ark_model* m, int32_t B, int32_t* token_ids, int32_t
   if (mega && (e = mega_upload(m, (const float* const*)k_cache, (const float* const*)v_cache, ws, st)))
     return e;
   int steps = 0;
+  bool prepared = false;  // the next persistent launch is prepared already
   for (int t = 0; t < max_steps; ++t) {
     bool room = true;
     for (int b = 0; b < B; ++b) room = room && pos[b] + 1 <= T;
     if (!room) break;
     if (mega) {
-      // one persistent kernel computes the logits and the masked greedy id
+      // one persistent kernel computes the logits and the masked greedy id;
+      // one small kernel then writes its deltas back, applies the stop rule
+      // and prepares the next launch
       e = mega_step(m, token_ids, pos[0], k_delta, v_delta, logits, nullptr, mask, token_ids, ws,
-                    st);
+                    st, nullptr, !prepared);
       if (e) return e;
+      const bool next = t + 1 < max_steps && pos[0] + 2 <= T;
+      e = mega_between(m, token_ids, pos[0], k_delta, v_delta, k_cache, v_cache,
+                       out_tokens + (size_t)t * B, end_id, done, ws, st, next);
+      if (e) return e;
+      prepared = next;
     } else {
       e = ark_decode_step(m, B, token_ids, pos.data(), (const float* const*)k_cache,
                           (const float* const*)v_cache, k_delta, v_delta, logits, nullptr,
@@ -1370,13 +1399,13 @@ int ark_greedy_decode(const ark_model* m, int32_t B, int32_t* token_ids, int32_t
       if (e) return e;
       if (launch_masked_argmax(st, B, m->d.vocab, logits, mask, token_ids) != hipSuccess)
         return ARK_E_HIP;
+      if (launch_greedy_post(st, B, token_ids, out_tokens + (size_t)t * B, end_id, done) !=
+          hipSuccess)
+        return ARK_E_HIP;
+      if (launch_cache_write(st, m->d.n_layers, B, 1, T, m->d.n_kv_heads * m->d.head_dim,
+                             pos.data(), k_cache, v_cache, k_delta, v_delta) != hipSuccess)
+        return ARK_E_HIP;
     }
-    if (launch_greedy_post(st, B, token_ids, out_tokens + (size_t)t * B, end_id, done) !=
-        hipSuccess)
-      return ARK_E_HIP;
-    if (launch_cache_write(st, m->d.n_layers, B, 1, T, m->d.n_kv_heads * m->d.head_dim,
-                           pos.data(), k_cache, v_cache, k_delta, v_delta) != hipSuccess)
-      return ARK_E_HIP;
     for (int b = 0; b < B; ++b) pos[b] += 1;
     ++steps;
     if ((t + 1) % check_every == 0 || t + 1 == max_steps) {

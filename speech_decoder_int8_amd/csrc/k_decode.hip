@@ -1815,6 +1815,71 @@ __global__ __launch_bounds__(256) void k_decode_prep(u64* xch, size_t nwords, ui
   }
 }
 
+
+// Between two tokens of the greedy loop on this path: the deltas of the
+// token just decoded written into the caches at its row (the arithmetic of
+// k_cache_write), the stop rule (k_greedy_post), and, when another token
+// follows, the preparation of its launch as k_decode_prep does it on an
+// initialised workspace (counters cleared, the next tag, the embedding of
+// the next input id in every replica of the first layer's input).  The
+// error word is left as it is: a wait that timed out in any step of the
+// loop stays recorded until the host reads it.  Workgroups 0 .. L-1 write the cache rows of their layer;
+// workgroup L + r publishes replica r, and workgroup L also applies the
+// stop rule.  Each of them derives the next input id itself: it equals the
+// stored id whether or not workgroup L has already written it back.
+struct BetweenArgs {
+  float* kc[kMaxLayers];
+  float* vc[kMaxLayers];
+  int L, pos;              // layers; cache row of the token just decoded
+  const float* kd;         // [L][KVD] deltas of that token
+  const float* vd;
+  int32_t* token;          // the greedy id, replaced by the next input id
+  int32_t* out_row;
+  int32_t end_id;
+  int32_t* done;
+  int prep;                // prepare the next launch
+  u64* xch;
+  uint32_t* ctr;
+  int nctr;
+  uint32_t* epoch;
+  const uint16_t* table;
+  int V;
+};
+
+__global__ __launch_bounds__(256) void k_decode_between(BetweenArgs A) {
+  const int blk = blockIdx.x, tid = threadIdx.x;
+  if (blk < A.L) {
+    const float4* kd = (const float4*)(A.kd + (size_t)blk * KVD);
+    const float4* vd = (const float4*)(A.vd + (size_t)blk * KVD);
+    float4* kc = (float4*)(A.kc[blk] + (size_t)A.pos * KVD);
+    float4* vc = (float4*)(A.vc[blk] + (size_t)A.pos * KVD);
+    for (int e = tid; e < KVD / 4; e += 256) {
+      kc[e] = kd[e];
+      vc[e] = vd[e];
+    }
+    return;
+  }
+  const int r = blk - A.L;  // replica
+  const int id = *A.done ? A.end_id : *A.token;
+  __syncthreads();          // this workgroup has read the id before it is written back
+  if (r == 0 && tid == 0) {
+    *A.token = id;
+    *A.out_row = id;
+    if (id == A.end_id) *A.done = 1;
+  }
+  if (!A.prep) return;
+  uint32_t e = A.epoch[0] + 1u;
+  if (e == 0) e = 1;
+  if (r == 0) {
+    for (int i = tid; i < A.nctr; i += 256) A.ctr[i] = 0;
+    if (tid == 0) A.epoch[1] = e;
+  }
+  for (int i = tid; i < H; i += 256) {
+    const float v = (id >= 0 && id < A.V) ? half_bits_to_float(A.table[(size_t)id * H + i])
+                                          : __int_as_float(0x7fc00000);
+    A.xch[OFF_X0 + (size_t)r * H + i] = ((u64)e << 32) | (u64)__float_as_uint(v);
+  }
+}
 }  // namespace mk
 
 // ------------------------------------------------------------------ host --
@@ -1900,16 +1965,19 @@ bool decode_mega_cooperative() {
 }
 
 hipError_t decode_mega_launch(hipStream_t st, void* ws, const MegaStep& S, hipEvent_t ev_begin,
-                              hipEvent_t ev_end) {
+                              hipEvent_t ev_end, bool prep) {
   MegaLayout lay = mega_layout(ws, S.L, S.T);
   // the exchange words and the partial attention states that follow them
   const size_t part_words = (size_t)S.L * mk::NKV * mk::HH * mk::NIH * mk::HPI * mk::PSTATE;
   const size_t nwords = (size_t)(lay.part - lay.xch) + part_words;
   const mk::u64 marker = mk::MAGIC ^ (mk::u64)nwords ^ ((mk::u64)S.T << 40);
-  hipLaunchKernelGGL(mk::k_decode_prep, dim3(mk::NWG), dim3(256), 0, st, lay.xch, nwords, lay.ctr,
-                     2 * S.L + 32, lay.err, lay.marker, marker, lay.epoch, S.token, S.table, S.V);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (prep) {
+    hipLaunchKernelGGL(mk::k_decode_prep, dim3(mk::NWG), dim3(256), 0, st, lay.xch, nwords, lay.ctr,
+                       2 * S.L + 32, lay.err, lay.marker, marker, lay.epoch, S.token, S.table, S.V);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   mk::MegaArgs A;
   A.layers = lay.table;
   A.L = S.L;
@@ -1953,6 +2021,35 @@ hipError_t decode_mega_launch(hipStream_t st, void* ws, const MegaStep& S, hipEv
           : hipLaunchKernel(fn, dim3(mk::NWG), dim3(mk::NT), args, sizeof(mk::Shared), st);
   if (ev_end) hipEventRecord(ev_end, st);
   return e;
+}
+
+hipError_t decode_mega_between(hipStream_t st, void* ws, const MegaStep& S, float* const* k_cache,
+                               float* const* v_cache, int32_t* out_row, int32_t end_id,
+                               int32_t* done, bool prep) {
+  if (S.L < 1 || S.L > kMaxLayers) return hipErrorInvalidValue;
+  MegaLayout lay = mega_layout(ws, S.L, S.T);
+  mk::BetweenArgs A;
+  for (int l = 0; l < S.L; ++l) {
+    A.kc[l] = k_cache[l];
+    A.vc[l] = v_cache[l];
+  }
+  A.L = S.L;
+  A.pos = S.pos;
+  A.kd = S.kdelta;
+  A.vd = S.vdelta;
+  A.token = const_cast<int32_t*>(S.token);
+  A.out_row = out_row;
+  A.end_id = end_id;
+  A.done = done;
+  A.prep = prep ? 1 : 0;
+  A.xch = lay.xch;
+  A.ctr = lay.ctr;
+  A.nctr = 2 * S.L + 32;
+  A.epoch = lay.epoch;
+  A.table = S.table;
+  A.V = S.V;
+  hipLaunchKernelGGL(mk::k_decode_between, dim3(S.L + mk::NREP), dim3(256), 0, st, A);
+  return hipGetLastError();
 }
 
 uint64_t* decode_mega_marker(void* ws, int L, int T) { return (uint64_t*)mega_layout(ws, L, T).marker; }

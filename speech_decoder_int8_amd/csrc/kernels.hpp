@@ -394,9 +394,17 @@ hipError_t decode_mega_init();
 bool decode_mega_cooperative();
 hipError_t decode_mega_upload(hipStream_t st, void* ws, int L, int T, const MegaLayer* layers);
 // ev_begin / ev_end (nullable) are recorded around the persistent kernel
-// alone (not its preparation kernel).
+// alone (not its preparation kernel).  prep = false: the launch was
+// prepared already (by decode_mega_between of the previous token).
 hipError_t decode_mega_launch(hipStream_t st, void* ws, const MegaStep& S, hipEvent_t ev_begin,
-                              hipEvent_t ev_end);
+                              hipEvent_t ev_end, bool prep = true);
+// After a step of the greedy loop (S as launched): its deltas into the
+// caches at row S.pos, the stop rule on *S.token (out_row, done, end_id as
+// for launch_greedy_post), and with prep the preparation of the next
+// step's launch for the resulting id.
+hipError_t decode_mega_between(hipStream_t st, void* ws, const MegaStep& S, float* const* k_cache,
+                               float* const* v_cache, int32_t* out_row, int32_t end_id,
+                               int32_t* done, bool prep);
 // Error word of the last persistent launch on this workspace (0: every
 // bounded wait was met; read after the stream has completed that launch).
 const uint32_t* decode_mega_err_word(const void* ws, int L, int T);

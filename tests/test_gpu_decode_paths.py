@@ -183,3 +183,42 @@ def test_persistent_wait_timeout_is_reported(models, monkeypatch):
     gs.load_caches(kc, vc)
     gs.decode(t(np.array([17], np.int32)), [200])
     assert ark.decode_check(gm, 1, gs.ws) == ark.ARK_OK
+
+
+def test_greedy_loop_stop_rules_persistent(models, path):
+    """The stop rule of the native loop on both paths at the real geometry:
+    an end id emitted at step 3 with the host checking every 4 steps (the
+    loop runs on to the check and reports end_id after it), and a cache
+    that fills up.  On the persistent path the write-back, the stop rule and
+    the next launch's preparation run in one kernel between launches."""
+    om, gm = models
+    rng = np.random.default_rng(31)
+    kc, vc = _caches(CFG, [60], rng)
+    mask = CFG.mask()
+    tok = np.array([123], np.int32)
+    want, cur, p = [], tok, np.array([60])
+    kco, vco = kc, vc
+    for _ in range(3):
+        lg, kdo, vdo, _ = oracle.decode_step(om, cur, p, kco, vco)
+        kco = [oracle.cache_write(kco[l], kdo[l], p) for l in range(CFG.n_layers)]
+        vco = [oracle.cache_write(vco[l], vdo[l], p) for l in range(CFG.n_layers)]
+        cur = oracle.masked_argmax(lg, mask)
+        want.append(int(cur[0]))
+        p = p + 1
+    end = want[2]                     # the third greedy id ends the sequence
+    if end in want[:2]:
+        pytest.skip("the seeded run repeats its third id earlier")
+    gs = GpuState(gm, 1, 1)
+    gs.load_caches(kc, vc)
+    out = torch.full((8, 1), -5, dtype=torch.int32, device="cuda")
+    kd1, vd1 = gs.deltas(1)
+    n, newpos = ark.greedy_decode(gm, t(tok), [60], gs.kc, gs.vc, kd1, vd1, gs.logits, t(mask),
+                                  end, 8, out, ws=gs.ws, check_every=4)
+    got = host(out)[:, 0].tolist()
+    assert n == 4 and newpos.tolist() == [64]
+    assert got[:4] == want[:3] + [end] and got[4:] == [-5] * 4
+    # a full cache: two rows left, two steps
+    T = CFG.max_total_len
+    n, newpos = ark.greedy_decode(gm, t(tok), [T - 2], gs.kc, gs.vc, kd1, vd1, gs.logits,
+                                  t(mask), -1, 8, out, ws=gs.ws, check_every=8)
+    assert n == 2 and newpos.tolist() == [T]
