@@ -59,12 +59,28 @@ __device__ __forceinline__ void put4(double* dst, float4 v) {
   *(double2*)(dst + 2) = double2{(double)v.z, (double)v.w};
 }
 
+// four values of a row from fp32 (BF false) or bf16 (BF true) storage
+template <bool BF>
+__device__ __forceinline__ float4 ld4e(gptr<const float> base, size_t off, int d4) {
+  if constexpr (BF) {
+    typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+    const u2 u = ((const u2 __attribute__((address_space(1)))*)((gptr<const uint16_t>)base + off))[d4];
+    return make_float4(bf2f((uint16_t)u.x), bf2f((uint16_t)(u.x >> 16)), bf2f((uint16_t)u.y),
+                       bf2f((uint16_t)(u.y >> 16)));
+  } else {
+    return ld4(base + off, d4);
+  }
+}
+
+// BF: the bf16 serving variant (q, caches, deltas and the output in bf16,
+// the output rounded once more from the fp32 value; no range).
+template <bool BF>
 __global__ __launch_bounds__(512) void k_attn_prefill(Attn2Params P) {
   using namespace a2;
   extern __shared__ __align__(16) unsigned char smem[];
   double* Ks = (double*)smem;                    // [KC][KP]
   double* Vs = Ks + KC * KP;                     // [KC][VP]
-  if (P.stats.cur) stats_clear_other(P.stats);
+  if (!BF && P.stats.cur) stats_clear_other(P.stats);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nthr = blockDim.x;
@@ -89,11 +105,17 @@ __global__ __launch_bounds__(512) void k_attn_prefill(Attn2Params P) {
   // and is zeroed)
   double qv[32];
   {
-    const gptr<const float> src =
-        uniform_ptr(P.q) + ((size_t)(b * S + min(qrow, S - 1)) * P.NH + h) * kHeadDim;
+    const size_t qoff = ((size_t)(b * S + min(qrow, S - 1)) * P.NH + h) * kHeadDim;
     float qf[32];
+    if constexpr (BF) {
+      const gptr<const uint16_t> src = uniform_ptr((const uint16_t*)P.q) + qoff;
 #pragma unroll
-    for (int s = 0; s < 32; ++s) qf[s] = src[4 * s + q4];
+      for (int s = 0; s < 32; ++s) qf[s] = bf2f(src[4 * s + q4]);
+    } else {
+      const gptr<const float> src = uniform_ptr(P.q) + qoff;
+#pragma unroll
+      for (int s = 0; s < 32; ++s) qf[s] = src[4 * s + q4];
+    }
 #pragma unroll
     for (int s = 0; s < 32; ++s) qv[s] = rowok ? (double)qf[s] : 0.0;
   }
@@ -120,8 +142,8 @@ __global__ __launch_bounds__(512) void k_attn_prefill(Attn2Params P) {
       const bool dl = j >= p;  // this call's rows come from the deltas
       const size_t off = dl ? ((size_t)(b * S + (j - p)) * P.NKV + g) * kHeadDim
                             : ((size_t)(b * T + j) * P.NKV + g) * kHeadDim;
-      kv = ld4((dl ? kdp : kcp) + off, d4);
-      vv = ld4((dl ? vdp : vcp) + off, d4);
+      kv = ld4e<BF>(dl ? kdp : kcp, off, d4);
+      vv = ld4e<BF>(dl ? vdp : vcp, off, d4);
     }
   };
   // with 512 threads (8 query heads) each thread holds 4 float4 of K and of V
@@ -207,7 +229,7 @@ __global__ __launch_bounds__(512) void k_attn_prefill(Attn2Params P) {
     }
   }
   // o[d][i] = O^T[dim 16 d + 4 i + q4][qrow]
-  float* dst = P.out + ((size_t)(b * S + qrow) * P.NH + h) * kHeadDim;
+  const size_t doff = ((size_t)(b * S + qrow) * P.NH + h) * kHeadDim;
   float lo = INFINITY, hi = -INFINITY;
   if (rowok) {
 #pragma unroll
@@ -215,12 +237,15 @@ __global__ __launch_bounds__(512) void k_attn_prefill(Attn2Params P) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float y = (float)(o[d][i] / l);
-        dst[16 * d + 4 * i + q4] = y;
+        if constexpr (BF)
+          ((uint16_t*)P.out)[doff + 16 * d + 4 * i + q4] = f2bf(y);
+        else
+          P.out[doff + 16 * d + 4 * i + q4] = y;
         lo = fminf(lo, y);
         hi = fmaxf(hi, y);
       }
   }
-  if (P.stats.cur) {
+  if (!BF && P.stats.cur) {
     lo = wave_min(lo);
     hi = wave_max(hi);
     if (lane == 0) stats_fold(P.stats, blockIdx.x * 8 + wave, b, lo, hi);
@@ -238,7 +263,7 @@ hipError_t launch_attention_prefill(hipStream_t st, int B, int S, int NH, int NK
   // one-time attribute set-up (a function-local static: initialised once,
   // thread-safe)
   static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)k_attn_prefill, hipFuncAttributeMaxDynamicSharedMemorySize, a2::LDS_BYTES);
+      (const void*)k_attn_prefill<false>, hipFuncAttributeMaxDynamicSharedMemorySize, a2::LDS_BYTES);
   if (attr != hipSuccess) return attr;
   Attn2Params P = {};
   P.B = B;
@@ -257,7 +282,32 @@ hipError_t launch_attention_prefill(hipStream_t st, int B, int S, int NH, int NK
   P.out = out;
   if (stats) P.stats = *stats;
   const int lds = a2::LDS_BYTES;
-  hipLaunchKernelGGL(k_attn_prefill, dim3(B * NKV * P.nqt), dim3(64 * P.G), lds, st, P);
+  hipLaunchKernelGGL(k_attn_prefill<false>, dim3(B * NKV * P.nqt), dim3(64 * P.G), lds, st, P);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_prefill_bf16(hipStream_t st, const AttnBf16Params& Q) {
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)k_attn_prefill<true>, hipFuncAttributeMaxDynamicSharedMemorySize, a2::LDS_BYTES);
+  if (attr != hipSuccess) return attr;
+  if (Q.S < 1 || !attention_prefill_supported(Q.NH, Q.NKV)) return hipErrorInvalidValue;
+  Attn2Params P = {};
+  P.B = Q.B;
+  P.S = Q.S;
+  P.NH = Q.NH;
+  P.NKV = Q.NKV;
+  P.G = Q.NH / Q.NKV;
+  P.T = Q.T;
+  P.nqt = (Q.S + a2::QT - 1) / a2::QT;
+  P.q = (const float*)Q.q;  // bf16 storage, read as such
+  P.kc = (const float*)Q.kc;
+  P.vc = (const float*)Q.vc;
+  P.kd = (const float*)Q.kd;
+  P.vd = (const float*)Q.vd;
+  P.pos = Q.pos;
+  P.out = (float*)Q.out;
+  hipLaunchKernelGGL(k_attn_prefill<true>, dim3(P.B * P.NKV * P.nqt), dim3(64 * P.G), a2::LDS_BYTES,
+                     st, P);
   return hipGetLastError();
 }
 

@@ -550,6 +550,10 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnBf16Params P) {
 }
 
 hipError_t launch_attn_bf16(hipStream_t st, const AttnBf16Params& P) {
+  // prefill rows: the fp64 matrix-core kernel of the int8 path on bf16
+  // storage (sums in fp64 where this kernel's are fp32)
+  if (P.S > 1 && attention_prefill_supported(P.NH, P.NKV))
+    return launch_attention_prefill_bf16(st, P);
   static const hipError_t attr = hipFuncSetAttribute(
       (const void*)k_attn_bf16, hipFuncAttributeMaxDynamicSharedMemorySize, ab::LDS);
   if (attr != hipSuccess) return attr;

@@ -488,6 +488,9 @@ struct AttnBf16Params {
 };
 bool attn_bf16_supported(int NH, int NKV);
 hipError_t launch_attn_bf16(hipStream_t st, const AttnBf16Params& P);
+// the prefill attention of k_attn2.hip on bf16 storage (S >= 1,
+// attention_prefill_supported(NH, NKV)); out rounded to bf16
+hipError_t launch_attention_prefill_bf16(hipStream_t st, const AttnBf16Params& P);
 hipError_t launch_embed_bf16(hipStream_t st, int R, int H, int V, const int32_t* ids,
                              const uint16_t* table, uint16_t* x);
 struct CacheBf16Args {
