@@ -733,7 +733,7 @@ int check_encoder(const ark_encoder* E, int B, int M) {
 
 // ---- bf16 serving variant
 struct PlanBf16 {
-  size_t x, h, qkv, q, attn, a, total;
+  size_t x, h, qkv, q, attn, a, part, total;
 };
 
 PlanBf16 plan_bf16(const ark_dims& d, int B, int S) {
@@ -752,6 +752,7 @@ PlanBf16 plan_bf16(const ark_dims& d, int B, int S) {
   p.q = take(R * Q * 2);
   p.attn = take(R * Q * 2);
   p.a = take(R * I * 2);
+  p.part = take(attention_ws_bytes(B, S, d.n_heads, d.max_total_len));  // decode partials
   p.total = o;
   return p;
 }
@@ -857,7 +858,10 @@ int run_forward_bf16(const ark_model_bf16* m, int B, int S, uint16_t* x, const i
     A.vd = vdl;
     A.pos = pos;
     A.out = attn;
-    HIP_TRY(launch_attn_bf16(st, A));
+    if (S == 1 && NH / NKV <= 8)
+      HIP_TRY(launch_attention_dec_bf16(st, A, ws + p.part));
+    else
+      HIP_TRY(launch_attn_bf16(st, A));
     BSeg os[1] = {bseg(L.o, x, H)};
     HIP_TRY(launch_gemm_bf16(st, R, Q, attn, Q, os, 1, BE_RESID));
     HIP_TRY(launch_rmsnorm_bf16(st, R, H, x, H, L.ln2, d.rms_eps, h));

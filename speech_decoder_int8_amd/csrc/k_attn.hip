@@ -267,11 +267,14 @@ __global__ __launch_bounds__(256) void k_attn(AttnParams P) {
 // the workgroup rotates its heads' q rows in LDS, and the split holding the
 // position rotates this call's key row and writes the key and value deltas
 // (the arithmetic of k_rope: fp64 products, rounded once to fp32).
+// BF: the bf16 serving variant (q, the caches and the deltas held as bf16 and
+// widened on load; the merge rounds the output to bf16; no rotary step).
 namespace ad {
 constexpr int DK = 32;       // keys per split
 constexpr int KPITCH = 132;  // floats per staged key row
 }  // namespace ad
 
+template <bool BF>
 __global__ __launch_bounds__(256) void k_attn_dec(AttnParams P) {
   using namespace ad;
   __shared__ __align__(16) double Qd[8][kHeadDim];  // reused for the weights
@@ -304,7 +307,7 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnParams P) {
   // with no branch or wait between them, before the first store (sources
   // are wave-uniform pointers chosen per lane with selects; rows past the
   // live keys load a live row and are zeroed afterwards)
-  const bool raw = P.rope.qkv != nullptr;
+  const bool raw = !BF && P.rope.qkv != nullptr;
   const gptr<const float> kcp = uniform_ptr(P.kc), vcp = uniform_ptr(P.vc);
   // q rows of heads g G .. and this call's k / v rows of KV head g
   const gptr<const float> qp = uniform_ptr(raw ? P.rope.qkv : P.q);
@@ -326,13 +329,17 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnParams P) {
   for (int k = 0; k < 4; ++k) {
     const int e = tid + 256 * k;
     const int qh = min(e >> 7, G - 1), d = e & (kHeadDim - 1);
-    qf[k] = qp[qbase + (size_t)qh * kHeadDim + d];
+    const size_t qo = qbase + (size_t)qh * kHeadDim + d;
+    if constexpr (BF)
+      qf[k] = bf2f(((gptr<const uint16_t>)qp)[qo]);
+    else
+      qf[k] = qp[qo];
     const int jj = e >> 5, d4 = e & 31;
     const int j = jbeg + min(jj, nk - 1);
     const bool dl = j == p;  // this call's row replaces cache row p
     const size_t off = ((size_t)(b * T + j) * NKV + g) * kHeadDim;
-    kv[k] = ld4(dl ? kdp + dko : kcp + off, d4);
-    vv[k] = ld4(dl ? vdp + dvo : vcp + off, d4);
+    kv[k] = ld4e<BF>(dl ? kdp : kcp, dl ? dko : off, d4);
+    vv[k] = ld4e<BF>(dl ? vdp : vcp, dl ? dvo : off, d4);
   }
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -435,6 +442,8 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnParams P) {
 }
 
 // Merge the split partial softmax states of one (sequence, head, row).
+// BF: out holds bf16, rounded from the fp32 value.
+template <bool BF>
 __global__ __launch_bounds__(128) void k_attn_combine(int S, int NH, int nsplit,
                                                       const double* __restrict__ part,
                                                       float* __restrict__ out) {
@@ -482,7 +491,11 @@ __global__ __launch_bounds__(128) void k_attn_combine(int S, int NH, int nsplit,
       O += os[u] * w;
     }
   }
-  out[((size_t)(b * S + i) * NH + h) * kHeadDim + d] = (float)(O / L);
+  const size_t oi = ((size_t)(b * S + i) * NH + h) * kHeadDim + d;
+  if constexpr (BF)
+    ((uint16_t*)out)[oi] = f2bf((float)(O / L));
+  else
+    out[oi] = (float)(O / L);
 }
 
 static int decode_split(int T) { return T / 32; }
@@ -520,8 +533,8 @@ hipError_t launch_attention(hipStream_t st, int B, int S, int NH, int NKV, int T
   if (S == 1 && P.G <= 8) {
     P.nsplit = decode_split(T);
     P.tsplit = ad::DK;
-    hipLaunchKernelGGL(k_attn_dec, dim3(P.nsplit, B * NKV), dim3(256), 0, st, P);
-    hipLaunchKernelGGL(k_attn_combine, dim3(B * NH), dim3(128), 0, st, 1, NH, P.nsplit, P.part,
+    hipLaunchKernelGGL(k_attn_dec<false>, dim3(P.nsplit, B * NKV), dim3(256), 0, st, P);
+    hipLaunchKernelGGL(k_attn_combine<false>, dim3(B * NH), dim3(128), 0, st, 1, NH, P.nsplit, P.part,
                        out);
   } else if (attention_prefill_supported(NH, NKV)) {
     return launch_attention_prefill(st, B, S, NH, NKV, T, q, k_cache, v_cache, k_delta, v_delta,
@@ -531,6 +544,32 @@ hipError_t launch_attention(hipStream_t st, int B, int S, int NH, int NKV, int T
     P.tsplit = T;
     hipLaunchKernelGGL((k_attn<8, 16>), dim3((S + 7) / 8, B * NKV), dim3(256), 0, st, P);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_dec_bf16(hipStream_t st, const AttnBf16Params& Q, void* part) {
+  if (Q.S != 1 || Q.NKV < 1 || Q.NH % Q.NKV != 0 || Q.NH / Q.NKV > 8 || !part)
+    return hipErrorInvalidValue;
+  AttnParams P = {};
+  P.B = Q.B;
+  P.S = 1;
+  P.NH = Q.NH;
+  P.NKV = Q.NKV;
+  P.G = Q.NH / Q.NKV;
+  P.T = Q.T;
+  P.q = (const float*)Q.q;  // bf16 storage, read as such
+  P.kc = (const float*)Q.kc;
+  P.vc = (const float*)Q.vc;
+  P.kd = (const float*)Q.kd;
+  P.vd = (const float*)Q.vd;
+  P.pos = Q.pos;
+  P.out = (float*)Q.out;
+  P.part = (double*)part;
+  P.nsplit = decode_split(Q.T);
+  P.tsplit = ad::DK;
+  hipLaunchKernelGGL(k_attn_dec<true>, dim3(P.nsplit, Q.B * Q.NKV), dim3(256), 0, st, P);
+  hipLaunchKernelGGL(k_attn_combine<true>, dim3(Q.B * Q.NH), dim3(128), 0, st, 1, Q.NH, P.nsplit,
+                     P.part, P.out);
   return hipGetLastError();
 }
 

@@ -59,19 +59,6 @@ __device__ __forceinline__ void put4(double* dst, float4 v) {
   *(double2*)(dst + 2) = double2{(double)v.z, (double)v.w};
 }
 
-// four values of a row from fp32 (BF false) or bf16 (BF true) storage
-template <bool BF>
-__device__ __forceinline__ float4 ld4e(gptr<const float> base, size_t off, int d4) {
-  if constexpr (BF) {
-    typedef unsigned int u2 __attribute__((ext_vector_type(2)));
-    const u2 u = ((const u2 __attribute__((address_space(1)))*)((gptr<const uint16_t>)base + off))[d4];
-    return make_float4(bf2f((uint16_t)u.x), bf2f((uint16_t)(u.x >> 16)), bf2f((uint16_t)u.y),
-                       bf2f((uint16_t)(u.y >> 16)));
-  } else {
-    return ld4(base + off, d4);
-  }
-}
-
 // BF: the bf16 serving variant (q, caches, deltas and the output in bf16,
 // the output rounded once more from the fp32 value; no range).
 template <bool BF>

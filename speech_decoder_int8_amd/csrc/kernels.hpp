@@ -433,6 +433,20 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 }
 __device__ __forceinline__ float rbf(float f) { return bf2f(f2bf(f)); }
 
+// four values of a row from fp32 (BF false) or bf16 (BF true) storage; off
+// counts elements of the storage type
+template <bool BF>
+__device__ __forceinline__ float4 ld4e(gptr<const float> base, size_t off, int d4) {
+  if constexpr (BF) {
+    typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+    const u2 u = ((const u2 __attribute__((address_space(1)))*)((gptr<const uint16_t>)base + off))[d4];
+    return make_float4(bf2f((uint16_t)u.x), bf2f((uint16_t)(u.x >> 16)), bf2f((uint16_t)u.y),
+                       bf2f((uint16_t)(u.y >> 16)));
+  } else {
+    return ld4(base + off, d4);
+  }
+}
+
 // ---- the epilogue of one output value
 // BE_STORE: bf16(acc + bias); BE_RESID: bf16(old + bf16(acc + bias));
 // BE_F32: fp32 acc (the logits); the SwiGLU pair is handled by the callers.
@@ -491,6 +505,10 @@ hipError_t launch_attn_bf16(hipStream_t st, const AttnBf16Params& P);
 // the prefill attention of k_attn2.hip on bf16 storage (S >= 1,
 // attention_prefill_supported(NH, NKV)); out rounded to bf16
 hipError_t launch_attention_prefill_bf16(hipStream_t st, const AttnBf16Params& P);
+// the split decode attention of k_attn.hip on bf16 storage (S == 1,
+// NH / NKV <= 8); part: attention_ws_bytes(B, 1, NH, T) bytes of partial
+// states; out rounded to bf16
+hipError_t launch_attention_dec_bf16(hipStream_t st, const AttnBf16Params& P, void* part);
 hipError_t launch_embed_bf16(hipStream_t st, int R, int H, int V, const int32_t* ids,
                              const uint16_t* table, uint16_t* x);
 struct CacheBf16Args {
