@@ -858,10 +858,7 @@ int run_forward_bf16(const ark_model_bf16* m, int B, int S, uint16_t* x, const i
     A.vd = vdl;
     A.pos = pos;
     A.out = attn;
-    if (S == 1 && NH / NKV <= 8)
-      HIP_TRY(launch_attention_dec_bf16(st, A, ws + p.part));
-    else
-      HIP_TRY(launch_attn_bf16(st, A));
+    HIP_TRY(launch_attn_bf16(st, A, ws + p.part));
     BSeg os[1] = {bseg(L.o, x, H)};
     HIP_TRY(launch_gemm_bf16(st, R, Q, attn, Q, os, 1, BE_RESID));
     HIP_TRY(launch_rmsnorm_bf16(st, R, H, x, H, L.ln2, d.rms_eps, h));

@@ -2,15 +2,17 @@
 // "dtype": bfloat16 is the default serving dtype): weights, activations and
 // the KV cache in bf16, every operation rounding its output once to bf16
 // (round to nearest even), fp32 logits.  Products of bf16 values are exact
-// in fp32; sums run in fp32 (matrix cores) or fp64 (norms, rotary step).
+// in fp32; sums run in fp32 (matrix cores) or fp64 (norms, rotary step,
+// attention).
 //   * k_to_bf16        fp32 -> bf16 of weights and inputs
 //   * k_gemv_bf16      up to 8 activation rows: one wave per pair of weight
 //                      rows, the rows of x read from cache
 //   * k_gemm_bf16      more rows: v_mfma_f32_16x16x32_bf16 tiles (the byte
 //                      layout of the int8 tiled GEMM: a 64-byte K step is
 //                      one matrix instruction per fragment pair)
-//   * k_rmsnorm_bf16, k_rope_bf16, k_attn_bf16, k_embed_bf16,
-//     k_cache_write_bf16
+//   * k_rmsnorm_bf16, k_rope_bf16, k_embed_bf16, k_cache_write_bf16
+//   * attention: the int8 path's kernels (k_attn2.hip, k_attn.hip) on bf16
+//     storage
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -404,166 +406,18 @@ hipError_t launch_rope_bf16(hipStream_t st, int B, int S, int NH, int NKV, const
   return hipGetLastError();
 }
 
-// ---- attention over the bf16 cache (fp32 scores, softmax and sums)
-// One workgroup = 16 query vectors sharing one KV head: for S > 1 the rows
-// i0 .. i0 + 15 of one query head, for S == 1 the G query heads of one KV
-// head.  256 threads = 16 vectors x 16 threads; each 64-key chunk of K and V
-// is staged in LDS as fp32.  A thread scores keys t, t + 16, t + 32, t + 48
-// of its vector and accumulates dims 8 t .. 8 t + 7 of the weighted sum.
-namespace ab {
-constexpr int D = 128, KC = 64, KP = 132, VPP = 128, NV = 16;
-constexpr int LDS = (NV * D + KC * KP + KC * VPP + NV * KC) * 4;
-}  // namespace ab
-
-__global__ __launch_bounds__(256) void k_attn_bf16(AttnBf16Params P) {
-  using namespace ab;
-  extern __shared__ __align__(16) float sm[];
-  float* Qs = sm;                 // [NV][D]
-  float* Ks = Qs + NV * D;        // [KC][KP]
-  float* Vs = Ks + KC * KP;       // [KC][VPP]
-  float* Ps = Vs + KC * VPP;      // [NV][KC]
-  const int tid = threadIdx.x, v = tid >> 4, t = tid & 15;
-  const int G = P.NH / P.NKV;
-  int b, g, head, row;
-  bool vok;
-  if (P.S > 1) {
-    const int nqt = (P.S + NV - 1) / NV;
-    const int qt = blockIdx.x % nqt;
-    const int bh = blockIdx.x / nqt;
-    b = bh / P.NH;
-    head = bh % P.NH;
-    g = head / G;
-    row = qt * NV + v;
-    vok = row < P.S;
-  } else {
-    b = blockIdx.x / P.NKV;
-    g = blockIdx.x % P.NKV;
-    head = g * G + v;
-    row = 0;
-    vok = v < G;
-  }
-  const int p = P.pos.p[b];
-  const int qpos = p + row;
-  // the last key any vector of this workgroup sees
-  int maxrow;
-  if (P.S > 1)
-    maxrow = min(((blockIdx.x % ((P.S + NV - 1) / NV)) + 1) * NV, P.S) - 1;
-  else
-    maxrow = 0;
-  const int maxq = p + maxrow;
-  // query vector -> LDS (fp32)
-  for (int e = tid; e < NV * D; e += 256) {
-    const int vv = e / D, d = e % D;
-    int hq, rq;
-    bool ok;
-    if (P.S > 1) {
-      hq = head;
-      rq = (blockIdx.x % ((P.S + NV - 1) / NV)) * NV + vv;
-      ok = rq < P.S;
-    } else {
-      hq = g * G + vv;
-      rq = 0;
-      ok = vv < G;
-    }
-    Qs[e] = ok ? bf2f(P.q[((size_t)(b * P.S + rq) * P.NH + hq) * D + d]) : 0.0f;
-  }
-  float acc[8];
-#pragma unroll
-  for (int d = 0; d < 8; ++d) acc[d] = 0.0f;
-  float m = -INFINITY, l = 0.0f;
-  const float scale = 0.08838834764831845f;  // 1 / sqrt(128) rounded to fp32
-  const int nch = maxq / KC + 1;
-  for (int c = 0; c < nch; ++c) {
-    const int j0 = c * KC;
-    __syncthreads();
-    // 64 keys x 16 units of 8 dims, K and V: 4 units per thread
-    for (int e = tid; e < KC * (D / 8); e += 256) {
-      const int jj = e >> 4, u = e & 15;
-      const int j = j0 + jj;
-      float kf[8], vf[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) kf[i] = vf[i] = 0.0f;
-      if (j < p + P.S && j < P.T) {
-        const uint16_t *ks, *vs;
-        if (j >= p) {
-          const size_t off = ((size_t)(b * P.S + (j - p)) * P.NKV + g) * D + 8 * u;
-          ks = P.kd + off;
-          vs = P.vd + off;
-        } else {
-          const size_t off = ((size_t)(b * P.T + j) * P.NKV + g) * D + 8 * u;
-          ks = P.kc + off;
-          vs = P.vc + off;
-        }
-        unpack8(*(const i32x4*)ks, kf);
-        unpack8(*(const i32x4*)vs, vf);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        Ks[jj * KP + 8 * u + i] = kf[i];
-        Vs[jj * VPP + 8 * u + i] = vf[i];
-      }
-    }
-    __syncthreads();
-    float sc[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int jj = t + 16 * kk;
-      const float* kr = Ks + jj * KP;
-      const float* qr = Qs + v * D;
-      float a = 0.0f;
-#pragma unroll 8
-      for (int d = 0; d < D; ++d) a = fmaf(qr[d], kr[d], a);
-      const int j = j0 + jj;
-      sc[kk] = (vok && j <= qpos) ? a * scale : -INFINITY;
-    }
-    float cmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, o, 16));
-    const float mnew = fmaxf(m, cmax);
-    const float alpha = (m == -INFINITY) ? 0.0f : expf(m - mnew);
-    float ls = 0.0f;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const float e = (sc[kk] == -INFINITY) ? 0.0f : expf(sc[kk] - mnew);
-      Ps[v * KC + t + 16 * kk] = e;
-      ls += e;
-    }
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) ls += __shfl_xor(ls, o, 16);
-    l = l * alpha + ls;
-    m = mnew;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) acc[d] *= alpha;
-    __syncthreads();
-    for (int jj = 0; jj < KC; ++jj) {
-      const float pw = Ps[v * KC + jj];
-      const float* vr = Vs + jj * VPP + 8 * t;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) acc[d] = fmaf(pw, vr[d], acc[d]);
-    }
-  }
-  if (vok) {
-    uint16_t* dst = P.out + ((size_t)(b * P.S + row) * P.NH + head) * D + 8 * t;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) dst[d] = f2bf(acc[d] / l);
-  }
-}
-
-hipError_t launch_attn_bf16(hipStream_t st, const AttnBf16Params& P) {
-  // prefill rows: the fp64 matrix-core kernel of the int8 path on bf16
-  // storage (sums in fp64 where this kernel's are fp32)
-  if (P.S > 1 && attention_prefill_supported(P.NH, P.NKV))
-    return launch_attention_prefill_bf16(st, P);
-  static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)k_attn_bf16, hipFuncAttributeMaxDynamicSharedMemorySize, ab::LDS);
-  if (attr != hipSuccess) return attr;
-  const int grid = P.S > 1 ? P.B * P.NH * ((P.S + ab::NV - 1) / ab::NV) : P.B * P.NKV;
-  hipLaunchKernelGGL(k_attn_bf16, dim3(grid), dim3(256), ab::LDS, st, P);
-  return hipGetLastError();
+// ---- attention over the bf16 cache: the int8 path's kernels on bf16
+// storage (loads widen bf16 to fp32, sums in fp64, the output rounded once
+// to bf16 from the fp32 value).  Prefill rows: the fp64 matrix-core kernel;
+// a decode row: 32-key splits and their merge (part: the partial states).
+hipError_t launch_attn_bf16(hipStream_t st, const AttnBf16Params& P, void* part) {
+  if (!attn_bf16_supported(P.NH, P.NKV)) return hipErrorInvalidValue;
+  if (P.S == 1) return launch_attention_dec_bf16(st, P, part);
+  return launch_attention_prefill_bf16(st, P);
 }
 
 bool attn_bf16_supported(int NH, int NKV) {
-  return NKV >= 1 && NH % NKV == 0 && NH / NKV <= ab::NV;
+  return NKV >= 1 && NH % NKV == 0 && NH / NKV <= 8;
 }
 
 // ---- embedding rows from the bf16 table; ids out of range give NaN rows

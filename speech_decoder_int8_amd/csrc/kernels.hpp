@@ -500,8 +500,10 @@ struct AttnBf16Params {
   PosArgs pos;
   uint16_t* out;       // [B][S][NH * 128]
 };
+// query heads per KV head at most 8; part: attention_ws_bytes(B, S, NH, T)
+// bytes (decode partial states; unused for S > 1)
 bool attn_bf16_supported(int NH, int NKV);
-hipError_t launch_attn_bf16(hipStream_t st, const AttnBf16Params& P);
+hipError_t launch_attn_bf16(hipStream_t st, const AttnBf16Params& P, void* part);
 // the prefill attention of k_attn2.hip on bf16 storage (S >= 1,
 // attention_prefill_supported(NH, NKV)); out rounded to bf16
 hipError_t launch_attention_prefill_bf16(hipStream_t st, const AttnBf16Params& P);
