@@ -211,7 +211,7 @@ def test_swiglu_elementwise_over_every_range():
 # short sequences per wave); the others take a separate range pass
 @pytest.mark.parametrize("B,R,n,k", [(3, 101, 200, 2048), (2, 200, 130, 1024), (40, 4, 96, 512),
                                      (1, 128, 64, 256), (4, 8, 96, 1024), (2, 30, 70, 2048),
-                                     (2, 300, 8000, 256), (2, 100, 100, 192)])
+                                     (2, 300, 8000, 256), (2, 100, 100, 192), (3, 400, 600, 256)])
 def test_gate_up_swiglu_and_sequence_range(B, R, n, k):
     rng = np.random.default_rng(7 * n + k + B * R)
     wg = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
