@@ -167,6 +167,42 @@ class Run:
             done += n
 
 
+def c2_bench(torch, ark, synth, gm, cfg) -> dict:
+    """The 30 s clip on one sequence: its 387-row prompt prefill (at the
+    ridge between the two rooflines, so both fractions are given: int8 ops
+    against 5 POPS, and the weight bytes streamed once against 8 TB/s), then
+    32 greedy decode steps from position 387 (the same kernels as the 3 s
+    clip with 387..418 live cache rows), against 8 TB/s on the full-T bytes.
+    The prompt rows are the 30 s clip's; the weights are the 3 s clip's
+    (timing does not depend on their values)."""
+    import numpy as np
+    c2 = synth.CONFIGS["c2"]
+    S2 = c2.prefill_len
+    r2 = Run(torch, ark, gm, 1, S2)
+    x2 = torch.empty((1, S2, cfg.hidden), dtype=torch.float32, device="cuda")
+    ark.embed_splice(gm.dims, torch.from_numpy(synth.prompt_ids(c2)).cuda(), gm.embed_f16,
+                     torch.from_numpy(synth.audio_rows(c2)).cuda(), c2.audio_offset, x2)
+    r2.prefill(x2, [0])
+    t = timed(torch, lambda: r2.prefill(x2, [0]), reps=5)
+    ops = prefill_int8_ops(cfg, S2, 1)
+    wbytes = decode_bytes(cfg, 1) - 2 * cfg.n_layers * cfg.max_total_len * cfg.kv_dim * 4
+    ex = {"prefill_c2_tok_s": round(S2 / t, 1), "prefill_c2_ms": round(t * 1e3, 3),
+          "prefill_c2_int8_frac_of_5POPS": round(ops / t / PEAK_INT8, 4),
+          "prefill_c2_weight_bytes_frac_of_8TBps": round(wbytes / t / PEAK_HBM, 4)}
+    ark.cache_write(gm.dims, [0], r2.kc, r2.vc, r2.kd, r2.vd)
+    ark.masked_argmax(r2.logits, r2.mask, r2.tok)
+    K2 = 32
+    out = torch.empty((K2, 1), dtype=torch.int32, device="cuda")
+    r2.greedy(S2, 4, out)
+    t2 = timed(torch, lambda: r2.greedy(S2, K2, out), reps=2)
+    ex["decode_bs1_c2_tok_s"] = round(K2 / t2, 1)
+    ex["decode_bs1_c2_ms_per_step"] = round(t2 * 1e3 / K2, 4)
+    ex["decode_bs1_c2_frac_of_8TBps"] = round(decode_bytes(cfg, 1) / (t2 / K2) / PEAK_HBM, 4)
+    del r2, x2, out
+    torch.cuda.empty_cache()
+    return ex
+
+
 def timed(torch, fn, reps=1):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -333,6 +369,7 @@ def gpu_bench(args):
         ex["prefill_c1_ms"] = round(t * 1e3, 3)
         del run
         torch.cuda.empty_cache()
+        ex.update(c2_bench(torch, ark, synth, gm, cfg))
         # batch-32 decode: 32 sequences, each from its own pre-filled cache
         # length (uniform in [50, 400], the c3 workload), 16 lockstep steps
         c3 = synth.CONFIGS["c3"]
