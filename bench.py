@@ -530,6 +530,19 @@ def encoder_probe() -> None:
     log(f"encoder: {ex}")
 
 
+def c2_probe() -> None:
+    """Only the 30 s clip's figures on one sequence (for profiler runs)."""
+    import torch
+
+    import synth
+    from speech_decoder_int8_amd import ark
+    ark.lib()
+    torch.cuda.set_device(0)
+    cfg = synth.CONFIGS["c1"]
+    gm = ark.load_model(cfg, synth)
+    log(f"c2: {c2_bench(torch, ark, synth, gm, cfg)}")
+
+
 def prefill_probe() -> None:
     """Only the coalesced 16 x 387 prefill at T = 512: one untimed call, then
     one timed call (for counter passes, which slow every dispatch)."""
@@ -657,6 +670,8 @@ def main():
                     help="only run the 16x387 prefill twice and exit (for counter passes)")
     ap.add_argument("--encoder-only", action="store_true",
                     help="only run the audio encoder workloads and exit (for profiler runs)")
+    ap.add_argument("--c2-only", action="store_true",
+                    help="only run the 30 s clip's prefill and decode figures and exit (for profiler runs)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -674,6 +689,9 @@ def main():
         return
     if args.encoder_only:
         encoder_probe()
+        return
+    if args.c2_only:
+        c2_probe()
         return
     result = gpu_bench(args)
     result["cpu_baseline"] = cpu_baseline(args.cpu_layers) if args.cpu else None

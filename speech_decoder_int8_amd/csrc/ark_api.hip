@@ -65,9 +65,10 @@ Plan plan(const ark_dims& d, int B, int S) {
   p.qz = take((size_t)std::max(B, 64) * 4);
   // decode-only regions are always reserved, so a workspace sized for a
   // prefill of B sequences also serves their decode steps
-  p.part = take(attention_ws_bytes(B, 1, d.n_heads, d.max_total_len));
+  p.part = take(std::max(attention_ws_bytes(B, 1, d.n_heads, d.max_total_len),
+                         attention_ws_bytes(B, S, d.n_heads, d.max_total_len)));
   p.done = take((size_t)kMaxBatch * 4);
-  p.gsk = take(gemm_skinny_ws_bytes());
+  p.gsk = take(gemm_ws_bytes(R));
   p.mega = take(B == 1 ? decode_mega_ws_bytes(d.n_layers, d.max_total_len) : 0);
   p.hn = take((size_t)B * H * 4);  // final-normed rows of the int4 LM tier
   p.total = o;
@@ -340,12 +341,16 @@ int run_forward(const ark_model* m, int B, int S, float* x, const int32_t* pos_h
   float* qs = (float*)(ws + p.qs);
   int* qz = (int*)(ws + p.qz);
   void* part = ws + p.part;
-  void* gsk = ws + p.gsk;  // few-row GEMM scratch
-  HIP_TRY(gemm_skinny_reset(st, gsk));
+  void* gsk = ws + p.gsk;  // GEMM scratch (few-row blocks, split-K blocks)
+  HIP_TRY(gemm_scratch_reset(st, gsk, (size_t)R));
   if (!gemv && !rowq) HIP_TRY(launch_seq_stats_init(st, sa.cur));
   PosArgs pos;
   memset(&pos, 0, sizeof(pos));
-  for (int b = 0; b < B; ++b) pos.p[b] = pos_host[b];
+  int pmax = 0;
+  for (int b = 0; b < B; ++b) {
+    pos.p[b] = pos_host[b];
+    pmax = std::max(pmax, pos_host[b]);
+  }
   const int ldqkv = Q + 2 * KV;
 
   for (int l = 0; l < d.n_layers; ++l) {
@@ -377,7 +382,7 @@ int run_forward(const ark_model* m, int B, int S, float* x, const int32_t* pos_h
     if (!rope_in_attn)
       HIP_TRY(launch_rope(st, B, S, NH, NKV, qkv, m->rope_cos, m->rope_sin, pos, q, kdl, vdl));
     const RopeIn ri = {qkv, ldqkv, m->rope_cos, m->rope_sin, kdl, vdl};
-    const bool att_stats = !gemv && !rowq && attention_stats(S, NH, NKV);
+    const bool att_stats = !gemv && !rowq && attention_stats(B, S, NH, NKV, T, pmax);
     HIP_TRY(launch_attention(st, B, S, NH, NKV, T, q, kc[l], vc[l], kdl, vdl, pos, attn, part,
                              att_stats ? &sb : nullptr, rope_in_attn ? &ri : nullptr));
     D2D(dptr(l, ARK_DUMP_ATTN), attn, (size_t)R * Q * 4);
@@ -650,7 +655,7 @@ AdapterPlan adapter_plan(const ark_adapter& A, int B, int frames, bool* compact 
   p.stats = take(2 * (size_t)kStatsSetInts * 4);
   p.qs = take((size_t)kMaxBatch * 4);
   p.qz = take((size_t)kMaxBatch * 4);
-  p.gsk = take(gemm_skinny_ws_bytes());
+  p.gsk = take(gemm_ws_bytes(R));
   p.total = o;
   return p;
 }
@@ -697,7 +702,7 @@ EncoderPlan encoder_plan(const ark_encoder& E, int B, int M) {
   p.stats = take(2 * (size_t)kStatsSetInts * 4);
   p.qs = take((size_t)kMaxBatch * 4);
   p.qz = take((size_t)kMaxBatch * 4);
-  p.gsk = take(gemm_skinny_ws_bytes());
+  p.gsk = take(gemm_ws_bytes(std::max(R1, R)));
   p.total = o;
   return p;
 }
@@ -1056,7 +1061,7 @@ int ark_audio_adapter(const ark_adapter* A, int32_t B, int32_t frames, const flo
   float* qs = (float*)(ws + p.qs);
   int* qz = (int*)(ws + p.qz);
   void* gsk = ws + p.gsk;
-  HIP_TRY(gemm_skinny_reset(st, gsk));
+  HIP_TRY(gemm_scratch_reset(st, gsk, (size_t)R));
   HIP_TRY(launch_seq_stats_init(st, sa.cur));
   // merged rows: range per sequence, codes, up projection (+ bias)
   HIP_TRY(launch_row_stats(st, R, K1, n, x, K1, nullptr, 0.0, rs, sa));
@@ -1104,7 +1109,7 @@ int ark_audio_encoder(const ark_encoder* E, int32_t B, int32_t mel_frames, const
   float* qs = (float*)(ws + p.qs);
   int* qz = (int*)(ws + p.qz);
   void* gsk = ws + p.gsk;
-  HIP_TRY(gemm_skinny_reset(st, gsk));
+  HIP_TRY(gemm_scratch_reset(st, gsk, (size_t)std::max(R1, R)));
   HIP_TRY(launch_seq_stats_init(st, sa.cur));
   // conv1: tap-major rows of the mel frames, their range and codes per clip,
   // the int8 GEMM (+ bias), GELU with its range (for conv2's codes)
@@ -1508,7 +1513,7 @@ int ark_test_enc_attention(int32_t B, int32_t F, int32_t H, const float* qkv,
 
 size_t ark_test_qlinear_workspace_bytes(int32_t rows, int32_t k, int32_t use_gemm) {
   if (rows < 1 || k < 1) return 0;
-  return align_up((size_t)rows * (k + 8) + 256) + (use_gemm == 1 ? gemm_skinny_ws_bytes() : 0);
+  return align_up((size_t)rows * (k + 8) + 256) + (use_gemm == 1 ? gemm_ws_bytes(rows) : 0);
 }
 
 int ark_test_qlinear(int32_t B, int32_t R, const uint8_t* codes, const float* scale,
@@ -1521,7 +1526,7 @@ int ark_test_qlinear(int32_t B, int32_t R, const uint8_t* codes, const float* sc
   if (!use_gemm && rows > 4) return ARK_E_SHAPE;
   if (use_gemm < 0 || use_gemm > 2) return ARK_E_SHAPE;
   const size_t base = align_up((size_t)rows * (W->k + 8) + 256);
-  const size_t need = base + (use_gemm == 1 ? gemm_skinny_ws_bytes() : 0);
+  const size_t need = base + (use_gemm == 1 ? gemm_ws_bytes(rows) : 0);
   if (workspace_bytes < need) return ARK_E_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
@@ -1534,7 +1539,7 @@ int ark_test_qlinear(int32_t B, int32_t R, const uint8_t* codes, const float* sc
   hipError_t err;
   if (use_gemm == 1) {
     void* gsk = ws + base;
-    err = gemm_skinny_reset(st, gsk);
+    err = gemm_scratch_reset(st, gsk, rows);
     if (err == hipSuccess)
       err = launch_gemm(st, rows, W->k, sc, srow, zrow, 1, &s, 1, EPI_STORE, acc, gsk);
   } else if (use_gemm == 2) {
@@ -1549,7 +1554,7 @@ size_t ark_test_gate_up_workspace_bytes(int32_t B, int32_t R, int32_t k) {
   if (B < 1 || R < 1 || k < 1) return 0;
   const size_t rows = (size_t)B * R;
   return align_up(rows * k) + 2 * align_up(rows * 4) + 3 * align_up((size_t)B * 4) +
-         ark_test_dynquant_workspace_bytes() + gemm_skinny_ws_bytes();
+         ark_test_dynquant_workspace_bytes() + gemm_ws_bytes(rows);
 }
 
 int ark_test_swiglu(int64_t n, const float* g, const float* u, float* y, void* stream) {
@@ -1586,12 +1591,12 @@ int ark_test_gate_up(int32_t B, int32_t R, const uint8_t* codes, const float* sc
   int* zseq = (int*)take((size_t)B * 4);
   int8_t* junk = (int8_t*)take((size_t)B * 4);
   int* stw = (int*)take(ark_test_dynquant_workspace_bytes());
-  void* gsk = take(gemm_skinny_ws_bytes());
+  void* gsk = take(gemm_ws_bytes(rows));
   const SeqStats sa = {stw, stw + kStatsSetInts, B};
   // shifted codes, then the per-sequence (s, z) as one-column "rows"
   HIP_TRY(launch_test_codes(st, rows, k, R, codes, sc, scale, zp, srow, zrow));
   HIP_TRY(launch_test_codes(st, B, 1, 1, codes, junk, scale, zp, sseq, zseq));
-  HIP_TRY(gemm_skinny_reset(st, gsk));
+  HIP_TRY(gemm_scratch_reset(st, gsk, rows));
   HIP_TRY(launch_seq_stats_init(st, sa.cur));
   Seg gus[2] = {seg_of(*gate, y, n), seg_of(*up, y, n)};
   const bool fused = gemm_swiglu_stats(rows, k, gsk);
@@ -1628,9 +1633,13 @@ int ark_test_attention(int32_t B, int32_t S, int32_t n_heads, int32_t n_kv_heads
   const SeqStats sa = {stw, stw + kStatsSetInts, B};
   PosArgs pos;
   memset(&pos, 0, sizeof(pos));
-  for (int b = 0; b < B; ++b) pos.p[b] = cache_position[b];
+  int pmax = 0;
+  for (int b = 0; b < B; ++b) {
+    pos.p[b] = cache_position[b];
+    pmax = std::max(pmax, cache_position[b]);
+  }
   HIP_TRY(launch_seq_stats_init(st, sa.cur));
-  const bool fused = attention_stats(S, n_heads, n_kv_heads);
+  const bool fused = attention_stats(B, S, n_heads, n_kv_heads, T, pmax);
   HIP_TRY(launch_attention(st, B, S, n_heads, n_kv_heads, T, q, k_cache, v_cache, k_delta,
                            v_delta, pos, out, ws, fused ? &sa : nullptr));
   const int Q = n_heads * kHeadDim;

@@ -501,12 +501,28 @@ __global__ __launch_bounds__(128) void k_attn_combine(int S, int NH, int nsplit,
 static int decode_split(int T) { return T / 32; }
 
 size_t attention_ws_bytes(int B, int S, int NH, int T) {
-  if (S != 1) return 0;
-  return (size_t)B * NH * decode_split(T) * kPart * sizeof(double);
+  if (S == 1) return (size_t)B * NH * decode_split(T) * kPart * sizeof(double);
+  // prefill with its key chunks split: at most the split of one KV head
+  // (more KV heads give more workgroups, so no larger split) at the last
+  // position a call of S rows may start at
+  const int ns = S < T ? attention_prefill_split(B, S, 1, T, T - S) : 1;
+  return ns > 1 ? (size_t)B * NH * S * ns * kPart * sizeof(double) : 0;
 }
 
-bool attention_stats(int S, int NH, int NKV) {
-  return S > 1 && attention_prefill_supported(NH, NKV);
+bool attention_stats(int B, int S, int NH, int NKV, int T, int pmax) {
+  return S > 1 && attention_prefill_supported(NH, NKV) &&
+         attention_prefill_split(B, S, NKV, T, pmax) == 1;
+}
+
+hipError_t launch_attention_merge(hipStream_t st, int B, int S, int NH, int nsplit,
+                                  const double* part, void* out, bool bf16) {
+  if (bf16)
+    hipLaunchKernelGGL(k_attn_combine<true>, dim3(B * NH * S), dim3(128), 0, st, S, NH, nsplit, part,
+                       (float*)out);
+  else
+    hipLaunchKernelGGL(k_attn_combine<false>, dim3(B * NH * S), dim3(128), 0, st, S, NH, nsplit, part,
+                       (float*)out);
+  return hipGetLastError();
 }
 
 hipError_t launch_attention(hipStream_t st, int B, int S, int NH, int NKV, int T, const float* q,
@@ -538,7 +554,7 @@ hipError_t launch_attention(hipStream_t st, int B, int S, int NH, int NKV, int T
                        out);
   } else if (attention_prefill_supported(NH, NKV)) {
     return launch_attention_prefill(st, B, S, NH, NKV, T, q, k_cache, v_cache, k_delta, v_delta,
-                                    pos, out, stats);
+                                    pos, out, stats, ws);
   } else {
     P.nsplit = 1;
     P.tsplit = T;

@@ -20,6 +20,8 @@
 // P^T[16 kb + 4 i + l / 16][l % 16] in lane l's register i, which is the B
 // operand that lane supplies for keys 4 t .. 4 t + 3 with t = 4 kb + i: the
 // weights never leave the registers.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -51,6 +53,12 @@ struct Attn2Params {
   PosArgs pos;
   float* out;
   SeqStats stats;  // per-sequence min/max of out (cur == nullptr: off)
+  // nsplit > 1: the key chunks of a query tile are dealt over nsplit
+  // workgroups (chunk c to split c % nsplit), each writing its unnormalised
+  // softmax state per row and head to part ([B][NH][S][nsplit][2 + 128]:
+  // max, sum, weighted values); the split merge writes out
+  int nsplit;
+  double* part;
 };
 
 // four fp32 values widened into LDS (exact)
@@ -72,9 +80,11 @@ __global__ __launch_bounds__(512) void k_attn_prefill(Attn2Params P) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nthr = blockDim.x;
   // heavy (late) query tiles first
+  const int ns = max(P.nsplit, 1);
+  const int split = (int)blockIdx.x % ns, tix = (int)blockIdx.x / ns;
   const int nbg = P.B * P.NKV;
-  const int qt = P.nqt - 1 - (int)blockIdx.x / nbg;
-  const int bg = blockIdx.x % nbg;
+  const int qt = P.nqt - 1 - tix / nbg;
+  const int bg = tix % nbg;
   const int b = bg / P.NKV, g = bg % P.NKV;
   const int i0 = qt * QT;
   const int p = P.pos.p[b];
@@ -140,8 +150,8 @@ __global__ __launch_bounds__(512) void k_attn_prefill(Attn2Params P) {
   float4 kn[PF], vn[PF];
   if (piped)
 #pragma unroll
-    for (int u = 0; u < PF; ++u) fetch(0, tid + 512 * u, kn[u], vn[u]);
-  for (int c = 0; c < nch; ++c) {
+    for (int u = 0; u < PF; ++u) fetch(split * KC, tid + 512 * u, kn[u], vn[u]);
+  for (int c = split; c < nch; c += ns) {
     const int j0 = c * KC;
     __syncthreads();  // the previous chunk's K, V and P are used
     if (piped) {
@@ -151,9 +161,9 @@ __global__ __launch_bounds__(512) void k_attn_prefill(Attn2Params P) {
         put4(Ks + jj * KP + 4 * d4, kn[u]);
         put4(Vs + jj * VP + 4 * d4, vn[u]);
       }
-      if (c + 1 < nch)
+      if (c + ns < nch)
 #pragma unroll
-        for (int u = 0; u < PF; ++u) fetch(j0 + KC, tid + 512 * u, kn[u], vn[u]);
+        for (int u = 0; u < PF; ++u) fetch(j0 + ns * KC, tid + 512 * u, kn[u], vn[u]);
     } else {
       for (int e = tid; e < KC * (kHeadDim / 4); e += nthr) {
         float4 kv, vv;
@@ -216,6 +226,22 @@ __global__ __launch_bounds__(512) void k_attn_prefill(Attn2Params P) {
     }
   }
   // o[d][i] = O^T[dim 16 d + 4 i + q4][qrow]
+  if (ns > 1) {
+    // this split's state of row qrow, head h (a split that saw no chunk
+    // leaves the empty state: m = -inf, l = 0, o = 0)
+    if (rowok) {
+      double* dst = P.part + ((((size_t)b * P.NH + h) * S + qrow) * ns + split) * (2 + kHeadDim);
+      if (q4 == 0) {
+        dst[0] = m;
+        dst[1] = l;
+      }
+#pragma unroll
+      for (int d = 0; d < 8; ++d)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[2 + 16 * d + 4 * i + q4] = o[d][i];
+    }
+    return;
+  }
   const size_t doff = ((size_t)(b * S + qrow) * P.NH + h) * kHeadDim;
   float lo = INFINITY, hi = -INFINITY;
   if (rowok) {
@@ -243,10 +269,24 @@ bool attention_prefill_supported(int NH, int NKV) {
   return NKV >= 1 && NH % NKV == 0 && NH / NKV <= a2::GMAX;
 }
 
+int attention_prefill_split(int B, int S, int NKV, int T, int pmax) {
+  const int nwg = B * NKV * ((S + a2::QT - 1) / a2::QT);
+  if (S < 2 || nwg >= 128) return 1;
+  const int nch = (std::min(pmax + S, T) - 1) / a2::KC + 1;  // chunks of the last tile
+  return std::max(1, std::min(std::min((512 + nwg - 1) / nwg, 8), nch));
+}
+
+static int max_pos(int B, const PosArgs& pos) {
+  int m = 0;
+  for (int b = 0; b < B; ++b) m = std::max(m, pos.p[b]);
+  return m;
+}
+
 hipError_t launch_attention_prefill(hipStream_t st, int B, int S, int NH, int NKV, int T,
                                     const float* q, const float* k_cache, const float* v_cache,
                                     const float* k_delta, const float* v_delta,
-                                    const PosArgs& pos, float* out, const SeqStats* stats) {
+                                    const PosArgs& pos, float* out, const SeqStats* stats,
+                                    void* part) {
   // one-time attribute set-up (a function-local static: initialised once,
   // thread-safe)
   static const hipError_t attr = hipFuncSetAttribute(
@@ -267,13 +307,17 @@ hipError_t launch_attention_prefill(hipStream_t st, int B, int S, int NH, int NK
   P.vd = v_delta;
   P.pos = pos;
   P.out = out;
-  if (stats) P.stats = *stats;
+  P.nsplit = part ? attention_prefill_split(B, S, NKV, T, max_pos(B, pos)) : 1;
+  P.part = (double*)part;
+  if (stats && P.nsplit == 1) P.stats = *stats;
   const int lds = a2::LDS_BYTES;
-  hipLaunchKernelGGL(k_attn_prefill<false>, dim3(B * NKV * P.nqt), dim3(64 * P.G), lds, st, P);
+  hipLaunchKernelGGL(k_attn_prefill<false>, dim3(B * NKV * P.nqt * P.nsplit), dim3(64 * P.G), lds,
+                     st, P);
+  if (P.nsplit > 1) return launch_attention_merge(st, B, S, NH, P.nsplit, P.part, out, false);
   return hipGetLastError();
 }
 
-hipError_t launch_attention_prefill_bf16(hipStream_t st, const AttnBf16Params& Q) {
+hipError_t launch_attention_prefill_bf16(hipStream_t st, const AttnBf16Params& Q, void* part) {
   static const hipError_t attr = hipFuncSetAttribute(
       (const void*)k_attn_prefill<true>, hipFuncAttributeMaxDynamicSharedMemorySize, a2::LDS_BYTES);
   if (attr != hipSuccess) return attr;
@@ -293,8 +337,11 @@ hipError_t launch_attention_prefill_bf16(hipStream_t st, const AttnBf16Params& Q
   P.vd = (const float*)Q.vd;
   P.pos = Q.pos;
   P.out = (float*)Q.out;
-  hipLaunchKernelGGL(k_attn_prefill<true>, dim3(P.B * P.NKV * P.nqt), dim3(64 * P.G), a2::LDS_BYTES,
-                     st, P);
+  P.nsplit = part ? attention_prefill_split(Q.B, Q.S, Q.NKV, Q.T, max_pos(Q.B, Q.pos)) : 1;
+  P.part = (double*)part;
+  hipLaunchKernelGGL(k_attn_prefill<true>, dim3(P.B * P.NKV * P.nqt * P.nsplit), dim3(64 * P.G),
+                     a2::LDS_BYTES, st, P);
+  if (P.nsplit > 1) return launch_attention_merge(st, Q.B, Q.S, Q.NH, P.nsplit, P.part, Q.out, true);
   return hipGetLastError();
 }
 

@@ -413,7 +413,7 @@ hipError_t launch_rope_bf16(hipStream_t st, int B, int S, int NH, int NKV, const
 hipError_t launch_attn_bf16(hipStream_t st, const AttnBf16Params& P, void* part) {
   if (!attn_bf16_supported(P.NH, P.NKV)) return hipErrorInvalidValue;
   if (P.S == 1) return launch_attention_dec_bf16(st, P, part);
-  return launch_attention_prefill_bf16(st, P);
+  return launch_attention_prefill_bf16(st, P, part);
 }
 
 bool attn_bf16_supported(int NH, int NKV) {

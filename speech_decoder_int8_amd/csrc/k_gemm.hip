@@ -228,7 +228,8 @@ hipError_t launch_gemm(hipStream_t st, int M, int K, const int8_t* codes, const 
   }
   P.ncols = (epi == EPI_SWIGLU) ? segs[0].n : P.seg_start[nseg];
   if (!tiled_only && gemm_big_supported(M, K))
-    return launch_gemm_big(st, M, K, codes, s, z, rows_per_seq, segs, nseg, epi, acc_out, stats);
+    return launch_gemm_big(st, M, K, codes, s, z, rows_per_seq, segs, nseg, epi, acc_out, stats,
+                           scratch ? (char*)scratch + gemm_skinny_ws_bytes() : nullptr);
   if (M <= 32) {
     constexpr int BM = 32, BN = 128;
     const int tn = epi == EPI_SWIGLU ? BN / 2 : BN;

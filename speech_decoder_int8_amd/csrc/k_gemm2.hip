@@ -32,6 +32,8 @@
 
 namespace ark {
 
+constexpr int kBigSplitMaxTiles = 64;  // launches of at most this many tiles may split K
+
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8_t2 __attribute__((ext_vector_type(8)));
@@ -50,6 +52,12 @@ struct Gemm2Params {
   // bf_out / bf_swiglu over these segments
   BSeg bs[3];
   int bepi;
+  // K split over ks workgroups per tile (ks > 1 only for the int8 GEMM of a
+  // launch with few tiles): nks K steps each; each split adds its int32
+  // sums into the tile's block of part (device-scope atomics), and a second
+  // kernel reads the totals, clears the blocks and runs the epilogue
+  int ks, nks;
+  int32_t* part;  // [tiles][BM * BN], zero between launches
 };
 
 __device__ __forceinline__ void dma16(const int8_t* src, int8_t* lds_base) {
@@ -71,7 +79,7 @@ __device__ __forceinline__ void wait_vm() {
 template <int FM, int FN>
 __device__ __forceinline__ void g2_epilogue(const Gemm2Params& P, i32x16 (&acc)[FM][FN], int m0,
                                             int nb, int wm, int wn, int lane, int rep) {
-  constexpr int RW = 64;
+  constexpr int RW = FM * 32;
   const bool swiglu = P.epi == EPI_SWIGLU, resid = P.epi == EPI_RESID;
   const int lr = lane & 31, lc = lane >> 5;
   const int rps = P.rows_per_seq;
@@ -159,28 +167,32 @@ __device__ __forceinline__ void g2_epilogue(const Gemm2Params& P, i32x16 (&acc)[
     }
   // SwiGLU outputs' min / max per row of this lane (neutral where no output)
   float elo[FM][16], ehi[FM][16];
+  // rows per batch of requests: 4, or all 16 of a block where a wave holds
+  // only one or two 32x32 blocks (the separate epilogue of a K-split launch,
+  // whose chain of dependent loads is its whole run time)
+  constexpr int VB = FM * FN <= 2 ? 16 : 4;
   const SwigluK SK = swiglu_consts();
 #pragma clang loop unroll(full)
   for (int i = 0; i < FM; ++i) {
 #pragma clang loop unroll(full)
-   for (int vh = 0; vh < 16; vh += 4) {
-    // residual inputs of these 4 rows, all requested before any store
-    float old[4][FN];
+   for (int vh = 0; vh < 16; vh += VB) {
+    // residual inputs of these VB rows, all requested before any store
+    float old[VB][FN];
     if (resid) {
 #pragma clang loop unroll(full)
-      for (int v = vh; v < vh + 4; ++v) {
+      for (int v = vh; v < vh + VB; ++v) {
         const int row = min(rbase + i * 32 + (v >> 2) * 8 + (v & 3), P.M - 1);
 #pragma clang loop unroll(full)
         for (int j = 0; j < FN; ++j) old[v - vh][j] = cout[j][(size_t)row * cldo[j]];
       }
     }
     if (swiglu) {
-      // the 4 rows' values first, with no branch between them (independent
+      // the VB rows' values first, with no branch between them (independent
       // fp64 chains the scheduler can interleave), then the guarded stores
-      float sv[4];
-      int zv[4];
+      float sv[VB];
+      int zv[VB];
 #pragma clang loop unroll(full)
-      for (int v = vh; v < vh + 4; ++v) {
+      for (int v = vh; v < vh + VB; ++v) {
         const int row = rbase + i * 32 + (v >> 2) * 8 + (v & 3);
         float s = rs[i][v >> 2];
         int zc = rz[i][v >> 2];
@@ -192,10 +204,10 @@ __device__ __forceinline__ void g2_epilogue(const Gemm2Params& P, i32x16 (&acc)[
         sv[v - vh] = s;
         zv[v - vh] = zc;
       }
-      float y[4][FN / 2];
-      int agc[4][FN / 2];
+      float y[VB][FN / 2];
+      int agc[VB][FN / 2];
 #pragma clang loop unroll(full)
-      for (int v = vh; v < vh + 4; ++v)
+      for (int v = vh; v < vh + VB; ++v)
 #pragma clang loop unroll(full)
         for (int j = 0; j < FN; j += 2) {
           agc[v - vh][j / 2] = acc[i][j][v] + zv[v - vh] * ccs[j];
@@ -205,11 +217,11 @@ __device__ __forceinline__ void g2_epilogue(const Gemm2Params& P, i32x16 (&acc)[
         }
       // computed here for every lane (not sunk into the guarded stores)
 #pragma clang loop unroll(full)
-      for (int v = 0; v < 4; ++v)
+      for (int v = 0; v < VB; ++v)
 #pragma clang loop unroll(full)
         for (int j = 0; j < FN / 2; ++j) asm volatile("" : "+v"(y[v][j]));
 #pragma clang loop unroll(full)
-      for (int v = vh; v < vh + 4; ++v) {
+      for (int v = vh; v < vh + VB; ++v) {
         elo[i][v] = INFINITY;
         ehi[i][v] = -INFINITY;
         const int row = rbase + i * 32 + (v >> 2) * 8 + (v & 3);
@@ -229,7 +241,7 @@ __device__ __forceinline__ void g2_epilogue(const Gemm2Params& P, i32x16 (&acc)[
       continue;
     }
 #pragma clang loop unroll(full)
-    for (int v = vh; v < vh + 4; ++v) {
+    for (int v = vh; v < vh + VB; ++v) {
       elo[i][v] = INFINITY;
       ehi[i][v] = -INFINITY;
       const int row = rbase + i * 32 + (v >> 2) * 8 + (v & 3);
@@ -294,7 +306,7 @@ __device__ __forceinline__ void g2_epilogue(const Gemm2Params& P, i32x16 (&acc)[
 template <int FM, int FN>
 __device__ __forceinline__ void bf16_epilogue(const Gemm2Params& P, f32x16 (&acc)[FM][FN], int m0,
                                               int nb, int wm, int wn, int lane) {
-  constexpr int RW = 64;
+  constexpr int RW = FM * 32;
   const bool swiglu = P.epi == EPI_SWIGLU;
   const int lr = lane & 31, lc = lane >> 5;
   const int rbase = m0 + wm * RW + lc * 4;
@@ -352,7 +364,22 @@ __device__ __forceinline__ void bf16_epilogue(const Gemm2Params& P, f32x16 (&acc
     }
 }
 
-template <int BM, int BN, int BK, int NS, int NTH, bool BF = false>
+// First row and column of tile t: tiles walk groups of 8 m-tiles x all
+// n-tiles, m fastest (SwiGLU tiles hold BN / 2 output columns).
+template <int BM, int BN>
+__device__ __forceinline__ void tile_origin(const Gemm2Params& P, int t, int& m0, int& nb) {
+  const int tiles_n = P.tiles / P.tiles_m;
+  const int grp = t / (8 * tiles_n);
+  const int gm = min(8, P.tiles_m - grp * 8);
+  const int tg = t - grp * 8 * tiles_n;
+  m0 = (grp * 8 + tg % gm) * BM;
+  nb = (tg / gm) * (P.epi == EPI_SWIGLU ? BN / 2 : BN);
+}
+
+// SPLIT: one K range of a K-split launch (P.ks ranges of P.nks steps per
+// tile): the int32 sums go to the tile's block of P.part and
+// k_gemm_big_epi runs the epilogue afterwards.
+template <int BM, int BN, int BK, int NS, int NTH, bool BF = false, bool SPLIT = false>
 __global__ __launch_bounds__(NTH, NTH == 256 ? 2 : 1) void k_gemm_big(Gemm2Params P) {
   constexpr int NWV = NTH / 64;             // waves
   constexpr int RW = 64;                    // rows per wave
@@ -380,16 +407,18 @@ __global__ __launch_bounds__(NTH, NTH == 256 ? 2 : 1) void k_gemm_big(Gemm2Param
   // n-tiles m-fastest, so the ~64 concurrent workgroups of an XCD share
   // about 8 activation and 8 weight tiles in their L2.
   if (P.stats.cur) stats_clear_other(P.stats);
-  const int per = (P.tiles + 7) / 8;
-  const int t = (blockIdx.x % 8) * per + blockIdx.x / 8;
-  if (t >= P.tiles) return;
-  const int tiles_n = P.tiles / P.tiles_m;
-  const int grp = t / (8 * tiles_n);
-  const int gm = min(8, P.tiles_m - grp * 8);
-  const int tg = t - grp * 8 * tiles_n;
-  const int m0 = (grp * 8 + tg % gm) * BM;
-  const int nb = (tg / gm) * (swiglu ? BN / 2 : BN);
-  const int K = P.K, nk = K / BK;
+  static_assert(!(BF && SPLIT), "K split: int8 only");
+  const int ks = SPLIT ? P.ks : 1;
+  const int per = (P.tiles * ks + 7) / 8;
+  const int u = (blockIdx.x % 8) * per + blockIdx.x / 8;  // split-major: an XCD's run
+  if (u >= P.tiles * ks) return;                           // is mostly one split
+  const int t = u % P.tiles, split = u / P.tiles;
+  int m0, nb;
+  tile_origin<BM, BN>(P, t, m0, nb);
+  const int K = P.K;
+  // this workgroup's K steps: kb .. kb + nk - 1
+  const int kb = SPLIT ? split * P.nks : 0;
+  const int nk = SPLIT ? min(P.nks, K / BK - kb) : K / BK;
 
   // per-lane DMA sources: A instructions wave*A_INS + i, B instructions
   // wave*B_INS + i; instruction u covers rows RPI u .. RPI u + RPI - 1
@@ -419,9 +448,9 @@ __global__ __launch_bounds__(NTH, NTH == 256 ? 2 : 1) void k_gemm_big(Gemm2Param
     bsrc[i] = w + 16 * c;
   }
 
-  auto issue = [&](int ks, int buf) {
+  auto issue = [&](int st, int buf) {
     int8_t* base = lds + buf * STAGE;
-    const int k0 = ks * BK;
+    const int k0 = (kb + st) * BK;
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) dma16(asrc[i] + k0, base + (wave * A_INS + i) * 1024);
 #pragma unroll
@@ -492,10 +521,68 @@ __global__ __launch_bounds__(NTH, NTH == 256 ? 2 : 1) void k_gemm_big(Gemm2Param
             acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
   }
 
+  if constexpr (SPLIT) {
+    // this K range's sums into the tile's block (device-scope atomics,
+    // lane-contiguous words); k_gemm_big_epi applies the epilogue to the
+    // totals after the launch
+    int32_t* blk = P.part + (size_t)t * BM * BN + (size_t)wave * FM * FN * 16 * 64 + lane;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          __hip_atomic_fetch_add(blk + ((i * FN + j) * 16 + v) * 64, acc[i][j][v], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
   if constexpr (BF)
     bf16_epilogue<FM, FN>(P, acc, m0, nb, wm, wn, lane);
   else
     g2_epilogue<FM, FN>(P, acc, m0, nb, wm, wn, lane, blockIdx.x * NWV + wave);
+}
+
+// The epilogue of a K-split launch: one workgroup per tile, one wave per
+// 32 rows x 64 columns (two 32x32 blocks: a SwiGLU pair, or two adjacent
+// store/residual blocks) of the k_gemm_big wave that summed them, so each
+// wave's chain of dependent loads is short.  It reads the tile's int32
+// totals from its block of P.part (in k_gemm_big's accumulator layout) and
+// clears the block for the next launch.
+template <int BM, int BN, int NTH>
+struct EpiShape {
+  static constexpr int NWV = NTH / 64, RW = 2 * BM / NWV, FM = RW / 32, FN = BN / 64;
+  static constexpr int SUB = FM * (FN / 2);                 // epilogue waves per summing wave
+  static constexpr int EW = NWV * SUB;                      // epilogue waves per tile
+  static constexpr int EPW = EW > 8 ? 8 : EW;               // of them per workgroup
+  static_assert(EW % EPW == 0, "epilogue waves");
+};
+
+template <int BM, int BN, int NTH>
+__global__ __launch_bounds__((EpiShape<BM, BN, NTH>::EPW * 64)) void k_gemm_big_epi(Gemm2Params P) {
+  using E = EpiShape<BM, BN, NTH>;
+  constexpr int NWV = E::NWV, RW = E::RW, FM = E::FM, FN = E::FN, SUB = E::SUB;
+  const int tid = threadIdx.x, lane = tid & 63, ew = blockIdx.y * E::EPW + (tid >> 6);
+  const int wave = ew / SUB, i = (ew % SUB) / (FN / 2), j0 = 2 * ((ew % SUB) % (FN / 2));
+  const int wm = wave >> 1, wn = wave & 1;
+  const int t = blockIdx.x;
+  int m0, nb;
+  tile_origin<BM, BN>(P, t, m0, nb);
+  int32_t* blk = P.part + (size_t)t * BM * BN + (size_t)wave * FM * FN * 16 * 64 + lane;
+  i32x16 acc[1][2];
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[0][jj][v] = blk[((i * FN + j0 + jj) * 16 + v) * 64];
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) blk[((i * FN + j0 + jj) * 16 + v) * 64] = 0;
+  // the two blocks as a one-wave 32 x 64 tile: rows m0 + wm RW + 32 i, and
+  // columns nb + wn (BN / 2) + 32 j0 (SwiGLU: output columns nb + (wn FN / 2
+  // + j0 / 2) 32, the pair j0, j0 + 1)
+  const int m1 = m0 + wm * RW + 32 * i;
+  const int n1 = P.epi == EPI_SWIGLU ? nb + (wn * (FN / 2) + j0 / 2) * 32 : nb + wn * (BN / 2) + 32 * j0;
+  g2_epilogue<1, 2>(P, acc, m1, n1, 0, 0, lane, t * E::EW + ew);
 }
 
 template <int BM, int BN, int BK, int NS, int NTH, bool BF = false>
@@ -510,17 +597,47 @@ static hipError_t launch_big(hipStream_t st, Gemm2Params P) {
   const int tn = P.epi == EPI_SWIGLU ? BN / 2 : BN;
   P.tiles_m = (P.M + BM - 1) / BM;
   P.tiles = P.tiles_m * ((P.ncols + tn - 1) / tn);
-  const int grid = 8 * ((P.tiles + 7) / 8);
+  // a launch of few tiles (a single 387-row prompt: 32 tiles for o and down)
+  // would leave most CUs idle: split K (at most 8 ways, at least 4 steps per
+  // split) until about 256 workgroups run
+  P.ks = 1;
+  if (!BF && P.part && P.tiles <= kBigSplitMaxTiles) {
+    const int nkt = P.K / BK;
+    int ks = 1;
+    while (ks < 8 && P.tiles * ks * 2 <= 256 && nkt / (ks * 2) >= 4) ks *= 2;
+    P.nks = (nkt + ks - 1) / ks;
+    P.ks = (nkt + P.nks - 1) / P.nks;  // every split non-empty
+  }
+  const int grid = 8 * ((P.tiles * P.ks + 7) / 8);
+  if constexpr (!BF) {
+    if (P.ks > 1) {
+      static const hipError_t attr_s = hipFuncSetAttribute(
+          (const void*)k_gemm_big<BM, BN, BK, NS, NTH, false, true>,
+          hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+      if (attr_s != hipSuccess) return attr_s;
+      hipLaunchKernelGGL((k_gemm_big<BM, BN, BK, NS, NTH, false, true>), dim3(grid), dim3(NTH), bytes,
+                         st, P);
+      using E = EpiShape<BM, BN, NTH>;
+      hipLaunchKernelGGL((k_gemm_big_epi<BM, BN, NTH>), dim3(P.tiles, E::EW / E::EPW), dim3(E::EPW * 64),
+                         0, st, P);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((k_gemm_big<BM, BN, BK, NS, NTH, BF>), dim3(grid), dim3(NTH), bytes, st, P);
   return hipGetLastError();
 }
 
 bool gemm_big_supported(int M, int K) { return M >= 128 && K % 64 == 0; }
 
+size_t gemm_big_split_ws_bytes() {
+  return (size_t)kBigSplitMaxTiles * 256 * 256 * 4;
+}
+
 hipError_t launch_gemm_big(hipStream_t st, int M, int K, const int8_t* codes, const float* s,
                            const int* z, int rows_per_seq, const Seg* segs, int nseg, Epi epi,
-                           int32_t* acc_out, const SeqStats* stats) {
+                           int32_t* acc_out, const SeqStats* stats, void* split_ws) {
   Gemm2Params P = {};
+  if (split_ws) P.part = (int32_t*)split_ws;
   if (stats && epi == EPI_SWIGLU) P.stats = *stats;
   P.M = M;
   P.K = K;

@@ -366,6 +366,16 @@ hipError_t gemm_skinny_reset(hipStream_t st, void* scratch) {
   return hipGetLastError();
 }
 
+size_t gemm_ws_bytes(size_t max_rows) {
+  return gemm_skinny_ws_bytes() + (max_rows >= 128 ? gemm_big_split_ws_bytes() : 0);
+}
+
+hipError_t gemm_scratch_reset(hipStream_t st, void* scratch, size_t max_rows) {
+  const int n = (int)(gemm_ws_bytes(max_rows) / 4);
+  hipLaunchKernelGGL(k_zero_u32, dim3(256), dim3(256), 0, st, (uint32_t*)scratch, n);
+  return hipGetLastError();
+}
+
 static hipError_t launch_gemm_skinny_rows(hipStream_t st, int M, int row0, int K,
                                           const int8_t* codes, const float* s, const int* z,
                                           int rows_per_seq, const Seg* segs, int nseg, Epi epi,

@@ -269,11 +269,15 @@ hipError_t launch_gemv_codes(hipStream_t st, int B, int K, const int8_t* codes, 
 // MFMA GEMM (k_gemm.hip): shifted codes [M][K]; row r uses (s[r / rows_per_seq],
 // z[r / rows_per_seq]).
 // Large-M GEMM (prefill): same contract as launch_gemm; requires
-// gemm_big_supported(M, K).
+// gemm_big_supported(M, K).  split_ws (optional): gemm_big_split_ws_bytes()
+// bytes, zero before the first launch (they stay zero between launches);
+// with it a launch of few tiles splits K over several workgroups per tile.
 bool gemm_big_supported(int M, int K);
+size_t gemm_big_split_ws_bytes();
 hipError_t launch_gemm_big(hipStream_t st, int M, int K, const int8_t* codes, const float* s,
                            const int* z, int rows_per_seq, const Seg* segs, int nseg, Epi epi,
-                           int32_t* acc_out, const SeqStats* stats = nullptr);
+                           int32_t* acc_out, const SeqStats* stats = nullptr,
+                           void* split_ws = nullptr);
 // Few-row GEMM (k_gemm_sk.hip, M < 128: batched decode, LM head of a
 // batch, short prompts; one pass per 64 rows): same contract; scratch =
 // gemm_skinny_ws_bytes() bytes whose counter words are zero
@@ -281,14 +285,20 @@ hipError_t launch_gemm_big(hipStream_t st, int M, int K, const int8_t* codes, co
 bool gemm_skinny_supported(int M, int K);
 size_t gemm_skinny_ws_bytes();
 hipError_t gemm_skinny_reset(hipStream_t st, void* scratch);
+// The scratch launch_gemm takes for calls of up to max_rows rows: the
+// few-row GEMM's, then (max_rows >= 128) the large-tile GEMM's split-K
+// blocks; gemm_scratch_reset zeroes all of it (once per forward call).
+size_t gemm_ws_bytes(size_t max_rows);
+hipError_t gemm_scratch_reset(hipStream_t st, void* scratch, size_t max_rows);
 // p[0..n) = 0 with a small kernel (no memset node, so it may be captured)
 hipError_t launch_zero_u32(hipStream_t st, uint32_t* p, int n);
 hipError_t launch_gemm_skinny(hipStream_t st, int M, int K, const int8_t* codes, const float* s,
                               const int* z, int rows_per_seq, const Seg* segs, int nseg, Epi epi,
                               int32_t* acc_out, void* scratch);
 // Dispatch: few-row GEMM when scratch is given and the shape allows it, the
-// large-tile GEMM for M >= 128, else the tiled GEMM; tiled_only forces the
-// latter (tests).  stats (EPI_SWIGLU only): the large-tile GEMM also
+// large-tile GEMM for M >= 128 (splitting K over the scratch's split-K
+// blocks when given: scratch must then hold gemm_ws_bytes(M) bytes), else
+// the tiled GEMM; tiled_only forces the latter (tests).  stats (EPI_SWIGLU only): the large-tile GEMM also
 // produces the per-sequence min / max of its output into *stats;
 // gemm_swiglu_stats(M, K, scratch) tells whether this call's dispatch does.
 bool gemm_swiglu_stats(int M, int K, const void* scratch);
@@ -308,18 +318,30 @@ struct PosArgs {
 
 // Prefill attention (S > 1) on fp64 matrix cores; G = NH / NKV <= 8.
 bool attention_prefill_supported(int NH, int NKV);
-// stats (optional): per-sequence min / max of out, as a stats producer.
+// Key-chunk split of a prefill launch of few workgroups (a single prompt):
+// the number of workgroups each query tile's chunks are dealt over (1: no
+// split), given the largest start position pmax.
+int attention_prefill_split(int B, int S, int NKV, int T, int pmax);
+// stats (optional): per-sequence min / max of out, as a stats producer (not
+// when the launch splits; attention_stats tells).  part (optional):
+// attention_ws_bytes(B, S, NH, T) bytes for the split partial states; with
+// it a launch of few workgroups splits its key chunks and merges the states.
 hipError_t launch_attention_prefill(hipStream_t st, int B, int S, int NH, int NKV, int T,
                                     const float* q, const float* k_cache, const float* v_cache,
                                     const float* k_delta, const float* v_delta,
                                     const PosArgs& pos, float* out,
-                                    const SeqStats* stats = nullptr);
+                                    const SeqStats* stats = nullptr, void* part = nullptr);
+// Merge of split partial softmax states part [B][NH][S][nsplit][2 + 128]
+// into out [B][S][NH][128] (fp32, or bf16 when bf16).
+hipError_t launch_attention_merge(hipStream_t st, int B, int S, int NH, int nsplit,
+                                  const double* part, void* out, bool bf16);
 hipError_t launch_rope(hipStream_t st, int B, int S, int NH, int NKV, const float* qkv,
                        const double* cosT, const double* sinT, const PosArgs& pos, float* q,
                        float* k_delta, float* v_delta);
 // Full-cache GQA attention.  out [B*S][NH*128] fp32.  ws: scratch for split
-// partials (decode); attention_ws_bytes gives its size.  stats: as for
-// launch_attention_prefill, honoured when attention_stats(S, NH, NKV).
+// partials (decode, and a split prefill); attention_ws_bytes gives its
+// size.  stats: as for launch_attention_prefill, honoured when
+// attention_stats(B, S, NH, NKV, T, pmax) with pmax the largest position.
 size_t attention_ws_bytes(int B, int S, int NH, int T);
 // Decode (S = 1, NH / NKV <= 8) with the rotary step folded in: q, k and v
 // are read unrotated from the q|k|v projection rows (stride ld) and the
@@ -333,7 +355,7 @@ struct RopeIn {
   float* kd_out;
   float* vd_out;
 };
-bool attention_stats(int S, int NH, int NKV);
+bool attention_stats(int B, int S, int NH, int NKV, int T, int pmax);
 hipError_t launch_attention(hipStream_t st, int B, int S, int NH, int NKV, int T, const float* q,
                             const float* k_cache, const float* v_cache, const float* k_delta,
                             const float* v_delta, const PosArgs& pos, float* out, void* ws,
@@ -506,7 +528,8 @@ bool attn_bf16_supported(int NH, int NKV);
 hipError_t launch_attn_bf16(hipStream_t st, const AttnBf16Params& P, void* part);
 // the prefill attention of k_attn2.hip on bf16 storage (S >= 1,
 // attention_prefill_supported(NH, NKV)); out rounded to bf16
-hipError_t launch_attention_prefill_bf16(hipStream_t st, const AttnBf16Params& P);
+hipError_t launch_attention_prefill_bf16(hipStream_t st, const AttnBf16Params& P,
+                                         void* part = nullptr);
 // the split decode attention of k_attn.hip on bf16 storage (S == 1,
 // NH / NKV <= 8); part: attention_ws_bytes(B, 1, NH, T) bytes of partial
 // states; out rounded to bf16
