@@ -757,7 +757,7 @@ PlanBf16 plan_bf16(const ark_dims& d, int B, int S) {
   p.q = take(R * Q * 2);
   p.attn = take(R * Q * 2);
   p.a = take(R * I * 2);
-  p.part = take(attention_ws_bytes(B, S, d.n_heads, d.max_total_len));  // decode partials
+  p.part = take(attention_ws_bytes(B, S, d.n_heads, d.max_total_len));  // split partials
   p.total = o;
   return p;
 }
