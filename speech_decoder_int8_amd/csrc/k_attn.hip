@@ -505,13 +505,13 @@ size_t attention_ws_bytes(int B, int S, int NH, int T) {
   // prefill with its key chunks split: at most the split of one KV head
   // (more KV heads give more workgroups, so no larger split) at the last
   // position a call of S rows may start at
-  const int ns = S < T ? attention_prefill_split(B, S, 1, T, T - S) : 1;
+  const int ns = S < T ? attention_prefill_split(B, S, NH, 1, T, T - S) : 1;
   return ns > 1 ? (size_t)B * NH * S * ns * kPart * sizeof(double) : 0;
 }
 
 bool attention_stats(int B, int S, int NH, int NKV, int T, int pmax) {
   return S > 1 && attention_prefill_supported(NH, NKV) &&
-         attention_prefill_split(B, S, NKV, T, pmax) == 1;
+         attention_prefill_split(B, S, NH, NKV, T, pmax) == 1;
 }
 
 hipError_t launch_attention_merge(hipStream_t st, int B, int S, int NH, int nsplit,

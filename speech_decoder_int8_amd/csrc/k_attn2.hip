@@ -10,7 +10,10 @@
 // out before the exponential.
 //
 // One workgroup = one (sequence, KV head g, 16-row query tile), one wave per
-// query head of g (the K/V chunk is staged in LDS once for all of them).  A
+// query head of g (the K/V chunk is staged in LDS once for all of them); a
+// launch of few workgroups gives each half of g's heads, and may deal the
+// tile's key chunks over several workgroups whose softmax states a merge
+// kernel combines (attention_prefill_split).  A
 // wave computes S^T = K Q^T as 16x16 blocks (A = 16 keys x 4 dims of K,
 // B = 4 dims x 16 rows of Q^T, kept in registers), the online-softmax update
 // per row, and O^T += V^T P^T (A = 16 dims x 4 keys of V^T, B = 4 keys x 16
@@ -59,6 +62,7 @@ struct Attn2Params {
   // max, sum, weighted values); the split merge writes out
   int nsplit;
   double* part;
+  int hsplit;  // query heads of a KV head dealt over hsplit workgroups
 };
 
 // four fp32 values widened into LDS (exact)
@@ -80,8 +84,9 @@ __global__ __launch_bounds__(512) void k_attn_prefill(Attn2Params P) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nthr = blockDim.x;
   // heavy (late) query tiles first
-  const int ns = max(P.nsplit, 1);
-  const int split = (int)blockIdx.x % ns, tix = (int)blockIdx.x / ns;
+  const int ns = max(P.nsplit, 1), hs = max(P.hsplit, 1);
+  const int split = (int)blockIdx.x % ns, hsel = ((int)blockIdx.x / ns) % hs;
+  const int tix = (int)blockIdx.x / (ns * hs);
   const int nbg = P.B * P.NKV;
   const int qt = P.nqt - 1 - tix / nbg;
   const int bg = tix % nbg;
@@ -89,7 +94,7 @@ __global__ __launch_bounds__(512) void k_attn_prefill(Attn2Params P) {
   const int i0 = qt * QT;
   const int p = P.pos.p[b];
   const int S = P.S, T = P.T;
-  const int h = g * P.G + wave;
+  const int h = g * P.G + hsel * (P.G / hs) + wave;
   const int c16 = lane & 15, q4 = lane >> 4;
   const int qrow = i0 + c16;                     // this lane's query row
   const bool rowok = qrow < S;
@@ -269,8 +274,15 @@ bool attention_prefill_supported(int NH, int NKV) {
   return NKV >= 1 && NH % NKV == 0 && NH / NKV <= a2::GMAX;
 }
 
-int attention_prefill_split(int B, int S, int NKV, int T, int pmax) {
-  const int nwg = B * NKV * ((S + a2::QT - 1) / a2::QT);
+// A launch of few workgroups (a single prompt) also deals the query heads
+// of a KV head over two workgroups of half the waves, so that a wave has a
+// SIMD's matrix core to itself.
+static int head_split(int B, int S, int NH, int NKV) {
+  return B * NKV * ((S + a2::QT - 1) / a2::QT) < 128 && (NH / NKV) % 2 == 0 ? 2 : 1;
+}
+
+int attention_prefill_split(int B, int S, int NH, int NKV, int T, int pmax) {
+  const int nwg = B * NKV * ((S + a2::QT - 1) / a2::QT) * head_split(B, S, NH, NKV);
   if (S < 2 || nwg >= 128) return 1;
   const int nch = (std::min(pmax + S, T) - 1) / a2::KC + 1;  // chunks of the last tile
   return std::max(1, std::min(std::min((512 + nwg - 1) / nwg, 8), nch));
@@ -307,12 +319,13 @@ hipError_t launch_attention_prefill(hipStream_t st, int B, int S, int NH, int NK
   P.vd = v_delta;
   P.pos = pos;
   P.out = out;
-  P.nsplit = part ? attention_prefill_split(B, S, NKV, T, max_pos(B, pos)) : 1;
+  P.nsplit = part ? attention_prefill_split(B, S, NH, NKV, T, max_pos(B, pos)) : 1;
   P.part = (double*)part;
+  P.hsplit = head_split(B, S, NH, NKV);
   if (stats && P.nsplit == 1) P.stats = *stats;
   const int lds = a2::LDS_BYTES;
-  hipLaunchKernelGGL(k_attn_prefill<false>, dim3(B * NKV * P.nqt * P.nsplit), dim3(64 * P.G), lds,
-                     st, P);
+  hipLaunchKernelGGL(k_attn_prefill<false>, dim3(B * NKV * P.nqt * P.hsplit * P.nsplit),
+                     dim3(64 * P.G / P.hsplit), lds, st, P);
   if (P.nsplit > 1) return launch_attention_merge(st, B, S, NH, P.nsplit, P.part, out, false);
   return hipGetLastError();
 }
@@ -337,10 +350,11 @@ hipError_t launch_attention_prefill_bf16(hipStream_t st, const AttnBf16Params& Q
   P.vd = (const float*)Q.vd;
   P.pos = Q.pos;
   P.out = (float*)Q.out;
-  P.nsplit = part ? attention_prefill_split(Q.B, Q.S, Q.NKV, Q.T, max_pos(Q.B, Q.pos)) : 1;
+  P.nsplit = part ? attention_prefill_split(Q.B, Q.S, Q.NH, Q.NKV, Q.T, max_pos(Q.B, Q.pos)) : 1;
   P.part = (double*)part;
-  hipLaunchKernelGGL(k_attn_prefill<true>, dim3(P.B * P.NKV * P.nqt * P.nsplit), dim3(64 * P.G),
-                     a2::LDS_BYTES, st, P);
+  P.hsplit = head_split(Q.B, Q.S, Q.NH, Q.NKV);
+  hipLaunchKernelGGL(k_attn_prefill<true>, dim3(P.B * P.NKV * P.nqt * P.hsplit * P.nsplit),
+                     dim3(64 * P.G / P.hsplit), a2::LDS_BYTES, st, P);
   if (P.nsplit > 1) return launch_attention_merge(st, Q.B, Q.S, Q.NH, P.nsplit, P.part, Q.out, true);
   return hipGetLastError();
 }

@@ -321,7 +321,7 @@ bool attention_prefill_supported(int NH, int NKV);
 // Key-chunk split of a prefill launch of few workgroups (a single prompt):
 // the number of workgroups each query tile's chunks are dealt over (1: no
 // split), given the largest start position pmax.
-int attention_prefill_split(int B, int S, int NKV, int T, int pmax);
+int attention_prefill_split(int B, int S, int NH, int NKV, int T, int pmax);
 // stats (optional): per-sequence min / max of out, as a stats producer (not
 // when the launch splits; attention_stats tells).  part (optional):
 // attention_ws_bytes(B, S, NH, T) bytes for the split partial states; with
