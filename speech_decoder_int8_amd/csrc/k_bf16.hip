@@ -45,19 +45,22 @@ hipError_t launch_to_bf16(hipStream_t st, int64_t n, const float* x, uint16_t* y
   return hipGetLastError();
 }
 
-// ---- few rows: one wave per RB weight rows (per RB gate + RB up rows).
-// A lane takes 16-byte chunks of K; U chunks of every row (and of the MM
-// rows of x) are requested before any is used, so a wave keeps
-// U x rows x 1 KB of weights in flight.
+// ---- few rows: one wave per RB weight rows (per RB gate + RB up rows), or
+// with KW = 4 (long rows: the down projection) the four waves of a
+// workgroup on the same rows, each over a quarter of K, their sums added
+// in LDS in a fixed order.  A lane takes 16-byte chunks of K; U chunks of
+// every row (and of the MM rows of x) are requested before any is used, so
+// a wave keeps U x rows x 1 KB of weights in flight.
 constexpr int kGvMaxRows = 8;
 constexpr int kGvRB = 2;
 
-template <int MM>
+template <int MM, int KW>
 __global__ __launch_bounds__(256) void k_gemv_bf16(GemvBf16Params P) {
   constexpr int U = MM <= 2 ? 4 : (MM <= 4 ? 2 : 1);
   constexpr int NR = 2 * kGvRB;
-  const int lane = threadIdx.x & 63;
-  const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
+  static_assert(KW == 1 || KW == 4, "waves per row group");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wv = KW == 1 ? blockIdx.x * 4 + wave : blockIdx.x;
   const bool swiglu = P.epi == BE_SWIGLU;
   const int n0 = wv * kGvRB;
   if (n0 >= P.ncols) return;
@@ -82,11 +85,14 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(GemvBf16Params P) {
   for (int r = 0; r < NR; ++r)
 #pragma unroll
     for (int m = 0; m < MM; ++m) acc[r][m] = 0.0f;
-  for (int c0 = lane; c0 < NC; c0 += 64 * U) {
+  // this wave's chunks of K: [cb, ce)
+  const int cq = KW == 1 ? NC : (NC + KW - 1) / KW;
+  const int cb = KW == 1 ? 0 : min(NC, wave * cq), ce = KW == 1 ? NC : min(NC, cb + cq);
+  for (int c0 = cb + lane; c0 < ce; c0 += 64 * U) {
     i32x4 wq[U][NR], xq[U][MM];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int c = min(c0 + 64 * u, NC - 1);
+      const int c = min(c0 + 64 * u, ce - 1);
 #pragma unroll
       for (int r = 0; r < NR; ++r)
         if (r < nr) wq[u][r] = __builtin_nontemporal_load((const i32x4*)(wr[r] + 8 * c));
@@ -96,7 +102,7 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(GemvBf16Params P) {
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (c0 + 64 * u >= NC) break;
+      if (c0 + 64 * u >= ce) break;
       float xf[MM][8];
 #pragma unroll
       for (int m = 0; m < MM; ++m) unpack8(xq[u][m], xf[m]);
@@ -121,6 +127,26 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(GemvBf16Params P) {
 #pragma unroll
     for (int m = 0; m < MM; ++m)
       if (r < nr) acc[r][m] = wave_sum_f32(acc[r][m]);
+  if constexpr (KW > 1) {
+    // the K quarters' sums, added in wave order by wave 0
+    __shared__ float part[KW][NR][MM];
+    if (lane == 0)
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int m = 0; m < MM; ++m) part[wave][r][m] = acc[r][m];
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int m = 0; m < MM; ++m) {
+        float a = part[0][r][m];
+#pragma unroll
+        for (int w = 1; w < KW; ++w) a += part[w][r][m];
+        acc[r][m] = a;
+      }
+  }
   if (lane != 0) return;
 #pragma unroll
   for (int r = 0; r < kGvRB; ++r) {
@@ -294,16 +320,29 @@ hipError_t launch_gemm_bf16(hipStream_t st, int M, int K, const uint16_t* x, int
   P.ncols = (epi == BE_SWIGLU) ? segs[0].n : P.seg_start[nseg];
   if (M >= 128 && ldx == K && (2 * K) % 64 == 0) return launch_gemm_big_bf16(st, M, K, x, segs, nseg, epi);
   if (M <= kGvMaxRows) {
-    const int waves = (P.ncols + kGvRB - 1) / kGvRB;
-    const dim3 g((waves + 3) / 4);
+    const int groups = (P.ncols + kGvRB - 1) / kGvRB;  // row groups of one wave
+    // long rows (K >= 4096: the down projection) take a workgroup per group
+    if (K >= 4096) {
+      const dim3 g(groups);
+      if (M == 1)
+        hipLaunchKernelGGL((k_gemv_bf16<1, 4>), g, dim3(256), 0, st, P);
+      else if (M == 2)
+        hipLaunchKernelGGL((k_gemv_bf16<2, 4>), g, dim3(256), 0, st, P);
+      else if (M <= 4)
+        hipLaunchKernelGGL((k_gemv_bf16<4, 4>), g, dim3(256), 0, st, P);
+      else
+        hipLaunchKernelGGL((k_gemv_bf16<8, 4>), g, dim3(256), 0, st, P);
+      return hipGetLastError();
+    }
+    const dim3 g((groups + 3) / 4);
     if (M == 1)
-      hipLaunchKernelGGL(k_gemv_bf16<1>, g, dim3(256), 0, st, P);
+      hipLaunchKernelGGL((k_gemv_bf16<1, 1>), g, dim3(256), 0, st, P);
     else if (M == 2)
-      hipLaunchKernelGGL(k_gemv_bf16<2>, g, dim3(256), 0, st, P);
+      hipLaunchKernelGGL((k_gemv_bf16<2, 1>), g, dim3(256), 0, st, P);
     else if (M <= 4)
-      hipLaunchKernelGGL(k_gemv_bf16<4>, g, dim3(256), 0, st, P);
+      hipLaunchKernelGGL((k_gemv_bf16<4, 1>), g, dim3(256), 0, st, P);
     else
-      hipLaunchKernelGGL(k_gemv_bf16<8>, g, dim3(256), 0, st, P);
+      hipLaunchKernelGGL((k_gemv_bf16<8, 1>), g, dim3(256), 0, st, P);
   } else if (M <= 32) {
     constexpr int BM = 32, BN = 64;
     const int tn = epi == BE_SWIGLU ? BN / 2 : BN;
