@@ -42,7 +42,10 @@ hipError_t launch_im2col(hipStream_t st, int B, int T, int C, int stride, const 
   return hipGetLastError();
 }
 
-// ---- LayerNorm: one wave per row, four rows per workgroup
+// ---- LayerNorm: one wave per row, four rows per workgroup.  With NPL > 0
+// (D <= 64 NPL) the row is read once into registers, every load requested
+// before the first sum; NPL = 0 reads it three times (any D).
+template <int NPL>
 __global__ __launch_bounds__(256) void k_layernorm(int R, int D, int rows_per_seq,
                                                    const float* __restrict__ x,
                                                    const float* __restrict__ g,
@@ -54,22 +57,52 @@ __global__ __launch_bounds__(256) void k_layernorm(int R, int D, int rows_per_se
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= R) return;
   const float* xr = x + (size_t)row * D;
-  double s = 0.0;
-  for (int i = lane; i < D; i += 64) s += (double)xr[i];
-  const double mu = wave_sum(s) / (double)D;
-  double v = 0.0;
-  for (int i = lane; i < D; i += 64) {
-    const double c = (double)xr[i] - mu;
-    v += c * c;
-  }
-  const double r = 1.0 / sqrt(wave_sum(v) / (double)D + eps);
   float lo = INFINITY, hi = -INFINITY;
   float* yr = y + (size_t)row * D;
-  for (int i = lane; i < D; i += 64) {
-    const float o = (float)((((double)xr[i] - mu) * r) * (double)g[i] + (double)bb[i]);
-    yr[i] = o;
-    lo = fminf(lo, o);
-    hi = fmaxf(hi, o);
+  if constexpr (NPL > 0) {
+    float xv[NPL];
+#pragma unroll
+    for (int k = 0; k < NPL; ++k) {
+      const int i = lane + 64 * k;
+      xv[k] = i < D ? xr[i] : 0.0f;
+    }
+    double s = 0.0;
+#pragma unroll
+    for (int k = 0; k < NPL; ++k) s += (double)xv[k];
+    const double mu = wave_sum(s) / (double)D;
+    double v = 0.0;
+#pragma unroll
+    for (int k = 0; k < NPL; ++k) {
+      const double c = lane + 64 * k < D ? (double)xv[k] - mu : 0.0;
+      v += c * c;
+    }
+    const double r = 1.0 / sqrt(wave_sum(v) / (double)D + eps);
+#pragma unroll
+    for (int k = 0; k < NPL; ++k) {
+      const int i = lane + 64 * k;
+      if (i < D) {
+        const float o = (float)((((double)xv[k] - mu) * r) * (double)g[i] + (double)bb[i]);
+        yr[i] = o;
+        lo = fminf(lo, o);
+        hi = fmaxf(hi, o);
+      }
+    }
+  } else {
+    double s = 0.0;
+    for (int i = lane; i < D; i += 64) s += (double)xr[i];
+    const double mu = wave_sum(s) / (double)D;
+    double v = 0.0;
+    for (int i = lane; i < D; i += 64) {
+      const double c = (double)xr[i] - mu;
+      v += c * c;
+    }
+    const double r = 1.0 / sqrt(wave_sum(v) / (double)D + eps);
+    for (int i = lane; i < D; i += 64) {
+      const float o = (float)((((double)xr[i] - mu) * r) * (double)g[i] + (double)bb[i]);
+      yr[i] = o;
+      lo = fminf(lo, o);
+      hi = fmaxf(hi, o);
+    }
   }
   if (stats) {
     lo = wave_min(lo);
@@ -81,8 +114,12 @@ __global__ __launch_bounds__(256) void k_layernorm(int R, int D, int rows_per_se
 hipError_t launch_layernorm(hipStream_t st, int R, int D, int rows_per_seq, const float* x,
                             const float* g, const float* b, double eps, float* y,
                             const SeqStats& S) {
-  hipLaunchKernelGGL(k_layernorm, dim3((R + 3) / 4), dim3(256), 0, st, R, D, rows_per_seq, x, g, b,
-                     eps, y, S);
+  if (D <= 64 * 20)
+    hipLaunchKernelGGL(k_layernorm<20>, dim3((R + 3) / 4), dim3(256), 0, st, R, D, rows_per_seq, x,
+                       g, b, eps, y, S);
+  else
+    hipLaunchKernelGGL(k_layernorm<0>, dim3((R + 3) / 4), dim3(256), 0, st, R, D, rows_per_seq, x,
+                       g, b, eps, y, S);
   return hipGetLastError();
 }
 
