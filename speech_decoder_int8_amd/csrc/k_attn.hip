@@ -11,6 +11,8 @@
 // staged in LDS once for all of them.  Decode (S = 1) splits T across
 // workgroups and merges the partial softmax states in a second kernel.
 
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -499,6 +501,13 @@ __global__ __launch_bounds__(128) void k_attn_combine(int S, int NH, int nsplit,
 }
 
 static int decode_split(int T) { return T / 32; }
+// the splits a decode launch needs: those holding a key at or before the
+// largest position (later ones would only write empty states)
+static int decode_split(int T, int B, const PosArgs& pos) {
+  int pmax = 0;
+  for (int b = 0; b < B; ++b) pmax = std::max(pmax, pos.p[b]);
+  return std::min(T / 32, pmax / ad::DK + 1);
+}
 
 size_t attention_ws_bytes(int B, int S, int NH, int T) {
   if (S == 1) return (size_t)B * NH * decode_split(T) * kPart * sizeof(double);
@@ -547,7 +556,7 @@ hipError_t launch_attention(hipStream_t st, int B, int S, int NH, int NKV, int T
   if (rope && !(S == 1 && P.G <= 8)) return hipErrorInvalidValue;
   if (rope) P.rope = *rope;
   if (S == 1 && P.G <= 8) {
-    P.nsplit = decode_split(T);
+    P.nsplit = decode_split(T, B, pos);
     P.tsplit = ad::DK;
     hipLaunchKernelGGL(k_attn_dec<false>, dim3(P.nsplit, B * NKV), dim3(256), 0, st, P);
     hipLaunchKernelGGL(k_attn_combine<false>, dim3(B * NH), dim3(128), 0, st, 1, NH, P.nsplit, P.part,
@@ -581,7 +590,7 @@ hipError_t launch_attention_dec_bf16(hipStream_t st, const AttnBf16Params& Q, vo
   P.pos = Q.pos;
   P.out = (float*)Q.out;
   P.part = (double*)part;
-  P.nsplit = decode_split(Q.T);
+  P.nsplit = decode_split(Q.T, Q.B, Q.pos);
   P.tsplit = ad::DK;
   hipLaunchKernelGGL(k_attn_dec<true>, dim3(P.nsplit, Q.B * Q.NKV), dim3(256), 0, st, P);
   hipLaunchKernelGGL(k_attn_combine<true>, dim3(Q.B * Q.NH), dim3(128), 0, st, 1, Q.NH, P.nsplit,
