@@ -513,8 +513,8 @@ size_t attention_ws_bytes(int B, int S, int NH, int T) {
   if (S == 1) return (size_t)B * NH * decode_split(T) * kPart * sizeof(double);
   // prefill with its key chunks split: at most the split of one KV head
   // (more KV heads give more workgroups, so no larger split) at the last
-  // position a call of S rows may start at
-  const int ns = S < T ? attention_prefill_split(B, S, NH, 1, T, T - S) : 1;
+  // position a call of S rows may start at (S <= T for any valid call)
+  const int ns = attention_prefill_split(B, S, NH, 1, T, std::max(0, T - S));
   return ns > 1 ? (size_t)B * NH * S * ns * kPart * sizeof(double) : 0;
 }
 

@@ -242,7 +242,9 @@ def test_gate_up_swiglu_and_sequence_range(B, R, n, k):
 @pytest.mark.parametrize("B,S,T,pos", [(2, 37, 512, (0, 300)), (3, 20, 64, (44, 0, 10)),
                                        (1, 1, 512, (100,)), (2, 1, 1024, (0, 1023)),
                                        (3, 1, 512, (31, 32, 511)), (4, 1, 64, (0, 63, 5, 33)),
-                                       (1, 70, 128, (58,))])
+                                       (1, 70, 128, (58,)),
+                                       # a prefill that fills the cache, its key chunks split
+                                       (1, 128, 128, (0,))])
 def test_attention_and_sequence_range(B, S, T, pos):
     NH, NKV, D = 16, 2, 128
     rng = np.random.default_rng(B * 1000 + S * 10 + T)
