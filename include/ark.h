@@ -516,8 +516,12 @@ int ark_test_layernorm(int32_t B, int32_t S, int32_t D, const float* x, const fl
  * frames and H heads of 64: qkv [B][F][3 H 64] (q | k | v rows as the
  * projections write them), rotary tables [>= F][32] fp64; out [B][F][H 64]
  * and each clip's (min, max) of out in lo[B], hi[B].  workspace >=
- * ark_test_dynquant_workspace_bytes().  Errors: ARK_E_NULL, ARK_E_SHAPE,
+ * ark_test_dynquant_workspace_bytes(); with
+ * ark_test_enc_attention_workspace_bytes(B, F, H) bytes a launch of few
+ * workgroups takes the split form ark_audio_encoder uses (key chunks over
+ * several workgroups, then a merge).  Errors: ARK_E_NULL, ARK_E_SHAPE,
  * ARK_E_WORKSPACE, ARK_E_HIP. */
+size_t ark_test_enc_attention_workspace_bytes(int32_t B, int32_t F, int32_t H);
 int ark_test_enc_attention(int32_t B, int32_t F, int32_t H, const float* qkv,
                            const double* rope_cos, const double* rope_sin, float* out, float* lo,
                            float* hi, void* workspace, size_t workspace_bytes, void* stream);

@@ -136,6 +136,7 @@ _SIGS = {
     "ark_test_dynquant_workspace_bytes": (C.c_size_t, []),
     "ark_test_layernorm": (C.c_int, [I32, I32, I32, P, P, P, C.c_double, P, P, P, P, C.c_size_t, P]),
     "ark_test_enc_attention": (C.c_int, [I32, I32, I32, P, P, P, P, P, P, P, C.c_size_t, P]),
+    "ark_test_enc_attention_workspace_bytes": (C.c_size_t, [I32, I32, I32]),
     "ark_test_swiglu": (C.c_int, [C.c_int64, P, P, P, P]),
     "ark_test_gate_up_workspace_bytes": (C.c_size_t, [I32, I32, I32]),
     "ark_test_gate_up": (C.c_int, [I32, I32, P, P, P, C.POINTER(ArkQLinear), C.POINTER(ArkQLinear),
@@ -833,7 +834,8 @@ def test_enc_attention(qkv, H, cos, sin, stream=None):
     out = torch.empty((B, F, H * 64), dtype=torch.float32, device=qkv.device)
     lo = torch.empty(B, dtype=torch.float32, device=qkv.device)
     hi = torch.empty_like(lo)
-    ws = _stats_ws()
+    ws = torch.empty(lib().ark_test_enc_attention_workspace_bytes(B, F, H), dtype=torch.uint8,
+                     device=qkv.device)
     _check("ark_test_enc_attention", lib().ark_test_enc_attention(
         B, F, H, _ptr(qkv), _ptr(cos), _ptr(sin), _ptr(out), _ptr(lo), _ptr(hi), _ptr(ws),
         ws.numel(), _stream(stream)))

@@ -677,7 +677,7 @@ int check_adapter(const ark_adapter* A, int B, int frames) {
 
 // ---- audio encoder
 struct EncoderPlan {
-  size_t cols, a1, x, h, qkv, attn, f, codes, rs, stats, qs, qz, gsk, total;
+  size_t cols, a1, x, h, qkv, attn, f, codes, rs, stats, qs, qz, gsk, part, total;
 };
 
 EncoderPlan encoder_plan(const ark_encoder& E, int B, int M) {
@@ -703,6 +703,7 @@ EncoderPlan encoder_plan(const ark_encoder& E, int B, int M) {
   p.qs = take((size_t)kMaxBatch * 4);
   p.qz = take((size_t)kMaxBatch * 4);
   p.gsk = take(gemm_ws_bytes(std::max(R1, R)));
+  p.part = take(enc_attention_ws_bytes(B, (int)F, E.n_heads));  // split attention states
   p.total = o;
   return p;
 }
@@ -1137,7 +1138,7 @@ int ark_audio_encoder(const ark_encoder* E, int32_t B, int32_t mel_frames, const
     Seg qkvs[3] = {seg_of(L.q, qkv, 3 * D), seg_of(L.k, qkv + D, 3 * D),
                    seg_of(L.v, qkv + 2 * D, 3 * D)};
     HIP_TRY(launch_gemm(st, R, D, codes, qs, qz, F, qkvs, 3, EPI_STORE, nullptr, gsk));
-    HIP_TRY(launch_enc_attention(st, B, F, H, qkv, E->rope_cos, E->rope_sin, attn, sb));
+    HIP_TRY(launch_enc_attention(st, B, F, H, qkv, E->rope_cos, E->rope_sin, attn, sb, ws + p.part));
     HIP_TRY(launch_quant_seq(st, R, D, F, attn, D, nullptr, nullptr, sb.cur, codes, nullptr, qs,
                              qz));
     Seg os[1] = {seg_of(L.o, x, D)};
@@ -1495,6 +1496,11 @@ int ark_test_layernorm(int32_t B, int32_t S, int32_t D, const float* x, const fl
   return ARK_OK;
 }
 
+size_t ark_test_enc_attention_workspace_bytes(int32_t B, int32_t F, int32_t H) {
+  if (B < 1 || F < 1 || H < 1) return 0;
+  return align_up(ark_test_dynquant_workspace_bytes()) + enc_attention_ws_bytes(B, F, H);
+}
+
 int ark_test_enc_attention(int32_t B, int32_t F, int32_t H, const float* qkv,
                            const double* rope_cos, const double* rope_sin, float* out, float* lo,
                            float* hi, void* workspace, size_t workspace_bytes, void* stream) {
@@ -1505,8 +1511,13 @@ int ark_test_enc_attention(int32_t B, int32_t F, int32_t H, const float* qkv,
   hipStream_t st = (hipStream_t)stream;
   int* stw = (int*)workspace;
   const SeqStats sa = {stw, stw + kStatsSetInts, B};
+  // the split form when the workspace holds its states
+  void* part = workspace_bytes >= ark_test_enc_attention_workspace_bytes(B, F, H) &&
+                       enc_attention_ws_bytes(B, F, H) > 0
+                   ? (char*)workspace + align_up(ark_test_dynquant_workspace_bytes())
+                   : nullptr;
   HIP_TRY(launch_seq_stats_init(st, sa.cur));
-  HIP_TRY(launch_enc_attention(st, B, F, H, qkv, rope_cos, rope_sin, out, sa));
+  HIP_TRY(launch_enc_attention(st, B, F, H, qkv, rope_cos, rope_sin, out, sa, part));
   HIP_TRY(launch_seq_stats_read(st, sa.cur, B, lo, hi));
   return ARK_OK;
 }

@@ -7,6 +7,8 @@
 //   * im2col of the width-3 convolutions (tap-major rows),
 //   * LayerNorm in fp64 with the per-sequence range of its output,
 //   * bidirectional rotary self-attention on fp64 matrix cores.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -158,6 +160,12 @@ struct EncAttnParams {
   const double* sin;
   float* out;
   SeqStats stats;
+  // nsplit > 1 (a clip of few query tiles): chunk c of the keys goes to
+  // split c % nsplit, which writes its unnormalised softmax state per row
+  // and head to part ([B][H][F][nsplit][2 + 64]: max, sum, weighted
+  // values); k_enc_merge writes out and folds the range
+  int nsplit;
+  double* part;
 };
 
 constexpr int ENC_ATTN_LDS = (ea::KC * ea::KP + ea::KC * ea::VP) * 8;
@@ -169,8 +177,10 @@ __global__ __launch_bounds__(512) void k_enc_attn(EncAttnParams P) {
   double* Vs = Ks + KC * KP;       // [KC][VP]
   if (P.stats.cur) stats_clear_other(P.stats);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int grp = blockIdx.x % P.ngrp;
-  const int bh = blockIdx.x / P.ngrp;
+  const int ns = max(P.nsplit, 1);
+  const int split = blockIdx.x % ns;
+  const int grp = (blockIdx.x / ns) % P.ngrp;
+  const int bh = blockIdx.x / ns / P.ngrp;
   const int b = bh / P.H, h = bh % P.H;
   const int F = P.F, W3 = 3 * P.H * DH;
   const int c16 = lane & 15, q4 = lane >> 4;
@@ -226,8 +236,8 @@ __global__ __launch_bounds__(512) void k_enc_attn(EncAttnParams P) {
       sn[e] = sr[e];
     }
   };
-  fetch(0);
-  for (int c = 0; c < nch; ++c) {
+  fetch(split * KC);
+  for (int c = split; c < nch; c += ns) {
     const int j0 = c * KC;
     __syncthreads();  // the previous chunk's K and V are used
     {
@@ -253,7 +263,7 @@ __global__ __launch_bounds__(512) void k_enc_attn(EncAttnParams P) {
       *(double2*)(vd + 32) = double2{wb[0], wb[1]};
       *(double2*)(vd + 34) = double2{wb[2], wb[3]};
     }
-    if (c + 1 < nch) fetch(j0 + KC);
+    if (c + ns < nch) fetch(j0 + ns * KC);
     __syncthreads();
 
     f64x4_t sc[4];
@@ -304,6 +314,20 @@ __global__ __launch_bounds__(512) void k_enc_attn(EncAttnParams P) {
     }
   }
   // o[d][i] = O^T[dim 16 d + 4 i + q4][qrow]
+  if (ns > 1) {
+    if (rowok) {
+      double* dst = P.part + ((((size_t)b * P.H + h) * F + qrow) * ns + split) * (2 + DH);
+      if (q4 == 0) {
+        dst[0] = m;
+        dst[1] = l;
+      }
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[2 + 16 * d + 4 * i + q4] = o[d][i];
+    }
+    return;
+  }
   float lo = INFINITY, hi = -INFINITY;
   if (rowok) {
     float* dst = P.out + ((size_t)b * F + qrow) * (P.H * DH) + h * DH;
@@ -324,9 +348,54 @@ __global__ __launch_bounds__(512) void k_enc_attn(EncAttnParams P) {
   }
 }
 
+// Merge of the split states of one (clip, head, row): one wave, a lane per
+// dim; each split weighted by exp(m_s - M) with M the largest m_s (a split
+// that saw no key of the row is skipped); the row's range folded into the
+// clip's.
+__global__ __launch_bounds__(64) void k_enc_merge(int F, int H, int ns, const double* __restrict__ part,
+                                                  float* __restrict__ out, SeqStats S) {
+  using namespace ea;
+  if (S.cur) stats_clear_other(S);
+  const int idx = blockIdx.x;  // (b H + h) F + row
+  const int row = idx % F, h = (idx / F) % H, b = idx / (F * H);
+  const int d = threadIdx.x;
+  const double* src = part + (size_t)idx * ns * (2 + DH);
+  double M = -INFINITY;
+  for (int u = 0; u < ns; ++u) M = fmax(M, src[(size_t)u * (2 + DH)]);
+  double L = 0.0, O = 0.0;
+  for (int u = 0; u < ns; ++u) {
+    const double* q = src + (size_t)u * (2 + DH);
+    const double mu = q[0];
+    if (mu == -INFINITY) continue;
+    const double w = exp(mu - M);
+    L += q[1] * w;
+    O += q[2 + d] * w;
+  }
+  const float y = (float)(O / L);
+  out[((size_t)b * F + row) * (H * DH) + h * DH + d] = y;
+  if (S.cur) {
+    const float lo = wave_min(y), hi = wave_max(y);
+    if (d == 0) stats_fold(S, idx, b, lo, hi);
+  }
+}
+
+// key-chunk splits of a launch of few workgroups (a short clip)
+int enc_attention_split(int B, int F, int H) {
+  const int nqt = (F + ea::QT - 1) / ea::QT;
+  const int nwg = B * H * ((nqt + ea::NW - 1) / ea::NW);
+  const int nch = (F + ea::KC - 1) / ea::KC;
+  if (nwg >= 128) return 1;
+  return std::max(1, std::min(std::min((256 + nwg - 1) / nwg, 8), nch));
+}
+
+size_t enc_attention_ws_bytes(int B, int F, int H) {
+  const int ns = enc_attention_split(B, F, H);
+  return ns > 1 ? (size_t)B * H * F * ns * (2 + ea::DH) * sizeof(double) : 0;
+}
+
 hipError_t launch_enc_attention(hipStream_t st, int B, int F, int H, const float* qkv,
                                 const double* cos, const double* sin, float* out,
-                                const SeqStats& S) {
+                                const SeqStats& S, void* part) {
   // one-time attribute set-up (a function-local static: initialised once,
   // thread-safe)
   static const hipError_t attr = hipFuncSetAttribute(
@@ -343,7 +412,13 @@ hipError_t launch_enc_attention(hipStream_t st, int B, int F, int H, const float
   P.sin = sin;
   P.out = out;
   P.stats = S;
-  hipLaunchKernelGGL(k_enc_attn, dim3(B * H * P.ngrp), dim3(64 * ea::NW), ENC_ATTN_LDS, st, P);
+  P.nsplit = part ? enc_attention_split(B, F, H) : 1;
+  P.part = (double*)part;
+  if (P.nsplit > 1) P.stats.cur = nullptr;  // the merge folds the range
+  hipLaunchKernelGGL(k_enc_attn, dim3(B * H * P.ngrp * P.nsplit), dim3(64 * ea::NW), ENC_ATTN_LDS, st,
+                     P);
+  if (P.nsplit > 1)
+    hipLaunchKernelGGL(k_enc_merge, dim3(B * H * F), dim3(64), 0, st, F, H, P.nsplit, P.part, out, S);
   return hipGetLastError();
 }
 

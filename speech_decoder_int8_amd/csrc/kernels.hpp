@@ -233,9 +233,12 @@ hipError_t launch_layernorm(hipStream_t st, int R, int D, int rows_per_seq, cons
 // rows [B][F][3 H 64] (q | k | v), q and k rotated (fp64 tables
 // [>= F][32]) and rounded to fp32 before use, softmax(q.k / 8) v in fp64;
 // out [B][F][H 64] and its per-sequence range into S (S.cur != nullptr).
+// part (optional): enc_attention_ws_bytes(B, F, H) bytes; with it a launch
+// of few workgroups (a short clip) splits the key chunks and merges.
+size_t enc_attention_ws_bytes(int B, int F, int H);
 hipError_t launch_enc_attention(hipStream_t st, int B, int F, int H, const float* qkv,
                                 const double* cos, const double* sin, float* out,
-                                const SeqStats& S);
+                                const SeqStats& S, void* part = nullptr);
 
 // Dynamic uint8 quantisation with one (s, z) per sequence from the range in
 // `set`: codes of x (or of h recomputed from x, rs and gain when rs !=
