@@ -29,7 +29,7 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
 struct Plan {
-  size_t x, rs, codes, qkv, q, attn, a, stats, qs, qz, part, done, gsk, mega, hn, total;
+  size_t x, rs, codes, qkv, q, attn, a, stats, qs, qz, part, done, rowpart, gsk, mega, hn, total;
 };
 
 bool use_mega(const ark_dims& d, int B, int S) {
@@ -68,6 +68,8 @@ Plan plan(const ark_dims& d, int B, int S) {
   p.part = take(std::max(attention_ws_bytes(B, 1, d.n_heads, d.max_total_len),
                          attention_ws_bytes(B, S, d.n_heads, d.max_total_len)));
   p.done = take((size_t)kMaxBatch * 4);
+  // split sums of the decode GEMMs that run their epilogue per row
+  p.rowpart = take(gemm_rows_part_bytes((int)std::min<size_t>(B, 64), (int)std::max(Q + 2 * KV, H)));
   p.gsk = take(gemm_ws_bytes(R));
   p.mega = take(B == 1 ? decode_mega_ws_bytes(d.n_layers, d.max_total_len) : 0);
   p.hn = take((size_t)B * H * 4);  // final-normed rows of the int4 LM tier
@@ -344,6 +346,12 @@ int run_forward(const ark_model* m, int B, int S, float* x, const int32_t* pos_h
   void* gsk = ws + p.gsk;  // GEMM scratch (few-row blocks, split-K blocks)
   HIP_TRY(gemm_scratch_reset(st, gsk, (size_t)R));
   if (!gemv && !rowq) HIP_TRY(launch_seq_stats_init(st, sa.cur));
+  // one row per sequence: the q|k|v, o and down GEMMs store their split sums
+  // and a row kernel runs the epilogue, for o and down together with the
+  // RMSNorm and quantiser that follow (RMSNorm 2; the next layer's RMSNorm 1
+  // or the final norm)
+  int32_t* rpart = (int32_t*)(ws + p.rowpart);
+  bool h1_ready = false;  // layer l's RMSNorm 1 codes came from layer l-1's down step
   PosArgs pos;
   memset(&pos, 0, sizeof(pos));
   int pmax = 0;
@@ -365,10 +373,14 @@ int run_forward(const ark_model* m, int B, int S, float* x, const int32_t* pos_h
     if (gemv) {
       HIP_TRY(launch_gemv(st, B, H, x, H, L.ln1, d.rms_eps, qkvs, 3, EPI_STORE, qdp(l, 0)));
     } else if (rowq) {
-      HIP_TRY(launch_norm_quant_row(st, B, H, x, H, L.ln1, d.rms_eps, codes, qs, qz,
-                                    (float*)dptr(l, ARK_DUMP_H1)));
+      if (!h1_ready)
+        HIP_TRY(launch_norm_quant_row(st, B, H, x, H, L.ln1, d.rms_eps, codes, qs, qz,
+                                      (float*)dptr(l, ARK_DUMP_H1)));
       QCOPY(l, 0, H);
-      HIP_TRY(launch_gemm(st, R, H, codes, qs, qz, S, qkvs, 3, EPI_STORE, nullptr, gsk));
+      if (gemm_rows_supported(R, H, EPI_STORE, ldqkv))
+        HIP_TRY(launch_gemm_rows(st, R, H, codes, qs, qz, qkvs, 3, EPI_STORE, rpart, nullptr));
+      else
+        HIP_TRY(launch_gemm(st, R, H, codes, qs, qz, S, qkvs, 3, EPI_STORE, nullptr, gsk));
     } else {
       HIP_TRY(launch_row_stats(st, R, H, S, x, H, L.ln1, d.rms_eps, rs, sa));
       HIP_TRY(launch_quant_seq(st, R, H, S, x, H, rs, L.ln1, sa.cur, codes, nullptr, qs, qz,
@@ -399,16 +411,37 @@ int run_forward(const ark_model* m, int B, int S, float* x, const int32_t* pos_h
     } else if (rowq) {
       HIP_TRY(launch_norm_quant_row(st, B, Q, attn, Q, nullptr, 0.0, codes, qs, qz));
       QCOPY(l, 1, Q);
-      HIP_TRY(launch_gemm(st, R, Q, codes, qs, qz, S, os, 1, EPI_RESID, nullptr, gsk));
-      D2D(dptr(l, ARK_DUMP_X1), x, (size_t)R * H * 4);
-      HIP_TRY(launch_norm_quant_row(st, B, H, x, H, L.ln2, d.rms_eps, codes, qs, qz,
-                                    (float*)dptr(l, ARK_DUMP_H2)));
+      if (gemm_rows_supported(R, Q, EPI_RESID, H)) {
+        const RowNorm n2 = {L.ln2, d.rms_eps, codes, qs, qz, (float*)dptr(l, ARK_DUMP_H2)};
+        HIP_TRY(launch_gemm_rows(st, R, Q, codes, qs, qz, os, 1, EPI_RESID, rpart, &n2));
+        D2D(dptr(l, ARK_DUMP_X1), x, (size_t)R * H * 4);
+      } else {
+        HIP_TRY(launch_gemm(st, R, Q, codes, qs, qz, S, os, 1, EPI_RESID, nullptr, gsk));
+        D2D(dptr(l, ARK_DUMP_X1), x, (size_t)R * H * 4);
+        HIP_TRY(launch_norm_quant_row(st, B, H, x, H, L.ln2, d.rms_eps, codes, qs, qz,
+                                      (float*)dptr(l, ARK_DUMP_H2)));
+      }
       QCOPY(l, 2, H);
       HIP_TRY(launch_gemm(st, R, H, codes, qs, qz, S, gus, 2, EPI_SWIGLU, nullptr, gsk));
       D2D(dptr(l, ARK_DUMP_A), a, (size_t)R * I * 4);
       HIP_TRY(launch_norm_quant_row(st, B, I, a, I, nullptr, 0.0, codes, qs, qz));
       QCOPY(l, 3, I);
-      HIP_TRY(launch_gemm(st, R, I, codes, qs, qz, S, ds, 1, EPI_RESID, nullptr, gsk));
+      // the down step also runs the next RMSNorm: layer l+1's, or the final
+      // norm of the int8 LM head over more than 4 rows
+      const bool last = l + 1 == d.n_layers;
+      const bool head_rows = last && logits && !m->lm_head4.w && B > 4;
+      if (gemm_rows_supported(R, I, EPI_RESID, H)) {
+        float* h_dump = last ? nullptr : (float*)dptr(l + 1, ARK_DUMP_H1);
+        if (last && dr && dr->base) h_dump = (float*)(dr->base + dr->head[0]);
+        const RowNorm n1 = {last ? m->final_norm : m->layers[l + 1].ln1, d.rms_eps, codes, qs, qz,
+                            h_dump};
+        h1_ready = !last || head_rows;
+        HIP_TRY(launch_gemm_rows(st, R, I, codes, qs, qz, ds, 1, EPI_RESID, rpart,
+                                 h1_ready ? &n1 : nullptr));
+      } else {
+        h1_ready = false;
+        HIP_TRY(launch_gemm(st, R, I, codes, qs, qz, S, ds, 1, EPI_RESID, nullptr, gsk));
+      }
     } else {
       if (!att_stats) HIP_TRY(launch_row_stats(st, R, Q, S, attn, Q, nullptr, 0.0, nullptr, sb));
       HIP_TRY(launch_quant_seq(st, R, Q, S, attn, Q, nullptr, nullptr, sb.cur, codes, nullptr, qs,
@@ -448,7 +481,9 @@ int run_forward(const ark_model* m, int B, int S, float* x, const int32_t* pos_h
       HIP_TRY(launch_gemv(st, B, H, last, S * H, m->final_norm, d.rms_eps, lm, 1, EPI_STORE,
                           hq.codes ? &hq : nullptr));
     } else {
-      if (norm_quant_row_supported(H)) {
+      if (rowq && h1_ready) {
+        // the last down step ran the final norm and its quantiser
+      } else if (norm_quant_row_supported(H)) {
         HIP_TRY(launch_norm_quant_row(st, B, H, last, S * H, m->final_norm, d.rms_eps, codes, qs,
                                       qz, hq.h));
       } else {

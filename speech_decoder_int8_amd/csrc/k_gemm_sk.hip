@@ -60,6 +60,7 @@ struct GemmSkParams {
   int32_t* part;     // [tiles][32 MB][ROWS] int32 sums of split launches, zero between launches
   uint32_t* ctr;     // [tiles] arrival counters, zero between launches
   int32_t* acc_out;  // optional [M][ncols]: raw sums (tests)
+  int32_t* pout;     // optional [ks][M][ncols]: each split's int32 sums, no epilogue
 };
 
 __device__ __forceinline__ int sk_swz(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
@@ -163,6 +164,23 @@ __global__ __launch_bounds__(256, 2) void k_gemm_sk(GemmSkParams P) {
 #pragma unroll
       for (int bI = 0; bI < MB; ++bI)
         acc[bI] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[bI][c], fb[c], acc[bI], 0, 0, 0);
+  }
+
+  if (P.pout) {
+    // this K range's sums as they are; a row kernel adds the splits and
+    // runs the epilogue
+    const int col = tile * ROWS + wave * 32 + j;
+    if (col < P.ncols) {
+      int32_t* dst = P.pout + (size_t)kp * P.M * P.ncols + col;
+#pragma unroll
+      for (int bI = 0; bI < MB; ++bI)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = 32 * bI + (r / 4) * 8 + half * 4 + r % 4;
+          if (m < P.M) dst[(size_t)m * P.ncols] = acc[bI][r];
+        }
+    }
+    return;
   }
 
   if (P.ks > 1) {
@@ -379,7 +397,8 @@ hipError_t gemm_scratch_reset(hipStream_t st, void* scratch, size_t max_rows) {
 static hipError_t launch_gemm_skinny_rows(hipStream_t st, int M, int row0, int K,
                                           const int8_t* codes, const float* s, const int* z,
                                           int rows_per_seq, const Seg* segs, int nseg, Epi epi,
-                                          int32_t* acc_out, void* scratch);
+                                          int32_t* acc_out, void* scratch,
+                                          int32_t* pout = nullptr, int* ks_out = nullptr);
 
 hipError_t launch_gemm_skinny(hipStream_t st, int M, int K, const int8_t* codes, const float* s,
                               const int* z, int rows_per_seq, const Seg* segs, int nseg, Epi epi,
@@ -423,7 +442,8 @@ static hipError_t launch_sk(hipStream_t st, const GemmSkParams& P) {
 static hipError_t launch_gemm_skinny_rows(hipStream_t st, int M, int row0, int K,
                                           const int8_t* codes, const float* s, const int* z,
                                           int rows_per_seq, const Seg* segs, int nseg, Epi epi,
-                                          int32_t* acc_out, void* scratch) {
+                                          int32_t* acc_out, void* scratch, int32_t* pout,
+                                          int* ks_out) {
   using namespace sk;
   GemmSkParams P = {};
   P.M = M;
@@ -457,7 +477,30 @@ static hipError_t launch_gemm_skinny_rows(hipStream_t st, int M, int row0, int K
   P.ks = (nss + P.nss - 1) / P.nss;
   P.part = (int32_t*)scratch;
   P.ctr = (uint32_t*)((char*)scratch + (size_t)SK_MAX_SPLIT_TILES * 32 * MAX_MB * ROWS * 4);
+  P.pout = pout;
+  if (ks_out) *ks_out = P.ks;
   return M > 32 ? launch_sk<2>(st, P) : launch_sk<1>(st, P);
+}
+
+bool gemm_rows_supported(int M, int K, Epi epi, int ncols) {
+  return gemm_skinny_supported(M, K) && M <= 32 * sk::MAX_MB && epi != EPI_SWIGLU &&
+         ncols >= 1 && row_epi_supported(ncols);
+}
+
+size_t gemm_rows_part_bytes(int M, int ncols) { return (size_t)8 * M * ncols * 4; }
+
+hipError_t launch_gemm_rows(hipStream_t st, int M, int K, const int8_t* codes, const float* s,
+                            const int* z, const Seg* segs, int nseg, Epi epi, int32_t* part,
+                            const RowNorm* norm) {
+  int ncols = 0;
+  for (int i = 0; i < nseg; ++i) ncols += segs[i].n;
+  if (!part || !gemm_rows_supported(M, K, epi, ncols) || (norm && (epi != EPI_RESID || nseg != 1)))
+    return hipErrorInvalidValue;
+  int ks = 0;
+  hipError_t e = launch_gemm_skinny_rows(st, M, 0, K, codes, s, z, 1, segs, nseg, epi, nullptr,
+                                         nullptr, part, &ks);
+  if (e != hipSuccess) return e;
+  return launch_row_epi(st, M, ks, part, s, z, segs, nseg, epi, norm);
 }
 
 }  // namespace ark

@@ -325,6 +325,156 @@ __global__ __launch_bounds__(QNT) void k_norm_quant_row(int K, const float* __re
 
 bool norm_quant_row_supported(int K) { return K >= 1 && K <= QNT * QMAX; }
 
+// Epilogue of a split few-row GEMM, one workgroup of 1024 threads per row
+// (sequence): adds the ks int32 partial sums of every output column
+// (part [ks][M][ncols], exact), dequantises as the GEMM epilogues do
+// (fp32(fp32(acc + (128 - z) * colsum) * fp32(s * sw)), + bias, + the
+// residual input), stores the row and, given a gain, runs RMSNorm and the
+// dynamic quantiser on it in registers exactly as k_norm_quant_row does
+// (same thread layout t + 1024 k, sums and reductions), so the codes are
+// those a separate k_norm_quant_row launch would give.  VPT values per
+// thread (ncols <= 1024 * VPT).
+struct RowEpiParams {
+  int M, ncols, ks, nseg, resid;
+  const int32_t* part;
+  const float* qs;
+  const int* qz;
+  Seg seg[3];
+  int seg_start[4];
+  RowNorm nrm;
+  int has_norm;
+};
+
+template <int VPT>
+__global__ __launch_bounds__(QNT) void k_row_epi(RowEpiParams P) {
+  static_assert(VPT <= QMAX, "row longer than the quantiser's registers");
+  __shared__ double redd[QNT / 64];
+  __shared__ float redf[2 * (QNT / 64)];
+  const int r = blockIdx.x, t = threadIdx.x;
+  const int ncols = P.ncols;
+  // every split's sums of this thread's columns requested together
+  int acc[VPT];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) acc[k] = 0;
+  {
+    int pv[8][VPT];
+#pragma unroll
+    for (int sp = 0; sp < 8; ++sp)
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        const int n = t + QNT * k;
+        pv[sp][k] = (sp < P.ks && n < ncols) ? P.part[((size_t)sp * P.M + r) * ncols + n] : 0;
+      }
+#pragma unroll
+    for (int sp = 0; sp < 8; ++sp)
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) acc[k] += pv[sp][k];
+  }
+  const float rs = P.qs[r];
+  const int rz = 128 - P.qz[r];
+  const int sb1 = P.nseg > 1 ? P.seg_start[1] : ncols, sb2 = P.nseg > 2 ? P.seg_start[2] : ncols;
+  int cs[VPT];
+  float sw[VPT], bv[VPT], old[VPT];
+  float* dst[VPT];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int n = min(t + QNT * k, ncols - 1);
+    const int si = n >= sb2 ? 2 : (n >= sb1 ? 1 : 0);
+    const Seg& S = P.seg[si];
+    const int nn = n - P.seg_start[si];
+    cs[k] = S.cs[nn];
+    sw[k] = S.sw[nn];
+    bv[k] = S.bias ? S.bias[nn] : 0.f;
+    dst[k] = S.out + (size_t)r * S.ldo + nn;
+    old[k] = P.resid ? *dst[k] : 0.f;
+  }
+  float v[QMAX];
+#pragma unroll
+  for (int k = 0; k < QMAX; ++k) v[k] = 0.f;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int n = t + QNT * k;
+    const int si = n >= sb2 ? 2 : (n >= sb1 ? 1 : 0);
+    float y = dequant(acc[k] + rz * cs[k], rs, sw[k]);
+    if (P.seg[si].bias) y = y + bv[k];
+    if (P.resid) y = old[k] + y;
+    v[k] = y;
+    if (n < ncols) *dst[k] = y;
+  }
+  if (!P.has_norm) return;
+  const RowNorm& N = P.nrm;
+  const int K = ncols;
+  float gv[QMAX];
+#pragma unroll
+  for (int k = 0; k < QMAX; ++k) gv[k] = (k < VPT && t + QNT * k < K) ? N.g[t + QNT * k] : 0.f;
+#pragma unroll
+  for (int k = 0; k < QMAX; ++k)
+    if (!(t + QNT * k < K)) v[k] = 0.f;
+  double ss = 0.0;
+#pragma unroll
+  for (int k = 0; k < QMAX; ++k) ss += (double)v[k] * (double)v[k];
+  ss = block_sum<QNT>(ss, redd);
+  const double rsn = 1.0 / sqrt(ss / (double)K + N.eps);
+#pragma unroll
+  for (int k = 0; k < QMAX; ++k)
+    if (t + QNT * k < K) v[k] = (float)(((double)v[k] * rsn) * (double)gv[k]);
+  float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < QMAX; ++k)
+    if (t + QNT * k < K) {
+      lo = fminf(lo, v[k]);
+      hi = fmaxf(hi, v[k]);
+    }
+  block_minmax<QNT>(lo, hi, redf);
+  const QParam p = quant_param(lo, hi);
+  if (t == 0) {
+    N.s[r] = p.s;
+    N.z[r] = p.z;
+  }
+  int8_t* cr = N.codes + (size_t)r * K;
+#pragma unroll
+  for (int k = 0; k < QMAX; ++k)
+    if (t + QNT * k < K) cr[t + QNT * k] = shift_code(quant_code(v[k], p));
+  if (N.h_out)
+#pragma unroll
+    for (int k = 0; k < QMAX; ++k)
+      if (t + QNT * k < K) N.h_out[(size_t)r * K + t + QNT * k] = v[k];
+}
+
+bool row_epi_supported(int ncols) { return ncols >= 1 && ncols <= QNT * 4; }
+
+hipError_t launch_row_epi(hipStream_t st, int M, int ks, const int32_t* part, const float* s,
+                          const int* z, const Seg* segs, int nseg, Epi epi, const RowNorm* norm) {
+  RowEpiParams P = {};
+  P.M = M;
+  P.ks = ks;
+  P.nseg = nseg;
+  P.resid = epi == EPI_RESID;
+  P.part = part;
+  P.qs = s;
+  P.qz = z;
+  P.seg_start[0] = 0;
+  for (int i = 0; i < nseg; ++i) {
+    P.seg[i] = segs[i];
+    P.seg_start[i + 1] = P.seg_start[i] + segs[i].n;
+  }
+  P.ncols = P.seg_start[nseg];
+  if (norm) {
+    P.nrm = *norm;
+    P.has_norm = 1;
+  }
+  if (ks < 1 || ks > 8 || nseg < 1 || nseg > 3 || epi == EPI_SWIGLU || !row_epi_supported(P.ncols))
+    return hipErrorInvalidValue;
+  const int vpt = (P.ncols + QNT - 1) / QNT;
+  if (vpt <= 2)
+    hipLaunchKernelGGL(k_row_epi<2>, dim3(M), dim3(QNT), 0, st, P);
+  else if (vpt <= 3)
+    hipLaunchKernelGGL(k_row_epi<3>, dim3(M), dim3(QNT), 0, st, P);
+  else
+    hipLaunchKernelGGL(k_row_epi<4>, dim3(M), dim3(QNT), 0, st, P);
+  return hipGetLastError();
+}
+
 hipError_t launch_norm_quant_row(hipStream_t st, int B, int K, const float* x, int ldx,
                                  const float* gain, double eps, int8_t* codes, float* s_out,
                                  int* z_out, float* h_out) {

@@ -312,6 +312,30 @@ hipError_t launch_gemm(hipStream_t st, int M, int K, const int8_t* codes, const 
                        int32_t* acc_out, void* scratch = nullptr, bool tiled_only = false,
                        const SeqStats* stats = nullptr);
 
+// Few-row GEMM in two launches (M <= 64 rows, one per sequence; store or
+// residual epilogue): the split-K launch stores each split's int32 sums
+// (part: gemm_rows_part_bytes(M, ncols) bytes), then a row kernel adds them
+// and runs the same epilogue, and with `norm` (residual, one segment) also
+// RMSNorm and the dynamic quantiser of each output row as
+// launch_norm_quant_row does.  Results are those of launch_gemm followed by
+// launch_norm_quant_row.
+struct RowNorm {
+  const float* g;
+  double eps;
+  int8_t* codes;
+  float* s;
+  int* z;
+  float* h_out;
+};
+bool row_epi_supported(int ncols);
+bool gemm_rows_supported(int M, int K, Epi epi, int ncols);
+size_t gemm_rows_part_bytes(int M, int ncols);
+hipError_t launch_gemm_rows(hipStream_t st, int M, int K, const int8_t* codes, const float* s,
+                            const int* z, const Seg* segs, int nseg, Epi epi, int32_t* part,
+                            const RowNorm* norm);
+hipError_t launch_row_epi(hipStream_t st, int M, int ks, const int32_t* part, const float* s,
+                          const int* z, const Seg* segs, int nseg, Epi epi, const RowNorm* norm);
+
 // ---- rotary + attention (k_attn.hip)
 // qkv_raw [R][q_dim + 2*kv_dim] (bias added) -> q_rot [R][q_dim], k_delta /
 // v_delta [R][kv_dim]; row r of sequence r / S sits at pos[r / S] + r % S.
