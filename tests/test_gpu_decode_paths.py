@@ -88,6 +88,52 @@ def test_decode_steps_match_oracle(models, path, p0):
         p = p + 1
 
 
+@pytest.mark.parametrize("B", [6, 40])
+def test_batched_decode_matches_oracle(models, B):
+    """The multi-kernel path at more than 4 sequences on the real geometry:
+    the q|k|v, o and down GEMMs store their split sums and a row kernel per
+    sequence runs the epilogue and, behind o and down, the RMSNorm and
+    quantiser that follow (B = 40: two 32-row blocks per weight fragment).
+    Each sequence at its own position, two steps against the oracle."""
+    om, gm = models
+    assert ark.decode_path(gm, B) == 0
+    rng = np.random.default_rng(B)
+    T = CFG.max_total_len
+    pos = rng.integers(1, T - 2, size=B)
+    shape = (B, T, CFG.n_kv_heads, CFG.head_dim)
+    kc, vc = [], []
+    for _ in range(CFG.n_layers):
+        k = rng.standard_normal(shape).astype(np.float32)
+        v = rng.standard_normal(shape).astype(np.float32)
+        for b in range(B):
+            k[b, pos[b]:] = np.nan  # unwritten rows: garbage the mask must drop
+            v[b, pos[b]:] = np.inf
+        kc.append(k)
+        vc.append(v)
+    gs = GpuState(gm, B, 1)
+    gs.load_caches(kc, vc)
+    mask = CFG.mask()
+    tok = rng.integers(0, CFG.vocab - 64, size=B).astype(np.int32)
+    p = pos.astype(np.int64)
+    for step in range(2):
+        kd, vd, hid = gs.decode(t(tok), p)
+        assert ark.decode_check(gm, B, gs.ws) == ark.ARK_OK
+        lo, kdo, vdo, hido = oracle.decode_step(om, tok, p, kc, vc)
+        for l in range(CFG.n_layers):
+            assert_close(host(kd[l]), kdo[l], f"B={B} step {step} k_delta {l}")
+            assert_close(host(vd[l]), vdo[l], f"B={B} step {step} v_delta {l}")
+        assert_close(host(hid), hido, f"B={B} step {step} hidden")
+        lg = host(gs.logits)
+        err = assert_close(lg, lo, f"B={B} step {step} logits") * np.max(np.abs(lo))
+        check_tokens(oracle.masked_argmax(lg, mask), oracle.masked_argmax(lo, mask), lo, mask, err,
+                     f"B={B} step {step}")
+        gs.write_back(p, kd, vd)
+        kc = [oracle.cache_write(kc[l], kdo[l], p) for l in range(CFG.n_layers)]
+        vc = [oracle.cache_write(vc[l], vdo[l], p) for l in range(CFG.n_layers)]
+        tok = oracle.masked_argmax(lo, mask)
+        p = p + 1
+
+
 def test_greedy_loop_matches_oracle(models, path):
     om, gm = models
     assert ark.decode_path(gm, 1) == (1 if path == "mega" else 0)

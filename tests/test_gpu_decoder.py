@@ -119,9 +119,11 @@ def test_small_prefill_at_positions_with_garbage_rows(small):
     run_parity(cfg, om, gm, x, pos, kc, vc, 3)
 
 
-@pytest.mark.parametrize("B", [1, 2, 6])
+@pytest.mark.parametrize("B", [1, 2, 6, 40])
 def test_small_decode_from_prefilled_caches(small, B):
-    # B <= 4 runs the fused decode GEMV, B > 4 the MFMA GEMM path
+    # B <= 4 runs the fused decode GEMV, B > 4 the MFMA GEMM path (33..64
+    # rows: two 32-row blocks per weight fragment, split sums through the
+    # row kernel)
     cfg, om, gm = small
     cfg = cfg.with_(batch=B, cache_fill=(5, 40))
     lengths = synth.cache_lengths(cfg)

@@ -87,14 +87,14 @@ def _rows(B, S, per_seq, rng):
     return out
 
 
-@pytest.mark.parametrize("case", ["mega_b1", "gemv_b1", "gemv_b3", "rows_b6"])
+@pytest.mark.parametrize("case", ["mega_b1", "gemv_b1", "gemv_b3", "rows_b6", "rows_b40"])
 def test_decode_record_small(small, case, monkeypatch):
     om, gm = small
     if case == "mega_b1":
         monkeypatch.delenv("ARK_DECODE_PATH", raising=False)
     else:
         monkeypatch.setenv("ARK_DECODE_PATH", "multi")
-    B = {"mega_b1": 1, "gemv_b1": 1, "gemv_b3": 3, "rows_b6": 6}[case]
+    B = {"mega_b1": 1, "gemv_b1": 1, "gemv_b3": 3, "rows_b6": 6, "rows_b40": 40}[case]
     assert ark.decode_path(gm, B) == (1 if case == "mega_b1" else 0)
     rng = np.random.default_rng(100 + B)
     lengths = rng.integers(0, CFG.max_total_len - 1, size=B)
