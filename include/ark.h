@@ -348,8 +348,8 @@ int ark_decode_step(const ark_model* m, int32_t B, const int32_t* token_ids,
  * ark_noalloc_max_bytes() bytes (64 MiB), held until the process ends; its
  * address is resolved on the first call on each device.  The call
  * allocates nothing.  A call whose ark_workspace_bytes(&m->d, B, 1) exceeds
- * that size returns ARK_E_NOALLOC (the ARK geometry at T = 512 needs about
- * 34 MiB at B = 1 and less at 2 <= B <= 64).  Every call on a GPU shares
+ * that size returns ARK_E_NOALLOC (the ARK geometry at T = 512 needs at
+ * most about 36 MiB: 34.6 MiB at B = 1, 9-36 MiB at 2 <= B <= 64).  Every call on a GPU shares
  * that GPU's array and it keeps the last call's contents (the step clears
  * what must start at zero): calls that overlap on one GPU - concurrent
  * streams or threads - race and give undefined results.  Status of a
