@@ -69,7 +69,7 @@ Plan plan(const ark_dims& d, int B, int S) {
                          attention_ws_bytes(B, S, d.n_heads, d.max_total_len)));
   p.done = take((size_t)kMaxBatch * 4);
   // split sums of the decode GEMMs that run their epilogue per row
-  p.rowpart = take(gemm_rows_part_bytes((int)std::min<size_t>(B, 64), (int)std::max(Q + 2 * KV, H)));
+  p.rowpart = take(gemm_rows_part_bytes((int)std::min<size_t>(B, 64), (int)H));
   p.gsk = take(gemm_ws_bytes(R));
   p.mega = take(B == 1 ? decode_mega_ws_bytes(d.n_layers, d.max_total_len) : 0);
   p.hn = take((size_t)B * H * 4);  // final-normed rows of the int4 LM tier
@@ -346,10 +346,9 @@ int run_forward(const ark_model* m, int B, int S, float* x, const int32_t* pos_h
   void* gsk = ws + p.gsk;  // GEMM scratch (few-row blocks, split-K blocks)
   HIP_TRY(gemm_scratch_reset(st, gsk, (size_t)R));
   if (!gemv && !rowq) HIP_TRY(launch_seq_stats_init(st, sa.cur));
-  // one row per sequence: the q|k|v, o and down GEMMs store their split sums
-  // and a row kernel runs the epilogue, for o and down together with the
-  // RMSNorm and quantiser that follow (RMSNorm 2; the next layer's RMSNorm 1
-  // or the final norm)
+  // one row per sequence: the o and down GEMMs store their split sums and a
+  // row kernel runs the epilogue together with the RMSNorm and quantiser
+  // that follow (RMSNorm 2; the next layer's RMSNorm 1 or the final norm)
   int32_t* rpart = (int32_t*)(ws + p.rowpart);
   bool h1_ready = false;  // layer l's RMSNorm 1 codes came from layer l-1's down step
   PosArgs pos;
@@ -377,10 +376,9 @@ int run_forward(const ark_model* m, int B, int S, float* x, const int32_t* pos_h
         HIP_TRY(launch_norm_quant_row(st, B, H, x, H, L.ln1, d.rms_eps, codes, qs, qz,
                                       (float*)dptr(l, ARK_DUMP_H1)));
       QCOPY(l, 0, H);
-      if (gemm_rows_supported(R, H, EPI_STORE, ldqkv))
-        HIP_TRY(launch_gemm_rows(st, R, H, codes, qs, qz, qkvs, 3, EPI_STORE, rpart, nullptr));
-      else
-        HIP_TRY(launch_gemm(st, R, H, codes, qs, qz, S, qkvs, 3, EPI_STORE, nullptr, gsk));
+      // q|k|v keep the split GEMM's own epilogue (faster here than the split
+      // sums through the row kernel: nothing follows it to fuse)
+      HIP_TRY(launch_gemm(st, R, H, codes, qs, qz, S, qkvs, 3, EPI_STORE, nullptr, gsk));
     } else {
       HIP_TRY(launch_row_stats(st, R, H, S, x, H, L.ln1, d.rms_eps, rs, sa));
       HIP_TRY(launch_quant_seq(st, R, H, S, x, H, rs, L.ln1, sa.cur, codes, nullptr, qs, qz,
